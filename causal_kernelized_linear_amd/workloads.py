@@ -1,0 +1,123 @@
+"""Seeded synthetic inputs for causal kernelized linear attention.
+
+This module only draws random numbers: it holds none of the attention
+arithmetic, so both the CPU oracle's tests and the HIP path can take their
+inputs from it.  Every draw comes from one ``torch.Generator('cpu')`` seeded
+per workload, in the fixed order Q, K, V, then the gate g or the decode state
+(S, z).  Low-precision tensors are made with ``.to(torch.bfloat16)``, which
+rounds to nearest even; the oracle later receives exactly those rounded values
+widened to float64.
+
+The five named workloads follow the shapes and value distributions of the
+workloads the pages discuss: head dimension 64 or 128 (the 32-head, 128-wide
+linear heads of the hybrid stacks on the learn.pranaymahendrakar.com page,
+"What modern variants change"), chunks of 64-256 (page 1 closing paragraph,
+page 2 "Implementation reality"), and decay gates close to one (page 2 "Try it
+yourself").  No dataset is involved.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str                     # "fwd", "gated" or "decode"
+    B: int
+    H: int
+    N: int                        # tokens (1 for a decode step)
+    D: int
+    Dv: int
+    dtype: str                    # "f32" or "bf16": dtype of q, k, v and o
+    chunks: tuple = (128,)
+    seed: int = 0
+    scale: float = 1.0            # multiplies N(0,1) draws of q, k, v (in fp32, before rounding)
+    eps: float = 1e-6
+    note: str = ""
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+
+WORKLOADS = {
+    "fp32_small": Workload("fp32_small", "fwd", 1, 2, 512, 64, 64, "f32", (64,), 1001,
+                           note="fp32 parity case, oracle finishes in seconds"),
+    "train_bf16": Workload("train_bf16", "fwd", 8, 16, 4096, 64, 64, "bf16", (128,), 1002,
+                           note="training-shaped layer"),
+    "longctx_bf16": Workload("longctx_bf16", "fwd", 1, 32, 65536, 128, 128, "bf16", (64, 128, 256), 1003,
+                             scale=0.5, note="long context, chunk sweep"),
+    "decode_bf16": Workload("decode_bf16", "decode", 256, 32, 1, 128, 128, "bf16", (1,), 1004,
+                            note="one recurrent step for 256 sequences, fp32 state"),
+    "gated_bf16": Workload("gated_bf16", "gated", 4, 16, 8192, 64, 64, "bf16", (128,), 1005,
+                           note="scalar gate per head per token"),
+}
+
+
+def _randn(gen, shape, scale=1.0):
+    x = torch.randn(*shape, generator=gen, dtype=torch.float32)
+    if scale != 1.0:
+        x = x * scale
+    return x
+
+
+def make_inputs(w: Workload, B=None, H=None, N=None):
+    """Draw the inputs of workload ``w`` (optionally with B, H or N overridden).
+
+    Returns a dict of CPU tensors in their stored dtypes:
+      fwd:    q, k [B,H,N,D]; v [B,H,N,Dv]
+      gated:  the same plus g [B,H,N] float32, g = 0.9 + 0.1*sigmoid(N(0,1))
+      decode: q, k [B,H,D]; v [B,H,Dv]; S [B,H,D,Dv] and z [B,H,D] float32,
+              each 1000*|N(0,1)| (a state after about 1000 tokens)
+    """
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    N = w.N if N is None else N
+    gen = torch.Generator(device="cpu").manual_seed(w.seed)
+    dt = w.torch_dtype
+    if w.kind == "decode":
+        q = _randn(gen, (B, H, w.D), w.scale).to(dt)
+        k = _randn(gen, (B, H, w.D), w.scale).to(dt)
+        v = _randn(gen, (B, H, w.Dv), w.scale).to(dt)
+        S = _randn(gen, (B, H, w.D, w.Dv)).abs_().mul_(1000.0)
+        z = _randn(gen, (B, H, w.D)).abs_().mul_(1000.0)
+        return {"q": q, "k": k, "v": v, "S": S, "z": z}
+    q = _randn(gen, (B, H, N, w.D), w.scale).to(dt)
+    k = _randn(gen, (B, H, N, w.D), w.scale).to(dt)
+    v = _randn(gen, (B, H, N, w.Dv), w.scale).to(dt)
+    out = {"q": q, "k": k, "v": v}
+    if w.kind == "gated":
+        out["g"] = 0.9 + 0.1 * torch.sigmoid(_randn(gen, (B, H, N)))
+    return out
+
+
+def random_inputs(seed, B, H, N, D, Dv, dtype="bf16", scale=1.0, gated=False,
+                  g_low=0.9, with_state=False, state_scale=1.0):
+    """Small ad-hoc seeded inputs for edge-case tests (ragged N, odd shapes).
+
+    g (if requested) is drawn uniformly in [g_low, 1].  With ``with_state`` an
+    initial state s0 = state_scale*|N(0,1)|-ish is drawn too (s0 may have either
+    sign; z0 is kept non-negative as a sum of positive features would be).
+    """
+    gen = torch.Generator(device="cpu").manual_seed(seed)
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    q = _randn(gen, (B, H, N, D), scale).to(dt)
+    k = _randn(gen, (B, H, N, D), scale).to(dt)
+    v = _randn(gen, (B, H, N, Dv), scale).to(dt)
+    out = {"q": q, "k": k, "v": v}
+    if gated:
+        u = torch.rand(B, H, N, generator=gen, dtype=torch.float32)
+        out["g"] = g_low + (1.0 - g_low) * u
+    if with_state:
+        out["s0"] = _randn(gen, (B, H, D, Dv)) * state_scale
+        out["z0"] = _randn(gen, (B, H, D)).abs_() * state_scale
+    return out
+
+
+def to_f64(t) -> np.ndarray:
+    """Exact widening of a stored tensor to a float64 numpy array."""
+    return t.detach().to("cpu").to(torch.float64).numpy()

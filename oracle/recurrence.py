@@ -1,0 +1,107 @@
+"""Plain fp64 CPU oracle: causal kernelized linear attention as a token-by-token recurrence.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module; the
+product path (the HIP library and its Python binding) never does.  It shares no
+code with the HIP path.
+
+What it computes (all arithmetic in float64, inputs widened exactly):
+
+* phi(x) = elu(x) + 1 with alpha = 1, i.e. x + 1 for x > 0 and exp(x) for
+  x <= 0.  The map is the one of "Transformers are RNNs" named on the
+  learn.pranaymahendrakar.com page (Researcher level, "Derivation") and on the
+  aicassindra.com page ("Linear Transformer: elu+1 ...").  The exp branch is
+  evaluated on min(x, 0) so the unused branch cannot overflow, as the
+  mlblogg.com page does in "An implementation you can check".
+
+* The causal recurrence of the learn.pranaymahendrakar.com page (Researcher
+  level, "Derivation", the display equations for S_i, z_i and o_i):
+      S_i = S_{i-1} + phi(k_i) v_i^T,   z_i = z_{i-1} + phi(k_i),
+      o_i = S_i^T phi(q_i) / (z_i^T phi(q_i)).
+  The current token is added to the state before the query reads it (the
+  mlblogg.com page, "The causal recurrence"; step 3 before step 4 of the
+  anandmoghan-problems page, "Step-by-Step Approach").  No 1/sqrt(d) scaling:
+  that belongs to the softmax similarity only.
+
+* The denominator is clamped, o_i = num_i / max(den_i, eps) with eps = 1e-6,
+  as the chunked code of the aiwiki.thehackersbrain.dev page divides by
+  ``clamp(min=1e-6)``.  (Other pages add eps instead; the clamp is the reading
+  taken.)
+
+* The gated recurrence with a scalar gate per head and token:
+      S_t = g_t S_{t-1} + phi(k_t) v_t^T,   z_t = g_t z_{t-1} + phi(k_t).
+  The decay form of S is the one on the aiwiki.thehackersbrain.dev page ("What
+  is actually lost", with G_t a scalar) and the learn.pranaymahendrakar.com
+  page ("Try it yourself", "Why plain linear attention underperforms"); the
+  same gate also decays z, which keeps o_i a normalised average with weights
+  prod_{l=j+1..i} g_l phi(q_i).phi(k_j).
+
+* An optional initial state (S0, z0) replaces the zero state, so a sequence
+  can be resumed from a saved state; the final state (S_N, z_N) is returned.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+EPS = 1e-6
+
+
+def phi(x):
+    """elu(x) + 1 with alpha = 1, in float64."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def causal_linear_attention(q, k, v, g=None, s0=None, z0=None, eps=EPS):
+    """Causal kernelized linear attention, one token at a time.
+
+    q, k: [..., N, D]; v: [..., N, Dv]; g: [..., N] or None;
+    s0: [..., D, Dv] or None; z0: [..., D] or None (None means zeros).
+    Leading dimensions (batch, heads) are independent and are vectorised.
+    Returns (o [..., N, Dv], S_N [..., D, Dv], z_N [..., D]), all float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    lead = q.shape[:-2]
+    n, d = q.shape[-2], q.shape[-1]
+    dv = v.shape[-1]
+    if s0 is None:
+        S = np.zeros(lead + (d, dv))
+    else:
+        S = np.array(s0, dtype=np.float64, copy=True)
+    if z0 is None:
+        z = np.zeros(lead + (d,))
+    else:
+        z = np.array(z0, dtype=np.float64, copy=True)
+    if g is not None:
+        g = np.asarray(g, dtype=np.float64)
+    o = np.zeros(lead + (n, dv))
+    for t in range(n):
+        fq = phi(q[..., t, :])
+        fk = phi(k[..., t, :])
+        if g is not None:
+            gt = g[..., t]
+            S = gt[..., None, None] * S
+            z = gt[..., None] * z
+        S = S + fk[..., :, None] * v[..., t, None, :]
+        z = z + fk
+        num = np.einsum("...d,...de->...e", fq, S)
+        den = np.einsum("...d,...d->...", fq, z)
+        o[..., t, :] = num / np.maximum(den, eps)[..., None]
+    return o, S, z
+
+
+def decode_step(q, k, v, S, z, g=None, eps=EPS):
+    """One recurrent decode step from a stored state.
+
+    q, k: [..., D]; v: [..., Dv]; S: [..., D, Dv]; z: [..., D]; g: [...] or None.
+    The new token is folded into the state first, then read, exactly as one
+    iteration of ``causal_linear_attention``.  Returns (o, S', z').
+    """
+    q = np.asarray(q, dtype=np.float64)[..., None, :]
+    k = np.asarray(k, dtype=np.float64)[..., None, :]
+    v = np.asarray(v, dtype=np.float64)[..., None, :]
+    gg = None if g is None else np.asarray(g, dtype=np.float64)[..., None]
+    o, S1, z1 = causal_linear_attention(q, k, v, g=gg, s0=S, z0=z, eps=eps)
+    return o[..., 0, :], S1, z1
