@@ -1,0 +1,338 @@
+"""Benchmark of the causal kernelized linear attention hot path on one MI355X.
+
+One step = one chunked forward (phi, per-chunk state totals, the segment scan,
+the masked intra-chunk products, the carried-state term and the divide) over the
+training-shaped workload B=8, H=16, N=4096, D=Dv=64, bf16, chunk 128, with the
+inputs already resident in HBM.  Input sets are rotated so no step starts with
+its inputs warm in the 256 MB Infinity Cache.  The scalar-gated forward
+(B=4, H=16, N=8192, D=Dv=64, chunk 128), the long-context forward
+(B=1, H=32, N=65536, D=Dv=128, chunk sweep) and the decode step (B=256, H=32,
+D=Dv=128, fp32 state) are timed in the same run and reported in extra fields.
+
+Prints ONE JSON line.  Per-kernel durations come from hipEvents recorded on the
+launch stream around each kernel (the library's measurement hook); the roofline
+object prices the dominant kernel (the output walk) against MI355X's 8 TB/s.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "causal linear-attn fwd tokens/s + % bf16 MFMA peak; decode GB/s % HBM peak"
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        import torch
+        path = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+        self.hip = ctypes.CDLL(path)
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.pool = []
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(h))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+            out.append(h.value)
+        self.pool.extend(out)
+        return out
+
+    def record(self, ev, stream):
+        rc = self.hip.hipEventRecord(ev, stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def ms(self, a, b):
+        f = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(f), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(f.value)
+
+    def close(self):
+        for h in self.pool:
+            self.hip.hipEventDestroy(h)
+        self.pool = []
+
+
+def _median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+
+def fwd_units(w):
+    return w.B * w.H * w.N
+
+
+def fwd_bytes_per_unit(w):
+    es = 4 if w.dtype == "f32" else 2
+    b = (2 * w.D + w.Dv) * es + w.Dv * es
+    if w.kind == "gated":
+        b += 4
+    return b
+
+
+def fwd_flops_per_unit(w, chunk):
+    return 4 * w.D * w.Dv + (chunk + 1) * (w.D + w.Dv)
+
+
+def time_forward(w, chunk, steps, warmup, ev, rotate_bytes=600e6):
+    """Time `steps` forwards of workload w; returns a dict of timings (ms)."""
+    import torch
+    from causal_kernelized_linear_amd import binding, workloads
+
+    dev = torch.device("cuda:0")
+    base = workloads.make_inputs(w)
+    sets = [{n: t.to(dev) for n, t in base.items()}]
+    per_set = sum(t.numel() * t.element_size() for t in sets[0].values())
+    nsets = max(2, min(6, int(rotate_bytes // max(per_set, 1)) + 1))
+    for _ in range(nsets - 1):
+        sets.append({n: t.clone() for n, t in sets[0].items()})
+    outs = [torch.empty(w.B, w.H, w.N, w.Dv, dtype=w.torch_dtype, device=dev) for _ in range(nsets)]
+    ws = torch.empty(max(binding.workspace_bytes(w.B, w.H, w.N, w.D, w.Dv, chunk), 1), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def call(i):
+        s = sets[i % nsets]
+        if w.kind == "gated":
+            binding.fwd_gated(s["q"], s["k"], s["v"], s["g"], chunk=chunk, out=outs[i % nsets], workspace=ws)
+        else:
+            binding.fwd_chunked(s["q"], s["k"], s["v"], chunk=chunk, out=outs[i % nsets], workspace=ws)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    evs = [ev.create(4) for _ in range(steps)]
+    t0, t1 = ev.create(2)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev.record(t0, stream)
+    for i in range(steps):
+        binding.linattn_set_profile_events(*evs[i])
+        call(i)
+    ev.record(t1, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = ev.ms(t0, t1)
+    k_tot = [ev.ms(e[0], e[1]) for e in evs]
+    k_scan = [ev.ms(e[1], e[2]) for e in evs]
+    k_out = [ev.ms(e[2], e[3]) for e in evs]
+    res = {
+        "ms_per_step": total_ms / steps,
+        "wall_ms_per_step": 1e3 * wall / steps,
+        "kernel_ms": {"walk_totals": sum(k_tot) / steps, "scan": sum(k_scan) / steps, "walk_output": sum(k_out) / steps},
+        "kernel_ms_median": {"walk_totals": _median(k_tot), "scan": _median(k_scan), "walk_output": _median(k_out)},
+        "input_sets": nsets,
+    }
+    del sets, outs, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def time_decode(w, steps, warmup, ev):
+    import torch
+    from causal_kernelized_linear_amd import binding, workloads
+
+    dev = torch.device("cuda:0")
+    base = workloads.make_inputs(w)
+    nsets = 2                                  # 2 x 516 MiB of state: never warm in the 256 MB cache
+    sets = [{n: t.to(dev) for n, t in base.items()}]
+    sets.append({n: t.clone() for n, t in sets[0].items()})
+    outs = [torch.empty(w.B, w.H, w.Dv, dtype=w.torch_dtype, device=dev) for _ in range(nsets)]
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def call(i):
+        s = sets[i % nsets]
+        binding.decode_step(s["q"], s["k"], s["v"], s["S"], s["z"], out=outs[i % nsets])
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    evs = [ev.create(2) for _ in range(steps)]
+    for i in range(steps):
+        ev.record(evs[i][0], stream)
+        call(i)
+        ev.record(evs[i][1], stream)
+    torch.cuda.synchronize()
+    ks = [ev.ms(a, b) for a, b in evs]
+    del sets, outs
+    torch.cuda.empty_cache()
+    return {"ms_per_step": sum(ks) / steps, "ms_median": _median(ks)}
+
+
+def decode_bytes(w):
+    es = 4 if w.dtype == "f32" else 2
+    per_head = 2 * (w.D * w.Dv + w.D) * 4 + (2 * w.D + w.Dv) * es + w.Dv * es
+    return per_head * w.B * w.H
+
+
+def cpu_baseline(w, seconds_hint=10.0):
+    """The fp64 oracle, as it stands, on a bounded sample of workload w (all heads,
+    the first tokens), on the host cores; returns tokens/s scaled to the workload."""
+    import numpy as np
+    from causal_kernelized_linear_amd import workloads
+    import oracle
+
+    ntok = 2048
+    inp = workloads.make_inputs(w, N=ntok)
+    q, k, v = (workloads.to_f64(inp[n]) for n in ("q", "k", "v"))
+    t = time.perf_counter()
+    oracle.causal_linear_attention(q, k, v)
+    dt = time.perf_counter() - t
+    # B*ntok token positions (every head) in dt seconds
+    return {
+        "value": w.B * ntok / dt,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"fp64 NumPy recurrence over all {w.B}x{w.H} heads, first {ntok} of {w.N} tokens, "
+                  f"{dt:.1f} s, one thread (elementwise NumPy and einsum), "
+                  f"host has {os.cpu_count()} cpus, affinity {len(os.sched_getaffinity(0))}",
+        "seconds": dt,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--chunk", type=int, default=128)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="time only the headline workload")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from causal_kernelized_linear_amd import binding, workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    binding.lib()
+    ev = HipEvents()
+
+    w = workloads.WORKLOADS["train_bf16"]
+    chunk = args.chunk
+    r = time_forward(w, chunk, args.steps, args.warmup, ev)
+    units = fwd_units(w)
+    tok_s = w.B * w.N / (r["ms_per_step"] * 1e-3)
+    bpu = fwd_bytes_per_unit(w)
+    fpu = fwd_flops_per_unit(w, chunk)
+    t_out = r["kernel_ms"]["walk_output"] * 1e-3
+    achieved = bpu * units / t_out / 1e9
+    step_s = r["ms_per_step"] * 1e-3
+    line = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "train_bf16: causal linear attention forward B=8 H=16 N=4096 D=Dv=64 bf16, "
+                               "fp32 state, chunk %d, eps 1e-6" % chunk,
+                   "B": w.B, "H": w.H, "N": w.N, "D": w.D, "Dv": w.Dv, "chunk": chunk},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "walk_kernel<bf16,64,64,%d,ungated,output>" % chunk,
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "algorithmic_bytes_per_launch": bpu * units,
+            "kernel_ms": r["kernel_ms"]["walk_output"],
+        },
+        "forward": {
+            "kernel_ms": r["kernel_ms"],
+            "kernel_ms_median": r["kernel_ms_median"],
+            "wall_ms_per_step": r["wall_ms_per_step"],
+            "algorithmic_GBps": bpu * units / step_s / 1e9,
+            "hbm_frac": bpu * units / step_s / 1e9 / HBM_PEAK_GBS,
+            "useful_TFLOPs": fpu * units / step_s / 1e12,
+            "mfma_bf16_frac": fpu * units / step_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "input_sets_rotated": r["input_sets"],
+        },
+    }
+
+    if not args.no_extra:
+        extra_steps = max(5, min(args.steps, 20))
+        extra_warm = max(2, min(args.warmup, 5))
+        wg = workloads.WORKLOADS["gated_bf16"]
+        rg = time_forward(wg, 128, extra_steps, extra_warm, ev)
+        ug = fwd_units(wg)
+        sg = rg["ms_per_step"] * 1e-3
+        line["gated"] = {
+            "workload": "gated_bf16: B=4 H=16 N=8192 D=Dv=64 bf16, scalar gate, chunk 128",
+            "tokens_per_s": wg.B * wg.N / sg, "ms_per_step": rg["ms_per_step"], "kernel_ms": rg["kernel_ms"],
+            "algorithmic_GBps": fwd_bytes_per_unit(wg) * ug / sg / 1e9,
+            "hbm_frac": fwd_bytes_per_unit(wg) * ug / sg / 1e9 / HBM_PEAK_GBS,
+            "useful_TFLOPs": fwd_flops_per_unit(wg, 128) * ug / sg / 1e12,
+            "mfma_bf16_frac": fwd_flops_per_unit(wg, 128) * ug / sg / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        }
+        wd = workloads.WORKLOADS["decode_bf16"]
+        rd = time_decode(wd, extra_steps, extra_warm, ev)
+        sd = rd["ms_per_step"] * 1e-3
+        line["decode"] = {
+            "workload": "decode_bf16: B=256 H=32 D=Dv=128, fp32 state, one token",
+            "GBps": decode_bytes(wd) / sd / 1e9, "hbm_frac": decode_bytes(wd) / sd / 1e9 / HBM_PEAK_GBS,
+            "tokens_per_s": wd.B / sd, "ms_per_step": rd["ms_per_step"], "ms_median": rd["ms_median"],
+            "bytes_per_step": decode_bytes(wd),
+        }
+        wl = workloads.WORKLOADS["longctx_bf16"]
+        sweep = {}
+        for c in wl.chunks:
+            try:
+                rl = time_forward(wl, c, max(3, extra_steps // 2), 2, ev, rotate_bytes=2.5e9)
+            except RuntimeError as e:
+                sweep[str(c)] = {"status": str(e)}
+                continue
+            ul = fwd_units(wl)
+            sl = rl["ms_per_step"] * 1e-3
+            sweep[str(c)] = {
+                "tokens_per_s": wl.B * wl.N / sl, "ms_per_step": rl["ms_per_step"], "kernel_ms": rl["kernel_ms"],
+                "algorithmic_GBps": fwd_bytes_per_unit(wl) * ul / sl / 1e9,
+                "hbm_frac": fwd_bytes_per_unit(wl) * ul / sl / 1e9 / HBM_PEAK_GBS,
+                "useful_TFLOPs": fwd_flops_per_unit(wl, c) * ul / sl / 1e12,
+                "mfma_bf16_frac": fwd_flops_per_unit(wl, c) * ul / sl / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            }
+        line["longctx_chunk_sweep"] = {"workload": "longctx_bf16: B=1 H=32 N=65536 D=Dv=128 bf16", **sweep}
+
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(w)
+        line["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+    ev.close()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

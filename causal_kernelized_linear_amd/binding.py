@@ -1,0 +1,209 @@
+"""ctypes binding of ``liblinattn.so`` (argument marshalling only).
+
+Every step of the computation runs in the library's HIP kernels; this module
+only turns torch tensors into device pointers, picks the current HIP stream,
+allocates the caller-side workspace and output tensors with torch, and raises
+``RuntimeError`` carrying the library's status string on any failure.  There is
+no fallback: if the library is missing, every call raises.
+
+Function names match the C ABI (include/linattn.h):
+    linattn_fwd_chunked, linattn_fwd_gated, linattn_decode_step,
+    linattn_fwd_workspace_size, linattn_status_string
+plus the tensor-level helpers fwd_chunked, fwd_gated and decode_step.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblinattn.so")
+
+F32, BF16 = 0, 1
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "hip"}
+
+_lock = threading.Lock()
+_lib = None
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+_sz = ctypes.c_size_t
+
+EXPORTS = {
+    "linattn_fwd_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "linattn_fwd_chunked": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p, _sz, _p]),
+    "linattn_fwd_gated": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p, _sz, _p]),
+    "linattn_decode_step": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p]),
+    "linattn_status_string": (ctypes.c_char_p, [_i]),
+    "linattn_set_profile_events": (_i, [_p, _p, _p, _p]),
+}
+
+
+def lib():
+    """Load the library once; raise if it was not built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                                   "`python -m causal_kernelized_linear_amd.build`")
+            h = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in EXPORTS.items():
+                fn = getattr(h, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = h
+        return _lib
+
+
+def linattn_status_string(code: int) -> str:
+    return lib().linattn_status_string(int(code)).decode()
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise RuntimeError(f"{what}: {linattn_status_string(code)} (status {code})")
+
+
+def linattn_fwd_workspace_size(B, H, N, D, Dv, chunk) -> int:
+    return int(lib().linattn_fwd_workspace_size(B, H, N, D, Dv, chunk))
+
+
+def linattn_fwd_chunked(q, k, v, o, s0, z0, s_out, z_out, B, H, N, D, Dv, chunk, dtype, eps, ws, ws_bytes,
+                        stream) -> int:
+    """Raw C call with integer pointers (0 = NULL); returns the status code."""
+    return int(lib().linattn_fwd_chunked(q, k, v, o, s0, z0, s_out, z_out, B, H, N, D, Dv, chunk, dtype, eps, ws,
+                                         ws_bytes, stream))
+
+
+def linattn_fwd_gated(q, k, v, g, o, s0, z0, s_out, z_out, B, H, N, D, Dv, chunk, dtype, eps, ws, ws_bytes,
+                      stream) -> int:
+    return int(lib().linattn_fwd_gated(q, k, v, g, o, s0, z0, s_out, z_out, B, H, N, D, Dv, chunk, dtype, eps, ws,
+                                       ws_bytes, stream))
+
+
+def linattn_decode_step(q, k, v, S, z, o, B, H, D, Dv, dtype, eps, stream) -> int:
+    return int(lib().linattn_decode_step(q, k, v, S, z, o, B, H, D, Dv, dtype, eps, stream))
+
+
+def linattn_set_profile_events(ev0, ev1, ev2, ev3) -> int:
+    """Arm the measurement hook with four raw hipEvent_t handles (ints; all 0 disarms)."""
+    return int(lib().linattn_set_profile_events(ev0, ev1, ev2, ev3))
+
+
+# ------------------------------------------------------------ tensor level ----
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    return 0 if t is None else t.data_ptr()
+
+
+def _need(t, name, dtype=None, device=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def workspace_bytes(B, H, N, D, Dv, chunk) -> int:
+    return linattn_fwd_workspace_size(B, H, N, D, Dv, chunk)
+
+
+def _fwd(q, k, v, g, chunk, eps, s0, z0, return_state, out, workspace):
+    dt = _dtype_code(q)
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _need(t, n, q.dtype, dev)
+    for t, n in ((g, "g"), (s0, "s0"), (z0, "z0")):
+        _need(t, n, torch.float32, dev)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, D]")
+    B, H, N, D = q.shape
+    Dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3]:
+        raise ValueError("k must match q, and v must be [B, H, N, Dv]")
+    if g is not None and tuple(g.shape) != (B, H, N):
+        raise ValueError("g must be [B, H, N]")
+    if s0 is not None and tuple(s0.shape) != (B, H, D, Dv):
+        raise ValueError("s0 must be [B, H, D, Dv]")
+    if z0 is not None and tuple(z0.shape) != (B, H, D):
+        raise ValueError("z0 must be [B, H, D]")
+    o = torch.empty(B, H, N, Dv, dtype=q.dtype, device=dev) if out is None else out
+    s_out = z_out = None
+    if return_state:
+        s_out = torch.empty(B, H, D, Dv, dtype=torch.float32, device=dev)
+        z_out = torch.empty(B, H, D, dtype=torch.float32, device=dev)
+    nbytes = linattn_fwd_workspace_size(B, H, N, D, Dv, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError("workspace too small")
+    wsb = workspace.numel() * workspace.element_size()
+    st = _stream(dev)
+    if g is None:
+        code = linattn_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(s0), _ptr(z0), _ptr(s_out),
+                                   _ptr(z_out), B, H, N, D, Dv, chunk, dt, eps, _ptr(workspace), wsb, st)
+        _check(code, "linattn_fwd_chunked")
+    else:
+        code = linattn_fwd_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(o), _ptr(s0), _ptr(z0), _ptr(s_out),
+                                 _ptr(z_out), B, H, N, D, Dv, chunk, dt, eps, _ptr(workspace), wsb, st)
+        _check(code, "linattn_fwd_gated")
+    if return_state:
+        return o, s_out, z_out
+    return o
+
+
+def fwd_chunked(q, k, v, chunk=128, eps=1e-6, s0=None, z0=None, return_state=False, out=None, workspace=None):
+    """Causal kernelized linear attention forward, chunked.  q, k [B,H,N,D]; v [B,H,N,Dv]
+    (bf16 or fp32, on the GPU).  Returns o (and S_N, z_N when return_state)."""
+    return _fwd(q, k, v, None, chunk, eps, s0, z0, return_state, out, workspace)
+
+
+def fwd_gated(q, k, v, g, chunk=128, eps=1e-6, s0=None, z0=None, return_state=False, out=None, workspace=None):
+    """Scalar-gated forward; g [B,H,N] float32 in (0, 1]."""
+    if g is None:
+        raise ValueError("fwd_gated needs g")
+    return _fwd(q, k, v, g, chunk, eps, s0, z0, return_state, out, workspace)
+
+
+def decode_step(q, k, v, S, z, eps=1e-6, out=None):
+    """One decode step: q, k [B,H,D], v [B,H,Dv]; S [B,H,D,Dv] and z [B,H,D] (float32)
+    are updated in place.  Returns o [B,H,Dv]."""
+    dt = _dtype_code(q)
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _need(t, n, q.dtype, dev)
+    _need(S, "S", torch.float32, dev)
+    _need(z, "z", torch.float32, dev)
+    if q.dim() != 3:
+        raise ValueError("q must be [B, H, D]")
+    B, H, D = q.shape
+    Dv = v.shape[-1]
+    if tuple(S.shape) != (B, H, D, Dv) or tuple(z.shape) != (B, H, D) or k.shape != q.shape:
+        raise ValueError("shape mismatch")
+    o = torch.empty(B, H, Dv, dtype=q.dtype, device=dev) if out is None else out
+    code = linattn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(z), _ptr(o), B, H, D, Dv, dt, eps,
+                               _stream(dev))
+    _check(code, "linattn_decode_step")
+    return o

@@ -1,0 +1,234 @@
+// C ABI of the library: argument checks, segment planning, workspace carving and
+// dispatch to the kernel instantiations.  The contract is documented in
+// include/linattn.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/linattn.h"
+#include "launch.hpp"
+
+namespace {
+
+using linattn::FwdLaunch;
+
+// Workgroups the walk should offer the GPU (several per compute unit).  The
+// sequence of each head is split into nseg segments of L chunks so that
+// BH * nseg reaches this count when the sequence is long enough.
+constexpr long kTargetWorkgroups = 1024;
+
+struct Plan {
+    int nseg = 0;
+    int L = 0;
+    size_t off_zt = 0, off_lg = 0, bytes = 0;
+};
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+Plan make_plan(long BH, int N, int D, int Dv, int chunk) {
+    Plan p;
+    const long nc = (long(N) + chunk - 1) / chunk;
+    long nseg = (kTargetWorkgroups + BH - 1) / BH;
+    if (nseg < 1) nseg = 1;
+    if (nseg > nc) nseg = nc;
+    const long L = (nc + nseg - 1) / nseg;
+    nseg = (nc + L - 1) / L;
+    p.nseg = int(nseg);
+    p.L = int(L);
+    const size_t heads = size_t(BH) * size_t(nseg);
+    const size_t st = round_up(heads * size_t(D) * size_t(Dv) * 4, 256);
+    const size_t zt = round_up(heads * size_t(D) * 4, 256);
+    const size_t lg = round_up(heads * 4, 256);
+    p.off_zt = st;
+    p.off_lg = st + zt;
+    p.bytes = st + zt + lg;
+    return p;
+}
+
+// Measurement hook (linattn_set_profile_events): one-shot, process-wide.
+std::mutex g_prof_mu;
+hipEvent_t g_prof[4] = {nullptr, nullptr, nullptr, nullptr};
+
+void take_profile_events(hipEvent_t out[4]) {
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    for (int i = 0; i < 4; ++i) {
+        out[i] = g_prof[i];
+        g_prof[i] = nullptr;
+    }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+bool dim_ok(int x) { return x == 64 || x == 128; }
+
+size_t esize(linattn_dtype_t dt) { return dt == LINATTN_BF16 ? 2 : 4; }
+
+bool dtype_ok(int dt) { return dt == LINATTN_F32 || dt == LINATTN_BF16; }
+
+// The device must be a gfx950.  Cached per device ordinal.
+linattn_status_t check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return LINATTN_ERR_HIP;
+    }
+    static std::mutex mu;
+    static signed char verdict[256];   // 0 unknown, 1 usable, -1 not usable
+    if (dev >= 256) return LINATTN_ERR_HIP;
+    std::lock_guard<std::mutex> lock(mu);
+    if (verdict[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return LINATTN_ERR_HIP;
+        }
+        verdict[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    }
+    return verdict[dev] == 1 ? LINATTN_OK : LINATTN_ERR_HIP;
+}
+
+linattn_status_t fwd_common(const void* q, const void* k, const void* v, const float* g, void* o, const float* s0,
+                            const float* z0, float* s_out, float* z_out, int B, int H, int N, int D, int Dv,
+                            int chunk, linattn_dtype_t dtype, float eps, void* ws, size_t ws_bytes, void* stream) {
+    if (B < 0 || H < 0 || N < 0 || D <= 0 || Dv <= 0 || chunk <= 0) return LINATTN_ERR_INVALID_ARGUMENT;
+    if (!dtype_ok(dtype) || !(eps > 0.0f) || !std::isfinite(eps)) return LINATTN_ERR_INVALID_ARGUMENT;
+    const long BH = long(B) * long(H);
+    if (BH == 0 || N == 0) return LINATTN_OK;
+    if (BH > (1L << 24) || long(N) * BH > (1L << 40)) return LINATTN_ERR_INVALID_ARGUMENT;
+    if (!q || !k || !v || !o) return LINATTN_ERR_INVALID_ARGUMENT;
+    for (const void* p : {q, k, v, static_cast<const void*>(o), static_cast<const void*>(g),
+                          static_cast<const void*>(s0), static_cast<const void*>(z0),
+                          static_cast<const void*>(s_out), static_cast<const void*>(z_out)})
+        if (p && !aligned16(p)) return LINATTN_ERR_INVALID_ARGUMENT;
+    const size_t es = esize(dtype);
+    const size_t nqk = size_t(BH) * N * D * es, nv = size_t(BH) * N * Dv * es;
+    if (overlap(o, nv, q, nqk) || overlap(o, nv, k, nqk) || overlap(o, nv, v, nv) ||
+        overlap(o, nv, g, size_t(BH) * N * 4))
+        return LINATTN_ERR_INVALID_ARGUMENT;
+    if (!dim_ok(D) || !dim_ok(Dv) || !linattn::chunk_is_built(chunk) ||
+        linattn::walk_lds_bytes(int(es), D, Dv, chunk) > linattn::kMaxLds)
+        return LINATTN_ERR_UNSUPPORTED;
+    const Plan plan = make_plan(BH, N, D, Dv, chunk);
+    if (ws_bytes < plan.bytes || !ws || !aligned16(ws)) return LINATTN_ERR_WORKSPACE;
+    const size_t ns = size_t(BH) * D * Dv * 4, nz = size_t(BH) * D * 4;
+    if (overlap(ws, plan.bytes, q, nqk) || overlap(ws, plan.bytes, k, nqk) || overlap(ws, plan.bytes, v, nv) ||
+        overlap(ws, plan.bytes, o, nv) || overlap(ws, plan.bytes, g, size_t(BH) * N * 4) ||
+        overlap(ws, plan.bytes, s0, ns) || overlap(ws, plan.bytes, s_out, ns) || overlap(ws, plan.bytes, z0, nz) ||
+        overlap(ws, plan.bytes, z_out, nz))
+        return LINATTN_ERR_WORKSPACE;
+    const linattn_status_t dst = check_device();
+    if (dst != LINATTN_OK) return dst;
+
+    FwdLaunch L;
+    L.prof[0] = L.prof[1] = L.prof[2] = L.prof[3] = nullptr;
+    L.q = q; L.k = k; L.v = v; L.g = g; L.o = o;
+    L.s0 = s0; L.z0 = z0; L.s_out = s_out; L.z_out = z_out;
+    char* w = static_cast<char*>(ws);
+    L.ws_st = reinterpret_cast<float*>(w);
+    L.ws_zt = reinterpret_cast<float*>(w + plan.off_zt);
+    L.ws_lg = reinterpret_cast<float*>(w + plan.off_lg);
+    L.BH = int(BH); L.N = N; L.D = D; L.Dv = Dv; L.chunk = chunk;
+    L.nseg = plan.nseg; L.L = plan.L; L.eps = eps;
+    L.stream = static_cast<hipStream_t>(stream);
+    take_profile_events(L.prof);
+    (void)hipGetLastError();   // start from a clean error state
+    const hipError_t e = dtype == LINATTN_BF16 ? linattn::launch_fwd_bf16(L) : linattn::launch_fwd_f32(L);
+    return e == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t linattn_fwd_workspace_size(int B, int H, int N, int D, int Dv, int chunk) {
+    if (B <= 0 || H <= 0 || N <= 0 || D <= 0 || Dv <= 0 || chunk <= 0) return 0;
+    return make_plan(long(B) * long(H), N, D, Dv, chunk).bytes;
+}
+
+linattn_status_t linattn_fwd_chunked(const void* q, const void* k, const void* v, void* o, const float* s0,
+                                     const float* z0, float* s_out, float* z_out, int B, int H, int N, int D, int Dv,
+                                     int chunk, linattn_dtype_t dtype, float eps, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+    try {
+        return fwd_common(q, k, v, nullptr, o, s0, z0, s_out, z_out, B, H, N, D, Dv, chunk, dtype, eps, workspace,
+                          workspace_bytes, stream);
+    } catch (...) {
+        return LINATTN_ERR_HIP;
+    }
+}
+
+linattn_status_t linattn_fwd_gated(const void* q, const void* k, const void* v, const float* g, void* o,
+                                   const float* s0, const float* z0, float* s_out, float* z_out, int B, int H, int N,
+                                   int D, int Dv, int chunk, linattn_dtype_t dtype, float eps, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    try {
+        if (!g && long(B) * long(H) * long(N) > 0) return LINATTN_ERR_INVALID_ARGUMENT;
+        return fwd_common(q, k, v, g, o, s0, z0, s_out, z_out, B, H, N, D, Dv, chunk, dtype, eps, workspace,
+                          workspace_bytes, stream);
+    } catch (...) {
+        return LINATTN_ERR_HIP;
+    }
+}
+
+linattn_status_t linattn_decode_step(const void* q, const void* k, const void* v, float* S, float* z, void* o, int B,
+                                     int H, int D, int Dv, linattn_dtype_t dtype, float eps, void* stream) {
+    try {
+        if (B < 0 || H < 0 || D <= 0 || Dv <= 0) return LINATTN_ERR_INVALID_ARGUMENT;
+        if (!dtype_ok(dtype) || !(eps > 0.0f) || !std::isfinite(eps)) return LINATTN_ERR_INVALID_ARGUMENT;
+        const long BH = long(B) * long(H);
+        if (BH == 0) return LINATTN_OK;
+        if (BH > (1L << 31) - 1) return LINATTN_ERR_INVALID_ARGUMENT;
+        if (!q || !k || !v || !S || !z || !o) return LINATTN_ERR_INVALID_ARGUMENT;
+        for (const void* p : {q, k, v, static_cast<const void*>(S), static_cast<const void*>(z),
+                              static_cast<const void*>(o)})
+            if (!aligned16(p)) return LINATTN_ERR_INVALID_ARGUMENT;
+        const size_t es = esize(dtype);
+        const size_t no = size_t(BH) * Dv * es;
+        if (overlap(o, no, q, size_t(BH) * D * es) || overlap(o, no, k, size_t(BH) * D * es) ||
+            overlap(o, no, v, no) || overlap(o, no, S, size_t(BH) * D * Dv * 4) || overlap(o, no, z, size_t(BH) * D * 4) ||
+            overlap(S, size_t(BH) * D * Dv * 4, z, size_t(BH) * D * 4))
+            return LINATTN_ERR_INVALID_ARGUMENT;
+        if (!dim_ok(D) || !dim_ok(Dv)) return LINATTN_ERR_UNSUPPORTED;
+        const linattn_status_t dst = check_device();
+        if (dst != LINATTN_OK) return dst;
+        (void)hipGetLastError();
+        const hipError_t e = linattn::launch_decode(int(dtype), q, k, v, S, z, o, int(BH), D, Dv, eps,
+                                                    static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP;
+    } catch (...) {
+        return LINATTN_ERR_HIP;
+    }
+}
+
+linattn_status_t linattn_set_profile_events(void* ev0, void* ev1, void* ev2, void* ev3) {
+    const int n = (ev0 != nullptr) + (ev1 != nullptr) + (ev2 != nullptr) + (ev3 != nullptr);
+    if (n != 0 && n != 4) return LINATTN_ERR_INVALID_ARGUMENT;
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    g_prof[0] = static_cast<hipEvent_t>(ev0);
+    g_prof[1] = static_cast<hipEvent_t>(ev1);
+    g_prof[2] = static_cast<hipEvent_t>(ev2);
+    g_prof[3] = static_cast<hipEvent_t>(ev3);
+    return LINATTN_OK;
+}
+
+const char* linattn_status_string(linattn_status_t status) {
+    switch (status) {
+        case LINATTN_OK: return "ok";
+        case LINATTN_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case LINATTN_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+        case LINATTN_ERR_WORKSPACE: return "workspace missing, too small, misaligned or overlapping";
+        case LINATTN_ERR_HIP: return "HIP error or no usable gfx950 device";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

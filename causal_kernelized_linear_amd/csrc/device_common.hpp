@@ -1,0 +1,87 @@
+// Device-side helpers shared by the gfx950 kernels: element traits, the
+// feature map, and the 16x16 MFMA step used by every chunk contraction.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace linattn {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;          // CDNA wavefront width
+constexpr int kThreads = 256;      // four waves per workgroup
+constexpr float kLog2e = 1.4426950408889634f;
+
+// phi(x) = elu(x) + 1: x + 1 above zero, exp(x) at or below it.  The exp branch
+// sees min(x, 0) so it cannot overflow when the other branch is taken.  exp(x) is
+// 2^(x * log2 e) on the hardware exp2 unit.
+__device__ __forceinline__ float phi(float x) {
+    const float e = __builtin_amdgcn_exp2f(fminf(x, 0.0f) * kLog2e);
+    return x > 0.0f ? x + 1.0f : e;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Element traits.  bf16 travels as its 16-bit pattern (uint16_t); widening is a
+// shift, narrowing is the hardware round-to-nearest-even conversion.
+template <typename E> struct Elem;
+
+template <> struct Elem<uint16_t> {
+    static __device__ __forceinline__ float to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+    static __device__ __forceinline__ uint16_t from_f32(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+};
+
+template <> struct Elem<float> {
+    static __device__ __forceinline__ float to_f32(float x) { return x; }
+    static __device__ __forceinline__ float from_f32(float f) { return f; }
+};
+
+// Eight consecutive elements: one MFMA operand fragment of one lane.
+template <typename E> struct alignas(16) F8 { E x[8]; };
+// Four consecutive elements (half a fragment, or one accumulator row quad).
+template <typename E> struct alignas(8) F4 { E x[4]; };
+
+// One 16x16 output tile step over 32 values of the contraction index:
+//   C[m][n] += sum_k A[m][k] B[k][n]
+// Lane l supplies row m = l % 16 of A and column n = l % 16 of B, each with the
+// eight contraction slots of lane group l / 16; A and B must fill the same slot
+// with the same contraction index.  The accumulator holds C[4*(l/16) + r][l % 16].
+// bf16 uses one v_mfma_f32_16x16x32_bf16; float uses eight v_mfma_f32_16x16x4_f32,
+// slot s of every lane feeding step s, so no value is ever rounded below fp32.
+__device__ __forceinline__ f32x4_t mma(const F8<uint16_t>& a, const F8<uint16_t>& b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t mma(const F8<float>& a, const F8<float>& b, f32x4_t c) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x[s], b.x[s], c, 0, 0, 0);
+    return c;
+}
+
+template <typename E>
+__device__ __forceinline__ F8<E> zero8() {
+    F8<E> r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r.x[i] = E(0);
+    return r;
+}
+
+template <typename E>
+__device__ __forceinline__ F8<E> lds_f8(const E* p) { return *reinterpret_cast<const F8<E>*>(p); }
+
+template <typename E>
+__device__ __forceinline__ F4<E> lds_f4(const E* p) { return *reinterpret_cast<const F4<E>*>(p); }
+
+template <typename E>
+__device__ __forceinline__ F8<E> join(const F4<E>& lo, const F4<E>& hi) {
+    F8<E> r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { r.x[i] = lo.x[i]; r.x[4 + i] = hi.x[i]; }
+    return r;
+}
+
+}  // namespace linattn

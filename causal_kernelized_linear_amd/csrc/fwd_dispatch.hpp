@@ -1,0 +1,69 @@
+// Template dispatch of the chunked forward over (D, Dv, chunk, gated) for one
+// element type; included once per element type so the instantiations compile in
+// parallel translation units.
+#pragma once
+
+#include "chunk_walk.hpp"
+#include "launch.hpp"
+
+namespace linattn {
+
+template <typename E, int D, int DV, int CH, bool GATED>
+hipError_t run_fwd(const FwdLaunch& p) {
+    using Sh = WalkShape<E, D, DV, CH>;
+    if constexpr (Sh::bytes(true) > kMaxLds) {
+        return hipErrorInvalidValue;           // rejected earlier by the ABI's support check
+    } else {
+        WalkArgs a;
+        a.q = p.q; a.k = p.k; a.v = p.v; a.g = p.g; a.o = p.o;
+        a.st = p.ws_st; a.zt = p.ws_zt; a.lg = p.ws_lg;
+        a.N = p.N; a.nseg = p.nseg; a.L = p.L; a.eps = p.eps;
+        auto* k_tot = walk_kernel<E, D, DV, CH, GATED, false>;
+        auto* k_out = walk_kernel<E, D, DV, CH, GATED, true>;
+        static bool attrs_set = false;         // benign race: idempotent attribute set
+        if (!attrs_set) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_tot),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, int(Sh::bytes(false)));
+            if (e != hipSuccess) return e;
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_out), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    int(Sh::bytes(true)));
+            if (e != hipSuccess) return e;
+            attrs_set = true;
+        }
+        const unsigned nwg = unsigned(p.BH) * unsigned(p.nseg);
+        auto mark = [&](int i) { if (p.prof[i]) (void)hipEventRecord(p.prof[i], p.stream); };
+        mark(0);
+        hipLaunchKernelGGL(k_tot, dim3(nwg), dim3(kThreads), Sh::bytes(false), p.stream, a);
+        mark(1);
+        constexpr int NBLK = (D * DV + D + kThreads - 1) / kThreads;
+        hipLaunchKernelGGL((scan_kernel<D, DV, GATED>), dim3(unsigned(p.BH) * NBLK), dim3(kThreads), 0, p.stream,
+                           p.ws_st, p.ws_zt, p.ws_lg, p.s0, p.z0, p.s_out, p.z_out, p.nseg);
+        mark(2);
+        hipLaunchKernelGGL(k_out, dim3(nwg), dim3(kThreads), Sh::bytes(true), p.stream, a);
+        mark(3);
+        return hipGetLastError();
+    }
+}
+
+template <typename E, int D, int DV>
+hipError_t run_fwd_chunk(const FwdLaunch& p) {
+    const bool gated = p.g != nullptr;
+    switch (p.chunk) {
+        case 32:  return gated ? run_fwd<E, D, DV, 32, true>(p) : run_fwd<E, D, DV, 32, false>(p);
+        case 64:  return gated ? run_fwd<E, D, DV, 64, true>(p) : run_fwd<E, D, DV, 64, false>(p);
+        case 128: return gated ? run_fwd<E, D, DV, 128, true>(p) : run_fwd<E, D, DV, 128, false>(p);
+        case 256: return gated ? run_fwd<E, D, DV, 256, true>(p) : run_fwd<E, D, DV, 256, false>(p);
+        default:  return hipErrorInvalidValue;
+    }
+}
+
+template <typename E>
+hipError_t run_fwd_typed(const FwdLaunch& p) {
+    if (p.D == 64 && p.Dv == 64) return run_fwd_chunk<E, 64, 64>(p);
+    if (p.D == 64 && p.Dv == 128) return run_fwd_chunk<E, 64, 128>(p);
+    if (p.D == 128 && p.Dv == 64) return run_fwd_chunk<E, 128, 64>(p);
+    if (p.D == 128 && p.Dv == 128) return run_fwd_chunk<E, 128, 128>(p);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace linattn

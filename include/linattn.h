@@ -1,0 +1,145 @@
+/*
+ * linattn.h - C ABI of the MI355X (gfx950) causal kernelized linear attention library.
+ *
+ * The operation (learn.pranaymahendrakar.com page, Researcher level, "Derivation";
+ * aicassindra.com page, "The quadratic wall, and the kernel that removes it"):
+ *
+ *     phi(x) = elu(x) + 1                     (alpha = 1, applied to q and k, never to v)
+ *     S_i = S_{i-1} + phi(k_i) v_i^T,  z_i = z_{i-1} + phi(k_i)
+ *     o_i = phi(q_i)^T S_i / max(phi(q_i)^T z_i, eps)
+ *
+ * computed in the chunked parallel form (aiwiki.thehackersbrain.dev page, the
+ * chunked listing and its closing paragraph): a causally masked quadratic product
+ * inside each chunk of `chunk` tokens, and the state (S, z) carried across chunks.
+ * There is no 1/sqrt(D) scaling.  The denominator is clamped to eps, as the chunked
+ * listing on that page does.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer is DEVICE memory owned by the caller.  The library never
+ *    allocates or frees device memory and keeps no pointer after it returns.
+ *  - Tensors are contiguous and row-major.  Base pointers must be 16-byte aligned.
+ *  - q, k, v, o hold `dtype` elements (LINATTN_F32: float, LINATTN_BF16: bfloat16
+ *    bit patterns).  States (S, z, s0, z0, s_out, z_out) and gates are always float.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null stream).
+ *    Results are valid once the stream has synchronised.
+ *  - Arguments are checked before anything is launched: a return other than
+ *    LINATTN_OK guarantees that no device memory was written.
+ *  - B*H*N == 0 (or B*H == 0 for decode) is LINATTN_OK and does nothing.
+ *  - NaN or Inf in the inputs propagate to the outputs; they are not trapped.
+ *  - Results are bitwise reproducible for identical inputs and shapes (no float atomics).
+ *  - Nothing aborts and no C++ exception crosses this interface.
+ *
+ * Supported shapes on the GPU: D and Dv in {64, 128}; chunk in {32, 64, 128, 256}
+ * when the chunk's on-chip tiles fit the 160 KiB LDS of a compute unit:
+ *   bf16: every chunk, except 256 when D = 128;
+ *   f32:  chunk <= 128 at D = Dv = 64, <= 64 when one of D, Dv is 128, 32 when both are.
+ * Other shapes return LINATTN_ERR_UNSUPPORTED.
+ */
+#ifndef LINATTN_H
+#define LINATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LINATTN_OK = 0,
+    LINATTN_ERR_INVALID_ARGUMENT = 1,  /* null pointer, negative size, eps <= 0, misalignment */
+    LINATTN_ERR_UNSUPPORTED = 2,       /* valid but not built: D/Dv/chunk/dtype combination */
+    LINATTN_ERR_WORKSPACE = 3,         /* workspace missing or smaller than linattn_fwd_workspace_size */
+    LINATTN_ERR_HIP = 4                /* no usable device, or a launch failed */
+} linattn_status_t;
+
+typedef enum {
+    LINATTN_F32 = 0,
+    LINATTN_BF16 = 1
+} linattn_dtype_t;
+
+/*
+ * Bytes of device scratch the chunked and gated forwards need for these sizes
+ * (per-segment state totals and prefixes, float).  0 when B*H*N == 0 or a size is
+ * not positive.  The same value serves both forwards.  Its contents are undefined
+ * after a call; it must not be shared by calls that may run concurrently.
+ */
+size_t linattn_fwd_workspace_size(int B, int H, int N, int D, int Dv, int chunk);
+
+/*
+ * Chunked forward of causal kernelized linear attention.
+ *
+ *  q, k   [B,H,N,D]   dtype         input, read-only
+ *  v      [B,H,N,Dv]  dtype         input, read-only
+ *  o      [B,H,N,Dv]  dtype         output; must not alias any input
+ *  s0     [B,H,D,Dv]  float or NULL initial state S (NULL: zeros)
+ *  z0     [B,H,D]     float or NULL initial normaliser z (NULL: zeros)
+ *  s_out  [B,H,D,Dv]  float or NULL final state S_N (NULL: not written); may equal s0
+ *  z_out  [B,H,D]     float or NULL final normaliser z_N (NULL: not written); may equal z0
+ *  chunk               tokens per chunk (the last chunk of a sequence may be shorter)
+ *  eps > 0             denominator clamp: o = num / max(den, eps)
+ *  workspace           device scratch of at least linattn_fwd_workspace_size(...) bytes,
+ *                      16-byte aligned (NULL allowed only when that size is 0)
+ *
+ * Resuming: fwd(N1) then fwd(N2) with s0/z0 = the first call's s_out/z_out equals
+ * fwd(N1 + N2) up to rounding (aiwiki.thehackersbrain.dev page, "It is a linear RNN":
+ * the state is a fixed-size summary of everything seen).
+ */
+linattn_status_t linattn_fwd_chunked(
+    const void* q, const void* k, const void* v, void* o,
+    const float* s0, const float* z0, float* s_out, float* z_out,
+    int B, int H, int N, int D, int Dv, int chunk, linattn_dtype_t dtype, float eps,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Scalar-gated chunked forward: S_t = g_t S_{t-1} + phi(k_t) v_t^T and
+ * z_t = g_t z_{t-1} + phi(k_t), o_t = phi(q_t)^T S_t / max(phi(q_t)^T z_t, eps)
+ * (the decay term of the aiwiki.thehackersbrain.dev page, "What is actually lost",
+ * with a scalar gate per head and token; the aicassindra.com page, "RetNet and gated
+ * linear attention").
+ *
+ *  g [B,H,N] float, device, read-only.  Precondition (not checked on the device):
+ *  0 < g <= 1.  Every other argument is as for linattn_fwd_chunked.
+ */
+linattn_status_t linattn_fwd_gated(
+    const void* q, const void* k, const void* v, const float* g, void* o,
+    const float* s0, const float* z0, float* s_out, float* z_out,
+    int B, int H, int N, int D, int Dv, int chunk, linattn_dtype_t dtype, float eps,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One recurrent decode step for B*H independent heads (aiwiki.thehackersbrain.dev page,
+ * "It is a linear RNN": O(D*Dv) work per token, no cache that grows):
+ *
+ *     S <- S + phi(k) v^T,  z <- z + phi(k),  o = phi(q)^T S / max(phi(q)^T z, eps)
+ *
+ * The token is added before it is read (mlblogg.com page, "The causal recurrence").
+ *
+ *  q, k  [B,H,D]     dtype   read-only
+ *  v     [B,H,Dv]    dtype   read-only
+ *  S     [B,H,D,Dv]  float   updated in place
+ *  z     [B,H,D]     float   updated in place
+ *  o     [B,H,Dv]    dtype   output; must not alias any other argument
+ */
+linattn_status_t linattn_decode_step(
+    const void* q, const void* k, const void* v, float* S, float* z, void* o,
+    int B, int H, int D, int Dv, linattn_dtype_t dtype, float eps, void* stream);
+
+/*
+ * Measurement hook, not part of the computation.  Arms the NEXT linattn_fwd_chunked or
+ * linattn_fwd_gated call on this process to record four caller-created hipEvent_t
+ * handles on its stream: ev0 before its first launch, ev1 after the segment-totals
+ * walk, ev2 after the segment scan, ev3 after the output walk.  The first forward whose
+ * arguments pass validation consumes (and disarms) the hook; four NULLs disarm it.
+ * Returns LINATTN_ERR_INVALID_ARGUMENT when only some handles are NULL.
+ */
+linattn_status_t linattn_set_profile_events(void* ev0, void* ev1, void* ev2, void* ev3);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* linattn_status_string(linattn_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINATTN_H */

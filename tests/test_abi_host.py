@@ -1,0 +1,125 @@
+"""Host-side checks of the C ABI (no kernel is launched; runs without a GPU).
+
+The library must load, export every entry point declared in include/linattn.h,
+and reject bad arguments with the documented status codes before touching any
+device memory.  The pointer values used here are fake but aligned and disjoint,
+and every call is built to fail validation before any launch; the one call that
+passes validation (to reach the device check) runs only where no GPU exists.
+"""
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+from causal_kernelized_linear_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "linattn.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIP = 0, 1, 2, 3, 4
+
+# fake, 16-byte aligned, disjoint device addresses (never dereferenced)
+Q, K, V, O, G, S0, Z0, SO, ZO, WS = (0x10_0000_0000 * (i + 1) for i in range(10))
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(linattn_[a-z_0-9]+)\s*\(", text)) - {"linattn_status_t", "linattn_dtype_t"})
+
+
+def test_library_exports_every_declared_symbol():
+    syms = declared_symbols()
+    assert set(syms) == set(binding.EXPORTS), syms
+    lib = binding.lib()
+    for s in syms:
+        assert getattr(lib, s) is not None
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True).stdout
+    for s in syms:
+        assert re.search(rf"\bT {s}\b", out), s
+
+
+def test_status_strings():
+    for code in range(5):
+        assert isinstance(binding.linattn_status_string(code), str)
+    assert binding.linattn_status_string(0) == "ok"
+    assert binding.linattn_status_string(99) == "unknown status"
+
+
+def test_workspace_size():
+    ws = binding.linattn_fwd_workspace_size
+    assert ws(0, 1, 128, 64, 64, 128) == 0
+    assert ws(1, 1, 0, 64, 64, 128) == 0
+    assert ws(1, 1, 128, 64, 64, -1) == 0
+    a = ws(8, 16, 4096, 64, 64, 128)
+    assert a > 0 and a % 256 == 0
+    # at least one fp32 state per head, at most one per chunk per head
+    assert 8 * 16 * 64 * 64 * 4 <= a <= 8 * 16 * 32 * (64 * 64 + 64 + 1) * 4 + 3 * 256
+
+
+def fwd(q=Q, k=K, v=V, o=O, s0=0, z0=0, so=0, zo=0, B=1, H=2, N=256, D=64, Dv=64, chunk=128, dt=1, eps=1e-6,
+        ws=WS, wsb=1 << 30, gated=False, g=G):
+    if gated:
+        return binding.linattn_fwd_gated(q, k, v, g, o, s0, z0, so, zo, B, H, N, D, Dv, chunk, dt, eps, ws, wsb, 0)
+    return binding.linattn_fwd_chunked(q, k, v, o, s0, z0, so, zo, B, H, N, D, Dv, chunk, dt, eps, ws, wsb, 0)
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_fwd_rejects_bad_arguments(gated):
+    assert fwd(B=-1, gated=gated) == INVALID
+    assert fwd(D=0, gated=gated) == INVALID
+    assert fwd(chunk=0, gated=gated) == INVALID
+    assert fwd(eps=0.0, gated=gated) == INVALID
+    assert fwd(eps=-1e-6, gated=gated) == INVALID
+    assert fwd(eps=float("nan"), gated=gated) == INVALID
+    assert fwd(dt=7, gated=gated) == INVALID
+    assert fwd(q=0, gated=gated) == INVALID
+    assert fwd(o=0, gated=gated) == INVALID
+    assert fwd(v=V + 8, gated=gated) == INVALID                 # misaligned
+    assert fwd(o=Q + 64, gated=gated) == INVALID                # o overlaps q
+    assert fwd(D=96, gated=gated) == UNSUPPORTED
+    assert fwd(Dv=32, gated=gated) == UNSUPPORTED
+    assert fwd(chunk=100, gated=gated) == UNSUPPORTED
+    assert fwd(chunk=16, gated=gated) == UNSUPPORTED
+    assert fwd(chunk=512, gated=gated) == UNSUPPORTED
+    assert fwd(D=128, Dv=128, chunk=256, gated=gated) == UNSUPPORTED     # tiles exceed 160 KiB of LDS
+    assert fwd(dt=0, D=128, Dv=128, chunk=128, gated=gated) == UNSUPPORTED
+    assert fwd(ws=0, gated=gated) == WORKSPACE
+    assert fwd(wsb=16, gated=gated) == WORKSPACE
+    assert fwd(ws=WS + 4, gated=gated) == WORKSPACE
+    assert fwd(ws=Q, gated=gated) == WORKSPACE                  # workspace overlaps q
+    # empty problems succeed without touching anything
+    assert fwd(B=0, q=0, k=0, v=0, o=0, ws=0, wsb=0, gated=gated) == OK
+    assert fwd(N=0, q=0, k=0, v=0, o=0, ws=0, wsb=0, gated=gated) == OK
+
+
+def test_profile_hook_arguments():
+    assert binding.linattn_set_profile_events(0, 0, 0, 0) == OK
+    assert binding.linattn_set_profile_events(16, 0, 0, 0) == INVALID
+
+
+def test_gated_requires_gate():
+    assert fwd(gated=True, g=0) == INVALID
+
+
+def decode(q=Q, k=K, v=V, S=S0, z=Z0, o=O, B=4, H=2, D=128, Dv=128, dt=1, eps=1e-6):
+    return binding.linattn_decode_step(q, k, v, S, z, o, B, H, D, Dv, dt, eps, 0)
+
+
+def test_decode_rejects_bad_arguments():
+    assert decode(B=-1) == INVALID
+    assert decode(S=0) == INVALID
+    assert decode(eps=0.0) == INVALID
+    assert decode(dt=3) == INVALID
+    assert decode(z=Z0 + 4) == INVALID
+    assert decode(o=S0) == INVALID                              # o overlaps S
+    assert decode(z=S0 + 16) == INVALID                         # z overlaps S
+    assert decode(D=96) == UNSUPPORTED
+    assert decode(B=0, q=0) == OK
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="only meaningful where no GPU is present")
+def test_no_device_is_reported_not_crashed():
+    assert fwd() == HIP
+    assert decode() == HIP

@@ -1,0 +1,252 @@
+"""GPU parity: the HIP path (through the C ABI binding) against the fp64 oracle.
+
+Every expected value comes from ``oracle/`` on the same seeded inputs.  Small
+cases compare every output; the full-size workloads compare sampled heads
+(each head is independent) at the same launch configuration the benchmark uses.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from causal_kernelized_linear_amd import binding, workloads
+from parity import TOL, matrix_rel_err, rowwise_rel_err, to64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def run_fwd(inp, chunk, eps=1e-6, s0=None, z0=None, return_state=False):
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    g = inp.get("g")
+    g = None if g is None else g.to(DEV)
+    s0 = None if s0 is None else s0.to(DEV)
+    z0 = None if z0 is None else z0.to(DEV)
+    if g is None:
+        r = binding.fwd_chunked(q, k, v, chunk=chunk, eps=eps, s0=s0, z0=z0, return_state=return_state)
+    else:
+        r = binding.fwd_gated(q, k, v, g, chunk=chunk, eps=eps, s0=s0, z0=z0, return_state=return_state)
+    torch.cuda.synchronize()
+    return r
+
+
+def oracle_fwd(inp, heads=None, eps=1e-6, s0=None, z0=None):
+    """Oracle on all heads, or on a list of (b, h) pairs."""
+    def pick(t):
+        if t is None:
+            return None
+        a = to64(t)
+        if heads is None:
+            return a
+        return np.stack([a[b, h] for b, h in heads])[None]
+    return oracle.causal_linear_attention(pick(inp["q"]), pick(inp["k"]), pick(inp["v"]), g=pick(inp.get("g")),
+                                          s0=pick(s0), z0=pick(z0), eps=eps)
+
+
+def sel(t, heads):
+    a = to64(t)
+    return np.stack([a[b, h] for b, h in heads])[None]
+
+
+# ------------------------------------------------------------- small cases ----
+
+SMALL = [
+    # (B, H, N, D, Dv, dtype, chunk)
+    (1, 2, 512, 64, 64, "f32", 64),
+    (1, 2, 300, 64, 64, "f32", 32),
+    (2, 1, 200, 128, 128, "f32", 32),
+    (1, 1, 97, 64, 128, "f32", 64),
+    (2, 2, 640, 64, 64, "bf16", 128),
+    (1, 3, 1000, 64, 64, "bf16", 64),
+    (1, 2, 777, 128, 128, "bf16", 128),
+    (1, 2, 333, 128, 64, "bf16", 64),
+    (2, 1, 515, 64, 128, "bf16", 256),
+    (1, 1, 1, 64, 64, "bf16", 128),
+    (1, 1, 17, 128, 128, "bf16", 32),
+    (3, 1, 2049, 64, 64, "bf16", 256),
+]
+
+
+@pytest.mark.parametrize("gated", [False, True], ids=["ungated", "gated"])
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "B{}H{}N{}D{}Dv{}{}c{}".format(*c))
+def test_small_against_oracle(case, gated):
+    B, H, N, D, Dv, dt, chunk = case
+    _say(f"small case {case} gated={gated}")
+    inp = workloads.random_inputs(11 + N + D, B, H, N, D, Dv, dtype=dt, gated=gated, g_low=0.8)
+    o, S, z = run_fwd(inp, chunk, return_state=True)
+    o_ref, S_ref, z_ref = oracle_fwd(inp)
+    tol = TOL[dt]
+    assert rowwise_rel_err(to64(o), o_ref) <= tol
+    assert matrix_rel_err(to64(S), S_ref) <= tol
+    assert matrix_rel_err(to64(z), z_ref) <= tol
+
+
+@pytest.mark.parametrize("gated", [False, True], ids=["ungated", "gated"])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_initial_state_and_resume(dt, gated):
+    B, H, N, D, Dv = 1, 2, 384, 64, 64
+    chunk = 64
+    inp = workloads.random_inputs(5, B, H, N, D, Dv, dtype=dt, gated=gated, g_low=0.85, with_state=True,
+                                  state_scale=20.0)
+    _say(f"resume dt={dt} gated={gated}")
+    o, S, z = run_fwd(inp, chunk, s0=inp["s0"], z0=inp["z0"], return_state=True)
+    o_ref, S_ref, z_ref = oracle_fwd(inp, s0=inp["s0"], z0=inp["z0"])
+    tol = TOL[dt]
+    assert rowwise_rel_err(to64(o), o_ref) <= tol
+    assert matrix_rel_err(to64(S), S_ref) <= tol
+    assert matrix_rel_err(to64(z), z_ref) <= tol
+    # split at a point that is not a chunk boundary and resume from the returned state
+    n1 = 150
+    first = {kk: t[:, :, :n1] for kk, t in inp.items() if kk in ("q", "k", "v", "g")}
+    second = {kk: t[:, :, n1:] for kk, t in inp.items() if kk in ("q", "k", "v", "g")}
+    o1, S1, z1 = run_fwd(first, chunk, s0=inp["s0"], z0=inp["z0"], return_state=True)
+    o2, S2, z2 = run_fwd(second, chunk, s0=S1, z0=z1, return_state=True)
+    assert rowwise_rel_err(np.concatenate([to64(o1), to64(o2)], axis=2), o_ref) <= tol
+    assert matrix_rel_err(to64(S2), S_ref) <= tol
+
+
+def test_eps_clamp_on_gpu():
+    # every query is very negative, so phi(q) ~ e^-16 and the denominator falls below eps
+    B, H, N, D, Dv = 1, 1, 64, 64, 64
+    inp = workloads.random_inputs(9, B, H, N, D, Dv, dtype="f32")
+    inp["q"] = torch.full_like(inp["q"], -16.0)
+    o = run_fwd(inp, 32)
+    o_ref, _, _ = oracle_fwd(inp)
+    # den = 64 * e^-16 * z: below eps for the first tokens, above it later
+    assert rowwise_rel_err(to64(o), o_ref) <= TOL["f32"]
+
+
+def test_first_output_is_v0_on_gpu():
+    inp = workloads.random_inputs(21, 2, 2, 128, 64, 64, dtype="f32", scale=2.0)
+    o = run_fwd(inp, 64)
+    np.testing.assert_allclose(to64(o)[:, :, 0], to64(inp["v"])[:, :, 0], rtol=1e-5, atol=1e-6)
+
+
+def test_deterministic_and_guard_bands():
+    B, H, N, D, Dv = 2, 2, 1000, 64, 64
+    inp = workloads.random_inputs(33, B, H, N, D, Dv, dtype="bf16", gated=True)
+    q, k, v, g = (inp[n].to(DEV) for n in ("q", "k", "v", "g"))
+    n_o = B * H * N * Dv
+    buf = torch.full((n_o + 4096,), 1.2345, dtype=torch.bfloat16, device=DEV)
+    out = buf[:n_o].view(B, H, N, Dv)
+    binding.fwd_gated(q, k, v, g, chunk=128, out=out)
+    torch.cuda.synchronize()
+    first = out.clone()
+    assert torch.all(buf[n_o:] == torch.tensor(1.2345, dtype=torch.bfloat16)).item()
+    binding.fwd_gated(q, k, v, g, chunk=128, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(first, out)
+
+
+def test_unsupported_raises():
+    inp = workloads.random_inputs(1, 1, 1, 64, 96, 64, dtype="bf16")
+    with pytest.raises(RuntimeError, match="unsupported"):
+        run_fwd(inp, 128)
+
+
+# ------------------------------------------------------------------ decode ----
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("dims", [(64, 64), (128, 128), (64, 128), (128, 64)])
+def test_decode_small(dt, dims):
+    D, Dv = dims
+    B, H = 3, 5
+    gen = torch.Generator().manual_seed(D + Dv)
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    q = torch.randn(B, H, D, generator=gen).to(tdt)
+    k = torch.randn(B, H, D, generator=gen).to(tdt)
+    v = torch.randn(B, H, Dv, generator=gen).to(tdt)
+    S = torch.randn(B, H, D, Dv, generator=gen) * 30
+    z = torch.randn(B, H, D, generator=gen).abs() * 30
+    o_ref, S_ref, z_ref = oracle.decode_step(to64(q), to64(k), to64(v), to64(S), to64(z))
+    Sd, zd = S.to(DEV), z.to(DEV)
+    o = binding.decode_step(q.to(DEV), k.to(DEV), v.to(DEV), Sd, zd)
+    torch.cuda.synchronize()
+    assert rowwise_rel_err(to64(o), o_ref) <= TOL[dt]
+    # the state update is one fp32 fma per element: compare tightly
+    assert matrix_rel_err(to64(Sd), S_ref) <= 1e-6
+    assert matrix_rel_err(to64(zd), z_ref) <= 1e-6
+
+
+def test_prefill_then_decode_handoff():
+    B, H, N, D, Dv = 1, 2, 257, 128, 128
+    inp = workloads.random_inputs(77, B, H, N + 1, D, Dv, dtype="bf16")
+    pre = {n: t[:, :, :N] for n, t in inp.items()}
+    _, S, z = run_fwd(pre, 128, return_state=True)
+    o = binding.decode_step(inp["q"][:, :, N].contiguous().to(DEV), inp["k"][:, :, N].contiguous().to(DEV),
+                            inp["v"][:, :, N].contiguous().to(DEV), S, z)
+    torch.cuda.synchronize()
+    o_ref, _, _ = oracle_fwd(inp)
+    assert rowwise_rel_err(to64(o), o_ref[:, :, N]) <= TOL["bf16"]
+
+
+# ---------------------------------------------------- full-size workloads ----
+
+def _heads(B, H, n, seed):
+    rng = np.random.default_rng(seed)
+    idx = rng.choice(B * H, size=min(n, B * H), replace=False)
+    return [(int(i) // H, int(i) % H) for i in sorted(idx)]
+
+
+def test_workload_fp32_small_full():
+    w = workloads.WORKLOADS["fp32_small"]
+    inp = workloads.make_inputs(w)
+    _say("fp32_small full")
+    o, S, z = run_fwd(inp, w.chunks[0], return_state=True)
+    o_ref, S_ref, z_ref = oracle_fwd(inp)
+    assert rowwise_rel_err(to64(o), o_ref) <= TOL["f32"]
+    assert matrix_rel_err(to64(S), S_ref) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("name", ["train_bf16", "gated_bf16"])
+def test_workload_sampled_heads(name):
+    w = workloads.WORKLOADS[name]
+    inp = workloads.make_inputs(w)
+    heads = _heads(w.B, w.H, 6, 5)
+    _say(f"{name} full size, oracle on heads {heads}")
+    o, S, z = run_fwd(inp, w.chunks[0], return_state=True)
+    o_ref, S_ref, z_ref = oracle_fwd(inp, heads=heads)
+    assert rowwise_rel_err(sel(o, heads), o_ref) <= TOL["bf16"]
+    assert matrix_rel_err(sel(S, heads), S_ref) <= TOL["bf16"]
+    assert matrix_rel_err(sel(z, heads), z_ref) <= TOL["bf16"]
+    assert torch.isfinite(o).all().item()
+
+
+def test_workload_longctx_sampled_heads():
+    w = workloads.WORKLOADS["longctx_bf16"]
+    inp = workloads.make_inputs(w)
+    heads = _heads(w.B, w.H, 2, 6)
+    _say(f"longctx full size, oracle on heads {heads}")
+    o_ref, S_ref, _ = oracle_fwd(inp, heads=heads)
+    for chunk in w.chunks:
+        _say(f"  chunk {chunk}")
+        try:
+            o, S, z = run_fwd(inp, chunk, return_state=True)
+        except RuntimeError as e:
+            assert chunk == 256 and "unsupported" in str(e)
+            continue
+        assert rowwise_rel_err(sel(o, heads), o_ref) <= TOL["bf16"]
+        assert matrix_rel_err(sel(S, heads), S_ref) <= TOL["bf16"]
+        del o, S, z
+
+
+def test_workload_decode_sampled_heads():
+    w = workloads.WORKLOADS["decode_bf16"]
+    inp = workloads.make_inputs(w)
+    heads = _heads(w.B, w.H, 64, 7)
+    _say("decode full size")
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    S, z = inp["S"].to(DEV), inp["z"].to(DEV)
+    o = binding.decode_step(q, k, v, S, z)
+    torch.cuda.synchronize()
+    o_ref, S_ref, z_ref = oracle.decode_step(sel(inp["q"], heads)[0], sel(inp["k"], heads)[0],
+                                             sel(inp["v"], heads)[0], sel(inp["S"], heads)[0],
+                                             sel(inp["z"], heads)[0])
+    assert rowwise_rel_err(sel(o, heads)[0], o_ref) <= TOL["bf16"]
+    assert matrix_rel_err(sel(S, heads), S_ref[None]) <= 1e-6
+    assert matrix_rel_err(sel(z, heads), z_ref[None]) <= 1e-6
