@@ -193,7 +193,7 @@ def cpu_baseline(w, seconds_hint=10.0):
     from causal_kernelized_linear_amd import workloads
     import oracle
 
-    ntok = 2048
+    ntok = w.N
     inp = workloads.make_inputs(w, N=ntok)
     q, k, v = (workloads.to_f64(inp[n]) for n in ("q", "k", "v"))
     t = time.perf_counter()
@@ -205,7 +205,7 @@ def cpu_baseline(w, seconds_hint=10.0):
         "unit": "tokens/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"fp64 NumPy recurrence over all {w.B}x{w.H} heads, first {ntok} of {w.N} tokens, "
+        "sample": f"fp64 NumPy recurrence over the whole workload ({w.B}x{w.H} heads, {ntok} tokens), "
                   f"{dt:.1f} s, one thread (elementwise NumPy and einsum), "
                   f"host has {os.cpu_count()} cpus, affinity {len(os.sched_getaffinity(0))}",
         "seconds": dt,
@@ -220,6 +220,8 @@ def main():
     ap.add_argument("--chunk", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="time only the headline workload")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (calibrates rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -234,6 +236,14 @@ def main():
         sys.exit(2)
     binding.lib()
     ev = HipEvents()
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
 
     w = workloads.WORKLOADS["train_bf16"]
     chunk = args.chunk
