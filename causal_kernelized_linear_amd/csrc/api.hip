@@ -3,6 +3,7 @@
 // include/linattn.h.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -23,10 +24,8 @@ constexpr long kTargetWorkgroups = 1024;
 struct Plan {
     int nseg = 0;
     int L = 0;
-    size_t off_zt = 0, off_lg = 0, bytes = 0;
+    size_t bytes = 0;
 };
-
-size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 Plan make_plan(long BH, int N, int D, int Dv, int chunk) {
     Plan p;
@@ -38,15 +37,12 @@ Plan make_plan(long BH, int N, int D, int Dv, int chunk) {
     nseg = (nc + L - 1) / L;
     p.nseg = int(nseg);
     p.L = int(L);
-    const size_t heads = size_t(BH) * size_t(nseg);
-    const size_t st = round_up(heads * size_t(D) * size_t(Dv) * 4, 256);
-    const size_t zt = round_up(heads * size_t(D) * 4, 256);
-    const size_t lg = round_up(heads * 4, 256);
-    p.off_zt = st;
-    p.off_lg = st + zt;
-    p.bytes = st + zt + lg;
+    p.bytes = linattn::fwd_workspace_bytes(size_t(BH) * size_t(nseg), D, Dv);
     return p;
 }
+
+// Forward algorithm (linattn_set_forward_algorithm): 0 picks the three-launch path.
+std::atomic<int> g_algo{0};
 
 // Measurement hook (linattn_set_profile_events): one-shot, process-wide.
 std::mutex g_prof_mu;
@@ -115,7 +111,7 @@ linattn_status_t fwd_common(const void* q, const void* k, const void* v, const f
         overlap(o, nv, g, size_t(BH) * N * 4))
         return LINATTN_ERR_INVALID_ARGUMENT;
     if (!dim_ok(D) || !dim_ok(Dv) || !linattn::chunk_is_built(chunk) ||
-        linattn::walk_lds_bytes(int(es), D, Dv, chunk) > linattn::kMaxLds)
+        linattn::walk_lds_bytes(int(es), D, Dv, chunk) + 16 > linattn::kMaxLds)
         return LINATTN_ERR_UNSUPPORTED;
     const Plan plan = make_plan(BH, N, D, Dv, chunk);
     if (ws_bytes < plan.bytes || !ws || !aligned16(ws)) return LINATTN_ERR_WORKSPACE;
@@ -132,13 +128,11 @@ linattn_status_t fwd_common(const void* q, const void* k, const void* v, const f
     L.prof[0] = L.prof[1] = L.prof[2] = L.prof[3] = nullptr;
     L.q = q; L.k = k; L.v = v; L.g = g; L.o = o;
     L.s0 = s0; L.z0 = z0; L.s_out = s_out; L.z_out = z_out;
-    char* w = static_cast<char*>(ws);
-    L.ws_st = reinterpret_cast<float*>(w);
-    L.ws_zt = reinterpret_cast<float*>(w + plan.off_zt);
-    L.ws_lg = reinterpret_cast<float*>(w + plan.off_lg);
+    L.ws = ws;
     L.BH = int(BH); L.N = N; L.D = D; L.Dv = Dv; L.chunk = chunk;
     L.nseg = plan.nseg; L.L = plan.L; L.eps = eps;
     L.stream = static_cast<hipStream_t>(stream);
+    L.algo = g_algo.load(std::memory_order_relaxed) == 2 ? 2 : 1;
     take_profile_events(L.prof);
     (void)hipGetLastError();   // start from a clean error state
     const hipError_t e = dtype == LINATTN_BF16 ? linattn::launch_fwd_bf16(L) : linattn::launch_fwd_f32(L);
@@ -207,6 +201,12 @@ linattn_status_t linattn_decode_step(const void* q, const void* k, const void* v
     } catch (...) {
         return LINATTN_ERR_HIP;
     }
+}
+
+linattn_status_t linattn_set_forward_algorithm(int algorithm) {
+    if (algorithm < 0 || algorithm > 2) return LINATTN_ERR_INVALID_ARGUMENT;
+    g_algo.store(algorithm, std::memory_order_relaxed);
+    return LINATTN_OK;
 }
 
 linattn_status_t linattn_set_profile_events(void* ev0, void* ev1, void* ev2, void* ev3) {

@@ -34,20 +34,32 @@
 //
 // Tile mapping (16x16 MFMA tiles, four waves):
 //   * transposed products: the kernel forms A^T = Fk Fq^T and O^T = V^T A^T + S^T Fq^T,
-//     so the A^T accumulator of two 16-key tiles is directly the B operand of the
-//     next product (its 8 contraction slots hold keys {4g..4g+3, 16+4g..16+4g+3}
-//     of lane group g; V^T is read with the same key order), and one lane owns one
+//     so the A^T accumulators of two 16-key tiles are directly the B operand of the
+//     next product (the tiles' rows are ordered so lane group g holds keys 8g..8g+7
+//     of the 32-key block, matching one 16-byte V^T read), and one lane owns one
 //     query row of O^T, so the row sums and the divide stay in the lane.
 //   * query strips of 16 rows are dealt to waves in pairs (w, 7-w) so every wave
 //     gets the same number of causal tiles.
-//   * the [D, Dv] state lives in MFMA accumulators (fp32) spread over the waves;
-//     its operand copy S^T (input precision) is re-staged in LDS once per chunk.
+//   * the [D, Dv] state lives in MFMA accumulators (fp32) spread over the waves,
+//     wave w owning the d-tiles [w D/64, (w+1) D/64) for every dv; z rides along as
+//     one more tile per d-tile whose B operand is a column of ones, so Fk^T 1 costs
+//     one MFMA per d-tile and no extra LDS traffic.  The operand copy S^T (input
+//     precision) and z are re-staged in LDS once per chunk.
+//   * loads are branch-free: rows past the end are clamped to the last row and their
+//     features zeroed; the next chunk's K and V are in flight while this chunk's
+//     products run, and its Q while this chunk's state is folded.
 //
 // LDS per workgroup: Fk [CH][D], Fk^T [D][CH], V^T [Dv][CH], S^T [Dv][D] in the
 // input precision, rows padded by 16 bytes, plus z [D] and Lambda [CH] in fp32.
 #pragma once
 
 #include "device_common.hpp"
+
+// Register sets for K and V: 2 loads the next chunk at the top of each chunk, 1 loads
+// it right after the current chunk is staged (fewer registers, shorter overlap).
+#ifndef LINATTN_KV_SETS
+#define LINATTN_KV_SETS 1
+#endif
 
 namespace linattn {
 
@@ -80,8 +92,8 @@ struct WalkShape {
     static constexpr int KPT = (NKU + kThreads - 1) / kThreads;
     static constexpr int VPT = (NVU + kThreads - 1) / kThreads;
     static constexpr int NA = D / 16, NB = DV / 16;
-    static constexpr int TPW = NA * NB / 4;           // state tiles per wave
-    static constexpr int TPD = kThreads / D;          // threads per z entry
+    static constexpr int ZT = NA / 4;                 // d-tiles owned by each wave
+    static constexpr int TPW = ZT * NB;               // state tiles per wave
     static constexpr int GPT = (CH + kWave - 1) / kWave;   // gate values per lane of wave 0
 
     static constexpr size_t bytes(bool output) {
@@ -99,174 +111,160 @@ __device__ __forceinline__ int strip_of(int w, int m) {
     return s < NSTRIP ? s : -1;
 }
 
-template <typename E, int D, int DV, int CH, bool GATED, bool OUTPUT>
-__global__ __launch_bounds__(kThreads) void walk_kernel(WalkArgs args) {
+// The per-thread machinery of one workgroup walking chunks of one head.
+// ROWK: also stage the row-major Fk (needed only when outputs are formed).
+template <typename E, int D, int DV, int CH, bool GATED, bool ROWK>
+struct ChunkWalker {
     using Sh = WalkShape<E, D, DV, CH>;
     using X = Elem<E>;
-    constexpr int LK = Sh::LK, LKT = Sh::LKT, LS = Sh::LS;
+    static constexpr int LK = Sh::LK, LKT = Sh::LKT, LS = Sh::LS;
 
-    extern __shared__ __align__(16) unsigned char smem[];
-    E* sK = reinterpret_cast<E*>(smem);
-    E* sKt = sK + (OUTPUT ? CH * LK : 0);
-    E* sVt = sKt + D * LKT;
-    E* sSt = sVt + DV * LKT;
-    float* sZ = reinterpret_cast<float*>(sSt + (OUTPUT ? DV * LS : 0));
-    float* sLam = sZ + D;
+    struct Regs {                       // one chunk of K, V (and gates) in flight
+        F8<E> rk[Sh::KPT][4];
+        F8<E> rv[Sh::VPT][4];
+        float rg[Sh::GPT];
+    };
+    struct QRegs {                      // this wave's query rows of one chunk
+        F8<E> rq[Sh::MAXS][D / 32];
+    };
 
-    const int tid = threadIdx.x;
-    const int w = tid / kWave;
-    const int lane = tid % kWave;
-    const int l16 = lane & 15;
-    const int g4 = lane >> 4;
+    E* sK;
+    E* sKt;
+    E* sVt;
+    E* sSt;
+    float* sZ;
+    float* sLam;
+    int tid, w, lane, l16, g4;
+    int N;
+    const E* qb;
+    const E* kb;
+    const E* vb;
+    const float* gb;
 
-    const int seg = blockIdx.x % args.nseg;
-    const int bh = blockIdx.x / args.nseg;
-    const int N = args.N;
-    const int nchunks_total = (N + CH - 1) / CH;
-    const int c0 = seg * args.L;
-    const int nch = min(args.L, nchunks_total - c0);
-
-    const E* qb = reinterpret_cast<const E*>(args.q) + size_t(bh) * N * D;
-    const E* kb = reinterpret_cast<const E*>(args.k) + size_t(bh) * N * D;
-    const E* vb = reinterpret_cast<const E*>(args.v) + size_t(bh) * N * DV;
-    const float* gb = GATED ? args.g + size_t(bh) * N : nullptr;
-    E* ob = OUTPUT ? reinterpret_cast<E*>(args.o) + size_t(bh) * N * DV : nullptr;
-    float* stp = args.st + (size_t(bh) * args.nseg + seg) * (D * DV);
-    float* ztp = args.zt + (size_t(bh) * args.nseg + seg) * D;
-
-    // ---- persistent state: S in accumulator tiles, z in registers ------------
-    f32x4_t sacc[Sh::TPW];
-    const int zd = tid / Sh::TPD;      // z entry owned (with TPD-1 neighbours)
-    const int zsub = tid % Sh::TPD;
-    float zr;
-    float lg_total = 0.0f;
-    if (OUTPUT) {
-#pragma unroll
-        for (int j = 0; j < Sh::TPW; ++j)
-            sacc[j] = *reinterpret_cast<const f32x4_t*>(stp + ((w * Sh::TPW + j) * kWave + lane) * 4);
-        zr = ztp[zd];
-    } else {
-#pragma unroll
-        for (int j = 0; j < Sh::TPW; ++j) sacc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        zr = 0.0f;
+    // Fk^T and V^T rows are [CH] keys stored as 16-byte groups of 8 keys; group j of
+    // row r sits at slot j ^ ((r / 8) mod (CH / 8)).  The transposed writes of a wave
+    // (8 rows x 8 key quads) then spread over all banks, and the MFMA operand reads
+    // (16 consecutive rows, one group) stay conflict-free.
+    static __device__ __forceinline__ int tidx(int row, int group) {
+        return row * LKT + ((group ^ ((row >> 3) & (CH / 8 - 1))) << 3);
+    }
+    // Fk rows are [D] features in 8-element groups; rows 8..15 of every 16 flip bit 2
+    // of the group index, so the operand read of keys {0-3, 8-11, ...} is conflict-free.
+    static __device__ __forceinline__ int kidx(int row, int group) {
+        return row * LK + ((group ^ (((row >> 3) & 1) << 2)) << 3);
     }
 
-    // S^T (operand precision) and z go to LDS for the first chunk's carried-state part.
-    auto stage_state = [&]() {
-#pragma unroll
-        for (int j = 0; j < Sh::TPW; ++j) {
-            const int u = w * Sh::TPW + j;
-            const int a = u / Sh::NB, b = u % Sh::NB;
-            F4<E> t;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) t.x[r] = X::from_f32(sacc[j][r]);
-            *reinterpret_cast<F4<E>*>(sSt + (16 * b + l16) * LS + 16 * a + 4 * g4) = t;
-        }
-        if (zsub == 0) sZ[zd] = zr;
-    };
-    if (OUTPUT) stage_state();
+    __device__ __forceinline__ void init(unsigned char* smem, int N_, const E* q, const E* k, const E* v,
+                                         const float* g) {
+        sK = reinterpret_cast<E*>(smem);
+        sKt = sK + (ROWK ? CH * LK : 0);
+        sVt = sKt + D * LKT;
+        sSt = sVt + DV * LKT;
+        sZ = reinterpret_cast<float*>(sSt + (ROWK ? DV * LS : 0));
+        sLam = sZ + D;
+        tid = threadIdx.x;
+        w = tid / kWave;
+        lane = tid % kWave;
+        l16 = lane & 15;
+        g4 = lane >> 4;
+        N = N_;
+        qb = q;
+        kb = k;
+        vb = v;
+        gb = g;
+    }
 
-    // ---- register staging of one chunk --------------------------------------
-    F8<E> rk[Sh::KPT][4];
-    F8<E> rv[Sh::VPT][4];
-    F8<E> rq[Sh::MAXS][D / 32];
-    float rg[Sh::GPT];
-
-    auto load_chunk = [&](int n) {
-        const int ts = (c0 + n) * CH;
+    // Global -> registers for the chunk starting at token ts.  Rows past N are
+    // clamped to N-1 (always in bounds); stage() zeroes their features.
+    __device__ __forceinline__ void load(Regs& R, int ts) const {
+        const int last = N - 1;
 #pragma unroll
         for (int it = 0; it < Sh::KPT; ++it) {
             const int u = tid + it * kThreads;
-            const int cg = u % (D / 8), kq = u / (D / 8);
+            const int cg = u % (D / 8), kq = (u / (D / 8)) % (CH / 4);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = ts + 4 * kq + r;
-                rk[it][r] = (u < Sh::NKU && row < N)
-                                ? *reinterpret_cast<const F8<E>*>(kb + size_t(row) * D + 8 * cg)
-                                : zero8<E>();
+                const int row = min(ts + 4 * kq + r, last);
+                R.rk[it][r] = *reinterpret_cast<const F8<E>*>(kb + size_t(row) * D + 8 * cg);
             }
         }
 #pragma unroll
         for (int it = 0; it < Sh::VPT; ++it) {
             const int u = tid + it * kThreads;
-            const int cg = u % (DV / 8), kq = u / (DV / 8);
+            const int cg = u % (DV / 8), kq = (u / (DV / 8)) % (CH / 4);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = ts + 4 * kq + r;
-                rv[it][r] = (u < Sh::NVU && row < N)
-                                ? *reinterpret_cast<const F8<E>*>(vb + size_t(row) * DV + 8 * cg)
-                                : zero8<E>();
+                const int row = min(ts + 4 * kq + r, last);
+                R.rv[it][r] = *reinterpret_cast<const F8<E>*>(vb + size_t(row) * DV + 8 * cg);
             }
         }
-        if (OUTPUT) {
-#pragma unroll
-            for (int m = 0; m < Sh::MAXS; ++m) {
-                const int s = strip_of<Sh::NSTRIP>(w, m);
-                const int row = ts + 16 * s + l16;
-#pragma unroll
-                for (int ks = 0; ks < D / 32; ++ks) {
-                    rq[m][ks] = (s >= 0 && row < N)
-                                    ? *reinterpret_cast<const F8<E>*>(qb + size_t(row) * D + 32 * ks + 8 * g4)
-                                    : zero8<E>();
-                }
-            }
-        }
-        if (GATED && w == 0) {
-#pragma unroll
-            for (int i = 0; i < Sh::GPT; ++i) {
-                const int j = lane * Sh::GPT + i;
-                const int row = ts + j;
-                rg[i] = (j < CH && row < N) ? gb[row] : 1.0f;
-            }
-        }
-    };
-
-    if (nch > 0) load_chunk(0);
-
-    for (int n = 0; n < nch; ++n) {
-        const int ts = (c0 + n) * CH;
-
-        // ---- Lambda: chunk-local inclusive cumulative log2 gate (wave 0) -------
-        if (GATED) {
+        if constexpr (GATED) {
             if (w == 0) {
-                float loc[Sh::GPT];
-                float run = 0.0f;
-#pragma unroll
-                for (int i = 0; i < Sh::GPT; ++i) { run += fast_log2(rg[i]); loc[i] = run; }
-                float incl = run;
-#pragma unroll
-                for (int off = 1; off < kWave; off <<= 1) {
-                    const float y = __shfl_up(incl, off, kWave);
-                    if (lane >= off) incl += y;
-                }
-                const float excl = incl - run;
 #pragma unroll
                 for (int i = 0; i < Sh::GPT; ++i) {
                     const int j = lane * Sh::GPT + i;
-                    if (j < CH) sLam[j] = excl + loc[i];
+                    const float gv = gb[min(ts + j, last)];
+                    R.rg[i] = (j < CH && ts + j < N) ? gv : 1.0f;
                 }
             }
-            __syncthreads();
         }
-        const float lam_last = GATED ? sLam[CH - 1] : 0.0f;
+    }
 
-        // ---- stage phi(K), phi(K)^T (decayed when gated) and V^T into LDS ------
+    __device__ __forceinline__ void load_q(QRegs& Q, int ts) const {
+        const int last = N - 1;
+#pragma unroll
+        for (int m = 0; m < Sh::MAXS; ++m) {
+            const int s = max(strip_of<Sh::NSTRIP>(w, m), 0);
+            const int row = min(ts + 16 * s + l16, last);
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks)
+                Q.rq[m][ks] = *reinterpret_cast<const F8<E>*>(qb + size_t(row) * D + 32 * ks + 8 * g4);
+        }
+    }
+
+    // Wave 0: Lambda_j = inclusive sum of log2 g over the chunk, into sLam.
+    __device__ __forceinline__ void lambda(const Regs& R) const {
+        if (w != 0) return;
+        float loc[Sh::GPT];
+        float run = 0.0f;
+#pragma unroll
+        for (int i = 0; i < Sh::GPT; ++i) {
+            run += fast_log2(R.rg[i]);
+            loc[i] = run;
+        }
+        float incl = run;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const float y = __shfl_up(incl, off, kWave);
+            if (lane >= off) incl += y;
+        }
+        const float excl = incl - run;
+#pragma unroll
+        for (int i = 0; i < Sh::GPT; ++i) {
+            const int j = lane * Sh::GPT + i;
+            if (j < CH) sLam[j] = excl + loc[i];
+        }
+    }
+
+    // phi(K) -> Fk (row-major, if WITHK) and Fk^T (decayed when gated); V -> V^T.
+    template <bool WITHK = ROWK>
+    __device__ __forceinline__ void stage(const Regs& R, int ts, float lam_last) const {
 #pragma unroll
         for (int it = 0; it < Sh::KPT; ++it) {
             const int u = tid + it * kThreads;
             if (u < Sh::NKU) {
                 const int cg = u % (D / 8), kq = u / (D / 8);
-                float f[4][8];
+                E fr[4][8];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const bool valid = ts + 4 * kq + r < N;
+                    const float mk = (ts + 4 * kq + r < N) ? 1.0f : 0.0f;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) f[r][e] = valid ? phi(X::to_f32(rk[it][r].x[e])) : 0.0f;
-                    if (OUTPUT) {
+                    for (int e = 0; e < 8; ++e) fr[r][e] = X::from_f32(phi(X::to_f32(R.rk[it][r].x[e])) * mk);
+                    if constexpr (WITHK) {
                         F8<E> t;
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) t.x[e] = X::from_f32(f[r][e]);
-                        *reinterpret_cast<F8<E>*>(sK + (4 * kq + r) * LK + 8 * cg) = t;
+                        for (int e = 0; e < 8; ++e) t.x[e] = fr[r][e];
+                        *reinterpret_cast<F8<E>*>(sK + kidx(4 * kq + r, cg)) = t;
                     }
                 }
                 float dec[4];
@@ -277,13 +275,9 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(WalkArgs args) {
                 for (int e = 0; e < 8; ++e) {
                     F4<E> t;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        // the decayed copy is rounded from the rounded feature, so the
-                        // ungated path stores exactly the values of Fk
-                        const float fr = X::to_f32(X::from_f32(f[r][e]));
-                        t.x[r] = X::from_f32(GATED ? fr * dec[r] : fr);
-                    }
-                    *reinterpret_cast<F4<E>*>(sKt + (8 * cg + e) * LKT + 4 * kq) = t;
+                    for (int r = 0; r < 4; ++r)
+                        t.x[r] = GATED ? X::from_f32(X::to_f32(fr[r][e]) * dec[r]) : fr[r][e];
+                    *reinterpret_cast<F4<E>*>(sKt + tidx(8 * cg + e, kq >> 1) + 4 * (kq & 1)) = t;
                 }
             }
         }
@@ -296,135 +290,253 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(WalkArgs args) {
                 for (int e = 0; e < 8; ++e) {
                     F4<E> t;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) t.x[r] = rv[it][r].x[e];
-                    *reinterpret_cast<F4<E>*>(sVt + (8 * cg + e) * LKT + 4 * kq) = t;
+                    for (int r = 0; r < 4; ++r) t.x[r] = R.rv[it][r].x[e];
+                    *reinterpret_cast<F4<E>*>(sVt + tidx(8 * cg + e, kq >> 1) + 4 * (kq & 1)) = t;
                 }
             }
         }
-        F8<E> fq[Sh::MAXS][D / 32];
-        if (OUTPUT) {
-#pragma unroll
-            for (int m = 0; m < Sh::MAXS; ++m)
-#pragma unroll
-                for (int ks = 0; ks < D / 32; ++ks)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) fq[m][ks].x[e] = X::from_f32(phi(X::to_f32(rq[m][ks].x[e])));
-        }
-        if (n + 1 < nch) load_chunk(n + 1);     // next chunk's loads overlap this chunk's math
-        __syncthreads();
+    }
 
-        // ---- outputs of this chunk -------------------------------------------
-        if (OUTPUT) {
+    __device__ __forceinline__ void phi_q(const QRegs& Q, F8<E> (&fq)[Sh::MAXS][D / 32]) const {
 #pragma unroll
-            for (int m = 0; m < Sh::MAXS; ++m) {
-                const int s = strip_of<Sh::NSTRIP>(w, m);
-                if (s < 0) continue;
-                const int qi = 16 * s + l16;               // query row of this lane
-                f32x4_t acc[DV / 16];
+        for (int m = 0; m < Sh::MAXS; ++m)
 #pragma unroll
-                for (int t = 0; t < DV / 16; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                // carried-state part: O^T += S^T Fq^T ; den += Fq . z
-                float den = 0.0f;
+            for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) fq[m][ks].x[e] = X::from_f32(phi(X::to_f32(Q.rq[m][ks].x[e])));
+    }
+
+    // S^T (operand precision) and z into LDS for the carried-state part.
+    __device__ __forceinline__ void stage_state(const f32x4_t (&sacc)[Sh::TPW], const f32x4_t (&zacc)[Sh::ZT]) const {
+#pragma unroll
+        for (int i = 0; i < Sh::ZT; ++i) {
+            const int a = w * Sh::ZT + i;
+#pragma unroll
+            for (int b = 0; b < Sh::NB; ++b) {
+                F4<E> t;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) t.x[r] = X::from_f32(sacc[i * Sh::NB + b][r]);
+                *reinterpret_cast<F4<E>*>(sSt + (16 * b + l16) * LS + 16 * a + 4 * g4) = t;
+            }
+            if (l16 == 0) *reinterpret_cast<f32x4_t*>(sZ + 16 * a + 4 * g4) = zacc[i];
+        }
+    }
+
+    // State fold: S = 2^lam_last S + Fk^T V (Fk^T already decayed), z alike.
+    __device__ __forceinline__ void fold(f32x4_t (&sacc)[Sh::TPW], f32x4_t (&zacc)[Sh::ZT], float lam_last) const {
+        if constexpr (GATED) {
+            const float dl = fast_exp2(lam_last);
+#pragma unroll
+            for (int j = 0; j < Sh::TPW; ++j) sacc[j] *= dl;
+#pragma unroll
+            for (int i = 0; i < Sh::ZT; ++i) zacc[i] *= dl;
+        }
+        F8<E> ones;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ones.x[e] = X::from_f32(l16 == 0 ? 1.0f : 0.0f);
+#pragma unroll
+        for (int kbk = 0; kbk < CH / 32; ++kbk) {
+            F8<E> vf[Sh::NB];
+#pragma unroll
+            for (int b = 0; b < Sh::NB; ++b) vf[b] = lds_f8(sVt + tidx(16 * b + l16, 4 * kbk + g4));
+#pragma unroll
+            for (int i = 0; i < Sh::ZT; ++i) {
+                const int a = w * Sh::ZT + i;
+                const F8<E> ka = lds_f8(sKt + tidx(16 * a + l16, 4 * kbk + g4));
+#pragma unroll
+                for (int b = 0; b < Sh::NB; ++b) sacc[i * Sh::NB + b] = mma(ka, vf[b], sacc[i * Sh::NB + b]);
+                zacc[i] = mma(ka, ones, zacc[i]);
+            }
+        }
+    }
+
+    // Walk chunks c0 .. c0+nch-1 of the head, folding each into (sacc, zacc); with OUT
+    // also form and store the outputs (S^T and z must then already be staged in LDS).
+    // K and V of the next chunk are loaded right after this chunk is staged (or, with
+    // two register sets, at the top of the chunk); Q of the next chunk is loaded once
+    // this chunk's outputs no longer need the single Q set.  The last chunk's fold is
+    // skipped when FOLD_LAST is false.
+    template <bool OUT, bool FOLD_LAST>
+    __device__ __forceinline__ void walk(int c0, int nch, f32x4_t (&sacc)[Sh::TPW], f32x4_t (&zacc)[Sh::ZT],
+                                         float& lg_total, E* ob, float eps) const {
+        constexpr bool kTwo = LINATTN_KV_SETS == 2;
+        Regs ra, rb_store;
+        Regs& rb = kTwo ? rb_store : ra;
+        QRegs qr;
+        auto step = [&](Regs& cur, Regs& nxt, int n) {
+            const int ts = (c0 + n) * CH;
+            const bool more = n + 1 < nch;
+            if (kTwo && more) load(nxt, ts + CH);
+            if constexpr (GATED) {
+                lambda(cur);
+                __syncthreads();
+            }
+            const float lam_last = GATED ? sLam[CH - 1] : 0.0f;
+            stage<OUT>(cur, ts, lam_last);
+            F8<E> fq[Sh::MAXS][D / 32];
+            if constexpr (OUT) phi_q(qr, fq);
+            if (!kTwo && more) load(nxt, ts + CH);
+            __syncthreads();
+            if constexpr (OUT) {
+                outputs(fq, ts, ob, eps);
+                if (more) load_q(qr, ts + CH);
+            }
+            if (FOLD_LAST || more) fold(sacc, zacc, lam_last);
+            lg_total += lam_last;
+            __syncthreads();
+            if (OUT && more) stage_state(sacc, zacc);
+        };
+        if (nch <= 0) return;
+        load(ra, c0 * CH);
+        if constexpr (OUT) load_q(qr, c0 * CH);
+        for (int n = 0; n < nch; n += 2) {
+            step(ra, rb, n);
+            if (n + 1 < nch) step(rb, ra, n + 1);
+        }
+    }
+
+    // Outputs of the chunk starting at ts for this wave's query strips.
+    __device__ __forceinline__ void outputs(const F8<E> (&fq)[Sh::MAXS][D / 32], int ts, E* ob, float eps) const {
+#pragma unroll
+        for (int m = 0; m < Sh::MAXS; ++m) {
+            const int s = strip_of<Sh::NSTRIP>(w, m);
+            if (s < 0) continue;
+            const int qi = 16 * s + l16;               // query row of this lane within the chunk
+            f32x4_t acc[DV / 16];
+#pragma unroll
+            for (int t = 0; t < DV / 16; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            // carried-state part: O^T += S^T Fq^T ; den += Fq . z
+            float den = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks) {
+#pragma unroll
+                for (int t = 0; t < DV / 16; ++t)
+                    acc[t] = mma(lds_f8(sSt + (16 * t + l16) * LS + 32 * ks + 8 * g4), fq[m][ks], acc[t]);
+                const f32x4_t z0 = *reinterpret_cast<const f32x4_t*>(sZ + 32 * ks + 8 * g4);
+                const f32x4_t z1 = *reinterpret_cast<const f32x4_t*>(sZ + 32 * ks + 8 * g4 + 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    den += X::to_f32(fq[m][ks].x[e]) * z0[e];
+                    den += X::to_f32(fq[m][ks].x[4 + e]) * z1[e];
+                }
+            }
+            float lam_q = 0.0f;
+            if constexpr (GATED) {
+                lam_q = sLam[qi];
+                const float sc = fast_exp2(lam_q);
+#pragma unroll
+                for (int t = 0; t < DV / 16; ++t) acc[t] *= sc;
+                den *= sc;
+            }
+            // causal part: key blocks of 32 up to the diagonal.  Row m of the first A^T
+            // tile is key 8(m/4) + m%4 of the block and row m of the second is that key
+            // + 4, so lane group g holds keys 8g..8g+7 of the block: a B operand of
+            // consecutive keys, matched by one 16-byte V^T read.
+            const int npairs = s / 2 + 1;
+            const int krow = 8 * (l16 >> 2) + (l16 & 3);
+            for (int p = 0; p < npairs; ++p) {
+                f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < D / 32; ++ks) {
-#pragma unroll
-                    for (int t = 0; t < DV / 16; ++t)
-                        acc[t] = mma(lds_f8(sSt + (16 * t + l16) * LS + 32 * ks + 8 * g4), fq[m][ks], acc[t]);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) den += X::to_f32(fq[m][ks].x[e]) * sZ[32 * ks + 8 * g4 + e];
+                    a0 = mma(lds_f8(sK + kidx(32 * p + krow, 4 * ks + g4)), fq[m][ks], a0);
+                    a1 = mma(lds_f8(sK + kidx(32 * p + krow + 4, 4 * ks + g4)), fq[m][ks], a1);
                 }
-                float lam_q = 0.0f;
-                if (GATED) {
-                    lam_q = sLam[qi];
-                    const float sc = fast_exp2(lam_q);
-#pragma unroll
-                    for (int t = 0; t < DV / 16; ++t) acc[t] *= sc;
-                    den *= sc;
+                F8<E> bA;
+                float rs = 0.0f;
+                f32x4_t l0 = {0.f, 0.f, 0.f, 0.f}, l1 = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (GATED) {
+                    l0 = *reinterpret_cast<const f32x4_t*>(sLam + 32 * p + 8 * g4);
+                    l1 = *reinterpret_cast<const f32x4_t*>(sLam + 32 * p + 8 * g4 + 4);
                 }
-                // causal part: key pairs of 32 up to the diagonal
-                const int npairs = s / 2 + 1;
-                for (int p = 0; p < npairs; ++p) {
-                    f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int ks = 0; ks < D / 32; ++ks) {
-                        a0 = mma(lds_f8(sK + (32 * p + l16) * LK + 32 * ks + 8 * g4), fq[m][ks], a0);
-                        a1 = mma(lds_f8(sK + (32 * p + 16 + l16) * LK + 32 * ks + 8 * g4), fq[m][ks], a1);
+                for (int r = 0; r < 4; ++r) {
+                    const int k0 = 32 * p + 8 * g4 + r, k1 = k0 + 4;
+                    float x0 = a0[r], x1 = a1[r];
+                    if constexpr (GATED) {
+                        x0 *= fast_exp2(fminf(lam_q - l0[r], 0.0f));
+                        x1 *= fast_exp2(fminf(lam_q - l1[r], 0.0f));
                     }
-                    F8<E> bA;
-                    float rs = 0.0f;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int k0 = 32 * p + 4 * g4 + r, k1 = k0 + 16;
-                        float x0 = a0[r], x1 = a1[r];
-                        if (GATED) {
-                            x0 *= fast_exp2(fminf(lam_q - sLam[k0], 0.0f));
-                            x1 *= fast_exp2(fminf(lam_q - sLam[k1], 0.0f));
-                        }
-                        x0 = k0 <= qi ? x0 : 0.0f;
-                        x1 = k1 <= qi ? x1 : 0.0f;
-                        const E e0 = X::from_f32(x0), e1 = X::from_f32(x1);
-                        bA.x[r] = e0;
-                        bA.x[4 + r] = e1;
-                        rs += X::to_f32(e0) + X::to_f32(e1);
-                    }
-                    den += rs;
-#pragma unroll
-                    for (int t = 0; t < DV / 16; ++t) {
-                        const E* vr = sVt + (16 * t + l16) * LKT + 32 * p + 4 * g4;
-                        acc[t] = mma(join(lds_f4(vr), lds_f4(vr + 16)), bA, acc[t]);
-                    }
+                    x0 = k0 <= qi ? x0 : 0.0f;
+                    x1 = k1 <= qi ? x1 : 0.0f;
+                    const E e0 = X::from_f32(x0), e1 = X::from_f32(x1);
+                    bA.x[r] = e0;
+                    bA.x[4 + r] = e1;
+                    rs += X::to_f32(e0) + X::to_f32(e1);
                 }
-                den += __shfl_xor(den, 16, kWave);
-                den += __shfl_xor(den, 32, kWave);
-                const float inv = 1.0f / fmaxf(den, args.eps);
-                const int row = ts + qi;
-                if (row < N) {
+                den += rs;
 #pragma unroll
-                    for (int t = 0; t < DV / 16; ++t) {
-                        F4<E> outv;
+                for (int t = 0; t < DV / 16; ++t)
+                    acc[t] = mma(lds_f8(sVt + tidx(16 * t + l16, 4 * p + g4)), bA, acc[t]);
+            }
+            den += __shfl_xor(den, 16, kWave);
+            den += __shfl_xor(den, 32, kWave);
+            const float inv = 1.0f / fmaxf(den, eps);
+            const int row = ts + qi;
+            if (row < N) {
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) outv.x[r] = X::from_f32(acc[t][r] * inv);
-                        *reinterpret_cast<F4<E>*>(ob + size_t(row) * DV + 16 * t + 4 * g4) = outv;
-                    }
+                for (int t = 0; t < DV / 16; ++t) {
+                    F4<E> outv;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) outv.x[r] = X::from_f32(acc[t][r] * inv);
+                    *reinterpret_cast<F4<E>*>(ob + size_t(row) * DV + 16 * t + 4 * g4) = outv;
                 }
             }
         }
-
-        // ---- fold the chunk into the state -------------------------------------
-        {
-            const float dl = GATED ? fast_exp2(lam_last) : 1.0f;
-#pragma unroll
-            for (int j = 0; j < Sh::TPW; ++j)
-                if (GATED) sacc[j] *= dl;
-#pragma unroll
-            for (int kbk = 0; kbk < CH / 32; ++kbk) {
-#pragma unroll
-                for (int j = 0; j < Sh::TPW; ++j) {
-                    const int u = w * Sh::TPW + j;
-                    const int a = u / Sh::NB, b = u % Sh::NB;
-                    sacc[j] = mma(lds_f8(sKt + (16 * a + l16) * LKT + 32 * kbk + 8 * g4),
-                                  lds_f8(sVt + (16 * b + l16) * LKT + 32 * kbk + 8 * g4), sacc[j]);
-                }
-            }
-            float zs = 0.0f;
-            constexpr int KP = CH / Sh::TPD;
-#pragma unroll 8
-            for (int j = 0; j < KP; ++j) zs += X::to_f32(sKt[zd * LKT + zsub * KP + j]);
-#pragma unroll
-            for (int off = 1; off < Sh::TPD; off <<= 1) zs += __shfl_xor(zs, off, kWave);
-            zr = dl * zr + zs;
-            lg_total += lam_last;
-        }
-        __syncthreads();
-        if (OUTPUT && n + 1 < nch) stage_state();
     }
+};
+
+template <typename E, int D, int DV, int CH, bool GATED, bool OUTPUT>
+__global__ __launch_bounds__(kThreads) void walk_kernel(WalkArgs args) {
+    using Sh = WalkShape<E, D, DV, CH>;
+    using W = ChunkWalker<E, D, DV, CH, GATED, OUTPUT>;
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const int seg = blockIdx.x % args.nseg;
+    const int bh = blockIdx.x / args.nseg;
+    const int N = args.N;
+    const int nchunks_total = (N + CH - 1) / CH;
+    const int c0 = seg * args.L;
+    const int nch = min(args.L, nchunks_total - c0);
+
+    W wk;
+    wk.init(smem, N, reinterpret_cast<const E*>(args.q) + size_t(bh) * N * D,
+            reinterpret_cast<const E*>(args.k) + size_t(bh) * N * D,
+            reinterpret_cast<const E*>(args.v) + size_t(bh) * N * DV, GATED ? args.g + size_t(bh) * N : nullptr);
+    E* ob = OUTPUT ? reinterpret_cast<E*>(args.o) + size_t(bh) * N * DV : nullptr;
+    float* stp = args.st + (size_t(bh) * args.nseg + seg) * (D * DV);
+    float* ztp = args.zt + (size_t(bh) * args.nseg + seg) * D;
+
+    // persistent state in accumulator tiles
+    f32x4_t sacc[Sh::TPW];
+    f32x4_t zacc[Sh::ZT];
+    if (OUTPUT) {
+#pragma unroll
+        for (int j = 0; j < Sh::TPW; ++j)
+            sacc[j] = *reinterpret_cast<const f32x4_t*>(stp + ((wk.w * Sh::TPW + j) * kWave + wk.lane) * 4);
+#pragma unroll
+        for (int i = 0; i < Sh::ZT; ++i) {
+            const f32x4_t zv = *reinterpret_cast<const f32x4_t*>(ztp + 16 * (wk.w * Sh::ZT + i) + 4 * wk.g4);
+            zacc[i] = wk.l16 == 0 ? zv : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        wk.stage_state(sacc, zacc);
+    } else {
+#pragma unroll
+        for (int j = 0; j < Sh::TPW; ++j) sacc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < Sh::ZT; ++i) zacc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    float lg_total = 0.0f;
+
+    wk.template walk<OUTPUT, !OUTPUT>(c0, nch, sacc, zacc, lg_total, ob, args.eps);
 
     if (!OUTPUT) {
 #pragma unroll
         for (int j = 0; j < Sh::TPW; ++j)
-            *reinterpret_cast<f32x4_t*>(stp + ((w * Sh::TPW + j) * kWave + lane) * 4) = sacc[j];
-        if (zsub == 0) ztp[zd] = zr;
-        if (GATED && tid == 0) args.lg[size_t(bh) * args.nseg + seg] = lg_total;
+            *reinterpret_cast<f32x4_t*>(stp + ((wk.w * Sh::TPW + j) * kWave + wk.lane) * 4) = sacc[j];
+#pragma unroll
+        for (int i = 0; i < Sh::ZT; ++i)
+            if (wk.l16 == 0) *reinterpret_cast<f32x4_t*>(ztp + 16 * (wk.w * Sh::ZT + i) + 4 * wk.g4) = zacc[i];
+        if (GATED && wk.tid == 0) args.lg[size_t(bh) * args.nseg + seg] = lg_total;
     }
 }
 
@@ -461,12 +573,24 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(float* st, float* zt, co
         init = z0;
         fin = z_out;
     }
+    const float* lgb = GATED ? lg + size_t(bh) * nseg : nullptr;
     float acc = init ? init[uidx] : 0.0f;
-    for (int s = 0; s < nseg; ++s) {
-        const float t = base[s * stride];
-        base[s * stride] = acc;
-        const float f = GATED ? fast_exp2(lg[size_t(bh) * nseg + s]) : 1.0f;
-        acc = f * acc + t;
+    constexpr int U = 8;                         // loads in flight per thread
+    for (int s0i = 0; s0i < nseg; s0i += U) {
+        float t[U], f[U];
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const int s = min(s0i + i, nseg - 1);
+            t[i] = base[size_t(s) * stride];
+            f[i] = GATED ? fast_exp2(lgb[s]) : 1.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            if (s0i + i < nseg) {
+                base[size_t(s0i + i) * stride] = acc;
+                acc = f[i] * acc + t[i];
+            }
+        }
     }
     if (fin) fin[uidx] = acc;
 }

@@ -14,11 +14,11 @@ constexpr int kWave = 64;          // CDNA wavefront width
 constexpr int kThreads = 256;      // four waves per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 
-// phi(x) = elu(x) + 1: x + 1 above zero, exp(x) at or below it.  The exp branch
-// sees min(x, 0) so it cannot overflow when the other branch is taken.  exp(x) is
-// 2^(x * log2 e) on the hardware exp2 unit.
+// phi(x) = elu(x) + 1: x + 1 above zero, exp(x) at or below it.  exp(x) is
+// 2^(x * log2 e) on the hardware exp2 unit; for large positive x it overflows to
+// +inf, which the select discards (NaN inputs stay NaN).
 __device__ __forceinline__ float phi(float x) {
-    const float e = __builtin_amdgcn_exp2f(fminf(x, 0.0f) * kLog2e);
+    const float e = __builtin_amdgcn_exp2f(x * kLog2e);
     return x > 0.0f ? x + 1.0f : e;
 }
 

@@ -48,6 +48,14 @@ def oracle_fwd(inp, heads=None, eps=1e-6, s0=None, z0=None):
                                           s0=pick(s0), z0=pick(z0), eps=eps)
 
 
+@pytest.fixture(params=[1, 2], ids=["three_pass", "single_pass"])
+def algo(request):
+    """Run the test under both forward algorithms of the library."""
+    assert binding.linattn_set_forward_algorithm(request.param) == 0
+    yield request.param
+    binding.linattn_set_forward_algorithm(0)
+
+
 def sel(t, heads):
     a = to64(t)
     return np.stack([a[b, h] for b, h in heads])[None]
@@ -74,7 +82,7 @@ SMALL = [
 
 @pytest.mark.parametrize("gated", [False, True], ids=["ungated", "gated"])
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: "B{}H{}N{}D{}Dv{}{}c{}".format(*c))
-def test_small_against_oracle(case, gated):
+def test_small_against_oracle(case, gated, algo):
     B, H, N, D, Dv, dt, chunk = case
     _say(f"small case {case} gated={gated}")
     inp = workloads.random_inputs(11 + N + D, B, H, N, D, Dv, dtype=dt, gated=gated, g_low=0.8)
@@ -88,7 +96,7 @@ def test_small_against_oracle(case, gated):
 
 @pytest.mark.parametrize("gated", [False, True], ids=["ungated", "gated"])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_initial_state_and_resume(dt, gated):
+def test_initial_state_and_resume(dt, gated, algo):
     B, H, N, D, Dv = 1, 2, 384, 64, 64
     chunk = 64
     inp = workloads.random_inputs(5, B, H, N, D, Dv, dtype=dt, gated=gated, g_low=0.85, with_state=True,
@@ -110,6 +118,40 @@ def test_initial_state_and_resume(dt, gated):
     assert matrix_rel_err(to64(S2), S_ref) <= tol
 
 
+@pytest.mark.parametrize("gated", [False, True], ids=["ungated", "gated"])
+def test_long_segment_chain(gated, algo):
+    # 128 chunks of 32 tokens per head and few heads: one chunk per segment, so every
+    # segment's state comes through a long chain of published predecessor states.
+    B, H, N, D, Dv = 1, 2, 4096, 64, 64
+    inp = workloads.random_inputs(41, B, H, N, D, Dv, dtype="bf16", gated=gated, g_low=0.97, with_state=True,
+                                  state_scale=10.0)
+    _say(f"long chain gated={gated}")
+    o, S, z = run_fwd(inp, 32, s0=inp["s0"], z0=inp["z0"], return_state=True)
+    o_ref, S_ref, z_ref = oracle_fwd(inp, s0=inp["s0"], z0=inp["z0"])
+    assert rowwise_rel_err(to64(o), o_ref) <= TOL["bf16"]
+    assert matrix_rel_err(to64(S), S_ref) <= TOL["bf16"]
+    assert matrix_rel_err(to64(z), z_ref) <= TOL["bf16"]
+
+
+def test_state_out_may_alias_state_in(algo):
+    B, H, N, D, Dv = 2, 2, 1000, 64, 64
+    inp = workloads.random_inputs(43, B, H, N, D, Dv, dtype="bf16", with_state=True, state_scale=5.0)
+    q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
+    S = inp["s0"].to(DEV)
+    z = inp["z0"].to(DEV)
+    ws = torch.empty(binding.workspace_bytes(B, H, N, D, Dv, 64), dtype=torch.uint8, device=DEV)
+    o = torch.empty(B, H, N, Dv, dtype=torch.bfloat16, device=DEV)
+    code = binding.linattn_fwd_chunked(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), S.data_ptr(),
+                                       z.data_ptr(), S.data_ptr(), z.data_ptr(), B, H, N, D, Dv, 64, binding.BF16,
+                                       1e-6, ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream)
+    assert code == 0
+    torch.cuda.synchronize()
+    o_ref, S_ref, z_ref = oracle_fwd(inp, s0=inp["s0"], z0=inp["z0"])
+    assert rowwise_rel_err(to64(o), o_ref) <= TOL["bf16"]
+    assert matrix_rel_err(to64(S), S_ref) <= TOL["bf16"]
+    assert matrix_rel_err(to64(z), z_ref) <= TOL["bf16"]
+
+
 def test_eps_clamp_on_gpu():
     # every query is very negative, so phi(q) ~ e^-16 and the denominator falls below eps
     B, H, N, D, Dv = 1, 1, 64, 64, 64
@@ -127,7 +169,7 @@ def test_first_output_is_v0_on_gpu():
     np.testing.assert_allclose(to64(o)[:, :, 0], to64(inp["v"])[:, :, 0], rtol=1e-5, atol=1e-6)
 
 
-def test_deterministic_and_guard_bands():
+def test_deterministic_and_guard_bands(algo):
     B, H, N, D, Dv = 2, 2, 1000, 64, 64
     inp = workloads.random_inputs(33, B, H, N, D, Dv, dtype="bf16", gated=True)
     q, k, v, g = (inp[n].to(DEV) for n in ("q", "k", "v", "g"))
@@ -204,7 +246,7 @@ def test_workload_fp32_small_full():
 
 
 @pytest.mark.parametrize("name", ["train_bf16", "gated_bf16"])
-def test_workload_sampled_heads(name):
+def test_workload_sampled_heads(name, algo):
     w = workloads.WORKLOADS[name]
     inp = workloads.make_inputs(w)
     heads = _heads(w.B, w.H, 6, 5)
