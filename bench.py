@@ -1,6 +1,6 @@
 """Benchmark of the causal kernelized linear attention hot path on one MI355X.
 
-One step = one chunked forward (phi, per-segment state totals, the look-back that
+One step = one chunked forward (phi, per-segment state totals, the scan that
 carries the state across segments, the masked intra-chunk products, the
 carried-state term and the divide) over the
 training-shaped workload B=8, H=16, N=4096, D=Dv=64, bf16, chunk 128, with the
@@ -12,7 +12,9 @@ D=Dv=128, fp32 state) are timed in the same run and reported in extra fields.
 
 Prints ONE JSON line.  Per-kernel durations come from hipEvents recorded on the
 launch stream around each kernel (the library's measurement hook); the roofline
-object prices the dominant kernel (the single-pass walk) against MI355X's 8 TB/s.
+object prices the dominant kernel (the output walk; the single-pass walk with
+--algorithm 2) against MI355X's 8 TB/s; its traffic figure comes from the committed
+rocprofv3 counter summary and is null once the kernel sources have changed.
 """
 from __future__ import annotations
 
@@ -28,6 +30,14 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+# the forward's three launches per algorithm (linattn_set_forward_algorithm)
+PHASES = {1: ("walk_totals", "scan", "walk_output"),     # segment totals, fp32 scan, output walk
+          2: ("clear", "fused", "final")}                # flag clear, single-pass walk, state copy-out
+DOMINANT = {1: ("walk_output", "walk_kernel<bf16,64,64,{c},ungated,output>"),
+            2: ("fused", "fused_kernel<bf16,64,64,{c},ungated>")}
+ALGORITHM = [1]
+KERNEL_SOURCES = os.path.join(ROOT, "causal_kernelized_linear_amd", "csrc")
+COUNTERS = os.path.join(ROOT, "profiles", "counters_walk_output_train_bf16.json")
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "causal linear-attn fwd tokens/s + % bf16 MFMA peak; decode GB/s % HBM peak"
 
@@ -135,9 +145,7 @@ def time_forward(w, chunk, steps, warmup, ev, rotate_bytes=600e6):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = ev.ms(t0, t1)
-    # the forward's three launches: clear the look-back flags, the single-pass walk,
-    # copy out the final state (empty here: no final state is requested)
-    names = ("clear", "fused", "final")
+    names = PHASES[ALGORITHM[0]]
     per = {nm: [ev.ms(e[i], e[i + 1]) for e in evs] for i, nm in enumerate(names)}
     res = {
         "ms_per_step": total_ms / steps,
@@ -188,6 +196,31 @@ def decode_bytes(w):
     return per_head * w.B * w.H
 
 
+def source_digest():
+    """sha256 over the kernel sources, to tell whether stored counters still apply."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_SOURCES)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(KERNEL_SOURCES, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(kernel_name):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter
+    summary, scaled by its copy-kernel calibration; None when the kernel sources changed
+    since the counters were taken."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("source_sha256") != source_digest() or c.get("kernel") != kernel_name:
+        return None
+    return 1024.0 * (c["fetch_kib"] * c["fetch_factor"] + c["write_kib"] * c["write_factor"])
+
+
 def cpu_baseline(w, seconds_hint=10.0):
     """The fp64 oracle, as it stands, on a bounded sample of workload w (all heads,
     the first tokens), on the host cores; returns tokens/s scaled to the workload."""
@@ -222,11 +255,13 @@ def main():
     ap.add_argument("--chunk", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="time only the headline workload")
+    ap.add_argument("--algorithm", type=int, default=1, choices=(1, 2),
+                    help="forward algorithm: 1 three launches, 2 single pass with look-back")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (calibrates rocprofv3 byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
 
@@ -237,6 +272,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     binding.lib()
+    ALGORITHM[0] = args.algorithm
+    if binding.linattn_set_forward_algorithm(args.algorithm) != 0:
+        raise RuntimeError("could not select the forward algorithm")
     ev = HipEvents()
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4
@@ -254,7 +292,9 @@ def main():
     tok_s = w.B * w.N / (r["ms_per_step"] * 1e-3)
     bpu = fwd_bytes_per_unit(w)
     fpu = fwd_flops_per_unit(w, chunk)
-    t_out = r["kernel_ms"]["fused"] * 1e-3
+    dom, dom_name = DOMINANT[args.algorithm]
+    dom_name = dom_name.format(c=chunk)
+    t_out = r["kernel_ms"][dom] * 1e-3
     achieved = bpu * units / t_out / 1e9
     step_s = r["ms_per_step"] * 1e-3
     line = {
@@ -275,16 +315,17 @@ def main():
                    "B": w.B, "H": w.H, "N": w.N, "D": w.D, "Dv": w.Dv, "chunk": chunk},
         "roofline": {
             "bound": "hbm",
-            "kernel": "fused_kernel<bf16,64,64,%d,ungated>" % chunk,
+            "kernel": dom_name,
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": stored_traffic(dom_name),
             "algorithmic_bytes_per_launch": bpu * units,
-            "kernel_ms": r["kernel_ms"]["fused"],
+            "kernel_ms": r["kernel_ms"][dom],
         },
         "forward": {
+            "algorithm": args.algorithm,
             "kernel_ms": r["kernel_ms"],
             "kernel_ms_median": r["kernel_ms_median"],
             "wall_ms_per_step": r["wall_ms_per_step"],
