@@ -1,6 +1,6 @@
 """Benchmark of the causal kernelized linear attention hot path on one MI355X.
 
-One step = one chunked forward (phi, per-segment state totals, the scan that
+One step = one chunked forward (phi, per-segment state totals, the prefix that
 carries the state across segments, the masked intra-chunk products, the
 carried-state term and the divide) over the
 training-shaped workload B=8, H=16, N=4096, D=Dv=64, bf16, chunk 128, with the
@@ -12,9 +12,9 @@ D=Dv=128, fp32 state) are timed in the same run and reported in extra fields.
 
 Prints ONE JSON line.  Per-kernel durations come from hipEvents recorded on the
 launch stream around each kernel (the library's measurement hook); the roofline
-object prices the dominant kernel (the output walk; the single-pass walk with
---algorithm 2) against MI355X's 8 TB/s; its traffic figure comes from the committed
-rocprofv3 counter summary and is null once the kernel sources have changed.
+object prices the dominant kernel (the output walk) against MI355X's 8 TB/s; its
+traffic figure comes from the committed rocprofv3 counter summary and is null once
+the kernel sources have changed.
 """
 from __future__ import annotations
 
@@ -30,12 +30,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-# the forward's three launches per algorithm (linattn_set_forward_algorithm)
-PHASES = {1: ("walk_totals", "scan", "walk_output"),     # segment totals, fp32 scan, output walk
-          2: ("clear", "fused", "final")}                # flag clear, single-pass walk, state copy-out
-DOMINANT = {1: ("walk_output", "walk_kernel<bf16,64,64,{c},ungated,output>"),
-            2: ("fused", "fused_kernel<bf16,64,64,{c},ungated>")}
-ALGORITHM = [1]
+# the forward's steps between the measurement hook's four events: segment totals, the
+# scan over segments (skipped when the output walk sums the prefix itself), output walk
+PHASES = ("walk_totals", "scan", "walk_output")
+DOMINANT = ("walk_output", "walk_kernel<bf16,64,64,{c},ungated,output>")
 KERNEL_SOURCES = os.path.join(ROOT, "causal_kernelized_linear_amd", "csrc")
 COUNTERS = os.path.join(ROOT, "profiles", "counters_walk_output_train_bf16.json")
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
@@ -145,7 +143,7 @@ def time_forward(w, chunk, steps, warmup, ev, rotate_bytes=600e6):
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = ev.ms(t0, t1)
-    names = PHASES[ALGORITHM[0]]
+    names = PHASES
     per = {nm: [ev.ms(e[i], e[i + 1]) for e in evs] for i, nm in enumerate(names)}
     res = {
         "ms_per_step": total_ms / steps,
@@ -255,8 +253,6 @@ def main():
     ap.add_argument("--chunk", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="time only the headline workload")
-    ap.add_argument("--algorithm", type=int, default=1, choices=(1, 2),
-                    help="forward algorithm: 1 three launches, 2 single pass with look-back")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (calibrates rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -272,9 +268,6 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     binding.lib()
-    ALGORITHM[0] = args.algorithm
-    if binding.linattn_set_forward_algorithm(args.algorithm) != 0:
-        raise RuntimeError("could not select the forward algorithm")
     ev = HipEvents()
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4
@@ -292,7 +285,7 @@ def main():
     tok_s = w.B * w.N / (r["ms_per_step"] * 1e-3)
     bpu = fwd_bytes_per_unit(w)
     fpu = fwd_flops_per_unit(w, chunk)
-    dom, dom_name = DOMINANT[args.algorithm]
+    dom, dom_name = DOMINANT
     dom_name = dom_name.format(c=chunk)
     t_out = r["kernel_ms"][dom] * 1e-3
     achieved = bpu * units / t_out / 1e9
@@ -325,7 +318,6 @@ def main():
             "kernel_ms": r["kernel_ms"][dom],
         },
         "forward": {
-            "algorithm": args.algorithm,
             "kernel_ms": r["kernel_ms"],
             "kernel_ms_median": r["kernel_ms_median"],
             "wall_ms_per_step": r["wall_ms_per_step"],

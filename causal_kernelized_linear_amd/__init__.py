@@ -13,7 +13,6 @@ from .binding import (  # noqa: F401
     linattn_fwd_chunked,
     linattn_fwd_gated,
     linattn_fwd_workspace_size,
-    linattn_set_forward_algorithm,
     linattn_set_profile_events,
     linattn_status_string,
     workspace_bytes,

@@ -40,7 +40,6 @@ EXPORTS = {
     "linattn_decode_step": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p]),
     "linattn_status_string": (ctypes.c_char_p, [_i]),
     "linattn_set_profile_events": (_i, [_p, _p, _p, _p]),
-    "linattn_set_forward_algorithm": (_i, [_i]),
 }
 
 
@@ -89,11 +88,6 @@ def linattn_fwd_gated(q, k, v, g, o, s0, z0, s_out, z_out, B, H, N, D, Dv, chunk
 
 def linattn_decode_step(q, k, v, S, z, o, B, H, D, Dv, dtype, eps, stream) -> int:
     return int(lib().linattn_decode_step(q, k, v, S, z, o, B, H, D, Dv, dtype, eps, stream))
-
-
-def linattn_set_forward_algorithm(algorithm: int) -> int:
-    """0 default, 1 three launches, 2 single pass with look-back (see linattn.h)."""
-    return int(lib().linattn_set_forward_algorithm(int(algorithm)))
 
 
 def linattn_set_profile_events(ev0, ev1, ev2, ev3) -> int:

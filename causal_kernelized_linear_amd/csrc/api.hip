@@ -3,7 +3,6 @@
 // include/linattn.h.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -37,12 +36,9 @@ Plan make_plan(long BH, int N, int D, int Dv, int chunk) {
     nseg = (nc + L - 1) / L;
     p.nseg = int(nseg);
     p.L = int(L);
-    p.bytes = linattn::fwd_workspace_bytes(size_t(BH) * size_t(nseg), D, Dv);
+    p.bytes = linattn::fwd_workspace_layout(size_t(BH) * size_t(nseg), D, Dv, nullptr, nullptr);
     return p;
 }
-
-// Forward algorithm (linattn_set_forward_algorithm): 0 picks the three-launch path.
-std::atomic<int> g_algo{0};
 
 // Measurement hook (linattn_set_profile_events): one-shot, process-wide.
 std::mutex g_prof_mu;
@@ -110,8 +106,10 @@ linattn_status_t fwd_common(const void* q, const void* k, const void* v, const f
     if (overlap(o, nv, q, nqk) || overlap(o, nv, k, nqk) || overlap(o, nv, v, nv) ||
         overlap(o, nv, g, size_t(BH) * N * 4))
         return LINATTN_ERR_INVALID_ARGUMENT;
+    // outputs are addressed with 32-bit byte offsets per head
+    if ((size_t(N) + 256) * size_t(Dv) * es >= (size_t(1) << 31)) return LINATTN_ERR_UNSUPPORTED;
     if (!dim_ok(D) || !dim_ok(Dv) || !linattn::chunk_is_built(chunk) ||
-        linattn::walk_lds_bytes(int(es), D, Dv, chunk) + 16 > linattn::kMaxLds)
+        linattn::walk_lds_bytes(int(es), D, Dv, chunk, g != nullptr) > linattn::kMaxLds)
         return LINATTN_ERR_UNSUPPORTED;
     const Plan plan = make_plan(BH, N, D, Dv, chunk);
     if (ws_bytes < plan.bytes || !ws || !aligned16(ws)) return LINATTN_ERR_WORKSPACE;
@@ -132,7 +130,6 @@ linattn_status_t fwd_common(const void* q, const void* k, const void* v, const f
     L.BH = int(BH); L.N = N; L.D = D; L.Dv = Dv; L.chunk = chunk;
     L.nseg = plan.nseg; L.L = plan.L; L.eps = eps;
     L.stream = static_cast<hipStream_t>(stream);
-    L.algo = g_algo.load(std::memory_order_relaxed) == 2 ? 2 : 1;
     take_profile_events(L.prof);
     (void)hipGetLastError();   // start from a clean error state
     const hipError_t e = dtype == LINATTN_BF16 ? linattn::launch_fwd_bf16(L) : linattn::launch_fwd_f32(L);
@@ -201,12 +198,6 @@ linattn_status_t linattn_decode_step(const void* q, const void* k, const void* v
     } catch (...) {
         return LINATTN_ERR_HIP;
     }
-}
-
-linattn_status_t linattn_set_forward_algorithm(int algorithm) {
-    if (algorithm < 0 || algorithm > 2) return LINATTN_ERR_INVALID_ARGUMENT;
-    g_algo.store(algorithm, std::memory_order_relaxed);
-    return LINATTN_OK;
 }
 
 linattn_status_t linattn_set_profile_events(void* ev0, void* ev1, void* ev2, void* ev3) {

@@ -1,25 +1,28 @@
 // Chunked forward of causal kernelized linear attention for gfx950.
 //
-// The sequence of every (batch, head) is cut into segments of L chunks of CH
-// tokens.  Three launches make one forward:
+// The sequence of every (batch, head) is cut into nseg segments of L chunks of CH
+// tokens.  One forward is:
 //
-//   1. walk<TOTALS>  one workgroup per (head, segment): walks the segment's
-//      chunks and accumulates the segment's own state total
+//   1. walk<TOTALS>  one workgroup per (head, segment) for every segment but the
+//      last: walks the segment's chunks and accumulates the segment's own total
 //          T = sum_j w_j phi(k_j) v_j^T,  t = sum_j w_j phi(k_j)
 //      (w_j = product of the gates after j inside the segment; 1 ungated) and,
 //      gated, the log2 of the segment's total decay.  Reads K and V only.
-//   2. scan          per (head, state element): exclusive prefix over segments,
-//          P_0 = S0,  P_{s+1} = Gamma_s P_s + T_s,
-//      in fp32, in place; writes S_N, z_N when asked.
-//   3. walk<OUTPUT>  one workgroup per (head, segment): starts from P_s and walks
-//      the segment's chunks carrying S and z in registers.  Per chunk it forms
-//      the masked quadratic part on MFMA, adds the carried-state part, divides by
-//      the clamped denominator, stores O, and folds the chunk into the state.
+//   2. the state in front of each segment,
+//          P_0 = S0,  P_{s+1} = Gamma_s P_s + T_s      (fp32),
+//      either summed by each output workgroup itself from the totals in front of
+//      it (few, small states) or by scan_kernel, in place, beforehand.
+//   3. walk<OUTPUT>  one workgroup per (head, segment): starts from P_s and walks the
+//      segment's chunks carrying S and z in registers.  Per chunk it forms the masked
+//      quadratic part on MFMA, adds the carried-state part, divides by the clamped
+//      denominator, stores O, and folds the chunk into the state.  The last
+//      segment's workgroup leaves S_N, z_N in the workspace for final_kernel when the
+//      caller asks for them.
 //
 // This is the chunked parallel form of the aiwiki.thehackersbrain.dev page (the
 // chunked listing: quadratic inside a chunk, recurrent across chunks, and the
 // closing paragraph on the O(c^2) / O(d^2) balance), with the state pass split
-// into segment totals plus a scan so every workgroup of the walk is independent.
+// into segment totals plus a prefix so every workgroup of the walk is independent.
 //
 // Chunk algebra for a chunk [s, s + CH) with Fq = phi(Q_c), Fk = phi(K_c):
 //     A     = tril(Fq Fk^T)                  (diagonal kept)
@@ -37,29 +40,28 @@
 //     so the A^T accumulators of two 16-key tiles are directly the B operand of the
 //     next product (the tiles' rows are ordered so lane group g holds keys 8g..8g+7
 //     of the 32-key block, matching one 16-byte V^T read), and one lane owns one
-//     query row of O^T, so the row sums and the divide stay in the lane.
+//     query row of O^T, so the divide stays in the lane.
+//   * the denominator rides on the same MFMAs as one more 16-row output tile: its
+//     A operand has ones in rows 0, 4, 8, 12 against A^T (the row sums of A, over
+//     exactly the rounded values the numerator uses) and z split into a high and a
+//     low part in rows 4g and 4g+1 against Fq^T, so every lane group ends up holding
+//     its queries' denominators in its first two accumulator slots.
 //   * query strips of 16 rows are dealt to waves in pairs (w, 7-w) so every wave
-//     gets the same number of causal tiles.
+//     gets the same number of causal tiles; only the diagonal key block is masked.
 //   * the [D, Dv] state lives in MFMA accumulators (fp32) spread over the waves,
 //     wave w owning the d-tiles [w D/64, (w+1) D/64) for every dv; z rides along as
-//     one more tile per d-tile whose B operand is a column of ones, so Fk^T 1 costs
-//     one MFMA per d-tile and no extra LDS traffic.  The operand copy S^T (input
-//     precision) and z are re-staged in LDS once per chunk.
-//   * loads are branch-free: rows past the end are clamped to the last row and their
-//     features zeroed; the next chunk's K and V are in flight while this chunk's
-//     products run, and its Q while this chunk's state is folded.
-//
-// LDS per workgroup: Fk [CH][D], Fk^T [D][CH], V^T [Dv][CH], S^T [Dv][D] in the
-// input precision, rows padded by 16 bytes, plus z [D] and Lambda [CH] in fp32.
+//     one more tile per d-tile whose B operand is a column of ones.  The operand copy
+//     S^T (input precision) and z are re-staged in LDS once per chunk.
+//   * the fold's key-major Fk operand comes from the row-major Fk tile through
+//     ds_read_b64_tr_b16 (bf16, ungated); the gated and fp32 walks and the totals walk
+//     stage a transposed copy (decayed when gated) instead.
+//   * loads are branch-free: rows past the end are clamped to the last row; in a
+//     chunk that crosses the end their features are zeroed.  The next chunk's K and V
+//     are in flight while this chunk's products run, and its Q while this chunk's
+//     state is folded.
 #pragma once
 
 #include "device_common.hpp"
-
-// Register sets for K and V: 2 loads the next chunk at the top of each chunk, 1 loads
-// it right after the current chunk is staged (fewer registers, shorter overlap).
-#ifndef LINATTN_KV_SETS
-#define LINATTN_KV_SETS 1
-#endif
 
 namespace linattn {
 
@@ -69,20 +71,27 @@ struct WalkArgs {
     const void* v;
     const float* g;      // gated only
     void* o;             // OUTPUT only
-    float* st;           // [BH][nseg][D*Dv] state totals/prefixes, accumulator layout
-    float* zt;           // [BH][nseg][D]
+    float* st;           // [BH][nseg][D*Dv] accumulator layout: slot s < nseg-1 holds T_s (after
+                         // the scan: P_{s+1}); slot nseg-1 receives S_N
+    float* zt;           // [BH][nseg][D], alike
     float* lg;           // [BH][nseg] log2 of each segment's total decay (gated)
+    const float* s0;     // [BH][D][Dv] initial state or NULL (caller layout)
+    const float* z0;     // [BH][D] or NULL
     int N;
     int nseg;            // segments per sequence
     int L;               // chunks per segment
+    int direct;          // 1: the output walk sums the totals in front of its segment itself
+    int want_final;      // 1: the last segment's output walk leaves S_N, z_N in slot nseg-1
     float eps;
 };
 
-template <typename E, int D, int DV, int CH>
+template <typename E, int D, int DV, int CH, bool GATED, bool OUT>
 struct WalkShape {
     static_assert(CH >= 32 && CH <= 256 && (CH & (CH - 1)) == 0, "chunk must be a power of two in [32, 256]");
+    static constexpr bool kBf16 = sizeof(E) == 2;
+    static constexpr bool kRowK = OUT;                         // row-major Fk tile
+    static constexpr bool kKT = !OUT || GATED || !kBf16;       // transposed (decayed) Fk^T tile
     static constexpr int PE = 16 / int(sizeof(E));   // 16-byte row padding, in elements
-    static constexpr int LK = D + PE;                 // row stride of Fk   [CH][D]
     static constexpr int LKT = CH + PE;               // row stride of Fk^T [D][CH] and V^T [Dv][CH]
     static constexpr int LS = D + PE;                 // row stride of S^T  [Dv][D]
     static constexpr int NSTRIP = CH / 16;
@@ -96,12 +105,32 @@ struct WalkShape {
     static constexpr int TPW = ZT * NB;               // state tiles per wave
     static constexpr int GPT = (CH + kWave - 1) / kWave;   // gate values per lane of wave 0
 
-    static constexpr size_t bytes(bool output) {
-        return (output ? size_t(CH) * LK * sizeof(E) : 0) + size_t(D) * LKT * sizeof(E) +
-               size_t(DV) * LKT * sizeof(E) + (output ? size_t(DV) * LS * sizeof(E) : 0) +
-               size_t(D) * 4 + size_t(CH) * 4;
-    }
+    // LDS carve-up, in bytes from the base.
+    static constexpr size_t kOffK = 0;
+    static constexpr size_t kOffKt = kOffK + (kRowK ? size_t(CH) * D * sizeof(E) : 0);
+    static constexpr size_t kOffVt = kOffKt + (kKT ? size_t(D) * LKT * sizeof(E) : 0);
+    static constexpr size_t kOffSt = kOffVt + size_t(DV) * LKT * sizeof(E);
+    static constexpr size_t kOffZb = kOffSt + (OUT ? size_t(DV) * LS * sizeof(E) : 0);
+    static constexpr size_t kOffLam = kOffZb + (OUT ? size_t(4) * D * sizeof(E) : 0);
+    static constexpr size_t kBytes = kOffLam + size_t(CH) * 4;
 };
+
+// Waves per SIMD each walk kernel is compiled for (one wave of every workgroup sits on
+// each SIMD, so this is also workgroups per compute unit): what its LDS allows, capped
+// by the register budget its shape can live with (512 / waves registers per lane).  A
+// fixed target keeps the compiler from squeezing registers for an occupancy the shape
+// cannot reach, which would make it wait for the next chunk's loads early.
+template <typename E, int D, int DV, int CH, bool GATED, bool OUT>
+constexpr int walk_waves() {
+    constexpr size_t kLdsPerCu = 160 * 1024;
+    const int lds = int(kLdsPerCu / WalkShape<E, D, DV, CH, GATED, OUT>::kBytes);
+    const int work = D * DV * (sizeof(E) == 2 ? 1 : 2) * (CH > 128 ? 2 : 1);   // grows with the live tiles
+    int regs = 1;
+    if (work <= 64 * 64) regs = OUT ? 2 : 3;
+    else if (work <= 2 * 64 * 64) regs = OUT ? 1 : 2;
+    const int v = lds < regs ? lds : regs;
+    return v < 1 ? 1 : v;
+}
 
 // Query strip handled by wave w in its m-th slot, or -1.
 template <int NSTRIP>
@@ -111,13 +140,64 @@ __device__ __forceinline__ int strip_of(int w, int m) {
     return s < NSTRIP ? s : -1;
 }
 
+// Row-major [rows][W] tile without padding whose 8-element groups are permuted per
+// row by ((row / 8) mod 2) ^ 2 (row mod 4).  The staging writes (4 rows x 8 columns
+// per thread), the A^T operand reads (16 rows in the key order of the transposed
+// products, one group) and the transpose reads (4 rows x 4 columns per 16 lanes) are
+// all free of LDS bank conflicts.
+template <int W>
+__device__ __forceinline__ int tile_off(int row, int col) {
+    const int sw = ((row >> 3) & 1) ^ ((row & 3) << 1);
+    return row * W + ((((col >> 3) ^ sw) & (W / 8 - 1)) << 3) + (col & 7);
+}
+
+// Key-major bf16 operand from a row-major tile_off<W> tile: slot e of lane l holds
+// tile[k0 + e][m0 + l % 16] (k0 includes the lane group's offset).  Each
+// ds_read_b64_tr_b16 gives every lane of a 16-lane block four rows of one column
+// when block lane j points at row k0 + j / 4, columns m0 + 4 (j % 4) .. + 3.
+template <int W>
+__device__ __forceinline__ F8<uint16_t> tr_operand(const uint16_t* tile, int k0, int m0, int l16) {
+    typedef short i16x4_t __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) i16x4_t* lds_ptr_t;
+    const int r = k0 + (l16 >> 2), c = m0 + 4 * (l16 & 3);
+    const i16x4_t a =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr_t)(const_cast<uint16_t*>(tile + tile_off<W>(r, c))));
+    const i16x4_t b =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr_t)(const_cast<uint16_t*>(tile + tile_off<W>(r + 4, c))));
+    F8<uint16_t> f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f.x[e] = uint16_t(a[e]);
+        f.x[4 + e] = uint16_t(b[e]);
+    }
+    return f;
+}
+
+// One head's output rows as a buffer resource: stores past its end (rows past N) are
+// dropped by the hardware, so the tail needs no branch.  Byte offsets are 32-bit; the
+// library keeps every head's output below 2 GiB.
+struct OutRsrc {
+    __amdgpu_buffer_rsrc_t r;
+    __device__ __forceinline__ void init(void* base, unsigned bytes) {
+        r = __builtin_amdgcn_make_buffer_rsrc(base, 0, int(bytes), 0x00020000);
+    }
+    __device__ __forceinline__ void store(const F4<uint16_t>& v, int off) const {
+        typedef int v2i __attribute__((ext_vector_type(2)));
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2i, v), r, off, 0, 0);
+    }
+    __device__ __forceinline__ void store(const F4<float>& v, int off) const {
+        typedef int v4i __attribute__((ext_vector_type(4)));
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), r, off, 0, 0);
+    }
+};
+
 // The per-thread machinery of one workgroup walking chunks of one head.
-// ROWK: also stage the row-major Fk (needed only when outputs are formed).
-template <typename E, int D, int DV, int CH, bool GATED, bool ROWK>
+// OUT: the workgroup forms outputs (row-major Fk, S^T and the split z in LDS).
+template <typename E, int D, int DV, int CH, bool GATED, bool OUT>
 struct ChunkWalker {
-    using Sh = WalkShape<E, D, DV, CH>;
+    using Sh = WalkShape<E, D, DV, CH, GATED, OUT>;
     using X = Elem<E>;
-    static constexpr int LK = Sh::LK, LKT = Sh::LKT, LS = Sh::LS;
+    static constexpr int LKT = Sh::LKT, LS = Sh::LS;
 
     struct Regs {                       // one chunk of K, V (and gates) in flight
         F8<E> rk[Sh::KPT][4];
@@ -132,10 +212,11 @@ struct ChunkWalker {
     E* sKt;
     E* sVt;
     E* sSt;
-    float* sZ;
+    E* sZb;        // [4][D]: z high part, z low part, two zero rows
     float* sLam;
     int tid, w, lane, l16, g4;
     int N;
+    int last;      // last row the loads may touch: the end of the walked range (clamped to N - 1)
     const E* qb;
     const E* kb;
     const E* vb;
@@ -148,36 +229,32 @@ struct ChunkWalker {
     static __device__ __forceinline__ int tidx(int row, int group) {
         return row * LKT + ((group ^ ((row >> 3) & (CH / 8 - 1))) << 3);
     }
-    // Fk rows are [D] features in 8-element groups; rows 8..15 of every 16 flip bit 2
-    // of the group index, so the operand read of keys {0-3, 8-11, ...} is conflict-free.
-    static __device__ __forceinline__ int kidx(int row, int group) {
-        return row * LK + ((group ^ (((row >> 3) & 1) << 2)) << 3);
-    }
 
     __device__ __forceinline__ void init(unsigned char* smem, int N_, const E* q, const E* k, const E* v,
                                          const float* g) {
-        sK = reinterpret_cast<E*>(smem);
-        sKt = sK + (ROWK ? CH * LK : 0);
-        sVt = sKt + D * LKT;
-        sSt = sVt + DV * LKT;
-        sZ = reinterpret_cast<float*>(sSt + (ROWK ? DV * LS : 0));
-        sLam = sZ + D;
+        sK = reinterpret_cast<E*>(smem + Sh::kOffK);
+        sKt = reinterpret_cast<E*>(smem + Sh::kOffKt);
+        sVt = reinterpret_cast<E*>(smem + Sh::kOffVt);
+        sSt = reinterpret_cast<E*>(smem + Sh::kOffSt);
+        sZb = reinterpret_cast<E*>(smem + Sh::kOffZb);
+        sLam = reinterpret_cast<float*>(smem + Sh::kOffLam);
         tid = threadIdx.x;
-        w = tid / kWave;
+        w = __builtin_amdgcn_readfirstlane(tid / kWave);
         lane = tid % kWave;
         l16 = lane & 15;
         g4 = lane >> 4;
         N = N_;
+        last = N_ - 1;
         qb = q;
         kb = k;
         vb = v;
         gb = g;
     }
 
-    // Global -> registers for the chunk starting at token ts.  Rows past N are
-    // clamped to N-1 (always in bounds); stage() zeroes their features.
+    // Global -> registers for the chunk starting at token ts.  Rows past `last` are
+    // clamped to it (always in bounds: the prefetch behind the walk's last chunk rereads
+    // one cached row); stage() zeroes the features of rows past N.
     __device__ __forceinline__ void load(Regs& R, int ts) const {
-        const int last = N - 1;
 #pragma unroll
         for (int it = 0; it < Sh::KPT; ++it) {
             const int u = tid + it * kThreads;
@@ -199,19 +276,18 @@ struct ChunkWalker {
             }
         }
         if constexpr (GATED) {
-            if (w == 0) {
+            // every wave loads the gates (cached; only wave 0 scans them), so the loads
+            // sit behind no branch
 #pragma unroll
-                for (int i = 0; i < Sh::GPT; ++i) {
-                    const int j = lane * Sh::GPT + i;
-                    const float gv = gb[min(ts + j, last)];
-                    R.rg[i] = (j < CH && ts + j < N) ? gv : 1.0f;
-                }
+            for (int i = 0; i < Sh::GPT; ++i) {
+                const int j = lane * Sh::GPT + i;
+                const float gv = gb[min(ts + j, last)];
+                R.rg[i] = (j < CH && ts + j < N) ? gv : 1.0f;
             }
         }
     }
 
     __device__ __forceinline__ void load_q(QRegs& Q, int ts) const {
-        const int last = N - 1;
 #pragma unroll
         for (int m = 0; m < Sh::MAXS; ++m) {
             const int s = max(strip_of<Sh::NSTRIP>(w, m), 0);
@@ -246,8 +322,9 @@ struct ChunkWalker {
         }
     }
 
-    // phi(K) -> Fk (row-major, if WITHK) and Fk^T (decayed when gated); V -> V^T.
-    template <bool WITHK = ROWK>
+    // phi(K) -> Fk (row-major) and/or Fk^T (decayed when gated); V -> V^T.  TAIL: the
+    // chunk crosses the end of the sequence, so rows past N get zero features.
+    template <bool TAIL>
     __device__ __forceinline__ void stage(const Regs& R, int ts, float lam_last) const {
 #pragma unroll
         for (int it = 0; it < Sh::KPT; ++it) {
@@ -257,27 +334,31 @@ struct ChunkWalker {
                 E fr[4][8];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float mk = (ts + 4 * kq + r < N) ? 1.0f : 0.0f;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) fr[r][e] = X::from_f32(phi(X::to_f32(R.rk[it][r].x[e])) * mk);
-                    if constexpr (WITHK) {
+                    for (int e = 0; e < 8; ++e) {
+                        const float f = phi(X::to_f32(R.rk[it][r].x[e]));
+                        fr[r][e] = X::from_f32(TAIL ? (ts + 4 * kq + r < N ? f : 0.0f) : f);
+                    }
+                    if constexpr (Sh::kRowK) {
                         F8<E> t;
 #pragma unroll
                         for (int e = 0; e < 8; ++e) t.x[e] = fr[r][e];
-                        *reinterpret_cast<F8<E>*>(sK + kidx(4 * kq + r, cg)) = t;
+                        *reinterpret_cast<F8<E>*>(sK + tile_off<D>(4 * kq + r, 8 * cg)) = t;
                     }
                 }
-                float dec[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    dec[r] = GATED ? fast_exp2(fminf(lam_last - sLam[4 * kq + r], 0.0f)) : 1.0f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    F4<E> t;
+                if constexpr (Sh::kKT) {
+                    float dec[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        t.x[r] = GATED ? X::from_f32(X::to_f32(fr[r][e]) * dec[r]) : fr[r][e];
-                    *reinterpret_cast<F4<E>*>(sKt + tidx(8 * cg + e, kq >> 1) + 4 * (kq & 1)) = t;
+                        dec[r] = GATED ? fast_exp2(fminf(lam_last - sLam[4 * kq + r], 0.0f)) : 1.0f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        F4<E> t;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            t.x[r] = GATED ? X::from_f32(X::to_f32(fr[r][e]) * dec[r]) : fr[r][e];
+                        *reinterpret_cast<F4<E>*>(sKt + tidx(8 * cg + e, kq >> 1) + 4 * (kq & 1)) = t;
+                    }
                 }
             }
         }
@@ -306,7 +387,16 @@ struct ChunkWalker {
                 for (int e = 0; e < 8; ++e) fq[m][ks].x[e] = X::from_f32(phi(X::to_f32(Q.rq[m][ks].x[e])));
     }
 
-    // S^T (operand precision) and z into LDS for the carried-state part.
+    // The two zero rows of the split-z operand; written once, before the first barrier.
+    __device__ __forceinline__ void clear_zb() const {
+        constexpr int NU = 2 * D * int(sizeof(E)) / 16;
+        if (tid < NU)
+            *reinterpret_cast<F8<uint16_t>*>(reinterpret_cast<unsigned char*>(sZb + 2 * D) + 16 * tid) =
+                zero8<uint16_t>();
+    }
+
+    // S^T (operand precision) and z = z_hi + z_lo (operand precision each) into LDS for
+    // the carried-state part.
     __device__ __forceinline__ void stage_state(const f32x4_t (&sacc)[Sh::TPW], const f32x4_t (&zacc)[Sh::ZT]) const {
 #pragma unroll
         for (int i = 0; i < Sh::ZT; ++i) {
@@ -318,11 +408,20 @@ struct ChunkWalker {
                 for (int r = 0; r < 4; ++r) t.x[r] = X::from_f32(sacc[i * Sh::NB + b][r]);
                 *reinterpret_cast<F4<E>*>(sSt + (16 * b + l16) * LS + 16 * a + 4 * g4) = t;
             }
-            if (l16 == 0) *reinterpret_cast<f32x4_t*>(sZ + 16 * a + 4 * g4) = zacc[i];
+            if (l16 == 0) {
+                F4<E> hi, lo;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    hi.x[r] = X::from_f32(zacc[i][r]);
+                    lo.x[r] = X::from_f32(zacc[i][r] - X::to_f32(hi.x[r]));
+                }
+                *reinterpret_cast<F4<E>*>(sZb + 16 * a + 4 * g4) = hi;
+                *reinterpret_cast<F4<E>*>(sZb + D + 16 * a + 4 * g4) = lo;
+            }
         }
     }
 
-    // State fold: S = 2^lam_last S + Fk^T V (Fk^T already decayed), z alike.
+    // State fold: S = 2^lam_last S + Fk^T V (Fk^T decayed when gated), z alike.
     __device__ __forceinline__ void fold(f32x4_t (&sacc)[Sh::TPW], f32x4_t (&zacc)[Sh::ZT], float lam_last) const {
         if constexpr (GATED) {
             const float dl = fast_exp2(lam_last);
@@ -342,7 +441,11 @@ struct ChunkWalker {
 #pragma unroll
             for (int i = 0; i < Sh::ZT; ++i) {
                 const int a = w * Sh::ZT + i;
-                const F8<E> ka = lds_f8(sKt + tidx(16 * a + l16, 4 * kbk + g4));
+                F8<E> ka;
+                if constexpr (Sh::kKT)
+                    ka = lds_f8(sKt + tidx(16 * a + l16, 4 * kbk + g4));
+                else
+                    ka = tr_operand<D>(sK, 32 * kbk + 8 * g4, 16 * a, l16);
 #pragma unroll
                 for (int b = 0; b < Sh::NB; ++b) sacc[i * Sh::NB + b] = mma(ka, vf[b], sacc[i * Sh::NB + b]);
                 zacc[i] = mma(ka, ones, zacc[i]);
@@ -352,51 +455,95 @@ struct ChunkWalker {
 
     // Walk chunks c0 .. c0+nch-1 of the head, folding each into (sacc, zacc); with OUT
     // also form and store the outputs (S^T and z must then already be staged in LDS).
-    // K and V of the next chunk are loaded right after this chunk is staged (or, with
-    // two register sets, at the top of the chunk); Q of the next chunk is loaded once
-    // this chunk's outputs no longer need the single Q set.  The last chunk's fold is
-    // skipped when FOLD_LAST is false.
-    template <bool OUT, bool FOLD_LAST>
+    // One register set: K and V of the next chunk are loaded right after this chunk is
+    // staged, Q of the next chunk once this chunk's outputs no longer need it.  Those
+    // loads are issued on every chunk, the last included (they then reread the range's
+    // last row), so the wait counts the compiler derives stay exact and nothing waits
+    // for a prefetch before its data is used.  The last chunk is folded only when
+    // fold_last is set.
     __device__ __forceinline__ void walk(int c0, int nch, f32x4_t (&sacc)[Sh::TPW], f32x4_t (&zacc)[Sh::ZT],
-                                         float& lg_total, E* ob, float eps) const {
-        constexpr bool kTwo = LINATTN_KV_SETS == 2;
-        Regs ra, rb_store;
-        Regs& rb = kTwo ? rb_store : ra;
+                                         float& lg_total, const OutRsrc& ob, float eps, bool fold_last) {
+        if (nch <= 0) return;
+        last = min(N, (c0 + nch) * CH) - 1;
+        Regs R;
         QRegs qr;
-        auto step = [&](Regs& cur, Regs& nxt, int n) {
+        load(R, c0 * CH);
+        if constexpr (OUT) load_q(qr, c0 * CH);
+        for (int n = 0; n < nch; ++n) {
             const int ts = (c0 + n) * CH;
-            const bool more = n + 1 < nch;
-            if (kTwo && more) load(nxt, ts + CH);
             if constexpr (GATED) {
-                lambda(cur);
+                lambda(R);
                 __syncthreads();
             }
             const float lam_last = GATED ? sLam[CH - 1] : 0.0f;
-            stage<OUT>(cur, ts, lam_last);
+            if (ts + CH <= N)
+                stage<false>(R, ts, lam_last);
+            else
+                stage<true>(R, ts, lam_last);
             F8<E> fq[Sh::MAXS][D / 32];
             if constexpr (OUT) phi_q(qr, fq);
-            if (!kTwo && more) load(nxt, ts + CH);
+            load(R, ts + CH);
             __syncthreads();
             if constexpr (OUT) {
                 outputs(fq, ts, ob, eps);
-                if (more) load_q(qr, ts + CH);
+                load_q(qr, ts + CH);
             }
-            if (FOLD_LAST || more) fold(sacc, zacc, lam_last);
+            const bool more = n + 1 < nch;
+            if (more || fold_last) fold(sacc, zacc, lam_last);
             lg_total += lam_last;
             __syncthreads();
             if (OUT && more) stage_state(sacc, zacc);
-        };
-        if (nch <= 0) return;
-        load(ra, c0 * CH);
-        if constexpr (OUT) load_q(qr, c0 * CH);
-        for (int n = 0; n < nch; n += 2) {
-            step(ra, rb, n);
-            if (n + 1 < nch) step(rb, ra, n + 1);
         }
     }
 
+    // One 32-key block p of the causal part for query strip s (query row qi of this
+    // lane): A^T tiles, decay and mask (DIAG: the block holding the diagonal), then
+    // O^T += V^T A^T and the denominator tile += ones A^T.
+    template <bool DIAG>
+    __device__ __forceinline__ void pair(int p, int qi, float lam_q, const F8<E> (&fqm)[D / 32], const F8<E>& ones_a,
+                                         f32x4_t (&acc)[DV / 16], f32x4_t& accd) const {
+        // Row m of the first A^T tile is key 8(m/4) + m%4 of the block and row m of the
+        // second is that key + 4, so lane group g holds keys 8g..8g+7 of the block.
+        const int krow = 8 * (l16 >> 2) + (l16 & 3);
+        f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+            a0 = mma(lds_f8(sK + tile_off<D>(32 * p + krow, 32 * ks + 8 * g4)), fqm[ks], a0);
+            a1 = mma(lds_f8(sK + tile_off<D>(32 * p + krow + 4, 32 * ks + 8 * g4)), fqm[ks], a1);
+        }
+        f32x4_t l0 = {0.f, 0.f, 0.f, 0.f}, l1 = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (GATED) {
+            l0 = *reinterpret_cast<const f32x4_t*>(sLam + 32 * p + 8 * g4);
+            l1 = *reinterpret_cast<const f32x4_t*>(sLam + 32 * p + 8 * g4 + 4);
+        }
+        F8<E> bA;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float x0 = a0[r], x1 = a1[r];
+            if constexpr (GATED) {
+                x0 *= fast_exp2(fminf(lam_q - l0[r], 0.0f));
+                x1 *= fast_exp2(fminf(lam_q - l1[r], 0.0f));
+            }
+            if constexpr (DIAG) {
+                const int k0 = 32 * p + 8 * g4 + r;
+                x0 = k0 <= qi ? x0 : 0.0f;
+                x1 = k0 + 4 <= qi ? x1 : 0.0f;
+            }
+            bA.x[r] = X::from_f32(x0);
+            bA.x[4 + r] = X::from_f32(x1);
+        }
+#pragma unroll
+        for (int t = 0; t < DV / 16; ++t) acc[t] = mma(lds_f8(sVt + tidx(16 * t + l16, 4 * p + g4)), bA, acc[t]);
+        accd = mma(ones_a, bA, accd);
+    }
+
     // Outputs of the chunk starting at ts for this wave's query strips.
-    __device__ __forceinline__ void outputs(const F8<E> (&fq)[Sh::MAXS][D / 32], int ts, E* ob, float eps) const {
+    __device__ __forceinline__ void outputs(const F8<E> (&fq)[Sh::MAXS][D / 32], int ts, const OutRsrc& ob,
+                                            float eps) const {
+        F8<E> ones_a;                  // rows 0, 4, 8, 12 of the denominator's A operand
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ones_a.x[e] = X::from_f32((l16 & 3) == 0 ? 1.0f : 0.0f);
+        const E* zrow = sZb + (l16 & 3) * D;   // z_hi, z_lo, 0, 0 by row mod 4
 #pragma unroll
         for (int m = 0; m < Sh::MAXS; ++m) {
             const int s = strip_of<Sh::NSTRIP>(w, m);
@@ -405,20 +552,14 @@ struct ChunkWalker {
             f32x4_t acc[DV / 16];
 #pragma unroll
             for (int t = 0; t < DV / 16; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            // carried-state part: O^T += S^T Fq^T ; den += Fq . z
-            float den = 0.0f;
+            f32x4_t accd = {0.f, 0.f, 0.f, 0.f};
+            // carried-state part: O^T += S^T Fq^T ; den += z^T Fq^T
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks) {
 #pragma unroll
                 for (int t = 0; t < DV / 16; ++t)
                     acc[t] = mma(lds_f8(sSt + (16 * t + l16) * LS + 32 * ks + 8 * g4), fq[m][ks], acc[t]);
-                const f32x4_t z0 = *reinterpret_cast<const f32x4_t*>(sZ + 32 * ks + 8 * g4);
-                const f32x4_t z1 = *reinterpret_cast<const f32x4_t*>(sZ + 32 * ks + 8 * g4 + 4);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    den += X::to_f32(fq[m][ks].x[e]) * z0[e];
-                    den += X::to_f32(fq[m][ks].x[4 + e]) * z1[e];
-                }
+                accd = mma(lds_f8(zrow + 32 * ks + 8 * g4), fq[m][ks], accd);
             }
             float lam_q = 0.0f;
             if constexpr (GATED) {
@@ -426,73 +567,38 @@ struct ChunkWalker {
                 const float sc = fast_exp2(lam_q);
 #pragma unroll
                 for (int t = 0; t < DV / 16; ++t) acc[t] *= sc;
-                den *= sc;
+                accd *= sc;
             }
-            // causal part: key blocks of 32 up to the diagonal.  Row m of the first A^T
-            // tile is key 8(m/4) + m%4 of the block and row m of the second is that key
-            // + 4, so lane group g holds keys 8g..8g+7 of the block: a B operand of
-            // consecutive keys, matched by one 16-byte V^T read.
             const int npairs = s / 2 + 1;
-            const int krow = 8 * (l16 >> 2) + (l16 & 3);
-            for (int p = 0; p < npairs; ++p) {
-                f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < D / 32; ++ks) {
-                    a0 = mma(lds_f8(sK + kidx(32 * p + krow, 4 * ks + g4)), fq[m][ks], a0);
-                    a1 = mma(lds_f8(sK + kidx(32 * p + krow + 4, 4 * ks + g4)), fq[m][ks], a1);
-                }
-                F8<E> bA;
-                float rs = 0.0f;
-                f32x4_t l0 = {0.f, 0.f, 0.f, 0.f}, l1 = {0.f, 0.f, 0.f, 0.f};
-                if constexpr (GATED) {
-                    l0 = *reinterpret_cast<const f32x4_t*>(sLam + 32 * p + 8 * g4);
-                    l1 = *reinterpret_cast<const f32x4_t*>(sLam + 32 * p + 8 * g4 + 4);
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int k0 = 32 * p + 8 * g4 + r, k1 = k0 + 4;
-                    float x0 = a0[r], x1 = a1[r];
-                    if constexpr (GATED) {
-                        x0 *= fast_exp2(fminf(lam_q - l0[r], 0.0f));
-                        x1 *= fast_exp2(fminf(lam_q - l1[r], 0.0f));
-                    }
-                    x0 = k0 <= qi ? x0 : 0.0f;
-                    x1 = k1 <= qi ? x1 : 0.0f;
-                    const E e0 = X::from_f32(x0), e1 = X::from_f32(x1);
-                    bA.x[r] = e0;
-                    bA.x[4 + r] = e1;
-                    rs += X::to_f32(e0) + X::to_f32(e1);
-                }
-                den += rs;
-#pragma unroll
-                for (int t = 0; t < DV / 16; ++t)
-                    acc[t] = mma(lds_f8(sVt + tidx(16 * t + l16, 4 * p + g4)), bA, acc[t]);
-            }
-            den += __shfl_xor(den, 16, kWave);
-            den += __shfl_xor(den, 32, kWave);
-            const float inv = 1.0f / fmaxf(den, eps);
+            for (int p = 0; p + 1 < npairs; ++p) pair<false>(p, qi, lam_q, fq[m], ones_a, acc, accd);
+            pair<true>(npairs - 1, qi, lam_q, fq[m], ones_a, acc, accd);
+            const float inv = __builtin_amdgcn_rcpf(fmaxf(accd[0] + accd[1], eps));
+            // rows past N fall outside the output resource and are dropped by the hardware
             const int row = ts + qi;
-            if (row < N) {
 #pragma unroll
-                for (int t = 0; t < DV / 16; ++t) {
-                    F4<E> outv;
+            for (int t = 0; t < DV / 16; ++t) {
+                F4<E> outv;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) outv.x[r] = X::from_f32(acc[t][r] * inv);
-                    *reinterpret_cast<F4<E>*>(ob + size_t(row) * DV + 16 * t + 4 * g4) = outv;
-                }
+                for (int r = 0; r < 4; ++r) outv.x[r] = X::from_f32(acc[t][r] * inv);
+                ob.store(outv, (row * DV + 16 * t + 4 * g4) * int(sizeof(E)));
             }
         }
     }
 };
 
+// Accumulator-layout element r of state tile j of wave w, lane (l16, g4):
+// S[16a + 4 g4 + r][16b + l16] with a = w ZT + j / NB, b = j % NB; z tile i of wave w
+// holds z[16(w ZT + i) + 4 g4 + r] in its l16 == 0 lanes (zero elsewhere).
 template <typename E, int D, int DV, int CH, bool GATED, bool OUTPUT>
-__global__ __launch_bounds__(kThreads) void walk_kernel(WalkArgs args) {
-    using Sh = WalkShape<E, D, DV, CH>;
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
+    walk_waves<E, D, DV, CH, GATED, OUTPUT>(), walk_waves<E, D, DV, CH, GATED, OUTPUT>()))) void walk_kernel(WalkArgs args) {
+    using Sh = WalkShape<E, D, DV, CH, GATED, OUTPUT>;
     using W = ChunkWalker<E, D, DV, CH, GATED, OUTPUT>;
     extern __shared__ __align__(16) unsigned char smem[];
 
-    const int seg = blockIdx.x % args.nseg;
-    const int bh = blockIdx.x / args.nseg;
+    const int nsw = OUTPUT ? args.nseg : args.nseg - 1;    // the totals skip the last segment
+    const int seg = blockIdx.x % nsw;
+    const int bh = blockIdx.x / nsw;
     const int N = args.N;
     const int nchunks_total = (N + CH - 1) / CH;
     const int c0 = seg * args.L;
@@ -502,50 +608,94 @@ __global__ __launch_bounds__(kThreads) void walk_kernel(WalkArgs args) {
     wk.init(smem, N, reinterpret_cast<const E*>(args.q) + size_t(bh) * N * D,
             reinterpret_cast<const E*>(args.k) + size_t(bh) * N * D,
             reinterpret_cast<const E*>(args.v) + size_t(bh) * N * DV, GATED ? args.g + size_t(bh) * N : nullptr);
-    E* ob = OUTPUT ? reinterpret_cast<E*>(args.o) + size_t(bh) * N * DV : nullptr;
-    float* stp = args.st + (size_t(bh) * args.nseg + seg) * (D * DV);
-    float* ztp = args.zt + (size_t(bh) * args.nseg + seg) * D;
+    const int w = wk.w, lane = wk.lane, l16 = wk.l16, g4 = wk.g4;
+    OutRsrc ob;
+    if constexpr (OUTPUT) ob.init(reinterpret_cast<E*>(args.o) + size_t(bh) * N * DV, unsigned(N) * DV * sizeof(E));
+    const size_t slot0 = size_t(bh) * args.nseg;
+    auto st_at = [&](int s, int j) {
+        return args.st + (slot0 + s) * (D * DV) + ((w * Sh::TPW + j) * kWave + lane) * 4;
+    };
+    auto zt_at = [&](int s, int i) { return args.zt + (slot0 + s) * D + 16 * (w * Sh::ZT + i) + 4 * g4; };
+    auto get4 = [](const float* p) { return *reinterpret_cast<const f32x4_t*>(p); };
+    const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
 
-    // persistent state in accumulator tiles
     f32x4_t sacc[Sh::TPW];
     f32x4_t zacc[Sh::ZT];
-    if (OUTPUT) {
 #pragma unroll
-        for (int j = 0; j < Sh::TPW; ++j)
-            sacc[j] = *reinterpret_cast<const f32x4_t*>(stp + ((wk.w * Sh::TPW + j) * kWave + wk.lane) * 4);
+    for (int j = 0; j < Sh::TPW; ++j) sacc[j] = zero4;
 #pragma unroll
-        for (int i = 0; i < Sh::ZT; ++i) {
-            const f32x4_t zv = *reinterpret_cast<const f32x4_t*>(ztp + 16 * (wk.w * Sh::ZT + i) + 4 * wk.g4);
-            zacc[i] = wk.l16 == 0 ? zv : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < Sh::ZT; ++i) zacc[i] = zero4;
+    const bool final_seg = seg == args.nseg - 1;
+
+    if constexpr (OUTPUT) {
+        // P_seg: from S0 and the totals in front (direct) or from the scanned slot.
+        if (args.direct || seg == 0) {
+            if (args.s0) {
+                const float* s0b = args.s0 + size_t(bh) * D * DV;
+#pragma unroll
+                for (int j = 0; j < Sh::TPW; ++j) {
+                    const int u = w * Sh::TPW + j;
+                    const int a = u / Sh::NB, b = u % Sh::NB;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sacc[j][r] = s0b[size_t(16 * a + 4 * g4 + r) * DV + 16 * b + l16];
+                }
+            }
+            if (args.z0) {
+                const float* z0b = args.z0 + size_t(bh) * D;
+#pragma unroll
+                for (int i = 0; i < Sh::ZT; ++i) {
+                    const f32x4_t zv = get4(z0b + 16 * (w * Sh::ZT + i) + 4 * g4);
+                    zacc[i] = l16 == 0 ? zv : zero4;
+                }
+            }
+            if (args.direct) {
+                const float* lgb = args.lg + slot0;
+#pragma unroll 2
+                for (int s = 0; s < seg; ++s) {
+                    const float f = GATED ? fast_exp2(lgb[s]) : 1.0f;
+#pragma unroll
+                    for (int j = 0; j < Sh::TPW; ++j) sacc[j] = f * sacc[j] + get4(st_at(s, j));
+#pragma unroll
+                    for (int i = 0; i < Sh::ZT; ++i) {
+                        const f32x4_t zv = get4(zt_at(s, i));
+                        zacc[i] = f * zacc[i] + (l16 == 0 ? zv : zero4);
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < Sh::TPW; ++j) sacc[j] = get4(st_at(seg - 1, j));
+#pragma unroll
+            for (int i = 0; i < Sh::ZT; ++i) {
+                const f32x4_t zv = get4(zt_at(seg - 1, i));
+                zacc[i] = l16 == 0 ? zv : zero4;
+            }
         }
+        wk.clear_zb();
         wk.stage_state(sacc, zacc);
-    } else {
-#pragma unroll
-        for (int j = 0; j < Sh::TPW; ++j) sacc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < Sh::ZT; ++i) zacc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
     float lg_total = 0.0f;
+    const bool keep = !OUTPUT || (final_seg && args.want_final);
 
-    wk.template walk<OUTPUT, !OUTPUT>(c0, nch, sacc, zacc, lg_total, ob, args.eps);
+    wk.walk(c0, nch, sacc, zacc, lg_total, ob, args.eps, keep);
 
-    if (!OUTPUT) {
+    if (keep) {
 #pragma unroll
-        for (int j = 0; j < Sh::TPW; ++j)
-            *reinterpret_cast<f32x4_t*>(stp + ((wk.w * Sh::TPW + j) * kWave + wk.lane) * 4) = sacc[j];
+        for (int j = 0; j < Sh::TPW; ++j) *reinterpret_cast<f32x4_t*>(st_at(seg, j)) = sacc[j];
 #pragma unroll
         for (int i = 0; i < Sh::ZT; ++i)
-            if (wk.l16 == 0) *reinterpret_cast<f32x4_t*>(ztp + 16 * (wk.w * Sh::ZT + i) + 4 * wk.g4) = zacc[i];
-        if (GATED && wk.tid == 0) args.lg[size_t(bh) * args.nseg + seg] = lg_total;
+            if (l16 == 0) *reinterpret_cast<f32x4_t*>(zt_at(seg, i)) = zacc[i];
+        if (!OUTPUT && GATED && wk.tid == 0) args.lg[slot0 + seg] = lg_total;
     }
 }
 
-// Exclusive prefix of segment totals, in place, one thread per state element.
+// In place over the totals of segments 0 .. nseg-2 of every head: slot s becomes
+// P_{s+1} = 2^lg_s P_s + T_s with P_0 = S0 (fp32), one thread per state element.
 // Element e < D*Dv is in accumulator layout: tile u = e / 256 (a = u / (Dv/16),
 // b = u % (Dv/16)), lane = (e / 4) % 64, r = e % 4, which is S[16a + 4(lane/16) + r][16b + lane%16].
 template <int D, int DV, bool GATED>
 __global__ __launch_bounds__(kThreads) void scan_kernel(float* st, float* zt, const float* lg, const float* s0,
-                                                       const float* z0, float* s_out, float* z_out, int nseg) {
+                                                       const float* z0, int nseg) {
     constexpr int NS = D * DV;
     constexpr int NBLK = (NS + D + kThreads - 1) / kThreads;   // workgroups per head
     const int e = (blockIdx.x % NBLK) * kThreads + threadIdx.x;
@@ -555,7 +705,6 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(float* st, float* zt, co
     size_t stride;
     size_t uidx;      // index into the caller's [D][Dv] or [D] layout
     const float* init;
-    float* fin;
     if (e < NS) {
         const int u = e / 256, lane = (e / 4) % 64, r = e % 4;
         const int a = u / (DV / 16), b = u % (DV / 16);
@@ -564,35 +713,56 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(float* st, float* zt, co
         base = st + size_t(bh) * nseg * NS + e;
         stride = NS;
         init = s0;
-        fin = s_out;
     } else {
         const int d = e - NS;
         uidx = size_t(bh) * D + d;
         base = zt + size_t(bh) * nseg * D + d;
         stride = D;
         init = z0;
-        fin = z_out;
     }
     const float* lgb = GATED ? lg + size_t(bh) * nseg : nullptr;
+    const int n = nseg - 1;
     float acc = init ? init[uidx] : 0.0f;
     constexpr int U = 8;                         // loads in flight per thread
-    for (int s0i = 0; s0i < nseg; s0i += U) {
+    for (int s0i = 0; s0i < n; s0i += U) {
         float t[U], f[U];
 #pragma unroll
         for (int i = 0; i < U; ++i) {
-            const int s = min(s0i + i, nseg - 1);
+            const int s = min(s0i + i, n - 1);
             t[i] = base[size_t(s) * stride];
             f[i] = GATED ? fast_exp2(lgb[s]) : 1.0f;
         }
 #pragma unroll
         for (int i = 0; i < U; ++i) {
-            if (s0i + i < nseg) {
-                base[size_t(s0i + i) * stride] = acc;
+            if (s0i + i < n) {
                 acc = f[i] * acc + t[i];
+                base[size_t(s0i + i) * stride] = acc;
             }
         }
     }
-    if (fin) fin[uidx] = acc;
+}
+
+// S_N, z_N from slot nseg-1 (accumulator layout) into the caller's s_out / z_out.
+// A launch of its own, so s_out may alias s0 (every read of s0 is done by then).
+template <int D, int DV>
+__global__ __launch_bounds__(kThreads) void final_kernel(const float* st, const float* zt, int nseg, float* s_out,
+                                                        float* z_out) {
+    constexpr int NS = D * DV;
+    constexpr int NBLK = (NS + D + kThreads - 1) / kThreads;
+    const int e = (blockIdx.x % NBLK) * kThreads + threadIdx.x;
+    const int bh = blockIdx.x / NBLK;
+    if (e >= NS + D) return;
+    const size_t slot = size_t(bh) * nseg + (nseg - 1);
+    if (e < NS) {
+        if (!s_out) return;
+        const int u = e / 256, lane = (e / 4) % 64, r = e % 4;
+        const int a = u / (DV / 16), b = u % (DV / 16);
+        const int d = 16 * a + 4 * (lane / 16) + r, dv = 16 * b + lane % 16;
+        s_out[size_t(bh) * NS + size_t(d) * DV + dv] = st[slot * NS + e];
+    } else {
+        if (!z_out) return;
+        z_out[size_t(bh) * D + (e - NS)] = zt[slot * D + (e - NS)];
+    }
 }
 
 }  // namespace linattn

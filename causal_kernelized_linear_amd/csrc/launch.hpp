@@ -17,53 +17,43 @@ struct FwdLaunch {
     const float* z0;
     float* s_out;
     float* z_out;
-    void* ws;                // caller's workspace, carved by the dispatch (see fwd_workspace_bytes)
+    void* ws;                // caller's workspace, carved by fwd_workspace_layout
     int BH, N, D, Dv, chunk, nseg, L;
     float eps;
     hipStream_t stream;
     hipEvent_t prof[4];      // measurement hook: all NULL when unused
-    int algo;                // 1: three launches, 2: single pass with look-back
 };
 
 // Chunk sizes with kernel instantiations.
 inline bool chunk_is_built(int chunk) { return chunk == 32 || chunk == 64 || chunk == 128 || chunk == 256; }
 
-// Dynamic LDS bytes of the output walk for (element size, D, Dv, chunk); the
-// same formula as WalkShape::bytes(true).
-inline size_t walk_lds_bytes(int esize, int D, int Dv, int chunk) {
-    const int pe = 16 / esize;
-    return size_t(chunk) * (D + pe) * esize + size_t(D) * (chunk + pe) * esize + size_t(Dv) * (chunk + pe) * esize +
-           size_t(Dv) * (D + pe) * esize + size_t(D) * 4 + size_t(chunk) * 4;
+// Dynamic LDS bytes of the output walk for (element size, D, Dv, chunk, gated); the
+// same carve-up as WalkShape<..., OUT = true>::kBytes.  The row-major Fk tile is
+// always there; the transposed Fk^T copy only when gated or in fp32.
+inline size_t walk_lds_bytes(int esize, int D, int Dv, int chunk, bool gated) {
+    const size_t pe = 16 / esize, es = size_t(esize);
+    const bool kt = gated || esize != 2;
+    return size_t(chunk) * D * es + (kt ? size_t(D) * (chunk + pe) * es : 0) + size_t(Dv) * (chunk + pe) * es +
+           size_t(Dv) * (D + pe) * es + size_t(4) * D * es + size_t(chunk) * 4;
 }
 
 constexpr size_t kMaxLds = 160 * 1024;   // LDS per compute unit on gfx950
 
 inline size_t round_up256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Workspace of the three-launch path: totals/prefixes [BH][nseg][D*Dv], z [BH][nseg][D],
-// log2 decays [BH][nseg].
-inline size_t three_pass_bytes(size_t heads, int D, int Dv, size_t* off_zt, size_t* off_lg) {
-    const size_t st = round_up256(heads * size_t(D) * Dv * 4);
-    const size_t zt = round_up256(heads * size_t(D) * 4);
+// Workspace of the forward: per-segment states [BH][nseg][D*Dv], z [BH][nseg][D], log2
+// decays [BH][nseg] (float), each region 256-byte aligned.
+inline size_t fwd_workspace_layout(size_t slots, int D, int Dv, size_t* off_zt, size_t* off_lg) {
+    const size_t st = round_up256(slots * size_t(D) * Dv * 4);
+    const size_t zt = round_up256(slots * size_t(D) * 4);
     if (off_zt) *off_zt = st;
     if (off_lg) *off_lg = st + zt;
-    return st + zt + round_up256(heads * 4);
+    return st + zt + round_up256(slots * 4);
 }
 
-// Workspace of the single-pass path: two records per segment, then the flags and
-// the ticket counter.
-inline size_t fused_record_floats(int D, int Dv) { return size_t((D * Dv + D + 1 + 63) / 64) * 64; }
-inline size_t fused_bytes(size_t heads, int D, int Dv, size_t* off_flags) {
-    const size_t rec = round_up256(heads * 2 * fused_record_floats(D, Dv) * 4);
-    if (off_flags) *off_flags = rec;
-    return rec + round_up256((heads + 1) * 4);
-}
-
-inline size_t fwd_workspace_bytes(size_t heads, int D, int Dv) {
-    const size_t a = three_pass_bytes(heads, D, Dv, nullptr, nullptr);
-    const size_t b = fused_bytes(heads, D, Dv, nullptr);
-    return a > b ? a : b;
-}
+// The output walk sums the totals in front of its segment itself when they are few
+// and small (at most seven 64 x 64 states); otherwise a scan launch does it first.
+inline bool prefix_direct(int nseg, int D, int Dv) { return size_t(nseg - 1) * D * Dv <= size_t(7) * 64 * 64; }
 
 hipError_t launch_fwd_bf16(const FwdLaunch& p);
 hipError_t launch_fwd_f32(const FwdLaunch& p);

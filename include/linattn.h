@@ -32,7 +32,7 @@
  *
  * Supported shapes on the GPU: D and Dv in {64, 128}; chunk in {32, 64, 128, 256}
  * when the chunk's on-chip tiles fit the 160 KiB LDS of a compute unit:
- *   bf16: every chunk, except 256 when D = 128;
+ *   bf16: every chunk, except 256 when D = Dv = 128, and 256 at D = 128 for the gated forward;
  *   f32:  chunk <= 128 at D = Dv = 64, <= 64 when one of D, Dv is 128, 32 when both are.
  * Other shapes return LINATTN_ERR_UNSUPPORTED.
  */
@@ -126,25 +126,12 @@ linattn_status_t linattn_decode_step(
     int B, int H, int D, int Dv, linattn_dtype_t dtype, float eps, void* stream);
 
 /*
- * Selects how later chunked and gated forwards of this process run (both compute the
- * same result up to rounding and need the same workspace):
- *   0  default (currently 1);
- *   1  three launches: per-segment state totals, an fp32 scan over segments, and an
- *      output walk that starts each segment from its scanned state;
- *   2  one pass: each workgroup publishes its segment's total, takes the state in
- *      front of its segment from its predecessors' published states (decoupled
- *      look-back) and then forms its outputs; a flag-clearing launch precedes it and,
- *      when s_out or z_out is given, a copy-out launch follows.
- * Returns LINATTN_ERR_INVALID_ARGUMENT for any other value.
- */
-linattn_status_t linattn_set_forward_algorithm(int algorithm);
-
-/*
  * Measurement hook, not part of the computation.  Arms the NEXT linattn_fwd_chunked or
  * linattn_fwd_gated call on this process to record four caller-created hipEvent_t
- * handles on its stream: ev0 before its first launch, ev1 after the first, ev2 after the
- * second, ev3 after the third (algorithm 1: totals walk, scan, output walk; algorithm 2:
- * flag clear, single-pass walk, state copy-out).  The first forward whose
+ * handles on its stream: ev0 before the segment-totals walk, ev1 after it, ev2 after the
+ * scan over segments, ev3 after the output walk and, when s_out or z_out is given, the
+ * final-state copy (a step that a shape does not need is skipped, so its two events
+ * bracket nothing).  The first forward whose
  * arguments pass validation consumes (and disarms) the hook; four NULLs disarm it.
  * Returns LINATTN_ERR_INVALID_ARGUMENT when only some handles are NULL.
  */

@@ -94,13 +94,6 @@ def test_fwd_rejects_bad_arguments(gated):
     assert fwd(N=0, q=0, k=0, v=0, o=0, ws=0, wsb=0, gated=gated) == OK
 
 
-def test_forward_algorithm_arguments():
-    assert binding.linattn_set_forward_algorithm(3) == INVALID
-    assert binding.linattn_set_forward_algorithm(-1) == INVALID
-    for a in (2, 1, 0):
-        assert binding.linattn_set_forward_algorithm(a) == OK
-
-
 def test_profile_hook_arguments():
     assert binding.linattn_set_profile_events(0, 0, 0, 0) == OK
     assert binding.linattn_set_profile_events(16, 0, 0, 0) == INVALID
