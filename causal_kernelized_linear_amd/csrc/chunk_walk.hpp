@@ -91,9 +91,9 @@ struct WalkShape {
     static constexpr bool kBf16 = sizeof(E) == 2;
     static constexpr bool kRowK = OUT;                         // row-major Fk tile
     static constexpr bool kKT = !OUT || GATED || !kBf16;       // transposed (decayed) Fk^T tile
-    static constexpr int PE = 16 / int(sizeof(E));   // 16-byte row padding, in elements
-    static constexpr int LKT = CH + PE;               // row stride of Fk^T [D][CH] and V^T [Dv][CH]
-    static constexpr int LS = D + PE;                 // row stride of S^T  [Dv][D]
+    static constexpr int LKT = CH + (CH == 32 ? 0 : 16);   // row stride of Fk^T [D][CH] and V^T [Dv][CH]
+    static constexpr int LS = D;                      // row stride of S^T [Dv][D] (groups swizzled)
+    static constexpr int LZ = D + 8;                  // row stride of the split z rows
     static constexpr int NSTRIP = CH / 16;
     static constexpr int MAXS = (NSTRIP + 3) / 4;     // query strips per wave
     static constexpr int NKU = (CH / 4) * (D / 8);    // staging units of K (4 rows x 8 columns)
@@ -111,7 +111,7 @@ struct WalkShape {
     static constexpr size_t kOffVt = kOffKt + (kKT ? size_t(D) * LKT * sizeof(E) : 0);
     static constexpr size_t kOffSt = kOffVt + size_t(DV) * LKT * sizeof(E);
     static constexpr size_t kOffZb = kOffSt + (OUT ? size_t(DV) * LS * sizeof(E) : 0);
-    static constexpr size_t kOffLam = kOffZb + (OUT ? size_t(4) * D * sizeof(E) : 0);
+    static constexpr size_t kOffLam = kOffZb + (OUT ? size_t(4) * LZ * sizeof(E) : 0);
     static constexpr size_t kBytes = kOffLam + size_t(CH) * 4;
 };
 
@@ -134,21 +134,40 @@ constexpr int walk_waves() {
 
 // Query strip handled by wave w in its m-th slot, or -1.
 template <int NSTRIP>
-__device__ __forceinline__ int strip_of(int w, int m) {
+__host__ __device__ constexpr int strip_of(int w, int m) {
     const int pair = m >> 1;
     const int s = (m & 1) ? (pair * 8 + 7 - w) : (pair * 8 + w);
     return s < NSTRIP ? s : -1;
 }
 
-// Row-major [rows][W] tile without padding whose 8-element groups are permuted per
-// row by ((row / 8) mod 2) ^ 2 (row mod 4).  The staging writes (4 rows x 8 columns
-// per thread), the A^T operand reads (16 rows in the key order of the transposed
-// products, one group) and the transpose reads (4 rows x 4 columns per 16 lanes) are
-// all free of LDS bank conflicts.
+// LDS layouts follow how gfx950 serves LDS, as measured with its bank-conflict counter:
+// 64 banks of 4 bytes for reads, a 16-byte read serving in one cycle the 16 lanes of a
+// 32-lane half whose lane bits 2..4 have the same parity, an 8-byte read (or transpose
+// read) 32 consecutive lanes; writes 128 bytes per cycle over 32 banks, 8 consecutive
+// lanes of a 16-byte write or 16 of an 8-byte one.  Every tile below is row-major with
+// its 8-element (16-byte) groups permuted per row as group ^ h(row); the h and the row
+// padding of each tile were found by searching that model over all of the tile's
+// accesses at every built shape.
+//
+// Row-major phi(K) tile [rows][W], no padding, h from row bits 1, 3 (W = 64) or 0, 1, 3
+// (W = 128): its staging writes, A^T operand reads (16 rows in the key order of the
+// transposed products) and transpose reads (4 rows x 4 columns per 16 lanes) are all
+// conflict-free.
 template <int W>
 __device__ __forceinline__ int tile_off(int row, int col) {
-    const int sw = ((row >> 3) & 1) ^ ((row & 3) << 1);
-    return row * W + ((((col >> 3) ^ sw) & (W / 8 - 1)) << 3) + (col & 7);
+    int h;
+    if constexpr (W == 64)
+        h = (((row >> 1) & 1) << 1) | (((row >> 3) & 1) << 2);
+    else
+        h = ((row & 1) << 1) | (((row >> 1) & 1) << 2) | (((row >> 3) & 1) << 3);
+    return row * W + ((((col >> 3) ^ h) & (W / 8 - 1)) << 3) + (col & 7);
+}
+
+// S^T tile [Dv][D], no padding, h = row mod (D / 8): conflict-free operand reads; the
+// 8-byte staging writes (once per chunk) take two cycles.
+template <int D>
+__device__ __forceinline__ int st_off(int row, int col) {
+    return row * D + ((((col >> 3) ^ row) & (D / 8 - 1)) << 3) + (col & 7);
 }
 
 // Key-major bf16 operand from a row-major tile_off<W> tile: slot e of lane l holds
@@ -212,7 +231,7 @@ struct ChunkWalker {
     E* sKt;
     E* sVt;
     E* sSt;
-    E* sZb;        // [4][D]: z high part, z low part, two zero rows
+    E* sZb;        // [4][LZ]: z high part, z low part, two zero rows
     float* sLam;
     int tid, w, lane, l16, g4;
     int N;
@@ -222,13 +241,26 @@ struct ChunkWalker {
     const E* vb;
     const float* gb;
 
-    // Fk^T and V^T rows are [CH] keys stored as 16-byte groups of 8 keys; group j of
-    // row r sits at slot j ^ ((r / 8) mod (CH / 8)).  The transposed writes of a wave
-    // (8 rows x 8 key quads) then spread over all banks, and the MFMA operand reads
-    // (16 consecutive rows, one group) stay conflict-free.
+    // Fk^T and V^T rows are [CH] keys in groups of 8 (16 bytes), padded by 16 elements
+    // (none at CH = 32); group j of row r sits at slot j ^ h(r).  The MFMA operand reads
+    // (16 consecutive rows, one group per lane group) are conflict-free at every shape;
+    // the transposed staging writes (4-key quads) take at most two cycles per 128 bytes
+    // (four at CH = 32 with 128 rows).
     static __device__ __forceinline__ int tidx(int row, int group) {
-        return row * LKT + ((group ^ ((row >> 3) & (CH / 8 - 1))) << 3);
+        int h;
+        if constexpr (CH == 32)
+            h = ((row >> 4) & 1) | (((row >> 3) & 1) << 1);
+        else if constexpr (CH == 64)
+            h = ((row >> 4) & 1) | (((row >> 5) & 1) << 1) | (((row >> 6) & 1) << 2);
+        else
+            h = ((row >> 3) & 7) | (((row >> 3) & 1) << 3);
+        return row * LKT + (((group ^ h) & (CH / 8 - 1)) << 3);
     }
+    // Rows of phi(K) held by staging unit kq, slot r: four consecutive keys when a
+    // transposed copy is written (one 8-byte quad per feature), else the strided rows
+    // kq, kq + CH/4, ... that tile_off serves without bank conflicts.
+    static constexpr bool kStridedK = !Sh::kKT;
+    static __device__ __forceinline__ int krow_of(int kq, int r) { return kStridedK ? kq + (CH / 4) * r : 4 * kq + r; }
 
     __device__ __forceinline__ void init(unsigned char* smem, int N_, const E* q, const E* k, const E* v,
                                          const float* g) {
@@ -261,7 +293,7 @@ struct ChunkWalker {
             const int cg = u % (D / 8), kq = (u / (D / 8)) % (CH / 4);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = min(ts + 4 * kq + r, last);
+                const int row = min(ts + krow_of(kq, r), last);
                 R.rk[it][r] = *reinterpret_cast<const F8<E>*>(kb + size_t(row) * D + 8 * cg);
             }
         }
@@ -337,13 +369,13 @@ struct ChunkWalker {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const float f = phi(X::to_f32(R.rk[it][r].x[e]));
-                        fr[r][e] = X::from_f32(TAIL ? (ts + 4 * kq + r < N ? f : 0.0f) : f);
+                        fr[r][e] = X::from_f32(TAIL ? (ts + krow_of(kq, r) < N ? f : 0.0f) : f);
                     }
                     if constexpr (Sh::kRowK) {
                         F8<E> t;
 #pragma unroll
                         for (int e = 0; e < 8; ++e) t.x[e] = fr[r][e];
-                        *reinterpret_cast<F8<E>*>(sK + tile_off<D>(4 * kq + r, 8 * cg)) = t;
+                        *reinterpret_cast<F8<E>*>(sK + tile_off<D>(krow_of(kq, r), 8 * cg)) = t;
                     }
                 }
                 if constexpr (Sh::kKT) {
@@ -389,9 +421,9 @@ struct ChunkWalker {
 
     // The two zero rows of the split-z operand; written once, before the first barrier.
     __device__ __forceinline__ void clear_zb() const {
-        constexpr int NU = 2 * D * int(sizeof(E)) / 16;
+        constexpr int NU = 2 * Sh::LZ * int(sizeof(E)) / 16;
         if (tid < NU)
-            *reinterpret_cast<F8<uint16_t>*>(reinterpret_cast<unsigned char*>(sZb + 2 * D) + 16 * tid) =
+            *reinterpret_cast<F8<uint16_t>*>(reinterpret_cast<unsigned char*>(sZb + 2 * Sh::LZ) + 16 * tid) =
                 zero8<uint16_t>();
     }
 
@@ -406,7 +438,7 @@ struct ChunkWalker {
                 F4<E> t;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) t.x[r] = X::from_f32(sacc[i * Sh::NB + b][r]);
-                *reinterpret_cast<F4<E>*>(sSt + (16 * b + l16) * LS + 16 * a + 4 * g4) = t;
+                *reinterpret_cast<F4<E>*>(sSt + st_off<D>(16 * b + l16, 16 * a + 4 * g4)) = t;
             }
             if (l16 == 0) {
                 F4<E> hi, lo;
@@ -416,7 +448,7 @@ struct ChunkWalker {
                     lo.x[r] = X::from_f32(zacc[i][r] - X::to_f32(hi.x[r]));
                 }
                 *reinterpret_cast<F4<E>*>(sZb + 16 * a + 4 * g4) = hi;
-                *reinterpret_cast<F4<E>*>(sZb + D + 16 * a + 4 * g4) = lo;
+                *reinterpret_cast<F4<E>*>(sZb + Sh::LZ + 16 * a + 4 * g4) = lo;
             }
         }
     }
@@ -496,9 +528,136 @@ struct ChunkWalker {
         }
     }
 
+    // Outputs of the chunk starting at ts for the query strips of wave WV (the variant
+    // used once D * Dv reaches 128 x 128).  The wave is a compile-time constant here, so its strips, their key-block counts and their
+    // diagonal blocks are too: the loops below unroll into straight-line code in which
+    // the strips' independent MFMA chains interleave.  Every S^T, phi(K) and V^T operand
+    // is read from LDS once per wave and used for all strips that need it.
+    //   carried part:  O^T += S^T Fq^T,  den += (z_hi, z_lo)^T Fq^T
+    //   causal part, per 32-key block p:  A^T = Fk Fq^T (two 16-key tiles whose rows are
+    //   ordered so lane group g holds keys 8g..8g+7), decay and, on the diagonal block
+    //   only, the causal mask; then O^T += V^T A^T and den += ones A^T.
+    template <int WV>
+    __device__ __forceinline__ void outputs_w(const F8<E> (&fq)[Sh::MAXS][D / 32], int ts, const OutRsrc& ob,
+                                              float eps) const {
+        constexpr int MS = Sh::MAXS, NT = DV / 16, KS = D / 32, MAXP = (Sh::NSTRIP + 1) / 2;
+        F8<E> ones_a;                  // rows 0, 4, 8, 12 of the denominator's A operand
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ones_a.x[e] = X::from_f32((l16 & 3) == 0 ? 1.0f : 0.0f);
+        const E* zrow = sZb + (l16 & 3) * Sh::LZ;   // z_hi, z_lo, 0, 0 by row mod 4
+        auto strip = [](int m) { return strip_of<Sh::NSTRIP>(WV, m); };
+        auto npairs = [&](int m) { return strip(m) < 0 ? 0 : strip(m) / 2 + 1; };
+        f32x4_t acc[MS][NT];
+        f32x4_t accd[MS];
+        float lam_q[MS];
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[m][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            accd[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            lam_q[m] = 0.0f;
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const F8<E> sop = lds_f8(sSt + st_off<D>(16 * t + l16, 32 * ks + 8 * g4));
+#pragma unroll
+                for (int m = 0; m < MS; ++m)
+                    if (strip(m) >= 0) acc[m][t] = mma(sop, fq[m][ks], acc[m][t]);
+            }
+            const F8<E> zop = lds_f8(zrow + 32 * ks + 8 * g4);
+#pragma unroll
+            for (int m = 0; m < MS; ++m)
+                if (strip(m) >= 0) accd[m] = mma(zop, fq[m][ks], accd[m]);
+        }
+        if constexpr (GATED) {
+#pragma unroll
+            for (int m = 0; m < MS; ++m) {
+                if (strip(m) < 0) continue;
+                lam_q[m] = sLam[16 * strip(m) + l16];
+                const float sc = fast_exp2(lam_q[m]);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) acc[m][t] *= sc;
+                accd[m] *= sc;
+            }
+        }
+        const int krow = 8 * (l16 >> 2) + (l16 & 3);
+#pragma unroll
+        for (int p = 0; p < MAXP; ++p) {
+            bool any = false;
+#pragma unroll
+            for (int m = 0; m < MS; ++m) any = any || p < npairs(m);
+            if (!any) continue;
+            F8<E> k0[KS], k1[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                k0[ks] = lds_f8(sK + tile_off<D>(32 * p + krow, 32 * ks + 8 * g4));
+                k1[ks] = lds_f8(sK + tile_off<D>(32 * p + krow + 4, 32 * ks + 8 * g4));
+            }
+            f32x4_t l0 = {0.f, 0.f, 0.f, 0.f}, l1 = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (GATED) {
+                l0 = *reinterpret_cast<const f32x4_t*>(sLam + 32 * p + 8 * g4);
+                l1 = *reinterpret_cast<const f32x4_t*>(sLam + 32 * p + 8 * g4 + 4);
+            }
+            F8<E> bA[MS];
+#pragma unroll
+            for (int m = 0; m < MS; ++m) {
+                if (p >= npairs(m)) continue;
+                f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    a0 = mma(k0[ks], fq[m][ks], a0);
+                    a1 = mma(k1[ks], fq[m][ks], a1);
+                }
+                const bool diag = p == npairs(m) - 1;
+                const int qi = 16 * strip(m) + l16;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float x0 = a0[r], x1 = a1[r];
+                    if constexpr (GATED) {
+                        x0 *= fast_exp2(fminf(lam_q[m] - l0[r], 0.0f));
+                        x1 *= fast_exp2(fminf(lam_q[m] - l1[r], 0.0f));
+                    }
+                    if (diag) {
+                        const int kk = 32 * p + 8 * g4 + r;
+                        x0 = kk <= qi ? x0 : 0.0f;
+                        x1 = kk + 4 <= qi ? x1 : 0.0f;
+                    }
+                    bA[m].x[r] = X::from_f32(x0);
+                    bA[m].x[4 + r] = X::from_f32(x1);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const F8<E> vop = lds_f8(sVt + tidx(16 * t + l16, 4 * p + g4));
+#pragma unroll
+                for (int m = 0; m < MS; ++m)
+                    if (p < npairs(m)) acc[m][t] = mma(vop, bA[m], acc[m][t]);
+            }
+#pragma unroll
+            for (int m = 0; m < MS; ++m)
+                if (p < npairs(m)) accd[m] = mma(ones_a, bA[m], accd[m]);
+        }
+#pragma unroll
+        for (int m = 0; m < MS; ++m) {
+            if (strip(m) < 0) continue;
+            const float inv = __builtin_amdgcn_rcpf(fmaxf(accd[m][0] + accd[m][1], eps));
+            // rows past N fall outside the output resource and are dropped by the hardware
+            const int row = ts + 16 * strip(m) + l16;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                F4<E> outv;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) outv.x[r] = X::from_f32(acc[m][t][r] * inv);
+                ob.store(outv, (row * DV + 16 * t + 4 * g4) * int(sizeof(E)));
+            }
+        }
+    }
+
     // One 32-key block p of the causal part for query strip s (query row qi of this
-    // lane): A^T tiles, decay and mask (DIAG: the block holding the diagonal), then
-    // O^T += V^T A^T and the denominator tile += ones A^T.
+    // lane), for the strip-by-strip variant below: A^T tiles, decay and mask (DIAG: the
+    // block holding the diagonal), then O^T += V^T A^T and den += ones A^T.
     template <bool DIAG>
     __device__ __forceinline__ void pair(int p, int qi, float lam_q, const F8<E> (&fqm)[D / 32], const F8<E>& ones_a,
                                          f32x4_t (&acc)[DV / 16], f32x4_t& accd) const {
@@ -536,29 +695,28 @@ struct ChunkWalker {
         for (int t = 0; t < DV / 16; ++t) acc[t] = mma(lds_f8(sVt + tidx(16 * t + l16, 4 * p + g4)), bA, acc[t]);
         accd = mma(ones_a, bA, accd);
     }
-
-    // Outputs of the chunk starting at ts for this wave's query strips.
-    __device__ __forceinline__ void outputs(const F8<E> (&fq)[Sh::MAXS][D / 32], int ts, const OutRsrc& ob,
-                                            float eps) const {
+    // Outputs strip by strip with a runtime block loop: fewer live registers; the
+    // faster variant while the operand tiles are small (D * Dv below 128 x 128).
+    __device__ __forceinline__ void outputs_seq(const F8<E> (&fq)[Sh::MAXS][D / 32], int ts, const OutRsrc& ob,
+                                                float eps) const {
         F8<E> ones_a;                  // rows 0, 4, 8, 12 of the denominator's A operand
 #pragma unroll
         for (int e = 0; e < 8; ++e) ones_a.x[e] = X::from_f32((l16 & 3) == 0 ? 1.0f : 0.0f);
-        const E* zrow = sZb + (l16 & 3) * D;   // z_hi, z_lo, 0, 0 by row mod 4
+        const E* zrow = sZb + (l16 & 3) * Sh::LZ;   // z_hi, z_lo, 0, 0 by row mod 4
 #pragma unroll
         for (int m = 0; m < Sh::MAXS; ++m) {
             const int s = strip_of<Sh::NSTRIP>(w, m);
             if (s < 0) continue;
-            const int qi = 16 * s + l16;               // query row of this lane within the chunk
+            const int qi = 16 * s + l16;
             f32x4_t acc[DV / 16];
 #pragma unroll
             for (int t = 0; t < DV / 16; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             f32x4_t accd = {0.f, 0.f, 0.f, 0.f};
-            // carried-state part: O^T += S^T Fq^T ; den += z^T Fq^T
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks) {
 #pragma unroll
                 for (int t = 0; t < DV / 16; ++t)
-                    acc[t] = mma(lds_f8(sSt + (16 * t + l16) * LS + 32 * ks + 8 * g4), fq[m][ks], acc[t]);
+                    acc[t] = mma(lds_f8(sSt + st_off<D>(16 * t + l16, 32 * ks + 8 * g4)), fq[m][ks], acc[t]);
                 accd = mma(lds_f8(zrow + 32 * ks + 8 * g4), fq[m][ks], accd);
             }
             float lam_q = 0.0f;
@@ -581,6 +739,21 @@ struct ChunkWalker {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) outv.x[r] = X::from_f32(acc[t][r] * inv);
                 ob.store(outv, (row * DV + 16 * t + 4 * g4) * int(sizeof(E)));
+            }
+        }
+    }
+
+    // Outputs of the chunk starting at ts for this wave's query strips (w is uniform).
+    __device__ __forceinline__ void outputs(const F8<E> (&fq)[Sh::MAXS][D / 32], int ts, const OutRsrc& ob,
+                                            float eps) const {
+        if constexpr (D * DV < 128 * 128) {
+            outputs_seq(fq, ts, ob, eps);
+        } else {
+            switch (w) {
+                case 0: outputs_w<0>(fq, ts, ob, eps); break;
+                case 1: outputs_w<1>(fq, ts, ob, eps); break;
+                case 2: outputs_w<2>(fq, ts, ob, eps); break;
+                default: outputs_w<3>(fq, ts, ob, eps); break;
             }
         }
     }

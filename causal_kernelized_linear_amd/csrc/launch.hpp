@@ -31,10 +31,10 @@ inline bool chunk_is_built(int chunk) { return chunk == 32 || chunk == 64 || chu
 // same carve-up as WalkShape<..., OUT = true>::kBytes.  The row-major Fk tile is
 // always there; the transposed Fk^T copy only when gated or in fp32.
 inline size_t walk_lds_bytes(int esize, int D, int Dv, int chunk, bool gated) {
-    const size_t pe = 16 / esize, es = size_t(esize);
+    const size_t es = size_t(esize), lkt = size_t(chunk) + (chunk == 32 ? 0 : 16);
     const bool kt = gated || esize != 2;
-    return size_t(chunk) * D * es + (kt ? size_t(D) * (chunk + pe) * es : 0) + size_t(Dv) * (chunk + pe) * es +
-           size_t(Dv) * (D + pe) * es + size_t(4) * D * es + size_t(chunk) * 4;
+    return size_t(chunk) * D * es + (kt ? size_t(D) * lkt * es : 0) + size_t(Dv) * lkt * es + size_t(Dv) * D * es +
+           size_t(4) * (D + 8) * es + size_t(chunk) * 4;
 }
 
 constexpr size_t kMaxLds = 160 * 1024;   // LDS per compute unit on gfx950
