@@ -15,10 +15,48 @@ namespace {
 
 using linattn::FwdLaunch;
 
-// Workgroups the walk should offer the GPU (several per compute unit).  The
-// sequence of each head is split into nseg segments of L chunks so that
-// BH * nseg reaches this count when the sequence is long enough.
-constexpr long kTargetWorkgroups = 1024;
+// Compute units of the current device (cached per ordinal); 256, an MI355X's count,
+// when no device answers.
+int device_cus() {
+    static std::mutex mu;
+    static int cus[256];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+            (void)hipGetLastError();
+            n = 256;
+        }
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+// Workgroups of one round of the output walk: compute units times the workgroups each
+// holds at once.  Each head's sequence is split into nseg segments of L chunks so that
+// B*H*nseg reaches this count when the sequence is long enough: every workgroup is then
+// resident from the start, and the per-workgroup set-up (the state in front of the
+// segment, the first loads) is paid once.
+long target_workgroups(int esize, int D, int Dv, int chunk, bool gated) {
+    return long(device_cus()) * linattn::walk_waves(esize, D, Dv, chunk, gated, true);
+}
+
+// The largest target over the element types and both forwards: the workspace size does
+// not depend on them.
+long max_target_workgroups(int D, int Dv, int chunk) {
+    long t = 0;
+    for (int es : {2, 4})
+        for (bool gated : {false, true}) {
+            const long x = target_workgroups(es, D, Dv, chunk, gated);
+            t = x > t ? x : t;
+        }
+    return t;
+}
 
 struct Plan {
     int nseg = 0;
@@ -26,10 +64,12 @@ struct Plan {
     size_t bytes = 0;
 };
 
-Plan make_plan(long BH, int N, int D, int Dv, int chunk) {
+// nseg grows with the target (never shrinks), so the workspace sized for the largest
+// target serves every smaller one.
+Plan make_plan(long BH, int N, int D, int Dv, int chunk, long target) {
     Plan p;
     const long nc = (long(N) + chunk - 1) / chunk;
-    long nseg = (kTargetWorkgroups + BH - 1) / BH;
+    long nseg = (target + BH - 1) / BH;
     if (nseg < 1) nseg = 1;
     if (nseg > nc) nseg = nc;
     const long L = (nc + nseg - 1) / nseg;
@@ -111,7 +151,7 @@ linattn_status_t fwd_common(const void* q, const void* k, const void* v, const f
     if (!dim_ok(D) || !dim_ok(Dv) || !linattn::chunk_is_built(chunk) ||
         linattn::walk_lds_bytes(int(es), D, Dv, chunk, g != nullptr) > linattn::kMaxLds)
         return LINATTN_ERR_UNSUPPORTED;
-    const Plan plan = make_plan(BH, N, D, Dv, chunk);
+    const Plan plan = make_plan(BH, N, D, Dv, chunk, target_workgroups(int(es), D, Dv, chunk, g != nullptr));
     if (ws_bytes < plan.bytes || !ws || !aligned16(ws)) return LINATTN_ERR_WORKSPACE;
     const size_t ns = size_t(BH) * D * Dv * 4, nz = size_t(BH) * D * 4;
     if (overlap(ws, plan.bytes, q, nqk) || overlap(ws, plan.bytes, k, nqk) || overlap(ws, plan.bytes, v, nv) ||
@@ -142,7 +182,7 @@ extern "C" {
 
 size_t linattn_fwd_workspace_size(int B, int H, int N, int D, int Dv, int chunk) {
     if (B <= 0 || H <= 0 || N <= 0 || D <= 0 || Dv <= 0 || chunk <= 0) return 0;
-    return make_plan(long(B) * long(H), N, D, Dv, chunk).bytes;
+    return make_plan(long(B) * long(H), N, D, Dv, chunk, max_target_workgroups(D, Dv, chunk)).bytes;
 }
 
 linattn_status_t linattn_fwd_chunked(const void* q, const void* k, const void* v, void* o, const float* s0,

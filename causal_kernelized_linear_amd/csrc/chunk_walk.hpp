@@ -62,6 +62,7 @@
 #pragma once
 
 #include "device_common.hpp"
+#include "launch.hpp"
 
 namespace linattn {
 
@@ -113,24 +114,12 @@ struct WalkShape {
     static constexpr size_t kOffZb = kOffSt + (OUT ? size_t(DV) * LS * sizeof(E) : 0);
     static constexpr size_t kOffLam = kOffZb + (OUT ? size_t(4) * LZ * sizeof(E) : 0);
     static constexpr size_t kBytes = kOffLam + size_t(CH) * 4;
+    static_assert(kBytes == walk_lds_bytes(int(sizeof(E)), D, DV, CH, GATED, OUT), "host LDS formula out of step");
+    // waves per SIMD the kernel is compiled for (amdgpu_waves_per_eu): a fixed target keeps
+    // the compiler from squeezing registers for an occupancy the shape cannot reach, which
+    // would make it wait for the next chunk's loads early
+    static constexpr int kWaves = walk_waves(int(sizeof(E)), D, DV, CH, GATED, OUT);
 };
-
-// Waves per SIMD each walk kernel is compiled for (one wave of every workgroup sits on
-// each SIMD, so this is also workgroups per compute unit): what its LDS allows, capped
-// by the register budget its shape can live with (512 / waves registers per lane).  A
-// fixed target keeps the compiler from squeezing registers for an occupancy the shape
-// cannot reach, which would make it wait for the next chunk's loads early.
-template <typename E, int D, int DV, int CH, bool GATED, bool OUT>
-constexpr int walk_waves() {
-    constexpr size_t kLdsPerCu = 160 * 1024;
-    const int lds = int(kLdsPerCu / WalkShape<E, D, DV, CH, GATED, OUT>::kBytes);
-    const int work = D * DV * (sizeof(E) == 2 ? 1 : 2) * (CH > 128 ? 2 : 1);   // grows with the live tiles
-    int regs = 1;
-    if (work <= 64 * 64) regs = OUT ? 2 : 3;
-    else if (work <= 2 * 64 * 64) regs = OUT ? 1 : 2;
-    const int v = lds < regs ? lds : regs;
-    return v < 1 ? 1 : v;
-}
 
 // Query strip handled by wave w in its m-th slot, or -1.
 template <int NSTRIP>
@@ -493,14 +482,19 @@ struct ChunkWalker {
     // last row), so the wait counts the compiler derives stay exact and nothing waits
     // for a prefetch before its data is used.  The last chunk is folded only when
     // fold_last is set.
+    // prologue() runs once the first chunk's loads are in flight (the output walk forms
+    // the state in front of its segment there).
+    template <typename Prologue>
     __device__ __forceinline__ void walk(int c0, int nch, f32x4_t (&sacc)[Sh::TPW], f32x4_t (&zacc)[Sh::ZT],
-                                         float& lg_total, const OutRsrc& ob, float eps, bool fold_last) {
-        if (nch <= 0) return;
-        last = min(N, (c0 + nch) * CH) - 1;
+                                         float& lg_total, const OutRsrc& ob, float eps, bool fold_last,
+                                         Prologue&& prologue) {
+        last = min(N, (c0 + max(nch, 1)) * CH) - 1;
         Regs R;
         QRegs qr;
         load(R, c0 * CH);
         if constexpr (OUT) load_q(qr, c0 * CH);
+        prologue();
+        if (nch <= 0) return;
         for (int n = 0; n < nch; ++n) {
             const int ts = (c0 + n) * CH;
             if constexpr (GATED) {
@@ -764,7 +758,7 @@ struct ChunkWalker {
 // holds z[16(w ZT + i) + 4 g4 + r] in its l16 == 0 lanes (zero elsewhere).
 template <typename E, int D, int DV, int CH, bool GATED, bool OUTPUT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
-    walk_waves<E, D, DV, CH, GATED, OUTPUT>(), walk_waves<E, D, DV, CH, GATED, OUTPUT>()))) void walk_kernel(WalkArgs args) {
+    WalkShape<E, D, DV, CH, GATED, OUTPUT>::kWaves, WalkShape<E, D, DV, CH, GATED, OUTPUT>::kWaves))) void walk_kernel(WalkArgs args) {
     using Sh = WalkShape<E, D, DV, CH, GATED, OUTPUT>;
     using W = ChunkWalker<E, D, DV, CH, GATED, OUTPUT>;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -800,57 +794,60 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     for (int i = 0; i < Sh::ZT; ++i) zacc[i] = zero4;
     const bool final_seg = seg == args.nseg - 1;
 
-    if constexpr (OUTPUT) {
-        // P_seg: from S0 and the totals in front (direct) or from the scanned slot.
-        if (args.direct || seg == 0) {
-            if (args.s0) {
-                const float* s0b = args.s0 + size_t(bh) * D * DV;
+    // P_seg (output walk): from S0 and the totals in front (direct) or from the scanned
+    // slot, formed while the first chunk's loads are in flight.
+    auto prologue = [&]() {
+        if constexpr (OUTPUT) {
+            if (args.direct || seg == 0) {
+                if (args.s0) {
+                    const float* s0b = args.s0 + size_t(bh) * D * DV;
 #pragma unroll
-                for (int j = 0; j < Sh::TPW; ++j) {
-                    const int u = w * Sh::TPW + j;
-                    const int a = u / Sh::NB, b = u % Sh::NB;
+                    for (int j = 0; j < Sh::TPW; ++j) {
+                        const int u = w * Sh::TPW + j;
+                        const int a = u / Sh::NB, b = u % Sh::NB;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) sacc[j][r] = s0b[size_t(16 * a + 4 * g4 + r) * DV + 16 * b + l16];
+                        for (int r = 0; r < 4; ++r) sacc[j][r] = s0b[size_t(16 * a + 4 * g4 + r) * DV + 16 * b + l16];
+                    }
                 }
-            }
-            if (args.z0) {
-                const float* z0b = args.z0 + size_t(bh) * D;
+                if (args.z0) {
+                    const float* z0b = args.z0 + size_t(bh) * D;
+#pragma unroll
+                    for (int i = 0; i < Sh::ZT; ++i) {
+                        const f32x4_t zv = get4(z0b + 16 * (w * Sh::ZT + i) + 4 * g4);
+                        zacc[i] = l16 == 0 ? zv : zero4;
+                    }
+                }
+                if (args.direct) {
+                    const float* lgb = args.lg + slot0;
+#pragma unroll 2
+                    for (int s = 0; s < seg; ++s) {
+                        const float f = GATED ? fast_exp2(lgb[s]) : 1.0f;
+#pragma unroll
+                        for (int j = 0; j < Sh::TPW; ++j) sacc[j] = f * sacc[j] + get4(st_at(s, j));
+#pragma unroll
+                        for (int i = 0; i < Sh::ZT; ++i) {
+                            const f32x4_t zv = get4(zt_at(s, i));
+                            zacc[i] = f * zacc[i] + (l16 == 0 ? zv : zero4);
+                        }
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < Sh::TPW; ++j) sacc[j] = get4(st_at(seg - 1, j));
 #pragma unroll
                 for (int i = 0; i < Sh::ZT; ++i) {
-                    const f32x4_t zv = get4(z0b + 16 * (w * Sh::ZT + i) + 4 * g4);
+                    const f32x4_t zv = get4(zt_at(seg - 1, i));
                     zacc[i] = l16 == 0 ? zv : zero4;
                 }
             }
-            if (args.direct) {
-                const float* lgb = args.lg + slot0;
-#pragma unroll 2
-                for (int s = 0; s < seg; ++s) {
-                    const float f = GATED ? fast_exp2(lgb[s]) : 1.0f;
-#pragma unroll
-                    for (int j = 0; j < Sh::TPW; ++j) sacc[j] = f * sacc[j] + get4(st_at(s, j));
-#pragma unroll
-                    for (int i = 0; i < Sh::ZT; ++i) {
-                        const f32x4_t zv = get4(zt_at(s, i));
-                        zacc[i] = f * zacc[i] + (l16 == 0 ? zv : zero4);
-                    }
-                }
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < Sh::TPW; ++j) sacc[j] = get4(st_at(seg - 1, j));
-#pragma unroll
-            for (int i = 0; i < Sh::ZT; ++i) {
-                const f32x4_t zv = get4(zt_at(seg - 1, i));
-                zacc[i] = l16 == 0 ? zv : zero4;
-            }
+            wk.clear_zb();
+            wk.stage_state(sacc, zacc);
         }
-        wk.clear_zb();
-        wk.stage_state(sacc, zacc);
-    }
+    };
     float lg_total = 0.0f;
     const bool keep = !OUTPUT || (final_seg && args.want_final);
 
-    wk.walk(c0, nch, sacc, zacc, lg_total, ob, args.eps, keep);
+    wk.walk(c0, nch, sacc, zacc, lg_total, ob, args.eps, keep, prologue);
 
     if (keep) {
 #pragma unroll

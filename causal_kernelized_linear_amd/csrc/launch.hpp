@@ -27,17 +27,33 @@ struct FwdLaunch {
 // Chunk sizes with kernel instantiations.
 inline bool chunk_is_built(int chunk) { return chunk == 32 || chunk == 64 || chunk == 128 || chunk == 256; }
 
-// Dynamic LDS bytes of the output walk for (element size, D, Dv, chunk, gated); the
-// same carve-up as WalkShape<..., OUT = true>::kBytes.  The row-major Fk tile is
-// always there; the transposed Fk^T copy only when gated or in fp32.
-inline size_t walk_lds_bytes(int esize, int D, int Dv, int chunk, bool gated) {
+// Dynamic LDS bytes of a walk kernel for (element size, D, Dv, chunk, gated; out: the
+// output walk, else the totals walk).  WalkShape<...>::kBytes is checked against it.
+// The output walk always stages the row-major Fk tile, S^T and the split z rows; the
+// transposed Fk^T copy is staged by the totals walk and, gated or in fp32, by the
+// output walk too.
+constexpr size_t walk_lds_bytes(int esize, int D, int Dv, int chunk, bool gated, bool out = true) {
     const size_t es = size_t(esize), lkt = size_t(chunk) + (chunk == 32 ? 0 : 16);
-    const bool kt = gated || esize != 2;
-    return size_t(chunk) * D * es + (kt ? size_t(D) * lkt * es : 0) + size_t(Dv) * lkt * es + size_t(Dv) * D * es +
-           size_t(4) * (D + 8) * es + size_t(chunk) * 4;
+    const bool kt = !out || gated || esize != 2;
+    return (out ? size_t(chunk) * D * es : 0) + (kt ? size_t(D) * lkt * es : 0) + size_t(Dv) * lkt * es +
+           (out ? size_t(Dv) * D * es + size_t(4) * (D + 8) * es : 0) + size_t(chunk) * 4;
 }
 
 constexpr size_t kMaxLds = 160 * 1024;   // LDS per compute unit on gfx950
+
+// Waves per SIMD a walk kernel is compiled for (one wave of every workgroup sits on each
+// SIMD, so this is also its workgroups per compute unit): what its LDS allows, capped by
+// the register budget its shape can live with.  The plan sizes one round of the output
+// walk with it.
+constexpr int walk_waves(int esize, int D, int Dv, int chunk, bool gated, bool out) {
+    const int lds = int(kMaxLds / walk_lds_bytes(esize, D, Dv, chunk, gated, out));
+    const int work = D * Dv * (esize == 2 ? 1 : 2) * (chunk > 128 ? 2 : 1);   // grows with the live tiles
+    int regs = 1;
+    if (work <= 64 * 64) regs = out ? 2 : 3;
+    else if (work <= 2 * 64 * 64) regs = out ? 1 : 2;
+    const int v = lds < regs ? lds : regs;
+    return v < 1 ? 1 : v;
+}
 
 inline size_t round_up256(size_t x) { return (x + 255) / 256 * 256; }
 
