@@ -480,10 +480,10 @@ struct ChunkWalker {
     // staged, Q of the next chunk once this chunk's outputs no longer need it.  Those
     // loads are issued on every chunk, the last included (they then reread the range's
     // last row), so the wait counts the compiler derives stay exact and nothing waits
-    // for a prefetch before its data is used.  The last chunk is folded only when
-    // fold_last is set.
-    // prologue() runs once the first chunk's loads are in flight (the output walk forms
-    // the state in front of its segment there).
+    // for a prefetch before its data is used.  (A second register set, loading two
+    // chunks ahead, made the totals walk slower.)  The last chunk is folded only when
+    // fold_last is set.  prologue() runs once the first chunk's loads are in flight (the
+    // output walk forms the state in front of its segment there).
     template <typename Prologue>
     __device__ __forceinline__ void walk(int c0, int nch, f32x4_t (&sacc)[Sh::TPW], f32x4_t (&zacc)[Sh::ZT],
                                          float& lg_total, const OutRsrc& ob, float eps, bool fold_last,
@@ -494,7 +494,6 @@ struct ChunkWalker {
         load(R, c0 * CH);
         if constexpr (OUT) load_q(qr, c0 * CH);
         prologue();
-        if (nch <= 0) return;
         for (int n = 0; n < nch; ++n) {
             const int ts = (c0 + n) * CH;
             if constexpr (GATED) {
