@@ -92,7 +92,7 @@ struct WalkShape {
     static constexpr bool kBf16 = sizeof(E) == 2;
     static constexpr bool kRowK = OUT;                         // row-major Fk tile
     static constexpr bool kKT = !OUT || GATED || !kBf16;       // transposed (decayed) Fk^T tile
-    static constexpr int LKT = CH + (CH == 32 ? 0 : 16);   // row stride of Fk^T [D][CH] and V^T [Dv][CH]
+    static constexpr int LKT = CH + (CH >= 128 ? 16 : 0);  // row stride of Fk^T [D][CH] and V^T [Dv][CH]
     static constexpr int LS = D;                      // row stride of S^T [Dv][D] (groups swizzled)
     static constexpr int LZ = D + 8;                  // row stride of the split z rows
     static constexpr int NSTRIP = CH / 16;
@@ -152,12 +152,19 @@ __device__ __forceinline__ int tile_off(int row, int col) {
     return row * W + ((((col >> 3) ^ h) & (W / 8 - 1)) << 3) + (col & 7);
 }
 
-// S^T tile [Dv][D], no padding, h = row mod (D / 8): conflict-free operand reads; the
-// 8-byte staging writes (once per chunk) take two cycles.
+// S^T tile [Dv][D], no padding, h from row bits 0, 1, 3: the operand reads (rows in the
+// output tiles' dv order, out_dv) are conflict-free; the 8-byte staging writes (once per
+// chunk) take two cycles.
 template <int D>
 __device__ __forceinline__ int st_off(int row, int col) {
-    return row * D + ((((col >> 3) ^ row) & (D / 8 - 1)) << 3) + (col & 7);
+    const int h = (row & 3) | (((row >> 3) & 1) << 2) | (D == 128 ? ((row & 1) << 3) : 0);
+    return row * D + ((((col >> 3) ^ h) & (D / 8 - 1)) << 3) + (col & 7);
 }
+
+// Row m of O^T tile u holds dv = out_dv(u, m): tiles 2t and 2t+1 together hold the 8
+// consecutive dv 32t + 8(m/4) .. + 7 in lane group m/4, so each lane writes its output
+// row as 16-byte pieces.
+__device__ __forceinline__ int out_dv(int u, int m) { return 32 * (u >> 1) + 8 * (m >> 2) + 4 * (u & 1) + (m & 3); }
 
 // Key-major bf16 operand from a row-major tile_off<W> tile: slot e of lane l holds
 // tile[k0 + e][m0 + l % 16] (k0 includes the lane group's offset).  Each
@@ -193,9 +200,15 @@ struct OutRsrc {
         typedef int v2i __attribute__((ext_vector_type(2)));
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2i, v), r, off, 0, 0);
     }
-    __device__ __forceinline__ void store(const F4<float>& v, int off) const {
+    __device__ __forceinline__ void store(const F8<uint16_t>& v, int off) const {
         typedef int v4i __attribute__((ext_vector_type(4)));
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), r, off, 0, 0);
+    }
+    __device__ __forceinline__ void store(const F8<float>& v, int off) const {
+        typedef int v4i __attribute__((ext_vector_type(4)));
+        const v4i* h = reinterpret_cast<const v4i*>(&v);
+        __builtin_amdgcn_raw_buffer_store_b128(h[0], r, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(h[1], r, off + 16, 0, 0);
     }
 };
 
@@ -231,16 +244,17 @@ struct ChunkWalker {
     const float* gb;
 
     // Fk^T and V^T rows are [CH] keys in groups of 8 (16 bytes), padded by 16 elements
-    // (none at CH = 32); group j of row r sits at slot j ^ h(r).  The MFMA operand reads
-    // (16 consecutive rows, one group per lane group) are conflict-free at every shape;
-    // the transposed staging writes (4-key quads) take at most two cycles per 128 bytes
-    // (four at CH = 32 with 128 rows).
+    // from CH = 128 up; group j of row r sits at slot j ^ h(r).  The MFMA operand reads
+    // (16 consecutive rows for the fold, rows in out_dv order for A V, one group per lane
+    // group) are conflict-free at every shape; the transposed staging writes (4-key
+    // quads) take at most two cycles per 128 bytes at 64-row tiles, four at 128-row tiles
+    // below CH = 128.
     static __device__ __forceinline__ int tidx(int row, int group) {
         int h;
         if constexpr (CH == 32)
-            h = ((row >> 4) & 1) | (((row >> 3) & 1) << 1);
+            h = ((row >> 5) & 1) | (((row >> 3) & 1) << 1);
         else if constexpr (CH == 64)
-            h = ((row >> 4) & 1) | (((row >> 5) & 1) << 1) | (((row >> 6) & 1) << 2);
+            h = ((row >> 5) & 1) | (((row >> 1) & 1) << 1) | (((row >> 3) & 1) << 2);
         else
             h = ((row >> 3) & 7) | (((row >> 3) & 1) << 3);
         return row * LKT + (((group ^ h) & (CH / 8 - 1)) << 3);
@@ -522,7 +536,7 @@ struct ChunkWalker {
     }
 
     // Outputs of the chunk starting at ts for the query strips of wave WV (the variant
-    // used once D * Dv reaches 128 x 128).  The wave is a compile-time constant here, so its strips, their key-block counts and their
+    // used once D * Dv reaches 128 x 128, with one strip per wave).  The wave is a compile-time constant here, so its strips, their key-block counts and their
     // diagonal blocks are too: the loops below unroll into straight-line code in which
     // the strips' independent MFMA chains interleave.  Every S^T, phi(K) and V^T operand
     // is read from LDS once per wave and used for all strips that need it.
@@ -554,7 +568,7 @@ struct ChunkWalker {
         for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                const F8<E> sop = lds_f8(sSt + st_off<D>(16 * t + l16, 32 * ks + 8 * g4));
+                const F8<E> sop = lds_f8(sSt + st_off<D>(out_dv(t, l16), 32 * ks + 8 * g4));
 #pragma unroll
                 for (int m = 0; m < MS; ++m)
                     if (strip(m) >= 0) acc[m][t] = mma(sop, fq[m][ks], acc[m][t]);
@@ -623,7 +637,7 @@ struct ChunkWalker {
             }
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                const F8<E> vop = lds_f8(sVt + tidx(16 * t + l16, 4 * p + g4));
+                const F8<E> vop = lds_f8(sVt + tidx(out_dv(t, l16), 4 * p + g4));
 #pragma unroll
                 for (int m = 0; m < MS; ++m)
                     if (p < npairs(m)) acc[m][t] = mma(vop, bA[m], acc[m][t]);
@@ -639,11 +653,14 @@ struct ChunkWalker {
             // rows past N fall outside the output resource and are dropped by the hardware
             const int row = ts + 16 * strip(m) + l16;
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                F4<E> outv;
+            for (int t = 0; t < NT / 2; ++t) {
+                F8<E> outv;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) outv.x[r] = X::from_f32(acc[m][t][r] * inv);
-                ob.store(outv, (row * DV + 16 * t + 4 * g4) * int(sizeof(E)));
+                for (int r = 0; r < 4; ++r) {
+                    outv.x[r] = X::from_f32(acc[m][2 * t][r] * inv);
+                    outv.x[4 + r] = X::from_f32(acc[m][2 * t + 1][r] * inv);
+                }
+                ob.store(outv, (row * DV + 32 * t + 8 * g4) * int(sizeof(E)));
             }
         }
     }
@@ -685,11 +702,12 @@ struct ChunkWalker {
             bA.x[4 + r] = X::from_f32(x1);
         }
 #pragma unroll
-        for (int t = 0; t < DV / 16; ++t) acc[t] = mma(lds_f8(sVt + tidx(16 * t + l16, 4 * p + g4)), bA, acc[t]);
+        for (int t = 0; t < DV / 16; ++t) acc[t] = mma(lds_f8(sVt + tidx(out_dv(t, l16), 4 * p + g4)), bA, acc[t]);
         accd = mma(ones_a, bA, accd);
     }
     // Outputs strip by strip with a runtime block loop: fewer live registers; the
-    // faster variant while the operand tiles are small (D * Dv below 128 x 128).
+    // faster variant while the operand tiles are small (D * Dv below 128 x 128), and the
+    // one that fits the registers when a wave holds several strips of 128 x 128 tiles.
     __device__ __forceinline__ void outputs_seq(const F8<E> (&fq)[Sh::MAXS][D / 32], int ts, const OutRsrc& ob,
                                                 float eps) const {
         F8<E> ones_a;                  // rows 0, 4, 8, 12 of the denominator's A operand
@@ -709,7 +727,7 @@ struct ChunkWalker {
             for (int ks = 0; ks < D / 32; ++ks) {
 #pragma unroll
                 for (int t = 0; t < DV / 16; ++t)
-                    acc[t] = mma(lds_f8(sSt + st_off<D>(16 * t + l16, 32 * ks + 8 * g4)), fq[m][ks], acc[t]);
+                    acc[t] = mma(lds_f8(sSt + st_off<D>(out_dv(t, l16), 32 * ks + 8 * g4)), fq[m][ks], acc[t]);
                 accd = mma(lds_f8(zrow + 32 * ks + 8 * g4), fq[m][ks], accd);
             }
             float lam_q = 0.0f;
@@ -727,11 +745,14 @@ struct ChunkWalker {
             // rows past N fall outside the output resource and are dropped by the hardware
             const int row = ts + qi;
 #pragma unroll
-            for (int t = 0; t < DV / 16; ++t) {
-                F4<E> outv;
+            for (int t = 0; t < DV / 32; ++t) {
+                F8<E> outv;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) outv.x[r] = X::from_f32(acc[t][r] * inv);
-                ob.store(outv, (row * DV + 16 * t + 4 * g4) * int(sizeof(E)));
+                for (int r = 0; r < 4; ++r) {
+                    outv.x[r] = X::from_f32(acc[2 * t][r] * inv);
+                    outv.x[4 + r] = X::from_f32(acc[2 * t + 1][r] * inv);
+                }
+                ob.store(outv, (row * DV + 32 * t + 8 * g4) * int(sizeof(E)));
             }
         }
     }
@@ -739,7 +760,7 @@ struct ChunkWalker {
     // Outputs of the chunk starting at ts for this wave's query strips (w is uniform).
     __device__ __forceinline__ void outputs(const F8<E> (&fq)[Sh::MAXS][D / 32], int ts, const OutRsrc& ob,
                                             float eps) const {
-        if constexpr (D * DV < 128 * 128) {
+        if constexpr (D * DV < 128 * 128 || Sh::MAXS > 1) {
             outputs_seq(fq, ts, ob, eps);
         } else {
             switch (w) {

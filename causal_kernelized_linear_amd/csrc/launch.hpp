@@ -33,7 +33,7 @@ inline bool chunk_is_built(int chunk) { return chunk == 32 || chunk == 64 || chu
 // transposed Fk^T copy is staged by the totals walk and, gated or in fp32, by the
 // output walk too.
 constexpr size_t walk_lds_bytes(int esize, int D, int Dv, int chunk, bool gated, bool out = true) {
-    const size_t es = size_t(esize), lkt = size_t(chunk) + (chunk == 32 ? 0 : 16);
+    const size_t es = size_t(esize), lkt = size_t(chunk) + (chunk >= 128 ? 16 : 0);
     const bool kt = !out || gated || esize != 2;
     return (out ? size_t(chunk) * D * es : 0) + (kt ? size_t(D) * lkt * es : 0) + size_t(Dv) * lkt * es +
            (out ? size_t(Dv) * D * es + size_t(4) * (D + 8) * es : 0) + size_t(chunk) * 4;
