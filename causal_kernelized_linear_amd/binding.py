@@ -91,7 +91,7 @@ def linattn_decode_step(q, k, v, S, z, o, B, H, D, Dv, dtype, eps, stream) -> in
 
 
 def linattn_set_profile_events(ev0, ev1, ev2, ev3) -> int:
-    """Arm the measurement hook with four raw hipEvent_t handles (ints; all 0 disarms)."""
+    """Arm the measurement hook with raw hipEvent_t handles (ints; 0 is not recorded, all 0 disarms)."""
     return int(lib().linattn_set_profile_events(ev0, ev1, ev2, ev3))
 
 

@@ -127,13 +127,14 @@ linattn_status_t linattn_decode_step(
 
 /*
  * Measurement hook, not part of the computation.  Arms the NEXT linattn_fwd_chunked or
- * linattn_fwd_gated call on this process to record four caller-created hipEvent_t
- * handles on its stream: ev0 before the segment-totals walk, ev1 after it, ev2 after the
- * scan over segments, ev3 after the output walk and, when s_out or z_out is given, the
- * final-state copy (a step that a shape does not need is skipped, so its two events
- * bracket nothing).  The first forward whose
+ * linattn_fwd_gated call on this process to record caller-created hipEvent_t handles on
+ * its stream: ev0 before the segment-totals walk, ev1 after it, ev2 after the scan over
+ * segments, ev3 after the output walk and, when s_out or z_out is given, the final-state
+ * copy (a step that a shape does not need is skipped, so its two events bracket
+ * nothing).  NULL handles are not recorded; every event recorded sits between dependent
+ * launches and delays the next one by a few microseconds.  The first forward whose
  * arguments pass validation consumes (and disarms) the hook; four NULLs disarm it.
- * Returns LINATTN_ERR_INVALID_ARGUMENT when only some handles are NULL.
+ * Always returns LINATTN_OK.
  */
 linattn_status_t linattn_set_profile_events(void* ev0, void* ev1, void* ev2, void* ev3);
 

@@ -96,7 +96,9 @@ def test_fwd_rejects_bad_arguments(gated):
 
 def test_profile_hook_arguments():
     assert binding.linattn_set_profile_events(0, 0, 0, 0) == OK
-    assert binding.linattn_set_profile_events(16, 0, 0, 0) == INVALID
+    # any subset of handles may be given; disarm again before anything could record them
+    assert binding.linattn_set_profile_events(16, 0, 0, 0) == OK
+    assert binding.linattn_set_profile_events(0, 0, 0, 0) == OK
 
 
 def test_gated_requires_gate():
