@@ -24,6 +24,8 @@ L_i = sum_{l=s..i} log g_l:
     den_i = exp(L_i) Fq_i . z_prev + sum_j A_ij
     S_next = exp(L_last) S_prev + sum_j exp(L_last - L_j) Fk_j v_j^T   (same for z)
 Every decay factor used is exp of a non-positive number, so nothing overflows.
+
+``normalize=False`` returns num alone, as the recurrence does.
 """
 from __future__ import annotations
 
@@ -32,7 +34,7 @@ import numpy as np
 from .recurrence import EPS, phi
 
 
-def chunked_linear_attention(q, k, v, chunk, g=None, s0=None, z0=None, eps=EPS):
+def chunked_linear_attention(q, k, v, chunk, g=None, s0=None, z0=None, eps=EPS, normalize=True):
     """Chunked form over [..., N, D] inputs.  Returns (o, S_N, z_N) in float64."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -69,5 +71,5 @@ def chunked_linear_attention(q, k, v, chunk, g=None, s0=None, z0=None, eps=EPS):
             last = np.exp(lam[..., -1])
             S = last[..., None, None] * S + np.swapaxes(fkd, -1, -2) @ vc
             z = last[..., None] * z + fkd.sum(-2)
-        o[..., s:e, :] = num / np.maximum(den, eps)
+        o[..., s:e, :] = num / np.maximum(den, eps) if normalize else num
     return o, S, z

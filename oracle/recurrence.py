@@ -38,6 +38,14 @@ What it computes (all arithmetic in float64, inputs widened exactly):
 
 * An optional initial state (S0, z0) replaces the zero state, so a sequence
   can be resumed from a saved state; the final state (S_N, z_N) is returned.
+
+* ``normalize=False`` returns the numerator alone, o_i = S_i^T phi(q_i): the
+  output of retention, which has no phi(q)^T z denominator and leaves the
+  scaling to a normalisation layer after the attention (aicassindra.com page,
+  "RetNet and gated linear attention"; learn.pranaymahendrakar.com page,
+  "Implementation reality": modern variants drop the normaliser).  The state
+  recurrence is unchanged, z included, so a run can switch modes on a resumed
+  state; eps is not used.
 """
 from __future__ import annotations
 
@@ -52,11 +60,12 @@ def phi(x):
     return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
 
 
-def causal_linear_attention(q, k, v, g=None, s0=None, z0=None, eps=EPS):
+def causal_linear_attention(q, k, v, g=None, s0=None, z0=None, eps=EPS, normalize=True):
     """Causal kernelized linear attention, one token at a time.
 
     q, k: [..., N, D]; v: [..., N, Dv]; g: [..., N] or None;
     s0: [..., D, Dv] or None; z0: [..., D] or None (None means zeros).
+    normalize: divide by max(phi(q)^T z, eps) (True) or return the numerator.
     Leading dimensions (batch, heads) are independent and are vectorised.
     Returns (o [..., N, Dv], S_N [..., D, Dv], z_N [..., D]), all float64.
     """
@@ -88,11 +97,11 @@ def causal_linear_attention(q, k, v, g=None, s0=None, z0=None, eps=EPS):
         z = z + fk
         num = np.einsum("...d,...de->...e", fq, S)
         den = np.einsum("...d,...d->...", fq, z)
-        o[..., t, :] = num / np.maximum(den, eps)[..., None]
+        o[..., t, :] = num / np.maximum(den, eps)[..., None] if normalize else num
     return o, S, z
 
 
-def decode_step(q, k, v, S, z, g=None, eps=EPS):
+def decode_step(q, k, v, S, z, g=None, eps=EPS, normalize=True):
     """One recurrent decode step from a stored state.
 
     q, k: [..., D]; v: [..., Dv]; S: [..., D, Dv]; z: [..., D]; g: [...] or None.
@@ -103,5 +112,5 @@ def decode_step(q, k, v, S, z, g=None, eps=EPS):
     k = np.asarray(k, dtype=np.float64)[..., None, :]
     v = np.asarray(v, dtype=np.float64)[..., None, :]
     gg = None if g is None else np.asarray(g, dtype=np.float64)[..., None]
-    o, S1, z1 = causal_linear_attention(q, k, v, g=gg, s0=S, z0=z, eps=eps)
+    o, S1, z1 = causal_linear_attention(q, k, v, g=gg, s0=S, z0=z, eps=eps, normalize=normalize)
     return o[..., 0, :], S1, z1

@@ -32,8 +32,11 @@ def elu1(x):
     return torch.nn.functional.elu(torch.as_tensor(np.asarray(x, dtype=np.float64))).numpy() + 1.0
 
 
-def pairwise(q, k, v, g=None, eps=1e-6):
-    """Brute force: W_ij = phi(q_i).phi(k_j) * prod_{l=j+1..i} g_l for j <= i, O = W V / max(W 1, eps).
+def pairwise(q, k, v, g=None, eps=1e-6, normalize=True):
+    """Brute force: W_ij = phi(q_i).phi(k_j) * prod_{l=j+1..i} g_l for j <= i, O = W V / max(W 1, eps),
+    or O = W V alone when ``normalize`` is False (the parallel form of retention on the
+    aicassindra.com page, "RetNet and gated linear attention": a decay-masked score
+    matrix times V, with no denominator).
 
     The explicit masked kernel-score form (learn.pranaymahendrakar.com page,
     Developer level, part 3 of linear_attention.py; anandmoghan-problems page,
@@ -58,7 +61,7 @@ def pairwise(q, k, v, g=None, eps=1e-6):
                         w *= float(g[idx + (l,)])
                 num += w * v[idx + (j,)]
                 den += w
-            o[idx + (i,)] = num / max(den, eps)
+            o[idx + (i,)] = num / max(den, eps) if normalize else num
     return o
 
 
@@ -273,6 +276,49 @@ def pin_decode_composition(orc):
     np.testing.assert_allclose(zd, z0 + fk, rtol=1e-15, atol=1e-13)
 
 
+def pin_numerator_mode(orc):
+    """Normaliser-free output (retention: aicassindra.com page, "RetNet and gated linear
+    attention"; learn.pranaymahendrakar.com page, "Implementation reality").
+
+    * brute force: o = W V with the decay-weighted scores, ungated and gated;
+    * closed form: q = k = 0 makes phi(q).phi(k) = D, so with V constant c, a constant
+      gate gamma and an initial state S0, o_i = gamma^(i+1) 1^T S0 + D c (1 - gamma^(i+1)) / (1 - gamma),
+      and gamma = 1 gives 1^T S0 + D c (i + 1);
+    * the state it returns is the normalised mode's, and a decode step in this mode
+      continues a run in this mode."""
+    for seed, (n, d, dv) in enumerate([(6, 3, 2), (9, 4, 4), (7, 8, 6)]):
+        q, k, v = _rng_inputs(900 + seed, (2,), n, d, dv, scale=1.5)
+        o, _, _ = orc.causal_linear_attention(q, k, v, normalize=False)
+        np.testing.assert_allclose(o, pairwise(q, k, v, normalize=False), rtol=1e-12, atol=1e-13)
+        g = np.random.default_rng(950 + seed).uniform(0.2, 1.0, size=(2, n))
+        o, _, _ = orc.causal_linear_attention(q, k, v, g=g, normalize=False)
+        np.testing.assert_allclose(o, pairwise(q, k, v, g=g, normalize=False), rtol=1e-12, atol=1e-13)
+    n, d, dv = 14, 6, 3
+    rng = np.random.default_rng(990)
+    c = rng.normal(size=(2, 1, dv))
+    S0 = rng.normal(size=(2, d, dv))
+    zero = np.zeros((2, n, d))
+    i = np.arange(n)[None, :, None]
+    for gamma in (1.0, 0.8):
+        g = np.full((2, n), gamma)
+        o, _, _ = orc.causal_linear_attention(zero, zero, np.broadcast_to(c, (2, n, dv)), g=g, s0=S0,
+                                              z0=np.ones((2, d)), normalize=False)
+        geo = (i + 1.0) if gamma == 1.0 else (1 - gamma ** (i + 1.0)) / (1 - gamma)
+        want = gamma ** (i + 1.0) * S0.sum(1)[:, None, :] + d * c * geo
+        np.testing.assert_allclose(o, want, rtol=1e-13, atol=1e-13)
+    q, k, v = _rng_inputs(995, (3,), 10, 5, 4)
+    g = np.random.default_rng(996).uniform(0.5, 1.0, size=(3, 10))
+    on, Sn, zn = orc.causal_linear_attention(q, k, v, g=g)
+    o, S, z = orc.causal_linear_attention(q, k, v, g=g, normalize=False)
+    np.testing.assert_array_equal(S, Sn)
+    np.testing.assert_array_equal(z, zn)
+    _, S9, z9 = orc.causal_linear_attention(q[..., :9, :], k[..., :9, :], v[..., :9, :], g=g[..., :9],
+                                            normalize=False)
+    od, Sd, zd = orc.decode_step(q[..., 9, :], k[..., 9, :], v[..., 9, :], S9, z9, g=g[..., 9], normalize=False)
+    np.testing.assert_allclose(od, o[..., 9, :], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(Sd, S, rtol=1e-13, atol=1e-13)
+
+
 ALL_PINS = [
     pin_phi_values,
     pin_hand_example,
@@ -287,4 +333,5 @@ ALL_PINS = [
     pin_unit_gate_is_ungated,
     pin_resume,
     pin_decode_composition,
+    pin_numerator_mode,
 ]

@@ -23,9 +23,11 @@ def _inputs(seed, lead, n, d, dv):
 @pytest.mark.parametrize("chunk", [1, 3, 16, 64, 100, 128, 1000])
 @pytest.mark.parametrize("gated", [False, True])
 @pytest.mark.parametrize("with_state", [False, True])
-def test_chunked_equals_recurrence(chunk, gated, with_state):
+@pytest.mark.parametrize("normalize", [True, False])
+def test_chunked_equals_recurrence(chunk, gated, with_state, normalize):
     q, k, v, g, s0, z0 = _inputs(chunk * 7 + gated, (2, 2), 100, 8, 6)
-    kw = dict(g=g if gated else None, s0=s0 if with_state else None, z0=z0 if with_state else None)
+    kw = dict(g=g if gated else None, s0=s0 if with_state else None, z0=z0 if with_state else None,
+              normalize=normalize)
     o_r, S_r, z_r = oracle.causal_linear_attention(q, k, v, **kw)
     o_c, S_c, z_c = oracle.chunked_linear_attention(q, k, v, chunk, **kw)
     np.testing.assert_allclose(o_c, o_r, rtol=1e-11, atol=1e-12)

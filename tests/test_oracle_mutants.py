@@ -35,6 +35,9 @@ MUTATIONS = {
     "initial_state_ignored": ("S = np.array(s0, dtype=np.float64, copy=True)", "S = np.zeros(lead + (d, dv))"),
     "value_index_lag": ("v[..., t, None, :]", "v[..., max(t - 1, 0), None, :]"),
     "gate_index_lag": ("gt = g[..., t]", "gt = g[..., max(t - 1, 0)]"),
+    "numerator_mode_still_divides": ("if normalize else num", "if normalize or True else num"),
+    "numerator_mode_divides_by_raw_den": ("if normalize else num", "if normalize else num / den[..., None]"),
+    "decode_drops_output_mode": ("eps=eps, normalize=normalize)", "eps=eps)"),
 }
 
 
