@@ -7,8 +7,10 @@ training-shaped workload B=8, H=16, N=4096, D=Dv=64, bf16, chunk 128, with the
 inputs already resident in HBM.  Input sets are rotated so no step starts with
 its inputs warm in the 256 MB Infinity Cache.  The scalar-gated forward
 (B=4, H=16, N=8192, D=Dv=64, chunk 128), the long-context forward
-(B=1, H=32, N=65536, D=Dv=128, chunk sweep) and the decode step (B=256, H=32,
-D=Dv=128, fp32 state) are timed in the same run and reported in extra fields.
+(B=1, H=32, N=65536, D=Dv=128, chunk sweep), the decode step (B=256, H=32,
+D=Dv=128, fp32 state), its gated form, and the normaliser-free output mode of the
+gated forward and of the gated decode are timed in the same run and reported in
+extra fields.
 
 Prints ONE JSON line.  ms_per_step and value come from a timed pass bracketed by
 two hipEvents only.  Per-kernel durations come from a second timed pass of the same
@@ -108,7 +110,7 @@ def fwd_flops_per_unit(w, chunk):
     return 4 * w.D * w.Dv + (chunk + 1) * (w.D + w.Dv)
 
 
-def time_forward(w, chunk, steps, warmup, ev, rotate_bytes=600e6):
+def time_forward(w, chunk, steps, warmup, ev, rotate_bytes=600e6, normalize=True):
     """Time `steps` forwards of workload w; returns a dict of timings (ms).
 
     Two timed passes of `steps` forwards each.  The first is bracketed by two hipEvents
@@ -133,7 +135,10 @@ def time_forward(w, chunk, steps, warmup, ev, rotate_bytes=600e6):
 
     def call(i):
         s = sets[i % nsets]
-        if w.kind == "gated":
+        if not normalize:
+            binding.fwd(s["q"], s["k"], s["v"], g=s.get("g"), chunk=chunk, out=outs[i % nsets], workspace=ws,
+                        normalize=False)
+        elif w.kind == "gated":
             binding.fwd_gated(s["q"], s["k"], s["v"], s["g"], chunk=chunk, out=outs[i % nsets], workspace=ws)
         else:
             binding.fwd_chunked(s["q"], s["k"], s["v"], chunk=chunk, out=outs[i % nsets], workspace=ws)
@@ -183,7 +188,9 @@ def time_forward(w, chunk, steps, warmup, ev, rotate_bytes=600e6):
     return res
 
 
-def time_decode(w, steps, warmup, ev):
+def time_decode(w, steps, warmup, ev, normalize=True):
+    """Per-step time of the decode step (gated when the workload carries g); in the
+    normaliser-free mode z is not passed, so the step moves no z bytes."""
     import torch
     from causal_kernelized_linear_amd import binding, workloads
 
@@ -197,7 +204,8 @@ def time_decode(w, steps, warmup, ev):
 
     def call(i):
         s = sets[i % nsets]
-        binding.decode_step(s["q"], s["k"], s["v"], s["S"], s["z"], out=outs[i % nsets])
+        binding.decode_step(s["q"], s["k"], s["v"], s["S"], s["z"] if normalize else None, out=outs[i % nsets],
+                            g=s.get("g"), normalize=normalize)
 
     for i in range(warmup):
         call(i)
@@ -214,9 +222,12 @@ def time_decode(w, steps, warmup, ev):
     return {"ms_per_step": sum(ks) / steps, "ms_median": _median(ks)}
 
 
-def decode_bytes(w):
+def decode_bytes(w, with_z=True):
+    """S (and z) read and written once, q, k, v read, o written, plus the gate when gated."""
     es = 4 if w.dtype == "f32" else 2
-    per_head = 2 * (w.D * w.Dv + w.D) * 4 + (2 * w.D + w.Dv) * es + w.Dv * es
+    per_head = 2 * (w.D * w.Dv + (w.D if with_z else 0)) * 4 + (2 * w.D + w.Dv) * es + w.Dv * es
+    if w.kind == "decode_gated":
+        per_head += 4
     return per_head * w.B * w.H
 
 
@@ -381,6 +392,26 @@ def main():
             "tokens_per_s": wd.B / sd, "ms_per_step": rd["ms_per_step"], "ms_median": rd["ms_median"],
             "bytes_per_step": decode_bytes(wd),
         }
+        rn = time_forward(wg, 128, extra_steps, extra_warm, ev, normalize=False)
+        sn = rn["ms_per_step"] * 1e-3
+        line["gated_numerator"] = {
+            "workload": "gated_bf16 in the normaliser-free output mode (o = phi(q)^T S)",
+            "tokens_per_s": wg.B * wg.N / sn, "ms_per_step": rn["ms_per_step"], "kernel_ms": rn["kernel_ms"],
+            "algorithmic_GBps": fwd_bytes_per_unit(wg) * ug / sn / 1e9,
+            "hbm_frac": fwd_bytes_per_unit(wg) * ug / sn / 1e9 / HBM_PEAK_GBS,
+        }
+        wdg = workloads.WORKLOADS["decode_gated_bf16"]
+        for key, norm in (("decode_gated", True), ("decode_gated_numerator", False)):
+            rdg = time_decode(wdg, extra_steps, extra_warm, ev, normalize=norm)
+            sdg = rdg["ms_per_step"] * 1e-3
+            nbytes = decode_bytes(wdg, with_z=norm)
+            line[key] = {
+                "workload": "decode_gated_bf16: B=256 H=32 D=Dv=128, fp32 state, one token, gate per head"
+                            + ("" if norm else "; normaliser-free, no z"),
+                "GBps": nbytes / sdg / 1e9, "hbm_frac": nbytes / sdg / 1e9 / HBM_PEAK_GBS,
+                "tokens_per_s": wdg.B / sdg, "ms_per_step": rdg["ms_per_step"], "ms_median": rdg["ms_median"],
+                "bytes_per_step": nbytes,
+            }
         wl = workloads.WORKLOADS["longctx_bf16"]
         sweep = {}
         for c in wl.chunks:

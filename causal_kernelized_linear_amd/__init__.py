@@ -7,10 +7,13 @@ not load the library; the first call does, and raises if it is missing.
 """
 from .binding import (  # noqa: F401
     decode_step,
+    fwd,
     fwd_chunked,
     fwd_gated,
     linattn_decode_step,
+    linattn_decode_step_ex,
     linattn_fwd_chunked,
+    linattn_fwd_ex,
     linattn_fwd_gated,
     linattn_fwd_workspace_size,
     linattn_set_profile_events,

@@ -7,9 +7,9 @@ allocates the caller-side workspace and output tensors with torch, and raises
 no fallback: if the library is missing, every call raises.
 
 Function names match the C ABI (include/linattn.h):
-    linattn_fwd_chunked, linattn_fwd_gated, linattn_decode_step,
-    linattn_fwd_workspace_size, linattn_status_string
-plus the tensor-level helpers fwd_chunked, fwd_gated and decode_step.
+    linattn_fwd_chunked, linattn_fwd_gated, linattn_fwd_ex, linattn_decode_step,
+    linattn_decode_step_ex, linattn_fwd_workspace_size, linattn_status_string
+plus the tensor-level helpers fwd_chunked, fwd_gated, fwd and decode_step.
 """
 from __future__ import annotations
 
@@ -23,6 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblinattn.so")
 
 F32, BF16 = 0, 1
+OUT_NORMALIZED, OUT_NUMERATOR = 0, 1
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "hip"}
 
 _lock = threading.Lock()
@@ -37,7 +38,9 @@ EXPORTS = {
     "linattn_fwd_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
     "linattn_fwd_chunked": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p, _sz, _p]),
     "linattn_fwd_gated": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p, _sz, _p]),
+    "linattn_fwd_ex": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i, _p, _sz, _p]),
     "linattn_decode_step": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p]),
+    "linattn_decode_step_ex": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p]),
     "linattn_status_string": (ctypes.c_char_p, [_i]),
     "linattn_set_profile_events": (_i, [_p, _p, _p, _p]),
 }
@@ -86,8 +89,18 @@ def linattn_fwd_gated(q, k, v, g, o, s0, z0, s_out, z_out, B, H, N, D, Dv, chunk
                                        ws_bytes, stream))
 
 
+def linattn_fwd_ex(q, k, v, g, o, s0, z0, s_out, z_out, B, H, N, D, Dv, chunk, dtype, eps, out, ws, ws_bytes,
+                   stream) -> int:
+    return int(lib().linattn_fwd_ex(q, k, v, g, o, s0, z0, s_out, z_out, B, H, N, D, Dv, chunk, dtype, eps, out, ws,
+                                    ws_bytes, stream))
+
+
 def linattn_decode_step(q, k, v, S, z, o, B, H, D, Dv, dtype, eps, stream) -> int:
     return int(lib().linattn_decode_step(q, k, v, S, z, o, B, H, D, Dv, dtype, eps, stream))
+
+
+def linattn_decode_step_ex(q, k, v, g, S, z, o, B, H, D, Dv, dtype, eps, out, stream) -> int:
+    return int(lib().linattn_decode_step_ex(q, k, v, g, S, z, o, B, H, D, Dv, dtype, eps, out, stream))
 
 
 def linattn_set_profile_events(ev0, ev1, ev2, ev3) -> int:
@@ -130,7 +143,7 @@ def workspace_bytes(B, H, N, D, Dv, chunk) -> int:
     return linattn_fwd_workspace_size(B, H, N, D, Dv, chunk)
 
 
-def _fwd(q, k, v, g, chunk, eps, s0, z0, return_state, out, workspace):
+def _fwd(q, k, v, g, chunk, eps, s0, z0, return_state, out, workspace, normalize=True):
     dt = _dtype_code(q)
     dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
@@ -161,7 +174,11 @@ def _fwd(q, k, v, g, chunk, eps, s0, z0, return_state, out, workspace):
         raise ValueError("workspace too small")
     wsb = workspace.numel() * workspace.element_size()
     st = _stream(dev)
-    if g is None:
+    if not normalize:
+        code = linattn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(o), _ptr(s0), _ptr(z0), _ptr(s_out),
+                              _ptr(z_out), B, H, N, D, Dv, chunk, dt, eps, OUT_NUMERATOR, _ptr(workspace), wsb, st)
+        _check(code, "linattn_fwd_ex")
+    elif g is None:
         code = linattn_fwd_chunked(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(s0), _ptr(z0), _ptr(s_out),
                                    _ptr(z_out), B, H, N, D, Dv, chunk, dt, eps, _ptr(workspace), wsb, st)
         _check(code, "linattn_fwd_chunked")
@@ -187,23 +204,41 @@ def fwd_gated(q, k, v, g, chunk=128, eps=1e-6, s0=None, z0=None, return_state=Fa
     return _fwd(q, k, v, g, chunk, eps, s0, z0, return_state, out, workspace)
 
 
-def decode_step(q, k, v, S, z, eps=1e-6, out=None):
+def fwd(q, k, v, g=None, chunk=128, eps=1e-6, s0=None, z0=None, return_state=False, out=None, workspace=None,
+        normalize=True):
+    """The general forward (linattn_fwd_ex): optional gate g [B,H,N] float32, and
+    ``normalize=False`` for the normaliser-free output o = phi(q)^T S."""
+    return _fwd(q, k, v, g, chunk, eps, s0, z0, return_state, out, workspace, normalize)
+
+
+def decode_step(q, k, v, S, z, eps=1e-6, out=None, g=None, normalize=True):
     """One decode step: q, k [B,H,D], v [B,H,Dv]; S [B,H,D,Dv] and z [B,H,D] (float32)
-    are updated in place.  Returns o [B,H,Dv]."""
+    are updated in place.  g [B,H] float32 gates the state first (S <- g S + ...); with
+    ``normalize=False`` the output is the numerator and z may be None.  Returns o [B,H,Dv]."""
     dt = _dtype_code(q)
     dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
         _need(t, n, q.dtype, dev)
     _need(S, "S", torch.float32, dev)
     _need(z, "z", torch.float32, dev)
+    _need(g, "g", torch.float32, dev)
     if q.dim() != 3:
         raise ValueError("q must be [B, H, D]")
     B, H, D = q.shape
     Dv = v.shape[-1]
-    if tuple(S.shape) != (B, H, D, Dv) or tuple(z.shape) != (B, H, D) or k.shape != q.shape:
+    if tuple(S.shape) != (B, H, D, Dv) or k.shape != q.shape or (z is not None and tuple(z.shape) != (B, H, D)):
         raise ValueError("shape mismatch")
+    if g is not None and tuple(g.shape) != (B, H):
+        raise ValueError("g must be [B, H]")
+    if z is None and normalize:
+        raise ValueError("the normalised output needs z")
     o = torch.empty(B, H, Dv, dtype=q.dtype, device=dev) if out is None else out
-    code = linattn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(z), _ptr(o), B, H, D, Dv, dt, eps,
-                               _stream(dev))
-    _check(code, "linattn_decode_step")
+    if g is None and normalize:
+        code = linattn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(z), _ptr(o), B, H, D, Dv, dt, eps,
+                                   _stream(dev))
+        _check(code, "linattn_decode_step")
+    else:
+        code = linattn_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(S), _ptr(z), _ptr(o), B, H, D, Dv, dt,
+                                      eps, OUT_NORMALIZED if normalize else OUT_NUMERATOR, _stream(dev))
+        _check(code, "linattn_decode_step_ex")
     return o

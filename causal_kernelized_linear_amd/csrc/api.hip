@@ -106,6 +106,8 @@ size_t esize(linattn_dtype_t dt) { return dt == LINATTN_BF16 ? 2 : 4; }
 
 bool dtype_ok(int dt) { return dt == LINATTN_F32 || dt == LINATTN_BF16; }
 
+bool out_ok(int m) { return m == LINATTN_OUT_NORMALIZED || m == LINATTN_OUT_NUMERATOR; }
+
 // The device must be a gfx950.  Cached per device ordinal.
 linattn_status_t check_device() {
     int dev = -1;
@@ -130,9 +132,10 @@ linattn_status_t check_device() {
 
 linattn_status_t fwd_common(const void* q, const void* k, const void* v, const float* g, void* o, const float* s0,
                             const float* z0, float* s_out, float* z_out, int B, int H, int N, int D, int Dv,
-                            int chunk, linattn_dtype_t dtype, float eps, void* ws, size_t ws_bytes, void* stream) {
+                            int chunk, linattn_dtype_t dtype, float eps, linattn_output_t out, void* ws,
+                            size_t ws_bytes, void* stream) {
     if (B < 0 || H < 0 || N < 0 || D <= 0 || Dv <= 0 || chunk <= 0) return LINATTN_ERR_INVALID_ARGUMENT;
-    if (!dtype_ok(dtype) || !(eps > 0.0f) || !std::isfinite(eps)) return LINATTN_ERR_INVALID_ARGUMENT;
+    if (!dtype_ok(dtype) || !out_ok(out) || !(eps > 0.0f) || !std::isfinite(eps)) return LINATTN_ERR_INVALID_ARGUMENT;
     const long BH = long(B) * long(H);
     if (BH == 0 || N == 0) return LINATTN_OK;
     if (BH > (1L << 24) || long(N) * BH > (1L << 40)) return LINATTN_ERR_INVALID_ARGUMENT;
@@ -169,10 +172,40 @@ linattn_status_t fwd_common(const void* q, const void* k, const void* v, const f
     L.ws = ws;
     L.BH = int(BH); L.N = N; L.D = D; L.Dv = Dv; L.chunk = chunk;
     L.nseg = plan.nseg; L.L = plan.L; L.eps = eps;
+    L.normalize = out == LINATTN_OUT_NORMALIZED ? 1 : 0;
     L.stream = static_cast<hipStream_t>(stream);
     take_profile_events(L.prof);
     (void)hipGetLastError();   // start from a clean error state
     const hipError_t e = dtype == LINATTN_BF16 ? linattn::launch_fwd_bf16(L) : linattn::launch_fwd_f32(L);
+    return e == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP;
+}
+
+linattn_status_t decode_common(const void* q, const void* k, const void* v, const float* g, float* S, float* z,
+                               void* o, int B, int H, int D, int Dv, linattn_dtype_t dtype, float eps,
+                               linattn_output_t out, void* stream) {
+    if (B < 0 || H < 0 || D <= 0 || Dv <= 0) return LINATTN_ERR_INVALID_ARGUMENT;
+    if (!dtype_ok(dtype) || !out_ok(out) || !(eps > 0.0f) || !std::isfinite(eps)) return LINATTN_ERR_INVALID_ARGUMENT;
+    const long BH = long(B) * long(H);
+    if (BH == 0) return LINATTN_OK;
+    if (BH > (1L << 31) - 1) return LINATTN_ERR_INVALID_ARGUMENT;
+    if (!q || !k || !v || !S || !o || (!z && out == LINATTN_OUT_NORMALIZED)) return LINATTN_ERR_INVALID_ARGUMENT;
+    for (const void* p : {q, k, v, static_cast<const void*>(g), static_cast<const void*>(S),
+                          static_cast<const void*>(z), static_cast<const void*>(o)})
+        if (p && !aligned16(p)) return LINATTN_ERR_INVALID_ARGUMENT;
+    const size_t es = esize(dtype);
+    const size_t no = size_t(BH) * Dv * es, ns = size_t(BH) * D * Dv * 4, nz = size_t(BH) * D * 4,
+                 ng = size_t(BH) * 4;
+    if (overlap(o, no, q, size_t(BH) * D * es) || overlap(o, no, k, size_t(BH) * D * es) || overlap(o, no, v, no) ||
+        overlap(o, no, S, ns) || overlap(o, no, z, nz) || overlap(S, ns, z, nz) || overlap(g, ng, S, ns) ||
+        overlap(g, ng, z, nz) || overlap(g, ng, o, no))
+        return LINATTN_ERR_INVALID_ARGUMENT;
+    if (!dim_ok(D) || !dim_ok(Dv)) return LINATTN_ERR_UNSUPPORTED;
+    const linattn_status_t dst = check_device();
+    if (dst != LINATTN_OK) return dst;
+    (void)hipGetLastError();
+    const hipError_t e = linattn::launch_decode(int(dtype), q, k, v, S, z, o, int(BH), D, Dv, eps, g,
+                                                out == LINATTN_OUT_NORMALIZED ? 1 : 0,
+                                                static_cast<hipStream_t>(stream));
     return e == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP;
 }
 
@@ -190,8 +223,8 @@ linattn_status_t linattn_fwd_chunked(const void* q, const void* k, const void* v
                                      int chunk, linattn_dtype_t dtype, float eps, void* workspace,
                                      size_t workspace_bytes, void* stream) {
     try {
-        return fwd_common(q, k, v, nullptr, o, s0, z0, s_out, z_out, B, H, N, D, Dv, chunk, dtype, eps, workspace,
-                          workspace_bytes, stream);
+        return fwd_common(q, k, v, nullptr, o, s0, z0, s_out, z_out, B, H, N, D, Dv, chunk, dtype, eps,
+                          LINATTN_OUT_NORMALIZED, workspace, workspace_bytes, stream);
     } catch (...) {
         return LINATTN_ERR_HIP;
     }
@@ -203,7 +236,19 @@ linattn_status_t linattn_fwd_gated(const void* q, const void* k, const void* v, 
                                    size_t workspace_bytes, void* stream) {
     try {
         if (!g && long(B) * long(H) * long(N) > 0) return LINATTN_ERR_INVALID_ARGUMENT;
-        return fwd_common(q, k, v, g, o, s0, z0, s_out, z_out, B, H, N, D, Dv, chunk, dtype, eps, workspace,
+        return fwd_common(q, k, v, g, o, s0, z0, s_out, z_out, B, H, N, D, Dv, chunk, dtype, eps,
+                          LINATTN_OUT_NORMALIZED, workspace, workspace_bytes, stream);
+    } catch (...) {
+        return LINATTN_ERR_HIP;
+    }
+}
+
+linattn_status_t linattn_fwd_ex(const void* q, const void* k, const void* v, const float* g, void* o, const float* s0,
+                                const float* z0, float* s_out, float* z_out, int B, int H, int N, int D, int Dv,
+                                int chunk, linattn_dtype_t dtype, float eps, linattn_output_t out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    try {
+        return fwd_common(q, k, v, g, o, s0, z0, s_out, z_out, B, H, N, D, Dv, chunk, dtype, eps, out, workspace,
                           workspace_bytes, stream);
     } catch (...) {
         return LINATTN_ERR_HIP;
@@ -213,28 +258,17 @@ linattn_status_t linattn_fwd_gated(const void* q, const void* k, const void* v, 
 linattn_status_t linattn_decode_step(const void* q, const void* k, const void* v, float* S, float* z, void* o, int B,
                                      int H, int D, int Dv, linattn_dtype_t dtype, float eps, void* stream) {
     try {
-        if (B < 0 || H < 0 || D <= 0 || Dv <= 0) return LINATTN_ERR_INVALID_ARGUMENT;
-        if (!dtype_ok(dtype) || !(eps > 0.0f) || !std::isfinite(eps)) return LINATTN_ERR_INVALID_ARGUMENT;
-        const long BH = long(B) * long(H);
-        if (BH == 0) return LINATTN_OK;
-        if (BH > (1L << 31) - 1) return LINATTN_ERR_INVALID_ARGUMENT;
-        if (!q || !k || !v || !S || !z || !o) return LINATTN_ERR_INVALID_ARGUMENT;
-        for (const void* p : {q, k, v, static_cast<const void*>(S), static_cast<const void*>(z),
-                              static_cast<const void*>(o)})
-            if (!aligned16(p)) return LINATTN_ERR_INVALID_ARGUMENT;
-        const size_t es = esize(dtype);
-        const size_t no = size_t(BH) * Dv * es;
-        if (overlap(o, no, q, size_t(BH) * D * es) || overlap(o, no, k, size_t(BH) * D * es) ||
-            overlap(o, no, v, no) || overlap(o, no, S, size_t(BH) * D * Dv * 4) || overlap(o, no, z, size_t(BH) * D * 4) ||
-            overlap(S, size_t(BH) * D * Dv * 4, z, size_t(BH) * D * 4))
-            return LINATTN_ERR_INVALID_ARGUMENT;
-        if (!dim_ok(D) || !dim_ok(Dv)) return LINATTN_ERR_UNSUPPORTED;
-        const linattn_status_t dst = check_device();
-        if (dst != LINATTN_OK) return dst;
-        (void)hipGetLastError();
-        const hipError_t e = linattn::launch_decode(int(dtype), q, k, v, S, z, o, int(BH), D, Dv, eps,
-                                                    static_cast<hipStream_t>(stream));
-        return e == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP;
+        return decode_common(q, k, v, nullptr, S, z, o, B, H, D, Dv, dtype, eps, LINATTN_OUT_NORMALIZED, stream);
+    } catch (...) {
+        return LINATTN_ERR_HIP;
+    }
+}
+
+linattn_status_t linattn_decode_step_ex(const void* q, const void* k, const void* v, const float* g, float* S,
+                                        float* z, void* o, int B, int H, int D, int Dv, linattn_dtype_t dtype,
+                                        float eps, linattn_output_t out, void* stream) {
+    try {
+        return decode_common(q, k, v, g, S, z, o, B, H, D, Dv, dtype, eps, out, stream);
     } catch (...) {
         return LINATTN_ERR_HIP;
     }

@@ -27,6 +27,7 @@
 // Chunk algebra for a chunk [s, s + CH) with Fq = phi(Q_c), Fk = phi(K_c):
 //     A     = tril(Fq Fk^T)                  (diagonal kept)
 //     num   = Fq S_prev + A V_c,   den = Fq z_prev + A 1,   O_c = num / max(den, eps)
+//     (O_c = num in the normaliser-free mode of retention)
 //     S_next = S_prev + Fk^T V_c,  z_next = z_prev + Fk^T 1
 // Gated (learn.pranaymahendrakar.com page, "Try it yourself": the weighted
 // quadratic form), with the chunk-local inclusive Lambda_i = sum_{l=s..i} log2 g_l:
@@ -84,6 +85,7 @@ struct WalkArgs {
     int direct;          // 1: the output walk sums the totals in front of its segment itself
     int want_final;      // 1: the last segment's output walk leaves S_N, z_N in slot nseg-1
     float eps;
+    int normalize;       // 1: o = num / max(den, eps); 0: o = num (the denominator is not used)
 };
 
 template <typename E, int D, int DV, int CH, bool GATED, bool OUT>
@@ -500,7 +502,7 @@ struct ChunkWalker {
     // output walk forms the state in front of its segment there).
     template <typename Prologue>
     __device__ __forceinline__ void walk(int c0, int nch, f32x4_t (&sacc)[Sh::TPW], f32x4_t (&zacc)[Sh::ZT],
-                                         float& lg_total, const OutRsrc& ob, float eps, bool fold_last,
+                                         float& lg_total, const OutRsrc& ob, float eps, int norm, bool fold_last,
                                          Prologue&& prologue) {
         last = min(N, (c0 + max(nch, 1)) * CH) - 1;
         Regs R;
@@ -524,7 +526,7 @@ struct ChunkWalker {
             load(R, ts + CH);
             __syncthreads();
             if constexpr (OUT) {
-                outputs(fq, ts, ob, eps);
+                outputs(fq, ts, ob, eps, norm);
                 load_q(qr, ts + CH);
             }
             const bool more = n + 1 < nch;
@@ -546,7 +548,7 @@ struct ChunkWalker {
     //   only, the causal mask; then O^T += V^T A^T and den += ones A^T.
     template <int WV>
     __device__ __forceinline__ void outputs_w(const F8<E> (&fq)[Sh::MAXS][D / 32], int ts, const OutRsrc& ob,
-                                              float eps) const {
+                                              float eps, int norm) const {
         constexpr int MS = Sh::MAXS, NT = DV / 16, KS = D / 32, MAXP = (Sh::NSTRIP + 1) / 2;
         F8<E> ones_a;                  // rows 0, 4, 8, 12 of the denominator's A operand
 #pragma unroll
@@ -649,7 +651,7 @@ struct ChunkWalker {
 #pragma unroll
         for (int m = 0; m < MS; ++m) {
             if (strip(m) < 0) continue;
-            const float inv = __builtin_amdgcn_rcpf(fmaxf(accd[m][0] + accd[m][1], eps));
+            const float inv = norm ? __builtin_amdgcn_rcpf(fmaxf(accd[m][0] + accd[m][1], eps)) : 1.0f;
             // rows past N fall outside the output resource and are dropped by the hardware
             const int row = ts + 16 * strip(m) + l16;
 #pragma unroll
@@ -709,7 +711,7 @@ struct ChunkWalker {
     // faster variant while the operand tiles are small (D * Dv below 128 x 128), and the
     // one that fits the registers when a wave holds several strips of 128 x 128 tiles.
     __device__ __forceinline__ void outputs_seq(const F8<E> (&fq)[Sh::MAXS][D / 32], int ts, const OutRsrc& ob,
-                                                float eps) const {
+                                                float eps, int norm) const {
         F8<E> ones_a;                  // rows 0, 4, 8, 12 of the denominator's A operand
 #pragma unroll
         for (int e = 0; e < 8; ++e) ones_a.x[e] = X::from_f32((l16 & 3) == 0 ? 1.0f : 0.0f);
@@ -741,7 +743,7 @@ struct ChunkWalker {
             const int npairs = s / 2 + 1;
             for (int p = 0; p + 1 < npairs; ++p) pair<false>(p, qi, lam_q, fq[m], ones_a, acc, accd);
             pair<true>(npairs - 1, qi, lam_q, fq[m], ones_a, acc, accd);
-            const float inv = __builtin_amdgcn_rcpf(fmaxf(accd[0] + accd[1], eps));
+            const float inv = norm ? __builtin_amdgcn_rcpf(fmaxf(accd[0] + accd[1], eps)) : 1.0f;
             // rows past N fall outside the output resource and are dropped by the hardware
             const int row = ts + qi;
 #pragma unroll
@@ -759,15 +761,15 @@ struct ChunkWalker {
 
     // Outputs of the chunk starting at ts for this wave's query strips (w is uniform).
     __device__ __forceinline__ void outputs(const F8<E> (&fq)[Sh::MAXS][D / 32], int ts, const OutRsrc& ob,
-                                            float eps) const {
+                                            float eps, int norm) const {
         if constexpr (D * DV < 128 * 128 || Sh::MAXS > 1) {
-            outputs_seq(fq, ts, ob, eps);
+            outputs_seq(fq, ts, ob, eps, norm);
         } else {
             switch (w) {
-                case 0: outputs_w<0>(fq, ts, ob, eps); break;
-                case 1: outputs_w<1>(fq, ts, ob, eps); break;
-                case 2: outputs_w<2>(fq, ts, ob, eps); break;
-                default: outputs_w<3>(fq, ts, ob, eps); break;
+                case 0: outputs_w<0>(fq, ts, ob, eps, norm); break;
+                case 1: outputs_w<1>(fq, ts, ob, eps, norm); break;
+                case 2: outputs_w<2>(fq, ts, ob, eps, norm); break;
+                default: outputs_w<3>(fq, ts, ob, eps, norm); break;
             }
         }
     }
@@ -867,7 +869,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     float lg_total = 0.0f;
     const bool keep = !OUTPUT || (final_seg && args.want_final);
 
-    wk.walk(c0, nch, sacc, zacc, lg_total, ob, args.eps, keep, prologue);
+    wk.walk(c0, nch, sacc, zacc, lg_total, ob, args.eps, args.normalize, keep, prologue);
 
     if (keep) {
 #pragma unroll

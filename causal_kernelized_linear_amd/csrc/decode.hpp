@@ -9,6 +9,12 @@
 // the row groups of a wave with lane exchanges and across waves through LDS; the
 // denominator phi(q) . z is reduced the same way.  The kernel is bound by HBM
 // bandwidth: 2 * D * Dv * 4 bytes of state traffic per head against 4 * D * Dv flops.
+//
+// The gated step decays the state first, S <- g S + phi(k) v^T and z <- g z + phi(k),
+// with one gate per head (aicassindra.com page, "RetNet and gated linear attention");
+// a NULL gate is 1, and since 1 * s is exact the ungated step is the same arithmetic.
+// In the normaliser-free mode (retention's output, no phi(q)^T z denominator) o is the
+// numerator and z, which may then be NULL, is left alone.
 #pragma once
 
 #include "device_common.hpp"
@@ -17,8 +23,9 @@ namespace linattn {
 
 template <typename E, int D, int DV>
 __global__ __launch_bounds__(kThreads) void decode_kernel(const E* __restrict__ q, const E* __restrict__ k,
-                                                         const E* __restrict__ v, float* __restrict__ S,
-                                                         float* __restrict__ z, E* __restrict__ o, float eps) {
+                                                         const E* __restrict__ v, const float* __restrict__ g,
+                                                         float* __restrict__ S, float* __restrict__ z,
+                                                         E* __restrict__ o, float eps, int normalize) {
     using X = Elem<E>;
     constexpr int CQ = DV / 4;            // 16-byte column quads per state row
     constexpr int RG = kThreads / CQ;     // row groups
@@ -48,11 +55,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const E* __restrict__ 
     float vv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) vv[r] = X::to_f32(vb[4 * cq + r]);
+    const float gt = g ? g[bh] : 1.0f;
 
-    // denominator: z' = z + phi(k), den = phi(q) . z'
+    // denominator: z' = g z + phi(k), den = phi(q) . z'
     float den = 0.0f;
-    if (tid < D) {
-        const float zn = z[size_t(bh) * D + tid] + phi(X::to_f32(kb[tid]));
+    if (z && tid < D) {
+        const float zn = fmaf(gt, z[size_t(bh) * D + tid], phi(X::to_f32(kb[tid])));
         z[size_t(bh) * D + tid] = zn;
         den = phi(X::to_f32(qb[tid])) * zn;
     }
@@ -65,7 +73,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const E* __restrict__ 
         const float fq = phi(X::to_f32(qb[d]));
         f32x4_t s = srow[i];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s[r] = fmaf(fk, vv[r], s[r]);
+        for (int r = 0; r < 4; ++r) s[r] = fmaf(fk, vv[r], gt * s[r]);
         __builtin_nontemporal_store(s, reinterpret_cast<f32x4_t*>(Sb + size_t(d) * DV + 4 * cq));
 #pragma unroll
         for (int r = 0; r < 4; ++r) num[r] = fmaf(fq, s[r], num[r]);
@@ -87,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const E* __restrict__ 
         float nsum = 0.0f, dsum = 0.0f;
 #pragma unroll
         for (int ww = 0; ww < kThreads / kWave; ++ww) { nsum += s_num[ww][tid]; dsum += s_den[ww]; }
-        o[size_t(bh) * DV + tid] = X::from_f32(nsum / fmaxf(dsum, eps));
+        o[size_t(bh) * DV + tid] = X::from_f32(normalize ? nsum / fmaxf(dsum, eps) : nsum);
     }
 }
 

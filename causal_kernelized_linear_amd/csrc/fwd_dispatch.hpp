@@ -21,7 +21,7 @@ hipError_t run_fwd_walks(const FwdLaunch& p) {
     a.zt = reinterpret_cast<float*>(wsb + off_zt);
     a.lg = reinterpret_cast<float*>(wsb + off_lg);
     a.s0 = p.s0; a.z0 = p.z0;
-    a.N = p.N; a.nseg = p.nseg; a.L = p.L; a.eps = p.eps;
+    a.N = p.N; a.nseg = p.nseg; a.L = p.L; a.eps = p.eps; a.normalize = p.normalize;
     a.direct = prefix_direct(p.nseg, D, DV) ? 1 : 0;
     a.want_final = (p.s_out || p.z_out) ? 1 : 0;
     auto* k_tot = walk_kernel<E, D, DV, CH, GATED, false>;

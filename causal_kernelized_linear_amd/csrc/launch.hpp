@@ -20,6 +20,7 @@ struct FwdLaunch {
     void* ws;                // caller's workspace, carved by fwd_workspace_layout
     int BH, N, D, Dv, chunk, nseg, L;
     float eps;
+    int normalize;           // 1: o = num / max(den, eps); 0: o = num
     hipStream_t stream;
     hipEvent_t prof[4];      // measurement hook: all NULL when unused
 };
@@ -74,6 +75,7 @@ inline bool prefix_direct(int nseg, int D, int Dv) { return size_t(nseg - 1) * D
 hipError_t launch_fwd_bf16(const FwdLaunch& p);
 hipError_t launch_fwd_f32(const FwdLaunch& p);
 hipError_t launch_decode(int dtype, const void* q, const void* k, const void* v, float* S, float* z, void* o,
-                         int BH, int D, int Dv, float eps, hipStream_t stream);
+                         int BH, int D, int Dv, float eps, const float* g, int normalize,
+                         hipStream_t stream);
 
 }  // namespace linattn

@@ -8,7 +8,7 @@ per workload, in the fixed order Q, K, V, then the gate g or the decode state
 rounds to nearest even; the oracle later receives exactly those rounded values
 widened to float64.
 
-The five named workloads follow the shapes and value distributions of the
+The named workloads follow the shapes and value distributions of the
 workloads the pages discuss: head dimension 64 or 128 (the 32-head, 128-wide
 linear heads of the hybrid stacks on the learn.pranaymahendrakar.com page,
 "What modern variants change"), chunks of 64-256 (page 1 closing paragraph,
@@ -26,7 +26,7 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                     # "fwd", "gated" or "decode"
+    kind: str                     # "fwd", "gated", "decode" or "decode_gated"
     B: int
     H: int
     N: int                        # tokens (1 for a decode step)
@@ -55,6 +55,8 @@ WORKLOADS = {
                             note="one recurrent step for 256 sequences, fp32 state"),
     "gated_bf16": Workload("gated_bf16", "gated", 4, 16, 8192, 64, 64, "bf16", (128,), 1005,
                            note="scalar gate per head per token"),
+    "decode_gated_bf16": Workload("decode_gated_bf16", "decode_gated", 256, 32, 1, 128, 128, "bf16", (1,), 1006,
+                                  note="one gated recurrent step: the decode form of the gated forward"),
 }
 
 
@@ -73,19 +75,24 @@ def make_inputs(w: Workload, B=None, H=None, N=None):
       gated:  the same plus g [B,H,N] float32, g = 0.9 + 0.1*sigmoid(N(0,1))
       decode: q, k [B,H,D]; v [B,H,Dv]; S [B,H,D,Dv] and z [B,H,D] float32,
               each 1000*|N(0,1)| (a state after about 1000 tokens)
+      decode_gated: the same plus this token's gate g [B,H] float32, drawn last as
+              0.9 + 0.1*sigmoid(N(0,1)) like the gated forward's gates
     """
     B = w.B if B is None else B
     H = w.H if H is None else H
     N = w.N if N is None else N
     gen = torch.Generator(device="cpu").manual_seed(w.seed)
     dt = w.torch_dtype
-    if w.kind == "decode":
+    if w.kind in ("decode", "decode_gated"):
         q = _randn(gen, (B, H, w.D), w.scale).to(dt)
         k = _randn(gen, (B, H, w.D), w.scale).to(dt)
         v = _randn(gen, (B, H, w.Dv), w.scale).to(dt)
         S = _randn(gen, (B, H, w.D, w.Dv)).abs_().mul_(1000.0)
         z = _randn(gen, (B, H, w.D)).abs_().mul_(1000.0)
-        return {"q": q, "k": k, "v": v, "S": S, "z": z}
+        out = {"q": q, "k": k, "v": v, "S": S, "z": z}
+        if w.kind == "decode_gated":
+            out["g"] = 0.9 + 0.1 * torch.sigmoid(_randn(gen, (B, H)))
+        return out
     q = _randn(gen, (B, H, N, w.D), w.scale).to(dt)
     k = _randn(gen, (B, H, N, w.D), w.scale).to(dt)
     v = _randn(gen, (B, H, N, w.Dv), w.scale).to(dt)

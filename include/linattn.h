@@ -59,6 +59,17 @@ typedef enum {
 } linattn_dtype_t;
 
 /*
+ * What o holds (linattn_fwd_ex, linattn_decode_step_ex).  The normaliser-free mode is
+ * the output of retention, which drops the phi(q)^T z denominator and leaves the scale
+ * to a normalisation layer after the attention (aicassindra.com page, "RetNet and gated
+ * linear attention"; learn.pranaymahendrakar.com page, "Implementation reality").
+ */
+typedef enum {
+    LINATTN_OUT_NORMALIZED = 0,   /* o = phi(q)^T S / max(phi(q)^T z, eps) */
+    LINATTN_OUT_NUMERATOR = 1     /* o = phi(q)^T S; eps is not used */
+} linattn_output_t;
+
+/*
  * Bytes of device scratch the chunked and gated forwards need for these sizes
  * (per-segment state totals and prefixes, float).  0 when B*H*N == 0 or a size is
  * not positive.  The same value serves both forwards.  Its contents are undefined
@@ -108,6 +119,20 @@ linattn_status_t linattn_fwd_gated(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The general forward: linattn_fwd_chunked when g is NULL, linattn_fwd_gated otherwise,
+ * with the output chosen by `out` (LINATTN_OUT_NORMALIZED gives exactly those two calls).
+ * In the numerator mode the state recurrence is unchanged: s_out and z_out receive the
+ * same S_N and z_N, so a sequence may be resumed in either mode.  An `out` outside the
+ * enum is LINATTN_ERR_INVALID_ARGUMENT.  Every other argument is as for
+ * linattn_fwd_gated, g [B,H,N] being optional.
+ */
+linattn_status_t linattn_fwd_ex(
+    const void* q, const void* k, const void* v, const float* g, void* o,
+    const float* s0, const float* z0, float* s_out, float* z_out,
+    int B, int H, int N, int D, int Dv, int chunk, linattn_dtype_t dtype, float eps,
+    linattn_output_t out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * One recurrent decode step for B*H independent heads (aiwiki.thehackersbrain.dev page,
  * "It is a linear RNN": O(D*Dv) work per token, no cache that grows):
  *
@@ -124,6 +149,26 @@ linattn_status_t linattn_fwd_gated(
 linattn_status_t linattn_decode_step(
     const void* q, const void* k, const void* v, float* S, float* z, void* o,
     int B, int H, int D, int Dv, linattn_dtype_t dtype, float eps, void* stream);
+
+/*
+ * The general decode step: the gated recurrence of linattn_fwd_gated for one token,
+ *
+ *     S <- g S + phi(k) v^T,  z <- g z + phi(k),  then o as chosen by `out`,
+ *
+ * the recurrent form of the gated forward (aicassindra.com page, "Linear Transformer:
+ * elu+1 and the RNN in disguise": the parallel form for training, the recurrence for
+ * generation; "RetNet and gated linear attention": S_i = gamma S_{i-1} + k_i v_i^T).
+ *
+ *  g  [B,H]  float or NULL  this token's gate per head, 0 < g <= 1 (not checked on the
+ *                           device); NULL means 1 and gives exactly linattn_decode_step
+ *  z  [B,H,D] float         updated in place; may be NULL only with LINATTN_OUT_NUMERATOR,
+ *                           and is then neither read nor written
+ *  out                      LINATTN_OUT_NORMALIZED or LINATTN_OUT_NUMERATOR
+ * Every other argument is as for linattn_decode_step; g must not overlap S, z or o.
+ */
+linattn_status_t linattn_decode_step_ex(
+    const void* q, const void* k, const void* v, const float* g, float* S, float* z, void* o,
+    int B, int H, int D, int Dv, linattn_dtype_t dtype, float eps, linattn_output_t out, void* stream);
 
 /*
  * Measurement hook, not part of the computation.  Arms the NEXT linattn_fwd_chunked or

@@ -26,7 +26,8 @@ Q, K, V, O, G, S0, Z0, SO, ZO, WS = (0x10_0000_0000 * (i + 1) for i in range(10)
 
 def declared_symbols():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"\b(linattn_[a-z_0-9]+)\s*\(", text)) - {"linattn_status_t", "linattn_dtype_t"})
+    return sorted(set(re.findall(r"\b(linattn_[a-z_0-9]+)\s*\(", text))
+                  - {"linattn_status_t", "linattn_dtype_t", "linattn_output_t"})
 
 
 def test_library_exports_every_declared_symbol():
@@ -59,7 +60,10 @@ def test_workspace_size():
 
 
 def fwd(q=Q, k=K, v=V, o=O, s0=0, z0=0, so=0, zo=0, B=1, H=2, N=256, D=64, Dv=64, chunk=128, dt=1, eps=1e-6,
-        ws=WS, wsb=1 << 30, gated=False, g=G):
+        ws=WS, wsb=1 << 30, gated=False, g=G, out=None):
+    if out is not None:
+        return binding.linattn_fwd_ex(q, k, v, g if gated else 0, o, s0, z0, so, zo, B, H, N, D, Dv, chunk, dt, eps,
+                                      out, ws, wsb, 0)
     if gated:
         return binding.linattn_fwd_gated(q, k, v, g, o, s0, z0, so, zo, B, H, N, D, Dv, chunk, dt, eps, ws, wsb, 0)
     return binding.linattn_fwd_chunked(q, k, v, o, s0, z0, so, zo, B, H, N, D, Dv, chunk, dt, eps, ws, wsb, 0)
@@ -105,8 +109,41 @@ def test_gated_requires_gate():
     assert fwd(gated=True, g=0) == INVALID
 
 
+@pytest.mark.parametrize("gated", [False, True])
+@pytest.mark.parametrize("out", [0, 1])
+def test_fwd_ex_checks_like_the_fixed_forwards(gated, out):
+    assert fwd(gated=gated, out=out, B=-1) == INVALID
+    assert fwd(gated=gated, out=out, eps=0.0) == INVALID
+    assert fwd(gated=gated, out=out, o=Q + 64) == INVALID
+    assert fwd(gated=gated, out=out, g=O + 32) == (INVALID if gated else fwd(gated=False))   # g overlaps o
+    assert fwd(gated=gated, out=out, D=96) == UNSUPPORTED
+    assert fwd(gated=gated, out=out, ws=0) == WORKSPACE
+    assert fwd(gated=gated, out=out, B=0, q=0, k=0, v=0, o=0, ws=0, wsb=0) == OK
+
+
+def test_fwd_ex_rejects_unknown_output_mode():
+    assert fwd(out=2) == INVALID
+    assert fwd(out=-1) == INVALID
+    assert fwd(out=2, gated=True) == INVALID
+
+
 def decode(q=Q, k=K, v=V, S=S0, z=Z0, o=O, B=4, H=2, D=128, Dv=128, dt=1, eps=1e-6):
     return binding.linattn_decode_step(q, k, v, S, z, o, B, H, D, Dv, dt, eps, 0)
+
+
+def decode_ex(q=Q, k=K, v=V, g=G, S=S0, z=Z0, o=O, B=4, H=2, D=128, Dv=128, dt=1, eps=1e-6, out=0):
+    return binding.linattn_decode_step_ex(q, k, v, g, S, z, o, B, H, D, Dv, dt, eps, out, 0)
+
+
+def test_decode_ex_rejects_bad_arguments():
+    assert decode_ex(out=2) == INVALID
+    assert decode_ex(z=0, out=0) == INVALID                     # the normalised output needs z
+    assert decode_ex(g=G + 4) == INVALID                        # misaligned gate
+    assert decode_ex(g=S0 + 16) == INVALID                      # gate overlaps S
+    assert decode_ex(g=O) == INVALID                            # gate overlaps o
+    assert decode_ex(S=0) == INVALID
+    assert decode_ex(D=96) == UNSUPPORTED
+    assert decode_ex(B=0, q=0) == OK
 
 
 def test_decode_rejects_bad_arguments():
@@ -124,4 +161,6 @@ def test_decode_rejects_bad_arguments():
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="only meaningful where no GPU is present")
 def test_no_device_is_reported_not_crashed():
     assert fwd() == HIP
+    assert fwd(out=1, gated=True) == HIP
     assert decode() == HIP
+    assert decode_ex(g=0, z=0, out=1) == HIP                    # valid: numerator mode needs no z
