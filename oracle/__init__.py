@@ -8,9 +8,12 @@ package imports nothing from them.
 Pins: every function here is pinned in ``tests/test_oracle.py`` against values
 fixed by the pages (worked examples stored under ``tests/golden/``), closed
 forms, invariants and brute force on tiny inputs; ``tests/test_oracle_mutants.py``
-plants mistakes in a copy of the recurrence and checks the pins catch each one.
+plants mistakes in a copy of the recurrence and checks the pins catch each one;
+``tests/test_oracle_bwd.py`` does the same for the backward (``tests/pins_bwd.py``).
 """
 from .recurrence import EPS, causal_linear_attention, decode_step, phi
 from .chunked import chunked_linear_attention
+from .backward import causal_linear_attention_bwd
 
-__all__ = ["EPS", "phi", "causal_linear_attention", "decode_step", "chunked_linear_attention"]
+__all__ = ["EPS", "phi", "causal_linear_attention", "decode_step", "chunked_linear_attention",
+           "causal_linear_attention_bwd"]
