@@ -6,10 +6,13 @@ build script and the seeded synthetic workloads.  Importing the package does
 not load the library; the first call does, and raises if it is missing.
 """
 from .binding import (  # noqa: F401
+    bwd,
     decode_step,
     fwd,
     fwd_chunked,
     fwd_gated,
+    linattn_bwd,
+    linattn_bwd_workspace_size,
     linattn_decode_step,
     linattn_decode_step_ex,
     linattn_fwd_chunked,

@@ -8,8 +8,9 @@ no fallback: if the library is missing, every call raises.
 
 Function names match the C ABI (include/linattn.h):
     linattn_fwd_chunked, linattn_fwd_gated, linattn_fwd_ex, linattn_decode_step,
-    linattn_decode_step_ex, linattn_fwd_workspace_size, linattn_status_string
-plus the tensor-level helpers fwd_chunked, fwd_gated, fwd and decode_step.
+    linattn_decode_step_ex, linattn_fwd_workspace_size, linattn_bwd,
+    linattn_bwd_workspace_size, linattn_status_string
+plus the tensor-level helpers fwd_chunked, fwd_gated, fwd, bwd and decode_step.
 """
 from __future__ import annotations
 
@@ -41,6 +42,9 @@ EXPORTS = {
     "linattn_fwd_ex": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i, _p, _sz, _p]),
     "linattn_decode_step": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p]),
     "linattn_decode_step_ex": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p]),
+    "linattn_bwd_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "linattn_bwd": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p, _sz,
+                         _p]),
     "linattn_status_string": (ctypes.c_char_p, [_i]),
     "linattn_set_profile_events": (_i, [_p, _p, _p, _p]),
 }
@@ -101,6 +105,16 @@ def linattn_decode_step(q, k, v, S, z, o, B, H, D, Dv, dtype, eps, stream) -> in
 
 def linattn_decode_step_ex(q, k, v, g, S, z, o, B, H, D, Dv, dtype, eps, out, stream) -> int:
     return int(lib().linattn_decode_step_ex(q, k, v, g, S, z, o, B, H, D, Dv, dtype, eps, out, stream))
+
+
+def linattn_bwd_workspace_size(B, H, N, D, Dv, dtype) -> int:
+    return int(lib().linattn_bwd_workspace_size(B, H, N, D, Dv, dtype))
+
+
+def linattn_bwd(q, k, v, g, dout, s0, z0, dq, dk, dv, dg, ds0, dz0, B, H, N, D, Dv, dtype, eps, out, ws, ws_bytes,
+                stream) -> int:
+    return int(lib().linattn_bwd(q, k, v, g, dout, s0, z0, dq, dk, dv, dg, ds0, dz0, B, H, N, D, Dv, dtype, eps, out,
+                                 ws, ws_bytes, stream))
 
 
 def linattn_set_profile_events(ev0, ev1, ev2, ev3) -> int:
@@ -209,6 +223,49 @@ def fwd(q, k, v, g=None, chunk=128, eps=1e-6, s0=None, z0=None, return_state=Fal
     """The general forward (linattn_fwd_ex): optional gate g [B,H,N] float32, and
     ``normalize=False`` for the normaliser-free output o = phi(q)^T S."""
     return _fwd(q, k, v, g, chunk, eps, s0, z0, return_state, out, workspace, normalize)
+
+
+def bwd(q, k, v, dout, g=None, s0=None, z0=None, eps=1e-6, normalize=True, state_grads=False, workspace=None,
+        grads=None):
+    """Gradients of sum(dout * o) for o = fwd(q, k, v, g, s0=s0, z0=z0, eps=eps, normalize=normalize).
+    Returns a dict with dq, dk, dv, dg (None when ungated) and, with ``state_grads``, ds0
+    and dz0.  ``grads`` may hold preallocated dq, dk, dv, dg tensors."""
+    dt = _dtype_code(q)
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
+        _need(t, n, q.dtype, dev)
+    for t, n in ((g, "g"), (s0, "s0"), (z0, "z0")):
+        _need(t, n, torch.float32, dev)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, D]")
+    B, H, N, D = q.shape
+    Dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or dout.shape != v.shape:
+        raise ValueError("k must match q; v and dout must be [B, H, N, Dv]")
+    if g is not None and tuple(g.shape) != (B, H, N):
+        raise ValueError("g must be [B, H, N]")
+    grads = dict(grads or {})
+    dq = grads.get("dq") if grads.get("dq") is not None else torch.empty_like(q)
+    dk = grads.get("dk") if grads.get("dk") is not None else torch.empty_like(k)
+    dv = grads.get("dv") if grads.get("dv") is not None else torch.empty_like(v)
+    dg = None
+    if g is not None:
+        dg = grads.get("dg") if grads.get("dg") is not None else torch.empty_like(g)
+    ds0 = dz0 = None
+    if state_grads:
+        ds0 = torch.empty(B, H, D, Dv, dtype=torch.float32, device=dev)
+        dz0 = torch.empty(B, H, D, dtype=torch.float32, device=dev)
+    nbytes = linattn_bwd_workspace_size(B, H, N, D, Dv, dt)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError("workspace too small")
+    code = linattn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(dout), _ptr(s0), _ptr(z0), _ptr(dq), _ptr(dk), _ptr(dv),
+                       _ptr(dg), _ptr(ds0), _ptr(dz0), B, H, N, D, Dv, dt, eps,
+                       OUT_NORMALIZED if normalize else OUT_NUMERATOR, _ptr(workspace),
+                       workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(code, "linattn_bwd")
+    return {"dq": dq, "dk": dk, "dv": dv, "dg": dg, "ds0": ds0, "dz0": dz0}
 
 
 def decode_step(q, k, v, S, z, eps=1e-6, out=None, g=None, normalize=True):

@@ -209,9 +209,78 @@ linattn_status_t decode_common(const void* q, const void* k, const void* v, cons
     return e == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP;
 }
 
+linattn_status_t bwd_common(const void* q, const void* k, const void* v, const float* g, const void* dout,
+                            const float* s0, const float* z0, void* dq, void* dk, void* dv, float* dg, float* ds0,
+                            float* dz0, int B, int H, int N, int D, int Dv, linattn_dtype_t dtype, float eps,
+                            linattn_output_t out, void* ws, size_t ws_bytes, void* stream) {
+    if (B < 0 || H < 0 || N < 0 || D <= 0 || Dv <= 0) return LINATTN_ERR_INVALID_ARGUMENT;
+    if (!dtype_ok(dtype) || !out_ok(out) || !(eps > 0.0f) || !std::isfinite(eps)) return LINATTN_ERR_INVALID_ARGUMENT;
+    const long BH = long(B) * long(H);
+    if (BH == 0 || N == 0) return LINATTN_OK;
+    if (BH > (1L << 24) || long(N) * BH > (1L << 40)) return LINATTN_ERR_INVALID_ARGUMENT;
+    if (!q || !k || !v || !dout || !dq || !dk || !dv) return LINATTN_ERR_INVALID_ARGUMENT;
+    for (const void* p : {q, k, v, dout, static_cast<const void*>(dq), static_cast<const void*>(dk),
+                          static_cast<const void*>(dv), static_cast<const void*>(g), static_cast<const void*>(s0),
+                          static_cast<const void*>(z0), static_cast<const void*>(dg), static_cast<const void*>(ds0),
+                          static_cast<const void*>(dz0)})
+        if (p && !aligned16(p)) return LINATTN_ERR_INVALID_ARGUMENT;
+    const size_t es = esize(dtype);
+    const size_t nqk = size_t(BH) * N * D * es, nv = size_t(BH) * N * Dv * es, ng = size_t(BH) * N * 4;
+    const size_t ns = size_t(BH) * D * Dv * 4, nz = size_t(BH) * D * 4;
+    struct Buf { const void* p; size_t n; };
+    const Buf ins[] = {{q, nqk}, {k, nqk}, {v, nv}, {g, ng}, {dout, nv}, {s0, ns}, {z0, nz}};
+    const Buf outs[] = {{dq, nqk}, {dk, nqk}, {dv, nv}, {g ? dg : nullptr, ng}, {ds0, ns}, {dz0, nz}};
+    for (const Buf& o : outs) {
+        for (const Buf& i : ins)
+            if (overlap(o.p, o.n, i.p, i.n)) return LINATTN_ERR_INVALID_ARGUMENT;
+        for (const Buf& o2 : outs)
+            if (&o2 != &o && overlap(o.p, o.n, o2.p, o2.n)) return LINATTN_ERR_INVALID_ARGUMENT;
+    }
+    if ((size_t(N) + 256) * size_t(Dv > D ? Dv : D) * es >= (size_t(1) << 31)) return LINATTN_ERR_UNSUPPORTED;
+    if (!dim_ok(D) || !dim_ok(Dv) || linattn::bwd_lds_bytes(int(es), D, Dv) > linattn::kMaxLds)
+        return LINATTN_ERR_UNSUPPORTED;
+    const linattn::BwdLayout lay = linattn::bwd_workspace_layout(size_t(BH), N, D, Dv);
+    if (ws_bytes < lay.bytes || !ws || !aligned16(ws)) return LINATTN_ERR_WORKSPACE;
+    for (const Buf& b : ins)
+        if (overlap(ws, lay.bytes, b.p, b.n)) return LINATTN_ERR_WORKSPACE;
+    for (const Buf& b : outs)
+        if (overlap(ws, lay.bytes, b.p, b.n)) return LINATTN_ERR_WORKSPACE;
+    const linattn_status_t dst = check_device();
+    if (dst != LINATTN_OK) return dst;
+
+    linattn::BwdLaunch L;
+    L.q = q; L.k = k; L.v = v; L.g = g; L.dout = dout; L.s0 = s0; L.z0 = z0;
+    L.dq = dq; L.dk = dk; L.dv = dv; L.dg = g ? dg : nullptr; L.ds0 = ds0; L.dz0 = dz0;
+    L.ws = ws;
+    L.BH = int(BH); L.N = N; L.D = D; L.Dv = Dv;
+    L.eps = eps;
+    L.normalize = out == LINATTN_OUT_NORMALIZED ? 1 : 0;
+    L.stream = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    const hipError_t e = dtype == LINATTN_BF16 ? linattn::launch_bwd_bf16(L) : linattn::launch_bwd_f32(L);
+    return e == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t linattn_bwd_workspace_size(int B, int H, int N, int D, int Dv, linattn_dtype_t dtype) {
+    if (B <= 0 || H <= 0 || N <= 0 || D <= 0 || Dv <= 0 || !dtype_ok(dtype)) return 0;
+    return linattn::bwd_workspace_layout(size_t(B) * size_t(H), N, D, Dv).bytes;
+}
+
+linattn_status_t linattn_bwd(const void* q, const void* k, const void* v, const float* g, const void* dout,
+                             const float* s0, const float* z0, void* dq, void* dk, void* dv, float* dg, float* ds0,
+                             float* dz0, int B, int H, int N, int D, int Dv, linattn_dtype_t dtype, float eps,
+                             linattn_output_t out, void* workspace, size_t workspace_bytes, void* stream) {
+    try {
+        return bwd_common(q, k, v, g, dout, s0, z0, dq, dk, dv, dg, ds0, dz0, B, H, N, D, Dv, dtype, eps, out,
+                          workspace, workspace_bytes, stream);
+    } catch (...) {
+        return LINATTN_ERR_HIP;
+    }
+}
 
 size_t linattn_fwd_workspace_size(int B, int H, int N, int D, int Dv, int chunk) {
     if (B <= 0 || H <= 0 || N <= 0 || D <= 0 || Dv <= 0 || chunk <= 0) return 0;

@@ -1,0 +1,792 @@
+// Gradients of the chunked forward on gfx950: dq, dk, dv, dg and the initial-state
+// gradients, for both output modes.
+//
+// The pages give the forward only and call the chunked form the training path
+// (aiwiki.thehackersbrain.dev page, the chunked listing's closing paragraph;
+// learn.pranaymahendrakar.com page, "Implementation reality").  The gradients are
+// those of the recurrence S_t = g_t S_{t-1} + phi(k_t) v_t^T, z alike, with
+// o_t = S_t^T phi(q_t) / max(phi(q_t) . z_t, eps) (learn.pranaymahendrakar.com page,
+// "Derivation" and "Try it yourself"), taken chunk by chunk.  With do the incoming
+// gradient, d_i = max(den_i, eps) and, where den_i >= eps,
+//     dnum_i = do_i / d_i,   dden_i = -(do_i . o_i) / d_i         (0 below the clamp)
+// (dnum_i = do_i and dden_i = 0 without the normaliser), and pairwise weights
+// w_ij = prod_{l=j+1..i} g_l for j <= i:
+//     dphi(q_i) = sum_{j<=i} w_ij (dnum_i . v_j + dden_i) phi(k_j)   (+ the S0 / z0 terms)
+//     dphi(k_j) = sum_{i>=j} w_ij (dnum_i . v_j + dden_i) phi(q_i)
+//     dv_j      = sum_{i>=j} w_ij (phi(q_i) . phi(k_j)) dnum_i
+//     d log g_l = sum over the pairs j < l <= i of P_ij,  P_ij = w_ij (phi(q_i) . phi(k_j)) (dnum_i . v_j + dden_i)
+// the last because log g_l enters exactly the weights w_ij of the pairs it separates
+// (the initial state counting as a key in front of token 0).
+//
+// Work per chunk of C = 64 tokens (one workgroup of four waves, wave w owning rows
+// 16w .. 16w + 15 of the chunk), with chunk-local Lambda_i = sum_{l=s..i} log2 g_l:
+//   bwd_dq_kernel   recomputes A = (Fq Fk^T) o decay o mask, num and den from the
+//                   state in front of the chunk, forms 1/d and dden, then
+//                   dFq = B Fk + 2^Lambda_i (dNum S_prev^T + dden z_prev^T) with
+//                   B = (dNum V^T + dden 1^T) o decay o mask, and folds the chunk's
+//                   adjoint total dR_c = Fq^T (2^Lambda dNum), dr_c = Fq^T (2^Lambda dden).
+//   bwd_dkv_kernel  with R, r the adjoint of the state at the chunk's end:
+//                   dFk = B^T Fq + 2^(Lambda_last - Lambda_j) (V R^T + 1 r^T),
+//                   dV  = A^T dNum + 2^(Lambda_last - Lambda_j) Fk R.
+// dNum never enters a product rounded: the products take the exact input dout and
+// scale by 1/d in fp32 (dNum V^T = diag(1/d) dOut V^T).  With the normaliser, dFq_i is
+// orthogonal to Fq_i (its terms cancel), and a rounded dnum breaks that cancellation
+// where d is small.
+//   bwd_dg_kernel   d log g_l for token l of chunk c as four sums that never leave the
+//                   chunk: the pairs inside it (X_l, from fp32 row and column sums of P
+//                   in the dq pass), keys in front of it against its queries i >= l
+//                   (Y_l, the running sum of Fq_i . dFq_i's carried-state part), its keys
+//                   j < l against later queries (Z_l, of Fk_j . dFk_j's carried-state
+//                   part) and keys in front against later queries (W_c =
+//                   2^Lambda_last (<R, S_prev> + <r, z_prev>)).  A running sum over the
+//                   whole sequence would cancel to the initial state's term and collect
+//                   the rounding of every token on the way.
+// The states in front of every chunk come from the forward's totals walk (one chunk
+// per segment) and its scan; the adjoint states from the same scan run over the
+// chunks' adjoint totals in reverse order.  Every MFMA operand is staged in LDS as a
+// row-major tile; an operand whose contraction index runs down the tile's rows is
+// read with ds_read_b64_tr_b16 (bf16) or element by element (fp32).
+#pragma once
+
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace linattn {
+
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;      // NULL: ungated
+    const void* dout;
+    const float* s0;     // [BH][D][Dv] or NULL
+    const float* z0;     // [BH][D] or NULL
+    void* dq;
+    void* dk;
+    void* dv;
+    float* fst;          // [BH][NC][D*Dv] accumulator layout: slot c < NC-1 holds the state after chunk c
+    float* fzt;          // [BH][NC][D]
+    float* rst;          // [BH][NC+1][D*Dv]: chunk c's adjoint total at slot NC-1-c; after the
+                         // scan slot NC-2-c holds the adjoint of the state after chunk c, and
+                         // slot NC-1 the gradient of S0
+    float* rzt;          // [BH][NC+1][D], alike
+    float* rlg;          // [BH][NC+1] log2 of each chunk's total decay, reversed like rst
+    float* inv;          // [BH][N]: 1 / max(den, eps) of every token (1 without the normaliser)
+    float* dden;         // [BH][N]
+    float* xs;           // [BH][N]: X_l, the pairs inside the chunk that straddle l
+    float* yq;           // [BH][N]: Fq_i . (carried-state part of dFq_i)
+    float* zk;           // [BH][N]: Fk_j . (carried-state part of dFk_j)
+    float* wc;           // [BH][NC]: W_c
+    int N;
+    int NC;
+    float eps;
+    int normalize;
+};
+
+constexpr int kBwdChunk = kBwdChunkHost;
+
+template <typename E, int D, int DV>
+struct BwdShape {
+    static constexpr int C = kBwdChunk;
+    static constexpr int PAD = 16 / int(sizeof(E));   // one 16-byte group per row
+    static constexpr int LQ = D + PAD;                 // phi(Q), phi(K) [C][D]
+    static constexpr int LV = DV + PAD;                // V, dNum [C][Dv]; S_prev / R [D][Dv]
+    static constexpr int LA = C + PAD;                 // A or B [C][C]
+    static constexpr size_t kOffQ = 0;
+    static constexpr size_t kOffK = kOffQ + size_t(C) * LQ * sizeof(E);
+    static constexpr size_t kOffV = kOffK + size_t(C) * LQ * sizeof(E);
+    static constexpr size_t kOffDn = kOffV + size_t(C) * LV * sizeof(E);
+    static constexpr size_t kOffS = kOffDn + size_t(C) * LV * sizeof(E);
+    static constexpr size_t kOffA = kOffS + size_t(D) * LV * sizeof(E);
+    static constexpr size_t kOffLam = kOffA + size_t(C) * LA * sizeof(E);
+    static constexpr size_t kOffDd = kOffLam + size_t(C) * 4;
+    static constexpr size_t kOffInv = kOffDd + size_t(C) * 4;
+    static constexpr size_t kOffCol = kOffInv + size_t(C) * 4;     // [4][C] per-wave column sums of P
+    static constexpr size_t kOffRow = kOffCol + size_t(4) * C * 4;  // [C] row sums of P
+    static constexpr size_t kOffZ = kOffRow + size_t(C) * 4;
+    static constexpr size_t kBytes = kOffZ + size_t(D) * 4;
+    static_assert(kBytes == bwd_lds_bytes(int(sizeof(E)), D, DV), "host LDS formula out of step");
+};
+
+// Operand of 16 rows from a row-major tile: lane supplies row `row`, contraction
+// slots k0 .. k0 + 7 (k0 includes the lane group's offset), one 16-byte read (bf16).
+template <typename E>
+__device__ __forceinline__ F8<E> frag_row(const E* t, int ld, int row, int k0) {
+    return lds_f8(t + row * ld + k0);
+}
+
+// Operand whose contraction index runs down the rows of a row-major tile: slot e of
+// lane l holds t[k0 + e][n0 + l % 16].  bf16: two ds_read_b64_tr_b16, each giving a
+// 16-lane block four rows of one column when block lane j points at row k0 + j / 4,
+// columns n0 + 4 (j % 4) .. + 3.  fp32: eight reads.
+__device__ __forceinline__ F8<uint16_t> frag_col(const uint16_t* t, int ld, int k0, int n0, int l16) {
+    typedef short i16x4_t __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) i16x4_t* lds_ptr_t;
+    const uint16_t* p = t + (k0 + (l16 >> 2)) * ld + n0 + 4 * (l16 & 3);
+    const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr_t)(const_cast<uint16_t*>(p)));
+    const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr_t)(const_cast<uint16_t*>(p + 4 * ld)));
+    F8<uint16_t> f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f.x[e] = uint16_t(a[e]);
+        f.x[4 + e] = uint16_t(b[e]);
+    }
+    return f;
+}
+
+__device__ __forceinline__ F8<float> frag_col(const float* t, int ld, int k0, int n0, int l16) {
+    F8<float> f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.x[e] = t[(k0 + e) * ld + n0 + l16];
+    return f;
+}
+
+// Sum over the 16 lanes of a lane group (the columns of an accumulator row).
+__device__ __forceinline__ float sum16(float x) {
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off, kWave);
+    return x;
+}
+
+// elu + 1 and its derivative at x (1 above zero, exp(x) at or below).
+__device__ __forceinline__ float dphi(float x) { return x > 0.0f ? 1.0f : __builtin_amdgcn_exp2f(x * kLog2e); }
+
+// The per-workgroup machinery shared by both gradient kernels.
+template <typename E, int D, int DV, bool GATED>
+struct BwdChunk {
+    using Sh = BwdShape<E, D, DV>;
+    using X = Elem<E>;
+    static constexpr int C = Sh::C, LQ = Sh::LQ, LV = Sh::LV, LA = Sh::LA;
+    static constexpr int GQ = D * int(sizeof(E)) / 16;    // 16-byte groups per q/k row
+    static constexpr int GV = DV * int(sizeof(E)) / 16;   // per v row
+    static constexpr int EPG = 16 / int(sizeof(E));       // elements per group
+
+    E* sQ;
+    E* sK;
+    E* sV;
+    E* sDn;
+    E* sS;
+    E* sA;
+    float* sLam;
+    float* sDd;
+    float* sInv;
+    float* sCol;
+    float* sRow;
+    float* sZ;
+    int tid, w, lane, l16, g4;
+    int bh, c, ts, nrows, N, NC;
+
+    __device__ __forceinline__ void init(unsigned char* smem, int N_, int NC_) {
+        sQ = reinterpret_cast<E*>(smem + Sh::kOffQ);
+        sK = reinterpret_cast<E*>(smem + Sh::kOffK);
+        sV = reinterpret_cast<E*>(smem + Sh::kOffV);
+        sDn = reinterpret_cast<E*>(smem + Sh::kOffDn);
+        sS = reinterpret_cast<E*>(smem + Sh::kOffS);
+        sA = reinterpret_cast<E*>(smem + Sh::kOffA);
+        sLam = reinterpret_cast<float*>(smem + Sh::kOffLam);
+        sDd = reinterpret_cast<float*>(smem + Sh::kOffDd);
+        sInv = reinterpret_cast<float*>(smem + Sh::kOffInv);
+        sCol = reinterpret_cast<float*>(smem + Sh::kOffCol);
+        sRow = reinterpret_cast<float*>(smem + Sh::kOffRow);
+        sZ = reinterpret_cast<float*>(smem + Sh::kOffZ);
+        tid = threadIdx.x;
+        w = __builtin_amdgcn_readfirstlane(tid / kWave);
+        lane = tid % kWave;
+        l16 = lane & 15;
+        g4 = lane >> 4;
+        N = N_;
+        NC = NC_;
+        c = blockIdx.x % NC;
+        bh = blockIdx.x / NC;
+        ts = c * C;
+        nrows = min(C, N - ts);
+    }
+
+    // Rows [ts, ts + C) of a [N][W] tensor into a row-major tile, through f (phi or the
+    // identity) in fp32; rows past the chunk's end are zero.
+    template <int W, bool PHI>
+    __device__ __forceinline__ void stage_rows(E* tile, int ld, const E* src) const {
+        constexpr int G = W * int(sizeof(E)) / 16;
+        for (int u = tid; u < C * G; u += kThreads) {
+            const int row = u / G, col = (u % G) * EPG;
+            F8<E> out;
+            if (row < nrows) {
+                const E* p = src + size_t(ts + row) * W + col;
+                if constexpr (sizeof(E) == 2) {
+                    const F8<E> in = *reinterpret_cast<const F8<E>*>(p);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) out.x[e] = PHI ? X::from_f32(phi(X::to_f32(in.x[e]))) : in.x[e];
+                } else {
+                    const F4<E> in = *reinterpret_cast<const F4<E>*>(p);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) out.x[e] = PHI ? phi(in.x[e]) : in.x[e];
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) out.x[e] = E(0);
+            }
+            if constexpr (sizeof(E) == 2)
+                *reinterpret_cast<F8<E>*>(tile + row * ld + col) = out;
+            else
+                *reinterpret_cast<F4<E>*>(tile + row * ld + col) = *reinterpret_cast<const F4<E>*>(&out);
+        }
+    }
+
+    // A [D][Dv] state into sS (row-major, operand precision) and its z part into sZ, from
+    // a workspace slot in accumulator layout, from the caller's layout, or zero.
+    __device__ __forceinline__ void stage_state(const float* slot_s, const float* slot_z, const float* user_s,
+                                                const float* user_z) const {
+        if (slot_s) {
+            for (int q4 = tid; q4 < D * DV / 4; q4 += kThreads) {
+                const f32x4_t v = *reinterpret_cast<const f32x4_t*>(slot_s + 4 * q4);
+                const int u = q4 / kWave, ln = q4 % kWave;
+                const int a = u / (DV / 16), b = u % (DV / 16);
+                const int d = 16 * a + 4 * (ln >> 4), e = 16 * b + (ln & 15);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sS[(d + r) * LV + e] = X::from_f32(v[r]);
+            }
+        } else {
+            for (int q4 = tid; q4 < D * DV / 4; q4 += kThreads) {
+                const int d = q4 / (DV / 4), e = 4 * (q4 % (DV / 4));
+                f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+                if (user_s) v = *reinterpret_cast<const f32x4_t*>(user_s + size_t(d) * DV + e);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sS[d * LV + e + r] = X::from_f32(v[r]);
+            }
+        }
+        for (int d = tid; d < D; d += kThreads) sZ[d] = slot_z ? slot_z[d] : (user_z ? user_z[d] : 0.0f);
+    }
+
+    // Chunk-local inclusive log2 cumulative decay into sLam (wave 0); rows past the end
+    // get a unit gate.  Returns nothing; sLam[C - 1] is the chunk's total.
+    __device__ __forceinline__ void stage_lambda(const float* gb) const {
+        if constexpr (GATED) {
+            if (w == 0) {
+                float x = lane < nrows ? fast_log2(gb[ts + lane]) : 0.0f;
+#pragma unroll
+                for (int off = 1; off < kWave; off <<= 1) {
+                    const float y = __shfl_up(x, off, kWave);
+                    if (lane >= off) x += y;
+                }
+                sLam[lane] = x;
+            }
+        }
+    }
+
+    __device__ __forceinline__ float lam(int i) const {
+        if constexpr (GATED) return sLam[i];
+        return 0.0f;
+    }
+};
+
+// ----------------------------------------------------------------- dq pass ----
+
+template <typename E, int D, int DV, bool GATED>
+__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs args) {
+    using B = BwdChunk<E, D, DV, GATED>;
+    using X = Elem<E>;
+    constexpr int C = B::C, LQ = B::LQ, LV = B::LV, LA = B::LA;
+    constexpr int ND = D / 16, NE = DV / 16, NJ = C / 16;
+    extern __shared__ __align__(16) unsigned char smem[];
+    B ck;
+    ck.init(smem, args.N, args.NC);
+    const int w = ck.w, lane = ck.lane, l16 = ck.l16, g4 = ck.g4, bh = ck.bh, c = ck.c, ts = ck.ts;
+    const int N = args.N, NC = args.NC;
+    const E* qb = reinterpret_cast<const E*>(args.q) + size_t(bh) * N * D;
+    const E* kb = reinterpret_cast<const E*>(args.k) + size_t(bh) * N * D;
+    const E* vb = reinterpret_cast<const E*>(args.v) + size_t(bh) * N * DV;
+    const E* dob = reinterpret_cast<const E*>(args.dout) + size_t(bh) * N * DV;
+
+    ck.template stage_rows<D, true>(ck.sQ, LQ, qb);
+    ck.template stage_rows<D, true>(ck.sK, LQ, kb);
+    ck.template stage_rows<DV, false>(ck.sV, LV, vb);
+    ck.template stage_rows<DV, false>(ck.sDn, LV, dob);
+    const size_t fslot = size_t(bh) * NC + (c - 1);
+    ck.stage_state(c > 0 ? args.fst + fslot * (D * DV) : nullptr, c > 0 ? args.fzt + fslot * D : nullptr,
+                   args.s0 ? args.s0 + size_t(bh) * D * DV : nullptr, args.z0 ? args.z0 + size_t(bh) * D : nullptr);
+    ck.stage_lambda(GATED ? args.g + size_t(bh) * N : nullptr);
+    __syncthreads();
+
+    const int i0 = 16 * w;            // this wave's query rows
+    float lam_r[4], rs[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) lam_r[r] = ck.lam(i0 + 4 * g4 + r);
+
+    // A = Fq Fk^T, decayed and masked, into sA (rows of this wave); row sums in fp32.
+    // acc keeps the undecayed fp32 scores for the pair sums of d log g.
+    f32x4_t acc[NJ];
+    {
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) acc[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+            const F8<E> a = frag_row(ck.sQ, LQ, i0 + l16, 32 * ks + 8 * g4);
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt)
+                if (jt <= w) acc[jt] = mma(a, frag_row(ck.sK, LQ, 16 * jt + l16, 32 * ks + 8 * g4), acc[jt]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) rs[r] = 0.0f;
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) {
+            const int j = 16 * jt + l16;
+            const float lj = ck.lam(j);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = i0 + 4 * g4 + r;
+                float x = (jt <= w && j <= i) ? acc[jt][r] : 0.0f;
+                if constexpr (GATED) x *= fast_exp2(fminf(lam_r[r] - lj, 0.0f));
+                const E xe = X::from_f32(x);
+                ck.sA[i * LA + j] = xe;
+                rs[r] += X::to_f32(xe);          // the row sum of the values the numerator uses
+            }
+        }
+    }
+    // den = 2^Lambda_i Fq_i . z_prev + sum_j A_ij
+    float den[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int i = i0 + 4 * g4 + r;
+        float zt = 0.0f;
+#pragma unroll
+        for (int t = 0; t < ND; ++t) zt += X::to_f32(ck.sQ[i * LQ + 16 * t + l16]) * ck.sZ[16 * t + l16];
+        den[r] = sum16(rs[r] + (GATED ? fast_exp2(lam_r[r]) : 1.0f) * zt);
+    }
+    __syncthreads();
+
+    // num = 2^Lambda_i Fq S_prev + A V
+    f32x4_t num[NE];
+#pragma unroll
+    for (int et = 0; et < NE; ++et) num[et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+        const F8<E> a = frag_row(ck.sQ, LQ, i0 + l16, 32 * ks + 8 * g4);
+#pragma unroll
+        for (int et = 0; et < NE; ++et) num[et] = mma(a, frag_col(ck.sS, LV, 32 * ks + 8 * g4, 16 * et, l16), num[et]);
+    }
+    if constexpr (GATED) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float f = fast_exp2(lam_r[r]);
+#pragma unroll
+            for (int et = 0; et < NE; ++et) num[et][r] *= f;
+        }
+    }
+    for (int ks = 0; ks <= (w >> 1); ++ks) {
+        const F8<E> a = frag_row(ck.sA, LA, i0 + l16, 32 * ks + 8 * g4);
+#pragma unroll
+        for (int et = 0; et < NE; ++et) num[et] = mma(a, frag_col(ck.sV, LV, 32 * ks + 8 * g4, 16 * et, l16), num[et]);
+    }
+
+    // 1/d and dden = -(dout . num) / d^2 (fp32); dnum = dout / d stays implicit
+    float dd[4], inv[4];
+    {
+        float dsum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) inv[r] = args.normalize ? 1.0f / fmaxf(den[r], args.eps) : 1.0f;
+#pragma unroll
+        for (int et = 0; et < NE; ++et)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                dsum[r] += X::to_f32(ck.sDn[(i0 + 4 * g4 + r) * LV + 16 * et + l16]) * num[et][r];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float s = sum16(dsum[r]);
+            const int i = i0 + 4 * g4 + r;
+            dd[r] = (args.normalize && den[r] >= args.eps) ? -s * inv[r] * inv[r] : 0.0f;
+            if (l16 == 0 && ts + i < N) {
+                args.dden[size_t(bh) * N + ts + i] = dd[r];
+                args.inv[size_t(bh) * N + ts + i] = inv[r];
+            }
+        }
+    }
+    __syncthreads();
+
+    // B = (diag(1/d) dOut V^T + dden 1^T) o decay o mask over this wave's rows, into sA
+    // (every read of A finished before the barrier above); with it the pair terms
+    // P_ij = (Fq_i . Fk_j) B_ij in fp32, summed by row (j < i) and by column (i > j)
+    {
+        f32x4_t bb[NJ];
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) bb[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < DV / 32; ++ks) {
+            const F8<E> a = frag_row(ck.sDn, LV, i0 + l16, 32 * ks + 8 * g4);
+#pragma unroll
+            for (int jt = 0; jt < NJ; ++jt)
+                if (jt <= w) bb[jt] = mma(a, frag_row(ck.sV, LV, 16 * jt + l16, 32 * ks + 8 * g4), bb[jt]);
+        }
+        float prow[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int jt = 0; jt < NJ; ++jt) {
+            const int j = 16 * jt + l16;
+            const float lj = ck.lam(j);
+            float pcol = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = i0 + 4 * g4 + r;
+                float x = (jt <= w && j <= i) ? bb[jt][r] * inv[r] + dd[r] : 0.0f;
+                if constexpr (GATED) x *= fast_exp2(fminf(lam_r[r] - lj, 0.0f));
+                ck.sA[i * LA + j] = X::from_f32(x);
+                if constexpr (GATED) {
+                    const float pij = j < i ? acc[jt][r] * x : 0.0f;
+                    prow[r] += pij;
+                    pcol += pij;
+                }
+            }
+            if constexpr (GATED) {
+                pcol += __shfl_xor(pcol, 16, kWave);
+                pcol += __shfl_xor(pcol, 32, kWave);
+                if (g4 == 0) ck.sCol[w * C + j] = pcol;
+            }
+        }
+        if constexpr (GATED) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float sr = sum16(prow[r]);
+                if (l16 == 0) ck.sRow[i0 + 4 * g4 + r] = sr;
+            }
+        }
+    }
+    __syncthreads();
+    // X_l = sum_{m < l} (col_m - row_m): the pairs inside the chunk with j < l <= i
+    if (GATED && w == 0) {
+        const float dm = ck.sCol[lane] + ck.sCol[C + lane] + ck.sCol[2 * C + lane] + ck.sCol[3 * C + lane] -
+                         ck.sRow[lane];
+        float x = dm;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const float y = __shfl_up(x, off, kWave);
+            if (lane >= off) x += y;
+        }
+        if (lane < ck.nrows) args.xs[size_t(bh) * N + ts + lane] = x - dm;
+    }
+
+    // dFq = 2^Lambda_i (diag(1/d) dOut S_prev^T + dden z_prev^T) + B Fk
+    f32x4_t dfq[ND];
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) dfq[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < DV / 32; ++ks) {
+        const F8<E> a = frag_row(ck.sDn, LV, i0 + l16, 32 * ks + 8 * g4);
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) dfq[dt] = mma(a, frag_row(ck.sS, LV, 16 * dt + l16, 32 * ks + 8 * g4), dfq[dt]);
+    }
+    {
+        float yq[4] = {0.f, 0.f, 0.f, 0.f};            // Fq_i . (carried-state part of dFq_i)
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) {
+            const float zd = ck.sZ[16 * dt + l16];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float x = dfq[dt][r] * inv[r] + dd[r] * zd;
+                dfq[dt][r] = GATED ? x * fast_exp2(lam_r[r]) : x;
+                if constexpr (GATED) yq[r] += X::to_f32(ck.sQ[(i0 + 4 * g4 + r) * LQ + 16 * dt + l16]) * dfq[dt][r];
+            }
+        }
+        if constexpr (GATED) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float s = sum16(yq[r]);
+                const int i = i0 + 4 * g4 + r;
+                if (l16 == 0 && ts + i < N) args.yq[size_t(bh) * N + ts + i] = s;
+            }
+        }
+    }
+    for (int ks = 0; ks <= (w >> 1); ++ks) {
+        const F8<E> a = frag_row(ck.sA, LA, i0 + l16, 32 * ks + 8 * g4);
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) dfq[dt] = mma(a, frag_col(ck.sK, LQ, 32 * ks + 8 * g4, 16 * dt, l16), dfq[dt]);
+    }
+
+    // dq = dFq * phi'(q)
+    {
+        E* dqb = reinterpret_cast<E*>(args.dq) + size_t(bh) * N * D;
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = i0 + 4 * g4 + r;
+                if (ts + i < N) {
+                    const float x = X::to_f32(qb[size_t(ts + i) * D + 16 * dt + l16]);
+                    dqb[size_t(ts + i) * D + 16 * dt + l16] = X::from_f32(dfq[dt][r] * dphi(x));
+                }
+            }
+        }
+    }
+
+    // the chunk's adjoint total: dR_c = Fq^T (2^Lambda dNum), dr_c = Fq^T (2^Lambda dden);
+    // this wave's rows of dOut become 2^Lambda_i dnum_i (every other read of them is done)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int i = i0 + 4 * g4 + r;
+        const float f = GATED ? fast_exp2(lam_r[r]) : 1.0f;
+#pragma unroll
+        for (int et = 0; et < NE; ++et) {
+            E& x = ck.sDn[i * LV + 16 * et + l16];
+            x = X::from_f32(X::to_f32(x) * (f * inv[r]));
+        }
+        if (l16 == 0) ck.sDd[i] = dd[r] * f;
+    }
+    __syncthreads();
+    {
+        const int rs_ = NC - 1 - c;                        // reversed slot
+        const size_t rslot = size_t(bh) * (NC + 1) + rs_;
+        constexpr int NT = ND * NE;                       // state tiles, dealt to the waves
+#pragma unroll
+        for (int u0 = 0; u0 < NT; u0 += 4) {
+            const int u = u0 + w;
+            if (u < NT) {
+                const int a = u / NE, b = u % NE;
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < C / 32; ++ks)
+                    acc = mma(frag_col(ck.sQ, LQ, 32 * ks + 8 * g4, 16 * a, l16),
+                              frag_col(ck.sDn, LV, 32 * ks + 8 * g4, 16 * b, l16), acc);
+                *reinterpret_cast<f32x4_t*>(args.rst + rslot * (D * DV) + (u * kWave + lane) * 4) = acc;
+            }
+        }
+        for (int d = ck.tid; d < D; d += kThreads) {
+            float s = 0.0f;
+            for (int i = 0; i < C; ++i) s += X::to_f32(ck.sQ[i * LQ + d]) * ck.sDd[i];
+            args.rzt[rslot * D + d] = s;
+        }
+        if (GATED && ck.tid == 0) args.rlg[rslot] = ck.sLam[C - 1];
+    }
+}
+
+// ------------------------------------------------------------ dk / dv pass ----
+
+template <typename E, int D, int DV, bool GATED>
+__global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwdArgs args) {
+    using B = BwdChunk<E, D, DV, GATED>;
+    using X = Elem<E>;
+    constexpr int C = B::C, LQ = B::LQ, LV = B::LV, LA = B::LA;
+    constexpr int ND = D / 16, NE = DV / 16, NI = C / 16;
+    extern __shared__ __align__(16) unsigned char smem[];
+    B ck;
+    ck.init(smem, args.N, args.NC);
+    const int w = ck.w, l16 = ck.l16, g4 = ck.g4, bh = ck.bh, c = ck.c, ts = ck.ts;
+    const int N = args.N, NC = args.NC;
+    const E* qb = reinterpret_cast<const E*>(args.q) + size_t(bh) * N * D;
+    const E* kb = reinterpret_cast<const E*>(args.k) + size_t(bh) * N * D;
+    const E* vb = reinterpret_cast<const E*>(args.v) + size_t(bh) * N * DV;
+    const E* dob = reinterpret_cast<const E*>(args.dout) + size_t(bh) * N * DV;
+
+    ck.template stage_rows<D, true>(ck.sQ, LQ, qb);
+    ck.template stage_rows<D, true>(ck.sK, LQ, kb);
+    ck.template stage_rows<DV, false>(ck.sV, LV, vb);
+    ck.template stage_rows<DV, false>(ck.sDn, LV, dob);
+    for (int i = ck.tid; i < C; i += kThreads) {
+        ck.sDd[i] = i < ck.nrows ? args.dden[size_t(bh) * N + ts + i] : 0.0f;
+        ck.sInv[i] = i < ck.nrows ? args.inv[size_t(bh) * N + ts + i] : 0.0f;
+    }
+    // R, r: the adjoint of the state after this chunk (zero after the last chunk)
+    const size_t rslot = size_t(bh) * (NC + 1) + (NC - 2 - c);
+    if (c < NC - 1)
+        ck.stage_state(args.rst + rslot * (D * DV), args.rzt + rslot * D, nullptr, nullptr);
+    else
+        ck.stage_state(nullptr, nullptr, nullptr, nullptr);
+    ck.stage_lambda(GATED ? args.g + size_t(bh) * N : nullptr);
+    // W_c = 2^Lambda_last (<R, S_prev> + <r, z_prev>): keys in front of the chunk against
+    // queries after it (both states fp32; R and the forward slots share one layout)
+    if constexpr (GATED) {
+        float wp = 0.0f;
+        if (c < NC - 1) {
+            const float* R = args.rst + rslot * (D * DV);
+            const float* rz = args.rzt + rslot * D;
+            if (c > 0) {
+                const size_t fslot = size_t(bh) * NC + (c - 1);
+                const float* F = args.fst + fslot * (D * DV);
+                const float* fz = args.fzt + fslot * D;
+                for (int e = ck.tid; e < D * DV; e += kThreads) wp += R[e] * F[e];
+                for (int d = ck.tid; d < D; d += kThreads) wp += rz[d] * fz[d];
+            } else {
+                if (args.s0) {
+                    const float* S0 = args.s0 + size_t(bh) * D * DV;
+                    for (int e = ck.tid; e < D * DV; e += kThreads) {
+                        const int u = e / 256, ln = (e / 4) % kWave, r = e % 4;
+                        const int a = u / (DV / 16), b = u % (DV / 16);
+                        wp += R[e] * S0[size_t(16 * a + 4 * (ln >> 4) + r) * DV + 16 * b + (ln & 15)];
+                    }
+                }
+                if (args.z0)
+                    for (int d = ck.tid; d < D; d += kThreads) wp += rz[d] * args.z0[size_t(bh) * D + d];
+            }
+        }
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) wp += __shfl_xor(wp, off, kWave);
+        if (ck.lane == 0) ck.sRow[w] = wp;
+    }
+    __syncthreads();
+    if (GATED && ck.tid == 0)
+        args.wc[size_t(bh) * NC + c] = (ck.sRow[0] + ck.sRow[1] + ck.sRow[2] + ck.sRow[3]) * fast_exp2(ck.lam(C - 1));
+
+    const int j0 = 16 * w;            // this wave's key rows
+    float lam_r[4], tail[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        lam_r[r] = ck.lam(j0 + 4 * g4 + r);
+        tail[r] = GATED ? fast_exp2(fminf(ck.lam(C - 1) - lam_r[r], 0.0f)) : 1.0f;   // 2^(Lambda_last - Lambda_j)
+    }
+
+    // A^T diag(1/d) = Fk Fq^T diag(1/d) and B^T = V dOut^T diag(1/d) + 1 dden^T, both
+    // decayed and masked (i >= j)
+    f32x4_t bt[NI];
+    {
+        f32x4_t at[NI];
+#pragma unroll
+        for (int it = 0; it < NI; ++it) {
+            at[it] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            bt[it] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+            const F8<E> a = frag_row(ck.sK, LQ, j0 + l16, 32 * ks + 8 * g4);
+#pragma unroll
+            for (int it = 0; it < NI; ++it)
+                if (it >= w) at[it] = mma(a, frag_row(ck.sQ, LQ, 16 * it + l16, 32 * ks + 8 * g4), at[it]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < DV / 32; ++ks) {
+            const F8<E> a = frag_row(ck.sV, LV, j0 + l16, 32 * ks + 8 * g4);
+#pragma unroll
+            for (int it = 0; it < NI; ++it)
+                if (it >= w) bt[it] = mma(a, frag_row(ck.sDn, LV, 16 * it + l16, 32 * ks + 8 * g4), bt[it]);
+        }
+#pragma unroll
+        for (int it = 0; it < NI; ++it) {
+            const int i = 16 * it + l16;
+            const float li = ck.lam(i);
+            const float ddi = ck.sDd[i], invi = ck.sInv[i];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = j0 + 4 * g4 + r;
+                const bool keep = it >= w && i >= j;
+                const float f = GATED ? fast_exp2(fminf(li - lam_r[r], 0.0f)) : 1.0f;
+                ck.sA[j * LA + i] = X::from_f32(keep ? at[it][r] * (f * invi) : 0.0f);
+                bt[it][r] = keep ? (bt[it][r] * invi + ddi) * f : 0.0f;
+            }
+        }
+    }
+    __syncthreads();
+
+    // dV = 2^(Lambda_last - Lambda_j) Fk R + (A^T diag(1/d)) dOut
+    {
+        f32x4_t dv[NE];
+#pragma unroll
+        for (int et = 0; et < NE; ++et) dv[et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+            const F8<E> a = frag_row(ck.sK, LQ, j0 + l16, 32 * ks + 8 * g4);
+#pragma unroll
+            for (int et = 0; et < NE; ++et) dv[et] = mma(a, frag_col(ck.sS, LV, 32 * ks + 8 * g4, 16 * et, l16), dv[et]);
+        }
+        if constexpr (GATED) {
+#pragma unroll
+            for (int et = 0; et < NE; ++et)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dv[et][r] *= tail[r];
+        }
+        for (int ks = w >> 1; ks < C / 32; ++ks) {
+            const F8<E> a = frag_row(ck.sA, LA, j0 + l16, 32 * ks + 8 * g4);
+#pragma unroll
+            for (int et = 0; et < NE; ++et) dv[et] = mma(a, frag_col(ck.sDn, LV, 32 * ks + 8 * g4, 16 * et, l16), dv[et]);
+        }
+        E* dvb = reinterpret_cast<E*>(args.dv) + size_t(bh) * N * DV;
+#pragma unroll
+        for (int et = 0; et < NE; ++et)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = j0 + 4 * g4 + r;
+                if (ts + j < N) dvb[size_t(ts + j) * DV + 16 * et + l16] = X::from_f32(dv[et][r]);
+            }
+    }
+    __syncthreads();
+    // B^T over this wave's rows into sA (every read of A^T finished before the barrier)
+#pragma unroll
+    for (int it = 0; it < NI; ++it)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ck.sA[(j0 + 4 * g4 + r) * LA + 16 * it + l16] = X::from_f32(bt[it][r]);
+    __syncthreads();
+
+    // dFk = 2^(Lambda_last - Lambda_j) (V R^T + 1 r^T) + B^T Fq
+    f32x4_t dfk[ND];
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) dfk[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < DV / 32; ++ks) {
+        const F8<E> a = frag_row(ck.sV, LV, j0 + l16, 32 * ks + 8 * g4);
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) dfk[dt] = mma(a, frag_row(ck.sS, LV, 16 * dt + l16, 32 * ks + 8 * g4), dfk[dt]);
+    }
+    {
+        float zk[4] = {0.f, 0.f, 0.f, 0.f};            // Fk_j . (carried-state part of dFk_j)
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) {
+            const float rd = ck.sZ[16 * dt + l16];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                dfk[dt][r] = (dfk[dt][r] + rd) * tail[r];
+                if constexpr (GATED) zk[r] += X::to_f32(ck.sK[(j0 + 4 * g4 + r) * LQ + 16 * dt + l16]) * dfk[dt][r];
+            }
+        }
+        if constexpr (GATED) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float s = sum16(zk[r]);
+                const int j = j0 + 4 * g4 + r;
+                if (l16 == 0 && ts + j < N) args.zk[size_t(bh) * N + ts + j] = s;
+            }
+        }
+    }
+    for (int ks = w >> 1; ks < C / 32; ++ks) {
+        const F8<E> a = frag_row(ck.sA, LA, j0 + l16, 32 * ks + 8 * g4);
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) dfk[dt] = mma(a, frag_col(ck.sQ, LQ, 32 * ks + 8 * g4, 16 * dt, l16), dfk[dt]);
+    }
+    {
+        E* dkb = reinterpret_cast<E*>(args.dk) + size_t(bh) * N * D;
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = j0 + 4 * g4 + r;
+                if (ts + j < N) {
+                    const float x = X::to_f32(kb[size_t(ts + j) * D + 16 * dt + l16]);
+                    dkb[size_t(ts + j) * D + 16 * dt + l16] = X::from_f32(dfk[dt][r] * dphi(x));
+                }
+            }
+        }
+    }
+}
+
+// --------------------------------------------------------------- gate pass ----
+
+// dg_l = (X_l + Y_l + Z_l + W_c) / g_l for token l of chunk c, one wave per chunk and
+// one lane per token: Y_l = sum_{i >= l} yq_i and Z_l = sum_{j < l} zk_j within the chunk.
+static __global__ __launch_bounds__(kThreads) void bwd_dg_kernel(const float* g, const float* xs, const float* yq,
+                                                                const float* zk, const float* wc, float* dg, int N,
+                                                                int NC, int nwork) {
+    constexpr int C = kBwdChunk;
+    static_assert(C == kWave, "one lane per token of a chunk");
+    const int item = blockIdx.x * (kThreads / kWave) + int(threadIdx.x) / kWave;   // (head, chunk)
+    if (item >= nwork) return;
+    const int lane = threadIdx.x % kWave;
+    const int bh = item / NC, c = item % NC;
+    const int t = c * C + lane;
+    const bool in = t < N;
+    const size_t at = size_t(bh) * N + (in ? t : 0);
+    const float x = in ? xs[at] : 0.0f, y = in ? yq[at] : 0.0f, z = in ? zk[at] : 0.0f;
+    float ysuf = y, zpre = z;                     // inclusive suffix of y, inclusive prefix of z
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const float a = __shfl_down(ysuf, off, kWave);
+        const float b = __shfl_up(zpre, off, kWave);
+        if (lane + off < kWave) ysuf += a;
+        if (lane >= off) zpre += b;
+    }
+    if (in) dg[at] = (x + ysuf + (zpre - z) + wc[size_t(bh) * NC + c]) / g[at];
+}
+
+}  // namespace linattn

@@ -934,17 +934,18 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(float* st, float* zt, co
     }
 }
 
-// S_N, z_N from slot nseg-1 (accumulator layout) into the caller's s_out / z_out.
-// A launch of its own, so s_out may alias s0 (every read of s0 is done by then).
+// One state slot (accumulator layout; nslots per head) into the caller's [D][Dv] and [D]
+// layouts: S_N, z_N from slot nseg-1 of the forward.  A launch of its own, so s_out may
+// alias s0 (every read of s0 is done by then).
 template <int D, int DV>
-__global__ __launch_bounds__(kThreads) void final_kernel(const float* st, const float* zt, int nseg, float* s_out,
-                                                        float* z_out) {
+__global__ __launch_bounds__(kThreads) void final_kernel(const float* st, const float* zt, int nslots, int which,
+                                                        float* s_out, float* z_out) {
     constexpr int NS = D * DV;
     constexpr int NBLK = (NS + D + kThreads - 1) / kThreads;
     const int e = (blockIdx.x % NBLK) * kThreads + threadIdx.x;
     const int bh = blockIdx.x / NBLK;
     if (e >= NS + D) return;
-    const size_t slot = size_t(bh) * nseg + (nseg - 1);
+    const size_t slot = size_t(bh) * nslots + which;
     if (e < NS) {
         if (!s_out) return;
         const int u = e / 256, lane = (e / 4) % 64, r = e % 4;

@@ -50,7 +50,7 @@ hipError_t run_fwd_walks(const FwdLaunch& p) {
     hipLaunchKernelGGL(k_out, dim3(unsigned(p.BH) * unsigned(p.nseg)), dim3(kThreads), ShO::kBytes, p.stream, a);
     if (a.want_final)
         hipLaunchKernelGGL((final_kernel<D, DV>), dim3(unsigned(p.BH) * NBLK), dim3(kThreads), 0, p.stream, a.st,
-                           a.zt, p.nseg, p.s_out, p.z_out);
+                           a.zt, p.nseg, p.nseg - 1, p.s_out, p.z_out);
     mark(3);
     return hipGetLastError();
 }

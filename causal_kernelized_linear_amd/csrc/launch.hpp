@@ -72,8 +72,66 @@ inline size_t fwd_workspace_layout(size_t slots, int D, int Dv, size_t* off_zt, 
 // and small (at most seven 64 x 64 states); otherwise a scan launch does it first.
 inline bool prefix_direct(int nseg, int D, int Dv) { return size_t(nseg - 1) * D * Dv <= size_t(7) * 64 * 64; }
 
+// Dynamic LDS bytes of a gradient kernel: phi(Q), phi(K) [C][D], V, dOut [C][Dv], one
+// state [D][Dv] and one [C][C] score tile, each row padded by 16 bytes, plus the chunk's
+// decays, dden, 1/d, the column and row sums of its pair terms and one fp32 [D] vector.  BwdShape<...>::kBytes is checked against it.
+constexpr int kBwdChunkHost = 64;
+constexpr size_t bwd_lds_bytes(int esize, int D, int Dv) {
+    const size_t es = size_t(esize), pad = 16 / es, C = kBwdChunkHost;
+    return (2 * C * (D + pad) + 2 * C * (Dv + pad) + size_t(D) * (Dv + pad) + C * (C + pad)) * es + (8 * C + D) * 4;
+}
+
+// Workspace of the backward: the state in front of every chunk (NC slots per head), the
+// chunks' adjoint totals and their reverse scan (NC + 1 slots), then five fp32 [BH][N]
+// rows (1/d, dden and the three per-token pair sums of d log g) and one [BH][NC] row.
+struct BwdLayout {
+    size_t fwd, fzt, flg, rev, rzt, rlg, inv, dden, xs, yq, zk, wc, bytes;
+};
+
+inline BwdLayout bwd_workspace_layout(size_t BH, int N, int D, int Dv) {
+    BwdLayout L;
+    const size_t nc = (size_t(N) + kBwdChunkHost - 1) / kBwdChunkHost;
+    size_t oz = 0, ol = 0;
+    const size_t fb = fwd_workspace_layout(BH * nc, D, Dv, &oz, &ol);
+    L.fwd = 0; L.fzt = oz; L.flg = ol;
+    const size_t rb = fwd_workspace_layout(BH * (nc + 1), D, Dv, &oz, &ol);
+    L.rev = fb; L.rzt = fb + oz; L.rlg = fb + ol;
+    const size_t row = round_up256(BH * size_t(N) * 4);
+    L.inv = fb + rb;
+    L.dden = L.inv + row;
+    L.xs = L.dden + row;
+    L.yq = L.xs + row;
+    L.zk = L.yq + row;
+    L.wc = L.zk + row;
+    L.bytes = L.wc + round_up256(BH * nc * 4);
+    return L;
+}
+
+struct BwdLaunch {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;          // NULL: ungated
+    const void* dout;
+    const float* s0;
+    const float* z0;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dg;               // NULL: not written (or ungated)
+    float* ds0;              // NULL: not written
+    float* dz0;              // NULL: not written
+    void* ws;
+    int BH, N, D, Dv;
+    float eps;
+    int normalize;
+    hipStream_t stream;
+};
+
 hipError_t launch_fwd_bf16(const FwdLaunch& p);
 hipError_t launch_fwd_f32(const FwdLaunch& p);
+hipError_t launch_bwd_bf16(const BwdLaunch& p);
+hipError_t launch_bwd_f32(const BwdLaunch& p);
 hipError_t launch_decode(int dtype, const void* q, const void* k, const void* v, float* S, float* z, void* o,
                          int BH, int D, int Dv, float eps, const float* g, int normalize,
                          hipStream_t stream);

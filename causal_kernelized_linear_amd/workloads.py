@@ -67,7 +67,7 @@ def _randn(gen, shape, scale=1.0):
     return x
 
 
-def make_inputs(w: Workload, B=None, H=None, N=None):
+def make_inputs(w: Workload, B=None, H=None, N=None, with_grad=False):
     """Draw the inputs of workload ``w`` (optionally with B, H or N overridden).
 
     Returns a dict of CPU tensors in their stored dtypes:
@@ -77,6 +77,8 @@ def make_inputs(w: Workload, B=None, H=None, N=None):
               each 1000*|N(0,1)| (a state after about 1000 tokens)
       decode_gated: the same plus this token's gate g [B,H] float32, drawn last as
               0.9 + 0.1*sigmoid(N(0,1)) like the gated forward's gates
+    With ``with_grad`` (forward kinds) an upstream gradient dout [B,H,N,Dv] ~ N(0,1) in
+    the input dtype is drawn after everything else, for the backward.
     """
     B = w.B if B is None else B
     H = w.H if H is None else H
@@ -99,16 +101,19 @@ def make_inputs(w: Workload, B=None, H=None, N=None):
     out = {"q": q, "k": k, "v": v}
     if w.kind == "gated":
         out["g"] = 0.9 + 0.1 * torch.sigmoid(_randn(gen, (B, H, N)))
+    if with_grad:
+        out["dout"] = _randn(gen, (B, H, N, w.Dv)).to(dt)
     return out
 
 
 def random_inputs(seed, B, H, N, D, Dv, dtype="bf16", scale=1.0, gated=False,
-                  g_low=0.9, with_state=False, state_scale=1.0):
+                  g_low=0.9, with_state=False, state_scale=1.0, with_grad=False):
     """Small ad-hoc seeded inputs for edge-case tests (ragged N, odd shapes).
 
     g (if requested) is drawn uniformly in [g_low, 1].  With ``with_state`` an
     initial state s0 = state_scale*|N(0,1)|-ish is drawn too (s0 may have either
-    sign; z0 is kept non-negative as a sum of positive features would be).
+    sign; z0 is kept non-negative as a sum of positive features would be); with
+    ``with_grad`` an upstream gradient dout ~ N(0,1) is drawn last.
     """
     gen = torch.Generator(device="cpu").manual_seed(seed)
     dt = torch.float32 if dtype == "f32" else torch.bfloat16
@@ -122,6 +127,8 @@ def random_inputs(seed, B, H, N, D, Dv, dtype="bf16", scale=1.0, gated=False,
     if with_state:
         out["s0"] = _randn(gen, (B, H, D, Dv)) * state_scale
         out["z0"] = _randn(gen, (B, H, D)).abs_() * state_scale
+    if with_grad:
+        out["dout"] = _randn(gen, (B, H, N, Dv)).to(dt)
     return out
 
 

@@ -133,6 +133,41 @@ linattn_status_t linattn_fwd_ex(
     linattn_output_t out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Bytes of device scratch linattn_bwd needs for these sizes and dtype (the state in
+ * front of every 64-token chunk and its adjoint, float, plus per-token intermediates).
+ * 0 when B*H*N == 0 or a size is not positive.  Contents are undefined after a call; it
+ * must not be shared by calls that may run concurrently.
+ */
+size_t linattn_bwd_workspace_size(int B, int H, int N, int D, int Dv, linattn_dtype_t dtype);
+
+/*
+ * Gradients of the forward (linattn_fwd_ex with the same g, s0, z0, eps and `out`) for
+ * the loss sum(dout * o): the reverse-mode derivative of the recurrence
+ * S_t = g_t S_{t-1} + phi(k_t) v_t^T, z alike, o_t as chosen by `out` (learn.pranaymahendrakar.com
+ * page, "Derivation" and "Try it yourself"; the chunked form is the training path, as
+ * the aiwiki.thehackersbrain.dev page's chunked listing and the learn page's
+ * "Implementation reality" say).  The clamp max(den, eps) passes no gradient where
+ * den < eps.  The chunking is the library's own (64 tokens); results do not depend on
+ * the forward's chunk.
+ *
+ *  q, k [B,H,N,D], v [B,H,N,Dv], dout [B,H,N,Dv]   dtype, read-only
+ *  g    [B,H,N] float or NULL                      as for the forward
+ *  s0   [B,H,D,Dv], z0 [B,H,D] float or NULL       the forward's initial state
+ *  dq, dk [B,H,N,D], dv [B,H,N,Dv]                 dtype, written; must not alias any input
+ *  dg   [B,H,N] float or NULL                      written when g is given (NULL: skipped)
+ *  ds0  [B,H,D,Dv], dz0 [B,H,D] float or NULL      gradients of the initial state (NULL: skipped)
+ *  workspace                                       at least linattn_bwd_workspace_size bytes
+ *
+ * Supported shapes: D, Dv in {64, 128}; bf16 at every pair, f32 unless D = Dv = 128
+ * (LINATTN_ERR_UNSUPPORTED).  Every other convention is the forward's.
+ */
+linattn_status_t linattn_bwd(
+    const void* q, const void* k, const void* v, const float* g, const void* dout,
+    const float* s0, const float* z0, void* dq, void* dk, void* dv, float* dg, float* ds0, float* dz0,
+    int B, int H, int N, int D, int Dv, linattn_dtype_t dtype, float eps, linattn_output_t out,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * One recurrent decode step for B*H independent heads (aiwiki.thehackersbrain.dev page,
  * "It is a linear RNN": O(D*Dv) work per token, no cache that grows):
  *

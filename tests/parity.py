@@ -26,6 +26,23 @@ def rowwise_rel_err(got, ref, axis=-1):
     return float((num / den).max())
 
 
+def grad_rel_err(got, ref, floor=1e-2):
+    """Row-wise relative error of a gradient [B, H, N, X]: max|diff| over a row divided by
+    the row's max|ref|, floored at `floor` times the largest such row scale of the same
+    (b, h).  Some gradient rows are exactly zero by structure (dq of the first token
+    when nothing precedes it: o_0 = v_0 whatever q_0 is), so their own scale cannot be
+    the denominator."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    if got.size == 0:
+        return 0.0
+    num = np.abs(got - ref).max(axis=-1)
+    den = np.abs(ref).max(axis=-1)
+    den = np.maximum(den, np.maximum(floor * den.max(axis=-1, keepdims=True), 1e-30))
+    return float((num / den).max())
+
+
 def matrix_rel_err(got, ref):
     """Per leading index (b, h): max|diff| / max|ref| over the trailing matrix dims."""
     got = np.asarray(got, dtype=np.float64)

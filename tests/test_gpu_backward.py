@@ -1,0 +1,131 @@
+"""GPU parity of the backward (linattn_bwd) against the fp64 backward oracle.
+
+The oracle differentiates the token recurrence in reverse (oracle/backward.py,
+pinned by finite differences and autograd of the pairwise form); the GPU path
+works chunk by chunk.  Gradients use the forward's row-wise metric per row of
+dq, dk (over D) and dv (over Dv), with each row's scale floored at 1% of its
+head's largest row (rows that are exactly zero by structure exist), per head for
+dg (over N) and for the state gradients (over the matrix).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from causal_kernelized_linear_amd import binding, workloads
+from parity import TOL, grad_rel_err, matrix_rel_err, to64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _dev(t):
+    return None if t is None else t.to(DEV)
+
+
+def gpu_bwd(inp, normalize=True, s0=None, z0=None, state_grads=False):
+    r = binding.bwd(*(_dev(inp[n]) for n in ("q", "k", "v", "dout")), g=_dev(inp.get("g")), s0=_dev(s0), z0=_dev(z0),
+                    normalize=normalize, state_grads=state_grads)
+    torch.cuda.synchronize()
+    return r
+
+
+def oracle_bwd(inp, normalize=True, s0=None, z0=None, heads=None):
+    def pick(t):
+        if t is None:
+            return None
+        a = to64(t)
+        return a if heads is None else np.stack([a[b, h] for b, h in heads])[None]
+    return oracle.causal_linear_attention_bwd(pick(inp["q"]), pick(inp["k"]), pick(inp["v"]), pick(inp["dout"]),
+                                              g=pick(inp.get("g")), s0=pick(s0), z0=pick(z0), normalize=normalize)
+
+
+def sel(t, heads):
+    a = to64(t)
+    return np.stack([a[b, h] for b, h in heads])[None]
+
+
+def check(got, ref, tol, heads=None, gated=False, state=False):
+    pickg = (lambda t: to64(t)) if heads is None else (lambda t: sel(t, heads))
+    errs = {n: grad_rel_err(pickg(got[n]), ref[n]) for n in ("dq", "dk", "dv")}
+    if gated:
+        errs["dg"] = matrix_rel_err(pickg(got["dg"]), ref["dg"])
+    if state:
+        errs["ds0"] = matrix_rel_err(pickg(got["ds0"]), ref["ds0"])
+        errs["dz0"] = matrix_rel_err(pickg(got["dz0"]), ref["dz0"])
+    _say("  errors " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    for n, e in errs.items():
+        assert e <= tol, (n, e)
+
+
+CASES = [
+    # (B, H, N, D, Dv, dtype)
+    (1, 2, 256, 64, 64, "f32"),
+    (1, 1, 150, 64, 128, "f32"),
+    (2, 1, 97, 128, 64, "f32"),
+    (1, 2, 512, 64, 64, "bf16"),
+    (2, 1, 333, 128, 128, "bf16"),
+    (1, 2, 200, 64, 128, "bf16"),
+    (1, 1, 130, 128, 64, "bf16"),
+    (1, 1, 1, 64, 64, "bf16"),
+    (1, 1, 64, 64, 64, "f32"),
+]
+
+
+@pytest.mark.parametrize("normalize", [True, False], ids=["normalized", "numerator"])
+@pytest.mark.parametrize("gated", [False, True], ids=["ungated", "gated"])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}H{}N{}D{}Dv{}{}".format(*c))
+def test_backward_small_against_oracle(case, gated, normalize):
+    B, H, N, D, Dv, dt = case
+    _say(f"backward {case} gated={gated} normalize={normalize}")
+    inp = workloads.random_inputs(61 + N + D, B, H, N, D, Dv, dtype=dt, gated=gated, g_low=0.8, with_state=True,
+                                  state_scale=5.0, with_grad=True)
+    got = gpu_bwd(inp, normalize, s0=inp["s0"], z0=inp["z0"], state_grads=True)
+    ref = oracle_bwd(inp, normalize, s0=inp["s0"], z0=inp["z0"])
+    check(got, ref, TOL[dt], gated=gated, state=True)
+
+
+def test_backward_without_initial_state():
+    inp = workloads.random_inputs(5, 1, 2, 300, 64, 64, dtype="bf16", gated=True, with_grad=True)
+    _say("backward without initial state")
+    got = gpu_bwd(inp, state_grads=True)
+    ref = oracle_bwd(inp)
+    check(got, ref, TOL["bf16"], gated=True, state=True)
+
+
+def test_backward_unsupported_raises():
+    inp = workloads.random_inputs(6, 1, 1, 64, 128, 128, dtype="f32", with_grad=True)
+    with pytest.raises(RuntimeError, match="unsupported"):
+        gpu_bwd(inp)
+
+
+def test_backward_deterministic():
+    inp = workloads.random_inputs(7, 2, 2, 500, 64, 64, dtype="bf16", gated=True, with_grad=True)
+    a = gpu_bwd(inp)
+    b = gpu_bwd(inp)
+    for n in ("dq", "dk", "dv", "dg"):
+        assert torch.equal(a[n], b[n]), n
+
+
+def _heads(B, H, n, seed):
+    rng = np.random.default_rng(seed)
+    idx = rng.choice(B * H, size=min(n, B * H), replace=False)
+    return [(int(i) // H, int(i) % H) for i in sorted(idx)]
+
+
+@pytest.mark.parametrize("name", ["train_bf16", "gated_bf16"])
+def test_backward_workload_sampled_heads(name):
+    w = workloads.WORKLOADS[name]
+    inp = workloads.make_inputs(w, with_grad=True)
+    heads = _heads(w.B, w.H, 3, 9)
+    _say(f"{name} backward full size, oracle on heads {heads}")
+    got = gpu_bwd(inp)
+    ref = oracle_bwd(inp, heads=heads)
+    check(got, ref, TOL["bf16"], heads=heads, gated=w.kind == "gated")
+    for n in ("dq", "dk", "dv"):
+        assert torch.isfinite(got[n]).all().item()
