@@ -8,9 +8,9 @@ inputs already resident in HBM.  Input sets are rotated so no step starts with
 its inputs warm in the 256 MB Infinity Cache.  The scalar-gated forward
 (B=4, H=16, N=8192, D=Dv=64, chunk 128), the long-context forward
 (B=1, H=32, N=65536, D=Dv=128, chunk sweep), the decode step (B=256, H=32,
-D=Dv=128, fp32 state), its gated form, and the normaliser-free output mode of the
-gated forward and of the gated decode are timed in the same run and reported in
-extra fields.
+D=Dv=128, fp32 state), its gated form, the normaliser-free output mode of the
+gated forward and of the gated decode, and the backward of the training-shaped and
+gated forwards are timed in the same run and reported in extra fields.
 
 Prints ONE JSON line.  ms_per_step and value come from a timed pass bracketed by
 two hipEvents only.  Per-kernel durations come from a second timed pass of the same
@@ -222,6 +222,60 @@ def time_decode(w, steps, warmup, ev, normalize=True):
     return {"ms_per_step": sum(ks) / steps, "ms_median": _median(ks)}
 
 
+BWD_CHUNK = 64                  # the backward's own chunk
+
+
+def bwd_bytes_per_unit(w):
+    """q, k, v, dout read once and dq, dk, dv written once (plus g read and dg written)."""
+    es = 4 if w.dtype == "f32" else 2
+    b = 2 * (2 * w.D + w.Dv) * es + w.Dv * es
+    if w.kind == "gated":
+        b += 8
+    return b
+
+
+def bwd_flops_per_unit(w):
+    """Products per token-head of the chunked backward, recompute included: six state-sized
+    products (the chunk totals, Fq S_prev, dOut S_prev^T, the adjoint fold, Fk R, V R^T)
+    of 2 D Dv each, and the causal halves of eight chunk products (A and B in both
+    kernels, A V, B Fk, A^T dOut, B^T Fq)."""
+    return 12 * w.D * w.Dv + 4 * (BWD_CHUNK + 1) * (w.D + w.Dv)
+
+
+def time_backward(w, steps, warmup, ev):
+    """Per-step time of linattn_bwd on workload w (inputs and outputs preallocated)."""
+    import torch
+    from causal_kernelized_linear_amd import binding, workloads
+
+    dev = torch.device("cuda:0")
+    base = workloads.make_inputs(w, with_grad=True)
+    sets = [{n: t.to(dev) for n, t in base.items()}]
+    sets.append({n: t.clone() for n, t in sets[0].items()})
+    grads = [{"dq": torch.empty_like(s["q"]), "dk": torch.empty_like(s["k"]), "dv": torch.empty_like(s["v"]),
+              "dg": torch.empty_like(s["g"]) if "g" in s else None} for s in sets]
+    dt = binding.BF16 if w.dtype == "bf16" else binding.F32
+    ws = torch.empty(binding.linattn_bwd_workspace_size(w.B, w.H, w.N, w.D, w.Dv, dt), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def call(i):
+        s = sets[i % 2]
+        binding.bwd(s["q"], s["k"], s["v"], s["dout"], g=s.get("g"), workspace=ws, grads=grads[i % 2])
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    t0, t1 = ev.create(2)
+    ev.record(t0, stream)
+    for i in range(steps):
+        call(i)
+    ev.record(t1, stream)
+    torch.cuda.synchronize()
+    ms = ev.ms(t0, t1) / steps
+    del sets, grads, ws
+    torch.cuda.empty_cache()
+    return {"ms_per_step": ms}
+
+
 def decode_bytes(w, with_z=True):
     """S (and z) read and written once, q, k, v read, o written, plus the gate when gated."""
     es = 4 if w.dtype == "f32" else 2
@@ -411,6 +465,20 @@ def main():
                 "GBps": nbytes / sdg / 1e9, "hbm_frac": nbytes / sdg / 1e9 / HBM_PEAK_GBS,
                 "tokens_per_s": wdg.B / sdg, "ms_per_step": rdg["ms_per_step"], "ms_median": rdg["ms_median"],
                 "bytes_per_step": nbytes,
+            }
+        for key, wname in (("backward", "train_bf16"), ("backward_gated", "gated_bf16")):
+            wb = workloads.WORKLOADS[wname]
+            rb = time_backward(wb, extra_steps, extra_warm, ev)
+            sb = rb["ms_per_step"] * 1e-3
+            ub = fwd_units(wb)
+            line[key] = {
+                "workload": f"{wname} backward: dq, dk, dv" + (", dg" if wb.kind == "gated" else "") +
+                            f" for sum(dout * o), chunk {BWD_CHUNK}",
+                "tokens_per_s": wb.B * wb.N / sb, "ms_per_step": rb["ms_per_step"],
+                "algorithmic_GBps": bwd_bytes_per_unit(wb) * ub / sb / 1e9,
+                "hbm_frac": bwd_bytes_per_unit(wb) * ub / sb / 1e9 / HBM_PEAK_GBS,
+                "useful_TFLOPs": bwd_flops_per_unit(wb) * ub / sb / 1e12,
+                "mfma_bf16_frac": bwd_flops_per_unit(wb) * ub / sb / 1e12 / MFMA_BF16_PEAK_TFLOPS,
             }
         wl = workloads.WORKLOADS["longctx_bf16"]
         sweep = {}

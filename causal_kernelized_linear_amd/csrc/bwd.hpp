@@ -202,57 +202,95 @@ struct BwdChunk {
         nrows = min(C, N - ts);
     }
 
-    // Rows [ts, ts + C) of a [N][W] tensor into a row-major tile, through f (phi or the
-    // identity) in fp32; rows past the chunk's end are zero.
-    template <int W, bool PHI>
-    __device__ __forceinline__ void stage_rows(E* tile, int ld, const E* src) const {
+    // Staging is split into a load phase and a store phase so that every global load of
+    // the chunk is in flight at once: a load followed by its use in a loop would make the
+    // workgroup wait for each one in turn.
+    //
+    // Rows [ts, ts + C) of a [N][W] tensor: 16-byte units, rows clamped to the last valid
+    // one (the loads are unconditional).
+    template <int W>
+    static constexpr int kRowUnits = C * W * int(sizeof(E)) / 16 / kThreads;
+
+    template <int W>
+    __device__ __forceinline__ void load_rows(f32x4_t (&r)[kRowUnits<W>], const E* src) const {
         constexpr int G = W * int(sizeof(E)) / 16;
-        for (int u = tid; u < C * G; u += kThreads) {
-            const int row = u / G, col = (u % G) * EPG;
-            F8<E> out;
+#pragma unroll
+        for (int u = 0; u < kRowUnits<W>; ++u) {
+            const int idx = tid + u * kThreads, row = idx / G, col = (idx % G) * EPG;
+            r[u] = *reinterpret_cast<const f32x4_t*>(src + size_t(ts + min(row, nrows - 1)) * W + col);
+        }
+    }
+
+    // ... into a row-major tile through phi (or as they are) in fp32; rows past the
+    // chunk's end become zero.
+    template <int W, bool PHI>
+    __device__ __forceinline__ void store_rows(E* tile, int ld, const f32x4_t (&r)[kRowUnits<W>]) const {
+        constexpr int G = W * int(sizeof(E)) / 16;
+#pragma unroll
+        for (int u = 0; u < kRowUnits<W>; ++u) {
+            const int idx = tid + u * kThreads, row = idx / G, col = (idx % G) * EPG;
+            f32x4_t out = {0.f, 0.f, 0.f, 0.f};
             if (row < nrows) {
-                const E* p = src + size_t(ts + row) * W + col;
                 if constexpr (sizeof(E) == 2) {
-                    const F8<E> in = *reinterpret_cast<const F8<E>*>(p);
+                    const F8<E> in = __builtin_bit_cast(F8<E>, r[u]);
+                    F8<E> o;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) out.x[e] = PHI ? X::from_f32(phi(X::to_f32(in.x[e]))) : in.x[e];
+                    for (int e = 0; e < 8; ++e) o.x[e] = PHI ? X::from_f32(phi(X::to_f32(in.x[e]))) : in.x[e];
+                    out = __builtin_bit_cast(f32x4_t, o);
                 } else {
-                    const F4<E> in = *reinterpret_cast<const F4<E>*>(p);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) out.x[e] = PHI ? phi(in.x[e]) : in.x[e];
+                    for (int e = 0; e < 4; ++e) out[e] = PHI ? phi(r[u][e]) : r[u][e];
                 }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) out.x[e] = E(0);
             }
-            if constexpr (sizeof(E) == 2)
-                *reinterpret_cast<F8<E>*>(tile + row * ld + col) = out;
-            else
-                *reinterpret_cast<F4<E>*>(tile + row * ld + col) = *reinterpret_cast<const F4<E>*>(&out);
+            *reinterpret_cast<f32x4_t*>(tile + row * ld + col) = out;
+        }
+    }
+
+    // The chunk's valid rows of a row-major tile out to a [N][W] tensor, 16 bytes at a time.
+    template <int W>
+    __device__ __forceinline__ void store_out(E* dst, const E* tile, int ld) const {
+        constexpr int G = W * int(sizeof(E)) / 16;
+#pragma unroll
+        for (int u = 0; u < kRowUnits<W>; ++u) {
+            const int idx = tid + u * kThreads, row = idx / G, col = (idx % G) * EPG;
+            if (row < nrows)
+                *reinterpret_cast<f32x4_t*>(dst + size_t(ts + row) * W + col) =
+                    *reinterpret_cast<const f32x4_t*>(tile + row * ld + col);
+        }
+    }
+
+    // A state slot in accumulator layout: D * Dv / 4 16-byte pieces per workgroup.
+    static constexpr int kStateUnits = D * DV / 4 / kThreads;
+
+    __device__ __forceinline__ void load_slot(f32x4_t (&r)[kStateUnits], const float* slot) const {
+#pragma unroll
+        for (int u = 0; u < kStateUnits; ++u) r[u] = *reinterpret_cast<const f32x4_t*>(slot + 4 * (tid + u * kThreads));
+    }
+
+    // ... into sS (row-major [D][Dv], operand precision).
+    __device__ __forceinline__ void store_slot(const f32x4_t (&r)[kStateUnits]) const {
+#pragma unroll
+        for (int u = 0; u < kStateUnits; ++u) {
+            const int q4 = tid + u * kThreads;
+            const int t = q4 / kWave, ln = q4 % kWave;
+            const int a = t / (DV / 16), b = t % (DV / 16);
+            const int d = 16 * a + 4 * (ln >> 4), e = 16 * b + (ln & 15);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) sS[(d + k) * LV + e] = X::from_f32(r[u][k]);
         }
     }
 
     // A [D][Dv] state into sS (row-major, operand precision) and its z part into sZ, from
-    // a workspace slot in accumulator layout, from the caller's layout, or zero.
+    // the caller's layout or zero (the workspace slots go through load_slot/store_slot).
     __device__ __forceinline__ void stage_state(const float* slot_s, const float* slot_z, const float* user_s,
                                                 const float* user_z) const {
-        if (slot_s) {
-            for (int q4 = tid; q4 < D * DV / 4; q4 += kThreads) {
-                const f32x4_t v = *reinterpret_cast<const f32x4_t*>(slot_s + 4 * q4);
-                const int u = q4 / kWave, ln = q4 % kWave;
-                const int a = u / (DV / 16), b = u % (DV / 16);
-                const int d = 16 * a + 4 * (ln >> 4), e = 16 * b + (ln & 15);
+        (void)slot_s;
+        for (int q4 = tid; q4 < D * DV / 4; q4 += kThreads) {
+            const int d = q4 / (DV / 4), e = 4 * (q4 % (DV / 4));
+            f32x4_t v = {0.f, 0.f, 0.f, 0.f};
+            if (user_s) v = *reinterpret_cast<const f32x4_t*>(user_s + size_t(d) * DV + e);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) sS[(d + r) * LV + e] = X::from_f32(v[r]);
-            }
-        } else {
-            for (int q4 = tid; q4 < D * DV / 4; q4 += kThreads) {
-                const int d = q4 / (DV / 4), e = 4 * (q4 % (DV / 4));
-                f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-                if (user_s) v = *reinterpret_cast<const f32x4_t*>(user_s + size_t(d) * DV + e);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sS[d * LV + e + r] = X::from_f32(v[r]);
-            }
+            for (int r = 0; r < 4; ++r) sS[d * LV + e + r] = X::from_f32(v[r]);
         }
         for (int d = tid; d < D; d += kThreads) sZ[d] = slot_z ? slot_z[d] : (user_z ? user_z[d] : 0.0f);
     }
@@ -297,17 +335,37 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs args) {
     const E* vb = reinterpret_cast<const E*>(args.v) + size_t(bh) * N * DV;
     const E* dob = reinterpret_cast<const E*>(args.dout) + size_t(bh) * N * DV;
 
-    ck.template stage_rows<D, true>(ck.sQ, LQ, qb);
-    ck.template stage_rows<D, true>(ck.sK, LQ, kb);
-    ck.template stage_rows<DV, false>(ck.sV, LV, vb);
-    ck.template stage_rows<DV, false>(ck.sDn, LV, dob);
-    const size_t fslot = size_t(bh) * NC + (c - 1);
-    ck.stage_state(c > 0 ? args.fst + fslot * (D * DV) : nullptr, c > 0 ? args.fzt + fslot * D : nullptr,
-                   args.s0 ? args.s0 + size_t(bh) * D * DV : nullptr, args.z0 ? args.z0 + size_t(bh) * D : nullptr);
+    {
+        f32x4_t rq[B::template kRowUnits<D>], rk[B::template kRowUnits<D>];
+        f32x4_t rv[B::template kRowUnits<DV>], ro[B::template kRowUnits<DV>];
+        f32x4_t rs[B::kStateUnits];
+        const size_t fslot = size_t(bh) * NC + (c - 1);
+        ck.template load_rows<D>(rq, qb);
+        ck.template load_rows<D>(rk, kb);
+        ck.template load_rows<DV>(rv, vb);
+        ck.template load_rows<DV>(ro, dob);
+        if (c > 0) ck.load_slot(rs, args.fst + fslot * (D * DV));
+        ck.template store_rows<D, true>(ck.sQ, LQ, rq);
+        ck.template store_rows<D, true>(ck.sK, LQ, rk);
+        ck.template store_rows<DV, false>(ck.sV, LV, rv);
+        ck.template store_rows<DV, false>(ck.sDn, LV, ro);
+        if (c > 0) {
+            ck.store_slot(rs);
+            for (int d = ck.tid; d < D; d += kThreads) ck.sZ[d] = args.fzt[fslot * D + d];
+        } else {
+            ck.stage_state(nullptr, nullptr, args.s0 ? args.s0 + size_t(bh) * D * DV : nullptr,
+                           args.z0 ? args.z0 + size_t(bh) * D : nullptr);
+        }
+    }
     ck.stage_lambda(GATED ? args.g + size_t(bh) * N : nullptr);
     __syncthreads();
 
     const int i0 = 16 * w;            // this wave's query rows
+    E xq[ND][4];                      // raw q of this lane's outputs, for phi'(q) at the end (rows clamped)
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) xq[dt][r] = qb[size_t(min(ts + i0 + 4 * g4 + r, N - 1)) * D + 16 * dt + l16];
     float lam_r[4], rs[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) lam_r[r] = ck.lam(i0 + 4 * g4 + r);
@@ -499,21 +557,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs args) {
         for (int dt = 0; dt < ND; ++dt) dfq[dt] = mma(a, frag_col(ck.sK, LQ, 32 * ks + 8 * g4, 16 * dt, l16), dfq[dt]);
     }
 
-    // dq = dFq * phi'(q)
-    {
-        E* dqb = reinterpret_cast<E*>(args.dq) + size_t(bh) * N * D;
+    // dq = dFq * phi'(q), written to LDS once every read of phi(K) is done
 #pragma unroll
-        for (int dt = 0; dt < ND; ++dt) {
+    for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = i0 + 4 * g4 + r;
-                if (ts + i < N) {
-                    const float x = X::to_f32(qb[size_t(ts + i) * D + 16 * dt + l16]);
-                    dqb[size_t(ts + i) * D + 16 * dt + l16] = X::from_f32(dfq[dt][r] * dphi(x));
-                }
-            }
-        }
-    }
+        for (int r = 0; r < 4; ++r) dfq[dt][r] *= dphi(X::to_f32(xq[dt][r]));
 
     // the chunk's adjoint total: dR_c = Fq^T (2^Lambda dNum), dr_c = Fq^T (2^Lambda dden);
     // this wave's rows of dOut become 2^Lambda_i dnum_i (every other read of them is done)
@@ -529,6 +577,11 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs args) {
         if (l16 == 0) ck.sDd[i] = dd[r] * f;
     }
     __syncthreads();
+    // phi(K) is no longer read: it takes dq for the coalesced store at the end
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ck.sK[(i0 + 4 * g4 + r) * LQ + 16 * dt + l16] = X::from_f32(dfq[dt][r]);
     {
         const int rs_ = NC - 1 - c;                        // reversed slot
         const size_t rslot = size_t(bh) * (NC + 1) + rs_;
@@ -553,6 +606,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs args) {
         }
         if (GATED && ck.tid == 0) args.rlg[rslot] = ck.sLam[C - 1];
     }
+    __syncthreads();
+    ck.template store_out<D>(reinterpret_cast<E*>(args.dq) + size_t(bh) * N * D, ck.sK, LQ);
 }
 
 // ------------------------------------------------------------ dk / dv pass ----
@@ -573,56 +628,84 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwdArgs args) {
     const E* vb = reinterpret_cast<const E*>(args.v) + size_t(bh) * N * DV;
     const E* dob = reinterpret_cast<const E*>(args.dout) + size_t(bh) * N * DV;
 
-    ck.template stage_rows<D, true>(ck.sQ, LQ, qb);
-    ck.template stage_rows<D, true>(ck.sK, LQ, kb);
-    ck.template stage_rows<DV, false>(ck.sV, LV, vb);
-    ck.template stage_rows<DV, false>(ck.sDn, LV, dob);
-    for (int i = ck.tid; i < C; i += kThreads) {
-        ck.sDd[i] = i < ck.nrows ? args.dden[size_t(bh) * N + ts + i] : 0.0f;
-        ck.sInv[i] = i < ck.nrows ? args.inv[size_t(bh) * N + ts + i] : 0.0f;
-    }
     // R, r: the adjoint of the state after this chunk (zero after the last chunk)
     const size_t rslot = size_t(bh) * (NC + 1) + (NC - 2 - c);
-    if (c < NC - 1)
-        ck.stage_state(args.rst + rslot * (D * DV), args.rzt + rslot * D, nullptr, nullptr);
-    else
-        ck.stage_state(nullptr, nullptr, nullptr, nullptr);
-    ck.stage_lambda(GATED ? args.g + size_t(bh) * N : nullptr);
-    // W_c = 2^Lambda_last (<R, S_prev> + <r, z_prev>): keys in front of the chunk against
-    // queries after it (both states fp32; R and the forward slots share one layout)
-    if constexpr (GATED) {
-        float wp = 0.0f;
+    {
+        f32x4_t rq[B::template kRowUnits<D>], rk[B::template kRowUnits<D>];
+        f32x4_t rv[B::template kRowUnits<DV>], ro[B::template kRowUnits<DV>];
+        f32x4_t rs[B::kStateUnits], rf[B::kStateUnits];
+        ck.template load_rows<D>(rq, qb);
+        ck.template load_rows<D>(rk, kb);
+        ck.template load_rows<DV>(rv, vb);
+        ck.template load_rows<DV>(ro, dob);
+        // W_c needs the state in front of the chunk too (GATED): the forward slot c - 1
+        const bool wpair = GATED && c < NC - 1 && c > 0;
+        if (c < NC - 1) ck.load_slot(rs, args.rst + rslot * (D * DV));
+        if (wpair) ck.load_slot(rf, args.fst + (size_t(bh) * NC + (c - 1)) * (D * DV));
+        float ddv = 0.0f, inv = 0.0f;
+        if (ck.tid < C) {
+            const size_t t = size_t(bh) * N + ts + min(ck.tid, ck.nrows - 1);
+            ddv = args.dden[t];
+            inv = args.inv[t];
+        }
+        ck.template store_rows<D, true>(ck.sQ, LQ, rq);
+        ck.template store_rows<D, true>(ck.sK, LQ, rk);
+        ck.template store_rows<DV, false>(ck.sV, LV, rv);
+        ck.template store_rows<DV, false>(ck.sDn, LV, ro);
+        if (ck.tid < C) {
+            ck.sDd[ck.tid] = ck.tid < ck.nrows ? ddv : 0.0f;
+            ck.sInv[ck.tid] = ck.tid < ck.nrows ? inv : 0.0f;
+        }
         if (c < NC - 1) {
-            const float* R = args.rst + rslot * (D * DV);
-            const float* rz = args.rzt + rslot * D;
-            if (c > 0) {
-                const size_t fslot = size_t(bh) * NC + (c - 1);
-                const float* F = args.fst + fslot * (D * DV);
-                const float* fz = args.fzt + fslot * D;
-                for (int e = ck.tid; e < D * DV; e += kThreads) wp += R[e] * F[e];
-                for (int d = ck.tid; d < D; d += kThreads) wp += rz[d] * fz[d];
-            } else {
+            ck.store_slot(rs);
+            for (int d = ck.tid; d < D; d += kThreads) ck.sZ[d] = args.rzt[rslot * D + d];
+        } else {
+            ck.stage_state(nullptr, nullptr, nullptr, nullptr);
+        }
+        // W_c = 2^Lambda_last (<R, S_prev> + <r, z_prev>): keys in front of the chunk
+        // against queries after it (both states fp32; R and the forward slots share one
+        // layout, S0 is mapped from the caller's)
+        if constexpr (GATED) {
+            float wp = 0.0f;
+            if (wpair) {
+#pragma unroll
+                for (int u = 0; u < B::kStateUnits; ++u)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) wp += rs[u][k] * rf[u][k];
+                const float* fz = args.fzt + (size_t(bh) * NC + (c - 1)) * D;
+                for (int d = ck.tid; d < D; d += kThreads) wp += args.rzt[rslot * D + d] * fz[d];
+            } else if (c == 0 && c < NC - 1) {
                 if (args.s0) {
                     const float* S0 = args.s0 + size_t(bh) * D * DV;
-                    for (int e = ck.tid; e < D * DV; e += kThreads) {
-                        const int u = e / 256, ln = (e / 4) % kWave, r = e % 4;
-                        const int a = u / (DV / 16), b = u % (DV / 16);
-                        wp += R[e] * S0[size_t(16 * a + 4 * (ln >> 4) + r) * DV + 16 * b + (ln & 15)];
+#pragma unroll
+                    for (int u = 0; u < B::kStateUnits; ++u) {
+                        const int q4 = ck.tid + u * kThreads;
+                        const int t = q4 / kWave, ln = q4 % kWave;
+                        const int a = t / (DV / 16), b = t % (DV / 16);
+#pragma unroll
+                        for (int k = 0; k < 4; ++k)
+                            wp += rs[u][k] * S0[size_t(16 * a + 4 * (ln >> 4) + k) * DV + 16 * b + (ln & 15)];
                     }
                 }
                 if (args.z0)
-                    for (int d = ck.tid; d < D; d += kThreads) wp += rz[d] * args.z0[size_t(bh) * D + d];
+                    for (int d = ck.tid; d < D; d += kThreads) wp += args.rzt[rslot * D + d] * args.z0[size_t(bh) * D + d];
             }
-        }
 #pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) wp += __shfl_xor(wp, off, kWave);
-        if (ck.lane == 0) ck.sRow[w] = wp;
+            for (int off = 1; off < kWave; off <<= 1) wp += __shfl_xor(wp, off, kWave);
+            if (ck.lane == 0) ck.sRow[ck.w] = wp;
+        }
     }
+    ck.stage_lambda(GATED ? args.g + size_t(bh) * N : nullptr);
     __syncthreads();
     if (GATED && ck.tid == 0)
         args.wc[size_t(bh) * NC + c] = (ck.sRow[0] + ck.sRow[1] + ck.sRow[2] + ck.sRow[3]) * fast_exp2(ck.lam(C - 1));
 
     const int j0 = 16 * w;            // this wave's key rows
+    E xk[ND][4];                      // raw k of this lane's outputs, for phi'(k) at the end
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) xk[dt][r] = kb[size_t(min(ts + j0 + 4 * g4 + r, N - 1)) * D + 16 * dt + l16];
     float lam_r[4], tail[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -672,8 +755,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwdArgs args) {
     __syncthreads();
 
     // dV = 2^(Lambda_last - Lambda_j) Fk R + (A^T diag(1/d)) dOut
+    f32x4_t dv[NE];
     {
-        f32x4_t dv[NE];
 #pragma unroll
         for (int et = 0; et < NE; ++et) dv[et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -693,14 +776,6 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwdArgs args) {
 #pragma unroll
             for (int et = 0; et < NE; ++et) dv[et] = mma(a, frag_col(ck.sDn, LV, 32 * ks + 8 * g4, 16 * et, l16), dv[et]);
         }
-        E* dvb = reinterpret_cast<E*>(args.dv) + size_t(bh) * N * DV;
-#pragma unroll
-        for (int et = 0; et < NE; ++et)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = j0 + 4 * g4 + r;
-                if (ts + j < N) dvb[size_t(ts + j) * DV + 16 * et + l16] = X::from_f32(dv[et][r]);
-            }
     }
     __syncthreads();
     // B^T over this wave's rows into sA (every read of A^T finished before the barrier)
@@ -745,20 +820,20 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwdArgs args) {
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) dfk[dt] = mma(a, frag_col(ck.sQ, LQ, 32 * ks + 8 * g4, 16 * dt, l16), dfk[dt]);
     }
-    {
-        E* dkb = reinterpret_cast<E*>(args.dk) + size_t(bh) * N * D;
+    // dk = dFk * phi'(k) and dv through the now free phi(K) and V tiles, stored coalesced
+    __syncthreads();
 #pragma unroll
-        for (int dt = 0; dt < ND; ++dt) {
+    for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = j0 + 4 * g4 + r;
-                if (ts + j < N) {
-                    const float x = X::to_f32(kb[size_t(ts + j) * D + 16 * dt + l16]);
-                    dkb[size_t(ts + j) * D + 16 * dt + l16] = X::from_f32(dfk[dt][r] * dphi(x));
-                }
-            }
-        }
-    }
+        for (int r = 0; r < 4; ++r)
+            ck.sK[(j0 + 4 * g4 + r) * LQ + 16 * dt + l16] = X::from_f32(dfk[dt][r] * dphi(X::to_f32(xk[dt][r])));
+#pragma unroll
+    for (int et = 0; et < NE; ++et)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ck.sV[(j0 + 4 * g4 + r) * LV + 16 * et + l16] = X::from_f32(dv[et][r]);
+    __syncthreads();
+    ck.template store_out<D>(reinterpret_cast<E*>(args.dk) + size_t(bh) * N * D, ck.sK, LQ);
+    ck.template store_out<DV>(reinterpret_cast<E*>(args.dv) + size_t(bh) * N * DV, ck.sV, LV);
 }
 
 // --------------------------------------------------------------- gate pass ----
