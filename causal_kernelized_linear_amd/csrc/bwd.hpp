@@ -106,6 +106,9 @@ struct BwdShape {
     static constexpr size_t kOffZ = kOffRow + size_t(C) * 4;
     static constexpr size_t kBytes = kOffZ + size_t(D) * 4;
     static_assert(kBytes == bwd_lds_bytes(int(sizeof(E)), D, DV), "host LDS formula out of step");
+    // workgroups (so waves per SIMD) the LDS allows: the register target of both kernels,
+    // so the compiler does not squeeze the accumulators for an occupancy out of reach
+    static constexpr int kWaves = int(kMaxLds / kBytes) < 1 ? 1 : int(kMaxLds / kBytes);
 };
 
 // Operand of 16 rows from a row-major tile: lane supplies row `row`, contraction
@@ -320,7 +323,9 @@ struct BwdChunk {
 // ----------------------------------------------------------------- dq pass ----
 
 template <typename E, int D, int DV, bool GATED>
-__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs args) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BwdShape<E, D, DV>::kWaves,
+                                                                           BwdShape<E, D, DV>::kWaves)))
+void bwd_dq_kernel(BwdArgs args) {
     using B = BwdChunk<E, D, DV, GATED>;
     using X = Elem<E>;
     constexpr int C = B::C, LQ = B::LQ, LV = B::LV, LA = B::LA;
@@ -613,7 +618,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs args) {
 // ------------------------------------------------------------ dk / dv pass ----
 
 template <typename E, int D, int DV, bool GATED>
-__global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(BwdArgs args) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BwdShape<E, D, DV>::kWaves,
+                                                                           BwdShape<E, D, DV>::kWaves)))
+void bwd_dkv_kernel(BwdArgs args) {
     using B = BwdChunk<E, D, DV, GATED>;
     using X = Elem<E>;
     constexpr int C = B::C, LQ = B::LQ, LV = B::LV, LA = B::LA;
