@@ -26,6 +26,12 @@ L_i = sum_{l=s..i} log g_l:
 Every decay factor used is exp of a non-positive number, so nothing overflows.
 
 ``normalize=False`` returns num alone, as the recurrence does.
+
+Per-dimension decay a [..., N, D] (gated linear attention), with the chunk-local
+inclusive L_i[d] = sum_{l=s..i} log a_l[d]:
+    A_ij  = sum_d Fq_i[d] Fk_j[d] exp(L_i[d] - L_j[d])   for j <= i
+    num_i = (Fq_i * exp(L_i)) S_prev + sum_j A_ij v_j,  den alike with z_prev
+    S_next = Diag(exp(L_last)) S_prev + (Fk * exp(L_last - L))^T V_c   (z alike)
 """
 from __future__ import annotations
 
@@ -34,7 +40,7 @@ import numpy as np
 from .recurrence import EPS, phi
 
 
-def chunked_linear_attention(q, k, v, chunk, g=None, s0=None, z0=None, eps=EPS, normalize=True):
+def chunked_linear_attention(q, k, v, chunk, g=None, s0=None, z0=None, eps=EPS, normalize=True, a=None):
     """Chunked form over [..., N, D] inputs.  Returns (o, S_N, z_N) in float64."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -52,7 +58,19 @@ def chunked_linear_attention(q, k, v, chunk, g=None, s0=None, z0=None, eps=EPS, 
         c = e - s
         tril = np.tril(np.ones((c, c)))
         scores = fq @ np.swapaxes(fk, -1, -2)
-        if g is None:
+        if a is not None:
+            lam = np.cumsum(np.log(np.asarray(a, dtype=np.float64)[..., s:e, :]), axis=-2)    # [.., c, D]
+            diff = lam[..., :, None, :] - lam[..., None, :, :]                             # [.., i, j, D]
+            w = np.exp(np.minimum(diff, 0.0)) * tril[..., None]
+            A = np.einsum("...id,...jd,...ijd->...ij", fq, fk, w)
+            fqd = fq * np.exp(lam)
+            num = fqd @ S + A @ vc
+            den = fqd @ z[..., :, None] + A.sum(-1, keepdims=True)
+            fkd = fk * np.exp(lam[..., -1:, :] - lam)
+            last = np.exp(lam[..., -1, :])
+            S = last[..., :, None] * S + np.swapaxes(fkd, -1, -2) @ vc
+            z = last * z + fkd.sum(-2)
+        elif g is None:
             A = scores * tril
             num = fq @ S + A @ vc
             den = fq @ z[..., :, None] + A.sum(-1, keepdims=True)

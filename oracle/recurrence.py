@@ -36,6 +36,14 @@ What it computes (all arithmetic in float64, inputs widened exactly):
   same gate also decays z, which keeps o_i a normalised average with weights
   prod_{l=j+1..i} g_l phi(q_i).phi(k_j).
 
+* The vector-valued (per key dimension) decay of gated linear attention:
+      S_t = Diag(a_t) S_{t-1} + phi(k_t) v_t^T,   z_t = a_t * z_{t-1} + phi(k_t),
+  a_t in (0, 1]^D per head and token (aicassindra.com page, "RetNet and gated linear
+  attention": S_i = Diag(alpha_i) S_{i-1} + k_i v_i^T; aiwiki.thehackersbrain.dev page,
+  "What is actually lost": the decay G_t multiplies S_{t-1} elementwise, here with
+  G_t[d, e] = a_t[d]).  z takes the same decay, as it does under the scalar gate.  A
+  scalar gate and a vector decay may both be given; they multiply.
+
 * An optional initial state (S0, z0) replaces the zero state, so a sequence
   can be resumed from a saved state; the final state (S_N, z_N) is returned.
 
@@ -60,12 +68,13 @@ def phi(x):
     return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
 
 
-def causal_linear_attention(q, k, v, g=None, s0=None, z0=None, eps=EPS, normalize=True):
+def causal_linear_attention(q, k, v, g=None, s0=None, z0=None, eps=EPS, normalize=True, a=None):
     """Causal kernelized linear attention, one token at a time.
 
     q, k: [..., N, D]; v: [..., N, Dv]; g: [..., N] or None;
     s0: [..., D, Dv] or None; z0: [..., D] or None (None means zeros).
     normalize: divide by max(phi(q)^T z, eps) (True) or return the numerator.
+    a: [..., N, D] per-dimension decay or None.
     Leading dimensions (batch, heads) are independent and are vectorised.
     Returns (o [..., N, Dv], S_N [..., D, Dv], z_N [..., D]), all float64.
     """
@@ -85,6 +94,8 @@ def causal_linear_attention(q, k, v, g=None, s0=None, z0=None, eps=EPS, normaliz
         z = np.array(z0, dtype=np.float64, copy=True)
     if g is not None:
         g = np.asarray(g, dtype=np.float64)
+    if a is not None:
+        a = np.asarray(a, dtype=np.float64)
     o = np.zeros(lead + (n, dv))
     for t in range(n):
         fq = phi(q[..., t, :])
@@ -93,6 +104,10 @@ def causal_linear_attention(q, k, v, g=None, s0=None, z0=None, eps=EPS, normaliz
             gt = g[..., t]
             S = gt[..., None, None] * S
             z = gt[..., None] * z
+        if a is not None:
+            at = a[..., t, :]
+            S = at[..., :, None] * S
+            z = at * z
         S = S + fk[..., :, None] * v[..., t, None, :]
         z = z + fk
         num = np.einsum("...d,...de->...e", fq, S)
@@ -101,10 +116,11 @@ def causal_linear_attention(q, k, v, g=None, s0=None, z0=None, eps=EPS, normaliz
     return o, S, z
 
 
-def decode_step(q, k, v, S, z, g=None, eps=EPS, normalize=True):
+def decode_step(q, k, v, S, z, g=None, eps=EPS, normalize=True, a=None):
     """One recurrent decode step from a stored state.
 
-    q, k: [..., D]; v: [..., Dv]; S: [..., D, Dv]; z: [..., D]; g: [...] or None.
+    q, k: [..., D]; v: [..., Dv]; S: [..., D, Dv]; z: [..., D]; g: [...] or None;
+    a: [..., D] or None.
     The new token is folded into the state first, then read, exactly as one
     iteration of ``causal_linear_attention``.  Returns (o, S', z').
     """
@@ -112,5 +128,6 @@ def decode_step(q, k, v, S, z, g=None, eps=EPS, normalize=True):
     k = np.asarray(k, dtype=np.float64)[..., None, :]
     v = np.asarray(v, dtype=np.float64)[..., None, :]
     gg = None if g is None else np.asarray(g, dtype=np.float64)[..., None]
-    o, S1, z1 = causal_linear_attention(q, k, v, g=gg, s0=S, z0=z, eps=eps, normalize=normalize)
+    aa = None if a is None else np.asarray(a, dtype=np.float64)[..., None, :]
+    o, S1, z1 = causal_linear_attention(q, k, v, g=gg, s0=S, z0=z, eps=eps, normalize=normalize, a=aa)
     return o[..., 0, :], S1, z1

@@ -319,6 +319,66 @@ def pin_numerator_mode(orc):
     np.testing.assert_allclose(Sd, S, rtol=1e-13, atol=1e-13)
 
 
+def _pairwise_vector(q, k, v, a, normalize=True, eps=1e-6):
+    """Brute force with per-dimension decay: A_ij = sum_d phi(q_i)[d] phi(k_j)[d] prod_{l=j+1..i} a_l[d]
+    for j <= i; O = A V / max(A 1, eps) (or A V).  Pure loops, tiny inputs only."""
+    fq, fk = elu1(q), elu1(k)
+    lead = q.shape[:-2]
+    n = q.shape[-2]
+    o = np.zeros(lead + (n, v.shape[-1]))
+    for idx in np.ndindex(*lead):
+        for i in range(n):
+            num = np.zeros(v.shape[-1])
+            den = 0.0
+            for j in range(i + 1):
+                w = fq[idx + (i,)] * fk[idx + (j,)]
+                for l in range(j + 1, i + 1):
+                    w = w * a[idx + (l,)]
+                wsum = float(w.sum())
+                num += wsum * v[idx + (j,)]
+                den += wsum
+            o[idx + (i,)] = num / max(den, eps) if normalize else num
+    return o
+
+
+def pin_vector_decay(orc):
+    """Per-dimension decay (gated linear attention's Diag(alpha_t), aicassindra.com page):
+    * the per-dimension decay-weighted pairwise form, both output modes, D != Dv;
+    * a decay equal in every dimension is the scalar gate;
+    * closed form: q = k = 0 and a constant decay gamma_d per dimension, V constant c,
+      no normaliser: o_i = c sum_d (1 - gamma_d^(i+1)) / (1 - gamma_d);
+    * a decode step with this token's decay continues the run."""
+    for seed, (n, d, dv) in enumerate([(6, 3, 2), (8, 4, 5)]):
+        q, k, v = _rng_inputs(1600 + seed, (2,), n, d, dv, scale=1.5)
+        a = np.random.default_rng(1650 + seed).uniform(0.3, 1.0, size=(2, n, d))
+        for normalize in (True, False):
+            o, _, _ = orc.causal_linear_attention(q, k, v, a=a, normalize=normalize)
+            np.testing.assert_allclose(o, _pairwise_vector(q, k, v, a, normalize), rtol=1e-12, atol=1e-13)
+    q, k, v = _rng_inputs(1700, (2, 2), 11, 4, 3)
+    g = np.random.default_rng(1701).uniform(0.5, 1.0, size=(2, 2, 11))
+    x = orc.causal_linear_attention(q, k, v, g=g)
+    y = orc.causal_linear_attention(q, k, v, a=np.repeat(g[..., None], 4, -1))
+    for p_, r_ in zip(x, y):
+        np.testing.assert_allclose(r_, p_, rtol=1e-13, atol=1e-14)
+    n, d, dv = 12, 4, 3
+    gam = np.array([0.5, 0.8, 0.95, 1.0])
+    c = np.random.default_rng(1702).normal(size=(1, 1, dv))
+    zero = np.zeros((1, n, d))
+    o, _, _ = orc.causal_linear_attention(zero, zero, np.broadcast_to(c, (1, n, dv)),
+                                          a=np.broadcast_to(gam, (1, n, d)), normalize=False)
+    i = np.arange(n, dtype=np.float64)[:, None]
+    geo = np.where(gam < 1.0, (1 - gam[None, :] ** (i + 1)) / np.where(gam < 1.0, 1 - gam[None, :], 1.0), i + 1)
+    np.testing.assert_allclose(o[0], c[0] * geo.sum(-1, keepdims=True), rtol=1e-13, atol=1e-13)
+    q, k, v = _rng_inputs(1703, (3,), 10, 5, 4)
+    a = np.random.default_rng(1704).uniform(0.5, 1.0, size=(3, 10, 5))
+    o, S, z = orc.causal_linear_attention(q, k, v, a=a)
+    _, S9, z9 = orc.causal_linear_attention(q[..., :9, :], k[..., :9, :], v[..., :9, :], a=a[..., :9, :])
+    od, Sd, zd = orc.decode_step(q[..., 9, :], k[..., 9, :], v[..., 9, :], S9, z9, a=a[..., 9, :])
+    np.testing.assert_allclose(od, o[..., 9, :], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(Sd, S, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(zd, z, rtol=1e-13, atol=1e-13)
+
+
 ALL_PINS = [
     pin_phi_values,
     pin_hand_example,
@@ -334,4 +394,5 @@ ALL_PINS = [
     pin_resume,
     pin_decode_composition,
     pin_numerator_mode,
+    pin_vector_decay,
 ]

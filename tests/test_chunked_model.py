@@ -35,6 +35,19 @@ def test_chunked_equals_recurrence(chunk, gated, with_state, normalize):
     np.testing.assert_allclose(z_c, z_r, rtol=1e-11, atol=1e-11)
 
 
+@pytest.mark.parametrize("chunk", [1, 16, 64, 100])
+@pytest.mark.parametrize("normalize", [True, False])
+def test_chunked_vector_decay_equals_recurrence(chunk, normalize):
+    q, k, v, _, s0, z0 = _inputs(chunk + 5, (2,), 90, 6, 5)
+    a = np.random.default_rng(chunk).uniform(0.4, 1.0, size=(2, 90, 6))
+    kw = dict(a=a, s0=s0, z0=z0, normalize=normalize)
+    o_r, S_r, z_r = oracle.causal_linear_attention(q, k, v, **kw)
+    o_c, S_c, z_c = oracle.chunked_linear_attention(q, k, v, chunk, **kw)
+    np.testing.assert_allclose(o_c, o_r, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(S_c, S_r, rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(z_c, z_r, rtol=1e-11, atol=1e-11)
+
+
 def test_chunked_long_decay_does_not_overflow():
     # 0.05 ** 300 underflows; chunk-local decays must keep every factor <= 1.
     q, k, v, _, _, _ = _inputs(11, (1,), 300, 4, 4)

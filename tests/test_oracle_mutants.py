@@ -37,7 +37,10 @@ MUTATIONS = {
     "gate_index_lag": ("gt = g[..., t]", "gt = g[..., max(t - 1, 0)]"),
     "numerator_mode_still_divides": ("if normalize else num", "if normalize or True else num"),
     "numerator_mode_divides_by_raw_den": ("if normalize else num", "if normalize else num / den[..., None]"),
-    "decode_drops_output_mode": ("eps=eps, normalize=normalize)", "eps=eps)"),
+    "decode_drops_output_mode": ("normalize=normalize, a=aa)", "a=aa)"),
+    "vector_decay_on_value_dim": ("S = at[..., :, None] * S", "S = at[..., :1, None] * S"),
+    "vector_decay_skips_z": ("            z = at * z\n", "            z = z\n"),
+    "vector_decay_index_lag": ("at = a[..., t, :]", "at = a[..., max(t - 1, 0), :]"),
 }
 
 
