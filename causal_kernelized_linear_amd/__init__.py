@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     decode_step,
     fwd,
     fwd_chunked,
+    fwd_vdecay,
     fwd_gated,
     linattn_bwd,
     linattn_bwd_workspace_size,
@@ -17,6 +18,9 @@ from .binding import (  # noqa: F401
     linattn_decode_step_ex,
     linattn_fwd_chunked,
     linattn_fwd_ex,
+    linattn_fwd_vdecay,
+    linattn_fwd_vdecay_workspace_size,
+    linattn_decode_step_vdecay,
     linattn_fwd_gated,
     linattn_fwd_workspace_size,
     linattn_set_profile_events,

@@ -9,8 +9,10 @@ no fallback: if the library is missing, every call raises.
 Function names match the C ABI (include/linattn.h):
     linattn_fwd_chunked, linattn_fwd_gated, linattn_fwd_ex, linattn_decode_step,
     linattn_decode_step_ex, linattn_fwd_workspace_size, linattn_bwd,
-    linattn_bwd_workspace_size, linattn_status_string
-plus the tensor-level helpers fwd_chunked, fwd_gated, fwd, bwd and decode_step.
+    linattn_bwd_workspace_size, linattn_fwd_vdecay, linattn_fwd_vdecay_workspace_size,
+    linattn_decode_step_vdecay, linattn_status_string
+plus the tensor-level helpers fwd_chunked, fwd_gated, fwd, fwd_vdecay, bwd and
+decode_step.
 """
 from __future__ import annotations
 
@@ -43,6 +45,9 @@ EXPORTS = {
     "linattn_decode_step": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p]),
     "linattn_decode_step_ex": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p]),
     "linattn_bwd_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "linattn_fwd_vdecay_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
+    "linattn_fwd_vdecay": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p, _sz, _p]),
+    "linattn_decode_step_vdecay": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p]),
     "linattn_bwd": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p, _sz,
                          _p]),
     "linattn_status_string": (ctypes.c_char_p, [_i]),
@@ -115,6 +120,20 @@ def linattn_bwd(q, k, v, g, dout, s0, z0, dq, dk, dv, dg, ds0, dz0, B, H, N, D, 
                 stream) -> int:
     return int(lib().linattn_bwd(q, k, v, g, dout, s0, z0, dq, dk, dv, dg, ds0, dz0, B, H, N, D, Dv, dtype, eps, out,
                                  ws, ws_bytes, stream))
+
+
+def linattn_fwd_vdecay_workspace_size(B, H, N, D, Dv) -> int:
+    return int(lib().linattn_fwd_vdecay_workspace_size(B, H, N, D, Dv))
+
+
+def linattn_fwd_vdecay(q, k, v, a, o, s0, z0, s_out, z_out, B, H, N, D, Dv, dtype, eps, out, ws, ws_bytes,
+                       stream) -> int:
+    return int(lib().linattn_fwd_vdecay(q, k, v, a, o, s0, z0, s_out, z_out, B, H, N, D, Dv, dtype, eps, out, ws,
+                                        ws_bytes, stream))
+
+
+def linattn_decode_step_vdecay(q, k, v, a, S, z, o, B, H, D, Dv, dtype, eps, out, stream) -> int:
+    return int(lib().linattn_decode_step_vdecay(q, k, v, a, S, z, o, B, H, D, Dv, dtype, eps, out, stream))
 
 
 def linattn_set_profile_events(ev0, ev1, ev2, ev3) -> int:
@@ -225,6 +244,39 @@ def fwd(q, k, v, g=None, chunk=128, eps=1e-6, s0=None, z0=None, return_state=Fal
     return _fwd(q, k, v, g, chunk, eps, s0, z0, return_state, out, workspace, normalize)
 
 
+def fwd_vdecay(q, k, v, a, eps=1e-6, s0=None, z0=None, return_state=False, out=None, workspace=None, normalize=True):
+    """Per-dimension decay forward (linattn_fwd_vdecay): a [B,H,N,D] float32 in [2^-8, 1]."""
+    dt = _dtype_code(q)
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _need(t, n, q.dtype, dev)
+    for t, n in ((a, "a"), (s0, "s0"), (z0, "z0")):
+        _need(t, n, torch.float32, dev)
+    if q.dim() != 4 or a is None or tuple(a.shape) != tuple(q.shape):
+        raise ValueError("q must be [B, H, N, D] and a of the same shape")
+    B, H, N, D = q.shape
+    Dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3]:
+        raise ValueError("k must match q, and v must be [B, H, N, Dv]")
+    o = torch.empty(B, H, N, Dv, dtype=q.dtype, device=dev) if out is None else out
+    s_out = z_out = None
+    if return_state:
+        s_out = torch.empty(B, H, D, Dv, dtype=torch.float32, device=dev)
+        z_out = torch.empty(B, H, D, dtype=torch.float32, device=dev)
+    nbytes = linattn_fwd_vdecay_workspace_size(B, H, N, D, Dv)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError("workspace too small")
+    code = linattn_fwd_vdecay(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(o), _ptr(s0), _ptr(z0), _ptr(s_out),
+                              _ptr(z_out), B, H, N, D, Dv, dt, eps, OUT_NORMALIZED if normalize else OUT_NUMERATOR,
+                              _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(code, "linattn_fwd_vdecay")
+    if return_state:
+        return o, s_out, z_out
+    return o
+
+
 def bwd(q, k, v, dout, g=None, s0=None, z0=None, eps=1e-6, normalize=True, state_grads=False, workspace=None,
         grads=None):
     """Gradients of sum(dout * o) for o = fwd(q, k, v, g, s0=s0, z0=z0, eps=eps, normalize=normalize).
@@ -268,9 +320,10 @@ def bwd(q, k, v, dout, g=None, s0=None, z0=None, eps=1e-6, normalize=True, state
     return {"dq": dq, "dk": dk, "dv": dv, "dg": dg, "ds0": ds0, "dz0": dz0}
 
 
-def decode_step(q, k, v, S, z, eps=1e-6, out=None, g=None, normalize=True):
+def decode_step(q, k, v, S, z, eps=1e-6, out=None, g=None, normalize=True, a=None):
     """One decode step: q, k [B,H,D], v [B,H,Dv]; S [B,H,D,Dv] and z [B,H,D] (float32)
-    are updated in place.  g [B,H] float32 gates the state first (S <- g S + ...); with
+    are updated in place.  g [B,H] float32 gates the state first (S <- g S + ...), or a
+    [B,H,D] float32 decays each of its rows (S <- Diag(a) S + ...); with
     ``normalize=False`` the output is the numerator and z may be None.  Returns o [B,H,Dv]."""
     dt = _dtype_code(q)
     dev = q.device
@@ -287,10 +340,17 @@ def decode_step(q, k, v, S, z, eps=1e-6, out=None, g=None, normalize=True):
         raise ValueError("shape mismatch")
     if g is not None and tuple(g.shape) != (B, H):
         raise ValueError("g must be [B, H]")
+    _need(a, "a", torch.float32, dev)
+    if a is not None and (tuple(a.shape) != (B, H, D) or g is not None):
+        raise ValueError("a must be [B, H, D], and not given with g")
     if z is None and normalize:
         raise ValueError("the normalised output needs z")
     o = torch.empty(B, H, Dv, dtype=q.dtype, device=dev) if out is None else out
-    if g is None and normalize:
+    if a is not None:
+        code = linattn_decode_step_vdecay(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(S), _ptr(z), _ptr(o), B, H, D, Dv,
+                                          dt, eps, OUT_NORMALIZED if normalize else OUT_NUMERATOR, _stream(dev))
+        _check(code, "linattn_decode_step_vdecay")
+    elif g is None and normalize:
         code = linattn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(S), _ptr(z), _ptr(o), B, H, D, Dv, dt, eps,
                                    _stream(dev))
         _check(code, "linattn_decode_step")

@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstring>
 #include <mutex>
+#include <utility>
 
 #include "../../include/linattn.h"
 #include "launch.hpp"
@@ -180,8 +181,8 @@ linattn_status_t fwd_common(const void* q, const void* k, const void* v, const f
     return e == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP;
 }
 
-linattn_status_t decode_common(const void* q, const void* k, const void* v, const float* g, float* S, float* z,
-                               void* o, int B, int H, int D, int Dv, linattn_dtype_t dtype, float eps,
+linattn_status_t decode_common(const void* q, const void* k, const void* v, const float* g, const float* ga, float* S,
+                               float* z, void* o, int B, int H, int D, int Dv, linattn_dtype_t dtype, float eps,
                                linattn_output_t out, void* stream) {
     if (B < 0 || H < 0 || D <= 0 || Dv <= 0) return LINATTN_ERR_INVALID_ARGUMENT;
     if (!dtype_ok(dtype) || !out_ok(out) || !(eps > 0.0f) || !std::isfinite(eps)) return LINATTN_ERR_INVALID_ARGUMENT;
@@ -189,21 +190,22 @@ linattn_status_t decode_common(const void* q, const void* k, const void* v, cons
     if (BH == 0) return LINATTN_OK;
     if (BH > (1L << 31) - 1) return LINATTN_ERR_INVALID_ARGUMENT;
     if (!q || !k || !v || !S || !o || (!z && out == LINATTN_OUT_NORMALIZED)) return LINATTN_ERR_INVALID_ARGUMENT;
-    for (const void* p : {q, k, v, static_cast<const void*>(g), static_cast<const void*>(S),
-                          static_cast<const void*>(z), static_cast<const void*>(o)})
+    for (const void* p : {q, k, v, static_cast<const void*>(g), static_cast<const void*>(ga),
+                          static_cast<const void*>(S), static_cast<const void*>(z), static_cast<const void*>(o)})
         if (p && !aligned16(p)) return LINATTN_ERR_INVALID_ARGUMENT;
     const size_t es = esize(dtype);
     const size_t no = size_t(BH) * Dv * es, ns = size_t(BH) * D * Dv * 4, nz = size_t(BH) * D * 4,
                  ng = size_t(BH) * 4;
     if (overlap(o, no, q, size_t(BH) * D * es) || overlap(o, no, k, size_t(BH) * D * es) || overlap(o, no, v, no) ||
         overlap(o, no, S, ns) || overlap(o, no, z, nz) || overlap(S, ns, z, nz) || overlap(g, ng, S, ns) ||
-        overlap(g, ng, z, nz) || overlap(g, ng, o, no))
+        overlap(g, ng, z, nz) || overlap(g, ng, o, no) || overlap(ga, nz, S, ns) || overlap(ga, nz, z, nz) ||
+        overlap(ga, nz, o, no))
         return LINATTN_ERR_INVALID_ARGUMENT;
     if (!dim_ok(D) || !dim_ok(Dv)) return LINATTN_ERR_UNSUPPORTED;
     const linattn_status_t dst = check_device();
     if (dst != LINATTN_OK) return dst;
     (void)hipGetLastError();
-    const hipError_t e = linattn::launch_decode(int(dtype), q, k, v, S, z, o, int(BH), D, Dv, eps, g,
+    const hipError_t e = linattn::launch_decode(int(dtype), q, k, v, S, z, o, int(BH), D, Dv, eps, g, ga,
                                                 out == LINATTN_OUT_NORMALIZED ? 1 : 0,
                                                 static_cast<hipStream_t>(stream));
     return e == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP;
@@ -258,6 +260,52 @@ linattn_status_t bwd_common(const void* q, const void* k, const void* v, const f
     L.stream = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     const hipError_t e = dtype == LINATTN_BF16 ? linattn::launch_bwd_bf16(L) : linattn::launch_bwd_f32(L);
+    return e == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP;
+}
+
+linattn_status_t vd_common(const void* q, const void* k, const void* v, const float* a, void* o, const float* s0,
+                           const float* z0, float* s_out, float* z_out, int B, int H, int N, int D, int Dv,
+                           linattn_dtype_t dtype, float eps, linattn_output_t out, void* ws, size_t ws_bytes,
+                           void* stream) {
+    if (B < 0 || H < 0 || N < 0 || D <= 0 || Dv <= 0) return LINATTN_ERR_INVALID_ARGUMENT;
+    if (!dtype_ok(dtype) || !out_ok(out) || !(eps > 0.0f) || !std::isfinite(eps)) return LINATTN_ERR_INVALID_ARGUMENT;
+    const long BH = long(B) * long(H);
+    if (BH == 0 || N == 0) return LINATTN_OK;
+    if (BH > (1L << 24) || long(N) * BH > (1L << 40)) return LINATTN_ERR_INVALID_ARGUMENT;
+    if (!q || !k || !v || !a || !o) return LINATTN_ERR_INVALID_ARGUMENT;
+    for (const void* p : {q, k, v, static_cast<const void*>(a), static_cast<const void*>(o),
+                          static_cast<const void*>(s0), static_cast<const void*>(z0), static_cast<const void*>(s_out),
+                          static_cast<const void*>(z_out)})
+        if (p && !aligned16(p)) return LINATTN_ERR_INVALID_ARGUMENT;
+    const size_t es = esize(dtype);
+    const size_t nqk = size_t(BH) * N * D * es, nv = size_t(BH) * N * Dv * es, na = size_t(BH) * N * D * 4;
+    const size_t ns = size_t(BH) * D * Dv * 4, nz = size_t(BH) * D * 4;
+    if (overlap(o, nv, q, nqk) || overlap(o, nv, k, nqk) || overlap(o, nv, v, nv) || overlap(o, nv, a, na) ||
+        overlap(s_out, ns, o, nv) || overlap(z_out, nz, o, nv) || overlap(s_out, ns, a, na) ||
+        overlap(z_out, nz, a, na))
+        return LINATTN_ERR_INVALID_ARGUMENT;
+    if ((size_t(N) + 256) * size_t(Dv > D ? Dv : D) * 4 >= (size_t(1) << 31)) return LINATTN_ERR_UNSUPPORTED;
+    if (!dim_ok(D) || !dim_ok(Dv) || linattn::vd_lds_bytes(int(es), D, Dv) > linattn::kMaxLds)
+        return LINATTN_ERR_UNSUPPORTED;
+    const linattn::VdLayout lay = linattn::vd_workspace_layout(size_t(BH), N, D, Dv);
+    if (ws_bytes < lay.bytes || !ws || !aligned16(ws)) return LINATTN_ERR_WORKSPACE;
+    for (const auto& b : {std::make_pair(static_cast<const void*>(q), nqk), std::make_pair(static_cast<const void*>(k), nqk),
+                          std::make_pair(static_cast<const void*>(v), nv), std::make_pair(static_cast<const void*>(a), na),
+                          std::make_pair(static_cast<const void*>(o), nv), std::make_pair(static_cast<const void*>(s0), ns),
+                          std::make_pair(static_cast<const void*>(z0), nz),
+                          std::make_pair(static_cast<const void*>(s_out), ns),
+                          std::make_pair(static_cast<const void*>(z_out), nz)})
+        if (overlap(ws, lay.bytes, b.first, b.second)) return LINATTN_ERR_WORKSPACE;
+    const linattn_status_t dst = check_device();
+    if (dst != LINATTN_OK) return dst;
+    linattn::VdLaunch L;
+    L.q = q; L.k = k; L.v = v; L.a = a; L.o = o; L.s0 = s0; L.z0 = z0; L.s_out = s_out; L.z_out = z_out;
+    L.ws = ws;
+    L.BH = int(BH); L.N = N; L.D = D; L.Dv = Dv; L.eps = eps;
+    L.normalize = out == LINATTN_OUT_NORMALIZED ? 1 : 0;
+    L.stream = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    const hipError_t e = dtype == LINATTN_BF16 ? linattn::launch_vd_bf16(L) : linattn::launch_vd_f32(L);
     return e == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP;
 }
 
@@ -327,7 +375,8 @@ linattn_status_t linattn_fwd_ex(const void* q, const void* k, const void* v, con
 linattn_status_t linattn_decode_step(const void* q, const void* k, const void* v, float* S, float* z, void* o, int B,
                                      int H, int D, int Dv, linattn_dtype_t dtype, float eps, void* stream) {
     try {
-        return decode_common(q, k, v, nullptr, S, z, o, B, H, D, Dv, dtype, eps, LINATTN_OUT_NORMALIZED, stream);
+        return decode_common(q, k, v, nullptr, nullptr, S, z, o, B, H, D, Dv, dtype, eps, LINATTN_OUT_NORMALIZED,
+                             stream);
     } catch (...) {
         return LINATTN_ERR_HIP;
     }
@@ -337,7 +386,35 @@ linattn_status_t linattn_decode_step_ex(const void* q, const void* k, const void
                                         float* z, void* o, int B, int H, int D, int Dv, linattn_dtype_t dtype,
                                         float eps, linattn_output_t out, void* stream) {
     try {
-        return decode_common(q, k, v, g, S, z, o, B, H, D, Dv, dtype, eps, out, stream);
+        return decode_common(q, k, v, g, nullptr, S, z, o, B, H, D, Dv, dtype, eps, out, stream);
+    } catch (...) {
+        return LINATTN_ERR_HIP;
+    }
+}
+
+linattn_status_t linattn_decode_step_vdecay(const void* q, const void* k, const void* v, const float* a, float* S,
+                                            float* z, void* o, int B, int H, int D, int Dv, linattn_dtype_t dtype,
+                                            float eps, linattn_output_t out, void* stream) {
+    try {
+        if (!a && long(B) * long(H) > 0) return LINATTN_ERR_INVALID_ARGUMENT;
+        return decode_common(q, k, v, nullptr, a, S, z, o, B, H, D, Dv, dtype, eps, out, stream);
+    } catch (...) {
+        return LINATTN_ERR_HIP;
+    }
+}
+
+size_t linattn_fwd_vdecay_workspace_size(int B, int H, int N, int D, int Dv) {
+    if (B <= 0 || H <= 0 || N <= 0 || D <= 0 || Dv <= 0) return 0;
+    return linattn::vd_workspace_layout(size_t(B) * size_t(H), N, D, Dv).bytes;
+}
+
+linattn_status_t linattn_fwd_vdecay(const void* q, const void* k, const void* v, const float* a, void* o,
+                                    const float* s0, const float* z0, float* s_out, float* z_out, int B, int H, int N,
+                                    int D, int Dv, linattn_dtype_t dtype, float eps, linattn_output_t out,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+    try {
+        return vd_common(q, k, v, a, o, s0, z0, s_out, z_out, B, H, N, D, Dv, dtype, eps, out, workspace,
+                         workspace_bytes, stream);
     } catch (...) {
         return LINATTN_ERR_HIP;
     }

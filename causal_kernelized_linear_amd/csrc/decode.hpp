@@ -13,6 +13,8 @@
 // The gated step decays the state first, S <- g S + phi(k) v^T and z <- g z + phi(k),
 // with one gate per head (aicassindra.com page, "RetNet and gated linear attention");
 // a NULL gate is 1, and since 1 * s is exact the ungated step is the same arithmetic.
+// With a per-dimension decay ga [D] per head (gated linear attention's Diag(alpha)),
+// row d of S and z[d] take ga[d] instead.
 // In the normaliser-free mode (retention's output, no phi(q)^T z denominator) o is the
 // numerator and z, which may then be NULL, is left alone.
 #pragma once
@@ -24,8 +26,9 @@ namespace linattn {
 template <typename E, int D, int DV>
 __global__ __launch_bounds__(kThreads) void decode_kernel(const E* __restrict__ q, const E* __restrict__ k,
                                                          const E* __restrict__ v, const float* __restrict__ g,
-                                                         float* __restrict__ S, float* __restrict__ z,
-                                                         E* __restrict__ o, float eps, int normalize) {
+                                                         const float* __restrict__ ga, float* __restrict__ S,
+                                                         float* __restrict__ z, E* __restrict__ o, float eps,
+                                                         int normalize) {
     using X = Elem<E>;
     constexpr int CQ = DV / 4;            // 16-byte column quads per state row
     constexpr int RG = kThreads / CQ;     // row groups
@@ -56,11 +59,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const E* __restrict__ 
 #pragma unroll
     for (int r = 0; r < 4; ++r) vv[r] = X::to_f32(vb[4 * cq + r]);
     const float gt = g ? g[bh] : 1.0f;
+    const float* gab = ga ? ga + size_t(bh) * D : nullptr;
 
     // denominator: z' = g z + phi(k), den = phi(q) . z'
     float den = 0.0f;
     if (z && tid < D) {
-        const float zn = fmaf(gt, z[size_t(bh) * D + tid], phi(X::to_f32(kb[tid])));
+        const float zn = fmaf(gab ? gab[tid] : gt, z[size_t(bh) * D + tid], phi(X::to_f32(kb[tid])));
         z[size_t(bh) * D + tid] = zn;
         den = phi(X::to_f32(qb[tid])) * zn;
     }
@@ -72,8 +76,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const E* __restrict__ 
         const float fk = phi(X::to_f32(kb[d]));
         const float fq = phi(X::to_f32(qb[d]));
         f32x4_t s = srow[i];
+        const float gd = gab ? gab[d] : gt;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s[r] = fmaf(fk, vv[r], gt * s[r]);
+        for (int r = 0; r < 4; ++r) s[r] = fmaf(fk, vv[r], gd * s[r]);
         __builtin_nontemporal_store(s, reinterpret_cast<f32x4_t*>(Sb + size_t(d) * DV + 4 * cq));
 #pragma unroll
         for (int r = 0; r < 4; ++r) num[r] = fmaf(fq, s[r], num[r]);

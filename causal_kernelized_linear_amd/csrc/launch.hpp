@@ -128,12 +128,59 @@ struct BwdLaunch {
     hipStream_t stream;
 };
 
+// Dynamic LDS bytes of the per-dimension-decay output kernel: phi(Q), phi(K) [C][D], V
+// [C][Dv], S_prev [D][Dv] and A [C][C] (rows padded by 16 bytes), the decays [C][D + 4]
+// and z_prev [D] in fp32.  VdShape<...>::kBytes is checked against it.
+constexpr size_t vd_lds_bytes(int esize, int D, int Dv) {
+    const size_t es = size_t(esize), pad = 16 / es, C = kBwdChunkHost;
+    return (2 * C * (D + pad) + C * (Dv + pad) + size_t(D) * (Dv + pad) + C * (C + pad)) * es +
+           C * (size_t(D) + 4) * 4 + size_t(D) * 4;
+}
+
+// Workspace of the per-dimension-decay forward: the state after every 64-token chunk
+// [BH][NC][D*Dv], its z [BH][NC][D] and each chunk's log2 decay per dimension [BH][NC][D].
+struct VdLayout {
+    size_t st, zt, lg, bytes;
+};
+
+inline VdLayout vd_workspace_layout(size_t BH, int N, int D, int Dv) {
+    VdLayout L;
+    const size_t nc = (size_t(N) + kBwdChunkHost - 1) / kBwdChunkHost;
+    size_t oz = 0, ol = 0;
+    const size_t fb = fwd_workspace_layout(BH * nc, D, Dv, &oz, &ol);
+    L.st = 0;
+    L.zt = oz;
+    L.lg = fb;
+    L.bytes = fb + round_up256(BH * nc * size_t(D) * 4);
+    return L;
+}
+
+struct VdLaunch {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* a;
+    void* o;
+    const float* s0;
+    const float* z0;
+    float* s_out;
+    float* z_out;
+    void* ws;
+    int BH, N, D, Dv;
+    float eps;
+    int normalize;
+    hipStream_t stream;
+};
+
+hipError_t launch_vd_bf16(const VdLaunch& p);
+hipError_t launch_vd_f32(const VdLaunch& p);
+
 hipError_t launch_fwd_bf16(const FwdLaunch& p);
 hipError_t launch_fwd_f32(const FwdLaunch& p);
 hipError_t launch_bwd_bf16(const BwdLaunch& p);
 hipError_t launch_bwd_f32(const BwdLaunch& p);
 hipError_t launch_decode(int dtype, const void* q, const void* k, const void* v, float* S, float* z, void* o,
-                         int BH, int D, int Dv, float eps, const float* g, int normalize,
+                         int BH, int D, int Dv, float eps, const float* g, const float* ga, int normalize,
                          hipStream_t stream);
 
 }  // namespace linattn

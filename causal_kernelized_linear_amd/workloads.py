@@ -26,7 +26,7 @@ import torch
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                     # "fwd", "gated", "decode" or "decode_gated"
+    kind: str                     # "fwd", "gated", "vdecay", "decode", "decode_gated" or "decode_vdecay"
     B: int
     H: int
     N: int                        # tokens (1 for a decode step)
@@ -57,6 +57,10 @@ WORKLOADS = {
                            note="scalar gate per head per token"),
     "decode_gated_bf16": Workload("decode_gated_bf16", "decode_gated", 256, 32, 1, 128, 128, "bf16", (1,), 1006,
                                   note="one gated recurrent step: the decode form of the gated forward"),
+    "vdecay_bf16": Workload("vdecay_bf16", "vdecay", 4, 16, 8192, 64, 64, "bf16", (64,), 1007,
+                            note="per-dimension decay per head and token (gated linear attention)"),
+    "decode_vdecay_bf16": Workload("decode_vdecay_bf16", "decode_vdecay", 256, 32, 1, 128, 128, "bf16", (1,), 1008,
+                                   note="one recurrent step under a per-dimension decay"),
 }
 
 
@@ -77,6 +81,9 @@ def make_inputs(w: Workload, B=None, H=None, N=None, with_grad=False):
               each 1000*|N(0,1)| (a state after about 1000 tokens)
       decode_gated: the same plus this token's gate g [B,H] float32, drawn last as
               0.9 + 0.1*sigmoid(N(0,1)) like the gated forward's gates
+      vdecay: the forward's q, k, v plus a per-dimension decay a [B,H,N,D] float32,
+              0.9 + 0.1*sigmoid(N(0,1)) elementwise
+      decode_vdecay: the decode inputs plus this token's decay a [B,H,D], drawn alike
     With ``with_grad`` (forward kinds) an upstream gradient dout [B,H,N,Dv] ~ N(0,1) in
     the input dtype is drawn after everything else, for the backward.
     """
@@ -85,7 +92,7 @@ def make_inputs(w: Workload, B=None, H=None, N=None, with_grad=False):
     N = w.N if N is None else N
     gen = torch.Generator(device="cpu").manual_seed(w.seed)
     dt = w.torch_dtype
-    if w.kind in ("decode", "decode_gated"):
+    if w.kind in ("decode", "decode_gated", "decode_vdecay"):
         q = _randn(gen, (B, H, w.D), w.scale).to(dt)
         k = _randn(gen, (B, H, w.D), w.scale).to(dt)
         v = _randn(gen, (B, H, w.Dv), w.scale).to(dt)
@@ -94,6 +101,8 @@ def make_inputs(w: Workload, B=None, H=None, N=None, with_grad=False):
         out = {"q": q, "k": k, "v": v, "S": S, "z": z}
         if w.kind == "decode_gated":
             out["g"] = 0.9 + 0.1 * torch.sigmoid(_randn(gen, (B, H)))
+        if w.kind == "decode_vdecay":
+            out["a"] = 0.9 + 0.1 * torch.sigmoid(_randn(gen, (B, H, w.D)))
         return out
     q = _randn(gen, (B, H, N, w.D), w.scale).to(dt)
     k = _randn(gen, (B, H, N, w.D), w.scale).to(dt)
@@ -101,6 +110,8 @@ def make_inputs(w: Workload, B=None, H=None, N=None, with_grad=False):
     out = {"q": q, "k": k, "v": v}
     if w.kind == "gated":
         out["g"] = 0.9 + 0.1 * torch.sigmoid(_randn(gen, (B, H, N)))
+    if w.kind == "vdecay":
+        out["a"] = 0.9 + 0.1 * torch.sigmoid(_randn(gen, (B, H, N, w.D)))
     if with_grad:
         out["dout"] = _randn(gen, (B, H, N, w.Dv)).to(dt)
     return out

@@ -133,6 +133,41 @@ linattn_status_t linattn_fwd_ex(
     linattn_output_t out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Per-dimension decay (gated linear attention):
+ *
+ *     S_t = Diag(a_t) S_{t-1} + phi(k_t) v_t^T,   z_t = a_t * z_{t-1} + phi(k_t),
+ *     o_t = S_t^T phi(q_t) / max(phi(q_t) . z_t, eps)   (or the numerator, `out`)
+ *
+ * (aicassindra.com page, "RetNet and gated linear attention": S_i = Diag(alpha_i) S_{i-1}
+ * + k_i v_i^T; aiwiki.thehackersbrain.dev page, "What is actually lost": an elementwise
+ * decay G_t of S_{t-1}, here G_t[d, e] = a_t[d]; z decays alike).
+ *
+ *  a  [B,H,N,D] float, device, read-only.  Precondition (not checked on the device):
+ *     2^-8 <= a <= 1 (within a 16-token block the rescaled operands of the chunk products
+ *     stay below 2^64).
+ *  Every other argument is as for linattn_fwd_ex; the workspace is sized by
+ *  linattn_fwd_vdecay_workspace_size (the state after every 64-token chunk).  Supported
+ *  shapes: D, Dv in {64, 128}; bf16 at every pair, f32 at D = 64.
+ */
+size_t linattn_fwd_vdecay_workspace_size(int B, int H, int N, int D, int Dv);
+
+linattn_status_t linattn_fwd_vdecay(
+    const void* q, const void* k, const void* v, const float* a, void* o,
+    const float* s0, const float* z0, float* s_out, float* z_out,
+    int B, int H, int N, int D, int Dv, linattn_dtype_t dtype, float eps, linattn_output_t out,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One decode step under the per-dimension decay: S <- Diag(a) S + phi(k) v^T,
+ * z <- a * z + phi(k), then o as chosen by `out`; a [B,H,D] float is this token's decay,
+ * 0 < a <= 1, and must not overlap S, z or o.  Every other argument is as for
+ * linattn_decode_step_ex (z may be NULL without the denominator).
+ */
+linattn_status_t linattn_decode_step_vdecay(
+    const void* q, const void* k, const void* v, const float* a, float* S, float* z, void* o,
+    int B, int H, int D, int Dv, linattn_dtype_t dtype, float eps, linattn_output_t out, void* stream);
+
+/*
  * Bytes of device scratch linattn_bwd needs for these sizes and dtype (the state in
  * front of every 64-token chunk and its adjoint, float, plus per-token intermediates).
  * 0 when B*H*N == 0 or a size is not positive.  Contents are undefined after a call; it
