@@ -9,8 +9,9 @@ its inputs warm in the 256 MB Infinity Cache.  The scalar-gated forward
 (B=4, H=16, N=8192, D=Dv=64, chunk 128), the long-context forward
 (B=1, H=32, N=65536, D=Dv=128, chunk sweep), the decode step (B=256, H=32,
 D=Dv=128, fp32 state), its gated form, the normaliser-free output mode of the
-gated forward and of the gated decode, and the backward of the training-shaped and
-gated forwards are timed in the same run and reported in extra fields.
+gated forward and of the gated decode, the backward of the training-shaped and
+gated forwards, and the per-dimension decay (forward and decode) are timed in the same
+run and reported in extra fields.
 
 Prints ONE JSON line.  ms_per_step and value come from a timed pass bracketed by
 two hipEvents only.  Per-kernel durations come from a second timed pass of the same
@@ -205,7 +206,7 @@ def time_decode(w, steps, warmup, ev, normalize=True):
     def call(i):
         s = sets[i % nsets]
         binding.decode_step(s["q"], s["k"], s["v"], s["S"], s["z"] if normalize else None, out=outs[i % nsets],
-                            g=s.get("g"), normalize=normalize)
+                            g=s.get("g"), normalize=normalize, a=s.get("a"))
 
     for i in range(warmup):
         call(i)
@@ -276,12 +277,53 @@ def time_backward(w, steps, warmup, ev):
     return {"ms_per_step": ms}
 
 
+def vd_bytes_per_unit(w):
+    """q, k, v and the per-dimension decay read once, o written once."""
+    es = 4 if w.dtype == "f32" else 2
+    return (2 * w.D + w.Dv) * es + 4 * w.D + w.Dv * es
+
+
+def time_vdecay(w, steps, warmup, ev):
+    """Per-step time of linattn_fwd_vdecay on workload w (two input sets rotated)."""
+    import torch
+    from causal_kernelized_linear_amd import binding, workloads
+
+    dev = torch.device("cuda:0")
+    base = workloads.make_inputs(w)
+    sets = [{n: t.to(dev) for n, t in base.items()}]
+    sets.append({n: t.clone() for n, t in sets[0].items()})
+    outs = [torch.empty(w.B, w.H, w.N, w.Dv, dtype=w.torch_dtype, device=dev) for _ in range(2)]
+    ws = torch.empty(binding.linattn_fwd_vdecay_workspace_size(w.B, w.H, w.N, w.D, w.Dv), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def call(i):
+        s = sets[i % 2]
+        binding.fwd_vdecay(s["q"], s["k"], s["v"], s["a"], out=outs[i % 2], workspace=ws)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    t0, t1 = ev.create(2)
+    ev.record(t0, stream)
+    for i in range(steps):
+        call(i)
+    ev.record(t1, stream)
+    torch.cuda.synchronize()
+    ms = ev.ms(t0, t1) / steps
+    del sets, outs, ws
+    torch.cuda.empty_cache()
+    return {"ms_per_step": ms}
+
+
 def decode_bytes(w, with_z=True):
     """S (and z) read and written once, q, k, v read, o written, plus the gate when gated."""
     es = 4 if w.dtype == "f32" else 2
     per_head = 2 * (w.D * w.Dv + (w.D if with_z else 0)) * 4 + (2 * w.D + w.Dv) * es + w.Dv * es
     if w.kind == "decode_gated":
         per_head += 4
+    if w.kind == "decode_vdecay":
+        per_head += 4 * w.D
     return per_head * w.B * w.H
 
 
@@ -480,6 +522,24 @@ def main():
                 "useful_TFLOPs": bwd_flops_per_unit(wb) * ub / sb / 1e12,
                 "mfma_bf16_frac": bwd_flops_per_unit(wb) * ub / sb / 1e12 / MFMA_BF16_PEAK_TFLOPS,
             }
+        wvd = workloads.WORKLOADS["vdecay_bf16"]
+        rvd = time_vdecay(wvd, extra_steps, extra_warm, ev)
+        svd = rvd["ms_per_step"] * 1e-3
+        uvd = fwd_units(wvd)
+        line["vdecay"] = {
+            "workload": "vdecay_bf16: B=4 H=16 N=8192 D=Dv=64 bf16, per-dimension decay a [B,H,N,D] fp32, chunk 64",
+            "tokens_per_s": wvd.B * wvd.N / svd, "ms_per_step": rvd["ms_per_step"],
+            "algorithmic_GBps": vd_bytes_per_unit(wvd) * uvd / svd / 1e9,
+            "hbm_frac": vd_bytes_per_unit(wvd) * uvd / svd / 1e9 / HBM_PEAK_GBS,
+        }
+        wdv = workloads.WORKLOADS["decode_vdecay_bf16"]
+        rdv = time_decode(wdv, extra_steps, extra_warm, ev)
+        sdv = rdv["ms_per_step"] * 1e-3
+        line["decode_vdecay"] = {
+            "workload": "decode_vdecay_bf16: B=256 H=32 D=Dv=128, fp32 state, one token, decay per dimension",
+            "GBps": decode_bytes(wdv) / sdv / 1e9, "hbm_frac": decode_bytes(wdv) / sdv / 1e9 / HBM_PEAK_GBS,
+            "tokens_per_s": wdv.B / sdv, "ms_per_step": rdv["ms_per_step"], "bytes_per_step": decode_bytes(wdv),
+        }
         wl = workloads.WORKLOADS["longctx_bf16"]
         sweep = {}
         for c in wl.chunks:

@@ -60,6 +60,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const E* __restrict__ 
     for (int r = 0; r < 4; ++r) vv[r] = X::to_f32(vb[4 * cq + r]);
     const float gt = g ? g[bh] : 1.0f;
     const float* gab = ga ? ga + size_t(bh) * D : nullptr;
+    // the decay of each of this thread's rows, read once (behind a uniform branch) while
+    // the state loads are in flight
+    float gd[RPT];
+    if (gab) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) gd[i] = gab[rg + RG * i];
+    } else {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) gd[i] = gt;
+    }
 
     // denominator: z' = g z + phi(k), den = phi(q) . z'
     float den = 0.0f;
@@ -76,9 +86,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const E* __restrict__ 
         const float fk = phi(X::to_f32(kb[d]));
         const float fq = phi(X::to_f32(qb[d]));
         f32x4_t s = srow[i];
-        const float gd = gab ? gab[d] : gt;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s[r] = fmaf(fk, vv[r], gd * s[r]);
+        for (int r = 0; r < 4; ++r) s[r] = fmaf(fk, vv[r], gd[i] * s[r]);
         __builtin_nontemporal_store(s, reinterpret_cast<f32x4_t*>(Sb + size_t(d) * DV + 4 * cq));
 #pragma unroll
         for (int r = 0; r < 4; ++r) num[r] = fmaf(fq, s[r], num[r]);
