@@ -11,9 +11,9 @@ forms, invariants and brute force on tiny inputs; ``tests/test_oracle_mutants.py
 plants mistakes in a copy of the recurrence and checks the pins catch each one;
 ``tests/test_oracle_bwd.py`` does the same for the backward (``tests/pins_bwd.py``).
 """
-from .recurrence import EPS, causal_linear_attention, decode_step, phi
+from .recurrence import EPS, causal_linear_attention, decode_step, favor_features, feature_map, phi, relu_features
 from .chunked import chunked_linear_attention
 from .backward import causal_linear_attention_bwd
 
-__all__ = ["EPS", "phi", "causal_linear_attention", "decode_step", "chunked_linear_attention",
-           "causal_linear_attention_bwd"]
+__all__ = ["EPS", "phi", "relu_features", "favor_features", "feature_map", "causal_linear_attention",
+           "decode_step", "chunked_linear_attention", "causal_linear_attention_bwd"]

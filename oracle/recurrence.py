@@ -14,6 +14,14 @@ What it computes (all arithmetic in float64, inputs widened exactly):
   evaluated on min(x, 0) so the unused branch cannot overflow, as the
   mlblogg.com page does in "An implementation you can check".
 
+* Other feature maps, by ``feature``: ``("relu", shift)`` gives max(x, 0) + shift (the
+  "F.relu(x) + eps" alternative the anandmoghan-problems page names under "Key Functions
+  & Tricks"); ``("favor", W)`` gives Performer's positive random features
+  phi(x)_r = exp(w_r . x - |x|^2 / 2) / sqrt(m) for the m rows w_r of W [H, m, D] (one
+  set per head; aicassindra.com page, "Performer: unbiased softmax by positive random
+  features", whose expected inner product is exp(q . k)).  The state is then
+  [m, Dv] and z [m].
+
 * The causal recurrence of the learn.pranaymahendrakar.com page (Researcher
   level, "Derivation", the display equations for S_i, z_i and o_i):
       S_i = S_{i-1} + phi(k_i) v_i^T,   z_i = z_{i-1} + phi(k_i),
@@ -68,13 +76,41 @@ def phi(x):
     return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
 
 
-def causal_linear_attention(q, k, v, g=None, s0=None, z0=None, eps=EPS, normalize=True, a=None):
+def relu_features(x, shift):
+    """max(x, 0) + shift, in float64."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.maximum(x, 0.0) + shift
+
+
+def favor_features(x, W):
+    """exp(W x - |x|^2 / 2) / sqrt(m) for x [..., H, D] and W [H, m, D] (float64)."""
+    x = np.asarray(x, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    proj = np.einsum("...hd,hmd->...hm", x, W)
+    return np.exp(proj - 0.5 * np.sum(x * x, axis=-1, keepdims=True)) / np.sqrt(W.shape[-2])
+
+
+def feature_map(feature):
+    """The map x [..., D] -> [..., m] that ``feature`` names (None: elu + 1)."""
+    if feature is None:
+        return phi
+    kind = feature[0]
+    if kind == "relu":
+        return lambda x: relu_features(x, feature[1])
+    if kind == "favor":
+        return lambda x: favor_features(x, feature[1])
+    raise ValueError(f"unknown feature map {kind!r}")
+
+
+def causal_linear_attention(q, k, v, g=None, s0=None, z0=None, eps=EPS, normalize=True, a=None, feature=None):
     """Causal kernelized linear attention, one token at a time.
 
     q, k: [..., N, D]; v: [..., N, Dv]; g: [..., N] or None;
     s0: [..., D, Dv] or None; z0: [..., D] or None (None means zeros).
     normalize: divide by max(phi(q)^T z, eps) (True) or return the numerator.
-    a: [..., N, D] per-dimension decay or None.
+    a: [..., N, m] per-dimension decay or None.
+    feature: None (elu + 1), ("relu", shift) or ("favor", W [H, m, D]); with FAVOR+ the
+    leading dimensions must end in H.
     Leading dimensions (batch, heads) are independent and are vectorised.
     Returns (o [..., N, Dv], S_N [..., D, Dv], z_N [..., D]), all float64.
     """
@@ -82,8 +118,10 @@ def causal_linear_attention(q, k, v, g=None, s0=None, z0=None, eps=EPS, normaliz
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     lead = q.shape[:-2]
-    n, d = q.shape[-2], q.shape[-1]
+    n = q.shape[-2]
     dv = v.shape[-1]
+    fmap = feature_map(feature)
+    d = np.asarray(fmap(q[..., :1, :][..., 0, :])).shape[-1]     # feature width m
     if s0 is None:
         S = np.zeros(lead + (d, dv))
     else:
@@ -98,8 +136,8 @@ def causal_linear_attention(q, k, v, g=None, s0=None, z0=None, eps=EPS, normaliz
         a = np.asarray(a, dtype=np.float64)
     o = np.zeros(lead + (n, dv))
     for t in range(n):
-        fq = phi(q[..., t, :])
-        fk = phi(k[..., t, :])
+        fq = fmap(q[..., t, :])
+        fk = fmap(k[..., t, :])
         if g is not None:
             gt = g[..., t]
             S = gt[..., None, None] * S
@@ -116,7 +154,7 @@ def causal_linear_attention(q, k, v, g=None, s0=None, z0=None, eps=EPS, normaliz
     return o, S, z
 
 
-def decode_step(q, k, v, S, z, g=None, eps=EPS, normalize=True, a=None):
+def decode_step(q, k, v, S, z, g=None, eps=EPS, normalize=True, a=None, feature=None):
     """One recurrent decode step from a stored state.
 
     q, k: [..., D]; v: [..., Dv]; S: [..., D, Dv]; z: [..., D]; g: [...] or None;
@@ -129,5 +167,13 @@ def decode_step(q, k, v, S, z, g=None, eps=EPS, normalize=True, a=None):
     v = np.asarray(v, dtype=np.float64)[..., None, :]
     gg = None if g is None else np.asarray(g, dtype=np.float64)[..., None]
     aa = None if a is None else np.asarray(a, dtype=np.float64)[..., None, :]
-    o, S1, z1 = causal_linear_attention(q, k, v, g=gg, s0=S, z0=z, eps=eps, normalize=normalize, a=aa)
+    if feature is not None and feature[0] == "favor":
+        # one token: the head axis sits in front of the token axis added above
+        q, k, v = (np.swapaxes(x, -2, -3) for x in (q, k, v))
+        o, S1, z1 = causal_linear_attention(q, k, v, g=None if gg is None else np.swapaxes(gg, -1, -2), s0=S,
+                                            z0=z, eps=eps, normalize=normalize,
+                                            a=None if aa is None else np.swapaxes(aa, -2, -3), feature=feature)
+        return np.swapaxes(o, -2, -3)[..., 0, :], S1, z1
+    o, S1, z1 = causal_linear_attention(q, k, v, g=gg, s0=S, z0=z, eps=eps, normalize=normalize, a=aa,
+                                        feature=feature)
     return o[..., 0, :], S1, z1

@@ -379,6 +379,68 @@ def pin_vector_decay(orc):
     np.testing.assert_allclose(zd, z, rtol=1e-13, atol=1e-13)
 
 
+def pin_relu_features(orc):
+    """ReLU plus a shift (anandmoghan-problems page, "Key Functions & Tricks"): the masked
+    pairwise form with torch's relu, both output modes; q = k = 0 makes every weight
+    D shift^2, so the normalised output is the prefix mean of V."""
+    shift = 0.05
+    q, k, v = _rng_inputs(1800, (2,), 9, 4, 3, scale=1.5)
+    fq = torch.relu(torch.as_tensor(q)).numpy() + shift
+    fk = torch.relu(torch.as_tensor(k)).numpy() + shift
+    for normalize in (True, False):
+        o, _, _ = orc.causal_linear_attention(q, k, v, feature=("relu", shift), normalize=normalize)
+        w = np.tril(np.einsum("bid,bjd->bij", fq, fk))
+        want = w @ v
+        if normalize:
+            want = want / np.maximum(w.sum(-1, keepdims=True), 1e-6)
+        np.testing.assert_allclose(o, want, rtol=1e-12, atol=1e-13)
+    zero = np.zeros((2, 9, 4))
+    o, _, _ = orc.causal_linear_attention(zero, zero, v, feature=("relu", shift))
+    np.testing.assert_allclose(o, np.cumsum(v, axis=-2) / np.arange(1, 10)[:, None], rtol=1e-12, atol=1e-13)
+
+
+def pin_favor_features(orc):
+    """FAVOR+ (aicassindra.com page, "Performer"): the features' expected inner product is
+    exp(q . k) over Gaussian projections (Monte Carlo over 4000 draws of 8 features,
+    within 5 standard errors), and with many features the causal attention they give
+    approaches causal softmax attention, o_i = sum_{j<=i} exp(q_i.k_j) v_j / sum exp(q_i.k_j),
+    written out directly."""
+    rng = np.random.default_rng(1900)
+    d = 4
+    q1 = rng.normal(size=(1, 1, d)) * 0.4
+    k1 = rng.normal(size=(1, 1, d)) * 0.4
+    est = []
+    for r in range(4000):
+        W = np.random.default_rng(10_000 + r).normal(size=(1, 8, d))
+        fq, fk = orc.favor_features(q1, W), orc.favor_features(k1, W)
+        est.append(float((fq * fk).sum()))
+    est = np.array(est)
+    target = float(np.exp((q1 * k1).sum()))
+    se = est.std() / np.sqrt(len(est))
+    assert abs(est.mean() - target) < 5 * se, (est.mean(), target, se)
+    n, h = 7, 2
+    q = rng.normal(size=(1, h, n, d)) * 0.3
+    k = rng.normal(size=(1, h, n, d)) * 0.3
+    v = rng.normal(size=(1, h, n, 3))
+    W = np.random.default_rng(1901).normal(size=(h, 20000, d))
+    o, S, z = orc.causal_linear_attention(q, k, v, feature=("favor", W))
+    assert S.shape == (1, h, 20000, 3) and z.shape == (1, h, 20000)
+    sm = np.zeros_like(o)
+    for hh in range(h):
+        for i in range(n):
+            wts = np.exp(np.array([q[0, hh, i] @ k[0, hh, j] for j in range(i + 1)]))
+            sm[0, hh, i] = (wts[:, None] * v[0, hh, : i + 1]).sum(0) / wts.sum()
+    np.testing.assert_allclose(o, sm, atol=0.05)
+    # a decode step with the same features continues a run (favor and relu)
+    W = np.random.default_rng(1902).normal(size=(h, 6, d))
+    for feat in (("favor", W), ("relu", 0.1)):
+        o, S, z = orc.causal_linear_attention(q, k, v, feature=feat)
+        _, S6, z6 = orc.causal_linear_attention(q[..., :6, :], k[..., :6, :], v[..., :6, :], feature=feat)
+        od, Sd, zd = orc.decode_step(q[..., 6, :], k[..., 6, :], v[..., 6, :], S6, z6, feature=feat)
+        np.testing.assert_allclose(od, o[..., 6, :], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(Sd, S, rtol=1e-12, atol=1e-13)
+
+
 ALL_PINS = [
     pin_phi_values,
     pin_hand_example,
@@ -395,4 +457,6 @@ ALL_PINS = [
     pin_decode_composition,
     pin_numerator_mode,
     pin_vector_decay,
+    pin_relu_features,
+    pin_favor_features,
 ]

@@ -25,8 +25,8 @@ MUTATIONS = {
                            "        den = np.einsum(\"...d,...d->...\", fq, z)\n"
                            "        S = S + fk[..., :, None] * v[..., t, None, :]\n        z = z + fk\n"),
     "state_transposed": ("np.einsum(\"...d,...de->...e\", fq, S)", "np.einsum(\"...e,...de->...d\", fq, S)"),
-    "key_query_swapped": ("fq = phi(q[..., t, :])\n        fk = phi(k[..., t, :])",
-                          "fq = phi(k[..., t, :])\n        fk = phi(q[..., t, :])"),
+    "key_query_swapped": ("fq = fmap(q[..., t, :])\n        fk = fmap(k[..., t, :])",
+                          "fq = fmap(k[..., t, :])\n        fk = fmap(q[..., t, :])"),
     "z_not_updated": ("        z = z + fk\n", "        z = z\n"),
     "z_not_gated": ("            z = gt[..., None] * z\n", "            z = z\n"),
     "gate_after_update": ("            S = gt[..., None, None] * S\n", "            S = S\n"),
@@ -37,10 +37,13 @@ MUTATIONS = {
     "gate_index_lag": ("gt = g[..., t]", "gt = g[..., max(t - 1, 0)]"),
     "numerator_mode_still_divides": ("if normalize else num", "if normalize or True else num"),
     "numerator_mode_divides_by_raw_den": ("if normalize else num", "if normalize else num / den[..., None]"),
-    "decode_drops_output_mode": ("normalize=normalize, a=aa)", "a=aa)"),
+    "decode_drops_output_mode": ("eps=eps, normalize=normalize, a=aa,", "eps=eps, a=aa,"),
     "vector_decay_on_value_dim": ("S = at[..., :, None] * S", "S = at[..., :1, None] * S"),
     "vector_decay_skips_z": ("            z = at * z\n", "            z = z\n"),
     "vector_decay_index_lag": ("at = a[..., t, :]", "at = a[..., max(t - 1, 0), :]"),
+    "relu_shift_dropped": ("return np.maximum(x, 0.0) + shift", "return np.maximum(x, 0.0) + 0.0"),
+    "favor_no_norm_term": ("np.exp(proj - 0.5 * np.sum(x * x, axis=-1, keepdims=True))", "np.exp(proj)"),
+    "favor_no_sqrt_m": ("/ np.sqrt(W.shape[-2])", "/ 1.0"),
 }
 
 
