@@ -167,13 +167,6 @@ def decode_step(q, k, v, S, z, g=None, eps=EPS, normalize=True, a=None, feature=
     v = np.asarray(v, dtype=np.float64)[..., None, :]
     gg = None if g is None else np.asarray(g, dtype=np.float64)[..., None]
     aa = None if a is None else np.asarray(a, dtype=np.float64)[..., None, :]
-    if feature is not None and feature[0] == "favor":
-        # one token: the head axis sits in front of the token axis added above
-        q, k, v = (np.swapaxes(x, -2, -3) for x in (q, k, v))
-        o, S1, z1 = causal_linear_attention(q, k, v, g=None if gg is None else np.swapaxes(gg, -1, -2), s0=S,
-                                            z0=z, eps=eps, normalize=normalize,
-                                            a=None if aa is None else np.swapaxes(aa, -2, -3), feature=feature)
-        return np.swapaxes(o, -2, -3)[..., 0, :], S1, z1
     o, S1, z1 = causal_linear_attention(q, k, v, g=gg, s0=S, z0=z, eps=eps, normalize=normalize, a=aa,
                                         feature=feature)
     return o[..., 0, :], S1, z1
