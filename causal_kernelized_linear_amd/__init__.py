@@ -9,7 +9,9 @@ from .binding import (  # noqa: F401
     bwd,
     decode_step,
     fwd,
+    decode_step_features,
     fwd_chunked,
+    fwd_features,
     fwd_vdecay,
     fwd_gated,
     linattn_bwd,
@@ -18,6 +20,8 @@ from .binding import (  # noqa: F401
     linattn_decode_step_ex,
     linattn_fwd_chunked,
     linattn_fwd_ex,
+    linattn_fwd_features,
+    linattn_fwd_features_workspace_size,
     linattn_fwd_vdecay,
     linattn_fwd_vdecay_workspace_size,
     linattn_decode_step_vdecay,

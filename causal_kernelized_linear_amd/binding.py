@@ -10,9 +10,10 @@ Function names match the C ABI (include/linattn.h):
     linattn_fwd_chunked, linattn_fwd_gated, linattn_fwd_ex, linattn_decode_step,
     linattn_decode_step_ex, linattn_fwd_workspace_size, linattn_bwd,
     linattn_bwd_workspace_size, linattn_fwd_vdecay, linattn_fwd_vdecay_workspace_size,
-    linattn_decode_step_vdecay, linattn_status_string
-plus the tensor-level helpers fwd_chunked, fwd_gated, fwd, fwd_vdecay, bwd and
-decode_step.
+    linattn_decode_step_vdecay, linattn_fwd_features, linattn_fwd_features_workspace_size,
+    linattn_status_string
+plus the tensor-level helpers fwd_chunked, fwd_gated, fwd, fwd_vdecay, fwd_features,
+decode_step_features, bwd and decode_step.
 """
 from __future__ import annotations
 
@@ -27,6 +28,7 @@ LIB_PATH = os.path.join(_HERE, "liblinattn.so")
 
 F32, BF16 = 0, 1
 OUT_NORMALIZED, OUT_NUMERATOR = 0, 1
+FEATURE_RELU, FEATURE_FAVOR = 1, 2
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "hip"}
 
 _lock = threading.Lock()
@@ -46,6 +48,9 @@ EXPORTS = {
     "linattn_decode_step_ex": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p]),
     "linattn_bwd_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
     "linattn_fwd_vdecay_workspace_size": (_sz, [_i, _i, _i, _i, _i]),
+    "linattn_fwd_features_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i, _i, _i]),
+    "linattn_fwd_features": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _f, _p, _i,
+                                  _p, _sz, _p]),
     "linattn_fwd_vdecay": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p, _sz, _p]),
     "linattn_decode_step_vdecay": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p]),
     "linattn_bwd": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p, _sz,
@@ -134,6 +139,16 @@ def linattn_fwd_vdecay(q, k, v, a, o, s0, z0, s_out, z_out, B, H, N, D, Dv, dtyp
 
 def linattn_decode_step_vdecay(q, k, v, a, S, z, o, B, H, D, Dv, dtype, eps, out, stream) -> int:
     return int(lib().linattn_decode_step_vdecay(q, k, v, a, S, z, o, B, H, D, Dv, dtype, eps, out, stream))
+
+
+def linattn_fwd_features_workspace_size(B, H, N, D, Dv, chunk, M, dtype) -> int:
+    return int(lib().linattn_fwd_features_workspace_size(B, H, N, D, Dv, chunk, M, dtype))
+
+
+def linattn_fwd_features(q, k, v, g, o, s0, z0, s_out, z_out, B, H, N, D, Dv, chunk, dtype, eps, out, feature, shift,
+                         W, M, ws, ws_bytes, stream) -> int:
+    return int(lib().linattn_fwd_features(q, k, v, g, o, s0, z0, s_out, z_out, B, H, N, D, Dv, chunk, dtype, eps, out,
+                                          feature, shift, W, M, ws, ws_bytes, stream))
 
 
 def linattn_set_profile_events(ev0, ev1, ev2, ev3) -> int:
@@ -275,6 +290,54 @@ def fwd_vdecay(q, k, v, a, eps=1e-6, s0=None, z0=None, return_state=False, out=N
     if return_state:
         return o, s_out, z_out
     return o
+
+
+def fwd_features(q, k, v, feature, shift=0.0, W=None, g=None, chunk=128, eps=1e-6, s0=None, z0=None,
+                 return_state=False, out=None, workspace=None, normalize=True, s_out=None, z_out=None):
+    """Forward under another feature map (linattn_fwd_features): feature "relu" (max(x, 0) +
+    shift) or "favor" (W [H, M, D] float32 random features).  The state has M rows."""
+    dt = _dtype_code(q)
+    dev = q.device
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _need(t, n, q.dtype, dev)
+    for t, n in ((g, "g"), (s0, "s0"), (z0, "z0"), (W, "W"), (s_out, "s_out"), (z_out, "z_out")):
+        _need(t, n, torch.float32, dev)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, D]")
+    B, H, N, D = q.shape
+    Dv = v.shape[-1]
+    kind = {"relu": FEATURE_RELU, "favor": FEATURE_FAVOR}[feature]
+    if kind == FEATURE_FAVOR and (W is None or W.dim() != 3 or W.shape[0] != H or W.shape[2] != D):
+        raise ValueError("favor needs W [H, M, D]")
+    M = W.shape[1] if kind == FEATURE_FAVOR else D
+    o = torch.empty(B, H, N, Dv, dtype=q.dtype, device=dev) if out is None else out
+    if return_state and s_out is None:
+        s_out = torch.empty(B, H, M, Dv, dtype=torch.float32, device=dev)
+        z_out = torch.empty(B, H, M, dtype=torch.float32, device=dev)
+    nbytes = linattn_fwd_features_workspace_size(B, H, N, D, Dv, chunk, M, dt)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError("workspace too small")
+    code = linattn_fwd_features(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(o), _ptr(s0), _ptr(z0), _ptr(s_out),
+                                _ptr(z_out), B, H, N, D, Dv, chunk, dt, eps,
+                                OUT_NORMALIZED if normalize else OUT_NUMERATOR, kind, shift,
+                                _ptr(W) if kind == FEATURE_FAVOR else 0, M, _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(code, "linattn_fwd_features")
+    if return_state:
+        return o, s_out, z_out
+    return o
+
+
+def decode_step_features(q, k, v, S, z, feature, shift=0.0, W=None, g=None, eps=1e-6, normalize=True):
+    """One decode step under another feature map: linattn_fwd_features over one token with
+    the state (S [B,H,M,Dv], z [B,H,M]) as both its initial and its final state, updated
+    in place.  q, k [B,H,D], v [B,H,Dv]; g [B,H] or None.  Returns o [B,H,Dv]."""
+    o = fwd_features(q.unsqueeze(2), k.unsqueeze(2), v.unsqueeze(2), feature, shift=shift, W=W,
+                     g=None if g is None else g.unsqueeze(2).contiguous(), chunk=64, eps=eps, s0=S, z0=z, s_out=S,
+                     z_out=z, normalize=normalize)
+    return o[:, :, 0]
 
 
 def bwd(q, k, v, dout, g=None, s0=None, z0=None, eps=1e-6, normalize=True, state_grads=False, workspace=None,

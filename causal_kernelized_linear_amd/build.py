@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblinattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["api.hip", "fwd_bf16.hip", "fwd_f32.hip", "decode.hip", "bwd_bf16.hip", "bwd_f32.hip", "vdecay.hip"]
+SOURCES = ["api.hip", "fwd_bf16.hip", "fwd_f32.hip", "decode.hip", "bwd_bf16.hip", "bwd_f32.hip", "vdecay.hip", "features.hip"]
 # Packed fp32 VALU instructions stay off: plain float code only.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

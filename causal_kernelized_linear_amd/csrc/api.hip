@@ -309,9 +309,92 @@ linattn_status_t vd_common(const void* q, const void* k, const void* v, const fl
     return e == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP;
 }
 
+size_t feature_bytes(long BH, int N, int M, size_t es) { return linattn::round_up256(size_t(BH) * N * M * es); }
+
+linattn_status_t feat_common(const void* q, const void* k, const void* v, const float* g, void* o, const float* s0,
+                             const float* z0, float* s_out, float* z_out, int B, int H, int N, int D, int Dv,
+                             int chunk, linattn_dtype_t dtype, float eps, linattn_output_t out, int feature,
+                             float shift, const float* W, int M, void* ws, size_t ws_bytes, void* stream) {
+    if (B < 0 || H < 0 || N < 0 || D <= 0 || Dv <= 0 || chunk <= 0 || M <= 0) return LINATTN_ERR_INVALID_ARGUMENT;
+    if (!dtype_ok(dtype) || !out_ok(out) || !(eps > 0.0f) || !std::isfinite(eps) || !std::isfinite(shift))
+        return LINATTN_ERR_INVALID_ARGUMENT;
+    if (feature != LINATTN_FEATURE_RELU && feature != LINATTN_FEATURE_FAVOR) return LINATTN_ERR_INVALID_ARGUMENT;
+    if ((feature == LINATTN_FEATURE_RELU) != (W == nullptr)) return LINATTN_ERR_INVALID_ARGUMENT;
+    if (feature == LINATTN_FEATURE_RELU && M != D) return LINATTN_ERR_INVALID_ARGUMENT;
+    const long BH = long(B) * long(H);
+    if (BH == 0 || N == 0) return LINATTN_OK;
+    if (BH > (1L << 24) || long(N) * BH > (1L << 40)) return LINATTN_ERR_INVALID_ARGUMENT;
+    if (!q || !k || !v || !o) return LINATTN_ERR_INVALID_ARGUMENT;
+    for (const void* p : {q, k, v, static_cast<const void*>(g), static_cast<const void*>(o),
+                          static_cast<const void*>(s0), static_cast<const void*>(z0), static_cast<const void*>(s_out),
+                          static_cast<const void*>(z_out), static_cast<const void*>(W)})
+        if (p && !aligned16(p)) return LINATTN_ERR_INVALID_ARGUMENT;
+    const size_t es = esize(dtype);
+    const size_t nqk = size_t(BH) * N * D * es, nv = size_t(BH) * N * Dv * es, nw = size_t(H) * M * D * 4;
+    const size_t ns = size_t(BH) * M * Dv * 4, nz = size_t(BH) * M * 4;
+    if (overlap(o, nv, q, nqk) || overlap(o, nv, k, nqk) || overlap(o, nv, v, nv) ||
+        overlap(o, nv, g, size_t(BH) * N * 4) || overlap(o, nv, W, nw))
+        return LINATTN_ERR_INVALID_ARGUMENT;
+    if ((size_t(N) + 256) * size_t(Dv > M ? Dv : M) * es >= (size_t(1) << 31)) return LINATTN_ERR_UNSUPPORTED;
+    if (!dim_ok(D) || !dim_ok(Dv) || !dim_ok(M) || (chunk != 64 && chunk != 128) ||
+        linattn::walk_lds_bytes(int(es), M, Dv, chunk, g != nullptr) > linattn::kMaxLds ||
+        (feature == LINATTN_FEATURE_FAVOR && (size_t(64) * (D + 4) + size_t(M) * (D + 4) + 64) * 4 > linattn::kMaxLds))
+        return LINATTN_ERR_UNSUPPORTED;
+    const Plan plan = make_plan(BH, N, M, Dv, chunk, target_workgroups(int(es), M, Dv, chunk, g != nullptr));
+    const size_t fb = feature_bytes(BH, N, M, es);
+    const size_t need = 2 * fb + plan.bytes;
+    if (ws_bytes < need || !ws || !aligned16(ws)) return LINATTN_ERR_WORKSPACE;
+    for (const auto& b : {std::make_pair(static_cast<const void*>(q), nqk), std::make_pair(static_cast<const void*>(k), nqk),
+                          std::make_pair(static_cast<const void*>(v), nv), std::make_pair(static_cast<const void*>(o), nv),
+                          std::make_pair(static_cast<const void*>(g), size_t(BH) * N * 4),
+                          std::make_pair(static_cast<const void*>(W), nw),
+                          std::make_pair(static_cast<const void*>(s0), ns), std::make_pair(static_cast<const void*>(z0), nz),
+                          std::make_pair(static_cast<const void*>(s_out), ns),
+                          std::make_pair(static_cast<const void*>(z_out), nz)})
+        if (overlap(ws, need, b.first, b.second)) return LINATTN_ERR_WORKSPACE;
+    const linattn_status_t dst = check_device();
+    if (dst != LINATTN_OK) return dst;
+    linattn::FeatLaunch L;
+    FwdLaunch& F = L.fwd;
+    F.prof[0] = F.prof[1] = F.prof[2] = F.prof[3] = nullptr;
+    F.q = q; F.k = k; F.v = v; F.g = g; F.o = o;
+    F.s0 = s0; F.z0 = z0; F.s_out = s_out; F.z_out = z_out;
+    F.ws = ws;
+    F.BH = int(BH); F.N = N; F.D = D; F.Dv = Dv; F.chunk = chunk;
+    F.nseg = plan.nseg; F.L = plan.L; F.eps = eps;
+    F.normalize = out == LINATTN_OUT_NORMALIZED ? 1 : 0;
+    F.stream = static_cast<hipStream_t>(stream);
+    L.kind = feature; L.shift = shift; L.W = W; L.H = H; L.M = M; L.es = int(es);
+    L.BH = int(BH); L.N = N; L.D = D; L.stream = F.stream;
+    (void)hipGetLastError();
+    const hipError_t e = linattn::launch_feature_fwd(L);
+    return e == hipSuccess ? LINATTN_OK : LINATTN_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t linattn_fwd_features_workspace_size(int B, int H, int N, int D, int Dv, int chunk, int M,
+                                           linattn_dtype_t dtype) {
+    if (B <= 0 || H <= 0 || N <= 0 || D <= 0 || Dv <= 0 || chunk <= 0 || M <= 0 || !dtype_ok(dtype)) return 0;
+    const long BH = long(B) * long(H);
+    const size_t es = esize(dtype);
+    return 2 * feature_bytes(BH, N, M, es) + make_plan(BH, N, M, Dv, chunk, max_target_workgroups(M, Dv, chunk)).bytes;
+}
+
+linattn_status_t linattn_fwd_features(const void* q, const void* k, const void* v, const float* g, void* o,
+                                      const float* s0, const float* z0, float* s_out, float* z_out, int B, int H,
+                                      int N, int D, int Dv, int chunk, linattn_dtype_t dtype, float eps,
+                                      linattn_output_t out, linattn_feature_t feature, float shift, const float* W,
+                                      int M, void* workspace, size_t workspace_bytes, void* stream) {
+    try {
+        return feat_common(q, k, v, g, o, s0, z0, s_out, z_out, B, H, N, D, Dv, chunk, dtype, eps, out, int(feature),
+                           shift, W, M, workspace, workspace_bytes, stream);
+    } catch (...) {
+        return LINATTN_ERR_HIP;
+    }
+}
 
 size_t linattn_bwd_workspace_size(int B, int H, int N, int D, int Dv, linattn_dtype_t dtype) {
     if (B <= 0 || H <= 0 || N <= 0 || D <= 0 || Dv <= 0 || !dtype_ok(dtype)) return 0;

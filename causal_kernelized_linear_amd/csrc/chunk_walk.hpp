@@ -216,11 +216,18 @@ struct OutRsrc {
 
 // The per-thread machinery of one workgroup walking chunks of one head.
 // OUT: the workgroup forms outputs (row-major Fk, S^T and the split z in LDS).
-template <typename E, int D, int DV, int CH, bool GATED, bool OUT>
+// IDENT: q and k already hold the features (another map applied beforehand), so the
+// walker uses them as they are instead of applying elu + 1.
+template <typename E, int D, int DV, int CH, bool GATED, bool OUT, bool IDENT = false>
 struct ChunkWalker {
     using Sh = WalkShape<E, D, DV, CH, GATED, OUT>;
     using X = Elem<E>;
     static constexpr int LKT = Sh::LKT, LS = Sh::LS;
+
+    static __device__ __forceinline__ float feat(float x) {
+        if constexpr (IDENT) return x;
+        else return phi(x);
+    }
 
     struct Regs {                       // one chunk of K, V (and gates) in flight
         F8<E> rk[Sh::KPT][4];
@@ -373,7 +380,7 @@ struct ChunkWalker {
                 for (int r = 0; r < 4; ++r) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float f = phi(X::to_f32(R.rk[it][r].x[e]));
+                        const float f = feat(X::to_f32(R.rk[it][r].x[e]));
                         fr[r][e] = X::from_f32(TAIL ? (ts + krow_of(kq, r) < N ? f : 0.0f) : f);
                     }
                     if constexpr (Sh::kRowK) {
@@ -421,7 +428,7 @@ struct ChunkWalker {
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) fq[m][ks].x[e] = X::from_f32(phi(X::to_f32(Q.rq[m][ks].x[e])));
+                for (int e = 0; e < 8; ++e) fq[m][ks].x[e] = X::from_f32(feat(X::to_f32(Q.rq[m][ks].x[e])));
     }
 
     // The two zero rows of the split-z operand; written once, before the first barrier.
@@ -778,11 +785,11 @@ struct ChunkWalker {
 // Accumulator-layout element r of state tile j of wave w, lane (l16, g4):
 // S[16a + 4 g4 + r][16b + l16] with a = w ZT + j / NB, b = j % NB; z tile i of wave w
 // holds z[16(w ZT + i) + 4 g4 + r] in its l16 == 0 lanes (zero elsewhere).
-template <typename E, int D, int DV, int CH, bool GATED, bool OUTPUT>
+template <typename E, int D, int DV, int CH, bool GATED, bool OUTPUT, bool IDENT = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     WalkShape<E, D, DV, CH, GATED, OUTPUT>::kWaves, WalkShape<E, D, DV, CH, GATED, OUTPUT>::kWaves))) void walk_kernel(WalkArgs args) {
     using Sh = WalkShape<E, D, DV, CH, GATED, OUTPUT>;
-    using W = ChunkWalker<E, D, DV, CH, GATED, OUTPUT>;
+    using W = ChunkWalker<E, D, DV, CH, GATED, OUTPUT, IDENT>;
     extern __shared__ __align__(16) unsigned char smem[];
 
     const int nsw = OUTPUT ? args.nseg : args.nseg - 1;    // the totals skip the last segment

@@ -175,6 +175,21 @@ struct VdLaunch {
 hipError_t launch_vd_bf16(const VdLaunch& p);
 hipError_t launch_vd_f32(const VdLaunch& p);
 
+// A forward under another feature map: the features of q and k (kind 1: relu + shift,
+// kind 2: FAVOR+ with W [H][M][D]) are written to the head of the workspace, then the
+// walk of `fwd` runs over them with M state rows.
+struct FeatLaunch {
+    FwdLaunch fwd;           // q, k: the inputs; ws: the whole workspace; D: their width
+    int kind;
+    float shift;
+    const float* W;
+    int H, M, es;
+    int BH, N, D;
+    hipStream_t stream;
+};
+
+hipError_t launch_feature_fwd(const FeatLaunch& p);
+
 hipError_t launch_fwd_bf16(const FwdLaunch& p);
 hipError_t launch_fwd_f32(const FwdLaunch& p);
 hipError_t launch_bwd_bf16(const BwdLaunch& p);

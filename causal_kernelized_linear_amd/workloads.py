@@ -59,6 +59,8 @@ WORKLOADS = {
                                   note="one gated recurrent step: the decode form of the gated forward"),
     "vdecay_bf16": Workload("vdecay_bf16", "vdecay", 4, 16, 8192, 64, 64, "bf16", (64,), 1007,
                             note="per-dimension decay per head and token (gated linear attention)"),
+    "favor_bf16": Workload("favor_bf16", "fwd", 8, 16, 4096, 64, 64, "bf16", (128,), 1009, scale=64 ** -0.25,
+                           note="FAVOR+ random features (64 per head) on training-shaped inputs scaled by D^-1/4"),
     "decode_vdecay_bf16": Workload("decode_vdecay_bf16", "decode_vdecay", 256, 32, 1, 128, 128, "bf16", (1,), 1008,
                                    note="one recurrent step under a per-dimension decay"),
 }
@@ -115,6 +117,12 @@ def make_inputs(w: Workload, B=None, H=None, N=None, with_grad=False):
     if with_grad:
         out["dout"] = _randn(gen, (B, H, N, w.Dv)).to(dt)
     return out
+
+
+def favor_projection(seed, H, M, D):
+    """Per-head FAVOR+ projections W [H, M, D]: independent N(0, 1) rows, float32."""
+    gen = torch.Generator(device="cpu").manual_seed(seed)
+    return torch.randn(H, M, D, generator=gen, dtype=torch.float32)
 
 
 def random_inputs(seed, B, H, N, D, Dv, dtype="bf16", scale=1.0, gated=False,

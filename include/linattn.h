@@ -168,6 +168,38 @@ linattn_status_t linattn_decode_step_vdecay(
     int B, int H, int D, int Dv, linattn_dtype_t dtype, float eps, linattn_output_t out, void* stream);
 
 /*
+ * Feature maps other than elu + 1 (the forward of linattn_fwd_ex with phi replaced):
+ *   LINATTN_FEATURE_RELU   phi(x) = max(x, 0) + shift, M = D (the "F.relu(x) + eps"
+ *                          alternative of the anandmoghan-problems page, "Key Functions
+ *                          & Tricks"); W must be NULL
+ *   LINATTN_FEATURE_FAVOR  phi(x)_r = exp(w_r . x - |x|^2 / 2) / sqrt(M) for the M rows of
+ *                          W [H][M][D] float (one set of random features per head, drawn
+ *                          by the caller), Performer's positive random features
+ *                          (aicassindra.com page, "Performer: unbiased softmax by
+ *                          positive random features"); shift is not used
+ * The state then has M rows: s0, s_out [B,H,M,Dv], z0, z_out [B,H,M].  The features are
+ * computed in a pass of their own into the workspace (linattn_fwd_features_workspace_size),
+ * then the chunked walk runs over them.  Supported: D, M, Dv in {64, 128}; chunk 64 or
+ * 128 (where the walk's tiles fit the LDS).  Every other argument is as for linattn_fwd_ex.
+ * A decode step under these maps is this call over one token (N = 1) with s_out = s0 and
+ * z_out = z0: the state is updated in place.
+ */
+typedef enum {
+    LINATTN_FEATURE_RELU = 1,
+    LINATTN_FEATURE_FAVOR = 2
+} linattn_feature_t;
+
+size_t linattn_fwd_features_workspace_size(int B, int H, int N, int D, int Dv, int chunk, int M,
+                                           linattn_dtype_t dtype);
+
+linattn_status_t linattn_fwd_features(
+    const void* q, const void* k, const void* v, const float* g, void* o,
+    const float* s0, const float* z0, float* s_out, float* z_out,
+    int B, int H, int N, int D, int Dv, int chunk, linattn_dtype_t dtype, float eps, linattn_output_t out,
+    linattn_feature_t feature, float shift, const float* W, int M,
+    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of device scratch linattn_bwd needs for these sizes and dtype (the state in
  * front of every 64-token chunk and its adjoint, float, plus per-token intermediates).
  * 0 when B*H*N == 0 or a size is not positive.  Contents are undefined after a call; it
