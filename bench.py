@@ -10,8 +10,8 @@ its inputs warm in the 256 MB Infinity Cache.  The scalar-gated forward
 (B=1, H=32, N=65536, D=Dv=128, chunk sweep), the decode step (B=256, H=32,
 D=Dv=128, fp32 state), its gated form, the normaliser-free output mode of the
 gated forward and of the gated decode, the backward of the training-shaped and
-gated forwards, and the per-dimension decay (forward and decode) are timed in the same
-run and reported in extra fields.
+gated forwards, the per-dimension decay (forward and decode) and the ReLU and FAVOR+
+feature maps are timed in the same run and reported in extra fields.
 
 Prints ONE JSON line.  ms_per_step and value come from a timed pass bracketed by
 two hipEvents only.  Per-kernel durations come from a second timed pass of the same
@@ -316,6 +316,43 @@ def time_vdecay(w, steps, warmup, ev):
     return {"ms_per_step": ms}
 
 
+def time_features(w, feature, steps, warmup, ev, M=64):
+    """Per-step time of linattn_fwd_features on workload w (two input sets rotated)."""
+    import torch
+    from causal_kernelized_linear_amd import binding, workloads
+
+    dev = torch.device("cuda:0")
+    base = workloads.make_inputs(w)
+    sets = [{n: t.to(dev) for n, t in base.items()}]
+    sets.append({n: t.clone() for n, t in sets[0].items()})
+    W = workloads.favor_projection(w.seed, w.H, M, w.D).to(dev) if feature == "favor" else None
+    m = M if feature == "favor" else w.D
+    dt = binding.BF16 if w.dtype == "bf16" else binding.F32
+    ws = torch.empty(binding.linattn_fwd_features_workspace_size(w.B, w.H, w.N, w.D, w.Dv, w.chunks[0], m, dt),
+                     dtype=torch.uint8, device=dev)
+    outs = [torch.empty(w.B, w.H, w.N, w.Dv, dtype=w.torch_dtype, device=dev) for _ in range(2)]
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def call(i):
+        s = sets[i % 2]
+        binding.fwd_features(s["q"], s["k"], s["v"], feature, shift=0.05, W=W, chunk=w.chunks[0], out=outs[i % 2],
+                             workspace=ws)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    t0, t1 = ev.create(2)
+    ev.record(t0, stream)
+    for i in range(steps):
+        call(i)
+    ev.record(t1, stream)
+    torch.cuda.synchronize()
+    ms = ev.ms(t0, t1) / steps
+    del sets, outs, ws
+    torch.cuda.empty_cache()
+    return {"ms_per_step": ms}
+
+
 def decode_bytes(w, with_z=True):
     """S (and z) read and written once, q, k, v read, o written, plus the gate when gated."""
     es = 4 if w.dtype == "f32" else 2
@@ -540,6 +577,18 @@ def main():
             "GBps": decode_bytes(wdv) / sdv / 1e9, "hbm_frac": decode_bytes(wdv) / sdv / 1e9 / HBM_PEAK_GBS,
             "tokens_per_s": wdv.B / sdv, "ms_per_step": rdv["ms_per_step"], "bytes_per_step": decode_bytes(wdv),
         }
+        for key, wname, feat in (("features_relu", "train_bf16", "relu"), ("features_favor", "favor_bf16", "favor")):
+            wf = workloads.WORKLOADS[wname]
+            rf = time_features(wf, feat, extra_steps, extra_warm, ev)
+            sf = rf["ms_per_step"] * 1e-3
+            uf = fwd_units(wf)
+            line[key] = {
+                "workload": f"{wname} forward under " + ("relu(x) + 0.05" if feat == "relu" else
+                                                         "FAVOR+ with 64 random features per head") + ", chunk 128",
+                "tokens_per_s": wf.B * wf.N / sf, "ms_per_step": rf["ms_per_step"],
+                "algorithmic_GBps": fwd_bytes_per_unit(wf) * uf / sf / 1e9,
+                "hbm_frac": fwd_bytes_per_unit(wf) * uf / sf / 1e9 / HBM_PEAK_GBS,
+            }
         wl = workloads.WORKLOADS["longctx_bf16"]
         sweep = {}
         for c in wl.chunks:

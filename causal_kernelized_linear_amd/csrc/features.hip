@@ -55,11 +55,33 @@ __global__ __launch_bounds__(kThreads) void feature_kernel(const E* __restrict__
         float* sW = sX + C * LX;                                 // [M][LX]
         float* sN = sW + M * LX;                                 // [C] |x|^2 / 2
         const float* Wh = W + size_t(bh % H) * M * D;
-        for (int i = tid; i < C * D; i += kThreads) {
-            const int row = i / D, col = i % D;
-            sX[row * LX + col] = row < nrows ? X::to_f32(xb[size_t(ts + row) * D + col]) : 0.0f;
+        // every load first: x in 16-byte units (rows clamped), W in fp32 quads
+        constexpr int EPG = 16 / int(sizeof(E)), G = D / EPG, UX = C * G / kThreads, UW = M * D / 4 / kThreads;
+        f32x4_t rx[UX], rw[UW];
+#pragma unroll
+        for (int u = 0; u < UX; ++u) {
+            const int idx = tid + u * kThreads, row = idx / G, col = (idx % G) * EPG;
+            rx[u] = *reinterpret_cast<const f32x4_t*>(xb + size_t(ts + min(row, nrows - 1)) * D + col);
         }
-        for (int i = tid; i < M * D; i += kThreads) sW[(i / D) * LX + i % D] = Wh[i];
+#pragma unroll
+        for (int u = 0; u < UW; ++u) rw[u] = *reinterpret_cast<const f32x4_t*>(Wh + 4 * (tid + u * kThreads));
+#pragma unroll
+        for (int u = 0; u < UX; ++u) {
+            const int idx = tid + u * kThreads, row = idx / G, col = (idx % G) * EPG;
+            if constexpr (sizeof(E) == 2) {
+                const F8<E> in = __builtin_bit_cast(F8<E>, rx[u]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) sX[row * LX + col + e] = row < nrows ? X::to_f32(in.x[e]) : 0.0f;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sX[row * LX + col + e] = row < nrows ? rx[u][e] : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UW; ++u) {
+            const int i = 4 * (tid + u * kThreads);
+            *reinterpret_cast<f32x4_t*>(sW + (i / D) * LX + i % D) = rw[u];
+        }
         __syncthreads();
         if (tid < C) {
             float s = 0.0f;
