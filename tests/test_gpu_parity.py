@@ -287,3 +287,23 @@ def test_workload_decode_sampled_heads():
     assert rowwise_rel_err(sel(o, heads)[0], o_ref) <= TOL["bf16"]
     assert matrix_rel_err(sel(S, heads), S_ref[None]) <= 1e-6
     assert matrix_rel_err(sel(z, heads), z_ref[None]) <= 1e-6
+
+
+# ------------------------------------------------ many heads, few segments ----
+
+@pytest.mark.parametrize("gated", [False, True], ids=["ungated", "gated"])
+@pytest.mark.parametrize("shape", [(8, 16, 1024, 64, 64, 64), (8, 16, 1000, 64, 64, 64), (4, 32, 2048, 128, 128, 64)],
+                         ids=["direct64", "direct64ragged", "scanned128"])
+def test_many_heads_few_segments(shape, gated):
+    # many heads and segments of several chunks each: the prefix in front of a segment
+    # sums a few totals (the direct prefix at D = Dv = 64, the scan at 128)
+    B, H, N, D, Dv, chunk = shape
+    inp = workloads.random_inputs(37 + N, B, H, N, D, Dv, dtype="bf16", gated=gated, g_low=0.9, with_state=True,
+                                  state_scale=5.0)
+    heads = _heads(B, H, 4, N)
+    _say(f"totals in parts {shape} gated={gated}, oracle on heads {heads}")
+    o, S, z = run_fwd(inp, chunk, s0=inp["s0"], z0=inp["z0"], return_state=True)
+    o_ref, S_ref, z_ref = oracle_fwd(inp, heads=heads, s0=inp["s0"], z0=inp["z0"])
+    assert rowwise_rel_err(sel(o, heads), o_ref) <= TOL["bf16"]
+    assert matrix_rel_err(sel(S, heads), S_ref) <= TOL["bf16"]
+    assert matrix_rel_err(sel(z, heads), z_ref) <= TOL["bf16"]
