@@ -117,18 +117,18 @@ linattn_status_t check_device() {
         return LINATTN_ERR_HIP;
     }
     static std::mutex mu;
-    static signed char verdict[256];   // 0 unknown, 1 usable, -1 not usable
+    static signed char usable[256];    // 0 unknown, 1 usable, -1 not usable
     if (dev >= 256) return LINATTN_ERR_HIP;
     std::lock_guard<std::mutex> lock(mu);
-    if (verdict[dev] == 0) {
+    if (usable[dev] == 0) {
         hipDeviceProp_t prop;
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
             (void)hipGetLastError();
             return LINATTN_ERR_HIP;
         }
-        verdict[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+        usable[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
     }
-    return verdict[dev] == 1 ? LINATTN_OK : LINATTN_ERR_HIP;
+    return usable[dev] == 1 ? LINATTN_OK : LINATTN_ERR_HIP;
 }
 
 linattn_status_t fwd_common(const void* q, const void* k, const void* v, const float* g, void* o, const float* s0,
