@@ -53,8 +53,8 @@ EXPORTS = {
                                   _p, _sz, _p]),
     "linattn_fwd_vdecay": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p, _sz, _p]),
     "linattn_decode_step_vdecay": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p]),
-    "linattn_bwd": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _p, _sz,
-                         _p]),
+    "linattn_bwd": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _f, _i, _i, _p,
+                         _sz, _p]),
     "linattn_status_string": (ctypes.c_char_p, [_i]),
     "linattn_set_profile_events": (_i, [_p, _p, _p, _p]),
 }
@@ -121,10 +121,10 @@ def linattn_bwd_workspace_size(B, H, N, D, Dv, dtype) -> int:
     return int(lib().linattn_bwd_workspace_size(B, H, N, D, Dv, dtype))
 
 
-def linattn_bwd(q, k, v, g, dout, s0, z0, dq, dk, dv, dg, ds0, dz0, B, H, N, D, Dv, dtype, eps, out, ws, ws_bytes,
-                stream) -> int:
+def linattn_bwd(q, k, v, g, dout, s0, z0, dq, dk, dv, dg, ds0, dz0, B, H, N, D, Dv, dtype, eps, out, run, ws,
+                ws_bytes, stream) -> int:
     return int(lib().linattn_bwd(q, k, v, g, dout, s0, z0, dq, dk, dv, dg, ds0, dz0, B, H, N, D, Dv, dtype, eps, out,
-                                 ws, ws_bytes, stream))
+                                 run, ws, ws_bytes, stream))
 
 
 def linattn_fwd_vdecay_workspace_size(B, H, N, D, Dv) -> int:
@@ -341,10 +341,11 @@ def decode_step_features(q, k, v, S, z, feature, shift=0.0, W=None, g=None, eps=
 
 
 def bwd(q, k, v, dout, g=None, s0=None, z0=None, eps=1e-6, normalize=True, state_grads=False, workspace=None,
-        grads=None):
+        grads=None, run=0):
     """Gradients of sum(dout * o) for o = fwd(q, k, v, g, s0=s0, z0=z0, eps=eps, normalize=normalize).
     Returns a dict with dq, dk, dv, dg (None when ungated) and, with ``state_grads``, ds0
-    and dz0.  ``grads`` may hold preallocated dq, dk, dv, dg tensors."""
+    and dz0.  ``grads`` may hold preallocated dq, dk, dv, dg tensors; ``run`` is the
+    chunks per run (0: the library's choice)."""
     dt = _dtype_code(q)
     dev = q.device
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
@@ -377,7 +378,7 @@ def bwd(q, k, v, dout, g=None, s0=None, z0=None, eps=1e-6, normalize=True, state
         raise ValueError("workspace too small")
     code = linattn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(dout), _ptr(s0), _ptr(z0), _ptr(dq), _ptr(dk), _ptr(dv),
                        _ptr(dg), _ptr(ds0), _ptr(dz0), B, H, N, D, Dv, dt, eps,
-                       OUT_NORMALIZED if normalize else OUT_NUMERATOR, _ptr(workspace),
+                       OUT_NORMALIZED if normalize else OUT_NUMERATOR, int(run), _ptr(workspace),
                        workspace.numel() * workspace.element_size(), _stream(dev))
     _check(code, "linattn_bwd")
     return {"dq": dq, "dk": dk, "dv": dv, "dg": dg, "ds0": ds0, "dz0": dz0}

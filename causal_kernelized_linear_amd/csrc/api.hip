@@ -214,8 +214,8 @@ linattn_status_t decode_common(const void* q, const void* k, const void* v, cons
 linattn_status_t bwd_common(const void* q, const void* k, const void* v, const float* g, const void* dout,
                             const float* s0, const float* z0, void* dq, void* dk, void* dv, float* dg, float* ds0,
                             float* dz0, int B, int H, int N, int D, int Dv, linattn_dtype_t dtype, float eps,
-                            linattn_output_t out, void* ws, size_t ws_bytes, void* stream) {
-    if (B < 0 || H < 0 || N < 0 || D <= 0 || Dv <= 0) return LINATTN_ERR_INVALID_ARGUMENT;
+                            linattn_output_t out, int run, void* ws, size_t ws_bytes, void* stream) {
+    if (B < 0 || H < 0 || N < 0 || D <= 0 || Dv <= 0 || run < 0) return LINATTN_ERR_INVALID_ARGUMENT;
     if (!dtype_ok(dtype) || !out_ok(out) || !(eps > 0.0f) || !std::isfinite(eps)) return LINATTN_ERR_INVALID_ARGUMENT;
     const long BH = long(B) * long(H);
     if (BH == 0 || N == 0) return LINATTN_OK;
@@ -257,6 +257,8 @@ linattn_status_t bwd_common(const void* q, const void* k, const void* v, const f
     L.BH = int(BH); L.N = N; L.D = D; L.Dv = Dv;
     L.eps = eps;
     L.normalize = out == LINATTN_OUT_NORMALIZED ? 1 : 0;
+    L.cus = device_cus();
+    L.run = run;
     L.stream = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     const hipError_t e = dtype == LINATTN_BF16 ? linattn::launch_bwd_bf16(L) : linattn::launch_bwd_f32(L);
@@ -404,9 +406,9 @@ size_t linattn_bwd_workspace_size(int B, int H, int N, int D, int Dv, linattn_dt
 linattn_status_t linattn_bwd(const void* q, const void* k, const void* v, const float* g, const void* dout,
                              const float* s0, const float* z0, void* dq, void* dk, void* dv, float* dg, float* ds0,
                              float* dz0, int B, int H, int N, int D, int Dv, linattn_dtype_t dtype, float eps,
-                             linattn_output_t out, void* workspace, size_t workspace_bytes, void* stream) {
+                             linattn_output_t out, int run, void* workspace, size_t workspace_bytes, void* stream) {
     try {
-        return bwd_common(q, k, v, g, dout, s0, z0, dq, dk, dv, dg, ds0, dz0, B, H, N, D, Dv, dtype, eps, out,
+        return bwd_common(q, k, v, g, dout, s0, z0, dq, dk, dv, dg, ds0, dz0, B, H, N, D, Dv, dtype, eps, out, run,
                           workspace, workspace_bytes, stream);
     } catch (...) {
         return LINATTN_ERR_HIP;

@@ -18,16 +18,20 @@
 // the last because log g_l enters exactly the weights w_ij of the pairs it separates
 // (the initial state counting as a key in front of token 0).
 //
-// Work per chunk of C = 64 tokens (one workgroup of four waves, wave w owning rows
-// 16w .. 16w + 15 of the chunk), with chunk-local Lambda_i = sum_{l=s..i} log2 g_l:
-//   bwd_dq_kernel   recomputes A = (Fq Fk^T) o decay o mask, num and den from the
-//                   state in front of the chunk, forms 1/d and dden, then
-//                   dFq = B Fk + 2^Lambda_i (dNum S_prev^T + dden z_prev^T) with
-//                   B = (dNum V^T + dden 1^T) o decay o mask, and folds the chunk's
-//                   adjoint total dR_c = Fq^T (2^Lambda dNum), dr_c = Fq^T (2^Lambda dden).
-//   bwd_dkv_kernel  with R, r the adjoint of the state at the chunk's end:
-//                   dFk = B^T Fq + 2^(Lambda_last - Lambda_j) (V R^T + 1 r^T),
-//                   dV  = A^T dNum + 2^(Lambda_last - Lambda_j) Fk R.
+// Work per chunk of C = 64 tokens (four waves, wave w owning rows 16w .. 16w + 15 of the
+// chunk), with chunk-local Lambda_i = sum_{l=s..i} log2 g_l.  A workgroup walks a run of
+// LC chunks and carries the states through it in fp32 registers, so the state slots in
+// memory are per run, not per chunk:
+//   bwd_dq_kernel   (run walked forwards, the state S_prev in front of the chunk carried)
+//                   recomputes A = (Fq Fk^T) o decay o mask, num and den, forms 1/d and
+//                   dden, then dFq = B Fk + 2^Lambda_i (dNum S_prev^T + dden z_prev^T)
+//                   with B = (dNum V^T + dden 1^T) o decay o mask; folds the chunk's
+//                   adjoint total dR_c = Fq^T (2^Lambda dNum), dr_c = Fq^T (2^Lambda dden)
+//                   into the run's, and steps the state across the chunk.
+//   bwd_dkv_kernel  (run walked backwards, the adjoint R, r of the state after the chunk
+//                   carried): dFk = B^T Fq + 2^(Lambda_last - Lambda_j) (V R^T + 1 r^T),
+//                   dV = A^T dNum + 2^(Lambda_last - Lambda_j) Fk R, then
+//                   R <- 2^Lambda_last R + dR_c.
 // dNum never enters a product rounded: the products take the exact input dout and
 // scale by 1/d in fp32 (dNum V^T = diag(1/d) dOut V^T).  With the normaliser, dFq_i is
 // orthogonal to Fq_i (its terms cancel), and a rounded dnum breaks that cancellation
@@ -37,13 +41,18 @@
 //                   in the dq pass), keys in front of it against its queries i >= l
 //                   (Y_l, the running sum of Fq_i . dFq_i's carried-state part), its keys
 //                   j < l against later queries (Z_l, of Fk_j . dFk_j's carried-state
-//                   part) and keys in front against later queries (W_c =
-//                   2^Lambda_last (<R, S_prev> + <r, z_prev>)).  A running sum over the
-//                   whole sequence would cancel to the initial state's term and collect
-//                   the rounding of every token on the way.
-// The states in front of every chunk come from the forward's totals walk (one chunk
-// per segment) and its scan; the adjoint states from the same scan run over the
-// chunks' adjoint totals in reverse order.  Every MFMA operand is staged in LDS as a
+//                   part) and keys in front against later queries (W_c).  With T_b the
+//                   pairs across the boundary b between chunks (keys before, queries
+//                   after; T = <R, S> + <r, z> of the state there and its adjoint),
+//                   W_c = T_end(c) - K_c and T_end(c-1) = W_c + Y_c, with Y_c, K_c the
+//                   chunk's sums of the yq and zk terms: the dk/dv pass forms T at the
+//                   run's end from the two fp32 states and steps it back chunk by chunk.
+//                   A running sum over the whole sequence would cancel to the initial
+//                   state's term and collect the rounding of every token on the way; over
+//                   one run it collects that of at most LC chunks.
+// The states in front of every run come from the forward's totals walk (one run per
+// segment) and its scan; the adjoint states from the same scan run over the runs'
+// adjoint totals in reverse order.  Every MFMA operand is staged in LDS as a
 // row-major tile; an operand whose contraction index runs down the tile's rows is
 // read with ds_read_b64_tr_b16 (bf16) or element by element (fp32).
 #pragma once
@@ -64,13 +73,13 @@ struct BwdArgs {
     void* dq;
     void* dk;
     void* dv;
-    float* fst;          // [BH][NC][D*Dv] accumulator layout: slot c < NC-1 holds the state after chunk c
-    float* fzt;          // [BH][NC][D]
-    float* rst;          // [BH][NC+1][D*Dv]: chunk c's adjoint total at slot NC-1-c; after the
-                         // scan slot NC-2-c holds the adjoint of the state after chunk c, and
-                         // slot NC-1 the gradient of S0
-    float* rzt;          // [BH][NC+1][D], alike
-    float* rlg;          // [BH][NC+1] log2 of each chunk's total decay, reversed like rst
+    float* fst;          // [BH][NR][D*Dv] accumulator layout: slot r < NR-1 holds the state after run r
+    float* fzt;          // [BH][NR][D]
+    float* rst;          // [BH][NR+1][D*Dv]: run r's adjoint total at slot NR-1-r; after the
+                         // scan slot NR-2-r holds the adjoint of the state after run r, and
+                         // slot NR-1 the gradient of S0
+    float* rzt;          // [BH][NR+1][D], alike
+    float* rlg;          // [BH][NR+1] log2 of each run's total decay, reversed like rst
     float* inv;          // [BH][N]: 1 / max(den, eps) of every token (1 without the normaliser)
     float* dden;         // [BH][N]
     float* xs;           // [BH][N]: X_l, the pairs inside the chunk that straddle l
@@ -78,7 +87,9 @@ struct BwdArgs {
     float* zk;           // [BH][N]: Fk_j . (carried-state part of dFk_j)
     float* wc;           // [BH][NC]: W_c
     int N;
-    int NC;
+    int NC;              // chunks of C tokens
+    int LC;              // chunks per run: one workgroup walks a run, carrying the states through it
+    int NR;              // runs, ceil(NC / LC)
     float eps;
     int normalize;
 };
@@ -109,6 +120,13 @@ struct BwdShape {
     // workgroups (so waves per SIMD) the LDS allows: the register target of both kernels,
     // so the compiler does not squeeze the accumulators for an occupancy out of reach
     static constexpr int kWaves = int(kMaxLds / kBytes) < 1 ? 1 : int(kMaxLds / kBytes);
+    // 16-byte pieces per thread of a state in accumulator layout, and of one chunk's four
+    // row tiles.  Loading the next chunk's rows during this chunk's products keeps them
+    // live across the products, beside the two carried states: done where all of it stays
+    // within 32 pieces (128 registers), else the rows are loaded chunk by chunk.
+    static constexpr int kStateUnits = D * DV / 4 / kThreads;
+    static constexpr int kRowPieces = (2 * C * D + 2 * C * DV) * int(sizeof(E)) / 16 / kThreads;
+    static constexpr bool kAhead = kRowPieces + 2 * kStateUnits <= 32;
 };
 
 // Operand of 16 rows from a row-major tile: lane supplies row `row`, contraction
@@ -151,8 +169,10 @@ __device__ __forceinline__ float sum16(float x) {
     return x;
 }
 
-// elu + 1 and its derivative at x (1 above zero, exp(x) at or below).
-__device__ __forceinline__ float dphi(float x) { return x > 0.0f ? 1.0f : __builtin_amdgcn_exp2f(x * kLog2e); }
+// The derivative of elu + 1 from its value: phi'(x) = 1 above zero, where phi(x) = x + 1 > 1,
+// and exp(x) = phi(x) at or below zero, so phi'(x) = min(phi(x), 1).  Taken from the staged
+// features (in the input precision), it adds one rounding of the size of the output's own.
+__device__ __forceinline__ float dphi_of(float f) { return fminf(f, 1.0f); }
 
 // The per-workgroup machinery shared by both gradient kernels.
 template <typename E, int D, int DV, bool GATED>
@@ -177,9 +197,9 @@ struct BwdChunk {
     float* sRow;
     float* sZ;
     int tid, w, lane, l16, g4;
-    int bh, c, ts, nrows, N, NC;
+    int bh, c, ts, nrows, N, NC, run, c_first, c_end;
 
-    __device__ __forceinline__ void init(unsigned char* smem, int N_, int NC_) {
+    __device__ __forceinline__ void init(unsigned char* smem, int N_, int NC_, int LC) {
         sQ = reinterpret_cast<E*>(smem + Sh::kOffQ);
         sK = reinterpret_cast<E*>(smem + Sh::kOffK);
         sV = reinterpret_cast<E*>(smem + Sh::kOffV);
@@ -199,8 +219,21 @@ struct BwdChunk {
         g4 = lane >> 4;
         N = N_;
         NC = NC_;
-        c = blockIdx.x % NC;
-        bh = blockIdx.x / NC;
+        const int ngrp = (NC + LC - 1) / LC;
+        bh = blockIdx.x / ngrp;
+        run = blockIdx.x % ngrp;
+        c_first = run * LC;
+        c_end = min(NC, c_first + LC);
+        set_chunk(c_first);
+    }
+
+    // The lane indices made opaque at the top of every chunk: the compiler then rebuilds
+    // the many LDS addresses derived from them inside the chunk loop instead of hoisting
+    // them all out of it and holding them in registers across the products.
+    __device__ __forceinline__ void refresh() { asm volatile("" : "+v"(tid), "+v"(lane), "+v"(l16), "+v"(g4)); }
+
+    __device__ __forceinline__ void set_chunk(int c_) {
+        c = c_;
         ts = c * C;
         nrows = min(C, N - ts);
     }
@@ -215,12 +248,12 @@ struct BwdChunk {
     static constexpr int kRowUnits = C * W * int(sizeof(E)) / 16 / kThreads;
 
     template <int W>
-    __device__ __forceinline__ void load_rows(f32x4_t (&r)[kRowUnits<W>], const E* src) const {
+    __device__ __forceinline__ void load_rows(f32x4_t (&r)[kRowUnits<W>], const E* src, int ts_, int nrows_) const {
         constexpr int G = W * int(sizeof(E)) / 16;
 #pragma unroll
         for (int u = 0; u < kRowUnits<W>; ++u) {
             const int idx = tid + u * kThreads, row = idx / G, col = (idx % G) * EPG;
-            r[u] = *reinterpret_cast<const f32x4_t*>(src + size_t(ts + min(row, nrows - 1)) * W + col);
+            r[u] = *reinterpret_cast<const f32x4_t*>(src + size_t(ts_ + min(row, nrows_ - 1)) * W + col);
         }
     }
 
@@ -263,7 +296,7 @@ struct BwdChunk {
     }
 
     // A state slot in accumulator layout: D * Dv / 4 16-byte pieces per workgroup.
-    static constexpr int kStateUnits = D * DV / 4 / kThreads;
+    static constexpr int kStateUnits = Sh::kStateUnits;
 
     __device__ __forceinline__ void load_slot(f32x4_t (&r)[kStateUnits], const float* slot) const {
 #pragma unroll
@@ -283,27 +316,48 @@ struct BwdChunk {
         }
     }
 
-    // A [D][Dv] state into sS (row-major, operand precision) and its z part into sZ, from
-    // the caller's layout or zero (the workspace slots go through load_slot/store_slot).
-    __device__ __forceinline__ void stage_state(const float* slot_s, const float* slot_z, const float* user_s,
-                                                const float* user_z) const {
-        (void)slot_s;
-        for (int q4 = tid; q4 < D * DV / 4; q4 += kThreads) {
-            const int d = q4 / (DV / 4), e = 4 * (q4 % (DV / 4));
-            f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-            if (user_s) v = *reinterpret_cast<const f32x4_t*>(user_s + size_t(d) * DV + e);
+    // A caller-layout [D][Dv] state (or zero) into this thread's accumulator-layout pieces.
+    __device__ __forceinline__ void load_user(f32x4_t (&r)[kStateUnits], const float* S) const {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sS[d * LV + e + r] = X::from_f32(v[r]);
+        for (int u = 0; u < kStateUnits; ++u) {
+            const int q4 = tid + u * kThreads;
+            const int t = q4 / kWave, ln = q4 % kWave;
+            const int a = t / (DV / 16), b = t % (DV / 16);
+            const int d = 16 * a + 4 * (ln >> 4), e = 16 * b + (ln & 15);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) r[u][k] = S ? S[size_t(d + k) * DV + e] : 0.0f;
         }
-        for (int d = tid; d < D; d += kThreads) sZ[d] = slot_z ? slot_z[d] : (user_z ? user_z[d] : 0.0f);
     }
 
-    // Chunk-local inclusive log2 cumulative decay into sLam (wave 0); rows past the end
-    // get a unit gate.  Returns nothing; sLam[C - 1] is the chunk's total.
-    __device__ __forceinline__ void stage_lambda(const float* gb) const {
+    // Accumulator-layout pieces out to a workspace slot.
+    __device__ __forceinline__ void put_slot(float* slot, const f32x4_t (&r)[kStateUnits]) const {
+#pragma unroll
+        for (int u = 0; u < kStateUnits; ++u) *reinterpret_cast<f32x4_t*>(slot + 4 * (tid + u * kThreads)) = r[u];
+    }
+
+    // One 16x16 state tile, contraction over the chunk's rows: lhs^T rhs for the tile's
+    // rows a and columns b of two row-major tiles (this lane's accumulator piece).
+    __device__ __forceinline__ f32x4_t tile_tn(const E* lhs, int ldl, int a, const E* rhs, int ldr, int b) const {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < C / 32; ++ks)
+            acc = mma(frag_col(lhs, ldl, 32 * ks + 8 * g4, 16 * a, l16), frag_col(rhs, ldr, 32 * ks + 8 * g4, 16 * b, l16),
+                      acc);
+        return acc;
+    }
+
+    // The gate of row `lane` of the chunk starting at ts_ (rows clamped), for stage_lambda.
+    __device__ __forceinline__ float load_gate(const float* gb, int ts_, int nrows_) const {
+        if constexpr (GATED) return gb[ts_ + min(lane, nrows_ - 1)];
+        return 1.0f;
+    }
+
+    // Chunk-local inclusive log2 cumulative decay into sLam (wave 0) from this lane's
+    // gate; rows past the end get a unit gate.  sLam[C - 1] is the chunk's total.
+    __device__ __forceinline__ void stage_lambda(float gv) const {
         if constexpr (GATED) {
             if (w == 0) {
-                float x = lane < nrows ? fast_log2(gb[ts + lane]) : 0.0f;
+                float x = lane < nrows ? fast_log2(gv) : 0.0f;
 #pragma unroll
                 for (int off = 1; off < kWave; off <<= 1) {
                     const float y = __shfl_up(x, off, kWave);
@@ -332,45 +386,65 @@ void bwd_dq_kernel(BwdArgs args) {
     constexpr int ND = D / 16, NE = DV / 16, NJ = C / 16;
     extern __shared__ __align__(16) unsigned char smem[];
     B ck;
-    ck.init(smem, args.N, args.NC);
-    const int w = ck.w, lane = ck.lane, l16 = ck.l16, g4 = ck.g4, bh = ck.bh, c = ck.c, ts = ck.ts;
+    ck.init(smem, args.N, args.NC, args.LC);
+    const int w = ck.w, bh = ck.bh;
     const int N = args.N, NC = args.NC;
     const E* qb = reinterpret_cast<const E*>(args.q) + size_t(bh) * N * D;
     const E* kb = reinterpret_cast<const E*>(args.k) + size_t(bh) * N * D;
     const E* vb = reinterpret_cast<const E*>(args.v) + size_t(bh) * N * DV;
     const E* dob = reinterpret_cast<const E*>(args.dout) + size_t(bh) * N * DV;
 
-    {
-        f32x4_t rq[B::template kRowUnits<D>], rk[B::template kRowUnits<D>];
-        f32x4_t rv[B::template kRowUnits<DV>], ro[B::template kRowUnits<DV>];
-        f32x4_t rs[B::kStateUnits];
-        const size_t fslot = size_t(bh) * NC + (c - 1);
-        ck.template load_rows<D>(rq, qb);
-        ck.template load_rows<D>(rk, kb);
-        ck.template load_rows<DV>(rv, vb);
-        ck.template load_rows<DV>(ro, dob);
-        if (c > 0) ck.load_slot(rs, args.fst + fslot * (D * DV));
-        ck.template store_rows<D, true>(ck.sQ, LQ, rq);
-        ck.template store_rows<D, true>(ck.sK, LQ, rk);
-        ck.template store_rows<DV, false>(ck.sV, LV, rv);
-        ck.template store_rows<DV, false>(ck.sDn, LV, ro);
-        if (c > 0) {
-            ck.store_slot(rs);
-            for (int d = ck.tid; d < D; d += kThreads) ck.sZ[d] = args.fzt[fslot * D + d];
-        } else {
-            ck.stage_state(nullptr, nullptr, args.s0 ? args.s0 + size_t(bh) * D * DV : nullptr,
-                           args.z0 ? args.z0 + size_t(bh) * D : nullptr);
-        }
+    // The state in front of the current chunk, carried through the run in fp32 (this
+    // thread's accumulator-layout pieces, z_prev[tid] for tid < D): from the scanned slot
+    // in front of the run, or S0 / z0 for the first run.
+    f32x4_t sacc[B::kStateUnits];
+    float zacc = 0.0f;
+    if (ck.run > 0) {
+        const size_t fslot = size_t(bh) * args.NR + (ck.run - 1);
+        ck.load_slot(sacc, args.fst + fslot * (D * DV));
+        if (ck.tid < D) zacc = args.fzt[fslot * D + ck.tid];
+    } else {
+        ck.load_user(sacc, args.s0 ? args.s0 + size_t(bh) * D * DV : nullptr);
+        if (ck.tid < D && args.z0) zacc = args.z0[size_t(bh) * D + ck.tid];
     }
-    ck.stage_lambda(GATED ? args.g + size_t(bh) * N : nullptr);
+    // The run's adjoint total (what its queries pass to the state in front of it): the sum
+    // over its chunks of the chunk's adjoint total times the decay from the run's start to
+    // the chunk's start, 2^logp.
+    f32x4_t racc[B::kStateUnits];
+#pragma unroll
+    for (int u = 0; u < B::kStateUnits; ++u) racc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float rzacc = 0.0f, logp = 0.0f;
+
+    // staging registers, loaded one chunk ahead of the products
+    f32x4_t sq[B::template kRowUnits<D>], sk[B::template kRowUnits<D>];
+    f32x4_t sv[B::template kRowUnits<DV>], so[B::template kRowUnits<DV>];
+    float sg = 1.0f;
+    auto issue = [&](int cn) {
+        const int tn = cn * C, nn = min(C, N - tn);
+        ck.template load_rows<D>(sq, qb, tn, nn);
+        ck.template load_rows<D>(sk, kb, tn, nn);
+        ck.template load_rows<DV>(sv, vb, tn, nn);
+        ck.template load_rows<DV>(so, dob, tn, nn);
+        if constexpr (GATED) sg = ck.load_gate(args.g + size_t(bh) * N, tn, nn);
+    };
+    if constexpr (B::Sh::kAhead) issue(ck.c_first);
+    for (int c = ck.c_first; c < ck.c_end; ++c) {
+    ck.refresh();
+    const int lane = ck.lane, l16 = ck.l16, g4 = ck.g4;
+    ck.set_chunk(c);
+    const int ts = ck.ts;
+    if constexpr (!B::Sh::kAhead) issue(c);
+    ck.template store_rows<D, true>(ck.sQ, LQ, sq);
+    ck.template store_rows<D, true>(ck.sK, LQ, sk);
+    ck.template store_rows<DV, false>(ck.sV, LV, sv);
+    ck.template store_rows<DV, false>(ck.sDn, LV, so);
+    ck.store_slot(sacc);
+    if (ck.tid < D) ck.sZ[ck.tid] = zacc;
+    ck.stage_lambda(sg);
     __syncthreads();
+    if (B::Sh::kAhead && c + 1 < ck.c_end) issue(c + 1);
 
     const int i0 = 16 * w;            // this wave's query rows
-    E xq[ND][4];                      // raw q of this lane's outputs, for phi'(q) at the end (rows clamped)
-#pragma unroll
-    for (int dt = 0; dt < ND; ++dt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) xq[dt][r] = qb[size_t(min(ts + i0 + 4 * g4 + r, N - 1)) * D + 16 * dt + l16];
     float lam_r[4], rs[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) lam_r[r] = ck.lam(i0 + 4 * g4 + r);
@@ -566,53 +640,73 @@ void bwd_dq_kernel(BwdArgs args) {
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dfq[dt][r] *= dphi(X::to_f32(xq[dt][r]));
+        for (int r = 0; r < 4; ++r) dfq[dt][r] *= dphi_of(X::to_f32(ck.sQ[(i0 + 4 * g4 + r) * LQ + 16 * dt + l16]));
 
-    // the chunk's adjoint total: dR_c = Fq^T (2^Lambda dNum), dr_c = Fq^T (2^Lambda dden);
-    // this wave's rows of dOut become 2^Lambda_i dnum_i (every other read of them is done)
+    // this wave's rows of dOut become 2^Lambda_i dnum_i and its rows of V become
+    // 2^(Lambda_last - Lambda_j) v_j (every other read of both is done)
+    const float lam_last = ck.lam(C - 1);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int i = i0 + 4 * g4 + r;
         const float f = GATED ? fast_exp2(lam_r[r]) : 1.0f;
+        const float fv = GATED ? fast_exp2(fminf(lam_last - lam_r[r], 0.0f)) : 1.0f;
 #pragma unroll
         for (int et = 0; et < NE; ++et) {
             E& x = ck.sDn[i * LV + 16 * et + l16];
             x = X::from_f32(X::to_f32(x) * (f * inv[r]));
+            if constexpr (GATED) {
+                E& y = ck.sV[i * LV + 16 * et + l16];
+                y = X::from_f32(X::to_f32(y) * fv);
+            }
         }
         if (l16 == 0) ck.sDd[i] = dd[r] * f;
     }
     __syncthreads();
-    // phi(K) is no longer read: it takes dq for the coalesced store at the end
+    // The chunk's adjoint total dR_c = Fq^T (2^Lambda dNum), dr_c = Fq^T (2^Lambda dden),
+    // into the run's with the decay 2^logp from the run's start; and the state carried
+    // across the chunk: S <- 2^Lambda_last S + Fk^T (2^(Lambda_last - Lambda_j) V), z alike.
+    {
+        const float fp = GATED ? fast_exp2(logp) : 1.0f, fc = GATED ? fast_exp2(lam_last) : 1.0f;
+#pragma unroll
+        for (int u = 0; u < B::kStateUnits; ++u) {
+            const int t = w + 4 * u, a = t / NE, b = t % NE;
+            const f32x4_t dr = ck.tile_tn(ck.sQ, LQ, a, ck.sDn, LV, b);
+            const f32x4_t ds = ck.tile_tn(ck.sK, LQ, a, ck.sV, LV, b);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                racc[u][k] += fp * dr[k];
+                sacc[u][k] = fc * sacc[u][k] + ds[k];
+            }
+        }
+        if (ck.tid < D) {
+            const int d = ck.tid;
+            float sr = 0.0f, sz = 0.0f;
+            for (int i = 0; i < C; ++i) {
+                sr += X::to_f32(ck.sQ[i * LQ + d]) * ck.sDd[i];
+                const float fk = X::to_f32(ck.sK[i * LQ + d]);
+                sz += GATED ? fk * fast_exp2(fminf(lam_last - ck.lam(i), 0.0f)) : fk;
+            }
+            rzacc += fp * sr;
+            zacc = fc * zacc + sz;
+        }
+        logp += lam_last;
+    }
+    __syncthreads();
+    // phi(K) is no longer read: it takes dq for the coalesced store
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) ck.sK[(i0 + 4 * g4 + r) * LQ + 16 * dt + l16] = X::from_f32(dfq[dt][r]);
-    {
-        const int rs_ = NC - 1 - c;                        // reversed slot
-        const size_t rslot = size_t(bh) * (NC + 1) + rs_;
-        constexpr int NT = ND * NE;                       // state tiles, dealt to the waves
-#pragma unroll
-        for (int u0 = 0; u0 < NT; u0 += 4) {
-            const int u = u0 + w;
-            if (u < NT) {
-                const int a = u / NE, b = u % NE;
-                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < C / 32; ++ks)
-                    acc = mma(frag_col(ck.sQ, LQ, 32 * ks + 8 * g4, 16 * a, l16),
-                              frag_col(ck.sDn, LV, 32 * ks + 8 * g4, 16 * b, l16), acc);
-                *reinterpret_cast<f32x4_t*>(args.rst + rslot * (D * DV) + (u * kWave + lane) * 4) = acc;
-            }
-        }
-        for (int d = ck.tid; d < D; d += kThreads) {
-            float s = 0.0f;
-            for (int i = 0; i < C; ++i) s += X::to_f32(ck.sQ[i * LQ + d]) * ck.sDd[i];
-            args.rzt[rslot * D + d] = s;
-        }
-        if (GATED && ck.tid == 0) args.rlg[rslot] = ck.sLam[C - 1];
-    }
     __syncthreads();
     ck.template store_out<D>(reinterpret_cast<E*>(args.dq) + size_t(bh) * N * D, ck.sK, LQ);
+    __syncthreads();                  // every read of this chunk's tiles is done
+    }
+
+    // the run's adjoint total at its reversed slot
+    const size_t rslot = size_t(bh) * (args.NR + 1) + (args.NR - 1 - ck.run);
+    ck.put_slot(args.rst + rslot * (D * DV), racc);
+    if (ck.tid < D) args.rzt[rslot * D + ck.tid] = rzacc;
+    if (GATED && ck.tid == 0) args.rlg[rslot] = logp;
 }
 
 // ------------------------------------------------------------ dk / dv pass ----
@@ -627,92 +721,104 @@ void bwd_dkv_kernel(BwdArgs args) {
     constexpr int ND = D / 16, NE = DV / 16, NI = C / 16;
     extern __shared__ __align__(16) unsigned char smem[];
     B ck;
-    ck.init(smem, args.N, args.NC);
-    const int w = ck.w, l16 = ck.l16, g4 = ck.g4, bh = ck.bh, c = ck.c, ts = ck.ts;
+    ck.init(smem, args.N, args.NC, args.LC);
+    const int w = ck.w, bh = ck.bh;
     const int N = args.N, NC = args.NC;
     const E* qb = reinterpret_cast<const E*>(args.q) + size_t(bh) * N * D;
     const E* kb = reinterpret_cast<const E*>(args.k) + size_t(bh) * N * D;
     const E* vb = reinterpret_cast<const E*>(args.v) + size_t(bh) * N * DV;
     const E* dob = reinterpret_cast<const E*>(args.dout) + size_t(bh) * N * DV;
+    static_assert(D <= kThreads && C <= kThreads, "one thread per state row and per token");
 
-    // R, r: the adjoint of the state after this chunk (zero after the last chunk)
-    const size_t rslot = size_t(bh) * (NC + 1) + (NC - 2 - c);
-    {
-        f32x4_t rq[B::template kRowUnits<D>], rk[B::template kRowUnits<D>];
-        f32x4_t rv[B::template kRowUnits<DV>], ro[B::template kRowUnits<DV>];
-        f32x4_t rs[B::kStateUnits], rf[B::kStateUnits];
-        ck.template load_rows<D>(rq, qb);
-        ck.template load_rows<D>(rk, kb);
-        ck.template load_rows<DV>(rv, vb);
-        ck.template load_rows<DV>(ro, dob);
-        // W_c needs the state in front of the chunk too (GATED): the forward slot c - 1
-        const bool wpair = GATED && c < NC - 1 && c > 0;
-        if (c < NC - 1) ck.load_slot(rs, args.rst + rslot * (D * DV));
-        if (wpair) ck.load_slot(rf, args.fst + (size_t(bh) * NC + (c - 1)) * (D * DV));
-        float ddv = 0.0f, inv = 0.0f;
+    // R, r: the adjoint of the state after the current chunk, carried backwards through
+    // the run in fp32 (accumulator-layout pieces, r[tid] for tid < D), from the scanned
+    // slot after the run (zero after the last run).
+    const bool last_run = ck.run == args.NR - 1;
+    f32x4_t racc[B::kStateUnits];
+    float rzacc = 0.0f;
+    if (!last_run) {
+        const size_t rsl = size_t(bh) * (args.NR + 1) + (args.NR - 2 - ck.run);
+        ck.load_slot(racc, args.rst + rsl * (D * DV));
+        if (ck.tid < D) rzacc = args.rzt[rsl * D + ck.tid];
+    } else {
+#pragma unroll
+        for (int u = 0; u < B::kStateUnits; ++u) racc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    // tb: the pairs across the boundary after the current chunk (keys up to it, queries
+    // after it), <R, S> + <r, z> with S, z the state after the chunk; at the run's end from
+    // the forward slot after the run, then back chunk by chunk (W_c = tb - K_c, and the
+    // boundary in front of the chunk carries W_c + Y_c).
+    float tb = 0.0f;
+    if constexpr (GATED) {
+        float wp = 0.0f;
+        if (!last_run) {
+            const size_t fsl = size_t(bh) * args.NR + ck.run;
+            f32x4_t sf[B::kStateUnits];
+            ck.load_slot(sf, args.fst + fsl * (D * DV));
+#pragma unroll
+            for (int u = 0; u < B::kStateUnits; ++u)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) wp += racc[u][k] * sf[u][k];
+            if (ck.tid < D) wp += rzacc * args.fzt[fsl * D + ck.tid];
+        }
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) wp += __shfl_xor(wp, off, kWave);
+        if (ck.lane == 0) ck.sRow[ck.w] = wp;
+        __syncthreads();
+        tb = ck.sRow[0] + ck.sRow[1] + ck.sRow[2] + ck.sRow[3];
+        __syncthreads();
+    }
+
+    // staging registers, loaded one chunk ahead of the products (the run is walked
+    // backwards)
+    f32x4_t sq[B::template kRowUnits<D>], sk[B::template kRowUnits<D>];
+    f32x4_t sv[B::template kRowUnits<DV>], so[B::template kRowUnits<DV>];
+    float sdd = 0.0f, sinv = 0.0f, syq = 0.0f, sg = 1.0f;
+    auto issue = [&](int cn) {
+        const int tn = cn * C, nn = min(C, N - tn);
+        ck.template load_rows<D>(sq, qb, tn, nn);
+        ck.template load_rows<D>(sk, kb, tn, nn);
+        ck.template load_rows<DV>(sv, vb, tn, nn);
+        ck.template load_rows<DV>(so, dob, tn, nn);
         if (ck.tid < C) {
-            const size_t t = size_t(bh) * N + ts + min(ck.tid, ck.nrows - 1);
-            ddv = args.dden[t];
-            inv = args.inv[t];
+            const size_t t = size_t(bh) * N + tn + min(ck.tid, nn - 1);
+            sdd = args.dden[t];
+            sinv = args.inv[t];
+            if constexpr (GATED) syq = args.yq[t];
         }
-        ck.template store_rows<D, true>(ck.sQ, LQ, rq);
-        ck.template store_rows<D, true>(ck.sK, LQ, rk);
-        ck.template store_rows<DV, false>(ck.sV, LV, rv);
-        ck.template store_rows<DV, false>(ck.sDn, LV, ro);
-        if (ck.tid < C) {
-            ck.sDd[ck.tid] = ck.tid < ck.nrows ? ddv : 0.0f;
-            ck.sInv[ck.tid] = ck.tid < ck.nrows ? inv : 0.0f;
-        }
-        if (c < NC - 1) {
-            ck.store_slot(rs);
-            for (int d = ck.tid; d < D; d += kThreads) ck.sZ[d] = args.rzt[rslot * D + d];
-        } else {
-            ck.stage_state(nullptr, nullptr, nullptr, nullptr);
-        }
-        // W_c = 2^Lambda_last (<R, S_prev> + <r, z_prev>): keys in front of the chunk
-        // against queries after it (both states fp32; R and the forward slots share one
-        // layout, S0 is mapped from the caller's)
-        if constexpr (GATED) {
-            float wp = 0.0f;
-            if (wpair) {
+        if constexpr (GATED) sg = ck.load_gate(args.g + size_t(bh) * N, tn, nn);
+    };
+    if constexpr (B::Sh::kAhead) issue(ck.c_end - 1);
+    for (int c = ck.c_end - 1; c >= ck.c_first; --c) {
+    ck.refresh();
+    const int lane = ck.lane, l16 = ck.l16, g4 = ck.g4;
+    ck.set_chunk(c);
+    const int ts = ck.ts;
+    if constexpr (!B::Sh::kAhead) issue(c);
+    ck.template store_rows<D, true>(ck.sQ, LQ, sq);
+    ck.template store_rows<D, true>(ck.sK, LQ, sk);
+    ck.template store_rows<DV, false>(ck.sV, LV, sv);
+    ck.template store_rows<DV, false>(ck.sDn, LV, so);
+    if (ck.tid < C) {
+        ck.sDd[ck.tid] = ck.tid < ck.nrows ? sdd : 0.0f;
+        ck.sInv[ck.tid] = ck.tid < ck.nrows ? sinv : 0.0f;
+    }
+    ck.store_slot(racc);
+    if (ck.tid < D) ck.sZ[ck.tid] = rzacc;
+    if constexpr (GATED) {
+        // Y_c = sum of yq over the chunk's queries (wave 0: one lane per token)
+        if (ck.w == 0) {
+            float y = lane < ck.nrows ? syq : 0.0f;
 #pragma unroll
-                for (int u = 0; u < B::kStateUnits; ++u)
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) wp += rs[u][k] * rf[u][k];
-                const float* fz = args.fzt + (size_t(bh) * NC + (c - 1)) * D;
-                for (int d = ck.tid; d < D; d += kThreads) wp += args.rzt[rslot * D + d] * fz[d];
-            } else if (c == 0 && c < NC - 1) {
-                if (args.s0) {
-                    const float* S0 = args.s0 + size_t(bh) * D * DV;
-#pragma unroll
-                    for (int u = 0; u < B::kStateUnits; ++u) {
-                        const int q4 = ck.tid + u * kThreads;
-                        const int t = q4 / kWave, ln = q4 % kWave;
-                        const int a = t / (DV / 16), b = t % (DV / 16);
-#pragma unroll
-                        for (int k = 0; k < 4; ++k)
-                            wp += rs[u][k] * S0[size_t(16 * a + 4 * (ln >> 4) + k) * DV + 16 * b + (ln & 15)];
-                    }
-                }
-                if (args.z0)
-                    for (int d = ck.tid; d < D; d += kThreads) wp += args.rzt[rslot * D + d] * args.z0[size_t(bh) * D + d];
-            }
-#pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) wp += __shfl_xor(wp, off, kWave);
-            if (ck.lane == 0) ck.sRow[ck.w] = wp;
+            for (int off = 1; off < kWave; off <<= 1) y += __shfl_xor(y, off, kWave);
+            if (lane == 0) ck.sRow[0] = y;
         }
     }
-    ck.stage_lambda(GATED ? args.g + size_t(bh) * N : nullptr);
+    ck.stage_lambda(sg);
     __syncthreads();
-    if (GATED && ck.tid == 0)
-        args.wc[size_t(bh) * NC + c] = (ck.sRow[0] + ck.sRow[1] + ck.sRow[2] + ck.sRow[3]) * fast_exp2(ck.lam(C - 1));
+    if (B::Sh::kAhead && c > ck.c_first) issue(c - 1);
 
     const int j0 = 16 * w;            // this wave's key rows
-    E xk[ND][4];                      // raw k of this lane's outputs, for phi'(k) at the end
-#pragma unroll
-    for (int dt = 0; dt < ND; ++dt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) xk[dt][r] = kb[size_t(min(ts + j0 + 4 * g4 + r, N - 1)) * D + 16 * dt + l16];
     float lam_r[4], tail[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -785,11 +891,24 @@ void bwd_dkv_kernel(BwdArgs args) {
         }
     }
     __syncthreads();
-    // B^T over this wave's rows into sA (every read of A^T finished before the barrier)
+    // B^T over this wave's rows into sA (every read of A^T finished before the barrier);
+    // dOut, dden are not read again as they are: their rows become 2^Lambda_i dnum_i and
+    // 2^Lambda_i dden_i for the chunk's adjoint total
 #pragma unroll
     for (int it = 0; it < NI; ++it)
 #pragma unroll
         for (int r = 0; r < 4; ++r) ck.sA[(j0 + 4 * g4 + r) * LA + 16 * it + l16] = X::from_f32(bt[it][r]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int i = j0 + 4 * g4 + r;
+        const float f = (GATED ? fast_exp2(lam_r[r]) : 1.0f) * ck.sInv[i];
+#pragma unroll
+        for (int et = 0; et < NE; ++et) {
+            E& x = ck.sDn[i * LV + 16 * et + l16];
+            x = X::from_f32(X::to_f32(x) * f);
+        }
+    }
+    if (GATED && ck.tid < C) ck.sDd[ck.tid] *= fast_exp2(ck.lam(ck.tid));
     __syncthreads();
 
     // dFk = 2^(Lambda_last - Lambda_j) (V R^T + 1 r^T) + B^T Fq
@@ -814,12 +933,17 @@ void bwd_dkv_kernel(BwdArgs args) {
             }
         }
         if constexpr (GATED) {
+            float kw = 0.0f;                           // K_c: this wave's part of sum_j zk_j
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float s = sum16(zk[r]);
                 const int j = j0 + 4 * g4 + r;
                 if (l16 == 0 && ts + j < N) args.zk[size_t(bh) * N + ts + j] = s;
+                kw += s;
             }
+            kw += __shfl_xor(kw, 16, kWave);
+            kw += __shfl_xor(kw, 32, kWave);
+            if (lane == 0) ck.sCol[w] = kw;
         }
     }
     for (int ks = w >> 1; ks < C / 32; ++ks) {
@@ -827,13 +951,39 @@ void bwd_dkv_kernel(BwdArgs args) {
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) dfk[dt] = mma(a, frag_col(ck.sQ, LQ, 32 * ks + 8 * g4, 16 * dt, l16), dfk[dt]);
     }
+    // the adjoint carried across the chunk: R <- 2^Lambda_last R + Fq^T (2^Lambda dNum),
+    // r <- 2^Lambda_last r + Fq^T (2^Lambda dden)
+    {
+        const float fc = GATED ? fast_exp2(ck.lam(C - 1)) : 1.0f;
+#pragma unroll
+        for (int u = 0; u < B::kStateUnits; ++u) {
+            const int t = w + 4 * u, a = t / NE, b = t % NE;
+            const f32x4_t dr = ck.tile_tn(ck.sQ, LQ, a, ck.sDn, LV, b);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) racc[u][k] = fc * racc[u][k] + dr[k];
+        }
+        if (ck.tid < D) {
+            float sr = 0.0f;
+            for (int i = 0; i < C; ++i) sr += X::to_f32(ck.sQ[i * LQ + ck.tid]) * ck.sDd[i];
+            rzacc = fc * rzacc + sr;
+        }
+    }
     // dk = dFk * phi'(k) and dv through the now free phi(K) and V tiles, stored coalesced
     __syncthreads();
+    if constexpr (GATED) {
+        // W_c = tb - K_c: keys in front of the chunk against queries after it
+        const float wcv = tb - (ck.sCol[0] + ck.sCol[1] + ck.sCol[2] + ck.sCol[3]);
+        if (ck.tid == 0) args.wc[size_t(bh) * NC + c] = wcv;
+        tb = wcv + ck.sRow[0];
+    }
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            ck.sK[(j0 + 4 * g4 + r) * LQ + 16 * dt + l16] = X::from_f32(dfk[dt][r] * dphi(X::to_f32(xk[dt][r])));
+        {
+            E& x = ck.sK[(j0 + 4 * g4 + r) * LQ + 16 * dt + l16];      // phi(k), read before it takes dk
+            x = X::from_f32(dfk[dt][r] * dphi_of(X::to_f32(x)));
+        }
 #pragma unroll
     for (int et = 0; et < NE; ++et)
 #pragma unroll
@@ -841,6 +991,8 @@ void bwd_dkv_kernel(BwdArgs args) {
     __syncthreads();
     ck.template store_out<D>(reinterpret_cast<E*>(args.dk) + size_t(bh) * N * D, ck.sK, LQ);
     ck.template store_out<DV>(reinterpret_cast<E*>(args.dv) + size_t(bh) * N * DV, ck.sV, LV);
+    __syncthreads();                  // every read of this chunk's tiles is done
+    }
 }
 
 // --------------------------------------------------------------- gate pass ----

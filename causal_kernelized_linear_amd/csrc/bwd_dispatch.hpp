@@ -51,25 +51,28 @@ hipError_t run_bwd(const BwdLaunch& p) {
         a.zk = reinterpret_cast<float*>(ws + lay.zk);
         a.wc = reinterpret_cast<float*>(ws + lay.wc);
         a.N = p.N; a.NC = NC; a.eps = p.eps; a.normalize = p.normalize;
+        a.LC = p.run > 0 ? (p.run < NC ? p.run : NC) : bwd_chunks_per_group(p.BH, NC, Sh::kBytes, p.cus);
+        const int NR = (NC + a.LC - 1) / a.LC;
+        a.NR = NR;
         constexpr int NBLK = (D * DV + D + kThreads - 1) / kThreads;
         const unsigned BH = unsigned(p.BH);
-        // the state in front of every chunk: the forward's totals walk with one chunk per
+        // the state in front of every run: the forward's totals walk with one run per
         // segment, then its scan (which starts from S0, z0)
-        if (NC > 1) {
+        if (NR > 1) {
             WalkArgs w;
             w.q = p.q; w.k = p.k; w.v = p.v; w.g = p.g; w.o = nullptr;
             w.st = a.fst; w.zt = a.fzt; w.lg = reinterpret_cast<float*>(ws + lay.flg);
             w.s0 = p.s0; w.z0 = p.z0;
-            w.N = p.N; w.nseg = NC; w.L = 1; w.direct = 0; w.want_final = 0; w.eps = p.eps; w.normalize = 1;
-            hipLaunchKernelGGL(k_tot, dim3(BH * unsigned(NC - 1)), dim3(kThreads), ShT::kBytes, p.stream, w);
+            w.N = p.N; w.nseg = NR; w.L = a.LC; w.direct = 0; w.want_final = 0; w.eps = p.eps; w.normalize = 1;
+            hipLaunchKernelGGL(k_tot, dim3(BH * unsigned(NR - 1)), dim3(kThreads), ShT::kBytes, p.stream, w);
             hipLaunchKernelGGL((scan_kernel<D, DV, GATED>), dim3(BH * NBLK), dim3(kThreads), 0, p.stream, a.fst, a.fzt,
-                               w.lg, p.s0, p.z0, NC);
+                               w.lg, p.s0, p.z0, NR);
         }
-        hipLaunchKernelGGL(k_dq, dim3(BH * unsigned(NC)), dim3(kThreads), Sh::kBytes, p.stream, a);
-        // adjoint states: the scan over the chunks' adjoint totals, last chunk first
+        hipLaunchKernelGGL(k_dq, dim3(BH * unsigned(NR)), dim3(kThreads), Sh::kBytes, p.stream, a);
+        // adjoint states: the scan over the runs' adjoint totals, last run first
         hipLaunchKernelGGL((scan_kernel<D, DV, GATED>), dim3(BH * NBLK), dim3(kThreads), 0, p.stream, a.rst, a.rzt,
-                           a.rlg, static_cast<const float*>(nullptr), static_cast<const float*>(nullptr), NC + 1);
-        hipLaunchKernelGGL(k_dkv, dim3(BH * unsigned(NC)), dim3(kThreads), Sh::kBytes, p.stream, a);
+                           a.rlg, static_cast<const float*>(nullptr), static_cast<const float*>(nullptr), NR + 1);
+        hipLaunchKernelGGL(k_dkv, dim3(BH * unsigned(NR)), dim3(kThreads), Sh::kBytes, p.stream, a);
         if (GATED && p.dg) {
             const int nwork = p.BH * NC, per = kThreads / kWave;
             hipLaunchKernelGGL(bwd_dg_kernel, dim3(unsigned((nwork + per - 1) / per)), dim3(kThreads), 0, p.stream, p.g,
@@ -77,7 +80,7 @@ hipError_t run_bwd(const BwdLaunch& p) {
         }
         if (p.ds0 || p.dz0)
             hipLaunchKernelGGL((final_kernel<D, DV>), dim3(BH * NBLK), dim3(kThreads), 0, p.stream, a.rst, a.rzt,
-                               NC + 1, NC - 1, p.ds0, p.dz0);
+                               NR + 1, NR - 1, p.ds0, p.dz0);
         return hipGetLastError();
     }
 }

@@ -81,9 +81,23 @@ constexpr size_t bwd_lds_bytes(int esize, int D, int Dv) {
     return (2 * C * (D + pad) + 2 * C * (Dv + pad) + size_t(D) * (Dv + pad) + C * (C + pad)) * es + (8 * C + D) * 4;
 }
 
-// Workspace of the backward: the state in front of every chunk (NC slots per head), the
-// chunks' adjoint totals and their reverse scan (NC + 1 slots), then five fp32 [BH][N]
-// rows (1/d, dden and the three per-token pair sums of d log g) and one [BH][NC] row.
+// Chunks per run of the dq and dk/dv passes.  A workgroup walks a run and carries the
+// states through it in registers, so the state traffic (a [D][Dv] fp32 slot read or
+// written per run by five passes) falls with the run's length; the runs are made as long
+// as still gives every resident slot (LDS-bound) a workgroup.  At most kBwdMaxRun.
+constexpr int kBwdMaxRun = 16;
+inline int bwd_chunks_per_group(long BH, int NC, size_t lds_bytes, int cus) {
+    const long resident = long(cus) * long(kMaxLds / lds_bytes < 1 ? 1 : kMaxLds / lds_bytes);
+    long run = BH * NC / resident;
+    if (run > kBwdMaxRun) run = kBwdMaxRun;
+    if (run > NC) run = NC;
+    return run < 1 ? 1 : int(run);
+}
+
+// Workspace of the backward: the state in front of every run and the runs' adjoint
+// totals with their reverse scan (sized for runs of one chunk, NC and NC + 1 slots per
+// head, so the size does not depend on the device), then five fp32 [BH][N] rows (1/d,
+// dden and the three per-token pair sums of d log g) and one [BH][NC] row.
 struct BwdLayout {
     size_t fwd, fzt, flg, rev, rzt, rlg, inv, dden, xs, yq, zk, wc, bytes;
 };
@@ -125,6 +139,8 @@ struct BwdLaunch {
     int BH, N, D, Dv;
     float eps;
     int normalize;
+    int cus;                 // compute units of the device (sizes the runs)
+    int run;                 // chunks per run; 0: chosen from the device's size
     hipStream_t stream;
 };
 

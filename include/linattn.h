@@ -223,6 +223,12 @@ size_t linattn_bwd_workspace_size(int B, int H, int N, int D, int Dv, linattn_dt
  *  dq, dk [B,H,N,D], dv [B,H,N,Dv]                 dtype, written; must not alias any input
  *  dg   [B,H,N] float or NULL                      written when g is given (NULL: skipped)
  *  ds0  [B,H,D,Dv], dz0 [B,H,D] float or NULL      gradients of the initial state (NULL: skipped)
+ *  run                                             chunks per run, >= 0: the passes walk runs of
+ *                                                  this many chunks and carry the states through
+ *                                                  them; 0 lets the library choose from the
+ *                                                  device's size (values past the chunk count
+ *                                                  act as the chunk count).  The results differ
+ *                                                  between choices only by rounding.
  *  workspace                                       at least linattn_bwd_workspace_size bytes
  *
  * Supported shapes: D, Dv in {64, 128}; bf16 at every pair, f32 unless D = Dv = 128
@@ -232,7 +238,7 @@ linattn_status_t linattn_bwd(
     const void* q, const void* k, const void* v, const float* g, const void* dout,
     const float* s0, const float* z0, void* dq, void* dk, void* dv, float* dg, float* ds0, float* dz0,
     int B, int H, int N, int D, int Dv, linattn_dtype_t dtype, float eps, linattn_output_t out,
-    void* workspace, size_t workspace_bytes, void* stream);
+    int run, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * One recurrent decode step for B*H independent heads (aiwiki.thehackersbrain.dev page,

@@ -158,9 +158,41 @@ def test_decode_rejects_bad_arguments():
     assert decode(B=0, q=0) == OK
 
 
+DO, DQ, DK, DV, DG = (0x10_0000_0000 * (i + 11) for i in range(5))
+
+
+def bwd(q=Q, k=K, v=V, g=G, do=DO, dq=DQ, dk=DK, dv=DV, dg=DG, B=2, H=2, N=256, D=64, Dv=64, dt=1, eps=1e-6, out=0,
+        run=0, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = binding.linattn_bwd_workspace_size(B, H, N, D, Dv, dt)
+    return binding.linattn_bwd(q, k, v, g, do, S0, Z0, dq, dk, dv, dg, 0, 0, B, H, N, D, Dv, dt, eps, out, run, WS,
+                               ws_bytes, 0)
+
+
+def test_bwd_rejects_bad_arguments():
+    assert bwd(run=-1) == INVALID
+    assert bwd(eps=0.0) == INVALID
+    assert bwd(out=2) == INVALID
+    assert bwd(dq=Q) == INVALID                                 # dq overlaps q
+    assert bwd(dg=DQ + 16) == INVALID                           # dg overlaps dq
+    assert bwd(dk=DK + 4) == INVALID                            # misaligned
+    assert bwd(D=96) == UNSUPPORTED
+    assert bwd(ws_bytes=binding.linattn_bwd_workspace_size(2, 2, 256, 64, 64, 1) - 1) == WORKSPACE
+    assert bwd(B=0, q=0) == OK
+
+
+def test_bwd_workspace_size():
+    ws = binding.linattn_bwd_workspace_size
+    assert ws(0, 1, 128, 64, 64, 1) == 0
+    a = ws(8, 16, 4096, 64, 64, 1)
+    # a state slot per chunk and per head (an upper bound for any run length), twice
+    assert a % 256 == 0 and a >= 2 * 8 * 16 * 64 * 64 * 64 * 4
+
+
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="only meaningful where no GPU is present")
 def test_no_device_is_reported_not_crashed():
     assert fwd() == HIP
     assert fwd(out=1, gated=True) == HIP
     assert decode() == HIP
     assert decode_ex(g=0, z=0, out=1) == HIP                    # valid: numerator mode needs no z
+    assert bwd(run=3) == HIP

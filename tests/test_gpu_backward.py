@@ -28,9 +28,9 @@ def _dev(t):
     return None if t is None else t.to(DEV)
 
 
-def gpu_bwd(inp, normalize=True, s0=None, z0=None, state_grads=False):
+def gpu_bwd(inp, normalize=True, s0=None, z0=None, state_grads=False, run=0):
     r = binding.bwd(*(_dev(inp[n]) for n in ("q", "k", "v", "dout")), g=_dev(inp.get("g")), s0=_dev(s0), z0=_dev(z0),
-                    normalize=normalize, state_grads=state_grads)
+                    normalize=normalize, state_grads=state_grads, run=run)
     torch.cuda.synchronize()
     return r
 
@@ -88,6 +88,47 @@ def test_backward_small_against_oracle(case, gated, normalize):
     got = gpu_bwd(inp, normalize, s0=inp["s0"], z0=inp["z0"], state_grads=True)
     ref = oracle_bwd(inp, normalize, s0=inp["s0"], z0=inp["z0"])
     check(got, ref, TOL[dt], gated=gated, state=True)
+
+
+RUN_CASES = [
+    # (B, H, N, D, Dv, dtype, chunks per run): several runs, ragged last run and chunk
+    (1, 2, 64 * 7 + 13, 64, 64, "bf16", 3),
+    (1, 1, 64 * 5, 64, 128, "bf16", 2),
+    (2, 1, 64 * 6 + 1, 128, 64, "f32", 4),
+    (1, 1, 64 * 4, 64, 64, "f32", 4),            # one run over the whole sequence
+    (1, 1, 64 * 9 + 30, 128, 128, "bf16", 16),   # a run longer than the sequence
+    (1, 2, 64 * 11, 64, 64, "bf16", 5),
+]
+
+
+@pytest.mark.parametrize("gated", [False, True], ids=["ungated", "gated"])
+@pytest.mark.parametrize("case", RUN_CASES, ids=lambda c: "B{}H{}N{}D{}Dv{}{}run{}".format(*c))
+def test_backward_runs_against_oracle(case, gated):
+    """The passes walk runs of several chunks, carrying the state forwards and its
+    adjoint backwards; the gate gradient steps the boundary pair sums back through them."""
+    B, H, N, D, Dv, dt, run = case
+    _say(f"backward {case} gated={gated}")
+    inp = workloads.random_inputs(71 + N + run, B, H, N, D, Dv, dtype=dt, gated=gated, g_low=0.8, with_state=True,
+                                  state_scale=5.0, with_grad=True)
+    got = gpu_bwd(inp, s0=inp["s0"], z0=inp["z0"], state_grads=True, run=run)
+    ref = oracle_bwd(inp, s0=inp["s0"], z0=inp["z0"])
+    check(got, ref, TOL[dt], gated=gated, state=True)
+
+
+def test_backward_run_lengths_agree():
+    """Every run length gives the same gradients up to rounding."""
+    inp = workloads.random_inputs(8, 2, 2, 64 * 12 + 5, 64, 64, dtype="bf16", gated=True, with_state=True,
+                                  state_scale=5.0, with_grad=True)
+    _say("backward run lengths 1, 4, 13 and the library's choice")
+    ref = gpu_bwd(inp, s0=inp["s0"], z0=inp["z0"], state_grads=True, run=1)
+    ref = {n: t for n, t in ref.items()}
+    for run in (4, 13, 0):
+        got = gpu_bwd(inp, s0=inp["s0"], z0=inp["z0"], state_grads=True, run=run)
+        errs = {n: grad_rel_err(to64(got[n]), to64(ref[n])) for n in ("dq", "dk", "dv")}
+        errs.update({n: matrix_rel_err(to64(got[n]), to64(ref[n])) for n in ("dg", "ds0", "dz0")})
+        _say(f"  run {run}: " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+        for n, e in errs.items():
+            assert e <= TOL["bf16"], (run, n, e)
 
 
 def test_backward_without_initial_state():
