@@ -117,6 +117,7 @@ struct BwdShape {
     static constexpr size_t kOffZ = kOffRow + size_t(C) * 4;
     static constexpr size_t kBytes = kOffZ + size_t(D) * 4;
     static_assert(kBytes == bwd_lds_bytes(int(sizeof(E)), D, DV), "host LDS formula out of step");
+    static_assert(4 * C >= kThreads && kThreads % D == 0, "column-sum slices fit sCol");
     // workgroups (so waves per SIMD) the LDS allows: the register target of both kernels,
     // so the compiler does not squeeze the accumulators for an occupancy out of reach
     static constexpr int kWaves = int(kMaxLds / kBytes) < 1 ? 1 : int(kMaxLds / kBytes);
@@ -162,10 +163,20 @@ __device__ __forceinline__ F8<float> frag_col(const float* t, int ld, int k0, in
     return f;
 }
 
-// Sum over the 16 lanes of a lane group (the columns of an accumulator row).
+// Sum over the 16 lanes of a lane group (the columns of an accumulator row), every lane
+// getting the total: DPP moves within each 16-lane row, no LDS round trip.  Quad swaps
+// (lanes 1,0,3,2 then 2,3,0,1) leave each quad's sum in all its lanes; the half-row
+// mirror (lane i from 7 - i) adds the neighbouring quad, the row mirror (i from 15 - i)
+// the other half.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
 __device__ __forceinline__ float sum16(float x) {
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off, kWave);
+    x += dpp_move<0xB1>(x);     // quad_perm [1, 0, 3, 2]
+    x += dpp_move<0x4E>(x);     // quad_perm [2, 3, 0, 1]
+    x += dpp_move<0x141>(x);    // row_half_mirror
+    x += dpp_move<0x140>(x);    // row_mirror
     return x;
 }
 
@@ -384,6 +395,7 @@ void bwd_dq_kernel(BwdArgs args) {
     using X = Elem<E>;
     constexpr int C = B::C, LQ = B::LQ, LV = B::LV, LA = B::LA;
     constexpr int ND = D / 16, NE = DV / 16, NJ = C / 16;
+    constexpr int kParts = kThreads / D, kRowsPer = C / kParts;   // column sums: threads per column, rows each
     extern __shared__ __align__(16) unsigned char smem[];
     B ck;
     ck.init(smem, args.N, args.NC, args.LC);
@@ -678,20 +690,35 @@ void bwd_dq_kernel(BwdArgs args) {
                 sacc[u][k] = fc * sacc[u][k] + ds[k];
             }
         }
-        if (ck.tid < D) {
-            const int d = ck.tid;
+        // the z parts, Fq^T (2^Lambda dden) and Fk^T 2^(Lambda_last - Lambda_j): every
+        // thread sums a slice of the rows of one column, into sA (free in this phase)
+        float* part = reinterpret_cast<float*>(ck.sA);
+        {
+            const int d = ck.tid % D, i0p = (ck.tid / D) * kRowsPer;
             float sr = 0.0f, sz = 0.0f;
-            for (int i = 0; i < C; ++i) {
+#pragma unroll
+            for (int ii = 0; ii < kRowsPer; ++ii) {
+                const int i = i0p + ii;
                 sr += X::to_f32(ck.sQ[i * LQ + d]) * ck.sDd[i];
                 const float fk = X::to_f32(ck.sK[i * LQ + d]);
                 sz += GATED ? fk * fast_exp2(fminf(lam_last - ck.lam(i), 0.0f)) : fk;
+            }
+            part[ck.tid] = sr;
+            part[kThreads + ck.tid] = sz;
+        }
+        __syncthreads();
+        if (ck.tid < D) {
+            float sr = 0.0f, sz = 0.0f;
+#pragma unroll
+            for (int p = 0; p < kParts; ++p) {
+                sr += part[p * D + ck.tid];
+                sz += part[kThreads + p * D + ck.tid];
             }
             rzacc += fp * sr;
             zacc = fc * zacc + sz;
         }
         logp += lam_last;
     }
-    __syncthreads();
     // phi(K) is no longer read: it takes dq for the coalesced store
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt)
@@ -719,6 +746,7 @@ void bwd_dkv_kernel(BwdArgs args) {
     using X = Elem<E>;
     constexpr int C = B::C, LQ = B::LQ, LV = B::LV, LA = B::LA;
     constexpr int ND = D / 16, NE = DV / 16, NI = C / 16;
+    constexpr int kParts = kThreads / D, kRowsPer = C / kParts;   // column sums: threads per column, rows each
     extern __shared__ __align__(16) unsigned char smem[];
     B ck;
     ck.init(smem, args.N, args.NC, args.LC);
@@ -943,7 +971,7 @@ void bwd_dkv_kernel(BwdArgs args) {
             }
             kw += __shfl_xor(kw, 16, kWave);
             kw += __shfl_xor(kw, 32, kWave);
-            if (lane == 0) ck.sCol[w] = kw;
+            if (lane == 0) ck.sRow[1 + w] = kw;
         }
     }
     for (int ks = w >> 1; ks < C / 32; ++ks) {
@@ -953,8 +981,8 @@ void bwd_dkv_kernel(BwdArgs args) {
     }
     // the adjoint carried across the chunk: R <- 2^Lambda_last R + Fq^T (2^Lambda dNum),
     // r <- 2^Lambda_last r + Fq^T (2^Lambda dden)
+    const float fc = GATED ? fast_exp2(ck.lam(C - 1)) : 1.0f;
     {
-        const float fc = GATED ? fast_exp2(ck.lam(C - 1)) : 1.0f;
 #pragma unroll
         for (int u = 0; u < B::kStateUnits; ++u) {
             const int t = w + 4 * u, a = t / NE, b = t % NE;
@@ -962,17 +990,25 @@ void bwd_dkv_kernel(BwdArgs args) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) racc[u][k] = fc * racc[u][k] + dr[k];
         }
-        if (ck.tid < D) {
-            float sr = 0.0f;
-            for (int i = 0; i < C; ++i) sr += X::to_f32(ck.sQ[i * LQ + ck.tid]) * ck.sDd[i];
-            rzacc = fc * rzacc + sr;
-        }
+        // the z part Fq^T (2^Lambda dden): every thread sums a slice of the rows of one
+        // column, into sCol
+        const int d = ck.tid % D, i0p = (ck.tid / D) * kRowsPer;
+        float sr = 0.0f;
+#pragma unroll
+        for (int ii = 0; ii < kRowsPer; ++ii) sr += X::to_f32(ck.sQ[(i0p + ii) * LQ + d]) * ck.sDd[i0p + ii];
+        ck.sCol[ck.tid] = sr;
     }
     // dk = dFk * phi'(k) and dv through the now free phi(K) and V tiles, stored coalesced
     __syncthreads();
+    if (ck.tid < D) {
+        float sr = 0.0f;
+#pragma unroll
+        for (int p = 0; p < kParts; ++p) sr += ck.sCol[p * D + ck.tid];
+        rzacc = fc * rzacc + sr;
+    }
     if constexpr (GATED) {
         // W_c = tb - K_c: keys in front of the chunk against queries after it
-        const float wcv = tb - (ck.sCol[0] + ck.sCol[1] + ck.sCol[2] + ck.sCol[3]);
+        const float wcv = tb - (ck.sRow[1] + ck.sRow[2] + ck.sRow[3] + ck.sRow[4]);
         if (ck.tid == 0) args.wc[size_t(bh) * NC + c] = wcv;
         tb = wcv + ck.sRow[0];
     }
