@@ -52,9 +52,18 @@
 //                   one run it collects that of at most LC chunks.
 // The states in front of every run come from the forward's totals walk (one run per
 // segment) and its scan; the adjoint states from the same scan run over the runs'
-// adjoint totals in reverse order.  Every MFMA operand is staged in LDS as a
-// row-major tile; an operand whose contraction index runs down the tile's rows is
-// read with ds_read_b64_tr_b16 (bf16) or element by element (fp32).
+// adjoint totals in reverse order.
+//
+// Layout.  The chunk's rows (phi(Q), phi(K), V, dOut) and one state are staged in LDS as
+// row-major tiles; an operand whose contraction index runs down a tile's rows is read
+// with ds_read_b64_tr_b16 (bf16) or element by element (fp32).  The [C][C] score tiles
+// never go to LDS: each wave computes them transposed (lane l16 owning one of its own
+// rows, four consecutive partners per lane group), which is exactly the operand layout of
+// the 16x16x16 MFMA that consumes them; the outputs come out transposed the same way and
+// go to memory as four consecutive columns per lane.  Sums that would take a loop over
+// the chunk (den's z part, the z vectors of the state steps) ride on the 16-byte pad
+// group of each row as two extra columns, an fp32 value split into a bf16 high and low
+// part, so they come out of the MFMA products that run anyway.
 #pragma once
 
 #include "device_common.hpp"
@@ -101,15 +110,13 @@ struct BwdShape {
     static constexpr int C = kBwdChunk;
     static constexpr int PAD = 16 / int(sizeof(E));   // one 16-byte group per row
     static constexpr int LQ = D + PAD;                 // phi(Q), phi(K) [C][D]
-    static constexpr int LV = DV + PAD;                // V, dNum [C][Dv]; S_prev / R [D][Dv]
-    static constexpr int LA = C + PAD;                 // A or B [C][C]
+    static constexpr int LV = DV + PAD;                // V, dOut [C][Dv]; S_prev / R [D][Dv]
     static constexpr size_t kOffQ = 0;
     static constexpr size_t kOffK = kOffQ + size_t(C) * LQ * sizeof(E);
     static constexpr size_t kOffV = kOffK + size_t(C) * LQ * sizeof(E);
     static constexpr size_t kOffDn = kOffV + size_t(C) * LV * sizeof(E);
     static constexpr size_t kOffS = kOffDn + size_t(C) * LV * sizeof(E);
-    static constexpr size_t kOffA = kOffS + size_t(D) * LV * sizeof(E);
-    static constexpr size_t kOffLam = kOffA + size_t(C) * LA * sizeof(E);
+    static constexpr size_t kOffLam = kOffS + size_t(D) * LV * sizeof(E);
     static constexpr size_t kOffDd = kOffLam + size_t(C) * 4;
     static constexpr size_t kOffInv = kOffDd + size_t(C) * 4;
     static constexpr size_t kOffCol = kOffInv + size_t(C) * 4;     // [4][C] per-wave column sums of P
@@ -117,17 +124,24 @@ struct BwdShape {
     static constexpr size_t kOffZ = kOffRow + size_t(C) * 4;
     static constexpr size_t kBytes = kOffZ + size_t(D) * 4;
     static_assert(kBytes == bwd_lds_bytes(int(sizeof(E)), D, DV), "host LDS formula out of step");
-    static_assert(4 * C >= kThreads && kThreads % D == 0, "column-sum slices fit sCol");
+    static_assert(PAD >= 2, "the pad group carries two extra columns");
+    // An extra 16-column operand block at column Dv reads the pad group and then, past it,
+    // the start of the next row (or, for a tile's last row, the next region: the next
+    // tile, or the fp32 vectors after S); those columns only feed output rows or columns
+    // that are thrown away.  Every tile is followed by at least that much LDS.
+    static_assert(kOffLam + size_t(16) * 4 <= kBytes, "room behind S for the extra block");
     // workgroups (so waves per SIMD) the LDS allows: the register target of both kernels,
     // so the compiler does not squeeze the accumulators for an occupancy out of reach
     static constexpr int kWaves = int(kMaxLds / kBytes) < 1 ? 1 : int(kMaxLds / kBytes);
     // 16-byte pieces per thread of a state in accumulator layout, and of one chunk's four
     // row tiles.  Loading the next chunk's rows during this chunk's products keeps them
     // live across the products, beside the two carried states: done where all of it stays
-    // within 32 pieces (128 registers), else the rows are loaded chunk by chunk.
+    // within 32 pieces (128 registers) and at most two workgroups share a CU; at three,
+    // the other workgroups hide the loads as well and the registers are better spent
+    // (measured equal or faster without).
     static constexpr int kStateUnits = D * DV / 4 / kThreads;
     static constexpr int kRowPieces = (2 * C * D + 2 * C * DV) * int(sizeof(E)) / 16 / kThreads;
-    static constexpr bool kAhead = kRowPieces + 2 * kStateUnits <= 32;
+    static constexpr bool kAhead = kWaves <= 2 && kRowPieces + 2 * kStateUnits <= 32;
 };
 
 // Operand of 16 rows from a row-major tile: lane supplies row `row`, contraction
@@ -141,12 +155,16 @@ __device__ __forceinline__ F8<E> frag_row(const E* t, int ld, int row, int k0) {
 // lane l holds t[k0 + e][n0 + l % 16].  bf16: two ds_read_b64_tr_b16, each giving a
 // 16-lane block four rows of one column when block lane j points at row k0 + j / 4,
 // columns n0 + 4 (j % 4) .. + 3.  fp32: eight reads.
-__device__ __forceinline__ F8<uint16_t> frag_col(const uint16_t* t, int ld, int k0, int n0, int l16) {
-    typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i16x4_t tr_read(const uint16_t* t, int ld, int k0, int n0, int l16) {
     typedef __attribute__((address_space(3))) i16x4_t* lds_ptr_t;
     const uint16_t* p = t + (k0 + (l16 >> 2)) * ld + n0 + 4 * (l16 & 3);
-    const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr_t)(const_cast<uint16_t*>(p)));
-    const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr_t)(const_cast<uint16_t*>(p + 4 * ld)));
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr_t)(const_cast<uint16_t*>(p)));
+}
+
+__device__ __forceinline__ F8<uint16_t> frag_col(const uint16_t* t, int ld, int k0, int n0, int l16) {
+    const i16x4_t a = tr_read(t, ld, k0, n0, l16), b = tr_read(t, ld, k0 + 4, n0, l16);
     F8<uint16_t> f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -161,6 +179,34 @@ __device__ __forceinline__ F8<float> frag_col(const float* t, int ld, int k0, in
 #pragma unroll
     for (int e = 0; e < 8; ++e) f.x[e] = t[(k0 + e) * ld + n0 + l16];
     return f;
+}
+
+// The same with four contraction slots, for the 16x16x16 product: slot e of lane l holds
+// t[k0 + e][n0 + l % 16].
+__device__ __forceinline__ F4<uint16_t> frag4_col(const uint16_t* t, int ld, int k0, int n0, int l16) {
+    return __builtin_bit_cast(F4<uint16_t>, tr_read(t, ld, k0, n0, l16));
+}
+
+__device__ __forceinline__ F4<float> frag4_col(const float* t, int ld, int k0, int n0, int l16) {
+    F4<float> f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f.x[e] = t[(k0 + e) * ld + n0 + l16];
+    return f;
+}
+
+// One 16x16 output tile step over 16 values of the contraction index: lane l supplies
+// row l % 16 of A and column l % 16 of B with the four slots of lane group l / 16
+// (contraction index 4 (l / 16) + slot); the accumulator layout is mma's.  bf16: one
+// v_mfma_f32_16x16x16_bf16; float: four v_mfma_f32_16x16x4_f32, slot s feeding step s.
+__device__ __forceinline__ f32x4_t mma4(const F4<uint16_t>& a, const F4<uint16_t>& b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a), __builtin_bit_cast(i16x4_t, b),
+                                                     c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t mma4(const F4<float>& a, const F4<float>& b, f32x4_t c) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x[s], b.x[s], c, 0, 0, 0);
+    return c;
 }
 
 // Sum over the 16 lanes of a lane group (the columns of an accumulator row), every lane
@@ -180,27 +226,63 @@ __device__ __forceinline__ float sum16(float x) {
     return x;
 }
 
+// Column 0 plus column 1 of an accumulator row, in lanes l16 = 0 and 1 (the high and low
+// parts of a split value).
+__device__ __forceinline__ float pair01(float x) { return x + dpp_move<0xB1>(x); }
+
+// Sum over the four lane groups (every lane getting the sum for its l16).
+__device__ __forceinline__ float sum_groups(float x) {
+    x += __shfl_xor(x, 16, kWave);
+    x += __shfl_xor(x, 32, kWave);
+    return x;
+}
+
 // The derivative of elu + 1 from its value: phi'(x) = 1 above zero, where phi(x) = x + 1 > 1,
 // and exp(x) = phi(x) at or below zero, so phi'(x) = min(phi(x), 1).  Taken from the staged
 // features (in the input precision), it adds one rounding of the size of the output's own.
 __device__ __forceinline__ float dphi_of(float f) { return fminf(f, 1.0f); }
+
+template <typename E>
+__device__ __forceinline__ F4<E> pack4(const f32x4_t& c) {
+    F4<E> f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) f.x[r] = Elem<E>::from_f32(c[r]);
+    return f;
+}
+
+// A 16-byte pad group holding x split as (high, low) in operand precision, then zeros.
+template <typename E>
+__device__ __forceinline__ f32x4_t split_pad(float x) {
+    using X = Elem<E>;
+    F8<E> o{};
+    constexpr int EPG = 16 / int(sizeof(E));
+    E h = X::from_f32(x);
+    E lo = X::from_f32(x - X::to_f32(h));
+    if constexpr (EPG == 8) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o.x[e] = E(0);
+        o.x[0] = h;
+        o.x[1] = lo;
+        return __builtin_bit_cast(f32x4_t, o);
+    } else {
+        return f32x4_t{X::to_f32(h), X::to_f32(lo), 0.0f, 0.0f};
+    }
+}
 
 // The per-workgroup machinery shared by both gradient kernels.
 template <typename E, int D, int DV, bool GATED>
 struct BwdChunk {
     using Sh = BwdShape<E, D, DV>;
     using X = Elem<E>;
-    static constexpr int C = Sh::C, LQ = Sh::LQ, LV = Sh::LV, LA = Sh::LA;
-    static constexpr int GQ = D * int(sizeof(E)) / 16;    // 16-byte groups per q/k row
-    static constexpr int GV = DV * int(sizeof(E)) / 16;   // per v row
-    static constexpr int EPG = 16 / int(sizeof(E));       // elements per group
+    static constexpr int C = Sh::C, LQ = Sh::LQ, LV = Sh::LV;
+    static constexpr int EPG = 16 / int(sizeof(E));       // elements per 16-byte group
+    static constexpr int KZ = D / 64;                      // 16-row z tiles per wave (tiles w, w + 4, ...)
 
     E* sQ;
     E* sK;
     E* sV;
     E* sDn;
     E* sS;
-    E* sA;
     float* sLam;
     float* sDd;
     float* sInv;
@@ -216,7 +298,6 @@ struct BwdChunk {
         sV = reinterpret_cast<E*>(smem + Sh::kOffV);
         sDn = reinterpret_cast<E*>(smem + Sh::kOffDn);
         sS = reinterpret_cast<E*>(smem + Sh::kOffS);
-        sA = reinterpret_cast<E*>(smem + Sh::kOffA);
         sLam = reinterpret_cast<float*>(smem + Sh::kOffLam);
         sDd = reinterpret_cast<float*>(smem + Sh::kOffDd);
         sInv = reinterpret_cast<float*>(smem + Sh::kOffInv);
@@ -293,17 +374,9 @@ struct BwdChunk {
         }
     }
 
-    // The chunk's valid rows of a row-major tile out to a [N][W] tensor, 16 bytes at a time.
-    template <int W>
-    __device__ __forceinline__ void store_out(E* dst, const E* tile, int ld) const {
-        constexpr int G = W * int(sizeof(E)) / 16;
-#pragma unroll
-        for (int u = 0; u < kRowUnits<W>; ++u) {
-            const int idx = tid + u * kThreads, row = idx / G, col = (idx % G) * EPG;
-            if (row < nrows)
-                *reinterpret_cast<f32x4_t*>(dst + size_t(ts + row) * W + col) =
-                    *reinterpret_cast<const f32x4_t*>(tile + row * ld + col);
-        }
+    // The pad group of row `row` of a tile with `ld` = width + PAD.
+    __device__ __forceinline__ f32x4_t* pad_of(E* tile, int ld, int width, int row) const {
+        return reinterpret_cast<f32x4_t*>(tile + row * ld + width);
     }
 
     // A state slot in accumulator layout: D * Dv / 4 16-byte pieces per workgroup.
@@ -346,6 +419,26 @@ struct BwdChunk {
         for (int u = 0; u < kStateUnits; ++u) *reinterpret_cast<f32x4_t*>(slot + 4 * (tid + u * kThreads)) = r[u];
     }
 
+    // A [D] vector in the z-holder lanes: lane l16 = 0 of group g4 in wave w holds entries
+    // 16 (w + 4 t) + 4 g4 + r of tile t < KZ (zero elsewhere).
+    __device__ __forceinline__ void load_zvec(float (&z)[KZ][4], const float* src) const {
+#pragma unroll
+        for (int t = 0; t < KZ; ++t) {
+            const f32x4_t v = (src && l16 == 0) ? *reinterpret_cast<const f32x4_t*>(src + 16 * (w + 4 * t) + 4 * g4)
+                                                : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) z[t][r] = v[r];
+        }
+    }
+
+    __device__ __forceinline__ void put_zvec(float* dst, const float (&z)[KZ][4]) const {
+        if (l16 == 0) {
+#pragma unroll
+            for (int t = 0; t < KZ; ++t)
+                *reinterpret_cast<f32x4_t*>(dst + 16 * (w + 4 * t) + 4 * g4) = f32x4_t{z[t][0], z[t][1], z[t][2], z[t][3]};
+        }
+    }
+
     // One 16x16 state tile, contraction over the chunk's rows: lhs^T rhs for the tile's
     // rows a and columns b of two row-major tiles (this lane's accumulator piece).
     __device__ __forceinline__ f32x4_t tile_tn(const E* lhs, int ldl, int a, const E* rhs, int ldr, int b) const {
@@ -355,6 +448,48 @@ struct BwdChunk {
             acc = mma(frag_col(lhs, ldl, 32 * ks + 8 * g4, 16 * a, l16), frag_col(rhs, ldr, 32 * ks + 8 * g4, 16 * b, l16),
                       acc);
         return acc;
+    }
+
+    // Rows of dOut scaled by 2^Lambda_i / d_i and their pad groups set to the split
+    // 2^Lambda_i dden_i (sDd holds dden_i, times 2^Lambda_i if DD_DECAYED), for the
+    // chunk's adjoint total; with V, rows scaled by 2^(Lambda_last - Lambda_j) and the pad
+    // to the split factor, for the state step.
+    template <bool WITH_V, bool DD_DECAYED>
+    __device__ __forceinline__ void scale_rows() const {
+        constexpr int G = DV * int(sizeof(E)) / 16 + 1;    // groups per row, pad included
+        const float lam_last = lam(C - 1);
+        for (int idx = tid; idx < C * G; idx += kThreads) {
+            const int row = idx / G, gi = idx % G;
+            const float fl = GATED ? fast_exp2(lam(row)) : 1.0f;
+            if (gi < G - 1) {
+                f32x4_t* p = reinterpret_cast<f32x4_t*>(sDn + row * LV + gi * EPG);
+                *p = scale16(*p, fl * sInv[row]);
+            } else {
+                *pad_of(sDn, LV, DV, row) = split_pad<E>(DD_DECAYED ? sDd[row] : sDd[row] * fl);
+            }
+            if constexpr (WITH_V && GATED) {
+                const float fv = fast_exp2(fminf(lam_last - lam(row), 0.0f));
+                if (gi < G - 1) {
+                    f32x4_t* p = reinterpret_cast<f32x4_t*>(sV + row * LV + gi * EPG);
+                    *p = scale16(*p, fv);
+                } else {
+                    *pad_of(sV, LV, DV, row) = split_pad<E>(row < nrows ? fv : 0.0f);
+                }
+            }
+        }
+    }
+
+    static __device__ __forceinline__ f32x4_t scale16(f32x4_t v, float f) {
+        if constexpr (sizeof(E) == 2) {
+            F8<E> x = __builtin_bit_cast(F8<E>, v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x.x[e] = X::from_f32(X::to_f32(x.x[e]) * f);
+            return __builtin_bit_cast(f32x4_t, x);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] *= f;
+            return v;
+        }
     }
 
     // The gate of row `lane` of the chunk starting at ts_ (rows clamped), for stage_lambda.
@@ -383,7 +518,19 @@ struct BwdChunk {
         if constexpr (GATED) return sLam[i];
         return 0.0f;
     }
+
+    // Lambda of rows i .. i + 3 (i a multiple of 4).
+    __device__ __forceinline__ f32x4_t lam4(int i) const {
+        if constexpr (GATED) return *reinterpret_cast<const f32x4_t*>(sLam + i);
+        return f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
 };
+
+// Four consecutive elements out to memory (8 bytes bf16, 16 bytes fp32).
+template <typename E>
+__device__ __forceinline__ void store4(E* p, const f32x4_t& v) {
+    *reinterpret_cast<F4<E>*>(p) = pack4<E>(v);
+}
 
 // ----------------------------------------------------------------- dq pass ----
 
@@ -393,31 +540,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BwdSha
 void bwd_dq_kernel(BwdArgs args) {
     using B = BwdChunk<E, D, DV, GATED>;
     using X = Elem<E>;
-    constexpr int C = B::C, LQ = B::LQ, LV = B::LV, LA = B::LA;
+    constexpr int C = B::C, LQ = B::LQ, LV = B::LV, KZ = B::KZ;
     constexpr int ND = D / 16, NE = DV / 16, NJ = C / 16;
-    constexpr int kParts = kThreads / D, kRowsPer = C / kParts;   // column sums: threads per column, rows each
     extern __shared__ __align__(16) unsigned char smem[];
     B ck;
     ck.init(smem, args.N, args.NC, args.LC);
     const int w = ck.w, bh = ck.bh;
-    const int N = args.N, NC = args.NC;
+    const int N = args.N;
     const E* qb = reinterpret_cast<const E*>(args.q) + size_t(bh) * N * D;
     const E* kb = reinterpret_cast<const E*>(args.k) + size_t(bh) * N * D;
     const E* vb = reinterpret_cast<const E*>(args.v) + size_t(bh) * N * DV;
     const E* dob = reinterpret_cast<const E*>(args.dout) + size_t(bh) * N * DV;
+    E* dqb = reinterpret_cast<E*>(args.dq) + size_t(bh) * N * D;
 
     // The state in front of the current chunk, carried through the run in fp32 (this
-    // thread's accumulator-layout pieces, z_prev[tid] for tid < D): from the scanned slot
+    // thread's accumulator-layout pieces; z in the z-holder lanes): from the scanned slot
     // in front of the run, or S0 / z0 for the first run.
     f32x4_t sacc[B::kStateUnits];
-    float zacc = 0.0f;
+    float zv[KZ][4];
     if (ck.run > 0) {
         const size_t fslot = size_t(bh) * args.NR + (ck.run - 1);
         ck.load_slot(sacc, args.fst + fslot * (D * DV));
-        if (ck.tid < D) zacc = args.fzt[fslot * D + ck.tid];
+        ck.load_zvec(zv, args.fzt + fslot * D);
     } else {
         ck.load_user(sacc, args.s0 ? args.s0 + size_t(bh) * D * DV : nullptr);
-        if (ck.tid < D && args.z0) zacc = args.z0[size_t(bh) * D + ck.tid];
+        ck.load_zvec(zv, args.z0 ? args.z0 + size_t(bh) * D : nullptr);
     }
     // The run's adjoint total (what its queries pass to the state in front of it): the sum
     // over its chunks of the chunk's adjoint total times the decay from the run's start to
@@ -425,7 +572,8 @@ void bwd_dq_kernel(BwdArgs args) {
     f32x4_t racc[B::kStateUnits];
 #pragma unroll
     for (int u = 0; u < B::kStateUnits; ++u) racc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float rzacc = 0.0f, logp = 0.0f;
+    float rzv[KZ][4] = {};
+    float logp = 0.0f;
 
     // staging registers, loaded one chunk ahead of the products
     f32x4_t sq[B::template kRowUnits<D>], sk[B::template kRowUnits<D>];
@@ -451,150 +599,183 @@ void bwd_dq_kernel(BwdArgs args) {
     ck.template store_rows<DV, false>(ck.sV, LV, sv);
     ck.template store_rows<DV, false>(ck.sDn, LV, so);
     ck.store_slot(sacc);
-    if (ck.tid < D) ck.sZ[ck.tid] = zacc;
+    if (l16 == 0) {
+        // z_prev into sZ and, split, into the state's pad columns (den's z part)
+#pragma unroll
+        for (int t = 0; t < KZ; ++t) {
+            const int d0 = 16 * (w + 4 * t) + 4 * g4;
+            *reinterpret_cast<f32x4_t*>(ck.sZ + d0) = f32x4_t{zv[t][0], zv[t][1], zv[t][2], zv[t][3]};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) *ck.pad_of(ck.sS, LV, DV, d0 + r) = split_pad<E>(zv[t][r]);
+        }
+    }
+    if (ck.tid < C) {
+        // V's pad: a column of ones (the row sums of A come out of A V), then zeros
+        *ck.pad_of(ck.sV, LV, DV, ck.tid) = split_pad<E>(ck.tid < ck.nrows ? 1.0f : 0.0f);
+    }
     ck.stage_lambda(sg);
     __syncthreads();
     if (B::Sh::kAhead && c + 1 < ck.c_end) issue(c + 1);
 
-    const int i0 = 16 * w;            // this wave's query rows
-    float lam_r[4], rs[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) lam_r[r] = ck.lam(i0 + 4 * g4 + r);
+    // This lane's query row of the wave's transposed tiles, and its decay.
+    const int i0 = 16 * w, il = i0 + l16;
+    const float lam_i = ck.lam(il), f_i = GATED ? fast_exp2(lam_i) : 1.0f;
 
-    // A = Fq Fk^T, decayed and masked, into sA (rows of this wave); row sums in fp32.
-    // acc keeps the undecayed fp32 scores for the pair sums of d log g.
-    f32x4_t acc[NJ];
-    {
+    // A, transposed: lane (l16, g4) holds query il against keys 16 jt + 4 g4 + r.  sc keeps
+    // the undecayed fp32 scores for the pair sums of d log g.
+    f32x4_t sc[NJ];
+    F4<E> pa[NJ];
 #pragma unroll
-        for (int jt = 0; jt < NJ; ++jt) acc[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) {
-            const F8<E> a = frag_row(ck.sQ, LQ, i0 + l16, 32 * ks + 8 * g4);
-#pragma unroll
-            for (int jt = 0; jt < NJ; ++jt)
-                if (jt <= w) acc[jt] = mma(a, frag_row(ck.sK, LQ, 16 * jt + l16, 32 * ks + 8 * g4), acc[jt]);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) rs[r] = 0.0f;
-#pragma unroll
-        for (int jt = 0; jt < NJ; ++jt) {
-            const int j = 16 * jt + l16;
-            const float lj = ck.lam(j);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = i0 + 4 * g4 + r;
-                float x = (jt <= w && j <= i) ? acc[jt][r] : 0.0f;
-                if constexpr (GATED) x *= fast_exp2(fminf(lam_r[r] - lj, 0.0f));
-                const E xe = X::from_f32(x);
-                ck.sA[i * LA + j] = xe;
-                rs[r] += X::to_f32(xe);          // the row sum of the values the numerator uses
-            }
-        }
-    }
-    // den = 2^Lambda_i Fq_i . z_prev + sum_j A_ij
-    float den[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int i = i0 + 4 * g4 + r;
-        float zt = 0.0f;
-#pragma unroll
-        for (int t = 0; t < ND; ++t) zt += X::to_f32(ck.sQ[i * LQ + 16 * t + l16]) * ck.sZ[16 * t + l16];
-        den[r] = sum16(rs[r] + (GATED ? fast_exp2(lam_r[r]) : 1.0f) * zt);
-    }
-    __syncthreads();
-
-    // num = 2^Lambda_i Fq S_prev + A V
-    f32x4_t num[NE];
-#pragma unroll
-    for (int et = 0; et < NE; ++et) num[et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int jt = 0; jt < NJ; ++jt) sc[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
-        const F8<E> a = frag_row(ck.sQ, LQ, i0 + l16, 32 * ks + 8 * g4);
+        const F8<E> bq = frag_row(ck.sQ, LQ, il, 32 * ks + 8 * g4);
 #pragma unroll
-        for (int et = 0; et < NE; ++et) num[et] = mma(a, frag_col(ck.sS, LV, 32 * ks + 8 * g4, 16 * et, l16), num[et]);
+        for (int jt = 0; jt < NJ; ++jt)
+            if (jt <= w) sc[jt] = mma(frag_row(ck.sK, LQ, 16 * jt + l16, 32 * ks + 8 * g4), bq, sc[jt]);
+    }
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt) {
+        const f32x4_t lj = ck.lam4(16 * jt + 4 * g4);
+        f32x4_t x;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = 16 * jt + 4 * g4 + r;
+            x[r] = (jt <= w && j <= il) ? sc[jt][r] : 0.0f;
+            if constexpr (GATED) x[r] *= fast_exp2(fminf(lam_i - lj[r], 0.0f));
+        }
+        pa[jt] = pack4<E>(x);
+    }
+
+    // num^T[e][i] = 2^Lambda_i (S^T Fq^T)[e][i] + (V^T A^T)[e][i], with one extra block of
+    // rows e = Dv, Dv + 1 holding den's parts (S's pad: z split; V's pad: 1, 0)
+    f32x4_t nt[NE + 1];
+#pragma unroll
+    for (int et = 0; et <= NE; ++et) nt[et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+        const F8<E> bq = frag_row(ck.sQ, LQ, il, 32 * ks + 8 * g4);
+#pragma unroll
+        for (int et = 0; et <= NE; ++et) nt[et] = mma(frag_col(ck.sS, LV, 32 * ks + 8 * g4, 16 * et, l16), bq, nt[et]);
     }
     if constexpr (GATED) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float f = fast_exp2(lam_r[r]);
+        for (int et = 0; et <= NE; ++et)
 #pragma unroll
-            for (int et = 0; et < NE; ++et) num[et][r] *= f;
+            for (int r = 0; r < 4; ++r) nt[et][r] *= f_i;
+    }
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt)
+        if (jt <= w) {
+#pragma unroll
+            for (int et = 0; et <= NE; ++et)
+                nt[et] = mma4(frag4_col(ck.sV, LV, 16 * jt + 4 * g4, 16 * et, l16), pa[jt], nt[et]);
+        }
+
+    // den (in lanes g4 = 0: rows Dv and Dv + 1 of the extra block), 1/d and
+    // dden = -(dout . num) / d^2 in fp32; dnum = dout / d stays implicit
+    const float den = __shfl(nt[NE][0] + nt[NE][1], l16, kWave);
+    const float inv = args.normalize ? 1.0f / fmaxf(den, args.eps) : 1.0f;
+    float dd;
+    {
+        float dsum = 0.0f;
+#pragma unroll
+        for (int et = 0; et < NE; ++et) {
+            const F4<E> o4 = lds_f4(ck.sDn + il * LV + 16 * et + 4 * g4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dsum += X::to_f32(o4.x[r]) * nt[et][r];
+        }
+        dsum = sum_groups(dsum);
+        dd = (args.normalize && den >= args.eps) ? -dsum * inv * inv : 0.0f;
+        if (g4 == 0) {
+            if (ts + il < N) {
+                args.dden[size_t(bh) * N + ts + il] = dd;
+                args.inv[size_t(bh) * N + ts + il] = inv;
+            }
+            ck.sInv[il] = inv;
+            ck.sDd[il] = dd * f_i;
         }
     }
-    for (int ks = 0; ks <= (w >> 1); ++ks) {
-        const F8<E> a = frag_row(ck.sA, LA, i0 + l16, 32 * ks + 8 * g4);
-#pragma unroll
-        for (int et = 0; et < NE; ++et) num[et] = mma(a, frag_col(ck.sV, LV, 32 * ks + 8 * g4, 16 * et, l16), num[et]);
-    }
 
-    // 1/d and dden = -(dout . num) / d^2 (fp32); dnum = dout / d stays implicit
-    float dd[4], inv[4];
-    {
-        float dsum[4] = {0.f, 0.f, 0.f, 0.f};
+    // B, transposed like A: ((dout_i . v_j) / d_i + dden_i) decayed and masked; with it the
+    // pair terms P_ij = (Fq_i . Fk_j) B_ij in fp32, summed by row (j < i) and by column
+    F4<E> pb[NJ];
+    float prow = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) inv[r] = args.normalize ? 1.0f / fmaxf(den[r], args.eps) : 1.0f;
+    for (int jt = 0; jt < NJ; ++jt) {
+        f32x4_t bt = {0.f, 0.f, 0.f, 0.f};
+        if (jt <= w) {
 #pragma unroll
-        for (int et = 0; et < NE; ++et)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                dsum[r] += X::to_f32(ck.sDn[(i0 + 4 * g4 + r) * LV + 16 * et + l16]) * num[et][r];
+            for (int ks = 0; ks < DV / 32; ++ks)
+                bt = mma(frag_row(ck.sV, LV, 16 * jt + l16, 32 * ks + 8 * g4), frag_row(ck.sDn, LV, il, 32 * ks + 8 * g4),
+                         bt);
+        }
+        const f32x4_t lj = ck.lam4(16 * jt + 4 * g4);
+        f32x4_t x, pc;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float s = sum16(dsum[r]);
-            const int i = i0 + 4 * g4 + r;
-            dd[r] = (args.normalize && den[r] >= args.eps) ? -s * inv[r] * inv[r] : 0.0f;
-            if (l16 == 0 && ts + i < N) {
-                args.dden[size_t(bh) * N + ts + i] = dd[r];
-                args.inv[size_t(bh) * N + ts + i] = inv[r];
+            const int j = 16 * jt + 4 * g4 + r;
+            x[r] = (jt <= w && j <= il) ? bt[r] * inv + dd : 0.0f;
+            if constexpr (GATED) {
+                x[r] *= fast_exp2(fminf(lam_i - lj[r], 0.0f));
+                const float p = (jt <= w && j < il) ? sc[jt][r] * x[r] : 0.0f;
+                prow += p;
+                pc[r] = sum16(p);
             }
         }
-    }
-    __syncthreads();
-
-    // B = (diag(1/d) dOut V^T + dden 1^T) o decay o mask over this wave's rows, into sA
-    // (every read of A finished before the barrier above); with it the pair terms
-    // P_ij = (Fq_i . Fk_j) B_ij in fp32, summed by row (j < i) and by column (i > j)
-    {
-        f32x4_t bb[NJ];
-#pragma unroll
-        for (int jt = 0; jt < NJ; ++jt) bb[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < DV / 32; ++ks) {
-            const F8<E> a = frag_row(ck.sDn, LV, i0 + l16, 32 * ks + 8 * g4);
-#pragma unroll
-            for (int jt = 0; jt < NJ; ++jt)
-                if (jt <= w) bb[jt] = mma(a, frag_row(ck.sV, LV, 16 * jt + l16, 32 * ks + 8 * g4), bb[jt]);
+        pb[jt] = pack4<E>(x);
+        if constexpr (GATED) {
+            if (l16 == 0) *reinterpret_cast<f32x4_t*>(ck.sCol + w * C + 16 * jt + 4 * g4) = pc;
         }
-        float prow[4] = {0.f, 0.f, 0.f, 0.f};
+    }
+    if constexpr (GATED) {
+        prow = sum_groups(prow);
+        if (g4 == 0) ck.sRow[il] = prow;
+    }
+
+    // dFq^T[d][i] = 2^Lambda_i ((S dOut^T)[d][i] / d_i + z_d dden_i) + (Fk^T B^T)[d][i]
+    f32x4_t ft[ND];
 #pragma unroll
-        for (int jt = 0; jt < NJ; ++jt) {
-            const int j = 16 * jt + l16;
-            const float lj = ck.lam(j);
-            float pcol = 0.0f;
+    for (int dt = 0; dt < ND; ++dt) {
+        ft[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < DV / 32; ++ks)
+            ft[dt] = mma(frag_row(ck.sS, LV, 16 * dt + l16, 32 * ks + 8 * g4), frag_row(ck.sDn, LV, il, 32 * ks + 8 * g4),
+                         ft[dt]);
+    }
+    {
+        float yq = 0.0f;                              // Fq_i . (carried-state part of dFq_i)
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) {
+            const f32x4_t z4 = *reinterpret_cast<const f32x4_t*>(ck.sZ + 16 * dt + 4 * g4);
+            const F4<E> q4 = lds_f4(ck.sQ + il * LQ + 16 * dt + 4 * g4);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int i = i0 + 4 * g4 + r;
-                float x = (jt <= w && j <= i) ? bb[jt][r] * inv[r] + dd[r] : 0.0f;
-                if constexpr (GATED) x *= fast_exp2(fminf(lam_r[r] - lj, 0.0f));
-                ck.sA[i * LA + j] = X::from_f32(x);
-                if constexpr (GATED) {
-                    const float pij = j < i ? acc[jt][r] * x : 0.0f;
-                    prow[r] += pij;
-                    pcol += pij;
-                }
-            }
-            if constexpr (GATED) {
-                pcol += __shfl_xor(pcol, 16, kWave);
-                pcol += __shfl_xor(pcol, 32, kWave);
-                if (g4 == 0) ck.sCol[w * C + j] = pcol;
+                ft[dt][r] = (ft[dt][r] * inv + dd * z4[r]) * f_i;
+                if constexpr (GATED) yq += X::to_f32(q4.x[r]) * ft[dt][r];
             }
         }
         if constexpr (GATED) {
+            yq = sum_groups(yq);
+            if (g4 == 0 && ts + il < N) args.yq[size_t(bh) * N + ts + il] = yq;
+        }
+    }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float sr = sum16(prow[r]);
-                if (l16 == 0) ck.sRow[i0 + 4 * g4 + r] = sr;
-            }
+    for (int jt = 0; jt < NJ; ++jt)
+        if (jt <= w) {
+#pragma unroll
+            for (int dt = 0; dt < ND; ++dt)
+                ft[dt] = mma4(frag4_col(ck.sK, LQ, 16 * jt + 4 * g4, 16 * dt, l16), pb[jt], ft[dt]);
+        }
+    // dq = dFq * phi'(q): four consecutive columns of row il per lane
+    if (ts + il < N) {
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) {
+            const F4<E> q4 = lds_f4(ck.sQ + il * LQ + 16 * dt + 4 * g4);
+            f32x4_t o;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] = ft[dt][r] * dphi_of(X::to_f32(q4.x[r]));
+            store4<E>(dqb + size_t(ts + il) * D + 16 * dt + 4 * g4, o);
         }
     }
     __syncthreads();
@@ -610,74 +791,16 @@ void bwd_dq_kernel(BwdArgs args) {
         }
         if (lane < ck.nrows) args.xs[size_t(bh) * N + ts + lane] = x - dm;
     }
-
-    // dFq = 2^Lambda_i (diag(1/d) dOut S_prev^T + dden z_prev^T) + B Fk
-    f32x4_t dfq[ND];
-#pragma unroll
-    for (int dt = 0; dt < ND; ++dt) dfq[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < DV / 32; ++ks) {
-        const F8<E> a = frag_row(ck.sDn, LV, i0 + l16, 32 * ks + 8 * g4);
-#pragma unroll
-        for (int dt = 0; dt < ND; ++dt) dfq[dt] = mma(a, frag_row(ck.sS, LV, 16 * dt + l16, 32 * ks + 8 * g4), dfq[dt]);
-    }
-    {
-        float yq[4] = {0.f, 0.f, 0.f, 0.f};            // Fq_i . (carried-state part of dFq_i)
-#pragma unroll
-        for (int dt = 0; dt < ND; ++dt) {
-            const float zd = ck.sZ[16 * dt + l16];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float x = dfq[dt][r] * inv[r] + dd[r] * zd;
-                dfq[dt][r] = GATED ? x * fast_exp2(lam_r[r]) : x;
-                if constexpr (GATED) yq[r] += X::to_f32(ck.sQ[(i0 + 4 * g4 + r) * LQ + 16 * dt + l16]) * dfq[dt][r];
-            }
-        }
-        if constexpr (GATED) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float s = sum16(yq[r]);
-                const int i = i0 + 4 * g4 + r;
-                if (l16 == 0 && ts + i < N) args.yq[size_t(bh) * N + ts + i] = s;
-            }
-        }
-    }
-    for (int ks = 0; ks <= (w >> 1); ++ks) {
-        const F8<E> a = frag_row(ck.sA, LA, i0 + l16, 32 * ks + 8 * g4);
-#pragma unroll
-        for (int dt = 0; dt < ND; ++dt) dfq[dt] = mma(a, frag_col(ck.sK, LQ, 32 * ks + 8 * g4, 16 * dt, l16), dfq[dt]);
-    }
-
-    // dq = dFq * phi'(q), written to LDS once every read of phi(K) is done
-#pragma unroll
-    for (int dt = 0; dt < ND; ++dt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dfq[dt][r] *= dphi_of(X::to_f32(ck.sQ[(i0 + 4 * g4 + r) * LQ + 16 * dt + l16]));
-
-    // this wave's rows of dOut become 2^Lambda_i dnum_i and its rows of V become
-    // 2^(Lambda_last - Lambda_j) v_j (every other read of both is done)
-    const float lam_last = ck.lam(C - 1);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int i = i0 + 4 * g4 + r;
-        const float f = GATED ? fast_exp2(lam_r[r]) : 1.0f;
-        const float fv = GATED ? fast_exp2(fminf(lam_last - lam_r[r], 0.0f)) : 1.0f;
-#pragma unroll
-        for (int et = 0; et < NE; ++et) {
-            E& x = ck.sDn[i * LV + 16 * et + l16];
-            x = X::from_f32(X::to_f32(x) * (f * inv[r]));
-            if constexpr (GATED) {
-                E& y = ck.sV[i * LV + 16 * et + l16];
-                y = X::from_f32(X::to_f32(y) * fv);
-            }
-        }
-        if (l16 == 0) ck.sDd[i] = dd[r] * f;
-    }
+    // rows of dOut become 2^Lambda_i dnum_i (pad: 2^Lambda_i dden_i split), rows of V
+    // 2^(Lambda_last - Lambda_j) v_j (pad: the factor split, for z's step)
+    ck.template scale_rows<true, true>();
     __syncthreads();
     // The chunk's adjoint total dR_c = Fq^T (2^Lambda dNum), dr_c = Fq^T (2^Lambda dden),
     // into the run's with the decay 2^logp from the run's start; and the state carried
     // across the chunk: S <- 2^Lambda_last S + Fk^T (2^(Lambda_last - Lambda_j) V), z alike.
+    // The z parts are the extra column block (pad columns 0 + 1) of the same products.
     {
+        const float lam_last = ck.lam(C - 1);
         const float fp = GATED ? fast_exp2(logp) : 1.0f, fc = GATED ? fast_exp2(lam_last) : 1.0f;
 #pragma unroll
         for (int u = 0; u < B::kStateUnits; ++u) {
@@ -690,49 +813,25 @@ void bwd_dq_kernel(BwdArgs args) {
                 sacc[u][k] = fc * sacc[u][k] + ds[k];
             }
         }
-        // the z parts, Fq^T (2^Lambda dden) and Fk^T 2^(Lambda_last - Lambda_j): every
-        // thread sums a slice of the rows of one column, into sA (free in this phase)
-        float* part = reinterpret_cast<float*>(ck.sA);
-        {
-            const int d = ck.tid % D, i0p = (ck.tid / D) * kRowsPer;
-            float sr = 0.0f, sz = 0.0f;
 #pragma unroll
-            for (int ii = 0; ii < kRowsPer; ++ii) {
-                const int i = i0p + ii;
-                sr += X::to_f32(ck.sQ[i * LQ + d]) * ck.sDd[i];
-                const float fk = X::to_f32(ck.sK[i * LQ + d]);
-                sz += GATED ? fk * fast_exp2(fminf(lam_last - ck.lam(i), 0.0f)) : fk;
-            }
-            part[ck.tid] = sr;
-            part[kThreads + ck.tid] = sz;
-        }
-        __syncthreads();
-        if (ck.tid < D) {
-            float sr = 0.0f, sz = 0.0f;
+        for (int t = 0; t < KZ; ++t) {
+            const f32x4_t dr = ck.tile_tn(ck.sQ, LQ, w + 4 * t, ck.sDn, LV, NE);
+            const f32x4_t ds = ck.tile_tn(ck.sK, LQ, w + 4 * t, ck.sV, LV, NE);
 #pragma unroll
-            for (int p = 0; p < kParts; ++p) {
-                sr += part[p * D + ck.tid];
-                sz += part[kThreads + p * D + ck.tid];
+            for (int r = 0; r < 4; ++r) {
+                rzv[t][r] += fp * pair01(dr[r]);
+                zv[t][r] = fc * zv[t][r] + pair01(ds[r]);
             }
-            rzacc += fp * sr;
-            zacc = fc * zacc + sz;
         }
         logp += lam_last;
     }
-    // phi(K) is no longer read: it takes dq for the coalesced store
-#pragma unroll
-    for (int dt = 0; dt < ND; ++dt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ck.sK[(i0 + 4 * g4 + r) * LQ + 16 * dt + l16] = X::from_f32(dfq[dt][r]);
-    __syncthreads();
-    ck.template store_out<D>(reinterpret_cast<E*>(args.dq) + size_t(bh) * N * D, ck.sK, LQ);
     __syncthreads();                  // every read of this chunk's tiles is done
     }
 
     // the run's adjoint total at its reversed slot
     const size_t rslot = size_t(bh) * (args.NR + 1) + (args.NR - 1 - ck.run);
     ck.put_slot(args.rst + rslot * (D * DV), racc);
-    if (ck.tid < D) args.rzt[rslot * D + ck.tid] = rzacc;
+    ck.put_zvec(args.rzt + rslot * D, rzv);
     if (GATED && ck.tid == 0) args.rlg[rslot] = logp;
 }
 
@@ -744,9 +843,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BwdSha
 void bwd_dkv_kernel(BwdArgs args) {
     using B = BwdChunk<E, D, DV, GATED>;
     using X = Elem<E>;
-    constexpr int C = B::C, LQ = B::LQ, LV = B::LV, LA = B::LA;
+    constexpr int C = B::C, LQ = B::LQ, LV = B::LV, KZ = B::KZ;
     constexpr int ND = D / 16, NE = DV / 16, NI = C / 16;
-    constexpr int kParts = kThreads / D, kRowsPer = C / kParts;   // column sums: threads per column, rows each
     extern __shared__ __align__(16) unsigned char smem[];
     B ck;
     ck.init(smem, args.N, args.NC, args.LC);
@@ -756,22 +854,25 @@ void bwd_dkv_kernel(BwdArgs args) {
     const E* kb = reinterpret_cast<const E*>(args.k) + size_t(bh) * N * D;
     const E* vb = reinterpret_cast<const E*>(args.v) + size_t(bh) * N * DV;
     const E* dob = reinterpret_cast<const E*>(args.dout) + size_t(bh) * N * DV;
-    static_assert(D <= kThreads && C <= kThreads, "one thread per state row and per token");
+    E* dkb = reinterpret_cast<E*>(args.dk) + size_t(bh) * N * D;
+    E* dvb = reinterpret_cast<E*>(args.dv) + size_t(bh) * N * DV;
+    static_assert(C <= kThreads, "one thread per token");
 
     // R, r: the adjoint of the state after the current chunk, carried backwards through
-    // the run in fp32 (accumulator-layout pieces, r[tid] for tid < D), from the scanned
-    // slot after the run (zero after the last run).
+    // the run in fp32 (accumulator-layout pieces; r in the z-holder lanes), from the
+    // scanned slot after the run (zero after the last run).
     const bool last_run = ck.run == args.NR - 1;
     f32x4_t racc[B::kStateUnits];
-    float rzacc = 0.0f;
+    float rzv[KZ][4];
+    size_t rsl = 0;
     if (!last_run) {
-        const size_t rsl = size_t(bh) * (args.NR + 1) + (args.NR - 2 - ck.run);
+        rsl = size_t(bh) * (args.NR + 1) + (args.NR - 2 - ck.run);
         ck.load_slot(racc, args.rst + rsl * (D * DV));
-        if (ck.tid < D) rzacc = args.rzt[rsl * D + ck.tid];
     } else {
 #pragma unroll
         for (int u = 0; u < B::kStateUnits; ++u) racc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
+    ck.load_zvec(rzv, last_run ? nullptr : args.rzt + rsl * D);
     // tb: the pairs across the boundary after the current chunk (keys up to it, queries
     // after it), <R, S> + <r, z> with S, z the state after the chunk; at the run's end from
     // the forward slot after the run, then back chunk by chunk (W_c = tb - K_c, and the
@@ -783,11 +884,16 @@ void bwd_dkv_kernel(BwdArgs args) {
             const size_t fsl = size_t(bh) * args.NR + ck.run;
             f32x4_t sf[B::kStateUnits];
             ck.load_slot(sf, args.fst + fsl * (D * DV));
+            float fz[KZ][4];
+            ck.load_zvec(fz, args.fzt + fsl * D);
 #pragma unroll
             for (int u = 0; u < B::kStateUnits; ++u)
 #pragma unroll
                 for (int k = 0; k < 4; ++k) wp += racc[u][k] * sf[u][k];
-            if (ck.tid < D) wp += rzacc * args.fzt[fsl * D + ck.tid];
+#pragma unroll
+            for (int t = 0; t < KZ; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) wp += rzv[t][r] * fz[t][r];
         }
 #pragma unroll
         for (int off = 1; off < kWave; off <<= 1) wp += __shfl_xor(wp, off, kWave);
@@ -832,7 +938,7 @@ void bwd_dkv_kernel(BwdArgs args) {
         ck.sInv[ck.tid] = ck.tid < ck.nrows ? sinv : 0.0f;
     }
     ck.store_slot(racc);
-    if (ck.tid < D) ck.sZ[ck.tid] = rzacc;
+    ck.put_zvec(ck.sZ, rzv);
     if constexpr (GATED) {
         // Y_c = sum of yq over the chunk's queries (wave 0: one lane per token)
         if (ck.w == 0) {
@@ -846,143 +952,148 @@ void bwd_dkv_kernel(BwdArgs args) {
     __syncthreads();
     if (B::Sh::kAhead && c > ck.c_first) issue(c - 1);
 
-    const int j0 = 16 * w;            // this wave's key rows
-    float lam_r[4], tail[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        lam_r[r] = ck.lam(j0 + 4 * g4 + r);
-        tail[r] = GATED ? fast_exp2(fminf(ck.lam(C - 1) - lam_r[r], 0.0f)) : 1.0f;   // 2^(Lambda_last - Lambda_j)
-    }
+    // This lane's key row of the wave's transposed tiles, and its decay to the chunk's end.
+    const int j0 = 16 * w, jl = j0 + l16;
+    const float lam_j = ck.lam(jl);
+    const float tail = GATED ? fast_exp2(fminf(ck.lam(C - 1) - lam_j, 0.0f)) : 1.0f;   // 2^(Lambda_last - Lambda_j)
 
-    // A^T diag(1/d) = Fk Fq^T diag(1/d) and B^T = V dOut^T diag(1/d) + 1 dden^T, both
-    // decayed and masked (i >= j)
-    f32x4_t bt[NI];
+    // A diag(1/d) and B, transposed: lane (l16, g4) holds key jl against queries
+    // 16 it + 4 g4 + r (it >= w), decayed and masked (i >= j):
+    //   pa = (Fq_i . Fk_j) 2^(Lambda_i - Lambda_j) / d_i,  pb = ((dout_i . v_j) / d_i + dden_i) 2^(...)
+    // Each is consumed (and dv stored) before the other is formed, to keep registers low.
+    const bool valid = ts + jl < N;
     {
-        f32x4_t at[NI];
+        F4<E> pa[NI];
 #pragma unroll
         for (int it = 0; it < NI; ++it) {
-            at[it] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            bt[it] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
+            f32x4_t at = {0.f, 0.f, 0.f, 0.f};
+            if (it >= w) {
 #pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) {
-            const F8<E> a = frag_row(ck.sK, LQ, j0 + l16, 32 * ks + 8 * g4);
-#pragma unroll
-            for (int it = 0; it < NI; ++it)
-                if (it >= w) at[it] = mma(a, frag_row(ck.sQ, LQ, 16 * it + l16, 32 * ks + 8 * g4), at[it]);
-        }
-#pragma unroll
-        for (int ks = 0; ks < DV / 32; ++ks) {
-            const F8<E> a = frag_row(ck.sV, LV, j0 + l16, 32 * ks + 8 * g4);
-#pragma unroll
-            for (int it = 0; it < NI; ++it)
-                if (it >= w) bt[it] = mma(a, frag_row(ck.sDn, LV, 16 * it + l16, 32 * ks + 8 * g4), bt[it]);
-        }
-#pragma unroll
-        for (int it = 0; it < NI; ++it) {
-            const int i = 16 * it + l16;
-            const float li = ck.lam(i);
-            const float ddi = ck.sDd[i], invi = ck.sInv[i];
+                for (int ks = 0; ks < D / 32; ++ks)
+                    at = mma(frag_row(ck.sQ, LQ, 16 * it + l16, 32 * ks + 8 * g4), frag_row(ck.sK, LQ, jl, 32 * ks + 8 * g4),
+                             at);
+            }
+            const int i4 = 16 * it + 4 * g4;
+            const f32x4_t li = ck.lam4(i4);
+            const f32x4_t iv = *reinterpret_cast<const f32x4_t*>(ck.sInv + i4);
+            f32x4_t xa;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int j = j0 + 4 * g4 + r;
-                const bool keep = it >= w && i >= j;
-                const float f = GATED ? fast_exp2(fminf(li - lam_r[r], 0.0f)) : 1.0f;
-                ck.sA[j * LA + i] = X::from_f32(keep ? at[it][r] * (f * invi) : 0.0f);
-                bt[it][r] = keep ? (bt[it][r] * invi + ddi) * f : 0.0f;
+                const bool keep = it >= w && i4 + r >= jl;
+                const float f = GATED ? fast_exp2(fminf(li[r] - lam_j, 0.0f)) : 1.0f;
+                xa[r] = keep ? at[r] * (f * iv[r]) : 0.0f;
             }
+            pa[it] = pack4<E>(xa);
         }
-    }
-    __syncthreads();
-
-    // dV = 2^(Lambda_last - Lambda_j) Fk R + (A^T diag(1/d)) dOut
-    f32x4_t dv[NE];
-    {
-#pragma unroll
-        for (int et = 0; et < NE; ++et) dv[et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) {
-            const F8<E> a = frag_row(ck.sK, LQ, j0 + l16, 32 * ks + 8 * g4);
-#pragma unroll
-            for (int et = 0; et < NE; ++et) dv[et] = mma(a, frag_col(ck.sS, LV, 32 * ks + 8 * g4, 16 * et, l16), dv[et]);
-        }
-        if constexpr (GATED) {
-#pragma unroll
-            for (int et = 0; et < NE; ++et)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) dv[et][r] *= tail[r];
-        }
-        for (int ks = w >> 1; ks < C / 32; ++ks) {
-            const F8<E> a = frag_row(ck.sA, LA, j0 + l16, 32 * ks + 8 * g4);
-#pragma unroll
-            for (int et = 0; et < NE; ++et) dv[et] = mma(a, frag_col(ck.sDn, LV, 32 * ks + 8 * g4, 16 * et, l16), dv[et]);
-        }
-    }
-    __syncthreads();
-    // B^T over this wave's rows into sA (every read of A^T finished before the barrier);
-    // dOut, dden are not read again as they are: their rows become 2^Lambda_i dnum_i and
-    // 2^Lambda_i dden_i for the chunk's adjoint total
-#pragma unroll
-    for (int it = 0; it < NI; ++it)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ck.sA[(j0 + 4 * g4 + r) * LA + 16 * it + l16] = X::from_f32(bt[it][r]);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int i = j0 + 4 * g4 + r;
-        const float f = (GATED ? fast_exp2(lam_r[r]) : 1.0f) * ck.sInv[i];
+        // dV^T[e][j] = 2^(Lambda_last - Lambda_j) (R^T Fk^T)[e][j] + (dOut^T (A diag(1/d)))[e][j]
+        f32x4_t dvt[NE];
 #pragma unroll
         for (int et = 0; et < NE; ++et) {
-            E& x = ck.sDn[i * LV + 16 * et + l16];
-            x = X::from_f32(X::to_f32(x) * f);
+            dvt[et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks)
+                dvt[et] = mma(frag_col(ck.sS, LV, 32 * ks + 8 * g4, 16 * et, l16), frag_row(ck.sK, LQ, jl, 32 * ks + 8 * g4),
+                              dvt[et]);
+            if constexpr (GATED) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dvt[et][r] *= tail;
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < NI; ++it)
+            if (it >= w) {
+#pragma unroll
+                for (int et = 0; et < NE; ++et)
+                    dvt[et] = mma4(frag4_col(ck.sDn, LV, 16 * it + 4 * g4, 16 * et, l16), pa[it], dvt[et]);
+            }
+        // dv: four consecutive columns of row jl per lane
+        if (valid) {
+#pragma unroll
+            for (int et = 0; et < NE; ++et) store4<E>(dvb + size_t(ts + jl) * DV + 16 * et + 4 * g4, dvt[et]);
         }
     }
-    if (GATED && ck.tid < C) ck.sDd[ck.tid] *= fast_exp2(ck.lam(ck.tid));
-    __syncthreads();
-
-    // dFk = 2^(Lambda_last - Lambda_j) (V R^T + 1 r^T) + B^T Fq
-    f32x4_t dfk[ND];
+    F4<E> pb[NI];
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt) dfk[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < NI; ++it) {
+        f32x4_t bt = {0.f, 0.f, 0.f, 0.f};
+        if (it >= w) {
 #pragma unroll
-    for (int ks = 0; ks < DV / 32; ++ks) {
-        const F8<E> a = frag_row(ck.sV, LV, j0 + l16, 32 * ks + 8 * g4);
+            for (int ks = 0; ks < DV / 32; ++ks)
+                bt = mma(frag_row(ck.sDn, LV, 16 * it + l16, 32 * ks + 8 * g4), frag_row(ck.sV, LV, jl, 32 * ks + 8 * g4),
+                         bt);
+        }
+        const int i4 = 16 * it + 4 * g4;
+        const f32x4_t li = ck.lam4(i4);
+        const f32x4_t iv = *reinterpret_cast<const f32x4_t*>(ck.sInv + i4);
+        const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(ck.sDd + i4);
+        f32x4_t xb;
 #pragma unroll
-        for (int dt = 0; dt < ND; ++dt) dfk[dt] = mma(a, frag_row(ck.sS, LV, 16 * dt + l16, 32 * ks + 8 * g4), dfk[dt]);
+        for (int r = 0; r < 4; ++r) {
+            const bool keep = it >= w && i4 + r >= jl;
+            const float f = GATED ? fast_exp2(fminf(li[r] - lam_j, 0.0f)) : 1.0f;
+            xb[r] = keep ? (bt[r] * iv[r] + d4[r]) * f : 0.0f;
+        }
+        pb[it] = pack4<E>(xb);
     }
+
+    // dFk^T[d][j] = 2^(Lambda_last - Lambda_j) ((R V^T)[d][j] + r_d) + (Fq^T B)[d][j]
+    f32x4_t fk[ND];
     {
-        float zk[4] = {0.f, 0.f, 0.f, 0.f};            // Fk_j . (carried-state part of dFk_j)
+        float zk = 0.0f;                              // Fk_j . (carried-state part of dFk_j)
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) {
-            const float rd = ck.sZ[16 * dt + l16];
+            fk[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < DV / 32; ++ks)
+                fk[dt] = mma(frag_row(ck.sS, LV, 16 * dt + l16, 32 * ks + 8 * g4), frag_row(ck.sV, LV, jl, 32 * ks + 8 * g4),
+                             fk[dt]);
+            const f32x4_t r4 = *reinterpret_cast<const f32x4_t*>(ck.sZ + 16 * dt + 4 * g4);
+            const F4<E> k4 = lds_f4(ck.sK + jl * LQ + 16 * dt + 4 * g4);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                dfk[dt][r] = (dfk[dt][r] + rd) * tail[r];
-                if constexpr (GATED) zk[r] += X::to_f32(ck.sK[(j0 + 4 * g4 + r) * LQ + 16 * dt + l16]) * dfk[dt][r];
+                fk[dt][r] = (fk[dt][r] + r4[r]) * tail;
+                if constexpr (GATED) zk += X::to_f32(k4.x[r]) * fk[dt][r];
             }
         }
         if constexpr (GATED) {
-            float kw = 0.0f;                           // K_c: this wave's part of sum_j zk_j
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float s = sum16(zk[r]);
-                const int j = j0 + 4 * g4 + r;
-                if (l16 == 0 && ts + j < N) args.zk[size_t(bh) * N + ts + j] = s;
-                kw += s;
-            }
-            kw += __shfl_xor(kw, 16, kWave);
-            kw += __shfl_xor(kw, 32, kWave);
+            zk = sum_groups(zk);
+            if (g4 == 0 && valid) args.zk[size_t(bh) * N + ts + jl] = zk;
+            const float kw = sum16(valid ? zk : 0.0f);     // K_c: this wave's part of sum_j zk_j
             if (lane == 0) ck.sRow[1 + w] = kw;
         }
     }
-    for (int ks = w >> 1; ks < C / 32; ++ks) {
-        const F8<E> a = frag_row(ck.sA, LA, j0 + l16, 32 * ks + 8 * g4);
 #pragma unroll
-        for (int dt = 0; dt < ND; ++dt) dfk[dt] = mma(a, frag_col(ck.sQ, LQ, 32 * ks + 8 * g4, 16 * dt, l16), dfk[dt]);
+    for (int it = 0; it < NI; ++it)
+        if (it >= w) {
+#pragma unroll
+            for (int dt = 0; dt < ND; ++dt)
+                fk[dt] = mma4(frag4_col(ck.sQ, LQ, 16 * it + 4 * g4, 16 * dt, l16), pb[it], fk[dt]);
+        }
+    // dk = dFk * phi'(k): four consecutive columns of row jl per lane
+    if (valid) {
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) {
+            const F4<E> k4 = lds_f4(ck.sK + jl * LQ + 16 * dt + 4 * g4);
+            f32x4_t o;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] = fk[dt][r] * dphi_of(X::to_f32(k4.x[r]));
+            store4<E>(dkb + size_t(ts + jl) * D + 16 * dt + 4 * g4, o);
+        }
     }
+    __syncthreads();
+    if constexpr (GATED) {
+        // W_c = tb - K_c: keys in front of the chunk against queries after it
+        const float wcv = tb - (ck.sRow[1] + ck.sRow[2] + ck.sRow[3] + ck.sRow[4]);
+        if (ck.tid == 0) args.wc[size_t(bh) * NC + c] = wcv;
+        tb = wcv + ck.sRow[0];
+    }
+    // rows of dOut become 2^Lambda_i dnum_i (pad: 2^Lambda_i dden_i split)
+    ck.template scale_rows<false, false>();
+    __syncthreads();
     // the adjoint carried across the chunk: R <- 2^Lambda_last R + Fq^T (2^Lambda dNum),
-    // r <- 2^Lambda_last r + Fq^T (2^Lambda dden)
-    const float fc = GATED ? fast_exp2(ck.lam(C - 1)) : 1.0f;
+    // r <- 2^Lambda_last r + Fq^T (2^Lambda dden) (the extra column block)
     {
+        const float fc = GATED ? fast_exp2(ck.lam(C - 1)) : 1.0f;
 #pragma unroll
         for (int u = 0; u < B::kStateUnits; ++u) {
             const int t = w + 4 * u, a = t / NE, b = t % NE;
@@ -990,43 +1101,13 @@ void bwd_dkv_kernel(BwdArgs args) {
 #pragma unroll
             for (int k = 0; k < 4; ++k) racc[u][k] = fc * racc[u][k] + dr[k];
         }
-        // the z part Fq^T (2^Lambda dden): every thread sums a slice of the rows of one
-        // column, into sCol
-        const int d = ck.tid % D, i0p = (ck.tid / D) * kRowsPer;
-        float sr = 0.0f;
 #pragma unroll
-        for (int ii = 0; ii < kRowsPer; ++ii) sr += X::to_f32(ck.sQ[(i0p + ii) * LQ + d]) * ck.sDd[i0p + ii];
-        ck.sCol[ck.tid] = sr;
-    }
-    // dk = dFk * phi'(k) and dv through the now free phi(K) and V tiles, stored coalesced
-    __syncthreads();
-    if (ck.tid < D) {
-        float sr = 0.0f;
+        for (int t = 0; t < KZ; ++t) {
+            const f32x4_t dr = ck.tile_tn(ck.sQ, LQ, w + 4 * t, ck.sDn, LV, NE);
 #pragma unroll
-        for (int p = 0; p < kParts; ++p) sr += ck.sCol[p * D + ck.tid];
-        rzacc = fc * rzacc + sr;
-    }
-    if constexpr (GATED) {
-        // W_c = tb - K_c: keys in front of the chunk against queries after it
-        const float wcv = tb - (ck.sRow[1] + ck.sRow[2] + ck.sRow[3] + ck.sRow[4]);
-        if (ck.tid == 0) args.wc[size_t(bh) * NC + c] = wcv;
-        tb = wcv + ck.sRow[0];
-    }
-#pragma unroll
-    for (int dt = 0; dt < ND; ++dt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-        {
-            E& x = ck.sK[(j0 + 4 * g4 + r) * LQ + 16 * dt + l16];      // phi(k), read before it takes dk
-            x = X::from_f32(dfk[dt][r] * dphi_of(X::to_f32(x)));
+            for (int r = 0; r < 4; ++r) rzv[t][r] = fc * rzv[t][r] + pair01(dr[r]);
         }
-#pragma unroll
-    for (int et = 0; et < NE; ++et)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ck.sV[(j0 + 4 * g4 + r) * LV + 16 * et + l16] = X::from_f32(dv[et][r]);
-    __syncthreads();
-    ck.template store_out<D>(reinterpret_cast<E*>(args.dk) + size_t(bh) * N * D, ck.sK, LQ);
-    ck.template store_out<DV>(reinterpret_cast<E*>(args.dv) + size_t(bh) * N * DV, ck.sV, LV);
+    }
     __syncthreads();                  // every read of this chunk's tiles is done
     }
 }

@@ -72,25 +72,29 @@ inline size_t fwd_workspace_layout(size_t slots, int D, int Dv, size_t* off_zt, 
 // and small (at most seven 64 x 64 states); otherwise a scan launch does it first.
 inline bool prefix_direct(int nseg, int D, int Dv) { return size_t(nseg - 1) * D * Dv <= size_t(7) * 64 * 64; }
 
-// Dynamic LDS bytes of a gradient kernel: phi(Q), phi(K) [C][D], V, dOut [C][Dv], one
-// state [D][Dv] and one [C][C] score tile, each row padded by 16 bytes, plus the chunk's
-// decays, dden, 1/d, the column and row sums of its pair terms and one fp32 [D] vector.  BwdShape<...>::kBytes is checked against it.
+// Dynamic LDS bytes of a gradient kernel: phi(Q), phi(K) [C][D], V, dOut [C][Dv] and one
+// state [D][Dv], each row padded by 16 bytes, plus the chunk's decays, dden, 1/d, the
+// column and row sums of its pair terms and one fp32 [D] vector.  BwdShape<...>::kBytes
+// is checked against it.
 constexpr int kBwdChunkHost = 64;
 constexpr size_t bwd_lds_bytes(int esize, int D, int Dv) {
     const size_t es = size_t(esize), pad = 16 / es, C = kBwdChunkHost;
-    return (2 * C * (D + pad) + 2 * C * (Dv + pad) + size_t(D) * (Dv + pad) + C * (C + pad)) * es + (8 * C + D) * 4;
+    return (2 * C * (D + pad) + 2 * C * (Dv + pad) + size_t(D) * (Dv + pad)) * es + (8 * C + D) * 4;
 }
 
 // Chunks per run of the dq and dk/dv passes.  A workgroup walks a run and carries the
 // states through it in registers, so the state traffic (a [D][Dv] fp32 slot read or
-// written per run by five passes) falls with the run's length; the runs are made as long
-// as still gives every resident slot (LDS-bound) a workgroup.  At most kBwdMaxRun.
+// written per run by five passes) falls with the run's length.  The runs per head are as
+// many as one round of resident workgroups (LDS-bound) holds, so the grid fills the
+// device once, and the run is the chunks shared out over them (at most kBwdMaxRun).
 constexpr int kBwdMaxRun = 16;
 inline int bwd_chunks_per_group(long BH, int NC, size_t lds_bytes, int cus) {
     const long resident = long(cus) * long(kMaxLds / lds_bytes < 1 ? 1 : kMaxLds / lds_bytes);
-    long run = BH * NC / resident;
+    long runs = resident / BH;
+    if (runs < 1) runs = 1;
+    if (runs > NC) runs = NC;
+    long run = (NC + runs - 1) / runs;
     if (run > kBwdMaxRun) run = kBwdMaxRun;
-    if (run > NC) run = NC;
     return run < 1 ? 1 : int(run);
 }
 
