@@ -142,6 +142,10 @@ struct BwdShape {
     static constexpr int kStateUnits = D * DV / 4 / kThreads;
     static constexpr int kRowPieces = (2 * C * D + 2 * C * DV) * int(sizeof(E)) / 16 / kThreads;
     static constexpr bool kAhead = kWaves <= 2 && kRowPieces + 2 * kStateUnits <= 32;
+    // Whether the lane indices are made opaque once per chunk (BwdChunk::refresh): with
+    // the larger tiles, addresses hoisted out of the chunk loop spill; the smallest shape
+    // (three workgroups per CU) holds them and saves a quarter of its VALU instructions.
+    static constexpr bool kOpaqueLanes = kWaves < 3;
 };
 
 // Operand of 16 rows from a row-major tile: lane supplies row `row`, contraction
@@ -319,10 +323,13 @@ struct BwdChunk {
         set_chunk(c_first);
     }
 
-    // The lane indices made opaque at the top of every chunk: the compiler then rebuilds
-    // the many LDS addresses derived from them inside the chunk loop instead of hoisting
-    // them all out of it and holding them in registers across the products.
-    __device__ __forceinline__ void refresh() { asm volatile("" : "+v"(tid), "+v"(lane), "+v"(l16), "+v"(g4)); }
+    // The lane indices made opaque at the top of every chunk (where the shape asks for
+    // it): the compiler then rebuilds the many LDS addresses derived from them inside the
+    // chunk loop instead of hoisting them all out of it and holding them in registers
+    // across the products.
+    __device__ __forceinline__ void refresh() {
+        if constexpr (Sh::kOpaqueLanes) asm volatile("" : "+v"(tid), "+v"(lane), "+v"(l16), "+v"(g4));
+    }
 
     __device__ __forceinline__ void set_chunk(int c_) {
         c = c_;
