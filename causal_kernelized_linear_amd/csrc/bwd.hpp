@@ -510,13 +510,7 @@ struct BwdChunk {
     __device__ __forceinline__ void stage_lambda(float gv) const {
         if constexpr (GATED) {
             if (w == 0) {
-                float x = lane < nrows ? fast_log2(gv) : 0.0f;
-#pragma unroll
-                for (int off = 1; off < kWave; off <<= 1) {
-                    const float y = __shfl_up(x, off, kWave);
-                    if (lane >= off) x += y;
-                }
-                sLam[lane] = x;
+                sLam[lane] = wave_incl_scan(lane < nrows ? fast_log2(gv) : 0.0f);
             }
         }
     }
@@ -790,12 +784,7 @@ void bwd_dq_kernel(BwdArgs args) {
     if (GATED && w == 0) {
         const float dm = ck.sCol[lane] + ck.sCol[C + lane] + ck.sCol[2 * C + lane] + ck.sCol[3 * C + lane] -
                          ck.sRow[lane];
-        float x = dm;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const float y = __shfl_up(x, off, kWave);
-            if (lane >= off) x += y;
-        }
+        const float x = wave_incl_scan(dm);
         if (lane < ck.nrows) args.xs[size_t(bh) * N + ts + lane] = x - dm;
     }
     // rows of dOut become 2^Lambda_i dnum_i (pad: 2^Lambda_i dden_i split), rows of V
@@ -949,10 +938,8 @@ void bwd_dkv_kernel(BwdArgs args) {
     if constexpr (GATED) {
         // Y_c = sum of yq over the chunk's queries (wave 0: one lane per token)
         if (ck.w == 0) {
-            float y = lane < ck.nrows ? syq : 0.0f;
-#pragma unroll
-            for (int off = 1; off < kWave; off <<= 1) y += __shfl_xor(y, off, kWave);
-            if (lane == 0) ck.sRow[0] = y;
+            const float y = wave_incl_scan(lane < ck.nrows ? syq : 0.0f);
+            if (lane == kWave - 1) ck.sRow[0] = y;
         }
     }
     ck.stage_lambda(sg);

@@ -352,13 +352,7 @@ struct ChunkWalker {
             run += fast_log2(R.rg[i]);
             loc[i] = run;
         }
-        float incl = run;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const float y = __shfl_up(incl, off, kWave);
-            if (lane >= off) incl += y;
-        }
-        const float excl = incl - run;
+        const float excl = wave_incl_scan(run) - run;
 #pragma unroll
         for (int i = 0; i < Sh::GPT; ++i) {
             const int j = lane * Sh::GPT + i;

@@ -23,6 +23,24 @@ __device__ __forceinline__ float phi(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Inclusive prefix sum over the 64 lanes of a wave, every lane active: DPP row shifts by
+// 1, 2, 4 and 8 scan each 16-lane row (a source outside the row reads 0), then
+// row_bcast:15 adds the last lane of row r - 1 to rows 1 and 3 and row_bcast:31 adds
+// lane 31 (the total of rows 0 and 1) to rows 2 and 3.  Six VALU steps, no LDS.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_add_from(float x) {
+    return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWS, 0xF, true));
+}
+__device__ __forceinline__ float wave_incl_scan(float x) {
+    x = dpp_add_from<0x111, 0xF>(x);   // row_shr:1
+    x = dpp_add_from<0x112, 0xF>(x);   // row_shr:2
+    x = dpp_add_from<0x114, 0xF>(x);   // row_shr:4
+    x = dpp_add_from<0x118, 0xF>(x);   // row_shr:8
+    x = dpp_add_from<0x142, 0xA>(x);   // row_bcast:15
+    x = dpp_add_from<0x143, 0xC>(x);   // row_bcast:31
+    return x;
+}
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // Element traits.  bf16 travels as its 16-bit pattern (uint16_t); widening is a
