@@ -86,6 +86,7 @@ struct WalkArgs {
     int want_final;      // 1: the last segment's output walk leaves S_N, z_N in slot nseg-1
     float eps;
     int normalize;       // 1: o = num / max(den, eps); 0: o = num (the denominator is not used)
+    float fshift;        // RELU walks only: the shift of relu(x) + shift
 };
 
 template <typename E, int D, int DV, int CH, bool GATED, bool OUT>
@@ -217,15 +218,18 @@ struct OutRsrc {
 // The per-thread machinery of one workgroup walking chunks of one head.
 // OUT: the workgroup forms outputs (row-major Fk, S^T and the split z in LDS).
 // IDENT: q and k already hold the features (another map applied beforehand), so the
-// walker uses them as they are instead of applying elu + 1.
-template <typename E, int D, int DV, int CH, bool GATED, bool OUT, bool IDENT = false>
+// walker uses them as they are instead of applying elu + 1.  RELU: the features are
+// relu(x) + fshift, applied while staging like elu + 1.
+template <typename E, int D, int DV, int CH, bool GATED, bool OUT, bool IDENT = false, bool RELU = false>
 struct ChunkWalker {
     using Sh = WalkShape<E, D, DV, CH, GATED, OUT>;
     using X = Elem<E>;
     static constexpr int LKT = Sh::LKT, LS = Sh::LS;
+    float fshift = 0.0f;
 
-    static __device__ __forceinline__ float feat(float x) {
+    __device__ __forceinline__ float feat(float x) const {
         if constexpr (IDENT) return x;
+        else if constexpr (RELU) return fmaxf(x, 0.0f) + fshift;
         else return phi(x);
     }
 
@@ -779,11 +783,11 @@ struct ChunkWalker {
 // Accumulator-layout element r of state tile j of wave w, lane (l16, g4):
 // S[16a + 4 g4 + r][16b + l16] with a = w ZT + j / NB, b = j % NB; z tile i of wave w
 // holds z[16(w ZT + i) + 4 g4 + r] in its l16 == 0 lanes (zero elsewhere).
-template <typename E, int D, int DV, int CH, bool GATED, bool OUTPUT, bool IDENT = false>
+template <typename E, int D, int DV, int CH, bool GATED, bool OUTPUT, bool IDENT = false, bool RELU = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     WalkShape<E, D, DV, CH, GATED, OUTPUT>::kWaves, WalkShape<E, D, DV, CH, GATED, OUTPUT>::kWaves))) void walk_kernel(WalkArgs args) {
     using Sh = WalkShape<E, D, DV, CH, GATED, OUTPUT>;
-    using W = ChunkWalker<E, D, DV, CH, GATED, OUTPUT, IDENT>;
+    using W = ChunkWalker<E, D, DV, CH, GATED, OUTPUT, IDENT, RELU>;
     extern __shared__ __align__(16) unsigned char smem[];
 
     const int nsw = OUTPUT ? args.nseg : args.nseg - 1;    // the totals skip the last segment
@@ -795,6 +799,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     const int nch = min(args.L, nchunks_total - c0);
 
     W wk;
+    if constexpr (RELU) wk.fshift = args.fshift;
     wk.init(smem, N, reinterpret_cast<const E*>(args.q) + size_t(bh) * N * D,
             reinterpret_cast<const E*>(args.k) + size_t(bh) * N * D,
             reinterpret_cast<const E*>(args.v) + size_t(bh) * N * DV, GATED ? args.g + size_t(bh) * N : nullptr);

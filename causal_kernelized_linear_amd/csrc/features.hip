@@ -1,10 +1,12 @@
-// Feature maps other than elu + 1, applied in a pass of their own before the chunked
-// walk, which then takes q and k as the features (its IDENT form):
+// Feature maps other than elu + 1:
 //   relu   phi(x) = max(x, 0) + shift   (the F.relu(x) + eps alternative of the
-//          anandmoghan-problems page, "Key Functions & Tricks")
+//          anandmoghan-problems page, "Key Functions & Tricks"), applied by the chunked
+//          walk itself while it stages q and k (its RELU form);
 //   favor  phi(x)_r = exp(w_r . x - |x|^2 / 2) / sqrt(m), the positive random features of
 //          Performer's FAVOR+ (aicassindra.com page, "Performer: unbiased softmax by
-//          positive random features"), for the m rows w_r of a per-head W [H][m][D].
+//          positive random features"), for the m rows w_r of a per-head W [H][m][D],
+//          written by a pass of their own; the walk then takes them as they are (its
+//          IDENT form).
 // The FAVOR+ projection is an fp32 MFMA product: rounding W or x to bf16 would put an
 // error of about 2^-9 |w| |x| into the exponent.
 #include "chunk_walk.hpp"
@@ -12,10 +14,10 @@
 
 namespace linattn {
 
-// One workgroup per (head, 64 rows): the rows' features into f [BH][N][M].
-template <typename E, int D, int M, bool FAVOR>
+// One workgroup per (head, 64 rows): the rows' FAVOR+ features into f [BH][N][M].
+template <typename E, int D, int M>
 __global__ __launch_bounds__(kThreads) void feature_kernel(const E* __restrict__ x, const float* __restrict__ W,
-                                                           E* __restrict__ f, int N, int H, float shift) {
+                                                           E* __restrict__ f, int N, int H) {
     using X = Elem<E>;
     constexpr int C = 64, LX = D + 4;
     const int nch = (N + C - 1) / C;
@@ -23,33 +25,7 @@ __global__ __launch_bounds__(kThreads) void feature_kernel(const E* __restrict__
     const int tid = threadIdx.x;
     const E* xb = x + size_t(bh) * N * D;
     E* fb = f + size_t(bh) * N * M;
-    if constexpr (!FAVOR) {
-        static_assert(M == D, "relu features keep the width");
-        // 16-byte units, every load issued before the first store (rows clamped)
-        constexpr int EPG = 16 / int(sizeof(E)), G = D / EPG, U = C * G / kThreads;
-        f32x4_t r[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int idx = tid + u * kThreads, row = idx / G, col = (idx % G) * EPG;
-            r[u] = *reinterpret_cast<const f32x4_t*>(xb + size_t(ts + min(row, nrows - 1)) * D + col);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int idx = tid + u * kThreads, row = idx / G, col = (idx % G) * EPG;
-            f32x4_t out;
-            if constexpr (sizeof(E) == 2) {
-                const F8<E> in = __builtin_bit_cast(F8<E>, r[u]);
-                F8<E> o;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) o.x[e] = X::from_f32(fmaxf(X::to_f32(in.x[e]), 0.0f) + shift);
-                out = __builtin_bit_cast(f32x4_t, o);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) out[e] = fmaxf(r[u][e], 0.0f) + shift;
-            }
-            if (row < nrows) *reinterpret_cast<f32x4_t*>(fb + size_t(ts + row) * D + col) = out;
-        }
-    } else {
+    {
         extern __shared__ __align__(16) unsigned char smem[];
         float* sX = reinterpret_cast<float*>(smem);            // [C][LX]
         float* sW = sX + C * LX;                                 // [M][LX]
@@ -124,24 +100,16 @@ template <typename E, int D, int M>
 static hipError_t run_features(const FeatLaunch& p, const void* x, void* f) {
     const int nch = (p.N + 63) / 64;
     const dim3 grid(unsigned(p.BH) * unsigned(nch)), block(kThreads);
-    if (p.kind == 1) {
-        if constexpr (D == M)
-            hipLaunchKernelGGL((feature_kernel<E, D, M, false>), grid, block, 0, p.stream, static_cast<const E*>(x),
-                               nullptr, static_cast<E*>(f), p.N, p.H, p.shift);
-        else
-            return hipErrorInvalidValue;
-    } else {
-        constexpr size_t lds = feature_lds_bytes<D, M>();
-        static bool attr = false;
-        if (!attr) {
-            const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(feature_kernel<E, D, M, true>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-            if (e != hipSuccess) return e;
-            attr = true;
-        }
-        hipLaunchKernelGGL((feature_kernel<E, D, M, true>), grid, block, lds, p.stream, static_cast<const E*>(x), p.W,
-                           static_cast<E*>(f), p.N, p.H, p.shift);
+    constexpr size_t lds = feature_lds_bytes<D, M>();
+    static bool attr = false;
+    if (!attr) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(feature_kernel<E, D, M>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+        if (e != hipSuccess) return e;
+        attr = true;
     }
+    hipLaunchKernelGGL((feature_kernel<E, D, M>), grid, block, lds, p.stream, static_cast<const E*>(x), p.W,
+                       static_cast<E*>(f), p.N, p.H);
     return hipGetLastError();
 }
 
@@ -156,8 +124,29 @@ static hipError_t run_feature_walks(const FwdLaunch& p) {
     }
 }
 
+// The walk under relu + shift features, over q and k as given.
+template <typename E, int D, int DV>
+static hipError_t run_relu_walks(const FwdLaunch& p) {
+    const bool gated = p.g != nullptr;
+    switch (p.chunk) {
+        case 64: return gated ? run_fwd<E, D, DV, 64, true, false, true>(p) : run_fwd<E, D, DV, 64, false, false, true>(p);
+        case 128: return gated ? run_fwd<E, D, DV, 128, true, false, true>(p) : run_fwd<E, D, DV, 128, false, false, true>(p);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <typename E>
 static hipError_t run_feature_fwd(const FeatLaunch& p) {
+    if (p.kind == 1) {
+        FwdLaunch w = p.fwd;
+        w.fshift = p.shift;
+        if (p.M != p.D) return hipErrorInvalidValue;
+        if (p.D == 64 && w.Dv == 64) return run_relu_walks<E, 64, 64>(w);
+        if (p.D == 64 && w.Dv == 128) return run_relu_walks<E, 64, 128>(w);
+        if (p.D == 128 && w.Dv == 64) return run_relu_walks<E, 128, 64>(w);
+        if (p.D == 128 && w.Dv == 128) return run_relu_walks<E, 128, 128>(w);
+        return hipErrorInvalidValue;
+    }
     char* ws = static_cast<char*>(p.fwd.ws);
     const size_t fbytes = round_up256(size_t(p.BH) * p.N * p.M * sizeof(E));
     void* fq = ws;

@@ -8,7 +8,7 @@
 
 namespace linattn {
 
-template <typename E, int D, int DV, int CH, bool GATED, bool IDENT = false>
+template <typename E, int D, int DV, int CH, bool GATED, bool IDENT = false, bool RELU = false>
 hipError_t run_fwd_walks(const FwdLaunch& p) {
     using ShT = WalkShape<E, D, DV, CH, GATED, false>;
     using ShO = WalkShape<E, D, DV, CH, GATED, true>;
@@ -21,11 +21,11 @@ hipError_t run_fwd_walks(const FwdLaunch& p) {
     a.zt = reinterpret_cast<float*>(wsb + off_zt);
     a.lg = reinterpret_cast<float*>(wsb + off_lg);
     a.s0 = p.s0; a.z0 = p.z0;
-    a.N = p.N; a.nseg = p.nseg; a.L = p.L; a.eps = p.eps; a.normalize = p.normalize;
+    a.N = p.N; a.nseg = p.nseg; a.L = p.L; a.eps = p.eps; a.normalize = p.normalize; a.fshift = p.fshift;
     a.direct = prefix_direct(p.nseg, D, DV) ? 1 : 0;
     a.want_final = (p.s_out || p.z_out) ? 1 : 0;
-    auto* k_tot = walk_kernel<E, D, DV, CH, GATED, false, IDENT>;
-    auto* k_out = walk_kernel<E, D, DV, CH, GATED, true, IDENT>;
+    auto* k_tot = walk_kernel<E, D, DV, CH, GATED, false, IDENT, RELU>;
+    auto* k_out = walk_kernel<E, D, DV, CH, GATED, true, IDENT, RELU>;
     static bool attrs_set = false;         // benign race: idempotent attribute set
     if (!attrs_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_tot),
@@ -55,12 +55,12 @@ hipError_t run_fwd_walks(const FwdLaunch& p) {
     return hipGetLastError();
 }
 
-template <typename E, int D, int DV, int CH, bool GATED, bool IDENT = false>
+template <typename E, int D, int DV, int CH, bool GATED, bool IDENT = false, bool RELU = false>
 hipError_t run_fwd(const FwdLaunch& p) {
     if constexpr (WalkShape<E, D, DV, CH, GATED, true>::kBytes > kMaxLds) {
         return hipErrorInvalidValue;           // rejected earlier by the ABI's support check
     } else {
-        return run_fwd_walks<E, D, DV, CH, GATED, IDENT>(p);
+        return run_fwd_walks<E, D, DV, CH, GATED, IDENT, RELU>(p);
     }
 }
 

@@ -23,6 +23,7 @@ struct FwdLaunch {
     int normalize;           // 1: o = num / max(den, eps); 0: o = num
     hipStream_t stream;
     hipEvent_t prof[4];      // measurement hook: all NULL when unused
+    float fshift = 0.0f;     // the walk under relu(x) + fshift features only
 };
 
 // Chunk sizes with kernel instantiations.
@@ -195,9 +196,9 @@ struct VdLaunch {
 hipError_t launch_vd_bf16(const VdLaunch& p);
 hipError_t launch_vd_f32(const VdLaunch& p);
 
-// A forward under another feature map: the features of q and k (kind 1: relu + shift,
-// kind 2: FAVOR+ with W [H][M][D]) are written to the head of the workspace, then the
-// walk of `fwd` runs over them with M state rows.
+// A forward under another feature map.  Kind 1, relu + shift: the walk applies it while
+// staging q and k.  Kind 2, FAVOR+ with W [H][M][D]: the features of q and k are written
+// to the head of the workspace, then the walk of `fwd` runs over them with M state rows.
 struct FeatLaunch {
     FwdLaunch fwd;           // q, k: the inputs; ws: the whole workspace; D: their width
     int kind;
