@@ -305,6 +305,7 @@ linattn_status_t vd_common(const void* q, const void* k, const void* v, const fl
     L.ws = ws;
     L.BH = int(BH); L.N = N; L.D = D; L.Dv = Dv; L.eps = eps;
     L.normalize = out == LINATTN_OUT_NORMALIZED ? 1 : 0;
+    L.cus = device_cus();
     L.stream = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     const hipError_t e = dtype == LINATTN_BF16 ? linattn::launch_vd_bf16(L) : linattn::launch_vd_f32(L);

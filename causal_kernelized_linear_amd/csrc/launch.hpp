@@ -158,7 +158,8 @@ constexpr size_t vd_lds_bytes(int esize, int D, int Dv) {
            C * (size_t(D) + 4) * 4 + size_t(D) * 4;
 }
 
-// Workspace of the per-dimension-decay forward: the state after every 64-token chunk
+// Workspace of the per-dimension-decay forward, sized for runs of one chunk (the run
+// length is chosen at launch): the state after every 64-token chunk
 // [BH][NC][D*Dv], its z [BH][NC][D] and each chunk's log2 decay per dimension [BH][NC][D].
 struct VdLayout {
     size_t st, zt, lg, bytes;
@@ -190,6 +191,7 @@ struct VdLaunch {
     int BH, N, D, Dv;
     float eps;
     int normalize;
+    int cus;                 // compute units of the device (sizes the runs)
     hipStream_t stream;
 };
 

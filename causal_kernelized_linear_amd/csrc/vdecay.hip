@@ -29,19 +29,22 @@ static hipError_t run_vd(const VdLaunch& p) {
         a.zt = reinterpret_cast<float*>(ws + lay.zt);
         a.lg = reinterpret_cast<float*>(ws + lay.lg);
         a.N = p.N; a.NC = NC; a.eps = p.eps; a.normalize = p.normalize;
+        const bool want_final = p.s_out || p.z_out;
+        a.LC = bwd_chunks_per_group(p.BH, NC, Sh::kBytes, p.cus);
+        a.NR = (NC + a.LC - 1) / a.LC;
+        a.NT = want_final ? a.NR : a.NR - 1;
         const unsigned BH = unsigned(p.BH);
         constexpr int NBLK = (D * DV + D + kThreads - 1) / kThreads;
-        const bool want_final = p.s_out || p.z_out;
-        // chunk totals, their scan (the state after every chunk, from S0), outputs
-        if (NC > 1 || want_final) {
-            hipLaunchKernelGGL(k_tot, dim3(BH * unsigned(NC)), dim3(kThreads), Sh::kBytes, p.stream, a);
+        // run totals, their scan (the state after every run, from S0), outputs
+        if (a.NT > 0) {
+            hipLaunchKernelGGL(k_tot, dim3(BH * unsigned(a.NT)), dim3(kThreads), Sh::kBytes, p.stream, a);
             hipLaunchKernelGGL((vd_scan_kernel<D, DV>), dim3(BH * NBLK), dim3(kThreads), 0, p.stream, a.st, a.zt, a.lg,
-                               p.s0, p.z0, NC);
+                               p.s0, p.z0, a.NT, a.NR);
         }
-        hipLaunchKernelGGL(k_out, dim3(BH * unsigned(NC)), dim3(kThreads), Sh::kBytes, p.stream, a);
+        hipLaunchKernelGGL(k_out, dim3(BH * unsigned(a.NR)), dim3(kThreads), Sh::kBytes, p.stream, a);
         if (want_final)
-            hipLaunchKernelGGL((final_kernel<D, DV>), dim3(BH * NBLK), dim3(kThreads), 0, p.stream, a.st, a.zt, NC,
-                               NC - 1, p.s_out, p.z_out);
+            hipLaunchKernelGGL((final_kernel<D, DV>), dim3(BH * NBLK), dim3(kThreads), 0, p.stream, a.st, a.zt, a.NR,
+                               a.NR - 1, p.s_out, p.z_out);
         return hipGetLastError();
     }
 }

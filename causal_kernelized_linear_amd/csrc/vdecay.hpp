@@ -18,9 +18,15 @@
 // last row and both factors are at most 1; for J = I, R is the block's middle row and
 // both exponents stay within 8 rows of decay, 2^64 at most when a >= 2^-8.
 //
-//   vd_totals_kernel  per (head, chunk): the chunk's decayed total and L_last
-//   vd_scan_kernel    per state element: the state after every chunk, from S0
-//   vd_out_kernel     per (head, chunk): the outputs from the state in front
+// The chunks of each head are walked in runs of LC (as the gradients' passes do): a
+// workgroup carries the state through its run in fp32 registers, so state slots exist
+// per run, not per chunk.
+//   vd_totals_kernel  per (head, run): the run's decayed total and its summed L_last
+//   vd_scan_kernel    per state element: the state after every run, from S0
+//   vd_out_kernel     per (head, run): the outputs, from the state in front of the run
+//                     stepped across each chunk, S <- Diag(2^L_last) S + Fk~^T V with
+//                     Fk~ = Fk * 2^(L_last - L); z alike, as an extra column block of
+//                     the same product (V's pad column holds 1).
 #pragma once
 
 #include "bwd.hpp"
@@ -35,11 +41,14 @@ struct VdArgs {
     void* o;
     const float* s0;     // [BH][D][Dv] or NULL
     const float* z0;     // [BH][D] or NULL
-    float* st;           // [BH][NC][D*Dv] accumulator layout: chunk totals, then (scan) the state after each chunk
-    float* zt;           // [BH][NC][D]
-    float* lg;           // [BH][NC][D]: L_last of each chunk (log2)
+    float* st;           // [BH][NR][D*Dv] accumulator layout: run totals, then (scan) the state after each run
+    float* zt;           // [BH][NR][D]
+    float* lg;           // [BH][NR][D]: the summed L_last of each run (log2)
     int N;
-    int NC;
+    int NC;              // chunks of C tokens
+    int LC;              // chunks per run
+    int NR;              // runs, ceil(NC / LC)
+    int NT;              // runs whose totals are formed: NR - 1, or NR when the final state is wanted
     float eps;
     int normalize;
 };
@@ -107,46 +116,134 @@ struct VdRows {
     }
 };
 
-// The decays of the chunk into sL as the inclusive log2 prefix L (rows past the end
-// decay by 1).  Loads first, then one thread per dimension walks the rows.
+// The decays of rows [ts, ts + C) as their inclusive log2 prefix L, into sL [C][LL]
+// (rows past the end decay by 1).  Wave w takes the columns of its quarter of D, lane
+// i row i (C = 64 lanes), four columns per 16-byte load, and scans each column with the
+// DPP wave scan; no barrier inside.  Loads first (load), then the scan and store.
 template <int D>
-__device__ __forceinline__ void vd_stage_lambda(float* sL, int LL, const float* ab, int tid, int ts, int nrows) {
-    constexpr int C = kBwdChunk;
-    constexpr int U = C * D / 4 / kThreads;
-    f32x4_t r[U];
+struct VdDecays {
+    static constexpr int C = kBwdChunk, NG = D / 16;   // 4-column groups per wave
+    static_assert(C == kWave, "one lane per row");
+    f32x4_t r[NG];
+
+    __device__ __forceinline__ void load(const float* ab, int w, int lane, int ts, int nrows) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int idx = tid + u * kThreads, row = idx / (D / 4), col = 4 * (idx % (D / 4));
-        r[u] = *reinterpret_cast<const f32x4_t*>(ab + size_t(ts + min(row, nrows - 1)) * D + col);
+        for (int g = 0; g < NG; ++g)
+            r[g] = *reinterpret_cast<const f32x4_t*>(ab + size_t(ts + min(lane, nrows - 1)) * D + w * (D / 4) + 4 * g);
     }
+
+    __device__ __forceinline__ void store(float* sL, int LL, int w, int lane, int nrows) const {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int idx = tid + u * kThreads, row = idx / (D / 4), col = 4 * (idx % (D / 4));
-        f32x4_t x;
+        for (int g = 0; g < NG; ++g) {
+            f32x4_t x;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = row < nrows ? fast_log2(r[u][e]) : 0.0f;
-        *reinterpret_cast<f32x4_t*>(sL + row * LL + col) = x;
+            for (int e = 0; e < 4; ++e) x[e] = wave_incl_scan(lane < nrows ? fast_log2(r[g][e]) : 0.0f);
+            *reinterpret_cast<f32x4_t*>(sL + lane * LL + w * (D / 4) + 4 * g) = x;
+        }
     }
-    __syncthreads();
-    if (tid < D) {
-        float acc = 0.0f;
-        for (int i = 0; i < C; ++i) {
-            acc += sL[i * LL + tid];
-            sL[i * LL + tid] = acc;
+};
+
+// Accumulator-layout state pieces of this thread (tiles w + 4u, as in the gradients):
+// loads and stores of a workspace slot, a caller-layout state, and the [D][Dv] staging.
+template <typename E, int D, int DV>
+struct VdState {
+    using X = Elem<E>;
+    static constexpr int SU = D * DV / 4 / kThreads, KZ = D / 64;
+    static __device__ __forceinline__ void load_slot(f32x4_t (&r)[SU], const float* slot, int tid) {
+#pragma unroll
+        for (int u = 0; u < SU; ++u) r[u] = *reinterpret_cast<const f32x4_t*>(slot + 4 * (tid + u * kThreads));
+    }
+    static __device__ __forceinline__ void put_slot(float* slot, const f32x4_t (&r)[SU], int tid) {
+#pragma unroll
+        for (int u = 0; u < SU; ++u) *reinterpret_cast<f32x4_t*>(slot + 4 * (tid + u * kThreads)) = r[u];
+    }
+    static __device__ __forceinline__ void load_user(f32x4_t (&r)[SU], const float* S, int tid) {
+#pragma unroll
+        for (int u = 0; u < SU; ++u) {
+            const int q4 = tid + u * kThreads, t = q4 / kWave, ln = q4 % kWave;
+            const int d = 16 * (t / (DV / 16)) + 4 * (ln >> 4), e = 16 * (t % (DV / 16)) + (ln & 15);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) r[u][k] = S ? S[size_t(d + k) * DV + e] : 0.0f;
+        }
+    }
+    static __device__ __forceinline__ void stage(E* sS, int LV, const f32x4_t (&r)[SU], int tid) {
+#pragma unroll
+        for (int u = 0; u < SU; ++u) {
+            const int q4 = tid + u * kThreads, t = q4 / kWave, ln = q4 % kWave;
+            const int d = 16 * (t / (DV / 16)) + 4 * (ln >> 4), e = 16 * (t % (DV / 16)) + (ln & 15);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) sS[(d + k) * LV + e] = X::from_f32(r[u][k]);
+        }
+    }
+    // A [D] vector in the z-holder lanes (lane l16 = 0 of group g4 in wave w: entries
+    // 16 (w + 4 t) + 4 g4 + r of tile t < KZ).
+    static __device__ __forceinline__ void load_z(float (&z)[KZ][4], const float* src, int w, int l16, int g4) {
+#pragma unroll
+        for (int t = 0; t < KZ; ++t) {
+            const f32x4_t v = (src && l16 == 0) ? *reinterpret_cast<const f32x4_t*>(src + 16 * (w + 4 * t) + 4 * g4)
+                                                : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) z[t][r] = v[r];
+        }
+    }
+    static __device__ __forceinline__ void put_z(float* dst, const float (&z)[KZ][4], int w, int l16, int g4) {
+        if (l16 == 0) {
+#pragma unroll
+            for (int t = 0; t < KZ; ++t)
+                *reinterpret_cast<f32x4_t*>(dst + 16 * (w + 4 * t) + 4 * g4) = f32x4_t{z[t][0], z[t][1], z[t][2], z[t][3]};
+        }
+    }
+};
+
+// One 16x16 state tile with the contraction over the chunk's rows: lhs^T rhs for rows a,
+// columns b of two row-major tiles.
+template <typename E>
+__device__ __forceinline__ f32x4_t vd_tile_tn(const E* lhs, int ldl, int a, const E* rhs, int ldr, int b, int g4,
+                                              int l16) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kBwdChunk / 32; ++ks)
+        acc = mma(frag_col(lhs, ldl, 32 * ks + 8 * g4, 16 * a, l16), frag_col(rhs, ldr, 32 * ks + 8 * g4, 16 * b, l16),
+                  acc);
+    return acc;
+}
+
+// Fk rows scaled in place to Fk~_j = Fk_j * 2^(L_last - L_j) (the keys as seen from the
+// chunk's end), 16 bytes per step.
+template <typename E, int D>
+__device__ __forceinline__ void vd_decay_keys(E* sK, int LQ, const float* sL, int LL, int tid) {
+    using X = Elem<E>;
+    constexpr int C = kBwdChunk, EPG = 16 / int(sizeof(E)), G = D / EPG;
+    for (int idx = tid; idx < C * G; idx += kThreads) {
+        const int row = idx / G, col = (idx % G) * EPG;
+        f32x4_t* p = reinterpret_cast<f32x4_t*>(sK + row * LQ + col);
+        if constexpr (sizeof(E) == 2) {
+            F8<E> x = __builtin_bit_cast(F8<E>, *p);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                x.x[e] = X::from_f32(X::to_f32(x.x[e]) *
+                                     fast_exp2(fminf(sL[(C - 1) * LL + col + e] - sL[row * LL + col + e], 0.0f)));
+            *p = __builtin_bit_cast(f32x4_t, x);
+        } else {
+            f32x4_t x = *p;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                x[e] *= fast_exp2(fminf(sL[(C - 1) * LL + col + e] - sL[row * LL + col + e], 0.0f));
+            *p = x;
         }
     }
 }
 
-// ------------------------------------------------------------ chunk totals ----
+// ------------------------------------------------------------ run totals ----
 
 template <typename E, int D, int DV>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(VdShape<E, D, DV>::kWaves,
                                                                            VdShape<E, D, DV>::kWaves)))
 void vd_totals_kernel(VdArgs args) {
     using Sh = VdShape<E, D, DV>;
-    using X = Elem<E>;
-    constexpr int C = Sh::C, LQ = Sh::LQ, LV = Sh::LV, LL = Sh::LL;
-    constexpr int NA = D / 16, NB = DV / 16;
+    using St = VdState<E, D, DV>;
+    constexpr int C = Sh::C, LQ = Sh::LQ, LV = Sh::LV, LL = Sh::LL, SU = St::SU, KZ = St::KZ;
+    constexpr int NB = DV / 16;
     extern __shared__ __align__(16) unsigned char smem[];
     E* sK = reinterpret_cast<E*>(smem + Sh::kOffK);
     E* sV = reinterpret_cast<E*>(smem + Sh::kOffV);
@@ -154,54 +251,67 @@ void vd_totals_kernel(VdArgs args) {
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
     const int l16 = lane & 15, g4 = lane >> 4;
     const int N = args.N, NC = args.NC;
-    const int c = blockIdx.x % NC, bh = blockIdx.x / NC, ts = c * C, nrows = min(C, N - ts);
+    const int run = blockIdx.x % args.NT, bh = blockIdx.x / args.NT;
+    const int c_first = run * args.LC, c_end = min(NC, c_first + args.LC);
 
-    VdRows<E, D> rk;
-    VdRows<E, DV> rv;
-    rk.load(reinterpret_cast<const E*>(args.k) + size_t(bh) * N * D, tid, ts, nrows);
-    rv.load(reinterpret_cast<const E*>(args.v) + size_t(bh) * N * DV, tid, ts, nrows);
-    vd_stage_lambda<D>(sL, LL, args.a + size_t(bh) * N * D, tid, ts, nrows);
-    rk.template store<true>(sK, LQ, tid, nrows);
-    rv.template store<false>(sV, LV, tid, nrows);
-    __syncthreads();
-    // decayed keys Fk_j * 2^(L_last - L_j) in place; z total in fp32 (one thread per dimension)
-    const size_t slot = size_t(bh) * NC + c;
-    if (tid < D) {
-        const float last = sL[(C - 1) * LL + tid];
-        float zs = 0.0f;
-        for (int j = 0; j < C; ++j) {
-            const float x = X::to_f32(sK[j * LQ + tid]) * fast_exp2(last - sL[j * LL + tid]);
-            zs += x;
-            sK[j * LQ + tid] = X::from_f32(x);
-        }
-        args.zt[slot * D + tid] = zs;
-        args.lg[slot * D + tid] = last;
-    }
-    __syncthreads();
-    // dS = Fk~^T V, tiles dealt to the waves, written in accumulator layout
-    constexpr int NT = NA * NB;
+    // The run's total, T <- Diag(2^L_last) T + Fk~^T V chunk by chunk, its z part and the
+    // summed L_last (z-holder lanes).
+    f32x4_t T[SU];
 #pragma unroll
-    for (int u0 = 0; u0 < NT; u0 += 4) {
-        const int u = u0 + w;
-        if (u < NT) {
-            const int ta = u / NB, tb = u % NB;
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < SU; ++u) T[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float tz[KZ][4] = {}, tl[KZ][4] = {};
+    for (int c = c_first; c < c_end; ++c) {
+        const int ts = c * C, nrows = min(C, N - ts);
+        VdRows<E, D> rk;
+        VdRows<E, DV> rv;
+        VdDecays<D> ra;
+        rk.load(reinterpret_cast<const E*>(args.k) + size_t(bh) * N * D, tid, ts, nrows);
+        rv.load(reinterpret_cast<const E*>(args.v) + size_t(bh) * N * DV, tid, ts, nrows);
+        ra.load(args.a + size_t(bh) * N * D, w, lane, ts, nrows);
+        ra.store(sL, LL, w, lane, nrows);
+        rk.template store<true>(sK, LQ, tid, nrows);
+        rv.template store<false>(sV, LV, tid, nrows);
+        // V's pad: a column of ones, so the z part comes out of the state product
+        if (tid < C)
+            *reinterpret_cast<f32x4_t*>(sV + tid * LV + DV) = split_pad<E>(tid < nrows ? 1.0f : 0.0f);
+        __syncthreads();
+        vd_decay_keys<E, D>(sK, LQ, sL, LL, tid);
+        __syncthreads();
 #pragma unroll
-            for (int ks = 0; ks < C / 32; ++ks)
-                acc = mma(frag_col(sK, LQ, 32 * ks + 8 * g4, 16 * ta, l16), frag_col(sV, LV, 32 * ks + 8 * g4, 16 * tb, l16),
-                          acc);
-            *reinterpret_cast<f32x4_t*>(args.st + slot * (D * DV) + (u * kWave + lane) * 4) = acc;
+        for (int u = 0; u < SU; ++u) {
+            const int t = w + 4 * u, a = t / NB, b = t % NB;
+            const f32x4_t ds = vd_tile_tn(sK, LQ, a, sV, LV, b, g4, l16);
+            const f32x4_t lf = *reinterpret_cast<const f32x4_t*>(sL + (C - 1) * LL + 16 * a + 4 * g4);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) T[u][k] = fast_exp2(lf[k]) * T[u][k] + ds[k];
         }
+#pragma unroll
+        for (int t = 0; t < KZ; ++t) {
+            const int a = w + 4 * t;
+            const f32x4_t dz = vd_tile_tn(sK, LQ, a, sV, LV, NB, g4, l16);
+            const f32x4_t lf = *reinterpret_cast<const f32x4_t*>(sL + (C - 1) * LL + 16 * a + 4 * g4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                tz[t][r] = fast_exp2(lf[r]) * tz[t][r] + pair01(dz[r]);
+                tl[t][r] += lf[r];
+            }
+        }
+        __syncthreads();              // every read of this chunk's tiles is done
     }
+    const size_t slot = size_t(bh) * args.NR + run;
+    St::put_slot(args.st + slot * (D * DV), T, tid);
+    St::put_z(args.zt + slot * D, tz, w, l16, g4);
+    St::put_z(args.lg + slot * D, tl, w, l16, g4);
 }
 
 // ------------------------------------------------------------------- scan ----
 
-// In place over the NC chunk slots of each head: slot c becomes the state after chunk c,
-// S_c = 2^(L_last,c[d]) S_{c-1} + dS_c (rows d), starting from S0 / z0.
+// In place over the first NC slots of each head's `stride_slots` (the run totals): slot c
+// becomes the state after run c, S_c = 2^(L_last,c[d]) S_{c-1} + dS_c (rows d), starting
+// from S0 / z0.
 template <int D, int DV>
 __global__ __launch_bounds__(kThreads) void vd_scan_kernel(float* st, float* zt, const float* lg, const float* s0,
-                                                           const float* z0, int NC) {
+                                                           const float* z0, int NC, int stride_slots) {
     constexpr int NS = D * DV;
     constexpr int NBLK = (NS + D + kThreads - 1) / kThreads;
     const int e = (blockIdx.x % NBLK) * kThreads + threadIdx.x;
@@ -217,17 +327,17 @@ __global__ __launch_bounds__(kThreads) void vd_scan_kernel(float* st, float* zt,
         d = 16 * ta + 4 * (ln / 16) + r;
         const int dv = 16 * tb + ln % 16;
         uidx = size_t(bh) * NS + size_t(d) * DV + dv;
-        base = st + size_t(bh) * NC * NS + e;
+        base = st + size_t(bh) * stride_slots * NS + e;
         stride = NS;
         init = s0;
     } else {
         d = e - NS;
         uidx = size_t(bh) * D + d;
-        base = zt + size_t(bh) * NC * D + d;
+        base = zt + size_t(bh) * stride_slots * D + d;
         stride = D;
         init = z0;
     }
-    const float* lgb = lg + size_t(bh) * NC * D + d;
+    const float* lgb = lg + size_t(bh) * stride_slots * D + d;
     float acc = init ? init[uidx] : 0.0f;
     constexpr int U = 8;                         // loads in flight per thread
     for (int c0 = 0; c0 < NC; c0 += U) {
@@ -255,8 +365,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(VdShap
                                                                            VdShape<E, D, DV>::kWaves)))
 void vd_out_kernel(VdArgs args) {
     using Sh = VdShape<E, D, DV>;
+    using St = VdState<E, D, DV>;
     using X = Elem<E>;
-    constexpr int C = Sh::C, LQ = Sh::LQ, LV = Sh::LV, LA = Sh::LA, LL = Sh::LL;
+    constexpr int C = Sh::C, LQ = Sh::LQ, LV = Sh::LV, LA = Sh::LA, LL = Sh::LL, SU = St::SU, KZ = St::KZ;
     constexpr int NE = DV / 16, NJ = C / 16, ND = D / 16;
     extern __shared__ __align__(16) unsigned char smem[];
     E* sQ = reinterpret_cast<E*>(smem + Sh::kOffQ);
@@ -269,48 +380,43 @@ void vd_out_kernel(VdArgs args) {
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
     const int l16 = lane & 15, g4 = lane >> 4;
     const int N = args.N, NC = args.NC;
-    const int c = blockIdx.x % NC, bh = blockIdx.x / NC, ts = c * C, nrows = min(C, N - ts);
+    const int run = blockIdx.x % args.NR, bh = blockIdx.x / args.NR;
+    const int c_first = run * args.LC, c_end = min(NC, c_first + args.LC);
+    E* ob = reinterpret_cast<E*>(args.o) + size_t(bh) * N * DV;
 
+    // The state in front of the current chunk, carried through the run in fp32: from the
+    // scanned slot in front of the run, or S0 / z0.
+    f32x4_t sacc[SU];
+    float zv[KZ][4];
+    if (run > 0) {
+        const size_t slot = size_t(bh) * args.NR + (run - 1);
+        St::load_slot(sacc, args.st + slot * (D * DV), tid);
+        St::load_z(zv, args.zt + slot * D, w, l16, g4);
+    } else {
+        St::load_user(sacc, args.s0 ? args.s0 + size_t(bh) * D * DV : nullptr, tid);
+        St::load_z(zv, args.z0 ? args.z0 + size_t(bh) * D : nullptr, w, l16, g4);
+    }
+
+    for (int c = c_first; c < c_end; ++c) {
+    const int ts = c * C, nrows = min(C, N - ts);
     // staging: every load first
     {
         VdRows<E, D> rq, rk;
         VdRows<E, DV> rv;
-        constexpr int SU = D * DV / 4 / kThreads;
-        f32x4_t rs[SU];
+        VdDecays<D> ra;
         rq.load(reinterpret_cast<const E*>(args.q) + size_t(bh) * N * D, tid, ts, nrows);
         rk.load(reinterpret_cast<const E*>(args.k) + size_t(bh) * N * D, tid, ts, nrows);
         rv.load(reinterpret_cast<const E*>(args.v) + size_t(bh) * N * DV, tid, ts, nrows);
-        const size_t pslot = size_t(bh) * NC + (c - 1);
-        if (c > 0) {
-#pragma unroll
-            for (int u = 0; u < SU; ++u)
-                rs[u] = *reinterpret_cast<const f32x4_t*>(args.st + pslot * (D * DV) + 4 * (tid + u * kThreads));
-        }
-        vd_stage_lambda<D>(sL, LL, args.a + size_t(bh) * N * D, tid, ts, nrows);
+        ra.load(args.a + size_t(bh) * N * D, w, lane, ts, nrows);
+        St::stage(sS, LV, sacc, tid);
+        St::put_z(sZ, zv, w, l16, g4);
+        ra.store(sL, LL, w, lane, nrows);
         rq.template store<true>(sQ, LQ, tid, nrows);
         rk.template store<true>(sK, LQ, tid, nrows);
         rv.template store<false>(sV, LV, tid, nrows);
-        if (c > 0) {
-#pragma unroll
-            for (int u = 0; u < SU; ++u) {
-                const int q4 = tid + u * kThreads, t = q4 / kWave, ln = q4 % kWave;
-                const int ta = t / (DV / 16), tb = t % (DV / 16);
-                const int d = 16 * ta + 4 * (ln >> 4), e = 16 * tb + (ln & 15);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sS[(d + r) * LV + e] = X::from_f32(rs[u][r]);
-            }
-            for (int d = tid; d < D; d += kThreads) sZ[d] = args.zt[pslot * D + d];
-        } else {
-            const float* us = args.s0 ? args.s0 + size_t(bh) * D * DV : nullptr;
-            for (int q4 = tid; q4 < D * DV / 4; q4 += kThreads) {
-                const int d = q4 / (DV / 4), e = 4 * (q4 % (DV / 4));
-                f32x4_t x = {0.f, 0.f, 0.f, 0.f};
-                if (us) x = *reinterpret_cast<const f32x4_t*>(us + size_t(d) * DV + e);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sS[d * LV + e + r] = X::from_f32(x[r]);
-            }
-            for (int d = tid; d < D; d += kThreads) sZ[d] = args.z0 ? args.z0[size_t(bh) * D + d] : 0.0f;
-        }
+        // V's pad: a column of ones, so the z step comes out of the state product
+        if (tid < C)
+            *reinterpret_cast<f32x4_t*>(sV + tid * LV + DV) = split_pad<E>(tid < nrows ? 1.0f : 0.0f);
     }
     __syncthreads();
 
@@ -378,29 +484,44 @@ void vd_out_kernel(VdArgs args) {
     for (int r = 0; r < 4; ++r) den[r] = sum16(rsum[r] + dz[r]);
     __syncthreads();
 
-    // num += A V
+    // num += A V; the keys, read for A above, become Fk~ for the state step
     for (int ks = 0; ks <= (w >> 1); ++ks) {
         const F8<E> a = frag_row(sA, LA, i0 + l16, 32 * ks + 8 * g4);
 #pragma unroll
         for (int et = 0; et < NE; ++et) num[et] = mma(a, frag_col(sV, LV, 32 * ks + 8 * g4, 16 * et, l16), num[et]);
     }
-    __syncthreads();                  // every read of V is done: it takes O
+    vd_decay_keys<E, D>(sK, LQ, sL, LL, tid);
+    __syncthreads();
+
+    // o = num / max(den, eps) (or num), written from the accumulators
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
+        const int i = i0 + 4 * g4 + r;
         const float inv = args.normalize ? 1.0f / fmaxf(den[r], args.eps) : 1.0f;
+        if (ts + i < N) {
 #pragma unroll
-        for (int et = 0; et < NE; ++et) sV[(i0 + 4 * g4 + r) * LV + 16 * et + l16] = X::from_f32(num[et][r] * inv);
-    }
-    __syncthreads();
-    {
-        constexpr int G = DV * int(sizeof(E)) / 16;
-        E* ob = reinterpret_cast<E*>(args.o) + size_t(bh) * N * DV;
-        for (int u = tid; u < C * G; u += kThreads) {
-            const int row = u / G, col = (u % G) * Sh::EPG;
-            if (row < nrows)
-                *reinterpret_cast<f32x4_t*>(ob + size_t(ts + row) * DV + col) =
-                    *reinterpret_cast<const f32x4_t*>(sV + row * LV + col);
+            for (int et = 0; et < NE; ++et) ob[size_t(ts + i) * DV + 16 * et + l16] = X::from_f32(num[et][r] * inv);
         }
+    }
+    // the state carried across the chunk: S <- Diag(2^L_last) S + Fk~^T V, z alike (the
+    // extra column block: V's pad column of ones)
+#pragma unroll
+    for (int u = 0; u < SU; ++u) {
+        const int t = w + 4 * u, a = t / NE, b = t % NE;
+        const f32x4_t ds = vd_tile_tn(sK, LQ, a, sV, LV, b, g4, l16);
+        const f32x4_t lf = *reinterpret_cast<const f32x4_t*>(sL + (C - 1) * LL + 16 * a + 4 * g4);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) sacc[u][k] = fast_exp2(lf[k]) * sacc[u][k] + ds[k];
+    }
+#pragma unroll
+    for (int t = 0; t < KZ; ++t) {
+        const int a = w + 4 * t;
+        const f32x4_t dzt = vd_tile_tn(sK, LQ, a, sV, LV, NE, g4, l16);
+        const f32x4_t lf = *reinterpret_cast<const f32x4_t*>(sL + (C - 1) * LL + 16 * a + 4 * g4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) zv[t][r] = fast_exp2(lf[r]) * zv[t][r] + pair01(dzt[r]);
+    }
+    __syncthreads();                  // every read of this chunk's tiles is done
     }
 }
 

@@ -157,6 +157,26 @@ def test_vdecay_workload_sampled_heads():
     assert torch.isfinite(o).all().item()
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_vdecay_runs_sampled_heads(dt):
+    """128 heads of 596 tokens: on a 256-CU device the launch walks each head in several
+    runs of chunks (the last run and chunk ragged), carrying the state through each run;
+    outputs, final state and z against the oracle on sampled heads."""
+    B, H, N, D, Dv = 2, 64, 596, 64, 64
+    inp = workloads.random_inputs(777, B, H, N, D, Dv, dtype=dt, with_state=True, state_scale=5.0)
+    a = decay(778, (B, H, N, D), 0.5)
+    heads = _heads(B, H, 4, 23)
+    _say(f"vdecay runs {dt}, oracle on heads {heads}")
+    o, S, z = binding.fwd_vdecay(*(_dev(inp[n]) for n in ("q", "k", "v")), _dev(a), s0=_dev(inp["s0"]),
+                                 z0=_dev(inp["z0"]), return_state=True)
+    torch.cuda.synchronize()
+    o_ref, S_ref, z_ref = oracle_run(inp, a, s0=inp["s0"], z0=inp["z0"], heads=heads)
+    sel = lambda t: np.stack([to64(t)[b, h] for b, h in heads])[None]     # noqa: E731
+    assert rowwise_rel_err(sel(o), o_ref) <= TOL[dt]
+    assert matrix_rel_err(sel(S), S_ref) <= TOL[dt]
+    assert matrix_rel_err(sel(z), z_ref) <= TOL[dt]
+
+
 def test_decode_vdecay_workload_sampled_heads():
     w = workloads.WORKLOADS["decode_vdecay_bf16"]
     inp = workloads.make_inputs(w)
