@@ -368,7 +368,7 @@ void vd_out_kernel(VdArgs args) {
     using St = VdState<E, D, DV>;
     using X = Elem<E>;
     constexpr int C = Sh::C, LQ = Sh::LQ, LV = Sh::LV, LA = Sh::LA, LL = Sh::LL, SU = St::SU, KZ = St::KZ;
-    constexpr int NE = DV / 16, NJ = C / 16, ND = D / 16;
+    constexpr int NE = DV / 16, NJ = C / 16;
     extern __shared__ __align__(16) unsigned char smem[];
     E* sQ = reinterpret_cast<E*>(smem + Sh::kOffQ);
     E* sK = reinterpret_cast<E*>(smem + Sh::kOffK);
@@ -376,7 +376,6 @@ void vd_out_kernel(VdArgs args) {
     E* sS = reinterpret_cast<E*>(smem + Sh::kOffS);
     E* sA = reinterpret_cast<E*>(smem + Sh::kOffA);
     float* sL = reinterpret_cast<float*>(smem + Sh::kOffL);
-    float* sZ = reinterpret_cast<float*>(smem + Sh::kOffZ);
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
     const int l16 = lane & 15, g4 = lane >> 4;
     const int N = args.N, NC = args.NC;
@@ -409,7 +408,14 @@ void vd_out_kernel(VdArgs args) {
         rv.load(reinterpret_cast<const E*>(args.v) + size_t(bh) * N * DV, tid, ts, nrows);
         ra.load(args.a + size_t(bh) * N * D, w, lane, ts, nrows);
         St::stage(sS, LV, sacc, tid);
-        St::put_z(sZ, zv, w, l16, g4);
+        if (l16 == 0) {
+            // z_prev, split, into the state's pad columns: den's z part comes out of num
+#pragma unroll
+            for (int t = 0; t < KZ; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    *reinterpret_cast<f32x4_t*>(sS + (16 * (w + 4 * t) + 4 * g4 + r) * LV + DV) = split_pad<E>(zv[t][r]);
+        }
         ra.store(sL, LL, w, lane, nrows);
         rq.template store<true>(sQ, LQ, tid, nrows);
         rk.template store<true>(sK, LQ, tid, nrows);
@@ -421,10 +427,11 @@ void vd_out_kernel(VdArgs args) {
     __syncthreads();
 
     const int i0 = 16 * w;            // this wave's query rows (block I = w)
-    // num = (Fq * 2^L_i) S_prev; den = (Fq * 2^L_i) . z_prev
-    f32x4_t num[NE];
+    // num = (Fq * 2^L_i) S_prev, with an extra column block: S's pad columns hold z_prev
+    // split, V's a column of ones, so columns 0 + 1 of num[NE] end as den
+    f32x4_t num[NE + 1];
 #pragma unroll
-    for (int et = 0; et < NE; ++et) num[et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int et = 0; et <= NE; ++et) num[et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
         const int d0 = 32 * ks + 8 * g4;
@@ -434,23 +441,10 @@ void vd_out_kernel(VdArgs args) {
         for (int e = 0; e < 8; ++e)
             a.x[e] = X::from_f32(X::to_f32(fq.x[e]) * fast_exp2(sL[(i0 + l16) * LL + d0 + e]));
 #pragma unroll
-        for (int et = 0; et < NE; ++et) num[et] = mma(a, frag_col(sS, LV, d0, 16 * et, l16), num[et]);
-    }
-    float dz[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int i = i0 + 4 * g4 + r;
-        float x = 0.0f;
-#pragma unroll
-        for (int t = 0; t < ND; ++t) {
-            const int d = 16 * t + l16;
-            x += X::to_f32(sQ[i * LQ + d]) * fast_exp2(sL[i * LL + d]) * sZ[d];
-        }
-        dz[r] = x;
+        for (int et = 0; et <= NE; ++et) num[et] = mma(a, frag_col(sS, LV, d0, 16 * et, l16), num[et]);
     }
 
-    // A over the blocks J <= I, each against its reference row, into sA (E); row sums
-    float rsum[4] = {0.f, 0.f, 0.f, 0.f};
+    // A over the blocks J <= I, each against its reference row, into sA (E)
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -474,30 +468,28 @@ void vd_out_kernel(VdArgs args) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = i0 + 4 * g4 + r, j = 16 * jt + l16;
-            const E xe = X::from_f32((jt <= w && j <= i) ? acc[r] : 0.0f);
-            sA[i * LA + j] = xe;
-            rsum[r] += X::to_f32(xe);
+            sA[i * LA + j] = X::from_f32((jt <= w && j <= i) ? acc[r] : 0.0f);
         }
     }
-    float den[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) den[r] = sum16(rsum[r] + dz[r]);
     __syncthreads();
 
-    // num += A V; the keys, read for A above, become Fk~ for the state step
+    // num += A V (the extra block adds A's row sums to den); the keys, read for A above,
+    // become Fk~ for the state step
     for (int ks = 0; ks <= (w >> 1); ++ks) {
         const F8<E> a = frag_row(sA, LA, i0 + l16, 32 * ks + 8 * g4);
 #pragma unroll
-        for (int et = 0; et < NE; ++et) num[et] = mma(a, frag_col(sV, LV, 32 * ks + 8 * g4, 16 * et, l16), num[et]);
+        for (int et = 0; et <= NE; ++et) num[et] = mma(a, frag_col(sV, LV, 32 * ks + 8 * g4, 16 * et, l16), num[et]);
     }
     vd_decay_keys<E, D>(sK, LQ, sL, LL, tid);
     __syncthreads();
 
-    // o = num / max(den, eps) (or num), written from the accumulators
+    // o = num / max(den, eps) (or num), written from the accumulators; den of row
+    // i0 + 4 g4 + r is columns 0 + 1 of num[NE], broadcast from lane 0 of the row group
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int i = i0 + 4 * g4 + r;
-        const float inv = args.normalize ? 1.0f / fmaxf(den[r], args.eps) : 1.0f;
+        const float den = dpp_move<0x150>(pair01(num[NE][r]));      // row_newbcast:0
+        const float inv = args.normalize ? 1.0f / fmaxf(den, args.eps) : 1.0f;
         if (ts + i < N) {
 #pragma unroll
             for (int et = 0; et < NE; ++et) ob[size_t(ts + i) * DV + 16 * et + l16] = X::from_f32(num[et][r] * inv);
