@@ -7,100 +7,177 @@
 //          positive random features"), for the m rows w_r of a per-head W [H][m][D],
 //          written by a pass of their own; the walk then takes them as they are (its
 //          IDENT form).
-// The FAVOR+ projection is an fp32 MFMA product: rounding W or x to bf16 would put an
+// The FAVOR+ projection w_r . x keeps fp32 accuracy on the bf16 MFMA: every fp32 operand
+// is split into a bf16 high part and a bf16 low part (the high part's rounding error),
+// and w . x = x_hi . w_hi + x_hi . w_lo + x_lo . w_hi, dropping x_lo . w_lo (about 2^-16
+// of the product); a bf16 input has no low part.  Each partial product of two bf16
+// values is exact in the fp32 accumulator.  Rounding W or x to bf16 alone would put an
 // error of about 2^-9 |w| |x| into the exponent.
+#include "bwd.hpp"          // MFMA fragment helpers and lane sums
 #include "chunk_walk.hpp"
 #include "fwd_dispatch.hpp"
 
 namespace linattn {
 
-// One workgroup per (head, 64 rows): the rows' FAVOR+ features into f [BH][N][M].
+// LDS of the feature pass: x (high and, for fp32 inputs, low parts) [64][D] and W's high
+// and low parts [M][D], bf16 rows padded by 16 bytes, and |x|^2 / 2 per row.
 template <typename E, int D, int M>
-__global__ __launch_bounds__(kThreads) void feature_kernel(const E* __restrict__ x, const float* __restrict__ W,
-                                                           E* __restrict__ f, int N, int H) {
-    using X = Elem<E>;
-    constexpr int C = 64, LX = D + 4;
-    const int nch = (N + C - 1) / C;
-    const int c = blockIdx.x % nch, bh = blockIdx.x / nch, ts = c * C, nrows = min(C, N - ts);
-    const int tid = threadIdx.x;
-    const E* xb = x + size_t(bh) * N * D;
-    E* fb = f + size_t(bh) * N * M;
-    {
-        extern __shared__ __align__(16) unsigned char smem[];
-        float* sX = reinterpret_cast<float*>(smem);            // [C][LX]
-        float* sW = sX + C * LX;                                 // [M][LX]
-        float* sN = sW + M * LX;                                 // [C] |x|^2 / 2
-        const float* Wh = W + size_t(bh % H) * M * D;
-        // every load first: x in 16-byte units (rows clamped), W in fp32 quads
-        constexpr int EPG = 16 / int(sizeof(E)), G = D / EPG, UX = C * G / kThreads, UW = M * D / 4 / kThreads;
-        f32x4_t rx[UX], rw[UW];
-#pragma unroll
-        for (int u = 0; u < UX; ++u) {
-            const int idx = tid + u * kThreads, row = idx / G, col = (idx % G) * EPG;
-            rx[u] = *reinterpret_cast<const f32x4_t*>(xb + size_t(ts + min(row, nrows - 1)) * D + col);
-        }
-#pragma unroll
-        for (int u = 0; u < UW; ++u) rw[u] = *reinterpret_cast<const f32x4_t*>(Wh + 4 * (tid + u * kThreads));
-#pragma unroll
-        for (int u = 0; u < UX; ++u) {
-            const int idx = tid + u * kThreads, row = idx / G, col = (idx % G) * EPG;
-            if constexpr (sizeof(E) == 2) {
-                const F8<E> in = __builtin_bit_cast(F8<E>, rx[u]);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) sX[row * LX + col + e] = row < nrows ? X::to_f32(in.x[e]) : 0.0f;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sX[row * LX + col + e] = row < nrows ? rx[u][e] : 0.0f;
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < UW; ++u) {
-            const int i = 4 * (tid + u * kThreads);
-            *reinterpret_cast<f32x4_t*>(sW + (i / D) * LX + i % D) = rw[u];
-        }
-        __syncthreads();
-        if (tid < C) {
-            float s = 0.0f;
-            for (int d = 0; d < D; ++d) s += sX[tid * LX + d] * sX[tid * LX + d];
-            sN[tid] = 0.5f * s;
-        }
-        __syncthreads();
-        const int w = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
-        const int l16 = lane & 15, g4 = lane >> 4;
-        constexpr int NR = M / 16;
-        f32x4_t acc[NR];
-#pragma unroll
-        for (int t = 0; t < NR; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) {
-            const F8<float> a = lds_f8(sX + (16 * w + l16) * LX + 32 * ks + 8 * g4);
-#pragma unroll
-            for (int t = 0; t < NR; ++t) acc[t] = mma(a, lds_f8(sW + (16 * t + l16) * LX + 32 * ks + 8 * g4), acc[t]);
-        }
-        const float rs = 1.0f / sqrtf(float(M));
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = 16 * w + 4 * g4 + r;
-            if (i < nrows) {
-                const float h = sN[i];
-#pragma unroll
-                for (int t = 0; t < NR; ++t)
-                    fb[size_t(ts + i) * M + 16 * t + l16] = X::from_f32(fast_exp2((acc[t][r] - h) * kLog2e) * rs);
-            }
-        }
+struct FeatShape {
+    static constexpr int C = 64, LX = D + 8;
+    static constexpr bool kSplitX = sizeof(E) == 4;
+    static constexpr size_t kOffXh = 0;
+    static constexpr size_t kOffXl = kOffXh + size_t(C) * LX * 2;
+    static constexpr size_t kOffWh = kOffXl + (kSplitX ? size_t(C) * LX * 2 : 0);
+    static constexpr size_t kOffWl = kOffWh + size_t(M) * LX * 2;
+    static constexpr size_t kOffN = kOffWl + size_t(M) * LX * 2;
+    static constexpr size_t kBytes = kOffN + size_t(C) * 4;
+};
+
+// Sum over G consecutive lanes (G in {8, 16, 32}, aligned), every lane getting it.
+template <int G>
+__device__ __forceinline__ float sum_lanes(float x) {
+    static_assert(G == 8 || G == 16 || G == 32, "lane group");
+    if constexpr (G == 8) {
+        x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
+        x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, true));
+        x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, true));
+        return x;
+    } else {
+        x = sum16(x);
+        if constexpr (G == 32) x += __shfl_xor(x, 16, kWave);
+        return x;
     }
 }
 
-template <int D, int M>
-constexpr size_t feature_lds_bytes() {
-    return (size_t(64) * (D + 4) + size_t(M) * (D + 4) + 64) * 4;
+// A value split into bf16 high and low parts.
+__device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) {
+    using B = Elem<uint16_t>;
+    hi = B::from_f32(v);
+    lo = B::from_f32(v - B::to_f32(hi));
+}
+
+// One workgroup per (head, kFeatBlocks blocks of 64 rows): the rows' FAVOR+ features into
+// f [BH][N][M].  W's split is staged once per workgroup and serves all its blocks.
+constexpr int kFeatBlocks = 4;
+
+template <typename E, int D, int M>
+__global__ __launch_bounds__(kThreads) void feature_kernel(const E* __restrict__ x, const float* __restrict__ W,
+                                                           E* __restrict__ f, int N, int H) {
+    using Sh = FeatShape<E, D, M>;
+    using X = Elem<E>;
+    constexpr int C = Sh::C, LX = Sh::LX, NR = M / 16;
+    extern __shared__ __align__(16) unsigned char smem[];
+    uint16_t* sXh = reinterpret_cast<uint16_t*>(smem + Sh::kOffXh);
+    uint16_t* sXl = reinterpret_cast<uint16_t*>(smem + Sh::kOffXl);
+    uint16_t* sWh = reinterpret_cast<uint16_t*>(smem + Sh::kOffWh);
+    uint16_t* sWl = reinterpret_cast<uint16_t*>(smem + Sh::kOffWl);
+    float* sN = reinterpret_cast<float*>(smem + Sh::kOffN);
+    const int nsup = (N + C * kFeatBlocks - 1) / (C * kFeatBlocks);
+    const int sup = blockIdx.x % nsup, bh = blockIdx.x / nsup;
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const E* xb = x + size_t(bh) * N * D;
+    E* fb = f + size_t(bh) * N * M;
+    const float* Wh = W + size_t(bh % H) * M * D;
+
+    // W's high and low parts, once
+    constexpr int EPG = 16 / int(sizeof(E)), G = D / EPG, UX = C * G / kThreads, UW = M * D / 4 / kThreads;
+    {
+        f32x4_t rw[UW];
+#pragma unroll
+        for (int u = 0; u < UW; ++u) rw[u] = *reinterpret_cast<const f32x4_t*>(Wh + 4 * (tid + u * kThreads));
+#pragma unroll
+        for (int u = 0; u < UW; ++u) {
+            const int i = 4 * (tid + u * kThreads), m = i / D, d = i % D;
+            F4<uint16_t> oh, ol;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) split_bf16(rw[u][e], oh.x[e], ol.x[e]);
+            *reinterpret_cast<F4<uint16_t>*>(sWh + m * LX + d) = oh;
+            *reinterpret_cast<F4<uint16_t>*>(sWl + m * LX + d) = ol;
+        }
+    }
+    for (int blk = 0; blk < kFeatBlocks; ++blk) {
+    const int ts = (sup * kFeatBlocks + blk) * C;
+    if (ts >= N) break;                                       // uniform over the workgroup
+    const int nrows = min(C, N - ts);
+    // the block's x in 16-byte units (rows clamped)
+    f32x4_t rx[UX];
+#pragma unroll
+    for (int u = 0; u < UX; ++u) {
+        const int idx = tid + u * kThreads, row = idx / G, col = (idx % G) * EPG;
+        rx[u] = *reinterpret_cast<const f32x4_t*>(xb + size_t(ts + min(row, nrows - 1)) * D + col);
+    }
+
+    // x into LDS (split when fp32), and each row's |x|^2 / 2 summed over the G lanes that
+    // hold it (rows past the end are zero)
+#pragma unroll
+    for (int u = 0; u < UX; ++u) {
+        const int idx = tid + u * kThreads, row = idx / G, col = (idx % G) * EPG;
+        const bool in = row < nrows;
+        float sq = 0.0f;
+        if constexpr (sizeof(E) == 2) {
+            const F8<uint16_t> v = __builtin_bit_cast(F8<uint16_t>, rx[u]);
+            F8<uint16_t> o;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float xv = in ? X::to_f32(v.x[e]) : 0.0f;
+                o.x[e] = in ? v.x[e] : uint16_t(0);
+                sq += xv * xv;
+            }
+            *reinterpret_cast<F8<uint16_t>*>(sXh + row * LX + col) = o;
+        } else {
+            F4<uint16_t> oh, ol;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float xv = in ? rx[u][e] : 0.0f;
+                split_bf16(xv, oh.x[e], ol.x[e]);
+                sq += xv * xv;
+            }
+            *reinterpret_cast<F4<uint16_t>*>(sXh + row * LX + col) = oh;
+            *reinterpret_cast<F4<uint16_t>*>(sXl + row * LX + col) = ol;
+        }
+        sq = sum_lanes<G>(sq);
+        if (idx % G == 0) sN[row] = 0.5f * sq;
+    }
+    __syncthreads();
+
+    // (W x)^T: lane (l16, g4) holds row i = 16 w + l16 against features 16 t + 4 g4 + r
+    f32x4_t acc[NR];
+#pragma unroll
+    for (int t = 0; t < NR; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+        const int k0 = 32 * ks + 8 * g4;
+        const F8<uint16_t> bh_ = frag_row(sXh, LX, 16 * w + l16, k0);
+#pragma unroll
+        for (int t = 0; t < NR; ++t) {
+            const F8<uint16_t> ah = frag_row(sWh, LX, 16 * t + l16, k0);
+            acc[t] = mma(ah, bh_, acc[t]);
+            acc[t] = mma(frag_row(sWl, LX, 16 * t + l16, k0), bh_, acc[t]);
+            if constexpr (Sh::kSplitX) acc[t] = mma(ah, frag_row(sXl, LX, 16 * w + l16, k0), acc[t]);
+        }
+    }
+    // features exp(w . x - |x|^2 / 2) / sqrt(M): four consecutive per lane
+    const int i = 16 * w + l16;
+    if (i < nrows) {
+        const float h = sN[i], rs = 1.0f / sqrtf(float(M));
+#pragma unroll
+        for (int t = 0; t < NR; ++t) {
+            f32x4_t o;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] = fast_exp2((acc[t][r] - h) * kLog2e) * rs;
+            *reinterpret_cast<F4<E>*>(fb + size_t(ts + i) * M + 16 * t + 4 * g4) = pack4<E>(o);
+        }
+    }
+    __syncthreads();                  // the block's x and |x|^2 are read: the next may overwrite
+    }
 }
 
 template <typename E, int D, int M>
 static hipError_t run_features(const FeatLaunch& p, const void* x, void* f) {
-    const int nch = (p.N + 63) / 64;
-    const dim3 grid(unsigned(p.BH) * unsigned(nch)), block(kThreads);
-    constexpr size_t lds = feature_lds_bytes<D, M>();
+    const int nsup = (p.N + 64 * kFeatBlocks - 1) / (64 * kFeatBlocks);
+    const dim3 grid(unsigned(p.BH) * unsigned(nsup)), block(kThreads);
+    constexpr size_t lds = FeatShape<E, D, M>::kBytes;
     static bool attr = false;
     if (!attr) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(feature_kernel<E, D, M>),
