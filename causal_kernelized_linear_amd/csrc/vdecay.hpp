@@ -444,12 +444,40 @@ void vd_out_kernel(VdArgs args) {
         for (int et = 0; et <= NE; ++et) num[et] = mma(a, frag_col(sS, LV, d0, 16 * et, l16), num[et]);
     }
 
-    // A over the blocks J <= I, each against its reference row, into sA (E)
+    // A over the blocks J <= I into sA (E).  The blocks J < I share one reference row,
+    // R = 16 I - 1 (the row in front of the wave's block): the queries are rescaled once,
+    // qa_i = Fq_i 2^(L_i - L_R) (at least 2^-128 over 16 rows), and every key block
+    // against it, kb_j = Fk_j 2^(L_R - L_j) <= 1 (a distant key that underflows carries a
+    // weight below 2^-128 anyway).  The diagonal block J = I uses its middle row.
+    F8<E> qa_off[D / 32];
+    if (w > 0) {
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+            const int d0 = 32 * ks + 8 * g4;
+            const F8<E> fq = frag_row(sQ, LQ, i0 + l16, d0);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                qa_off[ks].x[e] = X::from_f32(X::to_f32(fq.x[e]) *
+                                              fast_exp2(sL[(i0 + l16) * LL + d0 + e] - sL[(i0 - 1) * LL + d0 + e]));
+        }
+    }
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        if (jt <= w) {
-            const int ref = jt < w ? 16 * jt + 15 : 16 * jt + 7;
+        if (jt < w) {
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks) {
+                const int d0 = 32 * ks + 8 * g4;
+                const F8<E> fk = frag_row(sK, LQ, 16 * jt + l16, d0);
+                F8<E> kb;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    kb.x[e] = X::from_f32(X::to_f32(fk.x[e]) *
+                                          fast_exp2(sL[(i0 - 1) * LL + d0 + e] - sL[(16 * jt + l16) * LL + d0 + e]));
+                acc = mma(qa_off[ks], kb, acc);
+            }
+        } else if (jt == w) {
+            const int ref = 16 * jt + 7;
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks) {
                 const int d0 = 32 * ks + 8 * g4;
