@@ -51,7 +51,9 @@ hipError_t run_bwd(const BwdLaunch& p) {
         a.zk = reinterpret_cast<float*>(ws + lay.zk);
         a.wc = reinterpret_cast<float*>(ws + lay.wc);
         a.N = p.N; a.NC = NC; a.eps = p.eps; a.normalize = p.normalize;
-        a.LC = p.run > 0 ? (p.run < NC ? p.run : NC) : bwd_chunks_per_group(p.BH, NC, Sh::kBytes, p.cus);
+        // as many workgroups per CU as the LDS holds (three at D = Dv = 64 bf16): measured
+        // faster than fewer, longer runs
+        a.LC = p.run > 0 ? (p.run < NC ? p.run : NC) : bwd_chunks_per_group(p.BH, NC, Sh::kWaves, p.cus);
         const int NR = (NC + a.LC - 1) / a.LC;
         a.NR = NR;
         constexpr int NBLK = (D * DV + D + kThreads - 1) / kThreads;

@@ -83,14 +83,15 @@ constexpr size_t bwd_lds_bytes(int esize, int D, int Dv) {
     return (2 * C * (D + pad) + 2 * C * (Dv + pad) + size_t(D) * (Dv + pad)) * es + (8 * C + D) * 4;
 }
 
-// Chunks per run of the dq and dk/dv passes.  A workgroup walks a run and carries the
-// states through it in registers, so the state traffic (a [D][Dv] fp32 slot read or
-// written per run by five passes) falls with the run's length.  The runs per head are as
-// many as one round of resident workgroups (LDS-bound) holds, so the grid fills the
+// Chunks per run of the passes that walk runs of chunks (the gradients' dq and dk/dv
+// passes, the per-dimension decay's totals and outputs).  A workgroup walks a run and
+// carries the states through it in registers, so the state traffic (a [D][Dv] fp32 slot
+// read or written per run) falls with the run's length.  The runs per head are as many
+// as one round of `per_cu` workgroups per compute unit holds, so the grid fills the
 // device once, and the run is the chunks shared out over them (at most kBwdMaxRun).
 constexpr int kBwdMaxRun = 16;
-inline int bwd_chunks_per_group(long BH, int NC, size_t lds_bytes, int cus) {
-    const long resident = long(cus) * long(kMaxLds / lds_bytes < 1 ? 1 : kMaxLds / lds_bytes);
+inline int bwd_chunks_per_group(long BH, int NC, int per_cu, int cus) {
+    const long resident = long(cus) * long(per_cu < 1 ? 1 : per_cu);
     long runs = resident / BH;
     if (runs < 1) runs = 1;
     if (runs > NC) runs = NC;
@@ -149,13 +150,13 @@ struct BwdLaunch {
     hipStream_t stream;
 };
 
-// Dynamic LDS bytes of the per-dimension-decay output kernel: phi(Q), phi(K) [C][D], V
-// [C][Dv], S_prev [D][Dv] and A [C][C] (rows padded by 16 bytes), the decays [C][D + 4]
-// and z_prev [D] in fp32.  VdShape<...>::kBytes is checked against it.
+// Dynamic LDS bytes of the per-dimension-decay kernels: phi(Q), phi(K) [C][D], V [C][Dv]
+// and S_prev [D][Dv] (rows padded by 16 bytes), the decays [C][D + 4] and one [D] vector
+// in fp32.  VdShape<...>::kBytes is checked against it.
 constexpr size_t vd_lds_bytes(int esize, int D, int Dv) {
     const size_t es = size_t(esize), pad = 16 / es, C = kBwdChunkHost;
-    return (2 * C * (D + pad) + C * (Dv + pad) + size_t(D) * (Dv + pad) + C * (C + pad)) * es +
-           C * (size_t(D) + 4) * 4 + size_t(D) * 4;
+    return (2 * C * (D + pad) + C * (Dv + pad) + size_t(D) * (Dv + pad)) * es + C * (size_t(D) + 4) * 4 +
+           size_t(D) * 4;
 }
 
 // Workspace of the per-dimension-decay forward, sized for runs of one chunk (the run

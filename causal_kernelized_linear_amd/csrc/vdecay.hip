@@ -30,7 +30,7 @@ static hipError_t run_vd(const VdLaunch& p) {
         a.lg = reinterpret_cast<float*>(ws + lay.lg);
         a.N = p.N; a.NC = NC; a.eps = p.eps; a.normalize = p.normalize;
         const bool want_final = p.s_out || p.z_out;
-        a.LC = bwd_chunks_per_group(p.BH, NC, Sh::kBytes, p.cus);
+        a.LC = bwd_chunks_per_group(p.BH, NC, Sh::kWaves, p.cus);
         a.NR = (NC + a.LC - 1) / a.LC;
         a.NT = want_final ? a.NR : a.NR - 1;
         const unsigned BH = unsigned(p.BH);

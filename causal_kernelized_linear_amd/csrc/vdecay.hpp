@@ -59,18 +59,20 @@ struct VdShape {
     static constexpr int PAD = 16 / int(sizeof(E));
     static constexpr int LQ = D + PAD;
     static constexpr int LV = DV + PAD;
-    static constexpr int LA = C + PAD;
     static constexpr int LL = D + 4;                   // fp32 decay rows
     static constexpr size_t kOffQ = 0;                 // phi(Q) [C][D]
     static constexpr size_t kOffK = kOffQ + size_t(C) * LQ * sizeof(E);   // phi(K) [C][D]
     static constexpr size_t kOffV = kOffK + size_t(C) * LQ * sizeof(E);   // V [C][Dv] (then O)
     static constexpr size_t kOffS = kOffV + size_t(C) * LV * sizeof(E);   // S_prev [D][Dv]
-    static constexpr size_t kOffA = kOffS + size_t(D) * LV * sizeof(E);   // A [C][C]
-    static constexpr size_t kOffL = kOffA + size_t(C) * LA * sizeof(E);   // L [C][D] fp32
+    static constexpr size_t kOffL = kOffS + size_t(D) * LV * sizeof(E);   // L [C][D] fp32
     static constexpr size_t kOffZ = kOffL + size_t(C) * LL * 4;           // z_prev [D] fp32
     static constexpr size_t kBytes = kOffZ + size_t(D) * 4;
     static_assert(kBytes == vd_lds_bytes(int(sizeof(E)), D, DV), "host LDS formula out of step");
-    static constexpr int kWaves = int(kMaxLds / kBytes) < 1 ? 1 : int(kMaxLds / kBytes);
+    // workgroups (waves per SIMD) per CU the launch plans for and the register target:
+    // what the LDS allows, at most two (three, where the LDS would allow it, measured
+    // slower: vdecay_bf16 266 against 232 us)
+    static constexpr int kLdsWaves = int(kMaxLds / kBytes) < 1 ? 1 : int(kMaxLds / kBytes);
+    static constexpr int kWaves = kLdsWaves < 2 ? kLdsWaves : 2;
     static constexpr int EPG = 16 / int(sizeof(E));
 };
 
@@ -117,28 +119,43 @@ struct VdRows {
 };
 
 // The decays of rows [ts, ts + C) as their inclusive log2 prefix L, into sL [C][LL]
-// (rows past the end decay by 1).  Wave w takes the columns of its quarter of D, lane
-// i row i (C = 64 lanes), four columns per 16-byte load, and scans each column with the
-// DPP wave scan; no barrier inside.  Loads first (load), then the scan and store.
+// (rows past the end decay by 1).  load: coalesced 16-byte units (rows clamped); store:
+// log2 into sL row-major; then, after a barrier, scan: wave w takes the columns of its
+// quarter of D, lane i row i (C = 64 lanes), four columns per 16-byte LDS access, each
+// column scanned with the DPP wave scan in place.
 template <int D>
 struct VdDecays {
-    static constexpr int C = kBwdChunk, NG = D / 16;   // 4-column groups per wave
+    static constexpr int C = kBwdChunk, U = C * D / 4 / kThreads, G = D / 4, NG = D / 16;
     static_assert(C == kWave, "one lane per row");
-    f32x4_t r[NG];
+    f32x4_t r[U];
 
-    __device__ __forceinline__ void load(const float* ab, int w, int lane, int ts, int nrows) {
+    __device__ __forceinline__ void load(const float* ab, int tid, int ts, int nrows) {
 #pragma unroll
-        for (int g = 0; g < NG; ++g)
-            r[g] = *reinterpret_cast<const f32x4_t*>(ab + size_t(ts + min(lane, nrows - 1)) * D + w * (D / 4) + 4 * g);
+        for (int u = 0; u < U; ++u) {
+            const int idx = tid + u * kThreads, row = idx / G, col = 4 * (idx % G);
+            r[u] = *reinterpret_cast<const f32x4_t*>(ab + size_t(ts + min(row, nrows - 1)) * D + col);
+        }
     }
 
-    __device__ __forceinline__ void store(float* sL, int LL, int w, int lane, int nrows) const {
+    __device__ __forceinline__ void store(float* sL, int LL, int tid, int nrows) const {
 #pragma unroll
-        for (int g = 0; g < NG; ++g) {
+        for (int u = 0; u < U; ++u) {
+            const int idx = tid + u * kThreads, row = idx / G, col = 4 * (idx % G);
             f32x4_t x;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = wave_incl_scan(lane < nrows ? fast_log2(r[g][e]) : 0.0f);
-            *reinterpret_cast<f32x4_t*>(sL + lane * LL + w * (D / 4) + 4 * g) = x;
+            for (int e = 0; e < 4; ++e) x[e] = row < nrows ? fast_log2(r[u][e]) : 0.0f;
+            *reinterpret_cast<f32x4_t*>(sL + row * LL + col) = x;
+        }
+    }
+
+    static __device__ __forceinline__ void scan(float* sL, int LL, int w, int lane) {
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            f32x4_t* p = reinterpret_cast<f32x4_t*>(sL + lane * LL + w * (D / 4) + 4 * g);
+            f32x4_t x = *p;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = wave_incl_scan(x[e]);
+            *p = x;
         }
     }
 };
@@ -267,13 +284,15 @@ void vd_totals_kernel(VdArgs args) {
         VdDecays<D> ra;
         rk.load(reinterpret_cast<const E*>(args.k) + size_t(bh) * N * D, tid, ts, nrows);
         rv.load(reinterpret_cast<const E*>(args.v) + size_t(bh) * N * DV, tid, ts, nrows);
-        ra.load(args.a + size_t(bh) * N * D, w, lane, ts, nrows);
-        ra.store(sL, LL, w, lane, nrows);
+        ra.load(args.a + size_t(bh) * N * D, tid, ts, nrows);
+        ra.store(sL, LL, tid, nrows);
         rk.template store<true>(sK, LQ, tid, nrows);
         rv.template store<false>(sV, LV, tid, nrows);
         // V's pad: a column of ones, so the z part comes out of the state product
         if (tid < C)
             *reinterpret_cast<f32x4_t*>(sV + tid * LV + DV) = split_pad<E>(tid < nrows ? 1.0f : 0.0f);
+        __syncthreads();
+        VdDecays<D>::scan(sL, LL, w, lane);
         __syncthreads();
         vd_decay_keys<E, D>(sK, LQ, sL, LL, tid);
         __syncthreads();
@@ -367,14 +386,13 @@ void vd_out_kernel(VdArgs args) {
     using Sh = VdShape<E, D, DV>;
     using St = VdState<E, D, DV>;
     using X = Elem<E>;
-    constexpr int C = Sh::C, LQ = Sh::LQ, LV = Sh::LV, LA = Sh::LA, LL = Sh::LL, SU = St::SU, KZ = St::KZ;
+    constexpr int C = Sh::C, LQ = Sh::LQ, LV = Sh::LV, LL = Sh::LL, SU = St::SU, KZ = St::KZ;
     constexpr int NE = DV / 16, NJ = C / 16;
     extern __shared__ __align__(16) unsigned char smem[];
     E* sQ = reinterpret_cast<E*>(smem + Sh::kOffQ);
     E* sK = reinterpret_cast<E*>(smem + Sh::kOffK);
     E* sV = reinterpret_cast<E*>(smem + Sh::kOffV);
     E* sS = reinterpret_cast<E*>(smem + Sh::kOffS);
-    E* sA = reinterpret_cast<E*>(smem + Sh::kOffA);
     float* sL = reinterpret_cast<float*>(smem + Sh::kOffL);
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
     const int l16 = lane & 15, g4 = lane >> 4;
@@ -406,7 +424,7 @@ void vd_out_kernel(VdArgs args) {
         rq.load(reinterpret_cast<const E*>(args.q) + size_t(bh) * N * D, tid, ts, nrows);
         rk.load(reinterpret_cast<const E*>(args.k) + size_t(bh) * N * D, tid, ts, nrows);
         rv.load(reinterpret_cast<const E*>(args.v) + size_t(bh) * N * DV, tid, ts, nrows);
-        ra.load(args.a + size_t(bh) * N * D, w, lane, ts, nrows);
+        ra.load(args.a + size_t(bh) * N * D, tid, ts, nrows);
         St::stage(sS, LV, sacc, tid);
         if (l16 == 0) {
             // z_prev, split, into the state's pad columns: den's z part comes out of num
@@ -416,7 +434,7 @@ void vd_out_kernel(VdArgs args) {
                 for (int r = 0; r < 4; ++r)
                     *reinterpret_cast<f32x4_t*>(sS + (16 * (w + 4 * t) + 4 * g4 + r) * LV + DV) = split_pad<E>(zv[t][r]);
         }
-        ra.store(sL, LL, w, lane, nrows);
+        ra.store(sL, LL, tid, nrows);
         rq.template store<true>(sQ, LQ, tid, nrows);
         rk.template store<true>(sK, LQ, tid, nrows);
         rv.template store<false>(sV, LV, tid, nrows);
@@ -425,40 +443,45 @@ void vd_out_kernel(VdArgs args) {
             *reinterpret_cast<f32x4_t*>(sV + tid * LV + DV) = split_pad<E>(tid < nrows ? 1.0f : 0.0f);
     }
     __syncthreads();
+    VdDecays<D>::scan(sL, LL, w, lane);
+    __syncthreads();
 
-    const int i0 = 16 * w;            // this wave's query rows (block I = w)
-    // num = (Fq * 2^L_i) S_prev, with an extra column block: S's pad columns hold z_prev
-    // split, V's a column of ones, so columns 0 + 1 of num[NE] end as den
-    f32x4_t num[NE + 1];
+    // This wave's query rows (block I = w); this lane's row of the transposed tiles.
+    const int i0 = 16 * w, il = i0 + l16;
+    // num^T[e][i] = ((Fq * 2^L) S_prev)^T + (A V)^T, with an extra block of rows e = Dv,
+    // Dv + 1: S's pad columns hold z_prev split and V's a column of ones, so they end as
+    // den's two parts
+    f32x4_t nt[NE + 1];
 #pragma unroll
-    for (int et = 0; et <= NE; ++et) num[et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int et = 0; et <= NE; ++et) nt[et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
         const int d0 = 32 * ks + 8 * g4;
-        const F8<E> fq = frag_row(sQ, LQ, i0 + l16, d0);
+        const F8<E> fq = frag_row(sQ, LQ, il, d0);
         F8<E> a;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            a.x[e] = X::from_f32(X::to_f32(fq.x[e]) * fast_exp2(sL[(i0 + l16) * LL + d0 + e]));
+        for (int e = 0; e < 8; ++e) a.x[e] = X::from_f32(X::to_f32(fq.x[e]) * fast_exp2(sL[il * LL + d0 + e]));
 #pragma unroll
-        for (int et = 0; et <= NE; ++et) num[et] = mma(a, frag_col(sS, LV, d0, 16 * et, l16), num[et]);
+        for (int et = 0; et <= NE; ++et) nt[et] = mma(frag_col(sS, LV, d0, 16 * et, l16), a, nt[et]);
     }
 
-    // A over the blocks J <= I into sA (E).  The blocks J < I share one reference row,
-    // R = 16 I - 1 (the row in front of the wave's block): the queries are rescaled once,
-    // qa_i = Fq_i 2^(L_i - L_R) (at least 2^-128 over 16 rows), and every key block
-    // against it, kb_j = Fk_j 2^(L_R - L_j) <= 1 (a distant key that underflows carries a
-    // weight below 2^-128 anyway).  The diagonal block J = I uses its middle row.
+    // A over the blocks J <= I, transposed: lane (l16, g4) holds query il against keys
+    // 16 jt + 4 g4 + r, the operand layout of the 16x16x16 product with V.  The blocks
+    // J < I share one reference row, R = 16 I - 1 (the row in front of the wave's block):
+    // the queries are rescaled once, qa_i = Fq_i 2^(L_i - L_R) (at least 2^-128 over 16
+    // rows), and every key block against it, kb_j = Fk_j 2^(L_R - L_j) <= 1 (a distant key
+    // that underflows carries a weight below 2^-128 anyway).  The diagonal block J = I
+    // uses its middle row.
     F8<E> qa_off[D / 32];
     if (w > 0) {
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks) {
             const int d0 = 32 * ks + 8 * g4;
-            const F8<E> fq = frag_row(sQ, LQ, i0 + l16, d0);
+            const F8<E> fq = frag_row(sQ, LQ, il, d0);
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                qa_off[ks].x[e] = X::from_f32(X::to_f32(fq.x[e]) *
-                                              fast_exp2(sL[(i0 + l16) * LL + d0 + e] - sL[(i0 - 1) * LL + d0 + e]));
+                qa_off[ks].x[e] =
+                    X::from_f32(X::to_f32(fq.x[e]) * fast_exp2(sL[il * LL + d0 + e] - sL[(i0 - 1) * LL + d0 + e]));
         }
     }
 #pragma unroll
@@ -474,55 +497,55 @@ void vd_out_kernel(VdArgs args) {
                 for (int e = 0; e < 8; ++e)
                     kb.x[e] = X::from_f32(X::to_f32(fk.x[e]) *
                                           fast_exp2(sL[(i0 - 1) * LL + d0 + e] - sL[(16 * jt + l16) * LL + d0 + e]));
-                acc = mma(qa_off[ks], kb, acc);
+                acc = mma(kb, qa_off[ks], acc);
             }
         } else if (jt == w) {
             const int ref = 16 * jt + 7;
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks) {
                 const int d0 = 32 * ks + 8 * g4;
-                const F8<E> fq = frag_row(sQ, LQ, i0 + l16, d0);
+                const F8<E> fq = frag_row(sQ, LQ, il, d0);
                 const F8<E> fk = frag_row(sK, LQ, 16 * jt + l16, d0);
                 F8<E> qa, kb;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float lr = sL[ref * LL + d0 + e];
-                    qa.x[e] = X::from_f32(X::to_f32(fq.x[e]) * fast_exp2(sL[(i0 + l16) * LL + d0 + e] - lr));
+                    qa.x[e] = X::from_f32(X::to_f32(fq.x[e]) * fast_exp2(sL[il * LL + d0 + e] - lr));
                     kb.x[e] = X::from_f32(X::to_f32(fk.x[e]) * fast_exp2(lr - sL[(16 * jt + l16) * LL + d0 + e]));
                 }
-                acc = mma(qa, kb, acc);
+                acc = mma(kb, qa, acc);
             }
         }
+        if (jt <= w) {
+            f32x4_t x;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = i0 + 4 * g4 + r, j = 16 * jt + l16;
-            sA[i * LA + j] = X::from_f32((jt <= w && j <= i) ? acc[r] : 0.0f);
+            for (int r = 0; r < 4; ++r) x[r] = (16 * jt + 4 * g4 + r <= il) ? acc[r] : 0.0f;
+            const F4<E> pa = pack4<E>(x);
+#pragma unroll
+            for (int et = 0; et <= NE; ++et)
+                nt[et] = mma4(frag4_col(sV, LV, 16 * jt + 4 * g4, 16 * et, l16), pa, nt[et]);
         }
     }
-    __syncthreads();
 
-    // num += A V (the extra block adds A's row sums to den); the keys, read for A above,
-    // become Fk~ for the state step
-    for (int ks = 0; ks <= (w >> 1); ++ks) {
-        const F8<E> a = frag_row(sA, LA, i0 + l16, 32 * ks + 8 * g4);
+    // o = num / max(den, eps) (or num): four consecutive columns of row il per lane; den
+    // sits in lanes g4 = 0 (rows Dv and Dv + 1 of the extra block)
+    {
+        const float den = __shfl(nt[NE][0] + nt[NE][1], l16, kWave);
+        const float inv = args.normalize ? 1.0f / fmaxf(den, args.eps) : 1.0f;
+        if (ts + il < N) {
 #pragma unroll
-        for (int et = 0; et <= NE; ++et) num[et] = mma(a, frag_col(sV, LV, 32 * ks + 8 * g4, 16 * et, l16), num[et]);
+            for (int et = 0; et < NE; ++et) {
+                f32x4_t o;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[r] = nt[et][r] * inv;
+                store4<E>(ob + size_t(ts + il) * DV + 16 * et + 4 * g4, o);
+            }
+        }
     }
+    __syncthreads();                  // every read of the raw keys is done
     vd_decay_keys<E, D>(sK, LQ, sL, LL, tid);
     __syncthreads();
 
-    // o = num / max(den, eps) (or num), written from the accumulators; den of row
-    // i0 + 4 g4 + r is columns 0 + 1 of num[NE], broadcast from lane 0 of the row group
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int i = i0 + 4 * g4 + r;
-        const float den = dpp_move<0x150>(pair01(num[NE][r]));      // row_newbcast:0
-        const float inv = args.normalize ? 1.0f / fmaxf(den, args.eps) : 1.0f;
-        if (ts + i < N) {
-#pragma unroll
-            for (int et = 0; et < NE; ++et) ob[size_t(ts + i) * DV + 16 * et + l16] = X::from_f32(num[et][r] * inv);
-        }
-    }
     // the state carried across the chunk: S <- Diag(2^L_last) S + Fk~^T V, z alike (the
     // extra column block: V's pad column of ones)
 #pragma unroll

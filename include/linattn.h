@@ -146,8 +146,9 @@ linattn_status_t linattn_fwd_ex(
  *     2^-8 <= a <= 1 (within a 16-token block the rescaled operands of the chunk products
  *     stay below 2^64).
  *  Every other argument is as for linattn_fwd_ex; the workspace is sized by
- *  linattn_fwd_vdecay_workspace_size (the state after every 64-token chunk).  Supported
- *  shapes: D, Dv in {64, 128}; bf16 at every pair, f32 at D = 64.
+ *  linattn_fwd_vdecay_workspace_size (room for the state after every 64-token chunk).
+ *  Supported shapes: D, Dv in {64, 128}; bf16 at every pair, f32 unless D = Dv = 128
+ *  (LINATTN_ERR_UNSUPPORTED).
  */
 size_t linattn_fwd_vdecay_workspace_size(int B, int H, int N, int D, int Dv);
 

@@ -47,6 +47,7 @@ CASES = [
     (1, 2, 200, 64, 128, "bf16"),
     (1, 1, 1, 64, 64, "bf16"),
     (3, 1, 1025, 64, 64, "bf16"),
+    (1, 2, 150, 128, 64, "f32"),
 ]
 
 
@@ -68,7 +69,7 @@ def test_vdecay_small_against_oracle(case, normalize):
 
 
 def test_vdecay_unsupported_raises():
-    inp = workloads.random_inputs(3, 1, 1, 64, 128, 64, dtype="f32")
+    inp = workloads.random_inputs(3, 1, 1, 64, 128, 128, dtype="f32")
     a = decay(4, (1, 1, 64, 128), 0.5)
     with pytest.raises(RuntimeError, match="unsupported"):
         binding.fwd_vdecay(*(_dev(inp[n]) for n in ("q", "k", "v")), _dev(a))
