@@ -201,8 +201,9 @@ linattn_status_t linattn_fwd_features(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Bytes of device scratch linattn_bwd needs for these sizes and dtype (the state in
- * front of every 64-token chunk and its adjoint, float, plus per-token intermediates).
+ * Bytes of device scratch linattn_bwd needs for these sizes and dtype (room for the
+ * state in front of every run of 64-token chunks and its adjoint, float, at any run
+ * length, plus per-token intermediates).
  * 0 when B*H*N == 0 or a size is not positive.  Contents are undefined after a call; it
  * must not be shared by calls that may run concurrently.
  */
