@@ -116,7 +116,9 @@ struct WalkShape {
     static constexpr size_t kOffSt = kOffVt + size_t(DV) * LKT * sizeof(E);
     static constexpr size_t kOffZb = kOffSt + (OUT ? size_t(DV) * LS * sizeof(E) : 0);
     static constexpr size_t kOffLam = kOffZb + (OUT ? size_t(4) * LZ * sizeof(E) : 0);
-    static constexpr size_t kBytes = kOffLam + size_t(CH) * 4;
+    static constexpr size_t kOffO = kOffLam + size_t(CH) * 4;
+    static constexpr int kOBlock = 16 * 128;          // per wave: 16 rows x 128 bytes of o
+    static constexpr size_t kBytes = kOffO + (OUT ? size_t(kThreads / kWave) * kOBlock : 0);
     static_assert(kBytes == walk_lds_bytes(int(sizeof(E)), D, DV, CH, GATED, OUT), "host LDS formula out of step");
     // waves per SIMD the kernel is compiled for (amdgpu_waves_per_eu): a fixed target keeps
     // the compiler from squeezing registers for an occupancy the shape cannot reach, which
@@ -193,25 +195,19 @@ __device__ __forceinline__ F8<uint16_t> tr_operand(const uint16_t* tile, int k0,
 
 // One head's output rows as a buffer resource: stores past its end (rows past N) are
 // dropped by the hardware, so the tail needs no branch.  Byte offsets are 32-bit; the
-// library keeps every head's output below 2 GiB.
+// library keeps every head's output below 2 GiB.  The stores are non-temporal (cache
+// policy bit nt, aux = 2): o is written once and never read back by the walk, and keeping
+// it out of the caches leaves them to the K and V that the output walk reads again after
+// the totals walk (bf16, B=8 H=16 N=4096 D=Dv=64, 128-token chunks: the forward step 83.4 -> 80-82 us).
+typedef int v4i_t __attribute__((ext_vector_type(4)));
 struct OutRsrc {
+    static constexpr int kNonTemporal = 2;
     __amdgpu_buffer_rsrc_t r;
     __device__ __forceinline__ void init(void* base, unsigned bytes) {
         r = __builtin_amdgcn_make_buffer_rsrc(base, 0, int(bytes), 0x00020000);
     }
-    __device__ __forceinline__ void store(const F4<uint16_t>& v, int off) const {
-        typedef int v2i __attribute__((ext_vector_type(2)));
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2i, v), r, off, 0, 0);
-    }
-    __device__ __forceinline__ void store(const F8<uint16_t>& v, int off) const {
-        typedef int v4i __attribute__((ext_vector_type(4)));
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), r, off, 0, 0);
-    }
-    __device__ __forceinline__ void store(const F8<float>& v, int off) const {
-        typedef int v4i __attribute__((ext_vector_type(4)));
-        const v4i* h = reinterpret_cast<const v4i*>(&v);
-        __builtin_amdgcn_raw_buffer_store_b128(h[0], r, off, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(h[1], r, off + 16, 0, 0);
+    __device__ __forceinline__ void store(const v4i_t& v, int off) const {
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kNonTemporal);
     }
 };
 
@@ -248,6 +244,7 @@ struct ChunkWalker {
     E* sSt;
     E* sZb;        // [4][LZ]: z high part, z low part, two zero rows
     float* sLam;
+    unsigned char* sO;   // this wave's 16 x 128-byte block of o (output walk)
     int tid, w, lane, l16, g4;
     int N;
     int last;      // last row the loads may touch: the end of the walked range (clamped to N - 1)
@@ -288,6 +285,7 @@ struct ChunkWalker {
         sLam = reinterpret_cast<float*>(smem + Sh::kOffLam);
         tid = threadIdx.x;
         w = __builtin_amdgcn_readfirstlane(tid / kWave);
+        sO = smem + Sh::kOffO + size_t(w) * Sh::kOBlock;
         lane = tid % kWave;
         l16 = lane & 15;
         g4 = lane >> 4;
@@ -542,6 +540,42 @@ struct ChunkWalker {
         }
     }
 
+    // One query strip of o out to memory: rows row0 .. row0 + 15, the lane holding row
+    // l16's columns 32t + 8g4 .. 32t + 8g4 + 7 in outv[t].  A store of those directly
+    // writes half of each of 16 rows' 128-byte lines per instruction; here each 128-byte
+    // column block goes through this wave's LDS block first (16-byte group j of row r at
+    // slot j ^ (r & 7): conflict-free writes of 8 rows per cycle and reads of whole rows)
+    // and is read back so that each store instruction writes 8 whole rows' lines.  The
+    // wave's LDS operations complete in order, so only the compiler has to be kept from
+    // moving them (wave_barrier).  Rows past N fall outside the output resource and are
+    // dropped by the hardware.
+    __device__ __forceinline__ void store_strip(const F8<E> (&outv)[DV / 32], int row0, const OutRsrc& ob) const {
+        constexpr int RB = DV * int(sizeof(E));   // bytes per row of o
+        constexpr int GPT = int(sizeof(E)) / 2;   // 16-byte groups per lane in each outv[t]
+        const v4i_t* src = reinterpret_cast<const v4i_t*>(outv);
+#pragma unroll
+        for (int c = 0; c < RB / 128; ++c) {
+#pragma unroll
+            for (int t = 0; t < DV / 32; ++t) {
+                // group 4 GPT t + GPT g4 + h of the row: column block (4 GPT t) / 8 for every g4
+                if ((4 * GPT * t) / 8 != c) continue;
+#pragma unroll
+                for (int h = 0; h < GPT; ++h) {
+                    const int j = (4 * GPT * t) % 8 + GPT * g4 + h;
+                    *reinterpret_cast<v4i_t*>(sO + 128 * l16 + ((j ^ (l16 & 7)) << 4)) = src[GPT * t + h];
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int r = 8 * i + (lane >> 3), j = lane & 7;
+                const v4i_t x = *reinterpret_cast<const v4i_t*>(sO + 128 * r + ((j ^ (r & 7)) << 4));
+                ob.store(x, (row0 + r) * RB + 128 * c + 16 * j);
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+
     // Outputs of the chunk starting at ts for the query strips of wave WV (the variant
     // used once D * Dv reaches 128 x 128, with one strip per wave).  The wave is a compile-time constant here, so its strips, their key-block counts and their
     // diagonal blocks are too: the loops below unroll into straight-line code in which
@@ -657,18 +691,16 @@ struct ChunkWalker {
         for (int m = 0; m < MS; ++m) {
             if (strip(m) < 0) continue;
             const float inv = norm ? __builtin_amdgcn_rcpf(fmaxf(accd[m][0] + accd[m][1], eps)) : 1.0f;
-            // rows past N fall outside the output resource and are dropped by the hardware
-            const int row = ts + 16 * strip(m) + l16;
+            F8<E> outv[NT / 2];
 #pragma unroll
             for (int t = 0; t < NT / 2; ++t) {
-                F8<E> outv;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    outv.x[r] = X::from_f32(acc[m][2 * t][r] * inv);
-                    outv.x[4 + r] = X::from_f32(acc[m][2 * t + 1][r] * inv);
+                    outv[t].x[r] = X::from_f32(acc[m][2 * t][r] * inv);
+                    outv[t].x[4 + r] = X::from_f32(acc[m][2 * t + 1][r] * inv);
                 }
-                ob.store(outv, (row * DV + 32 * t + 8 * g4) * int(sizeof(E)));
             }
+            store_strip(outv, ts + 16 * strip(m), ob);
         }
     }
 
@@ -749,18 +781,16 @@ struct ChunkWalker {
             for (int p = 0; p + 1 < npairs; ++p) pair<false>(p, qi, lam_q, fq[m], ones_a, acc, accd);
             pair<true>(npairs - 1, qi, lam_q, fq[m], ones_a, acc, accd);
             const float inv = norm ? __builtin_amdgcn_rcpf(fmaxf(accd[0] + accd[1], eps)) : 1.0f;
-            // rows past N fall outside the output resource and are dropped by the hardware
-            const int row = ts + qi;
+            F8<E> outv[DV / 32];
 #pragma unroll
             for (int t = 0; t < DV / 32; ++t) {
-                F8<E> outv;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    outv.x[r] = X::from_f32(acc[2 * t][r] * inv);
-                    outv.x[4 + r] = X::from_f32(acc[2 * t + 1][r] * inv);
+                    outv[t].x[r] = X::from_f32(acc[2 * t][r] * inv);
+                    outv[t].x[4 + r] = X::from_f32(acc[2 * t + 1][r] * inv);
                 }
-                ob.store(outv, (row * DV + 32 * t + 8 * g4) * int(sizeof(E)));
             }
+            store_strip(outv, ts + 16 * s, ob);
         }
     }
 

@@ -37,8 +37,10 @@ inline bool chunk_is_built(int chunk) { return chunk == 32 || chunk == 64 || chu
 constexpr size_t walk_lds_bytes(int esize, int D, int Dv, int chunk, bool gated, bool out = true) {
     const size_t es = size_t(esize), lkt = size_t(chunk) + (chunk >= 128 ? 16 : 0);
     const bool kt = !out || gated || esize != 2;
+    // the output walk also holds one 16-row x 128-byte block of o for each of its four waves
     return (out ? size_t(chunk) * D * es : 0) + (kt ? size_t(D) * lkt * es : 0) + size_t(Dv) * lkt * es +
-           (out ? size_t(Dv) * D * es + size_t(4) * (D + 8) * es : 0) + size_t(chunk) * 4;
+           (out ? size_t(Dv) * D * es + size_t(4) * (D + 8) * es : 0) + size_t(chunk) * 4 +
+           (out ? size_t(4) * 16 * 128 : 0);
 }
 
 constexpr size_t kMaxLds = 160 * 1024;   // LDS per compute unit on gfx950
