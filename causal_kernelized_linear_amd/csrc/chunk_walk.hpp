@@ -202,6 +202,11 @@ __device__ __forceinline__ F8<uint16_t> tr_operand(const uint16_t* tile, int k0,
 // 27.4 us instead of 23.7 (bf16, B=8 H=16 N=4096 D=Dv=64, 128-token chunks; the forward
 // step went from 83.4 to 79-82 us).
 typedef int v4i_t __attribute__((ext_vector_type(4)));
+// The 16-byte groups of one F8<E> (one for bf16, two for fp32), as bits.
+template <typename E>
+struct Groups16 {
+    v4i_t g[sizeof(F8<E>) / 16];
+};
 struct OutRsrc {
     static constexpr int kNonTemporal = 2;
     __amdgpu_buffer_rsrc_t r;
@@ -554,17 +559,18 @@ struct ChunkWalker {
     __device__ __forceinline__ void store_strip(const F8<E> (&outv)[DV / 32], int row0, const OutRsrc& ob) const {
         constexpr int RB = DV * int(sizeof(E));   // bytes per row of o
         constexpr int GPT = int(sizeof(E)) / 2;   // 16-byte groups per lane in each outv[t]
-        const v4i_t* src = reinterpret_cast<const v4i_t*>(outv);
+        static_assert(sizeof(F8<E>) == 16 * GPT, "outv[t] is GPT 16-byte groups");
 #pragma unroll
         for (int c = 0; c < RB / 128; ++c) {
 #pragma unroll
             for (int t = 0; t < DV / 32; ++t) {
                 // group 4 GPT t + GPT g4 + h of the row: column block (4 GPT t) / 8 for every g4
                 if ((4 * GPT * t) / 8 != c) continue;
+                const Groups16<E> grp = __builtin_bit_cast(Groups16<E>, outv[t]);
 #pragma unroll
                 for (int h = 0; h < GPT; ++h) {
                     const int j = (4 * GPT * t) % 8 + GPT * g4 + h;
-                    *reinterpret_cast<v4i_t*>(sO + 128 * l16 + ((j ^ (l16 & 7)) << 4)) = src[GPT * t + h];
+                    *reinterpret_cast<v4i_t*>(sO + 128 * l16 + ((j ^ (l16 & 7)) << 4)) = grp.g[h];
                 }
             }
             __builtin_amdgcn_wave_barrier();
