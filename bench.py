@@ -599,7 +599,7 @@ def main():
         sweep = {}
         for c in wl.chunks:
             try:
-                rl = time_forward(wl, c, max(3, extra_steps // 2), 2, ev, rotate_bytes=2.5e9)
+                rl = time_forward(wl, c, max(3, extra_steps // 2), extra_warm, ev, rotate_bytes=2.5e9)
             except RuntimeError as e:
                 sweep[str(c)] = {"status": str(e)}
                 continue
