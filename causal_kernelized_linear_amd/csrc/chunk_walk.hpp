@@ -195,12 +195,13 @@ __device__ __forceinline__ F8<uint16_t> tr_operand(const uint16_t* tile, int k0,
 
 // One head's output rows as a buffer resource: stores past its end (rows past N) are
 // dropped by the hardware, so the tail needs no branch.  Byte offsets are 32-bit; the
-// library keeps every head's output below 2 GiB.  The stores are non-temporal (cache
-// policy bit nt, aux = 2) and write whole 128-byte lines (store_strip): o is written once
-// and never read back, and its write-back then happens inside this walk instead of
-// running beside the next kernel.  With plain stores the totals walk that follows took
-// 27.4 us instead of 23.7 (bf16, B=8 H=16 N=4096 D=Dv=64, 128-token chunks; the forward
-// step went from 83.4 to 79-82 us).
+// library keeps every head's output below 2 GiB.  The stores are non-temporal at device
+// scope (cache policy bits nt and sc1, aux = 18) and write whole 128-byte lines
+// (store_strip): o is written once and never read back, and its write-back then happens
+// inside this walk instead of running beside the next kernel.  With plain stores the
+// totals walk that follows took 29.4 us instead of 24.8; nt alone gave the output walk
+// 52.2 us, nt with sc1 49.8-50.7 (bf16, B=8 H=16 N=4096 D=Dv=64, 128-token chunks,
+// event-timed at steady clocks).
 typedef int v4i_t __attribute__((ext_vector_type(4)));
 // The 16-byte groups of one F8<E> (one for bf16, two for fp32), as bits.
 template <typename E>
@@ -208,7 +209,7 @@ struct Groups16 {
     v4i_t g[sizeof(F8<E>) / 16];
 };
 struct OutRsrc {
-    static constexpr int kNonTemporal = 2;
+    static constexpr int kNonTemporal = 18;
     __amdgpu_buffer_rsrc_t r;
     __device__ __forceinline__ void init(void* base, unsigned bytes) {
         r = __builtin_amdgcn_make_buffer_rsrc(base, 0, int(bytes), 0x00020000);
