@@ -146,10 +146,21 @@ linattn_status_t fwd_common(const void* q, const void* k, const void* v, const f
                           static_cast<const void*>(s_out), static_cast<const void*>(z_out)})
         if (p && !aligned16(p)) return LINATTN_ERR_INVALID_ARGUMENT;
     const size_t es = esize(dtype);
-    const size_t nqk = size_t(BH) * N * D * es, nv = size_t(BH) * N * Dv * es;
-    if (overlap(o, nv, q, nqk) || overlap(o, nv, k, nqk) || overlap(o, nv, v, nv) ||
-        overlap(o, nv, g, size_t(BH) * N * 4))
+    const size_t nqk = size_t(BH) * N * D * es, nv = size_t(BH) * N * Dv * es, ng = size_t(BH) * N * 4;
+    const size_t ns = size_t(BH) * D * Dv * 4, nz = size_t(BH) * D * 4;
+    // o is written while other workgroups still read every input and the initial state;
+    // the final state is written after every read of the inputs, so s_out / z_out may
+    // share memory with s0 / z0 but with nothing else
+    if (overlap(o, nv, q, nqk) || overlap(o, nv, k, nqk) || overlap(o, nv, v, nv) || overlap(o, nv, g, ng) ||
+        overlap(o, nv, s0, ns) || overlap(o, nv, z0, nz))
         return LINATTN_ERR_INVALID_ARGUMENT;
+    for (const auto& fin : {std::make_pair(static_cast<const void*>(s_out), ns),
+                            std::make_pair(static_cast<const void*>(z_out), nz)})
+        if (overlap(fin.first, fin.second, q, nqk) || overlap(fin.first, fin.second, k, nqk) ||
+            overlap(fin.first, fin.second, v, nv) || overlap(fin.first, fin.second, g, ng) ||
+            overlap(fin.first, fin.second, o, nv))
+            return LINATTN_ERR_INVALID_ARGUMENT;
+    if (overlap(s_out, ns, z_out, nz)) return LINATTN_ERR_INVALID_ARGUMENT;
     // outputs are addressed with 32-bit byte offsets per head
     if ((size_t(N) + 256) * size_t(Dv) * es >= (size_t(1) << 31)) return LINATTN_ERR_UNSUPPORTED;
     if (!dim_ok(D) || !dim_ok(Dv) || !linattn::chunk_is_built(chunk) ||
@@ -157,9 +168,8 @@ linattn_status_t fwd_common(const void* q, const void* k, const void* v, const f
         return LINATTN_ERR_UNSUPPORTED;
     const Plan plan = make_plan(BH, N, D, Dv, chunk, target_workgroups(int(es), D, Dv, chunk, g != nullptr));
     if (ws_bytes < plan.bytes || !ws || !aligned16(ws)) return LINATTN_ERR_WORKSPACE;
-    const size_t ns = size_t(BH) * D * Dv * 4, nz = size_t(BH) * D * 4;
     if (overlap(ws, plan.bytes, q, nqk) || overlap(ws, plan.bytes, k, nqk) || overlap(ws, plan.bytes, v, nv) ||
-        overlap(ws, plan.bytes, o, nv) || overlap(ws, plan.bytes, g, size_t(BH) * N * 4) ||
+        overlap(ws, plan.bytes, o, nv) || overlap(ws, plan.bytes, g, ng) ||
         overlap(ws, plan.bytes, s0, ns) || overlap(ws, plan.bytes, s_out, ns) || overlap(ws, plan.bytes, z0, nz) ||
         overlap(ws, plan.bytes, z_out, nz))
         return LINATTN_ERR_WORKSPACE;

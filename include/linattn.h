@@ -82,11 +82,14 @@ size_t linattn_fwd_workspace_size(int B, int H, int N, int D, int Dv, int chunk)
  *
  *  q, k   [B,H,N,D]   dtype         input, read-only
  *  v      [B,H,N,Dv]  dtype         input, read-only
- *  o      [B,H,N,Dv]  dtype         output; must not alias any input
+ *  o      [B,H,N,Dv]  dtype         output; must not overlap any input, s0 or z0
  *  s0     [B,H,D,Dv]  float or NULL initial state S (NULL: zeros)
  *  z0     [B,H,D]     float or NULL initial normaliser z (NULL: zeros)
  *  s_out  [B,H,D,Dv]  float or NULL final state S_N (NULL: not written); may equal s0
  *  z_out  [B,H,D]     float or NULL final normaliser z_N (NULL: not written); may equal z0
+ *                     (s_out and z_out may share memory with s0 and z0, which are read
+ *                     before the final state is written, but not with q, k, v, g, o or
+ *                     each other: LINATTN_ERR_INVALID_ARGUMENT)
  *  chunk               tokens per chunk (the last chunk of a sequence may be shorter)
  *  eps > 0             denominator clamp: o = num / max(den, eps)
  *  workspace           device scratch of at least linattn_fwd_workspace_size(...) bytes,

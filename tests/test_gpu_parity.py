@@ -65,6 +65,8 @@ SMALL = [
     (1, 3, 1000, 64, 64, "bf16", 64),
     (1, 2, 777, 128, 128, "bf16", 128),
     (1, 2, 333, 128, 64, "bf16", 64),
+    (1, 2, 777, 128, 64, "bf16", 256),
+    (1, 2, 300, 64, 64, "f32", 128),
     (2, 1, 515, 64, 128, "bf16", 256),
     (1, 1, 1, 64, 64, "bf16", 128),
     (1, 1, 17, 128, 128, "bf16", 32),
@@ -238,6 +240,7 @@ def test_workload_fp32_small_full():
     o_ref, S_ref, z_ref = oracle_fwd(inp)
     assert rowwise_rel_err(to64(o), o_ref) <= TOL["f32"]
     assert matrix_rel_err(to64(S), S_ref) <= TOL["f32"]
+    assert matrix_rel_err(to64(z), z_ref) <= TOL["f32"]
 
 
 @pytest.mark.parametrize("name", ["train_bf16", "gated_bf16"])
