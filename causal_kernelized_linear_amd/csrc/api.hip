@@ -43,12 +43,14 @@ int device_cus() {
 // B*H*nseg reaches this count when the sequence is long enough: every workgroup is then
 // resident from the start, and the per-workgroup set-up (the state in front of the
 // segment, the first loads) is paid once.
-long target_workgroups(int esize, int D, int Dv, int chunk, bool gated) {
-    return long(device_cus()) * linattn::walk_waves(esize, D, Dv, chunk, gated, true);
+// vs: the column parts of Dv the walk is cut into (walk_vsplit), each with its own
+// workgroups.
+long target_workgroups(int esize, int D, int Dv, int chunk, bool gated, int vs = 1) {
+    return long(device_cus()) * linattn::walk_waves(esize, D, Dv / vs, chunk, gated, true);
 }
 
-// The largest target over the element types and both forwards: the workspace size does
-// not depend on them.
+// The largest target over the element types and both forwards (for the feature maps'
+// walk, which is never cut into column parts): the workspace size does not depend on them.
 long max_target_workgroups(int D, int Dv, int chunk) {
     long t = 0;
     for (int es : {2, 4})
@@ -62,23 +64,52 @@ long max_target_workgroups(int D, int Dv, int chunk) {
 struct Plan {
     int nseg = 0;
     int L = 0;
+    int vs = 1;
     size_t bytes = 0;
 };
 
-// nseg grows with the target (never shrinks), so the workspace sized for the largest
-// target serves every smaller one.
-Plan make_plan(long BH, int N, int D, int Dv, int chunk, long target) {
+// Each of the B*H*vs (head, column part) pairs is cut into nseg segments so that their
+// count reaches the target.  nseg grows with the target (never shrinks), so the workspace
+// sized for the largest target serves every smaller one.
+Plan make_plan(long BH, int N, int D, int Dv, int chunk, long target, int vs = 1) {
     Plan p;
+    const long heads = BH * vs;
     const long nc = (long(N) + chunk - 1) / chunk;
-    long nseg = (target + BH - 1) / BH;
+    long nseg = (target + heads - 1) / heads;
     if (nseg < 1) nseg = 1;
     if (nseg > nc) nseg = nc;
     const long L = (nc + nseg - 1) / nseg;
     nseg = (nc + L - 1) / L;
     p.nseg = int(nseg);
     p.L = int(L);
-    p.bytes = linattn::fwd_workspace_layout(size_t(BH) * size_t(nseg), D, Dv, nullptr, nullptr);
+    p.vs = vs;
+    p.bytes = linattn::fwd_workspace_layout(size_t(heads) * size_t(nseg), D, Dv / vs, nullptr, nullptr);
     return p;
+}
+
+// The plan of the chunked or gated forward (vs = 0: the shape is not supported).
+Plan fwd_plan(int esize, long BH, int N, int D, int Dv, int chunk, bool gated) {
+    const int vs = linattn::walk_vsplit(esize, D, Dv, chunk, gated);
+    if (vs == 0) {
+        Plan p;
+        p.vs = 0;
+        return p;
+    }
+    return make_plan(BH, N, D, Dv, chunk, target_workgroups(esize, D, Dv, chunk, gated, vs), vs);
+}
+
+// Workspace bytes that serve the forward of this shape whatever its element type and
+// gating: the largest of their plans.
+size_t fwd_workspace_bytes(long BH, int N, int D, int Dv, int chunk) {
+    size_t b = 0;
+    for (int es : {2, 4})
+        for (bool gated : {false, true}) {
+            const Plan p = fwd_plan(es, BH, N, D, Dv, chunk, gated);
+            if (p.vs != 0 && p.bytes > b) b = p.bytes;
+        }
+    if (b == 0)   // no element type supports the shape: the plan it would have uncut
+        b = make_plan(BH, N, D, Dv, chunk, max_target_workgroups(D, Dv, chunk)).bytes;
+    return b;
 }
 
 // Measurement hook (linattn_set_profile_events): one-shot, process-wide.
@@ -163,10 +194,9 @@ linattn_status_t fwd_common(const void* q, const void* k, const void* v, const f
     if (overlap(s_out, ns, z_out, nz)) return LINATTN_ERR_INVALID_ARGUMENT;
     // outputs are addressed with 32-bit byte offsets per head
     if ((size_t(N) + 256) * size_t(Dv) * es >= (size_t(1) << 31)) return LINATTN_ERR_UNSUPPORTED;
-    if (!dim_ok(D) || !dim_ok(Dv) || !linattn::chunk_is_built(chunk) ||
-        linattn::walk_lds_bytes(int(es), D, Dv, chunk, g != nullptr) > linattn::kMaxLds)
-        return LINATTN_ERR_UNSUPPORTED;
-    const Plan plan = make_plan(BH, N, D, Dv, chunk, target_workgroups(int(es), D, Dv, chunk, g != nullptr));
+    if (!dim_ok(D) || !dim_ok(Dv) || !linattn::chunk_is_built(chunk)) return LINATTN_ERR_UNSUPPORTED;
+    const Plan plan = fwd_plan(int(es), BH, N, D, Dv, chunk, g != nullptr);
+    if (plan.vs == 0) return LINATTN_ERR_UNSUPPORTED;
     if (ws_bytes < plan.bytes || !ws || !aligned16(ws)) return LINATTN_ERR_WORKSPACE;
     if (overlap(ws, plan.bytes, q, nqk) || overlap(ws, plan.bytes, k, nqk) || overlap(ws, plan.bytes, v, nv) ||
         overlap(ws, plan.bytes, o, nv) || overlap(ws, plan.bytes, g, ng) ||
@@ -182,7 +212,7 @@ linattn_status_t fwd_common(const void* q, const void* k, const void* v, const f
     L.s0 = s0; L.z0 = z0; L.s_out = s_out; L.z_out = z_out;
     L.ws = ws;
     L.BH = int(BH); L.N = N; L.D = D; L.Dv = Dv; L.chunk = chunk;
-    L.nseg = plan.nseg; L.L = plan.L; L.eps = eps;
+    L.nseg = plan.nseg; L.L = plan.L; L.vsplit = plan.vs; L.eps = eps;
     L.normalize = out == LINATTN_OUT_NORMALIZED ? 1 : 0;
     L.stream = static_cast<hipStream_t>(stream);
     take_profile_events(L.prof);
@@ -428,7 +458,7 @@ linattn_status_t linattn_bwd(const void* q, const void* k, const void* v, const 
 
 size_t linattn_fwd_workspace_size(int B, int H, int N, int D, int Dv, int chunk) {
     if (B <= 0 || H <= 0 || N <= 0 || D <= 0 || Dv <= 0 || chunk <= 0) return 0;
-    return make_plan(long(B) * long(H), N, D, Dv, chunk, max_target_workgroups(D, Dv, chunk)).bytes;
+    return fwd_workspace_bytes(long(B) * long(H), N, D, Dv, chunk);
 }
 
 linattn_status_t linattn_fwd_chunked(const void* q, const void* k, const void* v, void* o, const float* s0,

@@ -60,6 +60,13 @@
 //     chunk that crosses the end their features are zeroed.  The next chunk's K and V
 //     are in flight while this chunk's products run, and its Q while this chunk's
 //     state is folded.
+//   * column parts (VS > 1): the value columns are cut into VS parts of DV columns
+//     (rows of v, o, S0 and S_N are DV * VS wide), and each part is walked by its own
+//     workgroups with its own [D, DV] slice of S.  Every column of o depends on S's
+//     own columns only, so the parts never exchange anything; each recomputes phi(Q),
+//     phi(K), A and z.  Blocks i and i + 8 of the grid walk the two parts of one
+//     (head, segment), so both sit on the same XCD (workgroups are dealt to the eight
+//     XCDs round-robin) and read Q and K through one L2.
 #pragma once
 
 #include "device_common.hpp"
@@ -80,6 +87,7 @@ struct WalkArgs {
     const float* s0;     // [BH][D][Dv] initial state or NULL (caller layout)
     const float* z0;     // [BH][D] or NULL
     int N;
+    int BH;              // heads (B * H)
     int nseg;            // segments per sequence
     int L;               // chunks per segment
     int direct;          // 1: the output walk sums the totals in front of its segment itself
@@ -88,6 +96,28 @@ struct WalkArgs {
     int normalize;       // 1: o = num / max(den, eps); 0: o = num (the denominator is not used)
     float fshift;        // RELU walks only: the shift of relu(x) + shift
 };
+
+// Column part and item (head * segments + segment) of a walk workgroup.  With VS parts,
+// groups of 8 consecutive blocks take 8 consecutive items, one group per part in turn,
+// so the parts of an item are 8 blocks apart (the same XCD) and dispatched together.
+// item >= items: a padding block of the last group, which does nothing.
+template <int VS>
+__device__ __forceinline__ void walk_block(int items, int& item, int& part) {
+    if constexpr (VS == 1) {
+        item = blockIdx.x;
+        part = 0;
+    } else {
+        const int lo = blockIdx.x % 8, hi = blockIdx.x / 8;
+        part = hi % VS;
+        item = (hi / VS) * 8 + lo;
+    }
+    (void)items;
+}
+
+// Blocks of a walk launch over `items` (head, segment) pairs and VS column parts.
+__host__ __device__ constexpr unsigned walk_grid(unsigned items, int VS) {
+    return VS == 1 ? items : (items + 7) / 8 * 8 * unsigned(VS);
+}
 
 template <typename E, int D, int DV, int CH, bool GATED, bool OUT>
 struct WalkShape {
@@ -224,11 +254,12 @@ struct OutRsrc {
 // IDENT: q and k already hold the features (another map applied beforehand), so the
 // walker uses them as they are instead of applying elu + 1.  RELU: the features are
 // relu(x) + fshift, applied while staging like elu + 1.
-template <typename E, int D, int DV, int CH, bool GATED, bool OUT, bool IDENT = false, bool RELU = false>
+template <typename E, int D, int DV, int CH, bool GATED, bool OUT, bool IDENT = false, bool RELU = false, int VS = 1>
 struct ChunkWalker {
     using Sh = WalkShape<E, D, DV, CH, GATED, OUT>;
     using X = Elem<E>;
     static constexpr int LKT = Sh::LKT, LS = Sh::LS;
+    static constexpr int DVF = DV * VS;     // row length of v and o (all column parts)
     float fshift = 0.0f;
 
     __device__ __forceinline__ float feat(float x) const {
@@ -326,7 +357,7 @@ struct ChunkWalker {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = min(ts + 4 * kq + r, last);
-                R.rv[it][r] = *reinterpret_cast<const F8<E>*>(vb + size_t(row) * DV + 8 * cg);
+                R.rv[it][r] = *reinterpret_cast<const F8<E>*>(vb + size_t(row) * DVF + 8 * cg);
             }
         }
         if constexpr (GATED) {
@@ -558,7 +589,8 @@ struct ChunkWalker {
     // moving them (wave_barrier).  Rows past N fall outside the output resource and are
     // dropped by the hardware.
     __device__ __forceinline__ void store_strip(const F8<E> (&outv)[DV / 32], int row0, const OutRsrc& ob) const {
-        constexpr int RB = DV * int(sizeof(E));   // bytes per row of o
+        constexpr int RB = DV * int(sizeof(E));   // bytes per row of this column part of o
+        constexpr int RBF = DVF * int(sizeof(E)); // bytes from one row of o to the next
         constexpr int GPT = int(sizeof(E)) / 2;   // 16-byte groups per lane in each outv[t]
         static_assert(sizeof(F8<E>) == 16 * GPT, "outv[t] is GPT 16-byte groups");
 #pragma unroll
@@ -579,7 +611,7 @@ struct ChunkWalker {
             for (int i = 0; i < 2; ++i) {
                 const int r = 8 * i + (lane >> 3), j = lane & 7;
                 const v4i_t x = *reinterpret_cast<const v4i_t*>(sO + 128 * r + ((j ^ (r & 7)) << 4));
-                ob.store(x, (row0 + r) * RB + 128 * c + 16 * j);
+                ob.store(x, (row0 + r) * RBF + 128 * c + 16 * j);
             }
             __builtin_amdgcn_wave_barrier();
         }
@@ -822,16 +854,24 @@ struct ChunkWalker {
 // Accumulator-layout element r of state tile j of wave w, lane (l16, g4):
 // S[16a + 4 g4 + r][16b + l16] with a = w ZT + j / NB, b = j % NB; z tile i of wave w
 // holds z[16(w ZT + i) + 4 g4 + r] in its l16 == 0 lanes (zero elsewhere).
-template <typename E, int D, int DV, int CH, bool GATED, bool OUTPUT, bool IDENT = false, bool RELU = false>
+// VS column parts of DV columns each (VS = 1: the whole of Dv = DV).  The workspace
+// slots are per (head, part): slot (bh * VS + part) * nseg + s holds that part's
+// [D, DV] slice of the state and its own copy of z.
+template <typename E, int D, int DV, int CH, bool GATED, bool OUTPUT, bool IDENT = false, bool RELU = false,
+          int VS = 1>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     WalkShape<E, D, DV, CH, GATED, OUTPUT>::kWaves, WalkShape<E, D, DV, CH, GATED, OUTPUT>::kWaves))) void walk_kernel(WalkArgs args) {
     using Sh = WalkShape<E, D, DV, CH, GATED, OUTPUT>;
-    using W = ChunkWalker<E, D, DV, CH, GATED, OUTPUT, IDENT, RELU>;
+    using W = ChunkWalker<E, D, DV, CH, GATED, OUTPUT, IDENT, RELU, VS>;
+    constexpr int DVF = DV * VS;
     extern __shared__ __align__(16) unsigned char smem[];
 
     const int nsw = OUTPUT ? args.nseg : args.nseg - 1;    // the totals skip the last segment
-    const int seg = blockIdx.x % nsw;
-    const int bh = blockIdx.x / nsw;
+    int item, part;
+    walk_block<VS>(args.BH * nsw, item, part);
+    if (item >= args.BH * nsw) return;                      // padding block (uniform over the workgroup)
+    const int seg = item % nsw;
+    const int bh = item / nsw;
     const int N = args.N;
     const int nchunks_total = (N + CH - 1) / CH;
     const int c0 = seg * args.L;
@@ -841,11 +881,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     if constexpr (RELU) wk.fshift = args.fshift;
     wk.init(smem, N, reinterpret_cast<const E*>(args.q) + size_t(bh) * N * D,
             reinterpret_cast<const E*>(args.k) + size_t(bh) * N * D,
-            reinterpret_cast<const E*>(args.v) + size_t(bh) * N * DV, GATED ? args.g + size_t(bh) * N : nullptr);
+            reinterpret_cast<const E*>(args.v) + size_t(bh) * N * DVF + part * DV,
+            GATED ? args.g + size_t(bh) * N : nullptr);
     const int w = wk.w, lane = wk.lane, l16 = wk.l16, g4 = wk.g4;
     OutRsrc ob;
-    if constexpr (OUTPUT) ob.init(reinterpret_cast<E*>(args.o) + size_t(bh) * N * DV, unsigned(N) * DV * sizeof(E));
-    const size_t slot0 = size_t(bh) * args.nseg;
+    if constexpr (OUTPUT)
+        ob.init(reinterpret_cast<E*>(args.o) + size_t(bh) * N * DVF + part * DV,
+                unsigned(N) * DVF * sizeof(E) - unsigned(part * DV * sizeof(E)));
+    const size_t slot0 = (size_t(bh) * VS + part) * args.nseg;
     auto st_at = [&](int s, int j) {
         return args.st + (slot0 + s) * (D * DV) + ((w * Sh::TPW + j) * kWave + lane) * 4;
     };
@@ -867,13 +910,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
         if constexpr (OUTPUT) {
             if (args.direct || seg == 0) {
                 if (args.s0) {
-                    const float* s0b = args.s0 + size_t(bh) * D * DV;
+                    const float* s0b = args.s0 + size_t(bh) * D * DVF + part * DV;
 #pragma unroll
                     for (int j = 0; j < Sh::TPW; ++j) {
                         const int u = w * Sh::TPW + j;
                         const int a = u / Sh::NB, b = u % Sh::NB;
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) sacc[j][r] = s0b[size_t(16 * a + 4 * g4 + r) * DV + 16 * b + l16];
+                        for (int r = 0; r < 4; ++r) sacc[j][r] = s0b[size_t(16 * a + 4 * g4 + r) * DVF + 16 * b + l16];
                     }
                 }
                 if (args.z0) {
@@ -930,13 +973,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
 // P_{s+1} = 2^lg_s P_s + T_s with P_0 = S0 (fp32), one thread per state element.
 // Element e < D*Dv is in accumulator layout: tile u = e / 256 (a = u / (Dv/16),
 // b = u % (Dv/16)), lane = (e / 4) % 64, r = e % 4, which is S[16a + 4(lane/16) + r][16b + lane%16].
-template <int D, int DV, bool GATED>
+// With VS column parts the slots are per (head, part), vbh = bh * VS + part, each a
+// [D][DV] slice whose initial value is columns part * DV .. of the caller's S0 rows.
+template <int D, int DV, bool GATED, int VS = 1>
 __global__ __launch_bounds__(kThreads) void scan_kernel(float* st, float* zt, const float* lg, const float* s0,
                                                        const float* z0, int nseg) {
     constexpr int NS = D * DV;
-    constexpr int NBLK = (NS + D + kThreads - 1) / kThreads;   // workgroups per head
+    constexpr int NBLK = (NS + D + kThreads - 1) / kThreads;   // workgroups per head and part
     const int e = (blockIdx.x % NBLK) * kThreads + threadIdx.x;
-    const int bh = blockIdx.x / NBLK;
+    const int vbh = blockIdx.x / NBLK;
+    const int bh = vbh / VS, part = vbh % VS;
     if (e >= NS + D) return;
     float* base;
     size_t stride;
@@ -946,18 +992,18 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(float* st, float* zt, co
         const int u = e / 256, lane = (e / 4) % 64, r = e % 4;
         const int a = u / (DV / 16), b = u % (DV / 16);
         const int d = 16 * a + 4 * (lane / 16) + r, dv = 16 * b + lane % 16;
-        uidx = size_t(bh) * NS + size_t(d) * DV + dv;
-        base = st + size_t(bh) * nseg * NS + e;
+        uidx = size_t(bh) * NS * VS + size_t(d) * DV * VS + part * DV + dv;
+        base = st + size_t(vbh) * nseg * NS + e;
         stride = NS;
         init = s0;
     } else {
         const int d = e - NS;
         uidx = size_t(bh) * D + d;
-        base = zt + size_t(bh) * nseg * D + d;
+        base = zt + size_t(vbh) * nseg * D + d;
         stride = D;
         init = z0;
     }
-    const float* lgb = GATED ? lg + size_t(bh) * nseg : nullptr;
+    const float* lgb = GATED ? lg + size_t(vbh) * nseg : nullptr;
     const int n = nseg - 1;
     float acc = init ? init[uidx] : 0.0f;
     constexpr int U = 8;                         // loads in flight per thread
@@ -982,23 +1028,26 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(float* st, float* zt, co
 // One state slot (accumulator layout; nslots per head) into the caller's [D][Dv] and [D]
 // layouts: S_N, z_N from slot nseg-1 of the forward.  A launch of its own, so s_out may
 // alias s0 (every read of s0 is done by then).
-template <int D, int DV>
+// With VS column parts, slot vbh = bh * VS + part fills columns part * DV .. of S_N's
+// rows, and part 0's copy of z gives z_N.
+template <int D, int DV, int VS = 1>
 __global__ __launch_bounds__(kThreads) void final_kernel(const float* st, const float* zt, int nslots, int which,
                                                         float* s_out, float* z_out) {
     constexpr int NS = D * DV;
     constexpr int NBLK = (NS + D + kThreads - 1) / kThreads;
     const int e = (blockIdx.x % NBLK) * kThreads + threadIdx.x;
-    const int bh = blockIdx.x / NBLK;
+    const int vbh = blockIdx.x / NBLK;
+    const int bh = vbh / VS, part = vbh % VS;
     if (e >= NS + D) return;
-    const size_t slot = size_t(bh) * nslots + which;
+    const size_t slot = size_t(vbh) * nslots + which;
     if (e < NS) {
         if (!s_out) return;
         const int u = e / 256, lane = (e / 4) % 64, r = e % 4;
         const int a = u / (DV / 16), b = u % (DV / 16);
         const int d = 16 * a + 4 * (lane / 16) + r, dv = 16 * b + lane % 16;
-        s_out[size_t(bh) * NS + size_t(d) * DV + dv] = st[slot * NS + e];
+        s_out[size_t(bh) * NS * VS + size_t(d) * DV * VS + part * DV + dv] = st[slot * NS + e];
     } else {
-        if (!z_out) return;
+        if (!z_out || part != 0) return;
         z_out[size_t(bh) * D + (e - NS)] = zt[slot * D + (e - NS)];
     }
 }

@@ -8,12 +8,13 @@
 
 namespace linattn {
 
-template <typename E, int D, int DV, int CH, bool GATED, bool IDENT = false, bool RELU = false>
+// DV is the width of one column part; VS parts make up the caller's Dv = DV * VS.
+template <typename E, int D, int DV, int CH, bool GATED, bool IDENT = false, bool RELU = false, int VS = 1>
 hipError_t run_fwd_walks(const FwdLaunch& p) {
     using ShT = WalkShape<E, D, DV, CH, GATED, false>;
     using ShO = WalkShape<E, D, DV, CH, GATED, true>;
     size_t off_zt = 0, off_lg = 0;
-    fwd_workspace_layout(size_t(p.BH) * p.nseg, D, DV, &off_zt, &off_lg);
+    fwd_workspace_layout(size_t(p.BH) * VS * p.nseg, D, DV, &off_zt, &off_lg);
     char* wsb = static_cast<char*>(p.ws);
     WalkArgs a;
     a.q = p.q; a.k = p.k; a.v = p.v; a.g = p.g; a.o = p.o;
@@ -21,11 +22,12 @@ hipError_t run_fwd_walks(const FwdLaunch& p) {
     a.zt = reinterpret_cast<float*>(wsb + off_zt);
     a.lg = reinterpret_cast<float*>(wsb + off_lg);
     a.s0 = p.s0; a.z0 = p.z0;
-    a.N = p.N; a.nseg = p.nseg; a.L = p.L; a.eps = p.eps; a.normalize = p.normalize; a.fshift = p.fshift;
+    a.N = p.N; a.BH = p.BH; a.nseg = p.nseg; a.L = p.L; a.eps = p.eps; a.normalize = p.normalize;
+    a.fshift = p.fshift;
     a.direct = prefix_direct(p.nseg, D, DV) ? 1 : 0;
     a.want_final = (p.s_out || p.z_out) ? 1 : 0;
-    auto* k_tot = walk_kernel<E, D, DV, CH, GATED, false, IDENT, RELU>;
-    auto* k_out = walk_kernel<E, D, DV, CH, GATED, true, IDENT, RELU>;
+    auto* k_tot = walk_kernel<E, D, DV, CH, GATED, false, IDENT, RELU, VS>;
+    auto* k_out = walk_kernel<E, D, DV, CH, GATED, true, IDENT, RELU, VS>;
     static bool attrs_set = false;         // benign race: idempotent attribute set
     if (!attrs_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_tot),
@@ -37,47 +39,60 @@ hipError_t run_fwd_walks(const FwdLaunch& p) {
         attrs_set = true;
     }
     constexpr int NBLK = (D * DV + D + kThreads - 1) / kThreads;
+    const unsigned vheads = unsigned(p.BH) * VS;
     auto mark = [&](int i) { if (p.prof[i]) (void)hipEventRecord(p.prof[i], p.stream); };
     mark(0);
     if (p.nseg > 1)
-        hipLaunchKernelGGL(k_tot, dim3(unsigned(p.BH) * unsigned(p.nseg - 1)), dim3(kThreads), ShT::kBytes,
-                           p.stream, a);
+        hipLaunchKernelGGL(k_tot, dim3(walk_grid(unsigned(p.BH) * unsigned(p.nseg - 1), VS)), dim3(kThreads),
+                           ShT::kBytes, p.stream, a);
     mark(1);
     if (p.nseg > 1 && !a.direct)
-        hipLaunchKernelGGL((scan_kernel<D, DV, GATED>), dim3(unsigned(p.BH) * NBLK), dim3(kThreads), 0, p.stream,
-                           a.st, a.zt, a.lg, p.s0, p.z0, p.nseg);
+        hipLaunchKernelGGL((scan_kernel<D, DV, GATED, VS>), dim3(vheads * NBLK), dim3(kThreads), 0, p.stream, a.st,
+                           a.zt, a.lg, p.s0, p.z0, p.nseg);
     mark(2);
-    hipLaunchKernelGGL(k_out, dim3(unsigned(p.BH) * unsigned(p.nseg)), dim3(kThreads), ShO::kBytes, p.stream, a);
+    hipLaunchKernelGGL(k_out, dim3(walk_grid(unsigned(p.BH) * unsigned(p.nseg), VS)), dim3(kThreads), ShO::kBytes,
+                       p.stream, a);
     if (a.want_final)
-        hipLaunchKernelGGL((final_kernel<D, DV>), dim3(unsigned(p.BH) * NBLK), dim3(kThreads), 0, p.stream, a.st,
-                           a.zt, p.nseg, p.nseg - 1, p.s_out, p.z_out);
+        hipLaunchKernelGGL((final_kernel<D, DV, VS>), dim3(vheads * NBLK), dim3(kThreads), 0, p.stream, a.st, a.zt,
+                           p.nseg, p.nseg - 1, p.s_out, p.z_out);
     mark(3);
     return hipGetLastError();
 }
 
-template <typename E, int D, int DV, int CH, bool GATED, bool IDENT = false, bool RELU = false>
+template <typename E, int D, int DV, int CH, bool GATED, bool IDENT = false, bool RELU = false, int VS = 1>
 hipError_t run_fwd(const FwdLaunch& p) {
     if constexpr (WalkShape<E, D, DV, CH, GATED, true>::kBytes > kMaxLds) {
         return hipErrorInvalidValue;           // rejected earlier by the ABI's support check
     } else {
-        return run_fwd_walks<E, D, DV, CH, GATED, IDENT, RELU>(p);
+        return run_fwd_walks<E, D, DV, CH, GATED, IDENT, RELU, VS>(p);
     }
 }
 
-template <typename E, int D, int DV>
+template <typename E, int D, int DV, int VS = 1>
 hipError_t run_fwd_chunk(const FwdLaunch& p) {
     const bool gated = p.g != nullptr;
     switch (p.chunk) {
-        case 32:  return gated ? run_fwd<E, D, DV, 32, true>(p) : run_fwd<E, D, DV, 32, false>(p);
-        case 64:  return gated ? run_fwd<E, D, DV, 64, true>(p) : run_fwd<E, D, DV, 64, false>(p);
-        case 128: return gated ? run_fwd<E, D, DV, 128, true>(p) : run_fwd<E, D, DV, 128, false>(p);
-        case 256: return gated ? run_fwd<E, D, DV, 256, true>(p) : run_fwd<E, D, DV, 256, false>(p);
+        case 32:  return gated ? run_fwd<E, D, DV, 32, true, false, false, VS>(p)
+                               : run_fwd<E, D, DV, 32, false, false, false, VS>(p);
+        case 64:  return gated ? run_fwd<E, D, DV, 64, true, false, false, VS>(p)
+                               : run_fwd<E, D, DV, 64, false, false, false, VS>(p);
+        case 128: return gated ? run_fwd<E, D, DV, 128, true, false, false, VS>(p)
+                               : run_fwd<E, D, DV, 128, false, false, false, VS>(p);
+        case 256: return gated ? run_fwd<E, D, DV, 256, true, false, false, VS>(p)
+                               : run_fwd<E, D, DV, 256, false, false, false, VS>(p);
         default:  return hipErrorInvalidValue;
     }
 }
 
+// p.vsplit column parts (walk_vsplit): 2 walks Dv = 128 as two parts of 64 columns.
 template <typename E>
 hipError_t run_fwd_typed(const FwdLaunch& p) {
+    if (p.vsplit == 2) {
+        if (p.D == 64 && p.Dv == 128) return run_fwd_chunk<E, 64, 64, 2>(p);
+        if (p.D == 128 && p.Dv == 128) return run_fwd_chunk<E, 128, 64, 2>(p);
+        return hipErrorInvalidValue;
+    }
+    if (p.vsplit != 1) return hipErrorInvalidValue;
     if (p.D == 64 && p.Dv == 64) return run_fwd_chunk<E, 64, 64>(p);
     if (p.D == 64 && p.Dv == 128) return run_fwd_chunk<E, 64, 128>(p);
     if (p.D == 128 && p.Dv == 64) return run_fwd_chunk<E, 128, 64>(p);

@@ -24,6 +24,7 @@ struct FwdLaunch {
     hipStream_t stream;
     hipEvent_t prof[4];      // measurement hook: all NULL when unused
     float fshift = 0.0f;     // the walk under relu(x) + fshift features only
+    int vsplit = 1;          // column parts of Dv walked by separate workgroups (walk_vsplit)
 };
 
 // Chunk sizes with kernel instantiations.
@@ -57,6 +58,15 @@ constexpr int walk_waves(int esize, int D, int Dv, int chunk, bool gated, bool o
     else if (work <= 2 * 64 * 64) regs = out ? 1 : 2;
     const int v = lds < regs ? lds : regs;
     return v < 1 ? 1 : v;
+}
+
+// Column parts the forward cuts the value dimension into (each part walked by its own
+// workgroups with a [D, Dv / parts] slice of the state): 1 when the full-width tiles fit
+// the LDS, else 2 when Dv = 128 and the 64-column tiles do, else 0 (not supported).
+constexpr int walk_vsplit(int esize, int D, int Dv, int chunk, bool gated) {
+    if (walk_lds_bytes(esize, D, Dv, chunk, gated) <= kMaxLds) return 1;
+    if (Dv == 128 && walk_lds_bytes(esize, D, 64, chunk, gated) <= kMaxLds) return 2;
+    return 0;
 }
 
 inline size_t round_up256(size_t x) { return (x + 255) / 256 * 256; }

@@ -31,9 +31,11 @@
  *  - Nothing aborts and no C++ exception crosses this interface.
  *
  * Supported shapes on the GPU: D and Dv in {64, 128}; chunk in {32, 64, 128, 256}
- * when the chunk's on-chip tiles fit the 160 KiB LDS of a compute unit:
- *   bf16: every chunk, except 256 when D = Dv = 128, and 256 at D = 128 for the gated forward;
- *   f32:  chunk <= 128 at D = Dv = 64, <= 64 when one of D, Dv is 128, 32 when both are.
+ * when the chunk's on-chip tiles fit the 160 KiB LDS of a compute unit.  When the
+ * full-width tiles do not fit but 64-column ones do (Dv = 128), the forward walks the
+ * value columns as two parts of 64, each with its own workgroups.  That leaves:
+ *   bf16: every chunk, except 256 at D = 128 for the gated forward;
+ *   f32:  chunk <= 128 when D = 64, <= 64 when D = 128.
  * Other shapes return LINATTN_ERR_UNSUPPORTED.
  */
 #ifndef LINATTN_H

@@ -78,6 +78,9 @@ SMALL = [
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: "B{}H{}N{}D{}Dv{}{}c{}".format(*c))
 def test_small_against_oracle(case, gated):
     B, H, N, D, Dv, dt, chunk = case
+    if gated and D == 128 and chunk == 256:
+        pytest.skip("not supported: the decayed key tile of a 256-token chunk at D = 128 exceeds the LDS "
+                    "(test_unsupported_raises checks the error)")
     _say(f"small case {case} gated={gated}")
     inp = workloads.random_inputs(11 + N + D, B, H, N, D, Dv, dtype=dt, gated=gated, g_low=0.8)
     o, S, z = run_fwd(inp, chunk, return_state=True)
@@ -186,6 +189,9 @@ def test_unsupported_raises():
     inp = workloads.random_inputs(1, 1, 1, 64, 96, 64, dtype="bf16")
     with pytest.raises(RuntimeError, match="unsupported"):
         run_fwd(inp, 128)
+    gated = workloads.random_inputs(2, 1, 1, 300, 128, 128, dtype="bf16", gated=True)
+    with pytest.raises(RuntimeError, match="unsupported"):
+        run_fwd(gated, 256)
 
 
 # ------------------------------------------------------------------ decode ----
@@ -257,22 +263,61 @@ def test_workload_sampled_heads(name):
     assert torch.isfinite(o).all().item()
 
 
-def test_workload_longctx_sampled_heads():
-    w = workloads.WORKLOADS["longctx_bf16"]
-    inp = workloads.make_inputs(w)
-    heads = _heads(w.B, w.H, 2, 6)
-    _say(f"longctx full size, oracle on heads {heads}")
-    o_ref, S_ref, _ = oracle_fwd(inp, heads=heads)
-    for chunk in w.chunks:
-        _say(f"  chunk {chunk}")
-        try:
-            o, S, z = run_fwd(inp, chunk, return_state=True)
-        except RuntimeError as e:
-            assert chunk == 256 and "unsupported" in str(e)
-            continue
-        assert rowwise_rel_err(sel(o, heads), o_ref) <= TOL["bf16"]
-        assert matrix_rel_err(sel(S, heads), S_ref) <= TOL["bf16"]
-        del o, S, z
+_LONGCTX = {}
+
+
+def _longctx_inputs_and_oracle():
+    """The long-context workload and the oracle on two sampled heads, computed once for
+    the three chunk sizes (the exact result does not depend on the chunk)."""
+    if not _LONGCTX:
+        w = workloads.WORKLOADS["longctx_bf16"]
+        inp = workloads.make_inputs(w)
+        heads = _heads(w.B, w.H, 2, 6)
+        _say(f"longctx full size, oracle on heads {heads}")
+        _LONGCTX.update(w=w, inp=inp, heads=heads, ref=oracle_fwd(inp, heads=heads))
+    return _LONGCTX
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+def test_workload_longctx_sampled_heads(chunk):
+    c = _longctx_inputs_and_oracle()
+    heads = c["heads"]
+    o_ref, S_ref, z_ref = c["ref"]
+    _say(f"  longctx chunk {chunk}")
+    o, S, z = run_fwd(c["inp"], chunk, return_state=True)
+    assert rowwise_rel_err(sel(o, heads), o_ref) <= TOL["bf16"]
+    assert matrix_rel_err(sel(S, heads), S_ref) <= TOL["bf16"]
+    assert matrix_rel_err(sel(z, heads), z_ref) <= TOL["bf16"]
+    assert torch.isfinite(o).all().item()
+    del o, S, z
+
+
+# Shapes whose full-width tiles do not fit the LDS: the value columns are walked as two
+# parts of 64, each part with its own workgroups and its own slice of the state.
+SPLIT = [
+    # (B, H, N, D, Dv, dtype, chunk, gated)
+    (1, 2, 777, 128, 128, "bf16", 256, False),
+    (1, 4, 8192, 128, 128, "bf16", 256, False),     # 32 segments per part: the scanned prefix
+    (3, 1, 1000, 128, 128, "bf16", 256, False),     # 4 segments per part: the direct prefix
+    (2, 2, 300, 128, 128, "f32", 64, False),
+    (2, 2, 300, 128, 128, "f32", 64, True),
+    (1, 3, 333, 64, 128, "f32", 128, False),
+    (1, 3, 333, 64, 128, "f32", 128, True),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT, ids=lambda c: "B{}H{}N{}D{}Dv{}{}c{}{}".format(*c[:7], "g" if c[7] else ""))
+def test_value_columns_in_two_parts(case):
+    B, H, N, D, Dv, dt, chunk, gated = case
+    _say(f"two column parts {case}")
+    inp = workloads.random_inputs(61 + N, B, H, N, D, Dv, dtype=dt, gated=gated, g_low=0.9, with_state=True,
+                                  state_scale=5.0)
+    o, S, z = run_fwd(inp, chunk, s0=inp["s0"], z0=inp["z0"], return_state=True)
+    o_ref, S_ref, z_ref = oracle_fwd(inp, s0=inp["s0"], z0=inp["z0"])
+    tol = TOL[dt]
+    assert rowwise_rel_err(to64(o), o_ref) <= tol
+    assert matrix_rel_err(to64(S), S_ref) <= tol
+    assert matrix_rel_err(to64(z), z_ref) <= tol
 
 
 def test_workload_decode_sampled_heads():
