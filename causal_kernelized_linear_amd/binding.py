@@ -7,7 +7,7 @@ allocates the caller-side workspace and output tensors with torch, and raises
 no fallback: if the library is missing, every call raises.
 
 Function names match the C ABI (include/linattn.h):
-    linattn_fwd_chunked, linattn_fwd_gated, linattn_fwd_ex, linattn_decode_step,
+    linattn_fwd_chunked, linattn_fwd_gated, linattn_fwd_ex, linattn_fwd_ex_noalloc, linattn_decode_step,
     linattn_decode_step_ex, linattn_fwd_workspace_size, linattn_bwd,
     linattn_bwd_workspace_size, linattn_fwd_vdecay, linattn_fwd_vdecay_workspace_size,
     linattn_decode_step_vdecay, linattn_fwd_features, linattn_fwd_features_workspace_size,
@@ -29,7 +29,8 @@ LIB_PATH = os.path.join(_HERE, "liblinattn.so")
 F32, BF16 = 0, 1
 OUT_NORMALIZED, OUT_NUMERATOR = 0, 1
 FEATURE_RELU, FEATURE_FAVOR = 1, 2
-_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "hip"}
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "hip", 5: "scratch limit"}
+NOALLOC_SCRATCH_BYTES = 32 << 20     # LINATTN_NOALLOC_SCRATCH_BYTES
 
 _lock = threading.Lock()
 _lib = None
@@ -44,6 +45,7 @@ EXPORTS = {
     "linattn_fwd_chunked": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p, _sz, _p]),
     "linattn_fwd_gated": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p, _sz, _p]),
     "linattn_fwd_ex": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i, _p, _sz, _p]),
+    "linattn_fwd_ex_noalloc": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _i, _p]),
     "linattn_decode_step": (_i, [_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p]),
     "linattn_decode_step_ex": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _p]),
     "linattn_bwd_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
@@ -107,6 +109,12 @@ def linattn_fwd_ex(q, k, v, g, o, s0, z0, s_out, z_out, B, H, N, D, Dv, chunk, d
                    stream) -> int:
     return int(lib().linattn_fwd_ex(q, k, v, g, o, s0, z0, s_out, z_out, B, H, N, D, Dv, chunk, dtype, eps, out, ws,
                                     ws_bytes, stream))
+
+
+def linattn_fwd_ex_noalloc(q, k, v, g, o, s0, z0, s_out, z_out, B, H, N, D, Dv, chunk, dtype, eps, out,
+                           stream) -> int:
+    return int(lib().linattn_fwd_ex_noalloc(q, k, v, g, o, s0, z0, s_out, z_out, B, H, N, D, Dv, chunk, dtype, eps,
+                                            out, stream))
 
 
 def linattn_decode_step(q, k, v, S, z, o, B, H, D, Dv, dtype, eps, stream) -> int:

@@ -112,6 +112,34 @@ size_t fwd_workspace_bytes(long BH, int N, int D, int Dv, int chunk) {
     return b;
 }
 
+// Scratch of linattn_fwd_ex_noalloc: a fixed array in device memory, one copy per device
+// (the runtime places it when the library's device code loads there), held until the
+// process ends.  Host code never uses the array's name as an address: its device address
+// on the current device comes from hipGetSymbolAddress, looked up once per device.
+constexpr size_t kScratchBytes = LINATTN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of `scratch` on the current device, or NULL when it cannot be looked up.
+void* device_scratch() {
+    static std::mutex mu;
+    static void* ptrs[256];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        ptrs[dev] = p;
+    }
+    return ptrs[dev];
+}
+
 // Measurement hook (linattn_set_profile_events): one-shot, process-wide.
 std::mutex g_prof_mu;
 hipEvent_t g_prof[4] = {nullptr, nullptr, nullptr, nullptr};
@@ -162,10 +190,12 @@ linattn_status_t check_device() {
     return usable[dev] == 1 ? LINATTN_OK : LINATTN_ERR_HIP;
 }
 
+// fixed_scratch: the workspace is the library's own device array (ws and ws_bytes are
+// ignored), for linattn_fwd_ex_noalloc.
 linattn_status_t fwd_common(const void* q, const void* k, const void* v, const float* g, void* o, const float* s0,
                             const float* z0, float* s_out, float* z_out, int B, int H, int N, int D, int Dv,
                             int chunk, linattn_dtype_t dtype, float eps, linattn_output_t out, void* ws,
-                            size_t ws_bytes, void* stream) {
+                            size_t ws_bytes, void* stream, bool fixed_scratch = false) {
     if (B < 0 || H < 0 || N < 0 || D <= 0 || Dv <= 0 || chunk <= 0) return LINATTN_ERR_INVALID_ARGUMENT;
     if (!dtype_ok(dtype) || !out_ok(out) || !(eps > 0.0f) || !std::isfinite(eps)) return LINATTN_ERR_INVALID_ARGUMENT;
     const long BH = long(B) * long(H);
@@ -197,6 +227,14 @@ linattn_status_t fwd_common(const void* q, const void* k, const void* v, const f
     if (!dim_ok(D) || !dim_ok(Dv) || !linattn::chunk_is_built(chunk)) return LINATTN_ERR_UNSUPPORTED;
     const Plan plan = fwd_plan(int(es), BH, N, D, Dv, chunk, g != nullptr);
     if (plan.vs == 0) return LINATTN_ERR_UNSUPPORTED;
+    if (fixed_scratch) {
+        if (plan.bytes > kScratchBytes) return LINATTN_ERR_SCRATCH_LIMIT;
+        const linattn_status_t dst = check_device();
+        if (dst != LINATTN_OK) return dst;
+        ws = device_scratch();
+        if (!ws) return LINATTN_ERR_HIP;
+        ws_bytes = kScratchBytes;
+    }
     if (ws_bytes < plan.bytes || !ws || !aligned16(ws)) return LINATTN_ERR_WORKSPACE;
     if (overlap(ws, plan.bytes, q, nqk) || overlap(ws, plan.bytes, k, nqk) || overlap(ws, plan.bytes, v, nv) ||
         overlap(ws, plan.bytes, o, nv) || overlap(ws, plan.bytes, g, ng) ||
@@ -498,6 +536,18 @@ linattn_status_t linattn_fwd_ex(const void* q, const void* k, const void* v, con
     }
 }
 
+linattn_status_t linattn_fwd_ex_noalloc(const void* q, const void* k, const void* v, const float* g, void* o,
+                                        const float* s0, const float* z0, float* s_out, float* z_out, int B, int H,
+                                        int N, int D, int Dv, int chunk, linattn_dtype_t dtype, float eps,
+                                        linattn_output_t out, void* stream) {
+    try {
+        return fwd_common(q, k, v, g, o, s0, z0, s_out, z_out, B, H, N, D, Dv, chunk, dtype, eps, out, nullptr, 0,
+                          stream, true);
+    } catch (...) {
+        return LINATTN_ERR_HIP;
+    }
+}
+
 linattn_status_t linattn_decode_step(const void* q, const void* k, const void* v, float* S, float* z, void* o, int B,
                                      int H, int D, int Dv, linattn_dtype_t dtype, float eps, void* stream) {
     try {
@@ -562,6 +612,8 @@ const char* linattn_status_string(linattn_status_t status) {
         case LINATTN_ERR_UNSUPPORTED: return "unsupported shape or dtype";
         case LINATTN_ERR_WORKSPACE: return "workspace missing, too small, misaligned or overlapping";
         case LINATTN_ERR_HIP: return "HIP error or no usable gfx950 device";
+        case LINATTN_ERR_SCRATCH_LIMIT:
+            return "problem needs more scratch than the fixed device array of linattn_fwd_ex_noalloc holds";
         default: return "unknown status";
     }
 }

@@ -52,7 +52,8 @@ typedef enum {
     LINATTN_ERR_INVALID_ARGUMENT = 1,  /* null pointer, negative size, eps <= 0, misalignment */
     LINATTN_ERR_UNSUPPORTED = 2,       /* valid but not built: D/Dv/chunk/dtype combination */
     LINATTN_ERR_WORKSPACE = 3,         /* workspace missing or smaller than linattn_fwd_workspace_size */
-    LINATTN_ERR_HIP = 4                /* no usable device, or a launch failed */
+    LINATTN_ERR_HIP = 4,               /* no usable device, or a launch failed */
+    LINATTN_ERR_SCRATCH_LIMIT = 5      /* linattn_fwd_ex_noalloc: more scratch than its fixed array */
 } linattn_status_t;
 
 typedef enum {
@@ -136,6 +137,31 @@ linattn_status_t linattn_fwd_ex(
     const float* s0, const float* z0, float* s_out, float* z_out,
     int B, int H, int N, int D, int Dv, int chunk, linattn_dtype_t dtype, float eps,
     linattn_output_t out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): linattn_fwd_ex without a workspace.
+ * Every argument is as for linattn_fwd_ex, and so are the results, bit for bit (the same
+ * kernels on the same plan).  The call allocates and frees nothing.  Its scratch is a
+ * fixed array of LINATTN_NOALLOC_SCRATCH_BYTES in device memory, one per device, placed
+ * when the library's device code loads on that device and held until the process ends;
+ * the first call on a device looks up its address there.
+ *  - Shapes whose scratch would exceed the array return LINATTN_ERR_SCRATCH_LIMIT before
+ *    anything is launched (linattn_fwd_workspace_size(...) <= LINATTN_NOALLOC_SCRATCH_BYTES
+ *    is sufficient for a shape to fit).
+ *  - Every call on one device shares that device's array, which keeps the last call's
+ *    contents (nothing in it needs to start at zero: a call writes every part it reads).
+ *    Calls that may overlap in time on one device (on different streams, or from
+ *    different host threads without ordering) race on it; calls on one stream are
+ *    ordered and safe.
+ */
+#define LINATTN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+linattn_status_t linattn_fwd_ex_noalloc(
+    const void* q, const void* k, const void* v, const float* g, void* o,
+    const float* s0, const float* z0, float* s_out, float* z_out,
+    int B, int H, int N, int D, int Dv, int chunk, linattn_dtype_t dtype, float eps,
+    linattn_output_t out, void* stream);
 
 /*
  * Per-dimension decay (gated linear attention):

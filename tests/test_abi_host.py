@@ -48,8 +48,9 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(5):
+    for code in range(6):
         assert isinstance(binding.linattn_status_string(code), str)
+    assert "scratch" in binding.linattn_status_string(5)
     assert binding.linattn_status_string(0) == "ok"
     assert binding.linattn_status_string(99) == "unknown status"
 
@@ -146,6 +147,34 @@ def test_fwd_ex_checks_like_the_fixed_forwards(gated, out):
     assert fwd(gated=gated, out=out, B=0, q=0, k=0, v=0, o=0, ws=0, wsb=0) == OK
 
 
+def fwd_noalloc(q=Q, k=K, v=V, g=0, o=O, s0=0, z0=0, so=0, zo=0, B=1, H=2, N=256, D=64, Dv=64, chunk=128, dt=1,
+                eps=1e-6, out=0):
+    return binding.linattn_fwd_ex_noalloc(q, k, v, g, o, s0, z0, so, zo, B, H, N, D, Dv, chunk, dt, eps, out, 0)
+
+
+@fake_ptrs
+def test_fwd_noalloc_checks_like_fwd_ex():
+    assert fwd_noalloc(B=-1) == INVALID
+    assert fwd_noalloc(eps=0.0) == INVALID
+    assert fwd_noalloc(out=2) == INVALID
+    assert fwd_noalloc(o=Q + 64) == INVALID
+    assert fwd_noalloc(g=O + 32) == INVALID                    # g overlaps o
+    assert fwd_noalloc(so=O) == INVALID                        # s_out overlaps o
+    assert fwd_noalloc(D=96) == UNSUPPORTED
+    assert fwd_noalloc(g=G, D=128, Dv=128, chunk=256) == UNSUPPORTED
+    assert fwd_noalloc(B=0, q=0, k=0, v=0, o=0) == OK
+
+
+@fake_ptrs
+def test_fwd_noalloc_rejects_shapes_beyond_its_scratch():
+    # one state slot of 64 KiB per head: 1024 heads need 64 MiB, beyond the fixed 32 MiB
+    assert binding.linattn_fwd_workspace_size(1024, 1, 64, 128, 128, 64) > binding.NOALLOC_SCRATCH_BYTES
+    assert fwd_noalloc(B=1024, H=1, N=64, D=128, Dv=128, chunk=64) == 5
+    # the long-context shape fits at every chunk
+    for chunk in (64, 128, 256):
+        assert binding.linattn_fwd_workspace_size(1, 32, 65536, 128, 128, chunk) <= binding.NOALLOC_SCRATCH_BYTES
+
+
 @fake_ptrs
 def test_fwd_ex_rejects_unknown_output_mode():
     assert fwd(out=2) == INVALID
@@ -222,6 +251,7 @@ def test_bwd_workspace_size():
 def test_no_device_is_reported_not_crashed():
     assert fwd() == HIP
     assert fwd(out=1, gated=True) == HIP
+    assert fwd_noalloc() == HIP
     assert decode() == HIP
     assert decode_ex(g=0, z=0, out=1) == HIP                    # valid: numerator mode needs no z
     assert bwd(run=3) == HIP
