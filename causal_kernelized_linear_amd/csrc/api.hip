@@ -65,13 +65,15 @@ struct Plan {
     int nseg = 0;
     int L = 0;
     int vs = 1;
+    int tparts = 1;
     size_t bytes = 0;
 };
 
 // Each of the B*H*vs (head, column part) pairs is cut into nseg segments so that their
-// count reaches the target.  nseg grows with the target (never shrinks), so the workspace
-// sized for the largest target serves every smaller one.
-Plan make_plan(long BH, int N, int D, int Dv, int chunk, long target, int vs = 1) {
+// count reaches the target, and each segment's total into tparts parts so that the
+// totals walk fills `totals_round` workgroups.  nseg grows with the target (never
+// shrinks), so the workspace sized for the largest target serves every smaller one.
+Plan make_plan(long BH, int N, int D, int Dv, int chunk, long target, int vs = 1, long totals_round = 0) {
     Plan p;
     const long heads = BH * vs;
     const long nc = (long(N) + chunk - 1) / chunk;
@@ -83,7 +85,9 @@ Plan make_plan(long BH, int N, int D, int Dv, int chunk, long target, int vs = 1
     p.nseg = int(nseg);
     p.L = int(L);
     p.vs = vs;
-    p.bytes = linattn::fwd_workspace_layout(size_t(heads) * size_t(nseg), D, Dv / vs, nullptr, nullptr);
+    p.tparts = linattn::totals_parts(heads, p.nseg, p.L, D, Dv / vs, totals_round);
+    const size_t nslots = size_t(p.nseg - 1) * size_t(p.tparts) + 1;
+    p.bytes = linattn::fwd_workspace_layout(size_t(heads) * nslots, D, Dv / vs, nullptr, nullptr);
     return p;
 }
 
@@ -95,7 +99,8 @@ Plan fwd_plan(int esize, long BH, int N, int D, int Dv, int chunk, bool gated) {
         p.vs = 0;
         return p;
     }
-    return make_plan(BH, N, D, Dv, chunk, target_workgroups(esize, D, Dv, chunk, gated, vs), vs);
+    const long totals_round = long(device_cus()) * linattn::walk_waves(esize, D, Dv / vs, chunk, gated, false);
+    return make_plan(BH, N, D, Dv, chunk, target_workgroups(esize, D, Dv, chunk, gated, vs), vs, totals_round);
 }
 
 // Workspace bytes that serve the forward of this shape whatever its element type and
@@ -250,7 +255,7 @@ linattn_status_t fwd_common(const void* q, const void* k, const void* v, const f
     L.s0 = s0; L.z0 = z0; L.s_out = s_out; L.z_out = z_out;
     L.ws = ws;
     L.BH = int(BH); L.N = N; L.D = D; L.Dv = Dv; L.chunk = chunk;
-    L.nseg = plan.nseg; L.L = plan.L; L.vsplit = plan.vs; L.eps = eps;
+    L.nseg = plan.nseg; L.L = plan.L; L.vsplit = plan.vs; L.tparts = plan.tparts; L.eps = eps;
     L.normalize = out == LINATTN_OUT_NORMALIZED ? 1 : 0;
     L.stream = static_cast<hipStream_t>(stream);
     take_profile_events(L.prof);

@@ -65,15 +65,15 @@ hipError_t run_bwd(const BwdLaunch& p) {
             w.q = p.q; w.k = p.k; w.v = p.v; w.g = p.g; w.o = nullptr;
             w.st = a.fst; w.zt = a.fzt; w.lg = reinterpret_cast<float*>(ws + lay.flg);
             w.s0 = p.s0; w.z0 = p.z0;
-            w.N = p.N; w.BH = p.BH; w.nseg = NR; w.L = a.LC; w.direct = 0; w.want_final = 0; w.eps = p.eps; w.normalize = 1;
+            w.N = p.N; w.BH = p.BH; w.nseg = NR; w.L = a.LC; w.tparts = 1; w.nslots = NR; w.direct = 0; w.want_final = 0; w.eps = p.eps; w.normalize = 1;
             hipLaunchKernelGGL(k_tot, dim3(BH * unsigned(NR - 1)), dim3(kThreads), ShT::kBytes, p.stream, w);
             hipLaunchKernelGGL((scan_kernel<D, DV, GATED>), dim3(BH * NBLK), dim3(kThreads), 0, p.stream, a.fst, a.fzt,
-                               w.lg, p.s0, p.z0, NR);
+                               w.lg, p.s0, p.z0, NR, NR - 1);
         }
         hipLaunchKernelGGL(k_dq, dim3(BH * unsigned(NR)), dim3(kThreads), Sh::kBytes, p.stream, a);
         // adjoint states: the scan over the runs' adjoint totals, last run first
         hipLaunchKernelGGL((scan_kernel<D, DV, GATED>), dim3(BH * NBLK), dim3(kThreads), 0, p.stream, a.rst, a.rzt,
-                           a.rlg, static_cast<const float*>(nullptr), static_cast<const float*>(nullptr), NR + 1);
+                           a.rlg, static_cast<const float*>(nullptr), static_cast<const float*>(nullptr), NR + 1, NR);
         hipLaunchKernelGGL(k_dkv, dim3(BH * unsigned(NR)), dim3(kThreads), Sh::kBytes, p.stream, a);
         if (GATED && p.dg) {
             const int nwork = p.BH * NC, per = kThreads / kWave;

@@ -3,15 +3,17 @@
 // The sequence of every (batch, head) is cut into nseg segments of L chunks of CH
 // tokens.  One forward is:
 //
-//   1. walk<TOTALS>  one workgroup per (head, segment) for every segment but the
-//      last: walks the segment's chunks and accumulates the segment's own total
+//   1. walk<TOTALS>  one workgroup per (head, segment, part) for every segment but
+//      the last, each segment cut into `tparts` parts of ceil(L / tparts) chunks:
+//      walks the part's chunks and accumulates its own total
 //          T = sum_j w_j phi(k_j) v_j^T,  t = sum_j w_j phi(k_j)
-//      (w_j = product of the gates after j inside the segment; 1 ungated) and,
-//      gated, the log2 of the segment's total decay.  Reads K and V only.
+//      (w_j = product of the gates after j inside the part; 1 ungated) and, gated,
+//      the log2 of the part's total decay.  Reads K and V only.
 //   2. the state in front of each segment,
-//          P_0 = S0,  P_{s+1} = Gamma_s P_s + T_s      (fp32),
+//          P_0 = S0,  P_{s+1} = Gamma_s P_s + T_s      (fp32, over the parts in order),
 //      either summed by each output workgroup itself from the totals in front of
-//      it (few, small states) or by scan_kernel, in place, beforehand.
+//      it (few, small states, one part per segment) or by scan_kernel, in place,
+//      beforehand.
 //   3. walk<OUTPUT>  one workgroup per (head, segment): starts from P_s and walks the
 //      segment's chunks carrying S and z in registers.  Per chunk it forms the masked
 //      quadratic part on MFMA, adds the carried-state part, divides by the clamped
@@ -80,18 +82,21 @@ struct WalkArgs {
     const void* v;
     const float* g;      // gated only
     void* o;             // OUTPUT only
-    float* st;           // [BH][nseg][D*Dv] accumulator layout: slot s < nseg-1 holds T_s (after
-                         // the scan: P_{s+1}); slot nseg-1 receives S_N
-    float* zt;           // [BH][nseg][D], alike
-    float* lg;           // [BH][nseg] log2 of each segment's total decay (gated)
+    float* st;           // [BH][nslots][D*Dv] accumulator layout: slot t < (nseg-1) tparts holds
+                         // the total of part t % tparts of segment t / tparts (after the scan:
+                         // the state after it); slot (nseg-1) tparts receives S_N
+    float* zt;           // [BH][nslots][D], alike
+    float* lg;           // [BH][nslots] log2 of each part's total decay (gated)
     const float* s0;     // [BH][D][Dv] initial state or NULL (caller layout)
     const float* z0;     // [BH][D] or NULL
     int N;
     int BH;              // heads (B * H)
     int nseg;            // segments per sequence
     int L;               // chunks per segment
+    int tparts;          // parts of a segment walked by separate totals workgroups (1: direct prefix)
+    int nslots;          // workspace slots per head: (nseg - 1) * tparts + 1
     int direct;          // 1: the output walk sums the totals in front of its segment itself
-    int want_final;      // 1: the last segment's output walk leaves S_N, z_N in slot nseg-1
+    int want_final;      // 1: the last segment's output walk leaves S_N, z_N in slot nslots - 1
     float eps;
     int normalize;       // 1: o = num / max(den, eps); 0: o = num (the denominator is not used)
     float fshift;        // RELU walks only: the shift of relu(x) + shift
@@ -154,6 +159,8 @@ struct WalkShape {
     // the compiler from squeezing registers for an occupancy the shape cannot reach, which
     // would make it wait for the next chunk's loads early
     static constexpr int kWaves = walk_waves(int(sizeof(E)), D, DV, CH, GATED, OUT);
+    // chunks whose loads are in flight ahead of the one being processed (walk_depth)
+    static constexpr int kDepth = walk_depth(int(sizeof(E)), D, DV, CH, GATED, OUT);
 };
 
 // Query strip handled by wave w in its m-th slot, or -1.
@@ -542,41 +549,66 @@ struct ChunkWalker {
     // chunks ahead, made the totals walk slower.)  The last chunk is folded only when
     // fold_last is set.  prologue() runs once the first chunk's loads are in flight (the
     // output walk forms the state in front of its segment there).
+    //
+    // With a prefetch depth of two (Sh::kDepth, for shapes that run one workgroup per
+    // compute unit and have the registers) two register sets alternate: the loads of
+    // chunk n + 2 go out while chunk n is processed, so twice the bytes are in flight.
     template <typename Prologue>
     __device__ __forceinline__ void walk(int c0, int nch, f32x4_t (&sacc)[Sh::TPW], f32x4_t (&zacc)[Sh::ZT],
                                          float& lg_total, const OutRsrc& ob, float eps, int norm, bool fold_last,
                                          Prologue&& prologue) {
         last = min(N, (c0 + max(nch, 1)) * CH) - 1;
-        Regs R;
-        QRegs qr;
-        load(R, c0 * CH);
-        if constexpr (OUT) load_q(qr, c0 * CH);
-        prologue();
-        for (int n = 0; n < nch; ++n) {
-            const int ts = (c0 + n) * CH;
-            if constexpr (GATED) {
-                lambda(R);
-                __syncthreads();
+        if constexpr (Sh::kDepth == 1) {
+            Regs R;
+            QRegs qr;
+            load(R, c0 * CH);
+            if constexpr (OUT) load_q(qr, c0 * CH);
+            prologue();
+            for (int n = 0; n < nch; ++n) step(R, qr, c0, n, nch, sacc, zacc, lg_total, ob, eps, norm, fold_last);
+        } else {
+            static_assert(Sh::kDepth == 2, "prefetch depth 1 or 2");
+            Regs R0, R1;
+            QRegs q0, q1;
+            load(R0, c0 * CH);
+            if constexpr (OUT) load_q(q0, c0 * CH);
+            load(R1, (c0 + 1) * CH);
+            if constexpr (OUT) load_q(q1, (c0 + 1) * CH);
+            prologue();
+            for (int n = 0; n < nch; n += 2) {
+                step(R0, q0, c0, n, nch, sacc, zacc, lg_total, ob, eps, norm, fold_last);
+                if (n + 1 < nch) step(R1, q1, c0, n + 1, nch, sacc, zacc, lg_total, ob, eps, norm, fold_last);
             }
-            const float lam_last = GATED ? sLam[CH - 1] : 0.0f;
-            if (ts + CH <= N)
-                stage<false>(R, ts, lam_last);
-            else
-                stage<true>(R, ts, lam_last);
-            F8<E> fq[Sh::MAXS][D / 32];
-            if constexpr (OUT) phi_q(qr, fq);
-            load(R, ts + CH);
-            __syncthreads();
-            if constexpr (OUT) {
-                outputs(fq, ts, ob, eps, norm);
-                load_q(qr, ts + CH);
-            }
-            const bool more = n + 1 < nch;
-            if (more || fold_last) fold(sacc, zacc, lam_last);
-            lg_total += lam_last;
-            __syncthreads();
-            if (OUT && more) stage_state(sacc, zacc);
         }
+    }
+
+    // Chunk c0 + n, whose K, V (R) and Q (qr) are loaded; R and qr are then reloaded with
+    // chunk c0 + n + kDepth (rows past the walked range reread its last row).
+    __device__ __forceinline__ void step(Regs& R, QRegs& qr, int c0, int n, int nch, f32x4_t (&sacc)[Sh::TPW],
+                                         f32x4_t (&zacc)[Sh::ZT], float& lg_total, const OutRsrc& ob, float eps,
+                                         int norm, bool fold_last) {
+        const int ts = (c0 + n) * CH;
+        if constexpr (GATED) {
+            lambda(R);
+            __syncthreads();
+        }
+        const float lam_last = GATED ? sLam[CH - 1] : 0.0f;
+        if (ts + CH <= N)
+            stage<false>(R, ts, lam_last);
+        else
+            stage<true>(R, ts, lam_last);
+        F8<E> fq[Sh::MAXS][D / 32];
+        if constexpr (OUT) phi_q(qr, fq);
+        load(R, ts + Sh::kDepth * CH);
+        __syncthreads();
+        if constexpr (OUT) {
+            outputs(fq, ts, ob, eps, norm);
+            load_q(qr, ts + Sh::kDepth * CH);
+        }
+        const bool more = n + 1 < nch;
+        if (more || fold_last) fold(sacc, zacc, lam_last);
+        lg_total += lam_last;
+        __syncthreads();
+        if (OUT && more) stage_state(sacc, zacc);
     }
 
     // One query strip of o out to memory: rows row0 .. row0 + 15, the lane holding row
@@ -855,8 +887,8 @@ struct ChunkWalker {
 // S[16a + 4 g4 + r][16b + l16] with a = w ZT + j / NB, b = j % NB; z tile i of wave w
 // holds z[16(w ZT + i) + 4 g4 + r] in its l16 == 0 lanes (zero elsewhere).
 // VS column parts of DV columns each (VS = 1: the whole of Dv = DV).  The workspace
-// slots are per (head, part): slot (bh * VS + part) * nseg + s holds that part's
-// [D, DV] slice of the state and its own copy of z.
+// slots are per (head, column part): slot (bh * VS + part) * nslots + t holds that
+// part's [D, DV] slice of the state and its own copy of z.
 template <typename E, int D, int DV, int CH, bool GATED, bool OUTPUT, bool IDENT = false, bool RELU = false,
           int VS = 1>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
@@ -866,16 +898,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     constexpr int DVF = DV * VS;
     extern __shared__ __align__(16) unsigned char smem[];
 
-    const int nsw = OUTPUT ? args.nseg : args.nseg - 1;    // the totals skip the last segment
+    // the totals skip the last segment and cut the others into tparts parts
+    const int nsw = OUTPUT ? args.nseg : (args.nseg - 1) * args.tparts;
     int item, part;
     walk_block<VS>(args.BH * nsw, item, part);
     if (item >= args.BH * nsw) return;                      // padding block (uniform over the workgroup)
-    const int seg = item % nsw;
+    const int sub = item % nsw;                             // segment (output) or totals slot
     const int bh = item / nsw;
+    const int seg = OUTPUT ? sub : sub / args.tparts;
     const int N = args.N;
     const int nchunks_total = (N + CH - 1) / CH;
-    const int c0 = seg * args.L;
-    const int nch = min(args.L, nchunks_total - c0);
+    int c0 = seg * args.L, nch = min(args.L, nchunks_total - c0);
+    if constexpr (!OUTPUT) {
+        // part sub % tparts of the segment; a part past the segment's chunks is empty
+        const int lp = (args.L + args.tparts - 1) / args.tparts;
+        const int end = c0 + nch;
+        c0 += (sub % args.tparts) * lp;
+        nch = max(0, min(lp, end - c0));
+        c0 = min(c0, end);
+    }
 
     W wk;
     if constexpr (RELU) wk.fshift = args.fshift;
@@ -888,7 +929,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     if constexpr (OUTPUT)
         ob.init(reinterpret_cast<E*>(args.o) + size_t(bh) * N * DVF + part * DV,
                 unsigned(N) * DVF * sizeof(E) - unsigned(part * DV * sizeof(E)));
-    const size_t slot0 = (size_t(bh) * VS + part) * args.nseg;
+    const size_t slot0 = (size_t(bh) * VS + part) * args.nslots;
     auto st_at = [&](int s, int j) {
         return args.st + (slot0 + s) * (D * DV) + ((w * Sh::TPW + j) * kWave + lane) * 4;
     };
@@ -942,11 +983,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
                     }
                 }
             } else {
+                const int pre = seg * args.tparts - 1;     // the scanned slot in front of the segment
 #pragma unroll
-                for (int j = 0; j < Sh::TPW; ++j) sacc[j] = get4(st_at(seg - 1, j));
+                for (int j = 0; j < Sh::TPW; ++j) sacc[j] = get4(st_at(pre, j));
 #pragma unroll
                 for (int i = 0; i < Sh::ZT; ++i) {
-                    const f32x4_t zv = get4(zt_at(seg - 1, i));
+                    const f32x4_t zv = get4(zt_at(pre, i));
                     zacc[i] = l16 == 0 ? zv : zero4;
                 }
             }
@@ -960,16 +1002,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     wk.walk(c0, nch, sacc, zacc, lg_total, ob, args.eps, args.normalize, keep, prologue);
 
     if (keep) {
+        const int slot = OUTPUT ? args.nslots - 1 : sub;
 #pragma unroll
-        for (int j = 0; j < Sh::TPW; ++j) *reinterpret_cast<f32x4_t*>(st_at(seg, j)) = sacc[j];
+        for (int j = 0; j < Sh::TPW; ++j) *reinterpret_cast<f32x4_t*>(st_at(slot, j)) = sacc[j];
 #pragma unroll
         for (int i = 0; i < Sh::ZT; ++i)
-            if (l16 == 0) *reinterpret_cast<f32x4_t*>(zt_at(seg, i)) = zacc[i];
-        if (!OUTPUT && GATED && wk.tid == 0) args.lg[slot0 + seg] = lg_total;
+            if (l16 == 0) *reinterpret_cast<f32x4_t*>(zt_at(slot, i)) = zacc[i];
+        if (!OUTPUT && GATED && wk.tid == 0) args.lg[slot0 + slot] = lg_total;
     }
 }
 
-// In place over the totals of segments 0 .. nseg-2 of every head: slot s becomes
+// In place over the first nscan of each head's nslots slots: slot s becomes
 // P_{s+1} = 2^lg_s P_s + T_s with P_0 = S0 (fp32), one thread per state element.
 // Element e < D*Dv is in accumulator layout: tile u = e / 256 (a = u / (Dv/16),
 // b = u % (Dv/16)), lane = (e / 4) % 64, r = e % 4, which is S[16a + 4(lane/16) + r][16b + lane%16].
@@ -977,7 +1020,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
 // [D][DV] slice whose initial value is columns part * DV .. of the caller's S0 rows.
 template <int D, int DV, bool GATED, int VS = 1>
 __global__ __launch_bounds__(kThreads) void scan_kernel(float* st, float* zt, const float* lg, const float* s0,
-                                                       const float* z0, int nseg) {
+                                                       const float* z0, int nslots, int nscan) {
     constexpr int NS = D * DV;
     constexpr int NBLK = (NS + D + kThreads - 1) / kThreads;   // workgroups per head and part
     const int e = (blockIdx.x % NBLK) * kThreads + threadIdx.x;
@@ -993,18 +1036,18 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(float* st, float* zt, co
         const int a = u / (DV / 16), b = u % (DV / 16);
         const int d = 16 * a + 4 * (lane / 16) + r, dv = 16 * b + lane % 16;
         uidx = size_t(bh) * NS * VS + size_t(d) * DV * VS + part * DV + dv;
-        base = st + size_t(vbh) * nseg * NS + e;
+        base = st + size_t(vbh) * nslots * NS + e;
         stride = NS;
         init = s0;
     } else {
         const int d = e - NS;
         uidx = size_t(bh) * D + d;
-        base = zt + size_t(vbh) * nseg * D + d;
+        base = zt + size_t(vbh) * nslots * D + d;
         stride = D;
         init = z0;
     }
-    const float* lgb = GATED ? lg + size_t(vbh) * nseg : nullptr;
-    const int n = nseg - 1;
+    const float* lgb = GATED ? lg + size_t(vbh) * nslots : nullptr;
+    const int n = nscan;
     float acc = init ? init[uidx] : 0.0f;
     constexpr int U = 8;                         // loads in flight per thread
     for (int s0i = 0; s0i < n; s0i += U) {
@@ -1026,7 +1069,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(float* st, float* zt, co
 }
 
 // One state slot (accumulator layout; nslots per head) into the caller's [D][Dv] and [D]
-// layouts: S_N, z_N from slot nseg-1 of the forward.  A launch of its own, so s_out may
+// layouts: S_N, z_N from the forward's last slot.  A launch of its own, so s_out may
 // alias s0 (every read of s0 is done by then).
 // With VS column parts, slot vbh = bh * VS + part fills columns part * DV .. of S_N's
 // rows, and part 0's copy of z gives z_N.

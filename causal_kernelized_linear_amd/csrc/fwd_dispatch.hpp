@@ -13,8 +13,10 @@ template <typename E, int D, int DV, int CH, bool GATED, bool IDENT = false, boo
 hipError_t run_fwd_walks(const FwdLaunch& p) {
     using ShT = WalkShape<E, D, DV, CH, GATED, false>;
     using ShO = WalkShape<E, D, DV, CH, GATED, true>;
+    const int tparts = prefix_direct(p.nseg, D, DV) ? 1 : p.tparts;
+    const int nslots = (p.nseg - 1) * tparts + 1;
     size_t off_zt = 0, off_lg = 0;
-    fwd_workspace_layout(size_t(p.BH) * VS * p.nseg, D, DV, &off_zt, &off_lg);
+    fwd_workspace_layout(size_t(p.BH) * VS * nslots, D, DV, &off_zt, &off_lg);
     char* wsb = static_cast<char*>(p.ws);
     WalkArgs a;
     a.q = p.q; a.k = p.k; a.v = p.v; a.g = p.g; a.o = p.o;
@@ -22,7 +24,8 @@ hipError_t run_fwd_walks(const FwdLaunch& p) {
     a.zt = reinterpret_cast<float*>(wsb + off_zt);
     a.lg = reinterpret_cast<float*>(wsb + off_lg);
     a.s0 = p.s0; a.z0 = p.z0;
-    a.N = p.N; a.BH = p.BH; a.nseg = p.nseg; a.L = p.L; a.eps = p.eps; a.normalize = p.normalize;
+    a.N = p.N; a.BH = p.BH; a.nseg = p.nseg; a.L = p.L; a.tparts = tparts; a.nslots = nslots;
+    a.eps = p.eps; a.normalize = p.normalize;
     a.fshift = p.fshift;
     a.direct = prefix_direct(p.nseg, D, DV) ? 1 : 0;
     a.want_final = (p.s_out || p.z_out) ? 1 : 0;
@@ -43,18 +46,18 @@ hipError_t run_fwd_walks(const FwdLaunch& p) {
     auto mark = [&](int i) { if (p.prof[i]) (void)hipEventRecord(p.prof[i], p.stream); };
     mark(0);
     if (p.nseg > 1)
-        hipLaunchKernelGGL(k_tot, dim3(walk_grid(unsigned(p.BH) * unsigned(p.nseg - 1), VS)), dim3(kThreads),
-                           ShT::kBytes, p.stream, a);
+        hipLaunchKernelGGL(k_tot, dim3(walk_grid(unsigned(p.BH) * unsigned((p.nseg - 1) * tparts), VS)),
+                           dim3(kThreads), ShT::kBytes, p.stream, a);
     mark(1);
     if (p.nseg > 1 && !a.direct)
         hipLaunchKernelGGL((scan_kernel<D, DV, GATED, VS>), dim3(vheads * NBLK), dim3(kThreads), 0, p.stream, a.st,
-                           a.zt, a.lg, p.s0, p.z0, p.nseg);
+                           a.zt, a.lg, p.s0, p.z0, nslots, nslots - 1);
     mark(2);
     hipLaunchKernelGGL(k_out, dim3(walk_grid(unsigned(p.BH) * unsigned(p.nseg), VS)), dim3(kThreads), ShO::kBytes,
                        p.stream, a);
     if (a.want_final)
         hipLaunchKernelGGL((final_kernel<D, DV, VS>), dim3(vheads * NBLK), dim3(kThreads), 0, p.stream, a.st, a.zt,
-                           p.nseg, p.nseg - 1, p.s_out, p.z_out);
+                           nslots, nslots - 1, p.s_out, p.z_out);
     mark(3);
     return hipGetLastError();
 }

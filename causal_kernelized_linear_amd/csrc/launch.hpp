@@ -25,6 +25,7 @@ struct FwdLaunch {
     hipEvent_t prof[4];      // measurement hook: all NULL when unused
     float fshift = 0.0f;     // the walk under relu(x) + fshift features only
     int vsplit = 1;          // column parts of Dv walked by separate workgroups (walk_vsplit)
+    int tparts = 1;          // parts of a segment walked by separate totals workgroups (scanned prefix only)
 };
 
 // Chunk sizes with kernel instantiations.
@@ -49,11 +50,14 @@ constexpr size_t kMaxLds = 160 * 1024;   // LDS per compute unit on gfx950
 // Waves per SIMD a walk kernel is compiled for (one wave of every workgroup sits on each
 // SIMD, so this is also its workgroups per compute unit): what its LDS allows, capped by
 // the register budget its shape can live with.  The plan sizes one round of the output
-// walk with it.
+// walk with it, and the totals walk's parts (totals_parts) fill one round of its own.
+// The totals walk holds no outputs and fits two waves at every shape but the gated one
+// at D = Dv = 128 from 128-token chunks (at D = Dv = 128, chunk 64: one wave gave 220 us
+// for the long-context totals, two with twice the workgroups 166 us).
 constexpr int walk_waves(int esize, int D, int Dv, int chunk, bool gated, bool out) {
     const int lds = int(kMaxLds / walk_lds_bytes(esize, D, Dv, chunk, gated, out));
     const int work = D * Dv * (esize == 2 ? 1 : 2) * (chunk > 128 ? 2 : 1);   // grows with the live tiles
-    int regs = 1;
+    int regs = out || (gated && work >= 128 * 128 && chunk >= 128) ? 1 : 2;
     if (work <= 64 * 64) regs = out ? 2 : 3;
     else if (work <= 2 * 64 * 64) regs = out ? 1 : 2;
     const int v = lds < regs ? lds : regs;
@@ -67,6 +71,15 @@ constexpr int walk_vsplit(int esize, int D, int Dv, int chunk, bool gated) {
     if (walk_lds_bytes(esize, D, Dv, chunk, gated) <= kMaxLds) return 1;
     if (Dv == 128 && walk_lds_bytes(esize, D, 64, chunk, gated) <= kMaxLds) return 2;
     return 0;
+}
+
+// Prefetch depth of a walk kernel: chunks whose K, V (and Q) loads are in flight ahead
+// of the chunk being processed.  Two for the ungated 128 x 128 output walks of chunks up
+// to 64 tokens: one workgroup per compute unit leaves them only their own loads to hide
+// HBM latency, and a second register set fits (the gated output walk would spill; the
+// totals walk would drop to one wave per SIMD).
+constexpr int walk_depth(int esize, int D, int Dv, int chunk, bool gated, bool out) {
+    return out && esize == 2 && !gated && D * Dv >= 128 * 128 && chunk <= 64 ? 2 : 1;
 }
 
 inline size_t round_up256(size_t x) { return (x + 255) / 256 * 256; }
@@ -84,6 +97,18 @@ inline size_t fwd_workspace_layout(size_t slots, int D, int Dv, size_t* off_zt, 
 // The output walk sums the totals in front of its segment itself when they are few
 // and small (at most seven 64 x 64 states); otherwise a scan launch does it first.
 inline bool prefix_direct(int nseg, int D, int Dv) { return size_t(nseg - 1) * D * Dv <= size_t(7) * 64 * 64; }
+
+// Parts each segment's total is cut into (scanned prefix only; the direct prefix sums
+// one total per segment): as many as fill one round of the totals walk, whose
+// (nseg - 1) segments per head alone can leave compute units idle, and at most one
+// per chunk.
+inline int totals_parts(long heads, int nseg, int L, int D, int Dv, long round) {
+    if (nseg <= 1 || prefix_direct(nseg, D, Dv)) return 1;
+    long p = round / (heads * long(nseg - 1));
+    if (p < 1) p = 1;
+    if (p > L) p = L;
+    return int(p);
+}
 
 // Dynamic LDS bytes of a gradient kernel: phi(Q), phi(K) [C][D], V, dOut [C][Dv] and one
 // state [D][Dv], each row padded by 16 bytes, plus the chunk's decays, dden, 1/d, the

@@ -337,6 +337,22 @@ def test_workload_decode_sampled_heads():
     assert matrix_rel_err(sel(z, heads), z_ref[None]) <= 1e-6
 
 
+@pytest.mark.parametrize("gated", [False, True], ids=["ungated", "gated"])
+def test_totals_in_parts(gated):
+    # 8 heads of D = Dv = 128 at chunk 64 on a 256-CU device: 32 segments of 3 chunks, so
+    # the prefix comes from the scan, and each segment's total is walked in two parts (of
+    # 2 and 1 chunks) that the scan chains in order; a ragged tail and an initial state
+    B, H, N, D, Dv, chunk = 1, 8, 6107, 128, 128, 64
+    inp = workloads.random_inputs(53, B, H, N, D, Dv, dtype="bf16", gated=gated, g_low=0.95, with_state=True,
+                                  state_scale=5.0)
+    _say(f"totals in parts gated={gated}")
+    o, S, z = run_fwd(inp, chunk, s0=inp["s0"], z0=inp["z0"], return_state=True)
+    o_ref, S_ref, z_ref = oracle_fwd(inp, s0=inp["s0"], z0=inp["z0"])
+    assert rowwise_rel_err(to64(o), o_ref) <= TOL["bf16"]
+    assert matrix_rel_err(to64(S), S_ref) <= TOL["bf16"]
+    assert matrix_rel_err(to64(z), z_ref) <= TOL["bf16"]
+
+
 # ------------------------------------------------ many heads, few segments ----
 
 @pytest.mark.parametrize("gated", [False, True], ids=["ungated", "gated"])
