@@ -1,17 +1,17 @@
 """Benchmark of the causal kernelized linear attention hot path on one MI355X.
 
-One step = one chunked forward (phi, per-segment state totals, the prefix that
+One step = one chunked forward (phi, the per-segment state totals, the prefix that
 carries the state across segments, the masked intra-chunk products, the
-carried-state term and the divide) over the
-training-shaped workload B=8, H=16, N=4096, D=Dv=64, bf16, chunk 128, with the
-inputs already resident in HBM.  Input sets are rotated so no step starts with
-its inputs warm in the 256 MB Infinity Cache.  The scalar-gated forward
-(B=4, H=16, N=8192, D=Dv=64, chunk 128), the long-context forward
-(B=1, H=32, N=65536, D=Dv=128, chunk sweep), the decode step (B=256, H=32,
-D=Dv=128, fp32 state), its gated form, the normaliser-free output mode of the
-gated forward and of the gated decode, the backward of the training-shaped and
-gated forwards, the per-dimension decay (forward and decode) and the ReLU and FAVOR+
-feature maps are timed in the same run and reported in extra fields.
+carried-state term and the divide) over the long-context workload B=1, H=32,
+N=65536, D=Dv=128, bf16 inputs 0.5 N(0,1), fp32 state, chunk 64 (--chunk), with the
+inputs already resident in HBM.  Input sets are rotated so no step starts with its
+inputs warm in the 256 MB Infinity Cache.  Timed in the same run and reported in
+extra fields: the chunk sweep 64/128/256 of that workload, the training-shaped
+forward (B=8, H=16, N=4096, D=Dv=64, chunk 128), the fp32 parity workload (B=1, H=2,
+N=512, D=Dv=64, chunk 64), the scalar-gated forward (B=4, H=16, N=8192, D=Dv=64, chunk
+128), the decode step (B=256, H=32, D=Dv=128, fp32 state), its gated form, the
+normaliser-free output mode, the backward of the training-shaped and gated forwards,
+the per-dimension decay (forward and decode) and the ReLU and FAVOR+ feature maps.
 
 Prints ONE JSON line.  ms_per_step and value come from a timed pass bracketed by
 two hipEvents only.  Per-kernel durations come from a second timed pass of the same
@@ -21,7 +21,10 @@ few microseconds each, so they never enter the headline.  A third pass brackets
 only the output walk (one event before it, one after); the roofline object prices
 that kernel time against MI355X's 8 TB/s.  Its traffic figure comes from the
 committed rocprofv3 counter summary and is null once the kernel sources have
-changed.
+changed.  The oracle baseline (cpu_baseline) runs before the GPU is touched, on a
+bounded sample of the headline workload, pooled over the host cores.
+
+--only selects legs (for profiling runs); --no-extra times the headline alone.
 """
 from __future__ import annotations
 
@@ -40,9 +43,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 # the forward's steps between the measurement hook's four events: segment totals, the
 # scan over segments (skipped when the output walk sums the prefix itself), output walk
 PHASES = ("walk_totals", "scan", "walk_output")
-DOMINANT = ("walk_output", "walk_kernel<bf16,64,64,{c},ungated,output>")
 KERNEL_SOURCES = os.path.join(ROOT, "causal_kernelized_linear_amd", "csrc")
-COUNTERS = os.path.join(ROOT, "profiles", "counters_walk_output_train_bf16.json")
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "causal linear-attn fwd tokens/s + % bf16 MFMA peak; decode GB/s % HBM peak"
 
@@ -364,8 +365,9 @@ def decode_bytes(w, with_z=True):
     return per_head * w.B * w.H
 
 
-# the files the dominant kernel (the bf16 output walk) is built from
-DOMINANT_SOURCES = ("chunk_walk.hpp", "device_common.hpp", "fwd_bf16.hip", "fwd_dispatch.hpp", "launch.hpp")
+# the files the dominant kernel (the bf16 output walk) and its launch plan are built from
+DOMINANT_SOURCES = ("chunk_walk.hpp", "device_common.hpp", "fwd_bf16.hip", "fwd_dispatch.hpp", "launch.hpp",
+                    "api.hip")
 
 
 def source_digest():
@@ -378,12 +380,16 @@ def source_digest():
     return h.hexdigest()
 
 
-def stored_traffic(kernel_name):
-    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter
-    summary, scaled by its copy-kernel calibration; None when the kernel sources changed
-    since the counters were taken."""
+def counters_path(workload, chunk):
+    return os.path.join(ROOT, "profiles", f"counters_walk_output_{workload}_c{chunk}.json")
+
+
+def stored_traffic(kernel_name, workload, chunk):
+    """HBM bytes per launch of the output walk from the committed rocprofv3 counter summary
+    of this workload and chunk, scaled by its copy-kernel calibration; None when there is
+    none or the kernel sources changed since the counters were taken."""
     try:
-        with open(COUNTERS) as f:
+        with open(counters_path(workload, chunk)) as f:
             c = json.load(f)
     except (OSError, ValueError):
         return None
@@ -392,29 +398,88 @@ def stored_traffic(kernel_name):
     return 1024.0 * (c["fetch_kib"] * c["fetch_factor"] + c["write_kib"] * c["write_factor"])
 
 
-def cpu_baseline(w, seconds_hint=10.0):
-    """The fp64 oracle, as it stands, on a bounded sample of workload w (all heads,
-    the first tokens), on the host cores; returns tokens/s scaled to the workload."""
-    import numpy as np
-    from causal_kernelized_linear_amd import workloads
-    import oracle
+# ---------------------------------------------------------------- oracle baseline ----
 
-    ntok = w.N
+_CPU_INPUTS = {}
+
+
+def _one_thread():
+    """Pool initializer: every worker keeps to one thread."""
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except ImportError:
+        pass
+
+
+def _oracle_heads(heads):
+    """The oracle over some (b, h) heads of the inputs the parent drew before forking."""
+    import numpy as np
+    import oracle
+    q, k, v = (_CPU_INPUTS[n] for n in ("q", "k", "v"))
+    pick = lambda a: np.stack([a[b, h] for b, h in heads])[None]
+    o, _, _ = oracle.causal_linear_attention(pick(q), pick(k), pick(v))
+    return float(o[0, :, -1].sum())
+
+
+def cpu_baseline(w, ntok):
+    """The fp64 oracle, as it stands, on a bounded sample of workload w: every head, the
+    first `ntok` tokens (drawn with the workload's seed at that length).  The heads are
+    dealt to a fork pool of one worker per host core this process may run on (at most 16,
+    the host share of one GPU), each kept to one thread.  Returns tokens/s of the sample
+    (B * ntok tokens over the wall time, all heads) and the core count used."""
+    import multiprocessing as mp
+    from causal_kernelized_linear_amd import workloads
+
     inp = workloads.make_inputs(w, N=ntok)
-    q, k, v = (workloads.to_f64(inp[n]) for n in ("q", "k", "v"))
-    t = time.perf_counter()
-    oracle.causal_linear_attention(q, k, v)
-    dt = time.perf_counter() - t
-    # B*ntok token positions (every head) in dt seconds
+    for n in ("q", "k", "v"):
+        _CPU_INPUTS[n] = workloads.to_f64(inp[n])
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    cores = max(1, min(len(os.sched_getaffinity(0)), 16, len(heads)))
+    groups = [heads[i::cores] for i in range(cores)]
+    ctx = mp.get_context("fork")
+    with ctx.Pool(cores, initializer=_one_thread) as pool:
+        t = time.perf_counter()
+        pool.map(_oracle_heads, groups, chunksize=1)
+        dt = time.perf_counter() - t
+    _CPU_INPUTS.clear()
     return {
         "value": w.B * ntok / dt,
         "unit": "tokens/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
-        "sample": f"fp64 NumPy recurrence over the whole workload ({w.B}x{w.H} heads, {ntok} tokens), "
-                  f"{dt:.1f} s, one thread (elementwise NumPy and einsum), "
-                  f"host has {os.cpu_count()} cpus, affinity {len(os.sched_getaffinity(0))}",
+        "sample": f"{w.name}: fp64 NumPy recurrence over all {w.B}x{w.H} heads and the first {ntok} of "
+                  f"{w.N} tokens, the heads dealt to {cores} single-threaded worker processes; "
+                  f"{dt:.2f} s wall (host: {os.cpu_count()} cpus, affinity {len(os.sched_getaffinity(0))})",
         "seconds": dt,
+    }
+
+
+# ------------------------------------------------------------------------- legs ----
+
+LEGS = ("longctx", "sweep", "train", "fp32", "gated", "gated_numerator", "decode", "decode_gated", "backward",
+        "vdecay", "decode_vdecay", "features")
+
+
+def fwd_leg(w, chunk, r):
+    """Rates of one timed forward leg (r from time_forward) against both peaks, and the
+    output walk's own HBM rate from its event-bracketed time."""
+    units = fwd_units(w)
+    bpu, fpu = fwd_bytes_per_unit(w), fwd_flops_per_unit(w, chunk)
+    step_s = r["ms_per_step"] * 1e-3
+    out_s = r["walk_output_ms_alone"] * 1e-3
+    return {
+        "tokens_per_s": w.B * w.N / step_s, "ms_per_step": r["ms_per_step"],
+        "kernel_ms": r["kernel_ms"], "kernel_ms_median": r["kernel_ms_median"],
+        "walk_output_ms_alone": r["walk_output_ms_alone"],
+        "walk_output_hbm_frac": bpu * units / out_s / 1e9 / HBM_PEAK_GBS,
+        "algorithmic_GBps": bpu * units / step_s / 1e9,
+        "hbm_frac": bpu * units / step_s / 1e9 / HBM_PEAK_GBS,
+        "useful_TFLOPs": fpu * units / step_s / 1e12,
+        "mfma_bf16_frac": fpu * units / step_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "input_sets_rotated": r["input_sets"],
     }
 
 
@@ -422,11 +487,13 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # The device needs tens of milliseconds of sustained work to reach its steady clocks:
-    # after 10 warmup steps (about 1 ms) train_bf16 measured 85-87 us per step, after 1000
-    # (about 80 ms) 71-72 us, run after run on one device.
-    ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--chunk", type=int, default=128)
+    # The device needs tens of milliseconds of sustained work to reach its steady clocks
+    # (train_bf16: 85-87 us per step after 10 warmup steps, 71-72 us after 1000).
+    ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--chunk", type=int, default=64, help="chunk of the long-context headline")
+    ap.add_argument("--only", default="", help="comma-separated legs to run (default: all): " + ", ".join(LEGS))
+    ap.add_argument("--cpu-tokens", type=int, default=16384,
+                    help="tokens per head of the oracle's bounded sample of the headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="time only the headline workload")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -436,9 +503,22 @@ def main():
         print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
+    legs = [x for x in args.only.split(",") if x] or (["longctx"] if args.no_extra else list(LEGS))
+    for x in legs:
+        if x not in LEGS:
+            print(f"unknown leg {x!r}; legs: {', '.join(LEGS)}", file=sys.stderr)
+            sys.exit(2)
+
+    from causal_kernelized_linear_amd import workloads
+    wl = workloads.WORKLOADS["longctx_bf16"]
+    # the oracle baseline runs first, in worker processes forked before this process
+    # touches the GPU
+    cb = None
+    if "longctx" in legs and not args.no_cpu_baseline:
+        cb = cpu_baseline(wl, min(args.cpu_tokens, wl.N))
 
     import torch
-    from causal_kernelized_linear_amd import binding, workloads
+    from causal_kernelized_linear_amd import binding
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -454,74 +534,72 @@ def main():
         del src, dst
         torch.cuda.empty_cache()
 
-    w = workloads.WORKLOADS["train_bf16"]
+    extra_steps = max(5, min(args.steps, 20))
+    extra_warm = max(2, min(args.warmup, 200))     # each leg follows host-side set-up
     chunk = args.chunk
-    r = time_forward(w, chunk, args.steps, args.warmup, ev)
-    units = fwd_units(w)
-    tok_s = w.B * w.N / (r["ms_per_step"] * 1e-3)
-    bpu = fwd_bytes_per_unit(w)
-    fpu = fwd_flops_per_unit(w, chunk)
-    dom, dom_name = DOMINANT
-    dom_name = dom_name.format(c=chunk)
-    t_out = r["walk_output_ms_alone"] * 1e-3
-    achieved = bpu * units / t_out / 1e9
-    step_s = r["ms_per_step"] * 1e-3
-    line = {
-        "metric": METRIC,
-        "value": tok_s,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": r["ms_per_step"],
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "train_bf16: causal linear attention forward B=8 H=16 N=4096 D=Dv=64 bf16, "
-                               "fp32 state, chunk %d, eps 1e-6" % chunk,
-                   "B": w.B, "H": w.H, "N": w.N, "D": w.D, "Dv": w.Dv, "chunk": chunk},
-        "roofline": {
-            "bound": "hbm",
-            "kernel": dom_name,
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS,
-            "traffic": stored_traffic(dom_name),
-            "algorithmic_bytes_per_launch": bpu * units,
-            "kernel_ms": r["walk_output_ms_alone"],
-            "kernel_ms_note": "hipEvents before and after the output walk only (third timed pass)",
-        },
-        "forward": {
-            "kernel_ms": r["kernel_ms"],
-            "kernel_ms_median": r["kernel_ms_median"],
-            "wall_ms_per_step": r["wall_ms_per_step"],
-            "ms_per_step_with_launch_events": r["ms_per_step_with_launch_events"],
-            "algorithmic_GBps": bpu * units / step_s / 1e9,
-            "hbm_frac": bpu * units / step_s / 1e9 / HBM_PEAK_GBS,
-            "useful_TFLOPs": fpu * units / step_s / 1e12,
-            "mfma_bf16_frac": fpu * units / step_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-            "input_sets_rotated": r["input_sets"],
-        },
-    }
+    line = {"metric": METRIC, "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
 
-    if not args.no_extra:
-        extra_steps = max(5, min(args.steps, 20))
-        extra_warm = max(2, min(args.warmup, 200))     # each leg follows host-side set-up
-        wg = workloads.WORKLOADS["gated_bf16"]
+    if "longctx" in legs:
+        r = time_forward(wl, chunk, args.steps, args.warmup, ev, rotate_bytes=2.5e9)
+        units = fwd_units(wl)
+        bpu = fwd_bytes_per_unit(wl)
+        dom_name = f"walk_kernel<bf16,{wl.D},{wl.Dv},{chunk},ungated,output>"
+        achieved = bpu * units / (r["walk_output_ms_alone"] * 1e-3) / 1e9
+        line.update({
+            "value": wl.B * wl.N / (r["ms_per_step"] * 1e-3),
+            "ms_per_step": r["ms_per_step"],
+            "config": {"workload": "longctx_bf16: causal linear attention forward B=1 H=32 N=65536 D=Dv=128 bf16 "
+                                   "(0.5 N(0,1) inputs), fp32 state, chunk %d, eps 1e-6" % chunk,
+                       "B": wl.B, "H": wl.H, "N": wl.N, "D": wl.D, "Dv": wl.Dv, "chunk": chunk},
+            "roofline": {
+                "bound": "hbm",
+                "kernel": dom_name,
+                "achieved": achieved,
+                "peak": HBM_PEAK_GBS,
+                "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS,
+                "traffic": stored_traffic(dom_name, wl.name, chunk),
+                "algorithmic_bytes_per_launch": bpu * units,
+                "kernel_ms": r["walk_output_ms_alone"],
+                "kernel_ms_note": "hipEvents on the launch stream before and after the output walk only "
+                                  "(third timed pass)",
+            },
+            "forward": fwd_leg(wl, chunk, r),
+        })
+        line["forward"]["wall_ms_per_step"] = r["wall_ms_per_step"]
+        line["forward"]["ms_per_step_with_launch_events"] = r["ms_per_step_with_launch_events"]
+
+    if "sweep" in legs:
+        sweep = {}
+        for c in wl.chunks:
+            rl = time_forward(wl, c, max(3, extra_steps // 2), extra_warm, ev, rotate_bytes=2.5e9)
+            sweep[str(c)] = fwd_leg(wl, c, rl)
+        line["longctx_chunk_sweep"] = {"workload": "longctx_bf16: B=1 H=32 N=65536 D=Dv=128 bf16", **sweep}
+
+    if "train" in legs:
+        wt = workloads.WORKLOADS["train_bf16"]
+        rt = time_forward(wt, 128, args.steps, extra_warm, ev)
+        line["train"] = {"workload": "train_bf16: B=8 H=16 N=4096 D=Dv=64 bf16, fp32 state, chunk 128",
+                         **fwd_leg(wt, 128, rt),
+                         "walk_output_traffic": stored_traffic("walk_kernel<bf16,64,64,128,ungated,output>",
+                                                               wt.name, 128)}
+
+    if "fp32" in legs:
+        wf = workloads.WORKLOADS["fp32_small"]
+        rf = time_forward(wf, 64, extra_steps, extra_warm, ev)
+        line["fp32_small"] = {"workload": "fp32_small: B=1 H=2 N=512 D=Dv=64 fp32, chunk 64 (launch-bound)",
+                              "tokens_per_s": wf.B * wf.N / (rf["ms_per_step"] * 1e-3),
+                              "ms_per_step": rf["ms_per_step"], "kernel_ms": rf["kernel_ms"]}
+
+    wg = workloads.WORKLOADS["gated_bf16"]
+    if "gated" in legs:
         rg = time_forward(wg, 128, extra_steps, extra_warm, ev)
-        ug = fwd_units(wg)
-        sg = rg["ms_per_step"] * 1e-3
-        line["gated"] = {
-            "workload": "gated_bf16: B=4 H=16 N=8192 D=Dv=64 bf16, scalar gate, chunk 128",
-            "tokens_per_s": wg.B * wg.N / sg, "ms_per_step": rg["ms_per_step"], "kernel_ms": rg["kernel_ms"],
-            "algorithmic_GBps": fwd_bytes_per_unit(wg) * ug / sg / 1e9,
-            "hbm_frac": fwd_bytes_per_unit(wg) * ug / sg / 1e9 / HBM_PEAK_GBS,
-            "useful_TFLOPs": fwd_flops_per_unit(wg, 128) * ug / sg / 1e12,
-            "mfma_bf16_frac": fwd_flops_per_unit(wg, 128) * ug / sg / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-        }
+        line["gated"] = {"workload": "gated_bf16: B=4 H=16 N=8192 D=Dv=64 bf16, scalar gate, chunk 128",
+                         **fwd_leg(wg, 128, rg)}
+
+    if "decode" in legs:
         wd = workloads.WORKLOADS["decode_bf16"]
         rd = time_decode(wd, extra_steps, extra_warm, ev)
         sd = rd["ms_per_step"] * 1e-3
@@ -531,14 +609,19 @@ def main():
             "tokens_per_s": wd.B / sd, "ms_per_step": rd["ms_per_step"], "ms_median": rd["ms_median"],
             "bytes_per_step": decode_bytes(wd),
         }
+
+    if "gated_numerator" in legs:
         rn = time_forward(wg, 128, extra_steps, extra_warm, ev, normalize=False)
         sn = rn["ms_per_step"] * 1e-3
+        ug = fwd_units(wg)
         line["gated_numerator"] = {
             "workload": "gated_bf16 in the normaliser-free output mode (o = phi(q)^T S)",
             "tokens_per_s": wg.B * wg.N / sn, "ms_per_step": rn["ms_per_step"], "kernel_ms": rn["kernel_ms"],
             "algorithmic_GBps": fwd_bytes_per_unit(wg) * ug / sn / 1e9,
             "hbm_frac": fwd_bytes_per_unit(wg) * ug / sn / 1e9 / HBM_PEAK_GBS,
         }
+
+    if "decode_gated" in legs:
         wdg = workloads.WORKLOADS["decode_gated_bf16"]
         for key, norm in (("decode_gated", True), ("decode_gated_numerator", False)):
             rdg = time_decode(wdg, extra_steps, extra_warm, ev, normalize=norm)
@@ -551,6 +634,8 @@ def main():
                 "tokens_per_s": wdg.B / sdg, "ms_per_step": rdg["ms_per_step"], "ms_median": rdg["ms_median"],
                 "bytes_per_step": nbytes,
             }
+
+    if "backward" in legs:
         for key, wname in (("backward", "train_bf16"), ("backward_gated", "gated_bf16")):
             wb = workloads.WORKLOADS[wname]
             rb = time_backward(wb, extra_steps, extra_warm, ev)
@@ -565,6 +650,8 @@ def main():
                 "useful_TFLOPs": bwd_flops_per_unit(wb) * ub / sb / 1e12,
                 "mfma_bf16_frac": bwd_flops_per_unit(wb) * ub / sb / 1e12 / MFMA_BF16_PEAK_TFLOPS,
             }
+
+    if "vdecay" in legs:
         wvd = workloads.WORKLOADS["vdecay_bf16"]
         rvd = time_vdecay(wvd, extra_steps, extra_warm, ev)
         svd = rvd["ms_per_step"] * 1e-3
@@ -575,6 +662,8 @@ def main():
             "algorithmic_GBps": vd_bytes_per_unit(wvd) * uvd / svd / 1e9,
             "hbm_frac": vd_bytes_per_unit(wvd) * uvd / svd / 1e9 / HBM_PEAK_GBS,
         }
+
+    if "decode_vdecay" in legs:
         wdv = workloads.WORKLOADS["decode_vdecay_bf16"]
         rdv = time_decode(wdv, extra_steps, extra_warm, ev)
         sdv = rdv["ms_per_step"] * 1e-3
@@ -583,6 +672,8 @@ def main():
             "GBps": decode_bytes(wdv) / sdv / 1e9, "hbm_frac": decode_bytes(wdv) / sdv / 1e9 / HBM_PEAK_GBS,
             "tokens_per_s": wdv.B / sdv, "ms_per_step": rdv["ms_per_step"], "bytes_per_step": decode_bytes(wdv),
         }
+
+    if "features" in legs:
         for key, wname, feat in (("features_relu", "train_bf16", "relu"), ("features_favor", "favor_bf16", "favor")):
             wf = workloads.WORKLOADS[wname]
             rf = time_features(wf, feat, extra_steps, extra_warm, ev)
@@ -595,28 +686,10 @@ def main():
                 "algorithmic_GBps": fwd_bytes_per_unit(wf) * uf / sf / 1e9,
                 "hbm_frac": fwd_bytes_per_unit(wf) * uf / sf / 1e9 / HBM_PEAK_GBS,
             }
-        wl = workloads.WORKLOADS["longctx_bf16"]
-        sweep = {}
-        for c in wl.chunks:
-            try:
-                rl = time_forward(wl, c, max(3, extra_steps // 2), extra_warm, ev, rotate_bytes=2.5e9)
-            except RuntimeError as e:
-                sweep[str(c)] = {"status": str(e)}
-                continue
-            ul = fwd_units(wl)
-            sl = rl["ms_per_step"] * 1e-3
-            sweep[str(c)] = {
-                "tokens_per_s": wl.B * wl.N / sl, "ms_per_step": rl["ms_per_step"], "kernel_ms": rl["kernel_ms"],
-                "algorithmic_GBps": fwd_bytes_per_unit(wl) * ul / sl / 1e9,
-                "hbm_frac": fwd_bytes_per_unit(wl) * ul / sl / 1e9 / HBM_PEAK_GBS,
-                "useful_TFLOPs": fwd_flops_per_unit(wl, c) * ul / sl / 1e12,
-                "mfma_bf16_frac": fwd_flops_per_unit(wl, c) * ul / sl / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-            }
-        line["longctx_chunk_sweep"] = {"workload": "longctx_bf16: B=1 H=32 N=65536 D=Dv=128 bf16", **sweep}
 
-    if not args.no_cpu_baseline:
-        cb = cpu_baseline(w)
+    if cb is not None:
         line["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+        line["cpu_baseline"]["gpu_speedup"] = line["value"] / cb["value"]
     ev.close()
     print(json.dumps(line), flush=True)
 

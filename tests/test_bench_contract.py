@@ -25,10 +25,16 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in (r.stdout + r.stderr)
 
 
+def test_unknown_leg_is_refused():
+    r = _bench("--only", "longctx,nosuchleg", timeout=120)
+    assert r.returncode == 2
+    assert "nosuchleg" in r.stderr
+
+
 @pytest.mark.gpu
 def test_bench_line_fields():
-    print("bench: --steps 3 --warmup 2 --no-extra", flush=True)
-    r = _bench("--steps", "3", "--warmup", "2", "--no-extra")
+    print("bench: --steps 3 --warmup 2 --no-extra --cpu-tokens 512", flush=True)
+    r = _bench("--steps", "3", "--warmup", "2", "--no-extra", "--cpu-tokens", "512")
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
     assert len(lines) == 1
@@ -40,6 +46,7 @@ def test_bench_line_fields():
     assert d["value"] > 0 and d["ms_per_step"] > 0 and d["higher_is_better"] is True
     assert d["unit"] == "tokens/s" and d["dtype"] == "bf16" and d["vs_baseline"] is None
     assert "workload" in d["config"] and "model" not in d["config"]
+    assert d["config"]["workload"].startswith("longctx_bf16") and d["config"]["chunk"] == 64
     # value is tokens per second of the timed forwards: B * N tokens per step
     cfg = d["config"]
     assert d["value"] == pytest.approx(cfg["B"] * cfg["N"] / (d["ms_per_step"] * 1e-3), rel=1e-6)
@@ -52,5 +59,5 @@ def test_bench_line_fields():
     if rf["traffic"] is not None:
         assert 1.0 <= rf["traffic"] / rf["algorithmic_bytes_per_launch"] < 1.2
     cb = d["cpu_baseline"]
-    assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
+    assert cb["kind"] == "oracle" and cb["value"] > 0 and 1 <= cb["cores"] <= 16
     assert cb["unit"] == "tokens/s" and cb["sample"]
