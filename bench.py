@@ -326,7 +326,7 @@ def time_features(w, feature, steps, warmup, ev, M=64):
     base = workloads.make_inputs(w)
     sets = [{n: t.to(dev) for n, t in base.items()}]
     sets.append({n: t.clone() for n, t in sets[0].items()})
-    W = workloads.favor_projection(w.seed, w.H, M, w.D).to(dev) if feature == "favor" else None
+    W = workloads.favor_projection(w.seed, w.H, M, w.D, orthogonal=True).to(dev) if feature == "favor" else None
     m = M if feature == "favor" else w.D
     dt = binding.BF16 if w.dtype == "bf16" else binding.F32
     ws = torch.empty(binding.linattn_fwd_features_workspace_size(w.B, w.H, w.N, w.D, w.Dv, w.chunks[0], m, dt),
@@ -681,7 +681,8 @@ def main():
             uf = fwd_units(wf)
             line[key] = {
                 "workload": f"{wname} forward under " + ("relu(x) + 0.05" if feat == "relu" else
-                                                         "FAVOR+ with 64 random features per head") + ", chunk 128",
+                                                         "FAVOR+ with 64 orthogonal random features per head") +
+                            ", chunk 128",
                 "tokens_per_s": wf.B * wf.N / sf, "ms_per_step": rf["ms_per_step"],
                 "algorithmic_GBps": fwd_bytes_per_unit(wf) * uf / sf / 1e9,
                 "hbm_frac": fwd_bytes_per_unit(wf) * uf / sf / 1e9 / HBM_PEAK_GBS,

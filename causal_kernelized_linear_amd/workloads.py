@@ -60,7 +60,7 @@ WORKLOADS = {
     "vdecay_bf16": Workload("vdecay_bf16", "vdecay", 4, 16, 8192, 64, 64, "bf16", (64,), 1007,
                             note="per-dimension decay per head and token (gated linear attention)"),
     "favor_bf16": Workload("favor_bf16", "fwd", 8, 16, 4096, 64, 64, "bf16", (128,), 1009, scale=64 ** -0.25,
-                           note="FAVOR+ random features (64 per head) on training-shaped inputs scaled by D^-1/4"),
+                           note="FAVOR+ random features (64 orthogonal rows per head) on training-shaped inputs scaled by D^-1/4"),
     "decode_vdecay_bf16": Workload("decode_vdecay_bf16", "decode_vdecay", 256, 32, 1, 128, 128, "bf16", (1,), 1008,
                                    note="one recurrent step under a per-dimension decay"),
 }
@@ -119,10 +119,29 @@ def make_inputs(w: Workload, B=None, H=None, N=None, with_grad=False):
     return out
 
 
-def favor_projection(seed, H, M, D):
-    """Per-head FAVOR+ projections W [H, M, D]: independent N(0, 1) rows, float32."""
+def favor_projection(seed, H, M, D, orthogonal=False):
+    """Per-head FAVOR+ projections W [H, M, D], float32.
+
+    Default: independent N(0, I_D) rows.  ``orthogonal=True``: the orthogonal random
+    features of Performer (aicassindra.com page, "Performer": the projections w_r are
+    made orthogonal).  Rows come in blocks of D; within a block their directions are the
+    orthonormal columns of the QR factor of a D x D Gaussian draw (signs fixed by R's
+    diagonal, so the basis is uniformly random), and each row is given the length of an
+    independent N(0, I_D) draw, so every single row is still distributed as N(0, I_D).
+    Blocks, and heads, are independent; the last block is cut to M rows."""
     gen = torch.Generator(device="cpu").manual_seed(seed)
-    return torch.randn(H, M, D, generator=gen, dtype=torch.float32)
+    if not orthogonal:
+        return torch.randn(H, M, D, generator=gen, dtype=torch.float32)
+    nblk = (M + D - 1) // D
+    W = torch.empty(H, nblk * D, D, dtype=torch.float64)
+    for h in range(H):
+        for b in range(nblk):
+            G = torch.randn(D, D, generator=gen, dtype=torch.float64)
+            Qf, R = torch.linalg.qr(G)
+            Qf = Qf * torch.sign(torch.diagonal(R))[None, :]
+            lengths = torch.randn(D, D, generator=gen, dtype=torch.float64).norm(dim=1)
+            W[h, b * D:(b + 1) * D] = Qf.T * lengths[:, None]
+    return W[:, :M].to(torch.float32).contiguous()
 
 
 def random_inputs(seed, B, H, N, D, Dv, dtype="bf16", scale=1.0, gated=False,

@@ -114,3 +114,22 @@ def test_features_workload_sampled_heads(feature):
                                                  feature=("relu", 0.05) if W is None else ("favor", Wsel))
     assert rowwise_rel_err(pick(o), o_ref) <= TOL["bf16"]
     assert torch.isfinite(o).all().item()
+
+
+@pytest.mark.parametrize("chunk", [64, 128])
+@pytest.mark.parametrize("M", [64, 128])
+def test_features_orthogonal_favor(M, chunk):
+    # the page's orthogonal projections (aicassindra.com page, "Performer"): blocks of D
+    # orthogonal rows, two blocks when M = 2 D
+    B, H, N, D, Dv = 2, 2, 700, 64, 64
+    inp = workloads.random_inputs(91 + M, B, H, N, D, Dv, dtype="bf16", scale=D ** -0.25, gated=True, g_low=0.9)
+    W = workloads.favor_projection(92 + M, H, M, D, orthogonal=True)
+    _say(f"orthogonal favor M={M} chunk={chunk}")
+    o, S, z = binding.fwd_features(*(_dev(inp[n]) for n in ("q", "k", "v")), "favor", W=_dev(W), g=_dev(inp["g"]),
+                                   chunk=chunk, return_state=True)
+    torch.cuda.synchronize()
+    o_ref, S_ref, z_ref = oracle.causal_linear_attention(to64(inp["q"]), to64(inp["k"]), to64(inp["v"]),
+                                                         g=to64(inp["g"]), feature=("favor", to64(W)))
+    assert rowwise_rel_err(to64(o), o_ref) <= TOL["bf16"]
+    assert matrix_rel_err(to64(S), S_ref) <= TOL["bf16"]
+    assert matrix_rel_err(to64(z), z_ref) <= TOL["bf16"]
