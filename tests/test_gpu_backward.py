@@ -159,11 +159,12 @@ def _heads(B, H, n, seed):
     return [(int(i) // H, int(i) % H) for i in sorted(idx)]
 
 
-@pytest.mark.parametrize("name", ["train_bf16", "gated_bf16"])
-def test_backward_workload_sampled_heads(name):
+@pytest.mark.parametrize("name,nheads", [("train_bf16", 3), ("gated_bf16", 3), ("longctx_bf16", 2)])
+def test_backward_workload_sampled_heads(name, nheads):
+    # longctx_bf16 is the D = Dv = 128 case at full size: 1024 chunks per head, runs of 16
     w = workloads.WORKLOADS[name]
     inp = workloads.make_inputs(w, with_grad=True)
-    heads = _heads(w.B, w.H, 3, 9)
+    heads = _heads(w.B, w.H, nheads, 9)
     _say(f"{name} backward full size, oracle on heads {heads}")
     got = gpu_bwd(inp)
     ref = oracle_bwd(inp, heads=heads)

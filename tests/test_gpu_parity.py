@@ -353,6 +353,40 @@ def test_totals_in_parts(gated):
     assert matrix_rel_err(to64(z), z_ref) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("shape", [(1, 3, 1000, 64, 64, 128), (1, 2, 700, 128, 128, 64), (2, 2, 900, 64, 128, 256)],
+                         ids=["D64c128", "D128c64", "D64Dv128c256"])
+def test_gated_weak_then_strong_gates(shape):
+    # gates near 1 for the first half of the sequence and in [0.2, 0.5] for the second:
+    # chunks whose total decay is mild, then chunks whose total decay falls far below
+    # 2^-60 (down to 2^-300 over 256 tokens), with the state carried across
+    B, H, N, D, Dv, chunk = shape
+    inp = workloads.random_inputs(71 + N, B, H, N, D, Dv, dtype="bf16", gated=True, g_low=0.95, with_state=True,
+                                  state_scale=5.0)
+    u = torch.rand(B, H, N, generator=torch.Generator().manual_seed(72))
+    inp["g"][:, :, N // 2:] = 0.2 + 0.3 * u[:, :, N // 2:]
+    _say(f"gated, both decay paths {shape}")
+    o, S, z = run_fwd(inp, chunk, s0=inp["s0"], z0=inp["z0"], return_state=True)
+    o_ref, S_ref, z_ref = oracle_fwd(inp, s0=inp["s0"], z0=inp["z0"])
+    assert rowwise_rel_err(to64(o), o_ref) <= TOL["bf16"]
+    assert matrix_rel_err(to64(S), S_ref) <= TOL["bf16"]
+    assert matrix_rel_err(to64(z), z_ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("g,chunk", [(0.7265, 128), (0.7210, 128), (0.5276, 64)],
+                         ids=["c128_decay_2^-59", "c128_decay_2^-60.4", "c64_decay_2^-59"])
+def test_gated_constant_strong_gate(g, chunk):
+    # a constant gate puts every full chunk's total decay next to 2^-60 (0.7265^128 =
+    # 2^-59.0, 0.7210^128 = 2^-60.4, 0.5276^64 = 2^-59.0): the weights inside a chunk span
+    # 18 decades
+    B, H, N, D, Dv = 1, 2, 600, 64, 64
+    inp = workloads.random_inputs(81, B, H, N, D, Dv, dtype="bf16", gated=True)
+    inp["g"] = torch.full_like(inp["g"], g)
+    _say(f"gated constant {g} chunk {chunk}")
+    o = run_fwd(inp, chunk)
+    o_ref, _, _ = oracle_fwd(inp)
+    assert rowwise_rel_err(to64(o), o_ref) <= TOL["bf16"]
+
+
 # ------------------------------------------------ many heads, few segments ----
 
 @pytest.mark.parametrize("gated", [False, True], ids=["ungated", "gated"])
