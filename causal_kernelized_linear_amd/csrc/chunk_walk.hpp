@@ -346,9 +346,13 @@ struct ChunkWalker {
     // Global -> registers for the chunk starting at token ts.  Rows past `last` are
     // clamped to it (always in bounds: the prefetch behind the walk's last chunk rereads
     // one cached row); stage() zeroes the features of rows past N.
+    // PARTS selects K (1), V (2) or both (3; the split walk divides them between its two
+    // kinds of wave).
+    template <int PARTS = 3>
     __device__ __forceinline__ void load(Regs& R, int ts) const {
 #pragma unroll
         for (int it = 0; it < Sh::KPT; ++it) {
+            if (!(PARTS & 1)) break;
             const int u = tid + it * kThreads;
             const int cg = u % (D / 8), kq = (u / (D / 8)) % (CH / 4);
 #pragma unroll
@@ -359,6 +363,7 @@ struct ChunkWalker {
         }
 #pragma unroll
         for (int it = 0; it < Sh::VPT; ++it) {
+            if (!(PARTS & 2)) break;
             const int u = tid + it * kThreads;
             const int cg = u % (DV / 8), kq = (u / (DV / 8)) % (CH / 4);
 #pragma unroll
@@ -410,12 +415,12 @@ struct ChunkWalker {
 
     // phi(K) -> Fk (row-major) and/or Fk^T (decayed when gated); V -> V^T.  TAIL: the
     // chunk crosses the end of the sequence, so rows past N get zero features.
-    template <bool TAIL>
+    template <bool TAIL, int PARTS = 3>
     __device__ __forceinline__ void stage(const Regs& R, int ts, float lam_last) const {
 #pragma unroll
         for (int it = 0; it < Sh::KPT; ++it) {
             const int u = tid + it * kThreads;
-            if (u < Sh::NKU) {
+            if ((PARTS & 1) && u < Sh::NKU) {
                 const int cg = u % (D / 8), kq = u / (D / 8);
                 E fr[4][8];
 #pragma unroll
@@ -451,7 +456,7 @@ struct ChunkWalker {
 #pragma unroll
         for (int it = 0; it < Sh::VPT; ++it) {
             const int u = tid + it * kThreads;
-            if (u < Sh::NVU) {
+            if ((PARTS & 2) && u < Sh::NVU) {
                 const int cg = u % (DV / 8), kq = u / (DV / 8);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -886,6 +891,65 @@ struct ChunkWalker {
 // Accumulator-layout element r of state tile j of wave w, lane (l16, g4):
 // S[16a + 4 g4 + r][16b + l16] with a = w ZT + j / NB, b = j % NB; z tile i of wave w
 // holds z[16(w ZT + i) + 4 g4 + r] in its l16 == 0 lanes (zero elsewhere).
+// The state in front of segment `seg` of head bh (column part `part`), in the
+// accumulator layout of wave w's tiles: S0 (or zero) plus, with the direct prefix, the
+// totals of the segments in front, decayed; else the scanned slot in front of it.
+template <typename Sh, bool GATED, int DV, int VS>
+__device__ __forceinline__ void segment_prefix(const WalkArgs& args, int bh, int part, int seg, size_t slot0, int w,
+                                               int lane, int l16, int g4, f32x4_t (&sacc)[Sh::TPW],
+                                               f32x4_t (&zacc)[Sh::ZT]) {
+    constexpr int D = Sh::NA * 16, DVF = DV * VS;
+    auto st_at = [&](int s, int j) {
+        return args.st + (slot0 + s) * (D * DV) + ((w * Sh::TPW + j) * kWave + lane) * 4;
+    };
+    auto zt_at = [&](int s, int i) { return args.zt + (slot0 + s) * D + 16 * (w * Sh::ZT + i) + 4 * g4; };
+    auto get4 = [](const float* p) { return *reinterpret_cast<const f32x4_t*>(p); };
+    const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+    if (args.direct || seg == 0) {
+        if (args.s0) {
+            const float* s0b = args.s0 + size_t(bh) * D * DVF + part * DV;
+#pragma unroll
+            for (int j = 0; j < Sh::TPW; ++j) {
+                const int u = w * Sh::TPW + j;
+                const int a = u / Sh::NB, b = u % Sh::NB;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sacc[j][r] = s0b[size_t(16 * a + 4 * g4 + r) * DVF + 16 * b + l16];
+            }
+        }
+        if (args.z0) {
+            const float* z0b = args.z0 + size_t(bh) * D;
+#pragma unroll
+            for (int i = 0; i < Sh::ZT; ++i) {
+                const f32x4_t zv = get4(z0b + 16 * (w * Sh::ZT + i) + 4 * g4);
+                zacc[i] = l16 == 0 ? zv : zero4;
+            }
+        }
+        if (args.direct) {
+            const float* lgb = args.lg + slot0;
+#pragma unroll 2
+            for (int s = 0; s < seg; ++s) {
+                const float f = GATED ? fast_exp2(lgb[s]) : 1.0f;
+#pragma unroll
+                for (int j = 0; j < Sh::TPW; ++j) sacc[j] = f * sacc[j] + get4(st_at(s, j));
+#pragma unroll
+                for (int i = 0; i < Sh::ZT; ++i) {
+                    const f32x4_t zv = get4(zt_at(s, i));
+                    zacc[i] = f * zacc[i] + (l16 == 0 ? zv : zero4);
+                }
+            }
+        }
+    } else {
+        const int pre = seg * args.tparts - 1;     // the scanned slot in front of the segment
+#pragma unroll
+        for (int j = 0; j < Sh::TPW; ++j) sacc[j] = get4(st_at(pre, j));
+#pragma unroll
+        for (int i = 0; i < Sh::ZT; ++i) {
+            const f32x4_t zv = get4(zt_at(pre, i));
+            zacc[i] = l16 == 0 ? zv : zero4;
+        }
+    }
+}
+
 // VS column parts of DV columns each (VS = 1: the whole of Dv = DV).  The workspace
 // slots are per (head, column part): slot (bh * VS + part) * nslots + t holds that
 // part's [D, DV] slice of the state and its own copy of z.
@@ -934,7 +998,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
         return args.st + (slot0 + s) * (D * DV) + ((w * Sh::TPW + j) * kWave + lane) * 4;
     };
     auto zt_at = [&](int s, int i) { return args.zt + (slot0 + s) * D + 16 * (w * Sh::ZT + i) + 4 * g4; };
-    auto get4 = [](const float* p) { return *reinterpret_cast<const f32x4_t*>(p); };
     const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
 
     f32x4_t sacc[Sh::TPW];
@@ -949,49 +1012,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     // slot, formed while the first chunk's loads are in flight.
     auto prologue = [&]() {
         if constexpr (OUTPUT) {
-            if (args.direct || seg == 0) {
-                if (args.s0) {
-                    const float* s0b = args.s0 + size_t(bh) * D * DVF + part * DV;
-#pragma unroll
-                    for (int j = 0; j < Sh::TPW; ++j) {
-                        const int u = w * Sh::TPW + j;
-                        const int a = u / Sh::NB, b = u % Sh::NB;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) sacc[j][r] = s0b[size_t(16 * a + 4 * g4 + r) * DVF + 16 * b + l16];
-                    }
-                }
-                if (args.z0) {
-                    const float* z0b = args.z0 + size_t(bh) * D;
-#pragma unroll
-                    for (int i = 0; i < Sh::ZT; ++i) {
-                        const f32x4_t zv = get4(z0b + 16 * (w * Sh::ZT + i) + 4 * g4);
-                        zacc[i] = l16 == 0 ? zv : zero4;
-                    }
-                }
-                if (args.direct) {
-                    const float* lgb = args.lg + slot0;
-#pragma unroll 2
-                    for (int s = 0; s < seg; ++s) {
-                        const float f = GATED ? fast_exp2(lgb[s]) : 1.0f;
-#pragma unroll
-                        for (int j = 0; j < Sh::TPW; ++j) sacc[j] = f * sacc[j] + get4(st_at(s, j));
-#pragma unroll
-                        for (int i = 0; i < Sh::ZT; ++i) {
-                            const f32x4_t zv = get4(zt_at(s, i));
-                            zacc[i] = f * zacc[i] + (l16 == 0 ? zv : zero4);
-                        }
-                    }
-                }
-            } else {
-                const int pre = seg * args.tparts - 1;     // the scanned slot in front of the segment
-#pragma unroll
-                for (int j = 0; j < Sh::TPW; ++j) sacc[j] = get4(st_at(pre, j));
-#pragma unroll
-                for (int i = 0; i < Sh::ZT; ++i) {
-                    const f32x4_t zv = get4(zt_at(pre, i));
-                    zacc[i] = l16 == 0 ? zv : zero4;
-                }
-            }
+            segment_prefix<Sh, GATED, DV, VS>(args, bh, part, seg, slot0, w, lane, l16, g4, sacc, zacc);
             wk.clear_zb();
             wk.stage_state(sacc, zacc);
         }
@@ -1009,6 +1030,144 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
         for (int i = 0; i < Sh::ZT; ++i)
             if (l16 == 0) *reinterpret_cast<f32x4_t*>(zt_at(slot, i)) = zacc[i];
         if (!OUTPUT && GATED && wk.tid == 0) args.lg[slot0 + slot] = lg_total;
+    }
+}
+
+// The output walk with its work split between two kinds of wave, for the shapes where
+// the 4-wave walk holds one workgroup per CU (D = Dv = 128 bf16, ungated, 64-token
+// chunks): 8 waves, two per SIMD.  Waves 0-3 (output waves) each take one 16-query strip
+// of the chunk: they load Q, apply phi and form the strip's outputs from S^T, phi(K) and
+// V^T in LDS.  Waves 4-7 (state waves) hold the carried state in their accumulators as
+// the 4-wave walk does: they load K and V, stage phi(K) and V^T, fold the chunk into the
+// state and stage S^T and z for the next chunk into the other of two LDS buffers.  Both
+// keep the loads of two chunks in flight.  Per
+// chunk both kinds meet at two barriers, after staging and after the outputs and fold;
+// in between, one SIMD runs an output wave and a state wave side by side, so that the
+// VALU, LDS and MFMA work and the waits of the two overlap.
+constexpr int kSplitThreads = 2 * kThreads;
+
+template <typename E, int D, int DV, int CH>
+struct SplitShape {
+    using W = ChunkWalker<E, D, DV, CH, false, true>;
+    using Sh = typename W::Sh;
+    // a second S^T and split-z buffer after the 4-wave walk's tiles
+    static constexpr size_t kOffSt2 = Sh::kBytes;
+    static constexpr size_t kOffZb2 = kOffSt2 + size_t(DV) * Sh::LS * sizeof(E);
+    static constexpr size_t kBytes = kOffZb2 + size_t(4) * Sh::LZ * sizeof(E);
+    static_assert(Sh::MAXS == 1 && Sh::NSTRIP == 4, "one query strip per output wave");
+    static_assert(kBytes == split_walk_lds_bytes(int(sizeof(E)), D, DV, CH), "host LDS formula out of step");
+};
+
+template <typename E, int D, int DV, int CH>
+__global__ __launch_bounds__(kSplitThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void walk_split_kernel(
+    WalkArgs args) {
+    using SS = SplitShape<E, D, DV, CH>;
+    using W = typename SS::W;
+    using Sh = typename SS::Sh;
+    extern __shared__ __align__(16) unsigned char smem[];
+
+    const int item = blockIdx.x;
+    const int seg = item % args.nseg;
+    const int bh = item / args.nseg;
+    const int N = args.N;
+    const int nchunks_total = (N + CH - 1) / CH;
+    const int c0 = seg * args.L, nch = min(args.L, nchunks_total - c0);
+
+    // the 4-wave walker's members, renumbered within each kind of wave
+    W wk;
+    wk.init(smem, N, reinterpret_cast<const E*>(args.q) + size_t(bh) * N * D,
+            reinterpret_cast<const E*>(args.k) + size_t(bh) * N * D,
+            reinterpret_cast<const E*>(args.v) + size_t(bh) * N * DV, nullptr);
+    const bool state_wave = threadIdx.x >= kThreads;       // uniform over each wave
+    wk.tid = threadIdx.x % kThreads;
+    wk.w = __builtin_amdgcn_readfirstlane(wk.tid / kWave);
+    wk.sO = smem + Sh::kOffO + size_t(wk.w) * Sh::kOBlock;
+    wk.last = min(N, (c0 + max(nch, 1)) * CH) - 1;
+    E* const st_buf[2] = {wk.sSt, reinterpret_cast<E*>(smem + SS::kOffSt2)};
+    E* const zb_buf[2] = {wk.sZb, reinterpret_cast<E*>(smem + SS::kOffZb2)};
+    const int w = wk.w, lane = wk.lane, l16 = wk.l16, g4 = wk.g4;
+
+    OutRsrc ob;
+    ob.init(reinterpret_cast<E*>(args.o) + size_t(bh) * N * DV, unsigned(N) * DV * sizeof(E));
+    const size_t slot0 = size_t(bh) * args.nslots;
+    const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+    const bool keep = seg == args.nseg - 1 && args.want_final;
+
+    // Each kind of wave runs its own loop, so that neither holds the other's registers;
+    // both loops meet at the same two barriers per chunk (nch is uniform over the
+    // workgroup, and the kind of wave is uniform over each wave).
+    if (state_wave) {
+        f32x4_t sacc[Sh::TPW];
+        f32x4_t zacc[Sh::ZT];
+#pragma unroll
+        for (int j = 0; j < Sh::TPW; ++j) sacc[j] = zero4;
+#pragma unroll
+        for (int i = 0; i < Sh::ZT; ++i) zacc[i] = zero4;
+        // two register sets of K and V: the loads of chunk n + 2 are in flight while
+        // chunk n is staged and folded (three would spill)
+        typename W::Regs R0, R1;
+        wk.load(R0, c0 * CH);
+        wk.load(R1, (c0 + 1) * CH);
+        segment_prefix<Sh, false, DV, 1>(args, bh, 0, seg, slot0, w, lane, l16, g4, sacc, zacc);
+        wk.sZb = zb_buf[0];
+        wk.clear_zb();
+        wk.stage_state(sacc, zacc);
+        auto step = [&](typename W::Regs& R, int n) {
+            const int ts = (c0 + n) * CH;
+            if (ts + CH <= N)
+                wk.template stage<false>(R, ts, 0.0f);
+            else
+                wk.template stage<true>(R, ts, 0.0f);
+            wk.load(R, ts + 2 * CH);
+            __syncthreads();
+            const bool more = n + 1 < nch;
+            if (more || keep) wk.fold(sacc, zacc, 0.0f);
+            if (more) {
+                wk.sSt = st_buf[(n + 1) & 1];
+                wk.sZb = zb_buf[(n + 1) & 1];
+                wk.stage_state(sacc, zacc);
+            }
+            __syncthreads();
+        };
+        for (int n = 0; n < nch; n += 2) {
+            step(R0, n);
+            if (n + 1 < nch) step(R1, n + 1);
+        }
+        if (keep) {
+            const size_t slot = slot0 + args.nslots - 1;
+#pragma unroll
+            for (int j = 0; j < Sh::TPW; ++j)
+                *reinterpret_cast<f32x4_t*>(args.st + slot * (D * DV) + ((w * Sh::TPW + j) * kWave + lane) * 4) =
+                    sacc[j];
+#pragma unroll
+            for (int i = 0; i < Sh::ZT; ++i)
+                if (l16 == 0)
+                    *reinterpret_cast<f32x4_t*>(args.zt + slot * D + 16 * (w * Sh::ZT + i) + 4 * g4) = zacc[i];
+        }
+    } else {
+        // two register sets of Q, as for K and V
+        typename W::QRegs q0, q1;
+        wk.load_q(q0, c0 * CH);
+        wk.load_q(q1, (c0 + 1) * CH);
+        wk.sZb = zb_buf[1];
+        wk.clear_zb();
+        auto step = [&](typename W::QRegs& qr, int n) {
+            const int ts = (c0 + n) * CH;
+            F8<E> fq[Sh::MAXS][D / 32];
+            wk.phi_q(qr, fq);
+            wk.load_q(qr, ts + 2 * CH);
+            __syncthreads();
+            wk.sSt = st_buf[n & 1];
+            wk.sZb = zb_buf[n & 1];
+            // the strip with a runtime key-block loop: the per-wave straight-line form
+            // holds more operands than two waves per SIMD leave registers for
+            wk.outputs_seq(fq, ts, ob, args.eps, args.normalize);
+            __syncthreads();
+        };
+        for (int n = 0; n < nch; n += 2) {
+            step(q0, n);
+            if (n + 1 < nch) step(q1, n + 1);
+        }
     }
 }
 

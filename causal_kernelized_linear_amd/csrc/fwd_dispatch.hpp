@@ -30,14 +30,23 @@ hipError_t run_fwd_walks(const FwdLaunch& p) {
     a.direct = prefix_direct(p.nseg, D, DV) ? 1 : 0;
     a.want_final = (p.s_out || p.z_out) ? 1 : 0;
     auto* k_tot = walk_kernel<E, D, DV, CH, GATED, false, IDENT, RELU, VS>;
-    auto* k_out = walk_kernel<E, D, DV, CH, GATED, true, IDENT, RELU, VS>;
+    // the output walk: the split 8-wave walk where its shape has one, else the 4-wave one
+    constexpr bool kSplit = walk_split(int(sizeof(E)), D, DV, CH, GATED) && VS == 1 && !IDENT && !RELU;
+    auto* k_out = [] {
+        if constexpr (kSplit)
+            return walk_split_kernel<E, D, DV, CH>;
+        else
+            return walk_kernel<E, D, DV, CH, GATED, true, IDENT, RELU, VS>;
+    }();
+    constexpr size_t kOutBytes = kSplit ? split_walk_lds_bytes(int(sizeof(E)), D, DV, CH) : ShO::kBytes;
+    constexpr unsigned kOutThreads = kSplit ? kSplitThreads : kThreads;
     static bool attrs_set = false;         // benign race: idempotent attribute set
     if (!attrs_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_tot),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, int(ShT::kBytes));
         if (e != hipSuccess) return e;
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_out), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                int(ShO::kBytes));
+                                int(kOutBytes));
         if (e != hipSuccess) return e;
         attrs_set = true;
     }
@@ -53,7 +62,7 @@ hipError_t run_fwd_walks(const FwdLaunch& p) {
         hipLaunchKernelGGL((scan_kernel<D, DV, GATED, VS>), dim3(vheads * NBLK), dim3(kThreads), 0, p.stream, a.st,
                            a.zt, a.lg, p.s0, p.z0, nslots, nslots - 1);
     mark(2);
-    hipLaunchKernelGGL(k_out, dim3(walk_grid(unsigned(p.BH) * unsigned(p.nseg), VS)), dim3(kThreads), ShO::kBytes,
+    hipLaunchKernelGGL(k_out, dim3(walk_grid(unsigned(p.BH) * unsigned(p.nseg), VS)), dim3(kOutThreads), kOutBytes,
                        p.stream, a);
     if (a.want_final)
         hipLaunchKernelGGL((final_kernel<D, DV, VS>), dim3(vheads * NBLK), dim3(kThreads), 0, p.stream, a.st, a.zt,

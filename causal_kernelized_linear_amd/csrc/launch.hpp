@@ -47,6 +47,17 @@ constexpr size_t walk_lds_bytes(int esize, int D, int Dv, int chunk, bool gated,
 
 constexpr size_t kMaxLds = 160 * 1024;   // LDS per compute unit on gfx950
 
+// Whether the output walk of a shape runs as the split 8-wave walk (walk_split_kernel):
+// bf16, D = Dv = 128, ungated, 64-token chunks, features elu + 1, Dv uncut.
+constexpr bool walk_split(int esize, int D, int Dv, int chunk, bool gated) {
+    return esize == 2 && D == 128 && Dv == 128 && chunk == 64 && !gated;
+}
+
+// Its LDS: the 4-wave output walk's tiles plus a second S^T and split-z buffer.
+constexpr size_t split_walk_lds_bytes(int esize, int D, int Dv, int chunk) {
+    return walk_lds_bytes(esize, D, Dv, chunk, false, true) + size_t(Dv) * D * esize + size_t(4) * (D + 8) * esize;
+}
+
 // Waves per SIMD a walk kernel is compiled for (one wave of every workgroup sits on each
 // SIMD, so this is also its workgroups per compute unit): what its LDS allows, capped by
 // the register budget its shape can live with.  The plan sizes one round of the output
