@@ -395,6 +395,18 @@ def source_digest():
     return h.hexdigest()
 
 
+def output_walk_name(w, chunk):
+    """The output walk kernel of forward workload w at this chunk, as the counter summaries
+    name it: the split 8-wave walk at D = Dv = 128 and chunk 64, the walk over two column
+    parts of 64 where the full tiles exceed the LDS (chunk 256 at D = Dv = 128)."""
+    if w.dtype == "bf16" and w.D == 128 and w.Dv == 128 and w.kind == "fwd":
+        if chunk == 64:
+            return "walk_split_kernel<bf16,128,128,64>"
+        if chunk == 256:
+            return "walk_kernel<bf16,128,64,256,ungated,output,parts2>"
+    return f"walk_kernel<{w.dtype},{w.D},{w.Dv},{chunk},{'gated' if w.kind == 'gated' else 'ungated'},output>"
+
+
 def counters_path(workload, chunk):
     return os.path.join(ROOT, "profiles", f"counters_walk_output_{workload}_c{chunk}.json")
 
@@ -567,8 +579,7 @@ def main():
         rt = time_forward(wt, 128, args.steps, extra_warm, ev)
         line["train"] = {"workload": "train_bf16: B=8 H=16 N=4096 D=Dv=64 bf16, fp32 state, chunk 128",
                          **fwd_leg(wt, 128, rt),
-                         "walk_output_traffic": stored_traffic("walk_kernel<bf16,64,64,128,ungated,output>",
-                                                               wt.name, 128)}
+                         "walk_output_traffic": stored_traffic(output_walk_name(wt, 128), wt.name, 128)}
 
     if "fp32" in legs:
         wf = workloads.WORKLOADS["fp32_small"]
@@ -688,7 +699,7 @@ def main():
         head_sets = None
         units = fwd_units(wl)
         bpu = fwd_bytes_per_unit(wl)
-        dom_name = f"walk_kernel<bf16,{wl.D},{wl.Dv},{chunk},ungated,output>"
+        dom_name = output_walk_name(wl, chunk)
         achieved = bpu * units / (r["walk_output_ms_alone"] * 1e-3) / 1e9
         line.update({
             "value": wl.B * wl.N / (r["ms_per_step"] * 1e-3),
