@@ -36,6 +36,16 @@
 // scale by 1/d in fp32 (dNum V^T = diag(1/d) dOut V^T).  With the normaliser, dFq_i is
 // orthogonal to Fq_i (its terms cancel), and a rounded dnum breaks that cancellation
 // where d is small.
+//
+// Precision (bf16 where the LDS holds the extra tiles, BwdShape::kSplit).  Operands that
+// are not exact bf16 inputs go to the MFMA products as two bf16 parts, x = hi + lo with
+// hi = bf16(x), lo = bf16(x - hi), and a product takes hi hi + lo hi + hi lo: the
+// features phi(Q), phi(K) in every product, the staged state (S in the dq pass, R in the
+// dk/dv pass), the scaled rows of the state steps, and A and B where the denominators
+// can be small (the sequence's first chunk; every chunk when gated).  The totals walk
+// that gives the states in front of the runs splits phi(K) the same way.  Rounded once,
+// each of these alone leaves a gradient row error of 5e-3 to 8e-3 at 4096 tokens (a CPU
+// model of the passes), which add up to 1.2e-2; split, dq and dk come to about 4e-3.
 //   bwd_dg_kernel   d log g_l for token l of chunk c as four sums that never leave the
 //                   chunk: the pairs inside it (X_l, from fp32 row and column sums of P
 //                   in the dq pass), keys in front of it against its queries i >= l
@@ -122,7 +132,13 @@ struct BwdShape {
     static constexpr size_t kOffCol = kOffInv + size_t(C) * 4;     // [4][C] per-wave column sums of P
     static constexpr size_t kOffRow = kOffCol + size_t(4) * C * 4;  // [C] row sums of P
     static constexpr size_t kOffZ = kOffRow + size_t(C) * 4;
-    static constexpr size_t kBytes = kOffZ + size_t(D) * 4;
+    // bf16 where the LDS allows (bwd_split): the low parts of phi(Q), phi(K) and of the
+    // staged state, each operand x going to the products as bf16(x) and bf16(x - bf16(x))
+    static constexpr bool kSplit = bwd_split(int(sizeof(E)), D, DV);
+    static constexpr size_t kOffQlo = kOffZ + size_t(D) * 4;
+    static constexpr size_t kOffKlo = kOffQlo + (kSplit ? size_t(C) * LQ * sizeof(E) : 0);
+    static constexpr size_t kOffSlo = kOffKlo + (kSplit ? size_t(C) * LQ * sizeof(E) : 0);
+    static constexpr size_t kBytes = kOffSlo + (kSplit ? size_t(D) * LV * sizeof(E) : 0);
     static_assert(kBytes == bwd_lds_bytes(int(sizeof(E)), D, DV), "host LDS formula out of step");
     static_assert(PAD >= 2, "the pad group carries two extra columns");
     // An extra 16-column operand block at column Dv reads the pad group and then, past it,
@@ -254,6 +270,14 @@ __device__ __forceinline__ F4<E> pack4(const f32x4_t& c) {
     return f;
 }
 
+template <typename E>
+__device__ __forceinline__ f32x4_t unpack4(const F4<E>& f) {
+    f32x4_t c;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) c[r] = Elem<E>::to_f32(f.x[r]);
+    return c;
+}
+
 // A 16-byte pad group holding x split as (high, low) in operand precision, then zeros.
 template <typename E>
 __device__ __forceinline__ f32x4_t split_pad(float x) {
@@ -287,6 +311,9 @@ struct BwdChunk {
     E* sV;
     E* sDn;
     E* sS;
+    E* sQlo;       // split operands (Sh::kSplit): low parts of phi(Q), phi(K) and the state
+    E* sKlo;
+    E* sSlo;
     float* sLam;
     float* sDd;
     float* sInv;
@@ -302,6 +329,9 @@ struct BwdChunk {
         sV = reinterpret_cast<E*>(smem + Sh::kOffV);
         sDn = reinterpret_cast<E*>(smem + Sh::kOffDn);
         sS = reinterpret_cast<E*>(smem + Sh::kOffS);
+        sQlo = reinterpret_cast<E*>(smem + Sh::kOffQlo);
+        sKlo = reinterpret_cast<E*>(smem + Sh::kOffKlo);
+        sSlo = reinterpret_cast<E*>(smem + Sh::kOffSlo);
         sLam = reinterpret_cast<float*>(smem + Sh::kOffLam);
         sDd = reinterpret_cast<float*>(smem + Sh::kOffDd);
         sInv = reinterpret_cast<float*>(smem + Sh::kOffInv);
@@ -357,28 +387,48 @@ struct BwdChunk {
     }
 
     // ... into a row-major tile through phi (or as they are) in fp32; rows past the
-    // chunk's end become zero.
-    template <int W, bool PHI>
-    __device__ __forceinline__ void store_rows(E* tile, int ld, const f32x4_t (&r)[kRowUnits<W>]) const {
+    // chunk's end become zero.  LO (bf16 phi only): the low parts phi - bf16(phi) into
+    // `lo`, laid out like the tile.
+    template <int W, bool PHI, bool LO = false>
+    __device__ __forceinline__ void store_rows(E* tile, int ld, const f32x4_t (&r)[kRowUnits<W>], E* lo = nullptr) const {
+        static_assert(!LO || (PHI && sizeof(E) == 2), "low parts: bf16 features only");
         constexpr int G = W * int(sizeof(E)) / 16;
 #pragma unroll
         for (int u = 0; u < kRowUnits<W>; ++u) {
             const int idx = tid + u * kThreads, row = idx / G, col = (idx % G) * EPG;
-            f32x4_t out = {0.f, 0.f, 0.f, 0.f};
+            f32x4_t out = {0.f, 0.f, 0.f, 0.f}, out_lo = {0.f, 0.f, 0.f, 0.f};
             if (row < nrows) {
                 if constexpr (sizeof(E) == 2) {
                     const F8<E> in = __builtin_bit_cast(F8<E>, r[u]);
-                    F8<E> o;
+                    F8<E> o, ol;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) o.x[e] = PHI ? X::from_f32(phi(X::to_f32(in.x[e]))) : in.x[e];
+                    for (int e = 0; e < 8; ++e) {
+                        if constexpr (PHI) {
+                            const float f = phi(X::to_f32(in.x[e]));
+                            o.x[e] = X::from_f32(f);
+                            if constexpr (LO) ol.x[e] = X::from_f32(f - X::to_f32(o.x[e]));
+                        } else {
+                            o.x[e] = in.x[e];
+                        }
+                    }
                     out = __builtin_bit_cast(f32x4_t, o);
+                    if constexpr (LO) out_lo = __builtin_bit_cast(f32x4_t, ol);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) out[e] = PHI ? phi(r[u][e]) : r[u][e];
                 }
             }
             *reinterpret_cast<f32x4_t*>(tile + row * ld + col) = out;
+            if constexpr (LO) *reinterpret_cast<f32x4_t*>(lo + row * ld + col) = out_lo;
         }
+    }
+
+    // Four consecutive staged features (element offset `at` of a phi tile), with their low
+    // parts added back where the operands are split.
+    __device__ __forceinline__ f32x4_t feat4(const E* hi, const E* lo, int at) const {
+        f32x4_t f = unpack4(lds_f4(hi + at));
+        if constexpr (Sh::kSplit) f += unpack4(lds_f4(lo + at));
+        return f;
     }
 
     // The pad group of row `row` of a tile with `ld` = width + PAD.
@@ -394,7 +444,8 @@ struct BwdChunk {
         for (int u = 0; u < kStateUnits; ++u) r[u] = *reinterpret_cast<const f32x4_t*>(slot + 4 * (tid + u * kThreads));
     }
 
-    // ... into sS (row-major [D][Dv], operand precision).
+    // ... into sS (row-major [D][Dv], operand precision); split (Sh::kSplit), the low
+    // parts into sSlo.
     __device__ __forceinline__ void store_slot(const f32x4_t (&r)[kStateUnits]) const {
 #pragma unroll
         for (int u = 0; u < kStateUnits; ++u) {
@@ -403,7 +454,11 @@ struct BwdChunk {
             const int a = t / (DV / 16), b = t % (DV / 16);
             const int d = 16 * a + 4 * (ln >> 4), e = 16 * b + (ln & 15);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) sS[(d + k) * LV + e] = X::from_f32(r[u][k]);
+            for (int k = 0; k < 4; ++k) {
+                const E h = X::from_f32(r[u][k]);
+                sS[(d + k) * LV + e] = h;
+                if constexpr (Sh::kSplit) sSlo[(d + k) * LV + e] = X::from_f32(r[u][k] - X::to_f32(h));
+            }
         }
     }
 
@@ -448,8 +503,8 @@ struct BwdChunk {
 
     // One 16x16 state tile, contraction over the chunk's rows: lhs^T rhs for the tile's
     // rows a and columns b of two row-major tiles (this lane's accumulator piece).
-    __device__ __forceinline__ f32x4_t tile_tn(const E* lhs, int ldl, int a, const E* rhs, int ldr, int b) const {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    __device__ __forceinline__ f32x4_t tile_tn(const E* lhs, int ldl, int a, const E* rhs, int ldr, int b,
+                                               f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f}) const {
 #pragma unroll
         for (int ks = 0; ks < C / 32; ++ks)
             acc = mma(frag_col(lhs, ldl, 32 * ks + 8 * g4, 16 * a, l16), frag_col(rhs, ldr, 32 * ks + 8 * g4, 16 * b, l16),
@@ -457,12 +512,36 @@ struct BwdChunk {
         return acc;
     }
 
+    // The state steps' products with split operands (Sh::kSplit): lhs^T rhs with the
+    // low parts lhs_lo of lhs and, unless null, rhs_lo of rhs (hi hi + lo hi + hi lo).
+    // rhs_lo has no pad group: for the extra column block (b = DV / 16) it is skipped.
+    __device__ __forceinline__ f32x4_t tile_tn_split(const E* lhs, const E* lhs_lo, int ldl, int a, const E* rhs,
+                                                     const E* rhs_lo, int ldr, int b) const {
+        if constexpr (!Sh::kSplit) {
+            return tile_tn(lhs, ldl, a, rhs, ldr, b);
+        } else {
+            const bool rlo = rhs_lo != nullptr && b < DV / 16;
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < C / 32; ++ks) {
+                const int k0 = 32 * ks + 8 * g4;
+                const F8<E> l = frag_col(lhs, ldl, k0, 16 * a, l16), r = frag_col(rhs, ldr, k0, 16 * b, l16);
+                acc = mma(l, r, acc);
+                acc = mma(frag_col(lhs_lo, ldl, k0, 16 * a, l16), r, acc);
+                if (rlo) acc = mma(l, frag_col(rhs_lo, ldr, k0, 16 * b, l16), acc);
+            }
+            return acc;
+        }
+    }
+
     // Rows of dOut scaled by 2^Lambda_i / d_i and their pad groups set to the split
     // 2^Lambda_i dden_i (sDd holds dden_i, times 2^Lambda_i if DD_DECAYED), for the
     // chunk's adjoint total; with V, rows scaled by 2^(Lambda_last - Lambda_j) and the pad
     // to the split factor, for the state step.
+    // Split (Sh::kSplit): the low parts of the scaled dOut rows go to dn_lo and those of
+    // the scaled V rows (gated, WITH_V) to v_lo, both laid out like sDn (no pad group).
     template <bool WITH_V, bool DD_DECAYED>
-    __device__ __forceinline__ void scale_rows() const {
+    __device__ __forceinline__ void scale_rows(E* dn_lo = nullptr, E* v_lo = nullptr) const {
         constexpr int G = DV * int(sizeof(E)) / 16 + 1;    // groups per row, pad included
         const float lam_last = lam(C - 1);
         for (int idx = tid; idx < C * G; idx += kThreads) {
@@ -470,7 +549,10 @@ struct BwdChunk {
             const float fl = GATED ? fast_exp2(lam(row)) : 1.0f;
             if (gi < G - 1) {
                 f32x4_t* p = reinterpret_cast<f32x4_t*>(sDn + row * LV + gi * EPG);
-                *p = scale16(*p, fl * sInv[row]);
+                if constexpr (Sh::kSplit)
+                    *p = scale16(*p, fl * sInv[row], reinterpret_cast<f32x4_t*>(dn_lo + row * LV + gi * EPG));
+                else
+                    *p = scale16(*p, fl * sInv[row]);
             } else {
                 *pad_of(sDn, LV, DV, row) = split_pad<E>(DD_DECAYED ? sDd[row] : sDd[row] * fl);
             }
@@ -478,7 +560,10 @@ struct BwdChunk {
                 const float fv = fast_exp2(fminf(lam_last - lam(row), 0.0f));
                 if (gi < G - 1) {
                     f32x4_t* p = reinterpret_cast<f32x4_t*>(sV + row * LV + gi * EPG);
-                    *p = scale16(*p, fv);
+                    if constexpr (Sh::kSplit)
+                        *p = scale16(*p, fv, reinterpret_cast<f32x4_t*>(v_lo + row * LV + gi * EPG));
+                    else
+                        *p = scale16(*p, fv);
                 } else {
                     *pad_of(sV, LV, DV, row) = split_pad<E>(row < nrows ? fv : 0.0f);
                 }
@@ -486,11 +571,18 @@ struct BwdChunk {
         }
     }
 
-    static __device__ __forceinline__ f32x4_t scale16(f32x4_t v, float f) {
+    // 16 bytes of elements times f, rounded to the operand type; with lo (bf16), the
+    // rounding's remainder bf16(x f - bf16(x f)) goes there.
+    static __device__ __forceinline__ f32x4_t scale16(f32x4_t v, float f, f32x4_t* lo = nullptr) {
         if constexpr (sizeof(E) == 2) {
-            F8<E> x = __builtin_bit_cast(F8<E>, v);
+            F8<E> x = __builtin_bit_cast(F8<E>, v), xl;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x.x[e] = X::from_f32(X::to_f32(x.x[e]) * f);
+            for (int e = 0; e < 8; ++e) {
+                const float y = X::to_f32(x.x[e]) * f;
+                x.x[e] = X::from_f32(y);
+                xl.x[e] = X::from_f32(y - X::to_f32(x.x[e]));
+            }
+            if (lo != nullptr) *lo = __builtin_bit_cast(f32x4_t, xl);
             return __builtin_bit_cast(f32x4_t, x);
         } else {
 #pragma unroll
@@ -543,6 +635,7 @@ void bwd_dq_kernel(BwdArgs args) {
     using X = Elem<E>;
     constexpr int C = B::C, LQ = B::LQ, LV = B::LV, KZ = B::KZ;
     constexpr int ND = D / 16, NE = DV / 16, NJ = C / 16;
+    constexpr bool kSplit = B::Sh::kSplit;
     extern __shared__ __align__(16) unsigned char smem[];
     B ck;
     ck.init(smem, args.N, args.NC, args.LC);
@@ -595,8 +688,8 @@ void bwd_dq_kernel(BwdArgs args) {
     ck.set_chunk(c);
     const int ts = ck.ts;
     if constexpr (!B::Sh::kAhead) issue(c);
-    ck.template store_rows<D, true>(ck.sQ, LQ, sq);
-    ck.template store_rows<D, true>(ck.sK, LQ, sk);
+    ck.template store_rows<D, true, kSplit>(ck.sQ, LQ, sq, ck.sQlo);
+    ck.template store_rows<D, true, kSplit>(ck.sK, LQ, sk, ck.sKlo);
     ck.template store_rows<DV, false>(ck.sV, LV, sv);
     ck.template store_rows<DV, false>(ck.sDn, LV, so);
     ck.store_slot(sacc);
@@ -625,16 +718,29 @@ void bwd_dq_kernel(BwdArgs args) {
     // A, transposed: lane (l16, g4) holds query il against keys 16 jt + 4 g4 + r.  sc keeps
     // the undecayed fp32 scores for the pair sums of d log g.
     f32x4_t sc[NJ];
-    F4<E> pa[NJ];
+    F4<E> pa[NJ], pa_lo[NJ];
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt) sc[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
         const F8<E> bq = frag_row(ck.sQ, LQ, il, 32 * ks + 8 * g4);
+        F8<E> bql;
+        if constexpr (kSplit) bql = frag_row(ck.sQlo, LQ, il, 32 * ks + 8 * g4);
 #pragma unroll
         for (int jt = 0; jt < NJ; ++jt)
-            if (jt <= w) sc[jt] = mma(frag_row(ck.sK, LQ, 16 * jt + l16, 32 * ks + 8 * g4), bq, sc[jt]);
+            if (jt <= w) {
+                const F8<E> kf = frag_row(ck.sK, LQ, 16 * jt + l16, 32 * ks + 8 * g4);
+                sc[jt] = mma(kf, bq, sc[jt]);
+                if constexpr (kSplit) {
+                    sc[jt] = mma(kf, bql, sc[jt]);
+                    sc[jt] = mma(frag_row(ck.sKlo, LQ, 16 * jt + l16, 32 * ks + 8 * g4), bq, sc[jt]);
+                }
+            }
     }
+    // where the denominators can be small (the sequence's first chunk, with no state in
+    // front; every chunk when gated, whose decay keeps the state short) the products also
+    // take the low parts of A and B
+    const bool first = kSplit && (GATED || c == 0);
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt) {
         const f32x4_t lj = ck.lam4(16 * jt + 4 * g4);
@@ -646,6 +752,7 @@ void bwd_dq_kernel(BwdArgs args) {
             if constexpr (GATED) x[r] *= fast_exp2(fminf(lam_i - lj[r], 0.0f));
         }
         pa[jt] = pack4<E>(x);
+        if constexpr (kSplit) pa_lo[jt] = pack4<E>(x - unpack4(pa[jt]));
     }
 
     // num^T[e][i] = 2^Lambda_i (S^T Fq^T)[e][i] + (V^T A^T)[e][i], with one extra block of
@@ -656,8 +763,19 @@ void bwd_dq_kernel(BwdArgs args) {
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
         const F8<E> bq = frag_row(ck.sQ, LQ, il, 32 * ks + 8 * g4);
+        F8<E> bql;
+        if constexpr (kSplit) bql = frag_row(ck.sQlo, LQ, il, 32 * ks + 8 * g4);
 #pragma unroll
-        for (int et = 0; et <= NE; ++et) nt[et] = mma(frag_col(ck.sS, LV, 32 * ks + 8 * g4, 16 * et, l16), bq, nt[et]);
+        for (int et = 0; et <= NE; ++et) {
+            const F8<E> sf = frag_col(ck.sS, LV, 32 * ks + 8 * g4, 16 * et, l16);
+            nt[et] = mma(sf, bq, nt[et]);
+            if constexpr (kSplit) {
+                // S Fq_lo (z's split pad included) and S_lo Fq (S_lo has no pad group:
+                // the extra block skips it)
+                nt[et] = mma(sf, bql, nt[et]);
+                if (et < NE) nt[et] = mma(frag_col(ck.sSlo, LV, 32 * ks + 8 * g4, 16 * et, l16), bq, nt[et]);
+            }
+        }
     }
     if constexpr (GATED) {
 #pragma unroll
@@ -669,8 +787,13 @@ void bwd_dq_kernel(BwdArgs args) {
     for (int jt = 0; jt < NJ; ++jt)
         if (jt <= w) {
 #pragma unroll
-            for (int et = 0; et <= NE; ++et)
-                nt[et] = mma4(frag4_col(ck.sV, LV, 16 * jt + 4 * g4, 16 * et, l16), pa[jt], nt[et]);
+            for (int et = 0; et <= NE; ++et) {
+                const F4<E> vf = frag4_col(ck.sV, LV, 16 * jt + 4 * g4, 16 * et, l16);
+                nt[et] = mma4(vf, pa[jt], nt[et]);
+                if constexpr (kSplit) {
+                    if (first) nt[et] = mma4(vf, pa_lo[jt], nt[et]);
+                }
+            }
         }
 
     // den (in lanes g4 = 0: rows Dv and Dv + 1 of the extra block), 1/d and
@@ -700,7 +823,7 @@ void bwd_dq_kernel(BwdArgs args) {
 
     // B, transposed like A: ((dout_i . v_j) / d_i + dden_i) decayed and masked; with it the
     // pair terms P_ij = (Fq_i . Fk_j) B_ij in fp32, summed by row (j < i) and by column
-    F4<E> pb[NJ];
+    F4<E> pb[NJ], pb_lo[NJ];
     float prow = 0.0f;
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt) {
@@ -725,6 +848,7 @@ void bwd_dq_kernel(BwdArgs args) {
             }
         }
         pb[jt] = pack4<E>(x);
+        if constexpr (kSplit) pb_lo[jt] = pack4<E>(x - unpack4(pb[jt]));
         if constexpr (GATED) {
             if (l16 == 0) *reinterpret_cast<f32x4_t*>(ck.sCol + w * C + 16 * jt + 4 * g4) = pc;
         }
@@ -740,9 +864,11 @@ void bwd_dq_kernel(BwdArgs args) {
     for (int dt = 0; dt < ND; ++dt) {
         ft[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < DV / 32; ++ks)
-            ft[dt] = mma(frag_row(ck.sS, LV, 16 * dt + l16, 32 * ks + 8 * g4), frag_row(ck.sDn, LV, il, 32 * ks + 8 * g4),
-                         ft[dt]);
+        for (int ks = 0; ks < DV / 32; ++ks) {
+            const F8<E> bo = frag_row(ck.sDn, LV, il, 32 * ks + 8 * g4);
+            ft[dt] = mma(frag_row(ck.sS, LV, 16 * dt + l16, 32 * ks + 8 * g4), bo, ft[dt]);
+            if constexpr (kSplit) ft[dt] = mma(frag_row(ck.sSlo, LV, 16 * dt + l16, 32 * ks + 8 * g4), bo, ft[dt]);
+        }
     }
     {
         float yq = 0.0f;                              // Fq_i . (carried-state part of dFq_i)
@@ -765,17 +891,23 @@ void bwd_dq_kernel(BwdArgs args) {
     for (int jt = 0; jt < NJ; ++jt)
         if (jt <= w) {
 #pragma unroll
-            for (int dt = 0; dt < ND; ++dt)
-                ft[dt] = mma4(frag4_col(ck.sK, LQ, 16 * jt + 4 * g4, 16 * dt, l16), pb[jt], ft[dt]);
+            for (int dt = 0; dt < ND; ++dt) {
+                const F4<E> kf = frag4_col(ck.sK, LQ, 16 * jt + 4 * g4, 16 * dt, l16);
+                ft[dt] = mma4(kf, pb[jt], ft[dt]);
+                if constexpr (kSplit) {
+                    ft[dt] = mma4(frag4_col(ck.sKlo, LQ, 16 * jt + 4 * g4, 16 * dt, l16), pb[jt], ft[dt]);
+                    if (first) ft[dt] = mma4(kf, pb_lo[jt], ft[dt]);
+                }
+            }
         }
     // dq = dFq * phi'(q): four consecutive columns of row il per lane
     if (ts + il < N) {
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) {
-            const F4<E> q4 = lds_f4(ck.sQ + il * LQ + 16 * dt + 4 * g4);
+            const f32x4_t f4 = ck.feat4(ck.sQ, ck.sQlo, il * LQ + 16 * dt + 4 * g4);
             f32x4_t o;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) o[r] = ft[dt][r] * dphi_of(X::to_f32(q4.x[r]));
+            for (int r = 0; r < 4; ++r) o[r] = ft[dt][r] * dphi_of(f4[r]);
             store4<E>(dqb + size_t(ts + il) * D + 16 * dt + 4 * g4, o);
         }
     }
@@ -788,8 +920,11 @@ void bwd_dq_kernel(BwdArgs args) {
         if (lane < ck.nrows) args.xs[size_t(bh) * N + ts + lane] = x - dm;
     }
     // rows of dOut become 2^Lambda_i dnum_i (pad: 2^Lambda_i dden_i split), rows of V
-    // 2^(Lambda_last - Lambda_j) v_j (pad: the factor split, for z's step)
-    ck.template scale_rows<true, true>();
+    // 2^(Lambda_last - Lambda_j) v_j (pad: the factor split, for z's step).  Split: their
+    // low parts go where the state's tiles were (read for the last time above).
+    E* const dn_lo = kSplit ? ck.sSlo : nullptr;
+    E* const v_lo = kSplit && GATED ? ck.sS : nullptr;
+    ck.template scale_rows<true, true>(dn_lo, v_lo);
     __syncthreads();
     // The chunk's adjoint total dR_c = Fq^T (2^Lambda dNum), dr_c = Fq^T (2^Lambda dden),
     // into the run's with the decay 2^logp from the run's start; and the state carried
@@ -801,8 +936,8 @@ void bwd_dq_kernel(BwdArgs args) {
 #pragma unroll
         for (int u = 0; u < B::kStateUnits; ++u) {
             const int t = w + 4 * u, a = t / NE, b = t % NE;
-            const f32x4_t dr = ck.tile_tn(ck.sQ, LQ, a, ck.sDn, LV, b);
-            const f32x4_t ds = ck.tile_tn(ck.sK, LQ, a, ck.sV, LV, b);
+            const f32x4_t dr = ck.tile_tn_split(ck.sQ, ck.sQlo, LQ, a, ck.sDn, dn_lo, LV, b);
+            const f32x4_t ds = ck.tile_tn_split(ck.sK, ck.sKlo, LQ, a, ck.sV, v_lo, LV, b);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 racc[u][k] += fp * dr[k];
@@ -811,8 +946,8 @@ void bwd_dq_kernel(BwdArgs args) {
         }
 #pragma unroll
         for (int t = 0; t < KZ; ++t) {
-            const f32x4_t dr = ck.tile_tn(ck.sQ, LQ, w + 4 * t, ck.sDn, LV, NE);
-            const f32x4_t ds = ck.tile_tn(ck.sK, LQ, w + 4 * t, ck.sV, LV, NE);
+            const f32x4_t dr = ck.tile_tn_split(ck.sQ, ck.sQlo, LQ, w + 4 * t, ck.sDn, nullptr, LV, NE);
+            const f32x4_t ds = ck.tile_tn_split(ck.sK, ck.sKlo, LQ, w + 4 * t, ck.sV, nullptr, LV, NE);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 rzv[t][r] += fp * pair01(dr[r]);
@@ -841,6 +976,7 @@ void bwd_dkv_kernel(BwdArgs args) {
     using X = Elem<E>;
     constexpr int C = B::C, LQ = B::LQ, LV = B::LV, KZ = B::KZ;
     constexpr int ND = D / 16, NE = DV / 16, NI = C / 16;
+    constexpr bool kSplit = B::Sh::kSplit;
     extern __shared__ __align__(16) unsigned char smem[];
     B ck;
     ck.init(smem, args.N, args.NC, args.LC);
@@ -925,8 +1061,8 @@ void bwd_dkv_kernel(BwdArgs args) {
     ck.set_chunk(c);
     const int ts = ck.ts;
     if constexpr (!B::Sh::kAhead) issue(c);
-    ck.template store_rows<D, true>(ck.sQ, LQ, sq);
-    ck.template store_rows<D, true>(ck.sK, LQ, sk);
+    ck.template store_rows<D, true, kSplit>(ck.sQ, LQ, sq, ck.sQlo);
+    ck.template store_rows<D, true, kSplit>(ck.sK, LQ, sk, ck.sKlo);
     ck.template store_rows<DV, false>(ck.sV, LV, sv);
     ck.template store_rows<DV, false>(ck.sDn, LV, so);
     if (ck.tid < C) {
@@ -956,6 +1092,8 @@ void bwd_dkv_kernel(BwdArgs args) {
     //   pa = (Fq_i . Fk_j) 2^(Lambda_i - Lambda_j) / d_i,  pb = ((dout_i . v_j) / d_i + dden_i) 2^(...)
     // Each is consumed (and dv stored) before the other is formed, to keep registers low.
     const bool valid = ts + jl < N;
+    // the low parts of B where the dq pass takes them
+    const bool first = kSplit && (GATED || c == 0);
     {
         F4<E> pa[NI];
 #pragma unroll
@@ -985,9 +1123,11 @@ void bwd_dkv_kernel(BwdArgs args) {
         for (int et = 0; et < NE; ++et) {
             dvt[et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < D / 32; ++ks)
-                dvt[et] = mma(frag_col(ck.sS, LV, 32 * ks + 8 * g4, 16 * et, l16), frag_row(ck.sK, LQ, jl, 32 * ks + 8 * g4),
-                              dvt[et]);
+            for (int ks = 0; ks < D / 32; ++ks) {
+                const F8<E> bk = frag_row(ck.sK, LQ, jl, 32 * ks + 8 * g4);
+                dvt[et] = mma(frag_col(ck.sS, LV, 32 * ks + 8 * g4, 16 * et, l16), bk, dvt[et]);
+                if constexpr (kSplit) dvt[et] = mma(frag_col(ck.sSlo, LV, 32 * ks + 8 * g4, 16 * et, l16), bk, dvt[et]);
+            }
             if constexpr (GATED) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) dvt[et][r] *= tail;
@@ -1006,7 +1146,7 @@ void bwd_dkv_kernel(BwdArgs args) {
             for (int et = 0; et < NE; ++et) store4<E>(dvb + size_t(ts + jl) * DV + 16 * et + 4 * g4, dvt[et]);
         }
     }
-    F4<E> pb[NI];
+    F4<E> pb[NI], pb_lo[NI];
 #pragma unroll
     for (int it = 0; it < NI; ++it) {
         f32x4_t bt = {0.f, 0.f, 0.f, 0.f};
@@ -1028,6 +1168,7 @@ void bwd_dkv_kernel(BwdArgs args) {
             xb[r] = keep ? (bt[r] * iv[r] + d4[r]) * f : 0.0f;
         }
         pb[it] = pack4<E>(xb);
+        if constexpr (kSplit) pb_lo[it] = pack4<E>(xb - unpack4(pb[it]));
     }
 
     // dFk^T[d][j] = 2^(Lambda_last - Lambda_j) ((R V^T)[d][j] + r_d) + (Fq^T B)[d][j]
@@ -1038,9 +1179,11 @@ void bwd_dkv_kernel(BwdArgs args) {
         for (int dt = 0; dt < ND; ++dt) {
             fk[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < DV / 32; ++ks)
-                fk[dt] = mma(frag_row(ck.sS, LV, 16 * dt + l16, 32 * ks + 8 * g4), frag_row(ck.sV, LV, jl, 32 * ks + 8 * g4),
-                             fk[dt]);
+            for (int ks = 0; ks < DV / 32; ++ks) {
+                const F8<E> bv = frag_row(ck.sV, LV, jl, 32 * ks + 8 * g4);
+                fk[dt] = mma(frag_row(ck.sS, LV, 16 * dt + l16, 32 * ks + 8 * g4), bv, fk[dt]);
+                if constexpr (kSplit) fk[dt] = mma(frag_row(ck.sSlo, LV, 16 * dt + l16, 32 * ks + 8 * g4), bv, fk[dt]);
+            }
             const f32x4_t r4 = *reinterpret_cast<const f32x4_t*>(ck.sZ + 16 * dt + 4 * g4);
             const F4<E> k4 = lds_f4(ck.sK + jl * LQ + 16 * dt + 4 * g4);
 #pragma unroll
@@ -1060,17 +1203,23 @@ void bwd_dkv_kernel(BwdArgs args) {
     for (int it = 0; it < NI; ++it)
         if (it >= w) {
 #pragma unroll
-            for (int dt = 0; dt < ND; ++dt)
-                fk[dt] = mma4(frag4_col(ck.sQ, LQ, 16 * it + 4 * g4, 16 * dt, l16), pb[it], fk[dt]);
+            for (int dt = 0; dt < ND; ++dt) {
+                const F4<E> qf = frag4_col(ck.sQ, LQ, 16 * it + 4 * g4, 16 * dt, l16);
+                fk[dt] = mma4(qf, pb[it], fk[dt]);
+                if constexpr (kSplit) {
+                    fk[dt] = mma4(frag4_col(ck.sQlo, LQ, 16 * it + 4 * g4, 16 * dt, l16), pb[it], fk[dt]);
+                    if (first) fk[dt] = mma4(qf, pb_lo[it], fk[dt]);
+                }
+            }
         }
     // dk = dFk * phi'(k): four consecutive columns of row jl per lane
     if (valid) {
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) {
-            const F4<E> k4 = lds_f4(ck.sK + jl * LQ + 16 * dt + 4 * g4);
+            const f32x4_t f4 = ck.feat4(ck.sK, ck.sKlo, jl * LQ + 16 * dt + 4 * g4);
             f32x4_t o;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) o[r] = fk[dt][r] * dphi_of(X::to_f32(k4.x[r]));
+            for (int r = 0; r < 4; ++r) o[r] = fk[dt][r] * dphi_of(f4[r]);
             store4<E>(dkb + size_t(ts + jl) * D + 16 * dt + 4 * g4, o);
         }
     }
@@ -1081,8 +1230,10 @@ void bwd_dkv_kernel(BwdArgs args) {
         if (ck.tid == 0) args.wc[size_t(bh) * NC + c] = wcv;
         tb = wcv + ck.sRow[0];
     }
-    // rows of dOut become 2^Lambda_i dnum_i (pad: 2^Lambda_i dden_i split)
-    ck.template scale_rows<false, false>();
+    // rows of dOut become 2^Lambda_i dnum_i (pad: 2^Lambda_i dden_i split); split, their
+    // low parts go where R's were (read for the last time above)
+    E* const dn_lo = kSplit ? ck.sSlo : nullptr;
+    ck.template scale_rows<false, false>(dn_lo);
     __syncthreads();
     // the adjoint carried across the chunk: R <- 2^Lambda_last R + Fq^T (2^Lambda dNum),
     // r <- 2^Lambda_last r + Fq^T (2^Lambda dden) (the extra column block)
@@ -1091,13 +1242,13 @@ void bwd_dkv_kernel(BwdArgs args) {
 #pragma unroll
         for (int u = 0; u < B::kStateUnits; ++u) {
             const int t = w + 4 * u, a = t / NE, b = t % NE;
-            const f32x4_t dr = ck.tile_tn(ck.sQ, LQ, a, ck.sDn, LV, b);
+            const f32x4_t dr = ck.tile_tn_split(ck.sQ, ck.sQlo, LQ, a, ck.sDn, dn_lo, LV, b);
 #pragma unroll
             for (int k = 0; k < 4; ++k) racc[u][k] = fc * racc[u][k] + dr[k];
         }
 #pragma unroll
         for (int t = 0; t < KZ; ++t) {
-            const f32x4_t dr = ck.tile_tn(ck.sQ, LQ, w + 4 * t, ck.sDn, LV, NE);
+            const f32x4_t dr = ck.tile_tn_split(ck.sQ, ck.sQlo, LQ, w + 4 * t, ck.sDn, nullptr, LV, NE);
 #pragma unroll
             for (int r = 0; r < 4; ++r) rzv[t][r] = fc * rzv[t][r] + pair01(dr[r]);
         }

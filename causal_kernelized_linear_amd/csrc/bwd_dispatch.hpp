@@ -25,12 +25,15 @@ hipError_t run_bwd(const BwdLaunch& p) {
         const int NC = (p.N + C - 1) / C;
         const BwdLayout lay = bwd_workspace_layout(size_t(p.BH), p.N, D, DV);
         char* ws = static_cast<char*>(p.ws);
-        auto* k_tot = walk_kernel<E, D, DV, C, GATED, false>;
+        // the totals walk with the features split like the gradient passes' operands
+        constexpr bool kSplitK = Sh::kSplit;
+        constexpr size_t kTotBytes = ShT::kBytes + (kSplitK ? size_t(D) * ShT::LKT * sizeof(E) : 0);
+        auto* k_tot = walk_kernel<E, D, DV, C, GATED, false, false, false, 1, kSplitK>;
         auto* k_dq = bwd_dq_kernel<E, D, DV, GATED>;
         auto* k_dkv = bwd_dkv_kernel<E, D, DV, GATED>;
         static bool attrs_set = false;         // benign race: idempotent attribute set
         if (!attrs_set) {
-            hipError_t e = set_lds(k_tot, ShT::kBytes);
+            hipError_t e = set_lds(k_tot, kTotBytes);
             if (e == hipSuccess) e = set_lds(k_dq, Sh::kBytes);
             if (e == hipSuccess) e = set_lds(k_dkv, Sh::kBytes);
             if (e != hipSuccess) return e;
@@ -51,8 +54,8 @@ hipError_t run_bwd(const BwdLaunch& p) {
         a.zk = reinterpret_cast<float*>(ws + lay.zk);
         a.wc = reinterpret_cast<float*>(ws + lay.wc);
         a.N = p.N; a.NC = NC; a.eps = p.eps; a.normalize = p.normalize;
-        // as many workgroups per CU as the LDS holds (three at D = Dv = 64 bf16): measured
-        // faster than fewer, longer runs
+        // as many workgroups per CU as the LDS holds (two at D = Dv = 64 bf16, with the
+        // split operands' tiles): measured faster than fewer, longer runs
         a.LC = p.run > 0 ? (p.run < NC ? p.run : NC) : bwd_chunks_per_group(p.BH, NC, Sh::kWaves, p.cus);
         const int NR = (NC + a.LC - 1) / a.LC;
         a.NR = NR;
@@ -66,7 +69,7 @@ hipError_t run_bwd(const BwdLaunch& p) {
             w.st = a.fst; w.zt = a.fzt; w.lg = reinterpret_cast<float*>(ws + lay.flg);
             w.s0 = p.s0; w.z0 = p.z0;
             w.N = p.N; w.BH = p.BH; w.nseg = NR; w.L = a.LC; w.tparts = 1; w.nslots = NR; w.direct = 0; w.want_final = 0; w.eps = p.eps; w.normalize = 1;
-            hipLaunchKernelGGL(k_tot, dim3(BH * unsigned(NR - 1)), dim3(kThreads), ShT::kBytes, p.stream, w);
+            hipLaunchKernelGGL(k_tot, dim3(BH * unsigned(NR - 1)), dim3(kThreads), kTotBytes, p.stream, w);
             hipLaunchKernelGGL((scan_kernel<D, DV, GATED>), dim3(BH * NBLK), dim3(kThreads), 0, p.stream, a.fst, a.fzt,
                                w.lg, p.s0, p.z0, NR, NR - 1);
         }

@@ -260,10 +260,15 @@ struct OutRsrc {
 // OUT: the workgroup forms outputs (row-major Fk, S^T and the split z in LDS).
 // IDENT: q and k already hold the features (another map applied beforehand), so the
 // walker uses them as they are instead of applying elu + 1.  RELU: the features are
-// relu(x) + fshift, applied while staging like elu + 1.
-template <typename E, int D, int DV, int CH, bool GATED, bool OUT, bool IDENT = false, bool RELU = false, int VS = 1>
+// relu(x) + fshift, applied while staging like elu + 1.  SPLITK (totals walk, bf16): each
+// element of Fk^T goes to LDS as a high and a low part, hi = bf16(f), lo = bf16(f - hi),
+// the low parts in a tile of their own after the shape's tiles, and the fold takes both,
+// so the totals carry the features to about 16 bits instead of 8.
+template <typename E, int D, int DV, int CH, bool GATED, bool OUT, bool IDENT = false, bool RELU = false, int VS = 1,
+          bool SPLITK = false>
 struct ChunkWalker {
     using Sh = WalkShape<E, D, DV, CH, GATED, OUT>;
+    static_assert(!SPLITK || (Sh::kKT && !OUT && sizeof(E) == 2), "split features: bf16 totals walk only");
     using X = Elem<E>;
     static constexpr int LKT = Sh::LKT, LS = Sh::LS;
     static constexpr int DVF = DV * VS;     // row length of v and o (all column parts)
@@ -286,6 +291,7 @@ struct ChunkWalker {
 
     E* sK;
     E* sKt;
+    E* sKtLo;      // SPLITK: low parts of Fk^T, laid out like sKt
     E* sVt;
     E* sSt;
     E* sZb;        // [4][LZ]: z high part, z low part, two zero rows
@@ -329,6 +335,7 @@ struct ChunkWalker {
         sSt = reinterpret_cast<E*>(smem + Sh::kOffSt);
         sZb = reinterpret_cast<E*>(smem + Sh::kOffZb);
         sLam = reinterpret_cast<float*>(smem + Sh::kOffLam);
+        sKtLo = reinterpret_cast<E*>(smem + Sh::kBytes);
         tid = threadIdx.x;
         w = __builtin_amdgcn_readfirstlane(tid / kWave);
         sO = smem + Sh::kOffO + size_t(w) * Sh::kOBlock;
@@ -423,12 +430,14 @@ struct ChunkWalker {
             if ((PARTS & 1) && u < Sh::NKU) {
                 const int cg = u % (D / 8), kq = u / (D / 8);
                 E fr[4][8];
+                float ff[4][8];      // SPLITK: the features before rounding
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const float f = feat(X::to_f32(R.rk[it][r].x[e]));
-                        fr[r][e] = X::from_f32(TAIL ? (ts + krow_of(kq, r) < N ? f : 0.0f) : f);
+                        ff[r][e] = TAIL ? (ts + krow_of(kq, r) < N ? f : 0.0f) : f;
+                        fr[r][e] = X::from_f32(ff[r][e]);
                     }
                     if constexpr (Sh::kRowK) {
                         F8<E> t;
@@ -444,11 +453,20 @@ struct ChunkWalker {
                         dec[r] = GATED ? fast_exp2(fminf(lam_last - sLam[4 * kq + r], 0.0f)) : 1.0f;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        F4<E> t;
+                        F4<E> t, tl;
 #pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            t.x[r] = GATED ? X::from_f32(X::to_f32(fr[r][e]) * dec[r]) : fr[r][e];
-                        *reinterpret_cast<F4<E>*>(sKt + tidx(8 * cg + e, kq >> 1) + 4 * (kq & 1)) = t;
+                        for (int r = 0; r < 4; ++r) {
+                            if constexpr (SPLITK) {
+                                const float fv = GATED ? ff[r][e] * dec[r] : ff[r][e];
+                                t.x[r] = X::from_f32(fv);
+                                tl.x[r] = X::from_f32(fv - X::to_f32(t.x[r]));
+                            } else {
+                                t.x[r] = GATED ? X::from_f32(X::to_f32(fr[r][e]) * dec[r]) : fr[r][e];
+                            }
+                        }
+                        const int at = tidx(8 * cg + e, kq >> 1) + 4 * (kq & 1);
+                        *reinterpret_cast<F4<E>*>(sKt + at) = t;
+                        if constexpr (SPLITK) *reinterpret_cast<F4<E>*>(sKtLo + at) = tl;
                     }
                 }
             }
@@ -540,6 +558,12 @@ struct ChunkWalker {
 #pragma unroll
                 for (int b = 0; b < Sh::NB; ++b) sacc[i * Sh::NB + b] = mma(ka, vf[b], sacc[i * Sh::NB + b]);
                 zacc[i] = mma(ka, ones, zacc[i]);
+                if constexpr (SPLITK) {
+                    const F8<E> kl = lds_f8(sKtLo + tidx(16 * a + l16, 4 * kbk + g4));
+#pragma unroll
+                    for (int b = 0; b < Sh::NB; ++b) sacc[i * Sh::NB + b] = mma(kl, vf[b], sacc[i * Sh::NB + b]);
+                    zacc[i] = mma(kl, ones, zacc[i]);
+                }
             }
         }
     }
@@ -954,11 +978,11 @@ __device__ __forceinline__ void segment_prefix(const WalkArgs& args, int bh, int
 // slots are per (head, column part): slot (bh * VS + part) * nslots + t holds that
 // part's [D, DV] slice of the state and its own copy of z.
 template <typename E, int D, int DV, int CH, bool GATED, bool OUTPUT, bool IDENT = false, bool RELU = false,
-          int VS = 1>
+          int VS = 1, bool SPLITK = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     WalkShape<E, D, DV, CH, GATED, OUTPUT>::kWaves, WalkShape<E, D, DV, CH, GATED, OUTPUT>::kWaves))) void walk_kernel(WalkArgs args) {
     using Sh = WalkShape<E, D, DV, CH, GATED, OUTPUT>;
-    using W = ChunkWalker<E, D, DV, CH, GATED, OUTPUT, IDENT, RELU, VS>;
+    using W = ChunkWalker<E, D, DV, CH, GATED, OUTPUT, IDENT, RELU, VS, SPLITK>;
     constexpr int DVF = DV * VS;
     extern __shared__ __align__(16) unsigned char smem[];
 

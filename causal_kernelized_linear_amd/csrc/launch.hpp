@@ -126,9 +126,21 @@ inline int totals_parts(long heads, int nseg, int L, int D, int Dv, long round) 
 // column and row sums of its pair terms and one fp32 [D] vector.  BwdShape<...>::kBytes
 // is checked against it.
 constexpr int kBwdChunkHost = 64;
-constexpr size_t bwd_lds_bytes(int esize, int D, int Dv) {
+constexpr size_t bwd_base_lds_bytes(int esize, int D, int Dv) {
     const size_t es = size_t(esize), pad = 16 / es, C = kBwdChunkHost;
     return (2 * C * (D + pad) + 2 * C * (Dv + pad) + size_t(D) * (Dv + pad)) * es + (8 * C + D) * 4;
+}
+// The low parts of phi(Q), phi(K) and of one state (bf16 operands split in two), where
+// they fit beside the rest: every bf16 shape but D = Dv = 128.
+constexpr size_t bwd_split_lds_bytes(int esize, int D, int Dv) {
+    const size_t es = size_t(esize), pad = 16 / es, C = kBwdChunkHost;
+    return (2 * C * (D + pad) + size_t(D) * (Dv + pad)) * es;
+}
+constexpr bool bwd_split(int esize, int D, int Dv) {
+    return esize == 2 && bwd_base_lds_bytes(esize, D, Dv) + bwd_split_lds_bytes(esize, D, Dv) <= kMaxLds;
+}
+constexpr size_t bwd_lds_bytes(int esize, int D, int Dv) {
+    return bwd_base_lds_bytes(esize, D, Dv) + (bwd_split(esize, D, Dv) ? bwd_split_lds_bytes(esize, D, Dv) : 0);
 }
 
 // Chunks per run of the passes that walk runs of chunks (the gradients' dq and dk/dv

@@ -50,7 +50,8 @@ def sel(t, heads):
     return np.stack([a[b, h] for b, h in heads])[None]
 
 
-def check(got, ref, tol, heads=None, gated=False, state=False):
+def check(got, ref, tol, heads=None, gated=False, state=False, tol_qk=None):
+    """tol for every gradient; tol_qk, if given, a tighter bound for dq and dk."""
     pickg = (lambda t: to64(t)) if heads is None else (lambda t: sel(t, heads))
     errs = {n: grad_rel_err(pickg(got[n]), ref[n]) for n in ("dq", "dk", "dv")}
     if gated:
@@ -60,7 +61,8 @@ def check(got, ref, tol, heads=None, gated=False, state=False):
         errs["dz0"] = matrix_rel_err(pickg(got["dz0"]), ref["dz0"])
     _say("  errors " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
     for n, e in errs.items():
-        assert e <= tol, (n, e)
+        bound = tol_qk if (tol_qk is not None and n in ("dq", "dk")) else tol
+        assert e <= bound, (n, e, bound)
 
 
 CASES = [
@@ -159,6 +161,13 @@ def _heads(B, H, n, seed):
     return [(int(i) // H, int(i) % H) for i in sorted(idx)]
 
 
+# dq and dk of the bf16 shapes whose products take split operands (features, states, and
+# A and B where the denominators can be small, each as bf16 high plus low part): a CPU
+# model of the passes puts them near 4e-3 at 4096 tokens, against 1.2e-2 with every
+# operand rounded once; D = Dv = 128 has no LDS left for the low parts and keeps TOL.
+TOL_QK_SPLIT = 1e-2
+
+
 @pytest.mark.parametrize("name,nheads", [("train_bf16", 3), ("gated_bf16", 3), ("longctx_bf16", 2)])
 def test_backward_workload_sampled_heads(name, nheads):
     # longctx_bf16 is the D = Dv = 128 case at full size: 1024 chunks per head, runs of 16
@@ -168,6 +177,7 @@ def test_backward_workload_sampled_heads(name, nheads):
     _say(f"{name} backward full size, oracle on heads {heads}")
     got = gpu_bwd(inp)
     ref = oracle_bwd(inp, heads=heads)
-    check(got, ref, TOL["bf16"], heads=heads, gated=w.kind == "gated")
+    split = w.D * w.Dv < 128 * 128
+    check(got, ref, TOL["bf16"], heads=heads, gated=w.kind == "gated", tol_qk=TOL_QK_SPLIT if split else None)
     for n in ("dq", "dk", "dv"):
         assert torch.isfinite(got[n]).all().item()
