@@ -56,13 +56,16 @@ __device__ __forceinline__ void split_bf16(float v, uint16_t& hi, uint16_t& lo) 
     lo = B::from_f32(v - B::to_f32(hi));
 }
 
-// One workgroup per (head, kFeatBlocks blocks of 64 rows): the rows' FAVOR+ features into
-// f [BH][N][M].  W's split is staged once per workgroup and serves all its blocks.
+// One workgroup per (tensor, head, kFeatBlocks blocks of 64 rows), q and k in one launch
+// (blocks 2i and 2i + 1 take the same rows of q and of k): the rows' FAVOR+ features into
+// fq or fk [BH][N][M].  W's split is staged once per workgroup and serves all its
+// blocks; each block's rows are loaded while the block before it is projected.
 constexpr int kFeatBlocks = 4;
 
 template <typename E, int D, int M>
-__global__ __launch_bounds__(kThreads) void feature_kernel(const E* __restrict__ x, const float* __restrict__ W,
-                                                           E* __restrict__ f, int N, int H) {
+__global__ __launch_bounds__(kThreads) void feature_kernel(const E* __restrict__ xq, const E* __restrict__ xk,
+                                                           const float* __restrict__ W, E* __restrict__ fq,
+                                                           E* __restrict__ fk, int N, int H) {
     using Sh = FeatShape<E, D, M>;
     using X = Elem<E>;
     constexpr int C = Sh::C, LX = Sh::LX, NR = M / 16;
@@ -73,15 +76,29 @@ __global__ __launch_bounds__(kThreads) void feature_kernel(const E* __restrict__
     uint16_t* sWl = reinterpret_cast<uint16_t*>(smem + Sh::kOffWl);
     float* sN = reinterpret_cast<float*>(smem + Sh::kOffN);
     const int nsup = (N + C * kFeatBlocks - 1) / (C * kFeatBlocks);
-    const int sup = blockIdx.x % nsup, bh = blockIdx.x / nsup;
+    const int which = blockIdx.x & 1, item = blockIdx.x >> 1;
+    const int sup = item % nsup, bh = item / nsup;
     const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
     const int l16 = lane & 15, g4 = lane >> 4;
-    const E* xb = x + size_t(bh) * N * D;
-    E* fb = f + size_t(bh) * N * M;
+    const E* xb = (which ? xk : xq) + size_t(bh) * N * D;
+    E* fb = (which ? fk : fq) + size_t(bh) * N * M;
     const float* Wh = W + size_t(bh % H) * M * D;
 
-    // W's high and low parts, once
     constexpr int EPG = 16 / int(sizeof(E)), G = D / EPG, UX = C * G / kThreads, UW = M * D / 4 / kThreads;
+    // a block's x in 16-byte units (rows clamped); the first block's go out before W's
+    f32x4_t rx[UX];
+    auto load_block = [&](int ts_, int nrows_) {
+#pragma unroll
+        for (int u = 0; u < UX; ++u) {
+            const int idx = tid + u * kThreads, row = idx / G, col = (idx % G) * EPG;
+            rx[u] = *reinterpret_cast<const f32x4_t*>(xb + size_t(ts_ + min(row, nrows_ - 1)) * D + col);
+        }
+    };
+    {
+        const int ts0 = sup * kFeatBlocks * C;
+        if (ts0 < N) load_block(ts0, min(C, N - ts0));
+    }
+    // W's high and low parts, once
     {
         f32x4_t rw[UW];
 #pragma unroll
@@ -100,13 +117,6 @@ __global__ __launch_bounds__(kThreads) void feature_kernel(const E* __restrict__
     const int ts = (sup * kFeatBlocks + blk) * C;
     if (ts >= N) break;                                       // uniform over the workgroup
     const int nrows = min(C, N - ts);
-    // the block's x in 16-byte units (rows clamped)
-    f32x4_t rx[UX];
-#pragma unroll
-    for (int u = 0; u < UX; ++u) {
-        const int idx = tid + u * kThreads, row = idx / G, col = (idx % G) * EPG;
-        rx[u] = *reinterpret_cast<const f32x4_t*>(xb + size_t(ts + min(row, nrows - 1)) * D + col);
-    }
 
     // x into LDS (split when fp32), and each row's |x|^2 / 2 summed over the G lanes that
     // hold it (rows past the end are zero)
@@ -139,6 +149,8 @@ __global__ __launch_bounds__(kThreads) void feature_kernel(const E* __restrict__
         sq = sum_lanes<G>(sq);
         if (idx % G == 0) sN[row] = 0.5f * sq;
     }
+    // the next block's rows, in flight during this block's products and stores
+    if (blk + 1 < kFeatBlocks && ts + C < N) load_block(ts + C, min(C, N - ts - C));
     __syncthreads();
 
     // (W x)^T: lane (l16, g4) holds row i = 16 w + l16 against features 16 t + 4 g4 + r
@@ -174,9 +186,9 @@ __global__ __launch_bounds__(kThreads) void feature_kernel(const E* __restrict__
 }
 
 template <typename E, int D, int M>
-static hipError_t run_features(const FeatLaunch& p, const void* x, void* f) {
+static hipError_t run_features(const FeatLaunch& p, void* fq, void* fk) {
     const int nsup = (p.N + 64 * kFeatBlocks - 1) / (64 * kFeatBlocks);
-    const dim3 grid(unsigned(p.BH) * unsigned(nsup)), block(kThreads);
+    const dim3 grid(2u * unsigned(p.BH) * unsigned(nsup)), block(kThreads);
     constexpr size_t lds = FeatShape<E, D, M>::kBytes;
     static bool attr = false;
     if (!attr) {
@@ -185,8 +197,8 @@ static hipError_t run_features(const FeatLaunch& p, const void* x, void* f) {
         if (e != hipSuccess) return e;
         attr = true;
     }
-    hipLaunchKernelGGL((feature_kernel<E, D, M>), grid, block, lds, p.stream, static_cast<const E*>(x), p.W,
-                       static_cast<E*>(f), p.N, p.H);
+    hipLaunchKernelGGL((feature_kernel<E, D, M>), grid, block, lds, p.stream, static_cast<const E*>(p.fwd.q),
+                       static_cast<const E*>(p.fwd.k), p.W, static_cast<E*>(fq), static_cast<E*>(fk), p.N, p.H);
     return hipGetLastError();
 }
 
@@ -231,8 +243,7 @@ static hipError_t run_feature_fwd(const FeatLaunch& p) {
     hipError_t e = hipSuccess;
 #define LINATTN_FEAT(DD, MM)                                                             \
     if (p.D == DD && p.M == MM) {                                                        \
-        e = run_features<E, DD, MM>(p, p.fwd.q, fq);                                     \
-        if (e == hipSuccess) e = run_features<E, DD, MM>(p, p.fwd.k, fk);                \
+        e = run_features<E, DD, MM>(p, fq, fk);                                          \
     } else
     LINATTN_FEAT(64, 64) LINATTN_FEAT(64, 128) LINATTN_FEAT(128, 64) LINATTN_FEAT(128, 128) { return hipErrorInvalidValue; }
 #undef LINATTN_FEAT
