@@ -100,6 +100,8 @@ struct WalkArgs {
     float eps;
     int normalize;       // 1: o = num / max(den, eps); 0: o = num (the denominator is not used)
     float fshift;        // RELU walks only: the shift of relu(x) + shift
+    const float* W;      // FAVOR walks only: the projections [H][D][D] (fp32), one set per head
+    int H;               // FAVOR walks only: heads per batch (W's head is bh % H)
 };
 
 // Column part and item (head * segments + segment) of a walk workgroup.  With VS parts,
@@ -263,12 +265,18 @@ struct OutRsrc {
 // relu(x) + fshift, applied while staging like elu + 1.  SPLITK (totals walk, bf16): each
 // element of Fk^T goes to LDS as a high and a low part, hi = bf16(f), lo = bf16(f - hi),
 // the low parts in a tile of their own after the shape's tiles, and the fold takes both,
-// so the totals carry the features to about 16 bits instead of 8.
+// so the totals carry the features to about 16 bits instead of 8.  FAVOR (bf16,
+// ungated, D features from D input dimensions): the features are FAVOR+'s positive random
+// features, exp(w_m . x - |x|^2 / 2) / sqrt(D), projected on the MFMA while staging (W
+// split into bf16 high and low parts in LDS after the shape's tiles, favor_lds_bytes).
 template <typename E, int D, int DV, int CH, bool GATED, bool OUT, bool IDENT = false, bool RELU = false, int VS = 1,
-          bool SPLITK = false>
+          bool SPLITK = false, bool FAVOR = false>
 struct ChunkWalker {
     using Sh = WalkShape<E, D, DV, CH, GATED, OUT>;
     static_assert(!SPLITK || (Sh::kKT && !OUT && sizeof(E) == 2), "split features: bf16 totals walk only");
+    static_assert(!FAVOR || (sizeof(E) == 2 && !GATED && !IDENT && !RELU && VS == 1 && !SPLITK),
+                  "in-walk FAVOR+ features: bf16, ungated");
+    static constexpr int LW = D + 8;        // row stride of W's split tiles
     using X = Elem<E>;
     static constexpr int LKT = Sh::LKT, LS = Sh::LS;
     static constexpr int DVF = DV * VS;     // row length of v and o (all column parts)
@@ -292,6 +300,8 @@ struct ChunkWalker {
     E* sK;
     E* sKt;
     E* sKtLo;      // SPLITK: low parts of Fk^T, laid out like sKt
+    E* sWh;        // FAVOR: W's high and low parts [D][LW], after the shape's tiles
+    E* sWl;
     E* sVt;
     E* sSt;
     E* sZb;        // [4][LZ]: z high part, z low part, two zero rows
@@ -336,6 +346,8 @@ struct ChunkWalker {
         sZb = reinterpret_cast<E*>(smem + Sh::kOffZb);
         sLam = reinterpret_cast<float*>(smem + Sh::kOffLam);
         sKtLo = reinterpret_cast<E*>(smem + Sh::kBytes);
+        sWh = reinterpret_cast<E*>(smem + Sh::kBytes);
+        sWl = sWh + D * LW;
         tid = threadIdx.x;
         w = __builtin_amdgcn_readfirstlane(tid / kWave);
         sO = smem + Sh::kOffO + size_t(w) * Sh::kOBlock;
@@ -424,10 +436,13 @@ struct ChunkWalker {
     // chunk crosses the end of the sequence, so rows past N get zero features.
     template <bool TAIL, int PARTS = 3>
     __device__ __forceinline__ void stage(const Regs& R, int ts, float lam_last) const {
+        if constexpr (FAVOR) {
+            if constexpr ((PARTS & 1) != 0) stage_favor_k<TAIL>(R, ts);
+        }
 #pragma unroll
         for (int it = 0; it < Sh::KPT; ++it) {
             const int u = tid + it * kThreads;
-            if ((PARTS & 1) && u < Sh::NKU) {
+            if (!FAVOR && (PARTS & 1) && u < Sh::NKU) {
                 const int cg = u % (D / 8), kq = u / (D / 8);
                 E fr[4][8];
                 float ff[4][8];      // SPLITK: the features before rounding
@@ -488,12 +503,189 @@ struct ChunkWalker {
     }
 
     __device__ __forceinline__ void phi_q(const QRegs& Q, F8<E> (&fq)[Sh::MAXS][D / 32]) const {
+        if constexpr (FAVOR) {
+            favor_q(Q, fq);
+        } else {
 #pragma unroll
-        for (int m = 0; m < Sh::MAXS; ++m)
+            for (int m = 0; m < Sh::MAXS; ++m)
+#pragma unroll
+                for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) fq[m][ks].x[e] = X::from_f32(feat(X::to_f32(Q.rq[m][ks].x[e])));
+        }
+    }
+
+    // ---- FAVOR+ features (FAVOR walks) ----
+    //
+    // W of this head, split (hi = bf16(w), lo = bf16(w - hi)), into sWh / sWl; once per
+    // workgroup, before the first chunk is staged (whose barriers order it).
+    __device__ __forceinline__ void stage_w(const float* Wb) const {
+        if constexpr (FAVOR) {
+            for (int u = tid; u < D * D / 4; u += kThreads) {
+                const f32x4_t w4 = *reinterpret_cast<const f32x4_t*>(Wb + 4 * u);
+                const int m = (4 * u) / D, d = (4 * u) % D;
+                F4<E> h, l;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    h.x[e] = X::from_f32(w4[e]);
+                    l.x[e] = X::from_f32(w4[e] - X::to_f32(h.x[e]));
+                }
+                *reinterpret_cast<F4<E>*>(sWh + m * LW + d) = h;
+                *reinterpret_cast<F4<E>*>(sWl + m * LW + d) = l;
+            }
+        }
+    }
+
+    // exp(y - h) / sqrt(D) for a projection y and a half squared norm h.
+    static __device__ __forceinline__ float favor_feat(float y, float h) {
+        return fast_exp2((y - h) * kLog2e) * __builtin_amdgcn_rsqf(float(D));
+    }
+
+    // The chunk's keys: the raw rows go to LDS where their features will be (the
+    // row-major phi(K) tile, or in the totals walk the transposed one's space, laid out
+    // row-major by tile_off) with each row's |k|^2 / 2 in sLam; after a barrier every
+    // wave projects its 16-row blocks of keys on the MFMA (W hi and lo against the
+    // exact bf16 rows) and forms the features; after a second barrier (every raw row
+    // read) they go to the tile the walk reads: phi(K) row-major (output walk) or phi(K)^T
+    // (totals walk).  Rows past N (TAIL) get zero features.
+    template <bool TAIL>
+    __device__ __forceinline__ void stage_favor_k(const Regs& R, int ts) const {
+        E* const raw = OUT ? sK : sKt;
+        float* const sNrm = sLam;
+#pragma unroll
+        for (int it = 0; it < Sh::KPT; ++it) {
+            const int u = tid + it * kThreads;
+            const int cg = u % (D / 8), kq = (u / (D / 8)) % (CH / 4);
+            float sq[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = krow_of(kq, r);
+                if (u < Sh::NKU) *reinterpret_cast<F8<E>*>(raw + tile_off<D>(row, 8 * cg)) = R.rk[it][r];
+                float acc = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = X::to_f32(R.rk[it][r].x[e]);
+                    acc += x * x;
+                }
+                sq[r] = lane_group_sum<D / 8>(acc);
+            }
+            if (u < Sh::NKU && cg == 0) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sNrm[krow_of(kq, r)] = 0.5f * sq[r];
+            }
+        }
+        __syncthreads();
+        // wave w: key blocks w, w + 4, ... (CH / 64 of them), all D / 16 feature tiles.
+        // Output walk: a wave reads the raw rows of its own blocks only and writes their
+        // features over them (its LDS accesses complete in order), so each block goes
+        // out as soon as it is formed.  Totals walk: the transposed features land on
+        // other waves' raw rows, so they wait in registers for a barrier.
+        constexpr int NJB = CH / 64, NMT = D / 16;
+        static_assert(NJB >= 1, "chunks of at least 64 tokens");
+        F4<E> fv[OUT ? 1 : NJB][NMT];
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb) {
+            const int j0 = 16 * (w + 4 * jb);
+            const int fb = OUT ? 0 : jb;
+            f32x4_t y[NMT];
+#pragma unroll
+            for (int mt = 0; mt < NMT; ++mt) y[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks) {
+                const F8<E> xf = lds_f8(raw + tile_off<D>(j0 + l16, 32 * ks + 8 * g4));
+#pragma unroll
+                for (int mt = 0; mt < NMT; ++mt) {
+                    const F8<E> wh = lds_f8(sWh + (16 * mt + l16) * LW + 32 * ks + 8 * g4);
+                    const F8<E> wl = lds_f8(sWl + (16 * mt + l16) * LW + 32 * ks + 8 * g4);
+                    if constexpr (OUT) {
+                        // y[m][j]: lane holds features 16 mt + 4 g4 + r of key j0 + l16
+                        y[mt] = mma(wh, xf, y[mt]);
+                        y[mt] = mma(wl, xf, y[mt]);
+                    } else {
+                        // y[j][m]: lane holds keys j0 + 4 g4 + r against feature 16 mt + l16
+                        y[mt] = mma(xf, wh, y[mt]);
+                        y[mt] = mma(xf, wl, y[mt]);
+                    }
+                }
+            }
+            if constexpr (OUT) {
+                const int j = j0 + l16;
+                const float h = sNrm[j];
+                const bool in = !TAIL || ts + j < N;
+#pragma unroll
+                for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) fv[fb][mt].x[r] = X::from_f32(in ? favor_feat(y[mt][r], h) : 0.0f);
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int mt = 0; mt < NMT; ++mt)
+                    *reinterpret_cast<F4<E>*>(sK + tile_off<D>(j, 16 * mt + 4 * g4)) = fv[fb][mt];
+            } else {
+                const f32x4_t h4 = *reinterpret_cast<const f32x4_t*>(sNrm + j0 + 4 * g4);
+#pragma unroll
+                for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const bool in = !TAIL || ts + j0 + 4 * g4 + r < N;
+                        fv[fb][mt].x[r] = X::from_f32(in ? favor_feat(y[mt][r], h4[r]) : 0.0f);
+                    }
+            }
+        }
+        if constexpr (!OUT) {
+            __syncthreads();
+#pragma unroll
+            for (int jb = 0; jb < NJB; ++jb) {
+                const int kq0 = 4 * (w + 4 * jb) + g4;      // keys 4 kq0 .. 4 kq0 + 3
+#pragma unroll
+                for (int mt = 0; mt < NMT; ++mt)
+                    *reinterpret_cast<F4<E>*>(sKt + tidx(16 * mt + l16, kq0 >> 1) + 4 * (kq0 & 1)) = fv[jb][mt];
+            }
+        }
+    }
+
+    // This wave's query strips: the projection W q on the MFMA (W's parts against the
+    // exact bf16 rows in registers: lane (l16, g4) gets features 16 mt + 4 g4 + r of
+    // query l16), |q|^2 / 2 summed over the four lane groups, the features, and their
+    // regrouping into the operand layout (features 32 ks + 8 g4 .. + 7 of query l16)
+    // through the wave's 16-row block of LDS, 64 features at a time.
+    __device__ __forceinline__ void favor_q(const QRegs& Q, F8<E> (&fq)[Sh::MAXS][D / 32]) const {
+        constexpr int NMT = D / 16;
+        E* const blk = reinterpret_cast<E*>(sO);          // 16 rows x 64 features
+#pragma unroll
+        for (int m = 0; m < Sh::MAXS; ++m) {
+            float sq = 0.0f;
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) fq[m][ks].x[e] = X::from_f32(feat(X::to_f32(Q.rq[m][ks].x[e])));
+                for (int e = 0; e < 8; ++e) {
+                    const float x = X::to_f32(Q.rq[m][ks].x[e]);
+                    sq += x * x;
+                }
+            sq += __shfl_xor(sq, 16, kWave);
+            sq += __shfl_xor(sq, 32, kWave);
+            const float h = 0.5f * sq;
+#pragma unroll
+            for (int half = 0; half < D / 64; ++half) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int mt = 4 * half + t;
+                    f32x4_t y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < D / 32; ++ks) {
+                        y = mma(lds_f8(sWh + (16 * mt + l16) * LW + 32 * ks + 8 * g4), Q.rq[m][ks], y);
+                        y = mma(lds_f8(sWl + (16 * mt + l16) * LW + 32 * ks + 8 * g4), Q.rq[m][ks], y);
+                    }
+                    F4<E> f;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) f.x[r] = X::from_f32(favor_feat(y[r], h));
+                    *reinterpret_cast<F4<E>*>(blk + l16 * 64 + 16 * t + 4 * g4) = f;
+                }
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) fq[m][2 * half + kk] = lds_f8(blk + l16 * 64 + 32 * kk + 8 * g4);
+                __builtin_amdgcn_wave_barrier();
+            }
+        }
     }
 
     // The two zero rows of the split-z operand; written once, before the first barrier.
@@ -974,15 +1166,26 @@ __device__ __forceinline__ void segment_prefix(const WalkArgs& args, int bh, int
     }
 }
 
+// Waves per SIMD a walk kernel is compiled for: the shape's, or with FAVOR's W tiles in
+// the LDS as many workgroups as then fit.
+template <typename Sh>
+constexpr int walk_kernel_waves(bool favor) {
+    if (!favor) return Sh::kWaves;
+    const int lds = int(kMaxLds / (Sh::kBytes + favor_lds_bytes(Sh::NA * 16)));
+    const int v = lds < Sh::kWaves ? lds : Sh::kWaves;
+    return v < 1 ? 1 : v;
+}
+
 // VS column parts of DV columns each (VS = 1: the whole of Dv = DV).  The workspace
 // slots are per (head, column part): slot (bh * VS + part) * nslots + t holds that
 // part's [D, DV] slice of the state and its own copy of z.
 template <typename E, int D, int DV, int CH, bool GATED, bool OUTPUT, bool IDENT = false, bool RELU = false,
-          int VS = 1, bool SPLITK = false>
+          int VS = 1, bool SPLITK = false, bool FAVOR = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
-    WalkShape<E, D, DV, CH, GATED, OUTPUT>::kWaves, WalkShape<E, D, DV, CH, GATED, OUTPUT>::kWaves))) void walk_kernel(WalkArgs args) {
+    walk_kernel_waves<WalkShape<E, D, DV, CH, GATED, OUTPUT>>(FAVOR),
+    walk_kernel_waves<WalkShape<E, D, DV, CH, GATED, OUTPUT>>(FAVOR)))) void walk_kernel(WalkArgs args) {
     using Sh = WalkShape<E, D, DV, CH, GATED, OUTPUT>;
-    using W = ChunkWalker<E, D, DV, CH, GATED, OUTPUT, IDENT, RELU, VS, SPLITK>;
+    using W = ChunkWalker<E, D, DV, CH, GATED, OUTPUT, IDENT, RELU, VS, SPLITK, FAVOR>;
     constexpr int DVF = DV * VS;
     extern __shared__ __align__(16) unsigned char smem[];
 
@@ -1013,6 +1216,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
             reinterpret_cast<const E*>(args.v) + size_t(bh) * N * DVF + part * DV,
             GATED ? args.g + size_t(bh) * N : nullptr);
     const int w = wk.w, lane = wk.lane, l16 = wk.l16, g4 = wk.g4;
+    if constexpr (FAVOR) wk.stage_w(args.W + size_t(bh % args.H) * D * D);
     OutRsrc ob;
     if constexpr (OUTPUT)
         ob.init(reinterpret_cast<E*>(args.o) + size_t(bh) * N * DVF + part * DV,

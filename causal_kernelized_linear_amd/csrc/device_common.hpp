@@ -32,6 +32,22 @@ template <int CTRL, int ROWS>
 __device__ __forceinline__ float dpp_add_from(float x) {
     return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWS, 0xF, true));
 }
+// Sum over each aligned group of G consecutive lanes (G = 8 or 16), every lane getting
+// its group's sum: quad swaps, then the half-row mirror, then (G = 16) the row mirror.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+template <int G>
+__device__ __forceinline__ float lane_group_sum(float x) {
+    static_assert(G == 8 || G == 16, "groups of 8 or 16 lanes");
+    x += dpp_mov<0xB1>(x);      // quad_perm [1, 0, 3, 2]
+    x += dpp_mov<0x4E>(x);      // quad_perm [2, 3, 0, 1]
+    x += dpp_mov<0x141>(x);     // row_half_mirror
+    if constexpr (G == 16) x += dpp_mov<0x140>(x);   // row_mirror
+    return x;
+}
+
 __device__ __forceinline__ float wave_incl_scan(float x) {
     x = dpp_add_from<0x111, 0xF>(x);   // row_shr:1
     x = dpp_add_from<0x112, 0xF>(x);   // row_shr:2

@@ -4,9 +4,10 @@
 //          walk itself while it stages q and k (its RELU form);
 //   favor  phi(x)_r = exp(w_r . x - |x|^2 / 2) / sqrt(m), the positive random features of
 //          Performer's FAVOR+ (aicassindra.com page, "Performer: unbiased softmax by
-//          positive random features"), for the m rows w_r of a per-head W [H][m][D],
-//          written by a pass of their own; the walk then takes them as they are (its
-//          IDENT form).
+//          positive random features"), for the m rows w_r of a per-head W [H][m][D]:
+//          for bf16 inputs, no gate and m = D = 64 formed by the walk itself while it stages
+//          k and q (its FAVOR form); otherwise written by a pass of their own, which the
+//          walk then takes as they are (its IDENT form).
 // The FAVOR+ projection w_r . x keeps fp32 accuracy on the bf16 MFMA: every fp32 operand
 // is split into a bf16 high part and a bf16 low part (the high part's rounding error),
 // and w . x = x_hi . w_hi + x_hi . w_lo + x_lo . w_hi, dropping x_lo . w_lo (about 2^-16
@@ -213,6 +214,16 @@ static hipError_t run_feature_walks(const FwdLaunch& p) {
     }
 }
 
+// The walk forming FAVOR+ features itself (bf16, ungated, M = D): no feature pass.
+template <int D, int DV>
+static hipError_t run_favor_walks(const FwdLaunch& p) {
+    switch (p.chunk) {
+        case 64: return run_fwd<uint16_t, D, DV, 64, false, false, false, 1, true>(p);
+        case 128: return run_fwd<uint16_t, D, DV, 128, false, false, false, 1, true>(p);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 // The walk under relu + shift features, over q and k as given.
 template <typename E, int D, int DV>
 static hipError_t run_relu_walks(const FwdLaunch& p) {
@@ -238,6 +249,18 @@ static hipError_t run_feature_fwd(const FeatLaunch& p) {
     }
     char* ws = static_cast<char*>(p.fwd.ws);
     const size_t fbytes = round_up256(size_t(p.BH) * p.N * p.M * sizeof(E));
+    if constexpr (sizeof(E) == 2) {
+        // bf16, ungated, M = D = 64: the walks project and exponentiate while staging
+        // (at D = 128 W's tiles leave too little LDS and too few registers)
+        if (p.fwd.g == nullptr && p.M == p.D && p.D == 64 && (p.fwd.chunk == 64 || p.fwd.chunk == 128)) {
+            FwdLaunch w = p.fwd;
+            w.W = p.W;
+            w.H = p.H;
+            w.ws = ws + 2 * fbytes;
+            if (w.Dv == 64) return run_favor_walks<64, 64>(w);
+            if (w.Dv == 128) return run_favor_walks<64, 128>(w);
+        }
+    }
     void* fq = ws;
     void* fk = ws + fbytes;
     hipError_t e = hipSuccess;

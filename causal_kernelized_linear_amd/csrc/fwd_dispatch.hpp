@@ -9,7 +9,8 @@
 namespace linattn {
 
 // DV is the width of one column part; VS parts make up the caller's Dv = DV * VS.
-template <typename E, int D, int DV, int CH, bool GATED, bool IDENT = false, bool RELU = false, int VS = 1>
+template <typename E, int D, int DV, int CH, bool GATED, bool IDENT = false, bool RELU = false, int VS = 1,
+          bool FAVOR = false>
 hipError_t run_fwd_walks(const FwdLaunch& p) {
     using ShT = WalkShape<E, D, DV, CH, GATED, false>;
     using ShO = WalkShape<E, D, DV, CH, GATED, true>;
@@ -27,23 +28,27 @@ hipError_t run_fwd_walks(const FwdLaunch& p) {
     a.N = p.N; a.BH = p.BH; a.nseg = p.nseg; a.L = p.L; a.tparts = tparts; a.nslots = nslots;
     a.eps = p.eps; a.normalize = p.normalize;
     a.fshift = p.fshift;
+    a.W = p.W;
+    a.H = p.H;
     a.direct = prefix_direct(p.nseg, D, DV) ? 1 : 0;
     a.want_final = (p.s_out || p.z_out) ? 1 : 0;
-    auto* k_tot = walk_kernel<E, D, DV, CH, GATED, false, IDENT, RELU, VS>;
+    auto* k_tot = walk_kernel<E, D, DV, CH, GATED, false, IDENT, RELU, VS, false, FAVOR>;
     // the output walk: the split 8-wave walk where its shape has one, else the 4-wave one
-    constexpr bool kSplit = walk_split(int(sizeof(E)), D, DV, CH, GATED) && VS == 1 && !IDENT && !RELU;
+    constexpr bool kSplit = walk_split(int(sizeof(E)), D, DV, CH, GATED) && VS == 1 && !IDENT && !RELU && !FAVOR;
     auto* k_out = [] {
         if constexpr (kSplit)
             return walk_split_kernel<E, D, DV, CH>;
         else
-            return walk_kernel<E, D, DV, CH, GATED, true, IDENT, RELU, VS>;
+            return walk_kernel<E, D, DV, CH, GATED, true, IDENT, RELU, VS, false, FAVOR>;
     }();
-    constexpr size_t kOutBytes = kSplit ? split_walk_lds_bytes(int(sizeof(E)), D, DV, CH) : ShO::kBytes;
+    constexpr size_t kFavorBytes = FAVOR ? favor_lds_bytes(D) : 0;
+    constexpr size_t kTotBytes = ShT::kBytes + kFavorBytes;
+    constexpr size_t kOutBytes = kSplit ? split_walk_lds_bytes(int(sizeof(E)), D, DV, CH) : ShO::kBytes + kFavorBytes;
     constexpr unsigned kOutThreads = kSplit ? kSplitThreads : kThreads;
     static bool attrs_set = false;         // benign race: idempotent attribute set
     if (!attrs_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_tot),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(ShT::kBytes));
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(kTotBytes));
         if (e != hipSuccess) return e;
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_out), hipFuncAttributeMaxDynamicSharedMemorySize,
                                 int(kOutBytes));
@@ -56,7 +61,7 @@ hipError_t run_fwd_walks(const FwdLaunch& p) {
     mark(0);
     if (p.nseg > 1)
         hipLaunchKernelGGL(k_tot, dim3(walk_grid(unsigned(p.BH) * unsigned((p.nseg - 1) * tparts), VS)),
-                           dim3(kThreads), ShT::kBytes, p.stream, a);
+                           dim3(kThreads), kTotBytes, p.stream, a);
     mark(1);
     if (p.nseg > 1 && !a.direct)
         hipLaunchKernelGGL((scan_kernel<D, DV, GATED, VS>), dim3(vheads * NBLK), dim3(kThreads), 0, p.stream, a.st,
@@ -71,12 +76,13 @@ hipError_t run_fwd_walks(const FwdLaunch& p) {
     return hipGetLastError();
 }
 
-template <typename E, int D, int DV, int CH, bool GATED, bool IDENT = false, bool RELU = false, int VS = 1>
+template <typename E, int D, int DV, int CH, bool GATED, bool IDENT = false, bool RELU = false, int VS = 1,
+          bool FAVOR = false>
 hipError_t run_fwd(const FwdLaunch& p) {
-    if constexpr (WalkShape<E, D, DV, CH, GATED, true>::kBytes > kMaxLds) {
+    if constexpr (WalkShape<E, D, DV, CH, GATED, true>::kBytes + (FAVOR ? favor_lds_bytes(D) : 0) > kMaxLds) {
         return hipErrorInvalidValue;           // rejected earlier by the ABI's support check
     } else {
-        return run_fwd_walks<E, D, DV, CH, GATED, IDENT, RELU, VS>(p);
+        return run_fwd_walks<E, D, DV, CH, GATED, IDENT, RELU, VS, FAVOR>(p);
     }
 }
 

@@ -26,6 +26,8 @@ struct FwdLaunch {
     float fshift = 0.0f;     // the walk under relu(x) + fshift features only
     int vsplit = 1;          // column parts of Dv walked by separate workgroups (walk_vsplit)
     int tparts = 1;          // parts of a segment walked by separate totals workgroups (scanned prefix only)
+    const float* W = nullptr;    // FAVOR walks: the projections [H][D][D] fp32
+    int H = 1;
 };
 
 // Chunk sizes with kernel instantiations.
@@ -52,6 +54,10 @@ constexpr size_t kMaxLds = 160 * 1024;   // LDS per compute unit on gfx950
 constexpr bool walk_split(int esize, int D, int Dv, int chunk, bool gated) {
     return esize == 2 && D == 128 && Dv == 128 && chunk == 64 && !gated;
 }
+
+// LDS the FAVOR walks add after the shape's tiles: W's high and low parts, [D][D + 8]
+// bf16 each.
+constexpr size_t favor_lds_bytes(int D) { return size_t(2) * D * (D + 8) * 2; }
 
 // Its LDS: the 4-wave output walk's tiles plus a second S^T and split-z buffer.
 constexpr size_t split_walk_lds_bytes(int esize, int D, int Dv, int chunk) {

@@ -36,6 +36,10 @@ CASES = [
     (2, 2, 640, 64, 64, 64, "bf16", 128, "favor"),
     (1, 2, 200, 128, 64, 64, "bf16", 128, "favor"),
     (1, 1, 1, 64, 64, 64, "bf16", 64, "favor"),
+    # bf16, M = D = 64: ungated, the walk forms the features while staging (ragged tails,
+    # several segments, Dv = 128)
+    (1, 3, 64 * 5 + 17, 64, 128, 64, "bf16", 128, "favor"),
+    (2, 1, 64 * 9 + 40, 64, 64, 64, "bf16", 64, "favor"),
 ]
 
 
@@ -116,20 +120,24 @@ def test_features_workload_sampled_heads(feature):
     assert torch.isfinite(o).all().item()
 
 
+@pytest.mark.parametrize("gated", [False, True], ids=["ungated", "gated"])
 @pytest.mark.parametrize("chunk", [64, 128])
 @pytest.mark.parametrize("M", [64, 128])
-def test_features_orthogonal_favor(M, chunk):
+def test_features_orthogonal_favor(M, chunk, gated):
     # the page's orthogonal projections (aicassindra.com page, "Performer"): blocks of D
-    # orthogonal rows, two blocks when M = 2 D
+    # orthogonal rows, two blocks when M = 2 D (ungated with M = D: features formed in
+    # the walk; otherwise by the feature pass)
     B, H, N, D, Dv = 2, 2, 700, 64, 64
-    inp = workloads.random_inputs(91 + M, B, H, N, D, Dv, dtype="bf16", scale=D ** -0.25, gated=True, g_low=0.9)
+    inp = workloads.random_inputs(91 + M, B, H, N, D, Dv, dtype="bf16", scale=D ** -0.25, gated=gated, g_low=0.9)
     W = workloads.favor_projection(92 + M, H, M, D, orthogonal=True)
-    _say(f"orthogonal favor M={M} chunk={chunk}")
-    o, S, z = binding.fwd_features(*(_dev(inp[n]) for n in ("q", "k", "v")), "favor", W=_dev(W), g=_dev(inp["g"]),
+    _say(f"orthogonal favor M={M} chunk={chunk} gated={gated}")
+    g = inp.get("g")
+    o, S, z = binding.fwd_features(*(_dev(inp[n]) for n in ("q", "k", "v")), "favor", W=_dev(W), g=_dev(g),
                                    chunk=chunk, return_state=True)
     torch.cuda.synchronize()
     o_ref, S_ref, z_ref = oracle.causal_linear_attention(to64(inp["q"]), to64(inp["k"]), to64(inp["v"]),
-                                                         g=to64(inp["g"]), feature=("favor", to64(W)))
+                                                         g=None if g is None else to64(g),
+                                                         feature=("favor", to64(W)))
     assert rowwise_rel_err(to64(o), o_ref) <= TOL["bf16"]
     assert matrix_rel_err(to64(S), S_ref) <= TOL["bf16"]
     assert matrix_rel_err(to64(z), z_ref) <= TOL["bf16"]
