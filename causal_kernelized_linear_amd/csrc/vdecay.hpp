@@ -73,6 +73,10 @@ struct VdShape {
     // slower: vdecay_bf16 266 against 232 us)
     static constexpr int kLdsWaves = int(kMaxLds / kBytes) < 1 ? 1 : int(kMaxLds / kBytes);
     static constexpr int kWaves = kLdsWaves < 2 ? kLdsWaves : 2;
+    // next chunk's rows in flight during this chunk's work (where the registers allow:
+    // the totals kernel below 128 x 128 bf16, the output kernel at 64 x 64 bf16)
+    static constexpr bool kAhead = sizeof(E) == 2 && D * DV < 128 * 128;
+    static constexpr bool kAheadOut = sizeof(E) == 2 && D * DV <= 64 * 64;
     static constexpr int EPG = 16 / int(sizeof(E));
 };
 
@@ -277,17 +281,25 @@ void vd_totals_kernel(VdArgs args) {
 #pragma unroll
     for (int u = 0; u < SU; ++u) T[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float tz[KZ][4] = {}, tl[KZ][4] = {};
+    // the rows of a chunk; with Sh::kAhead the next chunk's are loaded into the same
+    // registers as soon as this chunk's are in LDS, so they arrive during its products
+    VdRows<E, D> rk;
+    VdRows<E, DV> rv;
+    VdDecays<D> ra;
+    auto issue = [&](int cn) {
+        const int tn = cn * C, nn = min(C, N - tn);
+        rk.load(reinterpret_cast<const E*>(args.k) + size_t(bh) * N * D, tid, tn, nn);
+        rv.load(reinterpret_cast<const E*>(args.v) + size_t(bh) * N * DV, tid, tn, nn);
+        ra.load(args.a + size_t(bh) * N * D, tid, tn, nn);
+    };
+    if (Sh::kAhead && c_first < c_end) issue(c_first);
     for (int c = c_first; c < c_end; ++c) {
         const int ts = c * C, nrows = min(C, N - ts);
-        VdRows<E, D> rk;
-        VdRows<E, DV> rv;
-        VdDecays<D> ra;
-        rk.load(reinterpret_cast<const E*>(args.k) + size_t(bh) * N * D, tid, ts, nrows);
-        rv.load(reinterpret_cast<const E*>(args.v) + size_t(bh) * N * DV, tid, ts, nrows);
-        ra.load(args.a + size_t(bh) * N * D, tid, ts, nrows);
+        if (!Sh::kAhead) issue(c);
         ra.store(sL, LL, tid, nrows);
         rk.template store<true>(sK, LQ, tid, nrows);
         rv.template store<false>(sV, LV, tid, nrows);
+        if (Sh::kAhead && c + 1 < c_end) issue(c + 1);
         // V's pad: a column of ones, so the z part comes out of the state product
         if (tid < C)
             *reinterpret_cast<f32x4_t*>(sV + tid * LV + DV) = split_pad<E>(tid < nrows ? 1.0f : 0.0f);
@@ -414,17 +426,25 @@ void vd_out_kernel(VdArgs args) {
         St::load_z(zv, args.z0 ? args.z0 + size_t(bh) * D : nullptr, w, l16, g4);
     }
 
+    // the rows of a chunk; with Sh::kAheadOut the next chunk's are loaded into the same
+    // registers as soon as this chunk's are in LDS
+    VdRows<E, D> rq, rk;
+    VdRows<E, DV> rv;
+    VdDecays<D> ra;
+    auto issue = [&](int cn) {
+        const int tn = cn * C, nn = min(C, N - tn);
+        rq.load(reinterpret_cast<const E*>(args.q) + size_t(bh) * N * D, tid, tn, nn);
+        rk.load(reinterpret_cast<const E*>(args.k) + size_t(bh) * N * D, tid, tn, nn);
+        rv.load(reinterpret_cast<const E*>(args.v) + size_t(bh) * N * DV, tid, tn, nn);
+        ra.load(args.a + size_t(bh) * N * D, tid, tn, nn);
+    };
+    if (Sh::kAheadOut && c_first < c_end) issue(c_first);
+
     for (int c = c_first; c < c_end; ++c) {
     const int ts = c * C, nrows = min(C, N - ts);
     // staging: every load first
     {
-        VdRows<E, D> rq, rk;
-        VdRows<E, DV> rv;
-        VdDecays<D> ra;
-        rq.load(reinterpret_cast<const E*>(args.q) + size_t(bh) * N * D, tid, ts, nrows);
-        rk.load(reinterpret_cast<const E*>(args.k) + size_t(bh) * N * D, tid, ts, nrows);
-        rv.load(reinterpret_cast<const E*>(args.v) + size_t(bh) * N * DV, tid, ts, nrows);
-        ra.load(args.a + size_t(bh) * N * D, tid, ts, nrows);
+        if (!Sh::kAheadOut) issue(c);
         St::stage(sS, LV, sacc, tid);
         if (l16 == 0) {
             // z_prev, split, into the state's pad columns: den's z part comes out of num
@@ -441,6 +461,7 @@ void vd_out_kernel(VdArgs args) {
         // V's pad: a column of ones, so the z step comes out of the state product
         if (tid < C)
             *reinterpret_cast<f32x4_t*>(sV + tid * LV + DV) = split_pad<E>(tid < nrows ? 1.0f : 0.0f);
+        if (Sh::kAheadOut && c + 1 < c_end) issue(c + 1);
     }
     __syncthreads();
     VdDecays<D>::scan(sL, LL, w, lane);
