@@ -131,7 +131,10 @@ struct WalkShape {
     static_assert(CH >= 32 && CH <= 256 && (CH & (CH - 1)) == 0, "chunk must be a power of two in [32, 256]");
     static constexpr bool kBf16 = sizeof(E) == 2;
     static constexpr bool kRowK = OUT;                         // row-major Fk tile
-    static constexpr bool kKT = !OUT || GATED || !kBf16;       // transposed (decayed) Fk^T tile
+    static constexpr bool kKT = !OUT || !kBf16;                // transposed (decayed) Fk^T tile
+    // the gated bf16 output walk folds with the decay on V: S += Fk^T (2^(L_last - L) V),
+    // from a decayed copy of V^T ([Dv] rows instead of Fk^T's [D])
+    static constexpr bool kVD = OUT && GATED && kBf16;
     static constexpr int LKT = CH + (CH >= 128 ? 16 : 0);  // row stride of Fk^T [D][CH] and V^T [Dv][CH]
     static constexpr int LS = D;                      // row stride of S^T [Dv][D] (groups swizzled)
     static constexpr int LZ = D + 8;                  // row stride of the split z rows
@@ -150,10 +153,12 @@ struct WalkShape {
     static constexpr size_t kOffK = 0;
     static constexpr size_t kOffKt = kOffK + (kRowK ? size_t(CH) * D * sizeof(E) : 0);
     static constexpr size_t kOffVt = kOffKt + (kKT ? size_t(D) * LKT * sizeof(E) : 0);
-    static constexpr size_t kOffSt = kOffVt + size_t(DV) * LKT * sizeof(E);
+    static constexpr size_t kOffVd = kOffVt + size_t(DV) * LKT * sizeof(E);
+    static constexpr size_t kOffSt = kOffVd + (kVD ? size_t(DV) * LKT * sizeof(E) : 0);
     static constexpr size_t kOffZb = kOffSt + (OUT ? size_t(DV) * LS * sizeof(E) : 0);
     static constexpr size_t kOffLam = kOffZb + (OUT ? size_t(4) * LZ * sizeof(E) : 0);
-    static constexpr size_t kOffO = kOffLam + size_t(CH) * 4;
+    static constexpr size_t kOffDec = kOffLam + size_t(CH) * 4;   // kVD: each key's decay (bf16)
+    static constexpr size_t kOffO = kOffDec + (kVD ? size_t(CH) * sizeof(E) : 0);
     static constexpr int kOBlock = 16 * 128;          // per wave: 16 rows x 128 bytes of o
     static constexpr size_t kBytes = kOffO + (OUT ? size_t(kThreads / kWave) * kOBlock : 0);
     static_assert(kBytes == walk_lds_bytes(int(sizeof(E)), D, DV, CH, GATED, OUT), "host LDS formula out of step");
@@ -300,6 +305,8 @@ struct ChunkWalker {
     E* sK;
     E* sKt;
     E* sKtLo;      // SPLITK: low parts of Fk^T, laid out like sKt
+    E* sVd;        // kVD: decayed V^T, laid out like sVt
+    E* sDec;       // kVD: the keys' decays 2^(L_last - L_j), for z's fold
     E* sWh;        // FAVOR: W's high and low parts [D][LW], after the shape's tiles
     E* sWl;
     E* sVt;
@@ -341,6 +348,8 @@ struct ChunkWalker {
                                          const float* g) {
         sK = reinterpret_cast<E*>(smem + Sh::kOffK);
         sKt = reinterpret_cast<E*>(smem + Sh::kOffKt);
+        sVd = reinterpret_cast<E*>(smem + Sh::kOffVd);
+        sDec = reinterpret_cast<E*>(smem + Sh::kOffDec);
         sVt = reinterpret_cast<E*>(smem + Sh::kOffVt);
         sSt = reinterpret_cast<E*>(smem + Sh::kOffSt);
         sZb = reinterpret_cast<E*>(smem + Sh::kOffZb);
@@ -491,12 +500,28 @@ struct ChunkWalker {
             const int u = tid + it * kThreads;
             if ((PARTS & 2) && u < Sh::NVU) {
                 const int cg = u % (DV / 8), kq = u / (DV / 8);
+                float dec[4];
+                if constexpr (Sh::kVD) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dec[r] = fast_exp2(fminf(lam_last - sLam[4 * kq + r], 0.0f));
+                    if (cg == 0) {
+                        F4<E> d4;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) d4.x[r] = X::from_f32(dec[r]);
+                        *reinterpret_cast<F4<E>*>(sDec + 4 * kq) = d4;
+                    }
+                }
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    F4<E> t;
+                    F4<E> t, td;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) t.x[r] = R.rv[it][r].x[e];
-                    *reinterpret_cast<F4<E>*>(sVt + tidx(8 * cg + e, kq >> 1) + 4 * (kq & 1)) = t;
+                    for (int r = 0; r < 4; ++r) {
+                        t.x[r] = R.rv[it][r].x[e];
+                        if constexpr (Sh::kVD) td.x[r] = X::from_f32(X::to_f32(t.x[r]) * dec[r]);
+                    }
+                    const int at = tidx(8 * cg + e, kq >> 1) + 4 * (kq & 1);
+                    *reinterpret_cast<F4<E>*>(sVt + at) = t;
+                    if constexpr (Sh::kVD) *reinterpret_cast<F4<E>*>(sVd + at) = td;
                 }
             }
         }
@@ -722,7 +747,8 @@ struct ChunkWalker {
         }
     }
 
-    // State fold: S = 2^lam_last S + Fk^T V (Fk^T decayed when gated), z alike.
+    // State fold: S = 2^lam_last S + Fk^T V (Fk^T decayed when gated, or V in the gated
+    // bf16 output walk), z alike.
     __device__ __forceinline__ void fold(f32x4_t (&sacc)[Sh::TPW], f32x4_t (&zacc)[Sh::ZT], float lam_last) const {
         if constexpr (GATED) {
             const float dl = fast_exp2(lam_last);
@@ -737,8 +763,16 @@ struct ChunkWalker {
 #pragma unroll
         for (int kbk = 0; kbk < CH / 32; ++kbk) {
             F8<E> vf[Sh::NB];
+            const E* const vsrc = Sh::kVD ? sVd : sVt;
+            // z's B operand: a column of ones, or (kVD) of the keys' decays
+            F8<E> zb = ones;
+            if constexpr (Sh::kVD) {
+                const F8<E> d8 = lds_f8(sDec + 32 * kbk + 8 * g4);
 #pragma unroll
-            for (int b = 0; b < Sh::NB; ++b) vf[b] = lds_f8(sVt + tidx(16 * b + l16, 4 * kbk + g4));
+                for (int e = 0; e < 8; ++e) zb.x[e] = l16 == 0 ? d8.x[e] : X::from_f32(0.0f);
+            }
+#pragma unroll
+            for (int b = 0; b < Sh::NB; ++b) vf[b] = lds_f8(vsrc + tidx(16 * b + l16, 4 * kbk + g4));
 #pragma unroll
             for (int i = 0; i < Sh::ZT; ++i) {
                 const int a = w * Sh::ZT + i;
@@ -749,7 +783,7 @@ struct ChunkWalker {
                     ka = tr_operand<D>(sK, 32 * kbk + 8 * g4, 16 * a, l16);
 #pragma unroll
                 for (int b = 0; b < Sh::NB; ++b) sacc[i * Sh::NB + b] = mma(ka, vf[b], sacc[i * Sh::NB + b]);
-                zacc[i] = mma(ka, ones, zacc[i]);
+                zacc[i] = mma(ka, zb, zacc[i]);
                 if constexpr (SPLITK) {
                     const F8<E> kl = lds_f8(sKtLo + tidx(16 * a + l16, 4 * kbk + g4));
 #pragma unroll

@@ -36,13 +36,15 @@ inline bool chunk_is_built(int chunk) { return chunk == 32 || chunk == 64 || chu
 // Dynamic LDS bytes of a walk kernel for (element size, D, Dv, chunk, gated; out: the
 // output walk, else the totals walk).  WalkShape<...>::kBytes is checked against it.
 // The output walk always stages the row-major Fk tile, S^T and the split z rows; the
-// transposed Fk^T copy is staged by the totals walk and, gated or in fp32, by the
-// output walk too.
+// transposed Fk^T copy is staged by the totals walk and, in fp32, by the output walk
+// too; the gated bf16 output walk stages a decayed copy of V^T instead.
 constexpr size_t walk_lds_bytes(int esize, int D, int Dv, int chunk, bool gated, bool out = true) {
     const size_t es = size_t(esize), lkt = size_t(chunk) + (chunk >= 128 ? 16 : 0);
-    const bool kt = !out || gated || esize != 2;
+    const bool kt = !out || esize != 2;
+    const bool vd = out && gated && esize == 2;
     // the output walk also holds one 16-row x 128-byte block of o for each of its four waves
     return (out ? size_t(chunk) * D * es : 0) + (kt ? size_t(D) * lkt * es : 0) + size_t(Dv) * lkt * es +
+           (vd ? size_t(Dv) * lkt * es + size_t(chunk) * es : 0) +
            (out ? size_t(Dv) * D * es + size_t(4) * (D + 8) * es : 0) + size_t(chunk) * 4 +
            (out ? size_t(4) * 16 * 128 : 0);
 }

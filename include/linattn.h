@@ -34,7 +34,7 @@
  * when the chunk's on-chip tiles fit the 160 KiB LDS of a compute unit.  When the
  * full-width tiles do not fit but 64-column ones do (Dv = 128), the forward walks the
  * value columns as two parts of 64, each with its own workgroups.  That leaves:
- *   bf16: every chunk, except 256 at D = 128 for the gated forward;
+ *   bf16: every chunk;
  *   f32:  chunk <= 128 when D = 64, <= 64 when D = 128.
  * Other shapes return LINATTN_ERR_UNSUPPORTED.
  */

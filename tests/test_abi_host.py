@@ -105,10 +105,10 @@ def test_fwd_rejects_bad_arguments(gated):
     assert fwd(chunk=100, gated=gated) == UNSUPPORTED
     assert fwd(chunk=16, gated=gated) == UNSUPPORTED
     assert fwd(chunk=512, gated=gated) == UNSUPPORTED
-    if gated:
-        # the decayed key tile leaves no room at 256 tokens, even with the value columns in two parts
-        assert fwd(D=128, Dv=128, chunk=256, gated=gated) == UNSUPPORTED
-        assert fwd(D=128, Dv=64, chunk=256, gated=gated) == UNSUPPORTED
+    # 256 tokens at D = 128 pass the support checks (the value columns in two parts at
+    # Dv = 128) and stop at the device check, with no GPU here
+    assert fwd(D=128, Dv=128, chunk=256, gated=gated) == HIP
+    assert fwd(D=128, Dv=64, chunk=256, gated=gated) == HIP
     assert fwd(dt=0, D=128, Dv=128, chunk=128, gated=gated) == UNSUPPORTED
     assert fwd(dt=0, D=128, Dv=64, chunk=128, gated=gated) == UNSUPPORTED
     assert fwd(dt=0, D=64, Dv=64, chunk=256, gated=gated) == UNSUPPORTED
@@ -161,7 +161,7 @@ def test_fwd_noalloc_checks_like_fwd_ex():
     assert fwd_noalloc(g=O + 32) == INVALID                    # g overlaps o
     assert fwd_noalloc(so=O) == INVALID                        # s_out overlaps o
     assert fwd_noalloc(D=96) == UNSUPPORTED
-    assert fwd_noalloc(g=G, D=128, Dv=128, chunk=256) == UNSUPPORTED
+    assert fwd_noalloc(dt=0, D=128, Dv=128, chunk=128) == UNSUPPORTED
     assert fwd_noalloc(B=0, q=0, k=0, v=0, o=0) == OK
 
 
