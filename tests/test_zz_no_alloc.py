@@ -59,3 +59,43 @@ def test_noalloc_equals_workspace_entry(calls):
         ref = _run(case, False)
         for a, b, name in zip(got, ref, ("o", "s_out", "z_out")):
             assert torch.equal(a, b), (case, name, (a.float() - b.float()).abs().max().item())
+
+
+def test_noalloc_replayed_from_a_graph():
+    """The entry point for callers that cannot allocate, captured once into a HIP graph
+    (after one eager call has done the library's per-device set-up) and replayed three
+    times, with eager calls between the replays that reuse the shared scratch for another
+    problem: every replay matches the eager result on the same inputs."""
+    case = (81, 2, 4, 3000, 64, 64, "bf16", 128, True, True)
+    other = (82, 1, 8, 8192, 128, 128, "bf16", 64, False, True)
+    seed, B, H, N, D, Dv, dt, chunk, gated, normalize = case
+    inp = workloads.random_inputs(seed, B, H, N, D, Dv, dtype=dt, gated=gated, g_low=0.9, with_state=True,
+                                  state_scale=5.0)
+    x = {n: t.to(DEV) for n, t in inp.items()}
+    o = torch.empty(B, H, N, Dv, dtype=x["q"].dtype, device=DEV)
+    s_out = torch.empty(B, H, D, Dv, dtype=torch.float32, device=DEV)
+    z_out = torch.empty(B, H, D, dtype=torch.float32, device=DEV)
+    ptrs = [x["q"].data_ptr(), x["k"].data_ptr(), x["v"].data_ptr(), x["g"].data_ptr(), o.data_ptr(),
+            x["s0"].data_ptr(), x["z0"].data_ptr(), s_out.data_ptr(), z_out.data_ptr()]
+
+    def call(stream):
+        return binding.linattn_fwd_ex_noalloc(*ptrs, B, H, N, D, Dv, chunk, binding.BF16, 1e-6, binding.OUT_NORMALIZED,
+                                              stream)
+
+    _say(f"graph: eager call {case}")
+    assert call(torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (o, s_out, z_out)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        code = call(torch.cuda.current_stream().cuda_stream)
+    assert code == 0, binding.linattn_status_string(code)
+    for rep in range(3):
+        _say(f"graph: replay {rep} after an eager call on {other}")
+        for t in (o, s_out, z_out):
+            t.fill_(float("nan"))
+        _run(other, True)                       # the shared scratch now holds another problem
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b, name in zip((o, s_out, z_out), want, ("o", "s_out", "z_out")):
+            assert torch.equal(a, b), (rep, name)
