@@ -154,6 +154,10 @@ linattn_status_t linattn_fwd_ex(
  *    Calls that may overlap in time on one device (on different streams, or from
  *    different host threads without ordering) race on it; calls on one stream are
  *    ordered and safe.
+ *  - Under HIP graph capture: let one call of the same element type, D, Dv, gating and
+ *    chunk run on the device first (it looks up the array's address and sets the kernels'
+ *    LDS limits, which are not stream work); the captured launches then replay with the
+ *    pointers and sizes of the captured call.
  */
 #define LINATTN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 
