@@ -56,8 +56,9 @@
 //     one more tile per d-tile whose B operand is a column of ones.  The operand copy
 //     S^T (input precision) and z are re-staged in LDS once per chunk.
 //   * the fold's key-major Fk operand comes from the row-major Fk tile through
-//     ds_read_b64_tr_b16 (bf16, ungated); the gated and fp32 walks and the totals walk
-//     stage a transposed copy (decayed when gated) instead.
+//     ds_read_b64_tr_b16 in the bf16 output walks (gated: with a decayed copy of V^T
+//     and the keys' decays as z's operand); the fp32 walks and the totals walk stage a
+//     transposed copy of Fk (decayed when gated) instead.
 //   * loads are branch-free: rows past the end are clamped to the last row; in a
 //     chunk that crosses the end their features are zeroed.  The next chunk's K and V
 //     are in flight while this chunk's products run, and its Q while this chunk's
@@ -441,8 +442,9 @@ struct ChunkWalker {
         }
     }
 
-    // phi(K) -> Fk (row-major) and/or Fk^T (decayed when gated); V -> V^T.  TAIL: the
-    // chunk crosses the end of the sequence, so rows past N get zero features.
+    // phi(K) -> Fk (row-major) and/or Fk^T (decayed when gated); V -> V^T (and, kVD, its
+    // decayed copy and the keys' decays).  TAIL: the chunk crosses the end of the
+    // sequence, so rows past N get zero features.
     template <bool TAIL, int PARTS = 3>
     __device__ __forceinline__ void stage(const Regs& R, int ts, float lam_last) const {
         if constexpr (FAVOR) {
