@@ -1303,22 +1303,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
 // of the chunk: they load Q, apply phi and form the strip's outputs from S^T, phi(K) and
 // V^T in LDS.  Waves 4-7 (state waves) hold the carried state in their accumulators as
 // the 4-wave walk does: they load K and V, stage phi(K) and V^T, fold the chunk into the
-// state and stage S^T and z for the next chunk into the other of two LDS buffers.  Both
-// keep the loads of two chunks in flight.  Per
-// chunk both kinds meet at two barriers, after staging and after the outputs and fold;
-// in between, one SIMD runs an output wave and a state wave side by side, so that the
-// VALU, LDS and MFMA work and the waits of the two overlap.
+// state and stage S^T and z for the next chunk.  Both keep the loads of two chunks in
+// flight.  Every tile the two kinds share has two LDS buffers, so that the kinds meet at
+// one barrier per chunk: while the output waves form chunk n's outputs from buffer
+// n mod 2, the state waves fold chunk n from the same buffer and stage chunk n + 1 (its
+// phi(K), V^T and the state in front of it) into the other.  One SIMD runs an output
+// wave and a state wave side by side, so that the VALU, LDS and MFMA work and the waits
+// of the two overlap, and either kind's lighter phase fills the other's heavier one.
 constexpr int kSplitThreads = 2 * kThreads;
 
 template <typename E, int D, int DV, int CH>
 struct SplitShape {
     using W = ChunkWalker<E, D, DV, CH, false, true>;
     using Sh = typename W::Sh;
-    // a second S^T and split-z buffer after the 4-wave walk's tiles
-    static constexpr size_t kOffSt2 = Sh::kBytes;
-    static constexpr size_t kOffZb2 = kOffSt2 + size_t(DV) * Sh::LS * sizeof(E);
-    static constexpr size_t kBytes = kOffZb2 + size_t(4) * Sh::LZ * sizeof(E);
+    // Its own carve-up: each tile's two buffers side by side, so that one register holds
+    // a lane's address in both (the second is the first plus an instruction's immediate
+    // offset, under 64 KiB).
+    static constexpr size_t kK = size_t(CH) * D * sizeof(E);
+    static constexpr size_t kVt = size_t(DV) * Sh::LKT * sizeof(E);
+    static constexpr size_t kSt = size_t(DV) * Sh::LS * sizeof(E);
+    static constexpr size_t kZb = size_t(4) * Sh::LZ * sizeof(E);
+    static constexpr size_t kOffK = 0;
+    static constexpr size_t kOffVt = kOffK + 2 * kK;
+    static constexpr size_t kOffSt = kOffVt + 2 * kVt;
+    static constexpr size_t kOffZb = kOffSt + 2 * kSt;
+    static constexpr size_t kOffLam = kOffZb + 2 * kZb;
+    static constexpr size_t kOffO = kOffLam + size_t(CH) * 4;
+    static constexpr size_t kBytes = kOffO + size_t(kThreads / kWave) * Sh::kOBlock;
+    static_assert(kK < 65536 && kVt < 65536 && kSt < 65536 && kZb < 65536, "buffer pairs within an immediate offset");
     static_assert(Sh::MAXS == 1 && Sh::NSTRIP == 4, "one query strip per output wave");
+    static_assert(Sh::kRowK && !Sh::kKT && !Sh::kVD, "the walk stages the row-major phi(K) tile and V^T only");
     static_assert(kBytes == split_walk_lds_bytes(int(sizeof(E)), D, DV, CH), "host LDS formula out of step");
 };
 
@@ -1345,10 +1359,17 @@ __global__ __launch_bounds__(kSplitThreads) __attribute__((amdgpu_waves_per_eu(2
     const bool state_wave = threadIdx.x >= kThreads;       // uniform over each wave
     wk.tid = threadIdx.x % kThreads;
     wk.w = __builtin_amdgcn_readfirstlane(wk.tid / kWave);
-    wk.sO = smem + Sh::kOffO + size_t(wk.w) * Sh::kOBlock;
+    wk.sO = smem + SS::kOffO + size_t(wk.w) * Sh::kOBlock;
+    wk.sLam = reinterpret_cast<float*>(smem + SS::kOffLam);
     wk.last = min(N, (c0 + max(nch, 1)) * CH) - 1;
-    E* const st_buf[2] = {wk.sSt, reinterpret_cast<E*>(smem + SS::kOffSt2)};
-    E* const zb_buf[2] = {wk.sZb, reinterpret_cast<E*>(smem + SS::kOffZb2)};
+    E* const k_buf[2] = {reinterpret_cast<E*>(smem + SS::kOffK), reinterpret_cast<E*>(smem + SS::kOffK + SS::kK)};
+    E* const vt_buf[2] = {reinterpret_cast<E*>(smem + SS::kOffVt), reinterpret_cast<E*>(smem + SS::kOffVt + SS::kVt)};
+    E* const st_buf[2] = {reinterpret_cast<E*>(smem + SS::kOffSt), reinterpret_cast<E*>(smem + SS::kOffSt + SS::kSt)};
+    E* const zb_buf[2] = {reinterpret_cast<E*>(smem + SS::kOffZb), reinterpret_cast<E*>(smem + SS::kOffZb + SS::kZb)};
+    wk.sK = k_buf[0];
+    wk.sVt = vt_buf[0];
+    wk.sSt = st_buf[0];
+    wk.sZb = zb_buf[0];
     const int w = wk.w, lane = wk.lane, l16 = wk.l16, g4 = wk.g4;
 
     OutRsrc ob;
@@ -1358,8 +1379,8 @@ __global__ __launch_bounds__(kSplitThreads) __attribute__((amdgpu_waves_per_eu(2
     const bool keep = seg == args.nseg - 1 && args.want_final;
 
     // Each kind of wave runs its own loop, so that neither holds the other's registers;
-    // both loops meet at the same two barriers per chunk (nch is uniform over the
-    // workgroup, and the kind of wave is uniform over each wave).
+    // both meet at one barrier before the first chunk and one after each chunk (nch is
+    // uniform over the workgroup, and the kind of wave is uniform over each wave).
     if (state_wave) {
         f32x4_t sacc[Sh::TPW];
         f32x4_t zacc[Sh::ZT];
@@ -1367,24 +1388,35 @@ __global__ __launch_bounds__(kSplitThreads) __attribute__((amdgpu_waves_per_eu(2
         for (int j = 0; j < Sh::TPW; ++j) sacc[j] = zero4;
 #pragma unroll
         for (int i = 0; i < Sh::ZT; ++i) zacc[i] = zero4;
-        // two register sets of K and V: the loads of chunk n + 2 are in flight while
-        // chunk n is staged and folded (three would spill)
+        // two register sets of K and V: the loads of chunks n + 2 and n + 3 are in flight
+        // while chunk n + 1 is staged (three sets would spill)
         typename W::Regs R0, R1;
         wk.load(R0, c0 * CH);
         wk.load(R1, (c0 + 1) * CH);
         segment_prefix<Sh, false, DV, 1>(args, bh, 0, seg, slot0, w, lane, l16, g4, sacc, zacc);
-        wk.sZb = zb_buf[0];
-        wk.clear_zb();
-        wk.stage_state(sacc, zacc);
-        auto step = [&](typename W::Regs& R, int n) {
+        auto stage_chunk = [&](typename W::Regs& R, int n) {
             const int ts = (c0 + n) * CH;
+            wk.sK = k_buf[n & 1];
+            wk.sVt = vt_buf[n & 1];
             if (ts + CH <= N)
                 wk.template stage<false>(R, ts, 0.0f);
             else
                 wk.template stage<true>(R, ts, 0.0f);
             wk.load(R, ts + 2 * CH);
-            __syncthreads();
+        };
+        // chunk 0 and the state in front of it into the first buffers
+        wk.sZb = zb_buf[0];
+        wk.clear_zb();
+        wk.stage_state(sacc, zacc);
+        if (nch > 0) stage_chunk(R0, 0);
+        __syncthreads();
+        // chunk n: stage chunk n + 1 (R_next) into the other buffers, fold chunk n from
+        // buffer n & 1 and stage the state after it beside chunk n + 1
+        auto step = [&](typename W::Regs& R_next, int n) {
             const bool more = n + 1 < nch;
+            if (more) stage_chunk(R_next, n + 1);
+            wk.sK = k_buf[n & 1];
+            wk.sVt = vt_buf[n & 1];
             if (more || keep) wk.fold(sacc, zacc, 0.0f);
             if (more) {
                 wk.sSt = st_buf[(n + 1) & 1];
@@ -1394,8 +1426,8 @@ __global__ __launch_bounds__(kSplitThreads) __attribute__((amdgpu_waves_per_eu(2
             __syncthreads();
         };
         for (int n = 0; n < nch; n += 2) {
-            step(R0, n);
-            if (n + 1 < nch) step(R1, n + 1);
+            step(R1, n);
+            if (n + 1 < nch) step(R0, n + 1);
         }
         if (keep) {
             const size_t slot = slot0 + args.nslots - 1;
@@ -1415,14 +1447,16 @@ __global__ __launch_bounds__(kSplitThreads) __attribute__((amdgpu_waves_per_eu(2
         wk.load_q(q1, (c0 + 1) * CH);
         wk.sZb = zb_buf[1];
         wk.clear_zb();
+        __syncthreads();
         auto step = [&](typename W::QRegs& qr, int n) {
             const int ts = (c0 + n) * CH;
             F8<E> fq[Sh::MAXS][D / 32];
             wk.phi_q(qr, fq);
             wk.load_q(qr, ts + 2 * CH);
-            __syncthreads();
             wk.sSt = st_buf[n & 1];
             wk.sZb = zb_buf[n & 1];
+            wk.sK = k_buf[n & 1];
+            wk.sVt = vt_buf[n & 1];
             // the strip with a runtime key-block loop: the per-wave straight-line form
             // holds more operands than two waves per SIMD leave registers for
             wk.outputs_seq(fq, ts, ob, args.eps, args.normalize);

@@ -61,9 +61,11 @@ constexpr bool walk_split(int esize, int D, int Dv, int chunk, bool gated) {
 // bf16 each.
 constexpr size_t favor_lds_bytes(int D) { return size_t(2) * D * (D + 8) * 2; }
 
-// Its LDS: the 4-wave output walk's tiles plus a second S^T and split-z buffer.
+// Its LDS: the 4-wave output walk's tiles plus a second S^T and split-z buffer, a second
+// phi(K) tile and a second V^T tile.
 constexpr size_t split_walk_lds_bytes(int esize, int D, int Dv, int chunk) {
-    return walk_lds_bytes(esize, D, Dv, chunk, false, true) + size_t(Dv) * D * esize + size_t(4) * (D + 8) * esize;
+    return walk_lds_bytes(esize, D, Dv, chunk, false, true) + size_t(Dv) * D * esize + size_t(4) * (D + 8) * esize +
+           size_t(chunk) * D * esize + size_t(Dv) * (chunk + (chunk >= 128 ? 16 : 0)) * esize;
 }
 
 // Waves per SIMD a walk kernel is compiled for (one wave of every workgroup sits on each
