@@ -603,59 +603,69 @@ struct ChunkWalker {
         }
         __syncthreads();
         // wave w: key blocks w, w + 4, ... (CH / 64 of them), all D / 16 feature tiles.
+        // The wave first reads the raw rows of its blocks into registers, then takes W's
+        // operands one feature tile at a time and applies each to all of its blocks.
         // Output walk: a wave reads the raw rows of its own blocks only and writes their
-        // features over them (its LDS accesses complete in order), so each block goes
-        // out as soon as it is formed.  Totals walk: the transposed features land on
+        // features over them (its LDS accesses complete in order), so each feature tile
+        // goes out as soon as it is formed.  Totals walk: the transposed features land on
         // other waves' raw rows, so they wait in registers for a barrier.
-        constexpr int NJB = CH / 64, NMT = D / 16;
+        constexpr int NJB = CH / 64, NMT = D / 16, KS = D / 32;
         static_assert(NJB >= 1, "chunks of at least 64 tokens");
-        F4<E> fv[OUT ? 1 : NJB][NMT];
+        F8<E> xf[NJB][KS];
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) xf[jb][ks] = lds_f8(raw + tile_off<D>(16 * (w + 4 * jb) + l16, 32 * ks + 8 * g4));
+        float h[NJB];              // output walk: the norm term of key 16 (w + 4 jb) + l16
+        f32x4_t h4[NJB];           // totals walk: of keys 16 (w + 4 jb) + 4 g4 + r
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb) {
             const int j0 = 16 * (w + 4 * jb);
-            const int fb = OUT ? 0 : jb;
-            f32x4_t y[NMT];
+            if constexpr (OUT)
+                h[jb] = sNrm[j0 + l16];
+            else
+                h4[jb] = *reinterpret_cast<const f32x4_t*>(sNrm + j0 + 4 * g4);
+        }
+        __builtin_amdgcn_wave_barrier();
+        F4<E> fv[OUT ? 1 : NJB][NMT];
 #pragma unroll
-            for (int mt = 0; mt < NMT; ++mt) y[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int mt = 0; mt < NMT; ++mt) {
+            f32x4_t y[NJB];
 #pragma unroll
-            for (int ks = 0; ks < D / 32; ++ks) {
-                const F8<E> xf = lds_f8(raw + tile_off<D>(j0 + l16, 32 * ks + 8 * g4));
+            for (int jb = 0; jb < NJB; ++jb) y[jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int mt = 0; mt < NMT; ++mt) {
-                    const F8<E> wh = lds_f8(sWh + (16 * mt + l16) * LW + 32 * ks + 8 * g4);
-                    const F8<E> wl = lds_f8(sWl + (16 * mt + l16) * LW + 32 * ks + 8 * g4);
+            for (int ks = 0; ks < KS; ++ks) {
+                const F8<E> wh = lds_f8(sWh + (16 * mt + l16) * LW + 32 * ks + 8 * g4);
+                const F8<E> wl = lds_f8(sWl + (16 * mt + l16) * LW + 32 * ks + 8 * g4);
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb) {
                     if constexpr (OUT) {
                         // y[m][j]: lane holds features 16 mt + 4 g4 + r of key j0 + l16
-                        y[mt] = mma(wh, xf, y[mt]);
-                        y[mt] = mma(wl, xf, y[mt]);
+                        y[jb] = mma(wh, xf[jb][ks], y[jb]);
+                        y[jb] = mma(wl, xf[jb][ks], y[jb]);
                     } else {
                         // y[j][m]: lane holds keys j0 + 4 g4 + r against feature 16 mt + l16
-                        y[mt] = mma(xf, wh, y[mt]);
-                        y[mt] = mma(xf, wl, y[mt]);
+                        y[jb] = mma(xf[jb][ks], wh, y[jb]);
+                        y[jb] = mma(xf[jb][ks], wl, y[jb]);
                     }
                 }
             }
-            if constexpr (OUT) {
-                const int j = j0 + l16;
-                const float h = sNrm[j];
-                const bool in = !TAIL || ts + j < N;
 #pragma unroll
-                for (int mt = 0; mt < NMT; ++mt)
+            for (int jb = 0; jb < NJB; ++jb) {
+                const int j0 = 16 * (w + 4 * jb);
+                if constexpr (OUT) {
+                    const int j = j0 + l16;
+                    const bool in = !TAIL || ts + j < N;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) fv[fb][mt].x[r] = X::from_f32(in ? favor_feat(y[mt][r], h) : 0.0f);
-                __builtin_amdgcn_wave_barrier();
-#pragma unroll
-                for (int mt = 0; mt < NMT; ++mt)
-                    *reinterpret_cast<F4<E>*>(sK + tile_off<D>(j, 16 * mt + 4 * g4)) = fv[fb][mt];
-            } else {
-                const f32x4_t h4 = *reinterpret_cast<const f32x4_t*>(sNrm + j0 + 4 * g4);
-#pragma unroll
-                for (int mt = 0; mt < NMT; ++mt)
+                    for (int r = 0; r < 4; ++r) fv[0][mt].x[r] = X::from_f32(in ? favor_feat(y[jb][r], h[jb]) : 0.0f);
+                    *reinterpret_cast<F4<E>*>(sK + tile_off<D>(j, 16 * mt + 4 * g4)) = fv[0][mt];
+                } else {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const bool in = !TAIL || ts + j0 + 4 * g4 + r < N;
-                        fv[fb][mt].x[r] = X::from_f32(in ? favor_feat(y[mt][r], h4[r]) : 0.0f);
+                        fv[jb][mt].x[r] = X::from_f32(in ? favor_feat(y[jb][r], h4[jb][r]) : 0.0f);
                     }
+                }
             }
         }
         if constexpr (!OUT) {
@@ -676,13 +686,14 @@ struct ChunkWalker {
     // regrouping into the operand layout (features 32 ks + 8 g4 .. + 7 of query l16)
     // through the wave's 16-row block of LDS, 64 features at a time.
     __device__ __forceinline__ void favor_q(const QRegs& Q, F8<E> (&fq)[Sh::MAXS][D / 32]) const {
-        constexpr int NMT = D / 16;
+        constexpr int MS = Sh::MAXS, KS = D / 32;
         E* const blk = reinterpret_cast<E*>(sO);          // 16 rows x 64 features
+        float h[MS];
 #pragma unroll
-        for (int m = 0; m < Sh::MAXS; ++m) {
+        for (int m = 0; m < MS; ++m) {
             float sq = 0.0f;
 #pragma unroll
-            for (int ks = 0; ks < D / 32; ++ks)
+            for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float x = X::to_f32(Q.rq[m][ks].x[e]);
@@ -690,23 +701,38 @@ struct ChunkWalker {
                 }
             sq += __shfl_xor(sq, 16, kWave);
             sq += __shfl_xor(sq, 32, kWave);
-            const float h = 0.5f * sq;
+            h[m] = 0.5f * sq;
+        }
+        // each of W's operands is read once and applied to every strip of the wave; the
+        // strips' features go through the block one strip at a time
 #pragma unroll
-            for (int half = 0; half < D / 64; ++half) {
+        for (int half = 0; half < D / 64; ++half) {
+            F4<E> f[MS][4];
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int mt = 4 * half + t;
-                    f32x4_t y = {0.f, 0.f, 0.f, 0.f};
+            for (int t = 0; t < 4; ++t) {
+                const int mt = 4 * half + t;
+                f32x4_t y[MS];
 #pragma unroll
-                    for (int ks = 0; ks < D / 32; ++ks) {
-                        y = mma(lds_f8(sWh + (16 * mt + l16) * LW + 32 * ks + 8 * g4), Q.rq[m][ks], y);
-                        y = mma(lds_f8(sWl + (16 * mt + l16) * LW + 32 * ks + 8 * g4), Q.rq[m][ks], y);
+                for (int m = 0; m < MS; ++m) y[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const F8<E> wh = lds_f8(sWh + (16 * mt + l16) * LW + 32 * ks + 8 * g4);
+                    const F8<E> wl = lds_f8(sWl + (16 * mt + l16) * LW + 32 * ks + 8 * g4);
+#pragma unroll
+                    for (int m = 0; m < MS; ++m) {
+                        y[m] = mma(wh, Q.rq[m][ks], y[m]);
+                        y[m] = mma(wl, Q.rq[m][ks], y[m]);
                     }
-                    F4<E> f;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) f.x[r] = X::from_f32(favor_feat(y[r], h));
-                    *reinterpret_cast<F4<E>*>(blk + l16 * 64 + 16 * t + 4 * g4) = f;
                 }
+#pragma unroll
+                for (int m = 0; m < MS; ++m)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) f[m][t].x[r] = X::from_f32(favor_feat(y[m][r], h[m]));
+            }
+#pragma unroll
+            for (int m = 0; m < MS; ++m) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) *reinterpret_cast<F4<E>*>(blk + l16 * 64 + 16 * t + 4 * g4) = f[m][t];
                 __builtin_amdgcn_wave_barrier();
 #pragma unroll
                 for (int kk = 0; kk < 2; ++kk) fq[m][2 * half + kk] = lds_f8(blk + l16 * 64 + 32 * kk + 8 * g4);
