@@ -72,6 +72,11 @@ SMALL = [
     (1, 1, 17, 128, 128, "bf16", 32),
     (3, 1, 2049, 64, 64, "bf16", 256),
     (1, 2, 600, 128, 128, "bf16", 256),
+    # the split output walk (D = Dv = 128 bf16, chunk 64, ungated): one partial chunk, a
+    # one-row tail, and segments of several chunks
+    (1, 1, 40, 128, 128, "bf16", 64),
+    (1, 2, 129, 128, 128, "bf16", 64),
+    (2, 2, 1000, 128, 128, "bf16", 64),
 ]
 
 
