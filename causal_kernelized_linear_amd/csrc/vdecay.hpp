@@ -164,6 +164,72 @@ struct VdDecays {
     }
 };
 
+// The output kernel's rescaled operands and factor rows, formed by each wave for the
+// columns it has just scanned (so no barrier separates them from the scan): every row
+// of phi(Q) and phi(K) is referred to the middle row m(i) = 16 (i / 16) + 7 of its
+// 16-row block,
+//     Fq^_i = Fq_i 2^(L_i - L_m(i)),   Fk^_j = Fk_j 2^(L_m(j) - L_j)    (2^-64 .. 2^64 when a >= 2^-8),
+// in place, and the factors that move a block's reference elsewhere go into rows 0..14
+// of sL (the decays are no longer needed once these are formed), one row per factor:
+//     rows 0..3    2^(L_m(I))                   (the carried part's query factor, block I)
+//     rows 4..7    2^(L_last - L_m(J))          (the state step's key factor, block J)
+//     rows 8..13   2^(L_m(I) - L_m(J)), J < I   (row 8 + I (I - 1) / 2 + J: key block J against query block I)
+//     row  14      2^(L_last)                   (the state's decay over the chunk)
+// Then A_ij = Fq^_i . (Fk^_j * 2^(L_m(I) - L_m(J))) for J < I and Fq^_i . Fk^_j on the
+// diagonal block, both exponents of a product summing to L_i - L_j.
+constexpr int kVdRowFactors = 15;
+__host__ __device__ constexpr int vd_pair_row(int I, int J) { return 8 + I * (I - 1) / 2 + J; }
+
+template <typename E, int D>
+__device__ __forceinline__ void vd_scan_rescale(float* sL, int LL, E* sQ, E* sK, int LQ, int w, int lane) {
+    using X = Elem<E>;
+    constexpr int C = kBwdChunk, NG = D / 16, Q4 = D / 4;
+    const int col0 = w * Q4;
+    VdDecays<D>::scan(sL, LL, w, lane);
+    __builtin_amdgcn_wave_barrier();   // other lanes' rows of L are read below
+    // this lane's row i = lane of phi(Q) and phi(K), the wave's columns, 4 at a time
+    const int mid = (lane & ~15) | 7;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        const int c = col0 + 4 * g;
+        const f32x4_t li = *reinterpret_cast<const f32x4_t*>(sL + lane * LL + c);
+        const f32x4_t lm = *reinterpret_cast<const f32x4_t*>(sL + mid * LL + c);
+        F4<E>* pq = reinterpret_cast<F4<E>*>(sQ + lane * LQ + c);
+        F4<E>* pk = reinterpret_cast<F4<E>*>(sK + lane * LQ + c);
+        F4<E> fq = *pq, fk = *pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            fq.x[e] = X::from_f32(X::to_f32(fq.x[e]) * fast_exp2(li[e] - lm[e]));
+            fk.x[e] = X::from_f32(X::to_f32(fk.x[e]) * fast_exp2(lm[e] - li[e]));
+        }
+        *pq = fq;
+        *pk = fk;
+    }
+    // the factor rows: lane (l16, g4) forms factor l16 (< 15) of column col0 + 4 g + g4
+    const int l16 = lane & 15, g4 = lane >> 4;
+    int r1 = C - 1, r2 = -1;
+    if (l16 < 4) {
+        r1 = 16 * l16 + 7;
+    } else if (l16 < 8) {
+        r2 = 16 * (l16 - 4) + 7;
+    } else if (l16 < 14) {
+        const int p = l16 - 8, I = p < 1 ? 1 : (p < 3 ? 2 : 3), J = p - I * (I - 1) / 2;
+        r1 = 16 * I + 7;
+        r2 = 16 * J + 7;
+    }
+    float fac[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        const int c = col0 + 4 * g + g4;
+        fac[g] = fast_exp2(sL[r1 * LL + c] - (r2 >= 0 ? sL[r2 * LL + c] : 0.0f));
+    }
+    __builtin_amdgcn_wave_barrier();   // the wave's reads of its columns' L come first
+    if (l16 < kVdRowFactors) {
+#pragma unroll
+        for (int g = 0; g < NG; ++g) sL[l16 * LL + col0 + 4 * g + g4] = fac[g];
+    }
+}
+
 // Accumulator-layout state pieces of this thread (tiles w + 4u, as in the gradients):
 // loads and stores of a workspace slot, a caller-layout state, and the [D][Dv] staging.
 template <typename E, int D, int DV>
@@ -464,77 +530,67 @@ void vd_out_kernel(VdArgs args) {
         if (Sh::kAheadOut && c + 1 < c_end) issue(c + 1);
     }
     __syncthreads();
-    VdDecays<D>::scan(sL, LL, w, lane);
+    vd_scan_rescale<E, D>(sL, LL, sQ, sK, LQ, w, lane);
     __syncthreads();
 
-    // This wave's query rows (block I = w); this lane's row of the transposed tiles.
+    // This wave's query rows (block I = w); this lane's row of the transposed tiles.  The
+    // rows of phi(Q) and phi(K) in LDS are referred to their blocks' middle rows and sL
+    // holds the factor rows (vd_scan_rescale).
     const int i0 = 16 * w, il = i0 + l16;
     // num^T[e][i] = ((Fq * 2^L) S_prev)^T + (A V)^T, with an extra block of rows e = Dv,
     // Dv + 1: S's pad columns hold z_prev split and V's a column of ones, so they end as
-    // den's two parts
+    // den's two parts; Fq_i 2^L_i = Fq^_i 2^(L_m(I))
     f32x4_t nt[NE + 1];
 #pragma unroll
     for (int et = 0; et <= NE; ++et) nt[et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    F8<E> fqr[D / 32];                 // this lane's query row, rescaled, as the products' operand
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) fqr[ks] = frag_row(sQ, LQ, il, 32 * ks + 8 * g4);
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
         const int d0 = 32 * ks + 8 * g4;
-        const F8<E> fq = frag_row(sQ, LQ, il, d0);
+        const F8<E>& fq = fqr[ks];
+        const f32x4_t f0 = *reinterpret_cast<const f32x4_t*>(sL + w * LL + d0);
+        const f32x4_t f1 = *reinterpret_cast<const f32x4_t*>(sL + w * LL + d0 + 4);
         F8<E> a;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a.x[e] = X::from_f32(X::to_f32(fq.x[e]) * fast_exp2(sL[il * LL + d0 + e]));
+        for (int e = 0; e < 4; ++e) {
+            a.x[e] = X::from_f32(X::to_f32(fq.x[e]) * f0[e]);
+            a.x[4 + e] = X::from_f32(X::to_f32(fq.x[4 + e]) * f1[e]);
+        }
 #pragma unroll
         for (int et = 0; et <= NE; ++et) nt[et] = mma(frag_col(sS, LV, d0, 16 * et, l16), a, nt[et]);
     }
 
     // A over the blocks J <= I, transposed: lane (l16, g4) holds query il against keys
-    // 16 jt + 4 g4 + r, the operand layout of the 16x16x16 product with V.  The blocks
-    // J < I share one reference row, R = 16 I - 1 (the row in front of the wave's block):
-    // the queries are rescaled once, qa_i = Fq_i 2^(L_i - L_R) (at least 2^-128 over 16
-    // rows), and every key block against it, kb_j = Fk_j 2^(L_R - L_j) <= 1 (a distant key
-    // that underflows carries a weight below 2^-128 anyway).  The diagonal block J = I
-    // uses its middle row.
-    F8<E> qa_off[D / 32];
-    if (w > 0) {
-#pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) {
-            const int d0 = 32 * ks + 8 * g4;
-            const F8<E> fq = frag_row(sQ, LQ, il, d0);
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                qa_off[ks].x[e] =
-                    X::from_f32(X::to_f32(fq.x[e]) * fast_exp2(sL[il * LL + d0 + e] - sL[(i0 - 1) * LL + d0 + e]));
-        }
-    }
+    // 16 jt + 4 g4 + r, the operand layout of the 16x16x16 product with V.  Block J < I:
+    // the keys carried from their block's middle row to the query block's (a factor of at
+    // most 1: a distant key that underflows carries a weight below 2^-85 anyway); the
+    // diagonal block takes the rescaled rows as they are.
 #pragma unroll
     for (int jt = 0; jt < NJ; ++jt) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
         if (jt < w) {
+            const float* fr = sL + vd_pair_row(w, jt) * LL;
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks) {
                 const int d0 = 32 * ks + 8 * g4;
                 const F8<E> fk = frag_row(sK, LQ, 16 * jt + l16, d0);
+                const f32x4_t f0 = *reinterpret_cast<const f32x4_t*>(fr + d0);
+                const f32x4_t f1 = *reinterpret_cast<const f32x4_t*>(fr + d0 + 4);
                 F8<E> kb;
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    kb.x[e] = X::from_f32(X::to_f32(fk.x[e]) *
-                                          fast_exp2(sL[(i0 - 1) * LL + d0 + e] - sL[(16 * jt + l16) * LL + d0 + e]));
-                acc = mma(kb, qa_off[ks], acc);
+                for (int e = 0; e < 4; ++e) {
+                    kb.x[e] = X::from_f32(X::to_f32(fk.x[e]) * f0[e]);
+                    kb.x[4 + e] = X::from_f32(X::to_f32(fk.x[4 + e]) * f1[e]);
+                }
+                acc = mma(kb, fqr[ks], acc);
             }
         } else if (jt == w) {
-            const int ref = 16 * jt + 7;
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks) {
                 const int d0 = 32 * ks + 8 * g4;
-                const F8<E> fq = frag_row(sQ, LQ, il, d0);
-                const F8<E> fk = frag_row(sK, LQ, 16 * jt + l16, d0);
-                F8<E> qa, kb;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float lr = sL[ref * LL + d0 + e];
-                    qa.x[e] = X::from_f32(X::to_f32(fq.x[e]) * fast_exp2(sL[il * LL + d0 + e] - lr));
-                    kb.x[e] = X::from_f32(X::to_f32(fk.x[e]) * fast_exp2(lr - sL[(16 * jt + l16) * LL + d0 + e]));
-                }
-                acc = mma(kb, qa, acc);
+                acc = mma(frag_row(sK, LQ, 16 * jt + l16, d0), fqr[ks], acc);
             }
         }
         if (jt <= w) {
@@ -563,27 +619,37 @@ void vd_out_kernel(VdArgs args) {
             }
         }
     }
-    __syncthreads();                  // every read of the raw keys is done
-    vd_decay_keys<E, D>(sK, LQ, sL, LL, tid);
-    __syncthreads();
-
-    // the state carried across the chunk: S <- Diag(2^L_last) S + Fk~^T V, z alike (the
-    // extra column block: V's pad column of ones)
+    // the state carried across the chunk: S <- Diag(2^L_last) S + Fk~^T V with
+    // Fk~_j = Fk^_j 2^(L_last - L_m(J)), one 16-key block J at a time, its rows d scaled
+    // in fp32; z alike (the extra column block: V's pad column of ones).  It reads only
+    // tiles the outputs read, so no barrier separates the two.
+    auto carried = [&](int a, int b) {
+        f32x4_t ds = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int J = 0; J < NJ; ++J) {
+            const f32x4_t t = mma4(frag4_col(sK, LQ, 16 * J + 4 * g4, 16 * a, l16),
+                                   frag4_col(sV, LV, 16 * J + 4 * g4, 16 * b, l16), f32x4_t{0.f, 0.f, 0.f, 0.f});
+            const f32x4_t u = *reinterpret_cast<const f32x4_t*>(sL + (4 + J) * LL + 16 * a + 4 * g4);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) ds[k] += u[k] * t[k];
+        }
+        return ds;
+    };
 #pragma unroll
     for (int u = 0; u < SU; ++u) {
         const int t = w + 4 * u, a = t / NE, b = t % NE;
-        const f32x4_t ds = vd_tile_tn(sK, LQ, a, sV, LV, b, g4, l16);
-        const f32x4_t lf = *reinterpret_cast<const f32x4_t*>(sL + (C - 1) * LL + 16 * a + 4 * g4);
+        const f32x4_t ds = carried(a, b);
+        const f32x4_t lf = *reinterpret_cast<const f32x4_t*>(sL + (kVdRowFactors - 1) * LL + 16 * a + 4 * g4);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) sacc[u][k] = fast_exp2(lf[k]) * sacc[u][k] + ds[k];
+        for (int k = 0; k < 4; ++k) sacc[u][k] = lf[k] * sacc[u][k] + ds[k];
     }
 #pragma unroll
     for (int t = 0; t < KZ; ++t) {
         const int a = w + 4 * t;
-        const f32x4_t dzt = vd_tile_tn(sK, LQ, a, sV, LV, NE, g4, l16);
-        const f32x4_t lf = *reinterpret_cast<const f32x4_t*>(sL + (C - 1) * LL + 16 * a + 4 * g4);
+        const f32x4_t dzt = carried(a, NE);
+        const f32x4_t lf = *reinterpret_cast<const f32x4_t*>(sL + (kVdRowFactors - 1) * LL + 16 * a + 4 * g4);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) zv[t][r] = fast_exp2(lf[r]) * zv[t][r] + pair01(dzt[r]);
+        for (int r = 0; r < 4; ++r) zv[t][r] = lf[r] * zv[t][r] + pair01(dzt[r]);
     }
     __syncthreads();                  // every read of this chunk's tiles is done
     }
