@@ -122,15 +122,12 @@ struct VdRows {
     }
 };
 
-// The decays of rows [ts, ts + C) as their inclusive log2 prefix L, into sL [C][LL]
-// (rows past the end decay by 1).  load: coalesced 16-byte units (rows clamped); store:
-// log2 into sL row-major; then, after a barrier, scan: wave w takes the columns of its
-// quarter of D, lane i row i (C = 64 lanes), four columns per 16-byte LDS access, each
-// column scanned with the DPP wave scan in place.
+// The decays of rows [ts, ts + C) as log2 into sL [C][LL] (rows past the end decay by 1),
+// for vd_prefix to sum.  load: coalesced 16-byte units (rows clamped); store: log2 into sL
+// row-major.
 template <int D>
 struct VdDecays {
-    static constexpr int C = kBwdChunk, U = C * D / 4 / kThreads, G = D / 4, NG = D / 16;
-    static_assert(C == kWave, "one lane per row");
+    static constexpr int C = kBwdChunk, U = C * D / 4 / kThreads, G = D / 4;
     f32x4_t r[U];
 
     __device__ __forceinline__ void load(const float* ab, int tid, int ts, int nrows) {
@@ -151,83 +148,102 @@ struct VdDecays {
             *reinterpret_cast<f32x4_t*>(sL + row * LL + col) = x;
         }
     }
-
-    static __device__ __forceinline__ void scan(float* sL, int LL, int w, int lane) {
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-            f32x4_t* p = reinterpret_cast<f32x4_t*>(sL + lane * LL + w * (D / 4) + 4 * g);
-            f32x4_t x = *p;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = wave_incl_scan(x[e]);
-            *p = x;
-        }
-    }
 };
 
-// The output kernel's rescaled operands and factor rows, formed by each wave for the
-// columns it has just scanned (so no barrier separates them from the scan): every row
-// of phi(Q) and phi(K) is referred to the middle row m(i) = 16 (i / 16) + 7 of its
-// 16-row block,
-//     Fq^_i = Fq_i 2^(L_i - L_m(i)),   Fk^_j = Fk_j 2^(L_m(j) - L_j)    (2^-64 .. 2^64 when a >= 2^-8),
-// in place, and the factors that move a block's reference elsewhere go into rows 0..14
-// of sL (the decays are no longer needed once these are formed), one row per factor:
+// The chunk's decay prefix and what the kernels derive from it, formed by each wave for
+// the columns of its quarter of D (so no barrier separates them from the prefix).  Lane
+// (l16, s) takes column w D/4 + l16 (+ 16 k, k < D/64) over rows 16 s .. 16 s + 15, one
+// 16-row block: it sums the staged log2 decays down its rows in registers, then adds the
+// totals of the blocks above it (taken from the lanes that hold them), which gives L at
+// each of its rows, the block's middle row m = 16 s + 7 and (lanes s = 3) L_last.
+//   OUT (the output kernel): every row of phi(Q) and phi(K) is referred to the middle row
+//   m(i) = 16 (i / 16) + 7 of its block,
+//       Fq^_i = Fq_i 2^(L_i - L_m(i)),   Fk^_j = Fk_j 2^(L_m(j) - L_j)    (2^-64 .. 2^64 when a >= 2^-8),
+//   in place, so that A_ij = Fq^_i . (Fk^_j * 2^(L_m(I) - L_m(J))) for J < I and
+//   Fq^_i . Fk^_j on the diagonal block, both exponents of a product summing to L_i - L_j.
+//   Otherwise (the totals kernel): the keys as seen from the chunk's end,
+//   Fk~_j = Fk_j 2^(L_last - L_j), in place.
+// The decays are no longer needed then, and rows 0..15 of sL take one factor each:
 //     rows 0..3    2^(L_m(I))                   (the carried part's query factor, block I)
 //     rows 4..7    2^(L_last - L_m(J))          (the state step's key factor, block J)
 //     rows 8..13   2^(L_m(I) - L_m(J)), J < I   (row 8 + I (I - 1) / 2 + J: key block J against query block I)
 //     row  14      2^(L_last)                   (the state's decay over the chunk)
-// Then A_ij = Fq^_i . (Fk^_j * 2^(L_m(I) - L_m(J))) for J < I and Fq^_i . Fk^_j on the
-// diagonal block, both exponents of a product summing to L_i - L_j.
-constexpr int kVdRowFactors = 15;
+//     row  15      L_last
+// Lane (l16, s) writes rows 4 s .. 4 s + 3 of its column.
+constexpr int kVdRowDecay = 14, kVdRowLast = 15;
 __host__ __device__ constexpr int vd_pair_row(int I, int J) { return 8 + I * (I - 1) / 2 + J; }
 
-template <typename E, int D>
-__device__ __forceinline__ void vd_scan_rescale(float* sL, int LL, E* sQ, E* sK, int LQ, int w, int lane) {
+template <typename E, int D, bool OUT>
+__device__ __forceinline__ void vd_prefix(float* sL, int LL, E* sQ, E* sK, int LQ, int w, int lane) {
     using X = Elem<E>;
-    constexpr int C = kBwdChunk, NG = D / 16, Q4 = D / 4;
-    const int col0 = w * Q4;
-    VdDecays<D>::scan(sL, LL, w, lane);
-    __builtin_amdgcn_wave_barrier();   // other lanes' rows of L are read below
-    // this lane's row i = lane of phi(Q) and phi(K), the wave's columns, 4 at a time
-    const int mid = (lane & ~15) | 7;
+    constexpr int CPL = D / 64;
+    static_assert(kBwdChunk == 64 && D % 64 == 0, "four 16-row blocks, 16 columns per lane group");
+    const int s = lane >> 4, l16 = lane & 15;
+    float L[CPL][16];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-        const int c = col0 + 4 * g;
-        const f32x4_t li = *reinterpret_cast<const f32x4_t*>(sL + lane * LL + c);
-        const f32x4_t lm = *reinterpret_cast<const f32x4_t*>(sL + mid * LL + c);
-        F4<E>* pq = reinterpret_cast<F4<E>*>(sQ + lane * LQ + c);
-        F4<E>* pk = reinterpret_cast<F4<E>*>(sK + lane * LQ + c);
-        F4<E> fq = *pq, fk = *pk;
+    for (int k = 0; k < CPL; ++k) {
+        const int col = w * (D / 4) + l16 + 16 * k;
+        float run = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            fq.x[e] = X::from_f32(X::to_f32(fq.x[e]) * fast_exp2(li[e] - lm[e]));
-            fk.x[e] = X::from_f32(X::to_f32(fk.x[e]) * fast_exp2(lm[e] - li[e]));
+        for (int r = 0; r < 16; ++r) {
+            run += sL[(16 * s + r) * LL + col];
+            L[k][r] = run;
         }
-        *pq = fq;
-        *pk = fk;
     }
-    // the factor rows: lane (l16, g4) forms factor l16 (< 15) of column col0 + 4 g + g4
-    const int l16 = lane & 15, g4 = lane >> 4;
-    int r1 = C - 1, r2 = -1;
-    if (l16 < 4) {
-        r1 = 16 * l16 + 7;
-    } else if (l16 < 8) {
-        r2 = 16 * (l16 - 4) + 7;
-    } else if (l16 < 14) {
-        const int p = l16 - 8, I = p < 1 ? 1 : (p < 3 ? 2 : 3), J = p - I * (I - 1) / 2;
-        r1 = 16 * I + 7;
-        r2 = 16 * J + 7;
-    }
-    float fac[NG];
+    float fac[CPL][4];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-        const int c = col0 + 4 * g + g4;
-        fac[g] = fast_exp2(sL[r1 * LL + c] - (r2 >= 0 ? sL[r2 * LL + c] : 0.0f));
-    }
-    __builtin_amdgcn_wave_barrier();   // the wave's reads of its columns' L come first
-    if (l16 < kVdRowFactors) {
+    for (int k = 0; k < CPL; ++k) {
+        const int col = w * (D / 4) + l16 + 16 * k;
+        // the totals of the blocks above: lanes l16, l16 + 16, l16 + 32
+        const float t0 = __shfl(L[k][15], l16, kWave), t1 = __shfl(L[k][15], l16 + 16, kWave),
+                    t2 = __shfl(L[k][15], l16 + 32, kWave);
+        const float off = (s > 0 ? t0 : 0.0f) + (s > 1 ? t1 : 0.0f) + (s > 2 ? t2 : 0.0f);
 #pragma unroll
-        for (int g = 0; g < NG; ++g) sL[l16 * LL + col0 + 4 * g + g4] = fac[g];
+        for (int r = 0; r < 16; ++r) L[k][r] += off;
+        const float mid = L[k][7];
+        float m[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) m[b] = __shfl(mid, l16 + 16 * b, kWave);
+        const float last = __shfl(L[k][15], l16 + 48, kWave);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = 16 * s + r;
+            E* pk = sK + row * LQ + col;
+            if constexpr (OUT) {
+                E* pq = sQ + row * LQ + col;
+                *pq = X::from_f32(X::to_f32(*pq) * fast_exp2(L[k][r] - mid));
+                *pk = X::from_f32(X::to_f32(*pk) * fast_exp2(mid - L[k][r]));
+            } else {
+                *pk = X::from_f32(X::to_f32(*pk) * fast_exp2(fminf(last - L[k][r], 0.0f)));
+            }
+        }
+        // rows 4 s .. 4 s + 3 of the factor table
+        float x[4];
+        if (s == 0) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) x[b] = m[b];
+        } else if (s == 1) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) x[b] = last - m[b];
+        } else if (s == 2) {
+            x[0] = m[1] - m[0];
+            x[1] = m[2] - m[0];
+            x[2] = m[2] - m[1];
+            x[3] = m[3] - m[0];
+        } else {
+            x[0] = m[3] - m[1];
+            x[1] = m[3] - m[2];
+            x[2] = last;
+            x[3] = last;
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) fac[k][b] = (s == 3 && b == 3) ? x[b] : fast_exp2(x[b]);
     }
+    __builtin_amdgcn_wave_barrier();   // the wave's reads of its columns' decays come first
+#pragma unroll
+    for (int k = 0; k < CPL; ++k)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) sL[(4 * s + b) * LL + w * (D / 4) + l16 + 16 * k] = fac[k][b];
 }
 
 // Accumulator-layout state pieces of this thread (tiles w + 4u, as in the gradients):
@@ -295,32 +311,6 @@ __device__ __forceinline__ f32x4_t vd_tile_tn(const E* lhs, int ldl, int a, cons
     return acc;
 }
 
-// Fk rows scaled in place to Fk~_j = Fk_j * 2^(L_last - L_j) (the keys as seen from the
-// chunk's end), 16 bytes per step.
-template <typename E, int D>
-__device__ __forceinline__ void vd_decay_keys(E* sK, int LQ, const float* sL, int LL, int tid) {
-    using X = Elem<E>;
-    constexpr int C = kBwdChunk, EPG = 16 / int(sizeof(E)), G = D / EPG;
-    for (int idx = tid; idx < C * G; idx += kThreads) {
-        const int row = idx / G, col = (idx % G) * EPG;
-        f32x4_t* p = reinterpret_cast<f32x4_t*>(sK + row * LQ + col);
-        if constexpr (sizeof(E) == 2) {
-            F8<E> x = __builtin_bit_cast(F8<E>, *p);
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                x.x[e] = X::from_f32(X::to_f32(x.x[e]) *
-                                     fast_exp2(fminf(sL[(C - 1) * LL + col + e] - sL[row * LL + col + e], 0.0f)));
-            *p = __builtin_bit_cast(f32x4_t, x);
-        } else {
-            f32x4_t x = *p;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                x[e] *= fast_exp2(fminf(sL[(C - 1) * LL + col + e] - sL[row * LL + col + e], 0.0f));
-            *p = x;
-        }
-    }
-}
-
 // ------------------------------------------------------------ run totals ----
 
 template <typename E, int D, int DV>
@@ -370,27 +360,27 @@ void vd_totals_kernel(VdArgs args) {
         if (tid < C)
             *reinterpret_cast<f32x4_t*>(sV + tid * LV + DV) = split_pad<E>(tid < nrows ? 1.0f : 0.0f);
         __syncthreads();
-        VdDecays<D>::scan(sL, LL, w, lane);
-        __syncthreads();
-        vd_decay_keys<E, D>(sK, LQ, sL, LL, tid);
+        // L, the decayed keys Fk~ in place and the factor rows (vd_prefix)
+        vd_prefix<E, D, false>(sL, LL, nullptr, sK, LQ, w, lane);
         __syncthreads();
 #pragma unroll
         for (int u = 0; u < SU; ++u) {
             const int t = w + 4 * u, a = t / NB, b = t % NB;
             const f32x4_t ds = vd_tile_tn(sK, LQ, a, sV, LV, b, g4, l16);
-            const f32x4_t lf = *reinterpret_cast<const f32x4_t*>(sL + (C - 1) * LL + 16 * a + 4 * g4);
+            const f32x4_t lf = *reinterpret_cast<const f32x4_t*>(sL + kVdRowDecay * LL + 16 * a + 4 * g4);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) T[u][k] = fast_exp2(lf[k]) * T[u][k] + ds[k];
+            for (int k = 0; k < 4; ++k) T[u][k] = lf[k] * T[u][k] + ds[k];
         }
 #pragma unroll
         for (int t = 0; t < KZ; ++t) {
             const int a = w + 4 * t;
             const f32x4_t dz = vd_tile_tn(sK, LQ, a, sV, LV, NB, g4, l16);
-            const f32x4_t lf = *reinterpret_cast<const f32x4_t*>(sL + (C - 1) * LL + 16 * a + 4 * g4);
+            const f32x4_t lf = *reinterpret_cast<const f32x4_t*>(sL + kVdRowDecay * LL + 16 * a + 4 * g4);
+            const f32x4_t ll = *reinterpret_cast<const f32x4_t*>(sL + kVdRowLast * LL + 16 * a + 4 * g4);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                tz[t][r] = fast_exp2(lf[r]) * tz[t][r] + pair01(dz[r]);
-                tl[t][r] += lf[r];
+                tz[t][r] = lf[r] * tz[t][r] + pair01(dz[r]);
+                tl[t][r] += ll[r];
             }
         }
         __syncthreads();              // every read of this chunk's tiles is done
@@ -530,7 +520,7 @@ void vd_out_kernel(VdArgs args) {
         if (Sh::kAheadOut && c + 1 < c_end) issue(c + 1);
     }
     __syncthreads();
-    vd_scan_rescale<E, D>(sL, LL, sQ, sK, LQ, w, lane);
+    vd_prefix<E, D, true>(sL, LL, sQ, sK, LQ, w, lane);
     __syncthreads();
 
     // This wave's query rows (block I = w); this lane's row of the transposed tiles.  The
@@ -639,7 +629,7 @@ void vd_out_kernel(VdArgs args) {
     for (int u = 0; u < SU; ++u) {
         const int t = w + 4 * u, a = t / NE, b = t % NE;
         const f32x4_t ds = carried(a, b);
-        const f32x4_t lf = *reinterpret_cast<const f32x4_t*>(sL + (kVdRowFactors - 1) * LL + 16 * a + 4 * g4);
+        const f32x4_t lf = *reinterpret_cast<const f32x4_t*>(sL + kVdRowDecay * LL + 16 * a + 4 * g4);
 #pragma unroll
         for (int k = 0; k < 4; ++k) sacc[u][k] = lf[k] * sacc[u][k] + ds[k];
     }
@@ -647,7 +637,7 @@ void vd_out_kernel(VdArgs args) {
     for (int t = 0; t < KZ; ++t) {
         const int a = w + 4 * t;
         const f32x4_t dzt = carried(a, NE);
-        const f32x4_t lf = *reinterpret_cast<const f32x4_t*>(sL + (kVdRowFactors - 1) * LL + 16 * a + 4 * g4);
+        const f32x4_t lf = *reinterpret_cast<const f32x4_t*>(sL + kVdRowDecay * LL + 16 * a + 4 * g4);
 #pragma unroll
         for (int r = 0; r < 4; ++r) zv[t][r] = lf[r] * zv[t][r] + pair01(dzt[r]);
     }
