@@ -157,8 +157,10 @@ struct WalkShape {
     static constexpr size_t kOffVd = kOffVt + size_t(DV) * LKT * sizeof(E);
     static constexpr size_t kOffSt = kOffVd + (kVD ? size_t(DV) * LKT * sizeof(E) : 0);
     static constexpr size_t kOffZb = kOffSt + (OUT ? size_t(DV) * LS * sizeof(E) : 0);
+    // Lambda: one row for the workgroup, or (kLamPerWave) one per wave
+    static constexpr bool kLamPerWave = walk_lambda_per_wave(int(sizeof(E)), D, DV, CH, GATED, OUT);
     static constexpr size_t kOffLam = kOffZb + (OUT ? size_t(4) * LZ * sizeof(E) : 0);
-    static constexpr size_t kOffDec = kOffLam + size_t(CH) * 4;   // kVD: each key's decay (bf16)
+    static constexpr size_t kOffDec = kOffLam + size_t(CH) * 4 * (kLamPerWave ? 4 : 1);   // kVD: each key's decay (bf16)
     static constexpr size_t kOffO = kOffDec + (kVD ? size_t(CH) * sizeof(E) : 0);
     static constexpr int kOBlock = 16 * 128;          // per wave: 16 rows x 128 bytes of o
     static constexpr size_t kBytes = kOffO + (OUT ? size_t(kThreads / kWave) * kOBlock : 0);
@@ -354,12 +356,12 @@ struct ChunkWalker {
         sVt = reinterpret_cast<E*>(smem + Sh::kOffVt);
         sSt = reinterpret_cast<E*>(smem + Sh::kOffSt);
         sZb = reinterpret_cast<E*>(smem + Sh::kOffZb);
-        sLam = reinterpret_cast<float*>(smem + Sh::kOffLam);
         sKtLo = reinterpret_cast<E*>(smem + Sh::kBytes);
         sWh = reinterpret_cast<E*>(smem + Sh::kBytes);
         sWl = sWh + D * LW;
         tid = threadIdx.x;
         w = __builtin_amdgcn_readfirstlane(tid / kWave);
+        sLam = reinterpret_cast<float*>(smem + Sh::kOffLam) + (Sh::kLamPerWave ? w * CH : 0);
         sO = smem + Sh::kOffO + size_t(w) * Sh::kOBlock;
         lane = tid % kWave;
         l16 = lane & 15;
@@ -424,9 +426,11 @@ struct ChunkWalker {
         }
     }
 
-    // Wave 0: Lambda_j = inclusive sum of log2 g over the chunk, into sLam.
+    // Lambda_j = inclusive sum of log2 g over the chunk, into sLam: by wave 0 for the
+    // workgroup, or (kLamPerWave) by every wave into its own row, which only it reads, so
+    // that no barrier follows (every wave holds the chunk's gates).
     __device__ __forceinline__ void lambda(const Regs& R) const {
-        if (w != 0) return;
+        if (!Sh::kLamPerWave && w != 0) return;
         float loc[Sh::GPT];
         float run = 0.0f;
 #pragma unroll
@@ -872,7 +876,10 @@ struct ChunkWalker {
         const int ts = (c0 + n) * CH;
         if constexpr (GATED) {
             lambda(R);
-            __syncthreads();
+            if constexpr (Sh::kLamPerWave)
+                __builtin_amdgcn_wave_barrier();   // the wave's own row, read by its other lanes
+            else
+                __syncthreads();
         }
         const float lam_last = GATED ? sLam[CH - 1] : 0.0f;
         if (ts + CH <= N)

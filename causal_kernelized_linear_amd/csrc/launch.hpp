@@ -38,7 +38,10 @@ inline bool chunk_is_built(int chunk) { return chunk == 32 || chunk == 64 || chu
 // The output walk always stages the row-major Fk tile, S^T and the split z rows; the
 // transposed Fk^T copy is staged by the totals walk and, in fp32, by the output walk
 // too; the gated bf16 output walk stages a decayed copy of V^T instead.
-constexpr size_t walk_lds_bytes(int esize, int D, int Dv, int chunk, bool gated, bool out = true) {
+constexpr size_t kMaxLds = 160 * 1024;   // LDS per compute unit on gfx950
+
+// The walk's tiles with one row of chunk-local log2 decays (Lambda) for the workgroup.
+constexpr size_t walk_lds_bytes_shared_lambda(int esize, int D, int Dv, int chunk, bool gated, bool out = true) {
     const size_t es = size_t(esize), lkt = size_t(chunk) + (chunk >= 128 ? 16 : 0);
     const bool kt = !out || esize != 2;
     const bool vd = out && gated && esize == 2;
@@ -49,7 +52,17 @@ constexpr size_t walk_lds_bytes(int esize, int D, int Dv, int chunk, bool gated,
            (out ? size_t(4) * 16 * 128 : 0);
 }
 
-constexpr size_t kMaxLds = 160 * 1024;   // LDS per compute unit on gfx950
+// Whether each wave of a gated walk forms and keeps its own row of Lambda (no barrier
+// between the gates' scan and its first use): wherever the three more rows fit the LDS.
+constexpr bool walk_lambda_per_wave(int esize, int D, int Dv, int chunk, bool gated, bool out = true) {
+    return gated && walk_lds_bytes_shared_lambda(esize, D, Dv, chunk, gated, out) + size_t(3) * chunk * 4 <= kMaxLds;
+}
+
+// Dynamic LDS bytes of a walk kernel (WalkShape<...>::kBytes is checked against it).
+constexpr size_t walk_lds_bytes(int esize, int D, int Dv, int chunk, bool gated, bool out = true) {
+    return walk_lds_bytes_shared_lambda(esize, D, Dv, chunk, gated, out) +
+           (walk_lambda_per_wave(esize, D, Dv, chunk, gated, out) ? size_t(3) * chunk * 4 : 0);
+}
 
 // Whether the output walk of a shape runs as the split 8-wave walk (walk_split_kernel):
 // bf16, D = Dv = 128, ungated, 64-token chunks, features elu + 1, Dv uncut.
