@@ -103,6 +103,8 @@ struct WalkArgs {
     float fshift;        // RELU walks only: the shift of relu(x) + shift
     const float* W;      // FAVOR walks only: the projections [H][D][D] (fp32), one set per head
     int H;               // FAVOR walks only: heads per batch (W's head is bh % H)
+    int stream_kv = 0;   // totals walk: K and V loaded non-temporally (the output walk's reads
+                         // of them will not find them in the caches anyway)
 };
 
 // Column part and item (head * segments + segment) of a walk workgroup.  With VS parts,
@@ -320,6 +322,7 @@ struct ChunkWalker {
     int tid, w, lane, l16, g4;
     int N;
     int last;      // last row the loads may touch: the end of the walked range (clamped to N - 1)
+    int stream_kv = 0;   // totals walk: K and V loaded non-temporally (WalkArgs::stream_kv)
     const E* qb;
     const E* kb;
     const E* vb;
@@ -379,8 +382,27 @@ struct ChunkWalker {
     // one cached row); stage() zeroes the features of rows past N.
     // PARTS selects K (1), V (2) or both (3; the split walk divides them between its two
     // kinds of wave).
+    // The output walks read every row for the last time, so their loads are non-temporal;
+    // the totals walk's are where stream_kv says so.
     template <int PARTS = 3>
     __device__ __forceinline__ void load(Regs& R, int ts) const {
+        if (OUT || stream_kv)
+            load_kv<PARTS, true>(R, ts);
+        else
+            load_kv<PARTS, false>(R, ts);
+        if constexpr (GATED) {
+            // every wave loads the gates (cached; every wave, or wave 0, scans them), so the
+            // loads sit behind no branch
+#pragma unroll
+            for (int i = 0; i < Sh::GPT; ++i) {
+                const int j = lane * Sh::GPT + i;
+                const float gv = gb[min(ts + j, last)];
+                R.rg[i] = (j < CH && ts + j < N) ? gv : 1.0f;
+            }
+        }
+    }
+    template <int PARTS, bool NT>
+    __device__ __forceinline__ void load_kv(Regs& R, int ts) const {
 #pragma unroll
         for (int it = 0; it < Sh::KPT; ++it) {
             if (!(PARTS & 1)) break;
@@ -389,7 +411,7 @@ struct ChunkWalker {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = min(ts + krow_of(kq, r), last);
-                R.rk[it][r] = *reinterpret_cast<const F8<E>*>(kb + size_t(row) * D + 8 * cg);
+                R.rk[it][r] = global_f8<NT>(kb + size_t(row) * D + 8 * cg);
             }
         }
 #pragma unroll
@@ -400,17 +422,7 @@ struct ChunkWalker {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = min(ts + 4 * kq + r, last);
-                R.rv[it][r] = *reinterpret_cast<const F8<E>*>(vb + size_t(row) * DVF + 8 * cg);
-            }
-        }
-        if constexpr (GATED) {
-            // every wave loads the gates (cached; only wave 0 scans them), so the loads
-            // sit behind no branch
-#pragma unroll
-            for (int i = 0; i < Sh::GPT; ++i) {
-                const int j = lane * Sh::GPT + i;
-                const float gv = gb[min(ts + j, last)];
-                R.rg[i] = (j < CH && ts + j < N) ? gv : 1.0f;
+                R.rv[it][r] = global_f8<NT>(vb + size_t(row) * DVF + 8 * cg);
             }
         }
     }
@@ -422,7 +434,7 @@ struct ChunkWalker {
             const int row = min(ts + 16 * s + l16, last);
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks)
-                Q.rq[m][ks] = *reinterpret_cast<const F8<E>*>(qb + size_t(row) * D + 32 * ks + 8 * g4);
+                Q.rq[m][ks] = global_f8<true>(qb + size_t(row) * D + 32 * ks + 8 * g4);
         }
     }
 
@@ -1284,6 +1296,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
             reinterpret_cast<const E*>(args.k) + size_t(bh) * N * D,
             reinterpret_cast<const E*>(args.v) + size_t(bh) * N * DVF + part * DV,
             GATED ? args.g + size_t(bh) * N : nullptr);
+    wk.stream_kv = __builtin_amdgcn_readfirstlane(args.stream_kv);
     const int w = wk.w, lane = wk.lane, l16 = wk.l16, g4 = wk.g4;
     if constexpr (FAVOR) wk.stage_w(args.W + size_t(bh % args.H) * D * D);
     OutRsrc ob;

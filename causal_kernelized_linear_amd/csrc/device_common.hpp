@@ -107,6 +107,21 @@ __device__ __forceinline__ F8<E> zero8() {
 template <typename E>
 __device__ __forceinline__ F8<E> lds_f8(const E* p) { return *reinterpret_cast<const F8<E>*>(p); }
 
+// One fragment from global memory, plain or non-temporal (NT: the data is not expected to
+// be read again while it could still be in the caches).
+template <bool NT, typename E>
+__device__ __forceinline__ F8<E> global_f8(const E* p) {
+    if constexpr (!NT) {
+        return *reinterpret_cast<const F8<E>*>(p);
+    } else {
+        constexpr int NV = int(sizeof(F8<E>)) / 16;
+        f32x4_t v[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) v[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p) + i);
+        return __builtin_bit_cast(F8<E>, v);
+    }
+}
+
 template <typename E>
 __device__ __forceinline__ F4<E> lds_f4(const E* p) { return *reinterpret_cast<const F4<E>*>(p); }
 

@@ -32,6 +32,7 @@ hipError_t run_fwd_walks(const FwdLaunch& p) {
     a.H = p.H;
     a.direct = prefix_direct(p.nseg, D, DV) ? 1 : 0;
     a.want_final = (p.s_out || p.z_out) ? 1 : 0;
+    a.stream_kv = totals_stream_kv(p.BH, p.N, D, DV * VS, int(sizeof(E))) ? 1 : 0;
     auto* k_tot = walk_kernel<E, D, DV, CH, GATED, false, IDENT, RELU, VS, false, FAVOR>;
     // the output walk: the split 8-wave walk where its shape has one, else the 4-wave one
     constexpr bool kSplit = walk_split(int(sizeof(E)), D, DV, CH, GATED) && VS == 1 && !IDENT && !RELU && !FAVOR;

@@ -39,6 +39,14 @@ inline bool chunk_is_built(int chunk) { return chunk == 32 || chunk == 64 || chu
 // transposed Fk^T copy is staged by the totals walk and, in fp32, by the output walk
 // too; the gated bf16 output walk stages a decayed copy of V^T instead.
 constexpr size_t kMaxLds = 160 * 1024;   // LDS per compute unit on gfx950
+constexpr size_t kLastLevelCache = size_t(256) << 20;   // MI355X's memory-side cache
+
+// Whether the forward's totals walk loads K and V non-temporally: when K and V together
+// exceed the last-level cache, the output walk that reads them again cannot find them
+// there, and the totals walk's loads need not displace anything for it.
+constexpr bool totals_stream_kv(long BH, long N, int D, int Dv, int esize) {
+    return size_t(BH) * size_t(N) * size_t(D + Dv) * size_t(esize) > kLastLevelCache;
+}
 
 // The walk's tiles with one row of chunk-local log2 decays (Lambda) for the workgroup.
 constexpr size_t walk_lds_bytes_shared_lambda(int esize, int D, int Dv, int chunk, bool gated, bool out = true) {
