@@ -82,6 +82,9 @@ struct VdShape {
 
 // Rows [ts, ts + C) of a [N][W] tensor into registers (16-byte units, rows clamped to the
 // last valid one) and from them into a row-major LDS tile (rows past the end zeroed).
+// The loads are non-temporal, as are the decays': the output kernel reads every row for
+// the last time, and what the totals kernel reads (k, v and the fp32 decays, 268 MB on
+// vdecay_bf16) exceeds the 256 MB last-level cache before the output kernel rereads it.
 template <typename E, int W>
 struct VdRows {
     static constexpr int C = kBwdChunk;
@@ -94,7 +97,8 @@ struct VdRows {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int idx = tid + u * kThreads, row = idx / G, col = (idx % G) * EPG;
-            r[u] = *reinterpret_cast<const f32x4_t*>(src + size_t(ts + min(row, nrows - 1)) * W + col);
+            r[u] = __builtin_nontemporal_load(
+                reinterpret_cast<const f32x4_t*>(src + size_t(ts + min(row, nrows - 1)) * W + col));
         }
     }
 
@@ -134,7 +138,8 @@ struct VdDecays {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int idx = tid + u * kThreads, row = idx / G, col = 4 * (idx % G);
-            r[u] = *reinterpret_cast<const f32x4_t*>(ab + size_t(ts + min(row, nrows - 1)) * D + col);
+            r[u] = __builtin_nontemporal_load(
+                reinterpret_cast<const f32x4_t*>(ab + size_t(ts + min(row, nrows - 1)) * D + col));
         }
     }
 
