@@ -45,7 +45,9 @@ int device_cus() {
 // segment, the first loads) is paid once.
 // vs: the column parts of Dv the walk is cut into (walk_vsplit), each with its own
 // workgroups.
-long target_workgroups(int esize, int D, int Dv, int chunk, bool gated, int vs = 1) {
+long target_workgroups(int esize, int D, int Dv, int chunk, bool gated, int vs = 1, bool elu = true) {
+    // the split output walk (elu + 1 features only): one 8-wave workgroup per compute unit
+    if (elu && vs == 1 && linattn::walk_split(esize, D, Dv, chunk, gated)) return long(device_cus());
     return long(device_cus()) * linattn::walk_waves(esize, D, Dv / vs, chunk, gated, true);
 }
 
@@ -55,7 +57,7 @@ long max_target_workgroups(int D, int Dv, int chunk) {
     long t = 0;
     for (int es : {2, 4})
         for (bool gated : {false, true}) {
-            const long x = target_workgroups(es, D, Dv, chunk, gated);
+            const long x = target_workgroups(es, D, Dv, chunk, gated, 1, false);
             t = x > t ? x : t;
         }
     return t;
@@ -426,7 +428,7 @@ linattn_status_t feat_common(const void* q, const void* k, const void* v, const 
         linattn::walk_lds_bytes(int(es), M, Dv, chunk, g != nullptr) > linattn::kMaxLds ||
         (feature == LINATTN_FEATURE_FAVOR && (size_t(64) * (D + 4) + size_t(M) * (D + 4) + 64) * 4 > linattn::kMaxLds))
         return LINATTN_ERR_UNSUPPORTED;
-    const Plan plan = make_plan(BH, N, M, Dv, chunk, target_workgroups(int(es), M, Dv, chunk, g != nullptr));
+    const Plan plan = make_plan(BH, N, M, Dv, chunk, target_workgroups(int(es), M, Dv, chunk, g != nullptr, 1, false));
     const size_t fb = feature_bytes(BH, N, M, es);
     const size_t need = 2 * fb + plan.bytes;
     if (ws_bytes < need || !ws || !aligned16(ws)) return LINATTN_ERR_WORKSPACE;

@@ -1224,7 +1224,7 @@ __device__ __forceinline__ void segment_prefix(const WalkArgs& args, int bh, int
         if (args.direct) {
             const float* lgb = args.lg + slot0;
 #pragma unroll 2
-            for (int s = 0; s < seg; ++s) {
+            for (int s = 0; s < seg * args.tparts; ++s) {   // every part of every segment in front
                 const float f = GATED ? fast_exp2(lgb[s]) : 1.0f;
 #pragma unroll
                 for (int j = 0; j < Sh::TPW; ++j) sacc[j] = f * sacc[j] + get4(st_at(s, j));
@@ -1343,11 +1343,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     }
 }
 
-// The output walk with its work split between two kinds of wave, for the shapes where
-// the 4-wave walk holds one workgroup per CU (D = Dv = 128 bf16, ungated, 64-token
-// chunks): 8 waves, two per SIMD.  Waves 0-3 (output waves) each take one 16-query strip
-// of the chunk: they load Q, apply phi and form the strip's outputs from S^T, phi(K) and
-// V^T in LDS.  Waves 4-7 (state waves) hold the carried state in their accumulators as
+// The output walk with its work split between two kinds of wave (bf16, ungated): 8 waves
+// in one workgroup per CU, two per SIMD.  At D = Dv = 128 and 64-token chunks the 4-wave
+// walk would hold one workgroup per CU; at D = Dv = 64 and 128-token chunks it holds two,
+// but one workgroup per CU halves the segments, and with them the keys and values the
+// totals walk reads.  Waves 0-3 (output waves) take the chunk's 16-query strips, one each
+// at 64 tokens, strips w and 7 - w at 128 (the same causal work per wave): they load Q,
+// apply phi and form the strips' outputs from S^T, phi(K) and V^T in LDS.  Waves 4-7 (state waves) hold the carried state in their accumulators as
 // the 4-wave walk does: they load K and V, stage phi(K) and V^T, fold the chunk into the
 // state and stage S^T and z for the next chunk.  Both keep the loads of two chunks in
 // flight.  Every tile the two kinds share has two LDS buffers, so that the kinds meet at
@@ -1377,7 +1379,8 @@ struct SplitShape {
     static constexpr size_t kOffO = kOffLam + size_t(CH) * 4;
     static constexpr size_t kBytes = kOffO + size_t(kThreads / kWave) * Sh::kOBlock;
     static_assert(kK < 65536 && kVt < 65536 && kSt < 65536 && kZb < 65536, "buffer pairs within an immediate offset");
-    static_assert(Sh::MAXS == 1 && Sh::NSTRIP == 4, "one query strip per output wave");
+    static_assert((Sh::MAXS == 1 && Sh::NSTRIP == 4) || (Sh::MAXS == 2 && Sh::NSTRIP == 8),
+                  "one query strip per output wave, or two (strips w and 7 - w: equal causal work)");
     static_assert(Sh::kRowK && !Sh::kKT && !Sh::kVD, "the walk stages the row-major phi(K) tile and V^T only");
     static_assert(kBytes == split_walk_lds_bytes(int(sizeof(E)), D, DV, CH), "host LDS formula out of step");
 };

@@ -14,7 +14,7 @@ template <typename E, int D, int DV, int CH, bool GATED, bool IDENT = false, boo
 hipError_t run_fwd_walks(const FwdLaunch& p) {
     using ShT = WalkShape<E, D, DV, CH, GATED, false>;
     using ShO = WalkShape<E, D, DV, CH, GATED, true>;
-    const int tparts = prefix_direct(p.nseg, D, DV) ? 1 : p.tparts;
+    const int tparts = p.tparts;
     const int nslots = (p.nseg - 1) * tparts + 1;
     size_t off_zt = 0, off_lg = 0;
     fwd_workspace_layout(size_t(p.BH) * VS * nslots, D, DV, &off_zt, &off_lg);

@@ -72,10 +72,11 @@ constexpr size_t walk_lds_bytes(int esize, int D, int Dv, int chunk, bool gated,
            (walk_lambda_per_wave(esize, D, Dv, chunk, gated, out) ? size_t(3) * chunk * 4 : 0);
 }
 
-// Whether the output walk of a shape runs as the split 8-wave walk (walk_split_kernel):
-// bf16, D = Dv = 128, ungated, 64-token chunks, features elu + 1, Dv uncut.
+// Whether the output walk of a shape runs as the split 8-wave walk (walk_split_kernel),
+// one workgroup per CU: bf16, ungated, features elu + 1, Dv uncut, and D = Dv = 128 with
+// 64-token chunks or D = Dv = 64 with 128-token chunks.
 constexpr bool walk_split(int esize, int D, int Dv, int chunk, bool gated) {
-    return esize == 2 && D == 128 && Dv == 128 && chunk == 64 && !gated;
+    return esize == 2 && !gated && ((D == 128 && Dv == 128 && chunk == 64) || (D == 64 && Dv == 64 && chunk == 128));
 }
 
 // LDS the FAVOR walks add after the shape's tiles: W's high and low parts, [D][D + 8]
@@ -137,18 +138,27 @@ inline size_t fwd_workspace_layout(size_t slots, int D, int Dv, size_t* off_zt, 
 }
 
 // The output walk sums the totals in front of its segment itself when they are few
-// and small (at most seven 64 x 64 states); otherwise a scan launch does it first.
+// and small (at most seven 64 x 64 states, with one part per segment; totals_parts keeps
+// the parts within the same budget); otherwise a scan launch does it first.
 inline bool prefix_direct(int nseg, int D, int Dv) { return size_t(nseg - 1) * D * Dv <= size_t(7) * 64 * 64; }
 
-// Parts each segment's total is cut into (scanned prefix only; the direct prefix sums
-// one total per segment): as many as fill one round of the totals walk, whose
-// (nseg - 1) segments per head alone can leave compute units idle, and at most one
-// per chunk.
+// Parts each segment's total is cut into: as many as fill one round of the totals walk,
+// whose (nseg - 1) segments per head alone can leave compute units idle, at most one per
+// chunk, and with the direct prefix no more than keep every part in front of the last
+// segment within its budget.
 inline int totals_parts(long heads, int nseg, int L, int D, int Dv, long round) {
-    if (nseg <= 1 || prefix_direct(nseg, D, Dv)) return 1;
+    if (nseg <= 1) return 1;
     long p = round / (heads * long(nseg - 1));
     if (p < 1) p = 1;
     if (p > L) p = L;
+    if (prefix_direct(nseg, D, Dv)) {
+        // parts only where the segments alone would fill less than half a round (the
+        // output walk then sums more totals), and the output walk sums every part in front
+        // of its segment: at most seven 64 x 64 states in all
+        if (heads * long(nseg - 1) * 2 > round) return 1;
+        const long cap = long(7) * 64 * 64 / (long(nseg - 1) * D * Dv);
+        if (p > cap) p = cap < 1 ? 1 : cap;
+    }
     return int(p);
 }
 
