@@ -397,12 +397,15 @@ def source_digest():
 
 def output_walk_name(w, chunk):
     """The output walk kernel of forward workload w at this chunk, as the counter summaries
-    name it: the split 8-wave walk at D = Dv = 128 and chunk 64, the walk over two column
-    parts of 64 where the full tiles exceed the LDS (chunk 256 at D = Dv = 128)."""
-    if w.dtype == "bf16" and w.D == 128 and w.Dv == 128 and w.kind == "fwd":
-        if chunk == 64:
+    name it: the split 8-wave walk at D = Dv = 128 and chunk 64 and at D = Dv = 64 and
+    chunk 128 (ungated bf16), the walk over two column parts of 64 where the full tiles
+    exceed the LDS (chunk 256 at D = Dv = 128)."""
+    if w.dtype == "bf16" and w.kind == "fwd":
+        if w.D == 128 and w.Dv == 128 and chunk == 64:
             return "walk_split_kernel<bf16,128,128,64>"
-        if chunk == 256:
+        if w.D == 64 and w.Dv == 64 and chunk == 128:
+            return "walk_split_kernel<bf16,64,64,128>"
+        if w.D == 128 and w.Dv == 128 and chunk == 256:
             return "walk_kernel<bf16,128,64,256,ungated,output,parts2>"
     return f"walk_kernel<{w.dtype},{w.D},{w.Dv},{chunk},{'gated' if w.kind == 'gated' else 'ungated'},output>"
 
