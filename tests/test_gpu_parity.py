@@ -356,6 +356,22 @@ def test_totals_in_parts(gated):
     assert matrix_rel_err(to64(z), z_ref) <= TOL["bf16"]
 
 
+def test_parted_direct_prefix():
+    # 128 heads of D = Dv = 64 at chunk 128 (the split output walk, one workgroup per CU):
+    # two segments of four chunks per head, the first one's total cut into four parts that
+    # the second segment's output walk sums itself, with an initial state, a ragged tail
+    # and the final state returned
+    B, H, N, D, Dv, chunk = 8, 16, 128 * 7 + 77, 64, 64, 128
+    inp = workloads.random_inputs(61, B, H, N, D, Dv, dtype="bf16", with_state=True, state_scale=5.0)
+    heads = _heads(B, H, 4, 61)
+    _say(f"parted direct prefix, oracle on heads {heads}")
+    o, S, z = run_fwd(inp, chunk, s0=inp["s0"], z0=inp["z0"], return_state=True)
+    o_ref, S_ref, z_ref = oracle_fwd(inp, heads=heads, s0=inp["s0"], z0=inp["z0"])
+    assert rowwise_rel_err(sel(o, heads), o_ref) <= TOL["bf16"]
+    assert matrix_rel_err(sel(S, heads), S_ref) <= TOL["bf16"]
+    assert matrix_rel_err(sel(z, heads), z_ref) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("shape", [(1, 3, 1000, 64, 64, 128), (1, 2, 700, 128, 128, 64), (2, 2, 900, 64, 128, 256),
                                    (1, 2, 700, 128, 128, 256)],
                          ids=["D64c128", "D128c64", "D64Dv128c256", "D128c256"])
