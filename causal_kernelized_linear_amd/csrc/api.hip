@@ -449,7 +449,7 @@ linattn_status_t feat_common(const void* q, const void* k, const void* v, const 
     F.s0 = s0; F.z0 = z0; F.s_out = s_out; F.z_out = z_out;
     F.ws = ws;
     F.BH = int(BH); F.N = N; F.D = D; F.Dv = Dv; F.chunk = chunk;
-    F.nseg = plan.nseg; F.L = plan.L; F.eps = eps;
+    F.nseg = plan.nseg; F.L = plan.L; F.tparts = plan.tparts; F.eps = eps;
     F.normalize = out == LINATTN_OUT_NORMALIZED ? 1 : 0;
     F.stream = static_cast<hipStream_t>(stream);
     L.kind = feature; L.shift = shift; L.W = W; L.H = H; L.M = M; L.es = int(es);

@@ -25,7 +25,7 @@ struct FwdLaunch {
     hipEvent_t prof[4];      // measurement hook: all NULL when unused
     float fshift = 0.0f;     // the walk under relu(x) + fshift features only
     int vsplit = 1;          // column parts of Dv walked by separate workgroups (walk_vsplit)
-    int tparts = 1;          // parts of a segment walked by separate totals workgroups (scanned prefix only)
+    int tparts = 1;          // parts of a segment walked by separate totals workgroups
     const float* W = nullptr;    // FAVOR walks: the projections [H][D][D] fp32
     int H = 1;
 };

@@ -120,6 +120,28 @@ def test_features_workload_sampled_heads(feature):
     assert torch.isfinite(o).all().item()
 
 
+def test_favor_in_walk_many_heads():
+    # FAVOR+ on 128 heads of D = Dv = M = 64 at chunk 128, the walks forming the features
+    # while staging: several segments per head whose totals the output walk sums itself,
+    # with an initial state, a ragged tail and the final state returned
+    B, H, N, D, Dv, chunk = 8, 16, 128 * 7 + 77, 64, 64, 128
+    inp = workloads.random_inputs(63, B, H, N, D, Dv, dtype="bf16", scale=D ** -0.25, with_state=True,
+                                  state_scale=2.0)
+    W = workloads.favor_projection(63, H, D, D)
+    heads = _heads(B, H, 4, 63)
+    _say(f"favor in-walk features, 128 heads, oracle on heads {heads}")
+    o, S, z = binding.fwd_features(*(_dev(inp[n]) for n in ("q", "k", "v")), "favor", W=_dev(W), chunk=chunk,
+                                   s0=_dev(inp["s0"]), z0=_dev(inp["z0"]), return_state=True)
+    torch.cuda.synchronize()
+    pick = lambda t: np.stack([to64(t)[b, h] for b, h in heads])[None]    # noqa: E731
+    o_ref, S_ref, z_ref = oracle.causal_linear_attention(
+        pick(inp["q"]), pick(inp["k"]), pick(inp["v"]), s0=pick(inp["s0"]), z0=pick(inp["z0"]),
+        feature=("favor", to64(W)[[h for _, h in heads]]))
+    assert rowwise_rel_err(pick(o), o_ref) <= TOL["bf16"]
+    assert matrix_rel_err(pick(S), S_ref) <= TOL["bf16"]
+    assert matrix_rel_err(pick(z), z_ref) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("gated", [False, True], ids=["ungated", "gated"])
 @pytest.mark.parametrize("chunk", [64, 128])
 @pytest.mark.parametrize("M", [64, 128])
