@@ -92,8 +92,9 @@ struct BwdArgs {
     void* dq;
     void* dk;
     void* dv;
-    float* fst;          // [BH][NR][D*Dv] accumulator layout: slot r < NR-1 holds the state after run r
-    float* fzt;          // [BH][NR][D]
+    float* fst;          // [BH][FS][D*Dv] accumulator layout: slot t < FS-1 holds the state after
+                         // part t % FP of run t / FP (the state after run r: slot (r+1) FP - 1)
+    float* fzt;          // [BH][FS][D]
     float* rst;          // [BH][NR+1][D*Dv]: run r's adjoint total at slot NR-1-r; after the
                          // scan slot NR-2-r holds the adjoint of the state after run r, and
                          // slot NR-1 the gradient of S0
@@ -109,6 +110,8 @@ struct BwdArgs {
     int NC;              // chunks of C tokens
     int LC;              // chunks per run: one workgroup walks a run, carrying the states through it
     int NR;              // runs, ceil(NC / LC)
+    int FP;              // parts each run's forward total is walked in (by separate workgroups)
+    int FS;              // forward state slots per head, (NR - 1) FP + 1
     float eps;
     int normalize;
 };
@@ -654,7 +657,7 @@ void bwd_dq_kernel(BwdArgs args) {
     f32x4_t sacc[B::kStateUnits];
     float zv[KZ][4];
     if (ck.run > 0) {
-        const size_t fslot = size_t(bh) * args.NR + (ck.run - 1);
+        const size_t fslot = size_t(bh) * args.FS + (size_t(ck.run) * args.FP - 1);
         ck.load_slot(sacc, args.fst + fslot * (D * DV));
         ck.load_zvec(zv, args.fzt + fslot * D);
     } else {
@@ -1014,7 +1017,7 @@ void bwd_dkv_kernel(BwdArgs args) {
     if constexpr (GATED) {
         float wp = 0.0f;
         if (!last_run) {
-            const size_t fsl = size_t(bh) * args.NR + ck.run;
+            const size_t fsl = size_t(bh) * args.FS + (size_t(ck.run + 1) * args.FP - 1);
             f32x4_t sf[B::kStateUnits];
             ck.load_slot(sf, args.fst + fsl * (D * DV));
             float fz[KZ][4];

@@ -59,19 +59,31 @@ hipError_t run_bwd(const BwdLaunch& p) {
         a.LC = p.run > 0 ? (p.run < NC ? p.run : NC) : bwd_chunks_per_group(p.BH, NC, Sh::kWaves, p.cus);
         const int NR = (NC + a.LC - 1) / a.LC;
         a.NR = NR;
+        // each run's forward total in as many parts as fill one round of the totals walk
+        // (its runs alone can leave compute units idle), at most one per chunk; the slots
+        // then number (NR - 1) FP + 1 <= NC per head, within the workspace
+        {
+            const long waves = walk_waves(int(sizeof(E)), D, DV, C, GATED, false);
+            const long fit = long(kMaxLds / kTotBytes);
+            const long round = long(p.cus) * (waves < fit ? waves : fit);
+            long fp = NR > 1 ? round / (long(p.BH) * (NR - 1)) : 1;
+            if (fp > a.LC) fp = a.LC;
+            a.FP = fp < 1 ? 1 : int(fp);
+        }
+        a.FS = (NR - 1) * a.FP + 1;
         constexpr int NBLK = (D * DV + D + kThreads - 1) / kThreads;
         const unsigned BH = unsigned(p.BH);
         // the state in front of every run: the forward's totals walk with one run per
-        // segment, then its scan (which starts from S0, z0)
+        // segment (in FP parts), then its scan over the parts (which starts from S0, z0)
         if (NR > 1) {
             WalkArgs w;
             w.q = p.q; w.k = p.k; w.v = p.v; w.g = p.g; w.o = nullptr;
             w.st = a.fst; w.zt = a.fzt; w.lg = reinterpret_cast<float*>(ws + lay.flg);
             w.s0 = p.s0; w.z0 = p.z0;
-            w.N = p.N; w.BH = p.BH; w.nseg = NR; w.L = a.LC; w.tparts = 1; w.nslots = NR; w.direct = 0; w.want_final = 0; w.eps = p.eps; w.normalize = 1;
-            hipLaunchKernelGGL(k_tot, dim3(BH * unsigned(NR - 1)), dim3(kThreads), kTotBytes, p.stream, w);
+            w.N = p.N; w.BH = p.BH; w.nseg = NR; w.L = a.LC; w.tparts = a.FP; w.nslots = a.FS; w.direct = 0; w.want_final = 0; w.eps = p.eps; w.normalize = 1;
+            hipLaunchKernelGGL(k_tot, dim3(BH * unsigned((NR - 1) * a.FP)), dim3(kThreads), kTotBytes, p.stream, w);
             hipLaunchKernelGGL((scan_kernel<D, DV, GATED>), dim3(BH * NBLK), dim3(kThreads), 0, p.stream, a.fst, a.fzt,
-                               w.lg, p.s0, p.z0, NR, NR - 1);
+                               w.lg, p.s0, p.z0, a.FS, a.FS - 1);
         }
         hipLaunchKernelGGL(k_dq, dim3(BH * unsigned(NR)), dim3(kThreads), Sh::kBytes, p.stream, a);
         // adjoint states: the scan over the runs' adjoint totals, last run first
