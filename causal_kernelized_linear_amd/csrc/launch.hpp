@@ -142,24 +142,30 @@ inline size_t fwd_workspace_layout(size_t slots, int D, int Dv, size_t* off_zt, 
 // the parts within the same budget); otherwise a scan launch does it first.
 inline bool prefix_direct(int nseg, int D, int Dv) { return size_t(nseg - 1) * D * Dv <= size_t(7) * 64 * 64; }
 
-// Parts each segment's total is cut into: as many as fill one round of the totals walk,
-// whose (nseg - 1) segments per head alone can leave compute units idle, at most one per
-// chunk, and with the direct prefix no more than keep every part in front of the last
-// segment within its budget.
+// Parts each segment's total is cut into, where the totals walk's (nseg - 1) segments
+// per head alone can leave compute units idle: as many as fill one round of that walk
+// with a scanned prefix, half of one with the direct prefix (whose output walk reads
+// every part in front of its segment, within the direct prefix's budget), at most one
+// per chunk.
 inline int totals_parts(long heads, int nseg, int L, int D, int Dv, long round) {
     if (nseg <= 1) return 1;
     long p = round / (heads * long(nseg - 1));
     if (p < 1) p = 1;
     if (p > L) p = L;
     if (prefix_direct(nseg, D, Dv)) {
-        // parts only where the segments alone would fill less than half a round (the
-        // output walk then sums more totals), and the output walk sums every part in front
-        // of its segment: at most seven 64 x 64 states in all
+        // parts only where the segments alone would fill less than half a round, and then
+        // as many as fill half of it: the output walk sums every part in front of its
+        // segment (train_bf16: three parts 73-75 us, six 75-77 us), at most seven 64 x 64
+        // states in all
         if (heads * long(nseg - 1) * 2 > round) return 1;
+        p = round / (2 * heads * long(nseg - 1));
+        if (p > L) p = L;
         const long cap = long(7) * 64 * 64 / (long(nseg - 1) * D * Dv);
         if (p > cap) p = cap < 1 ? 1 : cap;
     }
-    return int(p);
+    // no empty parts: as many as parts of ceil(L / p) chunks take
+    const long lp = (L + p - 1) / p;
+    return int((L + lp - 1) / lp);
 }
 
 // Dynamic LDS bytes of a gradient kernel: phi(Q), phi(K) [C][D], V, dOut [C][Dv] and one

@@ -358,10 +358,10 @@ def test_totals_in_parts(gated):
 
 def test_parted_direct_prefix():
     # 128 heads of D = Dv = 64 at chunk 128 (the split output walk, one workgroup per CU):
-    # two segments of four chunks per head, the first one's total cut into four parts that
-    # the second segment's output walk sums itself, with an initial state, a ragged tail
-    # and the final state returned
-    B, H, N, D, Dv, chunk = 8, 16, 128 * 7 + 77, 64, 64, 128
+    # two segments of eight chunks per head, the first one's total cut into three parts
+    # (three, three and two chunks) that the second segment's output walk sums itself,
+    # with an initial state, a ragged tail and the final state returned
+    B, H, N, D, Dv, chunk = 8, 16, 128 * 15 + 77, 64, 64, 128
     inp = workloads.random_inputs(61, B, H, N, D, Dv, dtype="bf16", with_state=True, state_scale=5.0)
     heads = _heads(B, H, 4, 61)
     _say(f"parted direct prefix, oracle on heads {heads}")
