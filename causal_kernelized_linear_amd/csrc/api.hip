@@ -45,9 +45,10 @@ int device_cus() {
 // segment, the first loads) is paid once.
 // vs: the column parts of Dv the walk is cut into (walk_vsplit), each with its own
 // workgroups.
-long target_workgroups(int esize, int D, int Dv, int chunk, bool gated, int vs = 1, bool elu = true) {
-    // the split output walk (elu + 1 features only): one 8-wave workgroup per compute unit
-    if (elu && vs == 1 && linattn::walk_split(esize, D, Dv, chunk, gated)) return long(device_cus());
+// split: the features allow the split output walk (elu + 1, relu + shift).
+long target_workgroups(int esize, int D, int Dv, int chunk, bool gated, int vs = 1, bool split = true) {
+    // the split output walk: one 8-wave workgroup per compute unit
+    if (split && vs == 1 && linattn::walk_split(esize, D, Dv, chunk, gated)) return long(device_cus());
     return long(device_cus()) * linattn::walk_waves(esize, D, Dv / vs, chunk, gated, true);
 }
 
@@ -103,6 +104,14 @@ Plan fwd_plan(int esize, long BH, int N, int D, int Dv, int chunk, bool gated) {
     }
     const long totals_round = long(device_cus()) * linattn::walk_waves(esize, D, Dv / vs, chunk, gated, false);
     return make_plan(BH, N, D, Dv, chunk, target_workgroups(esize, D, Dv, chunk, gated, vs), vs, totals_round);
+}
+
+// The plan of the walks under other feature maps (state rows M): relu + shift walks q
+// and k as given, so it takes the chunked forward's plan, split walk included; FAVOR+
+// keeps the 4-wave walks' plan with one part per segment total.
+Plan feature_plan(int esize, bool gated, long BH, int N, int M, int Dv, int chunk, bool relu) {
+    const long round = relu ? long(device_cus()) * linattn::walk_waves(esize, M, Dv, chunk, gated, false) : 0;
+    return make_plan(BH, N, M, Dv, chunk, target_workgroups(esize, M, Dv, chunk, gated, 1, relu), 1, round);
 }
 
 // Workspace bytes that serve the forward of this shape whatever its element type and
@@ -428,7 +437,7 @@ linattn_status_t feat_common(const void* q, const void* k, const void* v, const 
         linattn::walk_lds_bytes(int(es), M, Dv, chunk, g != nullptr) > linattn::kMaxLds ||
         (feature == LINATTN_FEATURE_FAVOR && (size_t(64) * (D + 4) + size_t(M) * (D + 4) + 64) * 4 > linattn::kMaxLds))
         return LINATTN_ERR_UNSUPPORTED;
-    const Plan plan = make_plan(BH, N, M, Dv, chunk, target_workgroups(int(es), M, Dv, chunk, g != nullptr, 1, false));
+    const Plan plan = feature_plan(int(es), g != nullptr, BH, N, M, Dv, chunk, feature == LINATTN_FEATURE_RELU);
     const size_t fb = feature_bytes(BH, N, M, es);
     const size_t need = 2 * fb + plan.bytes;
     if (ws_bytes < need || !ws || !aligned16(ws)) return LINATTN_ERR_WORKSPACE;
@@ -468,7 +477,14 @@ size_t linattn_fwd_features_workspace_size(int B, int H, int N, int D, int Dv, i
     if (B <= 0 || H <= 0 || N <= 0 || D <= 0 || Dv <= 0 || chunk <= 0 || M <= 0 || !dtype_ok(dtype)) return 0;
     const long BH = long(B) * long(H);
     const size_t es = esize(dtype);
-    return 2 * feature_bytes(BH, N, M, es) + make_plan(BH, N, M, Dv, chunk, max_target_workgroups(M, Dv, chunk)).bytes;
+    // the largest of the feature maps' plans over gating (relu + shift may take the split
+    // walk's plan: fewer segments, but their totals in parts)
+    size_t b = make_plan(BH, N, M, Dv, chunk, max_target_workgroups(M, Dv, chunk)).bytes;
+    for (bool gated : {false, true}) {
+        const size_t r = feature_plan(int(es), gated, BH, N, M, Dv, chunk, true).bytes;
+        b = r > b ? r : b;
+    }
+    return 2 * feature_bytes(BH, N, M, es) + b;
 }
 
 linattn_status_t linattn_fwd_features(const void* q, const void* k, const void* v, const float* g, void* o,

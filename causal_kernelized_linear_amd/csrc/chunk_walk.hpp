@@ -1360,9 +1360,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
 // of the two overlap, and either kind's lighter phase fills the other's heavier one.
 constexpr int kSplitThreads = 2 * kThreads;
 
-template <typename E, int D, int DV, int CH>
+template <typename E, int D, int DV, int CH, bool RELU = false>
 struct SplitShape {
-    using W = ChunkWalker<E, D, DV, CH, false, true>;
+    using W = ChunkWalker<E, D, DV, CH, false, true, false, RELU>;
     using Sh = typename W::Sh;
     // Its own carve-up: each tile's two buffers side by side, so that one register holds
     // a lane's address in both (the second is the first plus an instruction's immediate
@@ -1385,10 +1385,10 @@ struct SplitShape {
     static_assert(kBytes == split_walk_lds_bytes(int(sizeof(E)), D, DV, CH), "host LDS formula out of step");
 };
 
-template <typename E, int D, int DV, int CH>
+template <typename E, int D, int DV, int CH, bool RELU = false>
 __global__ __launch_bounds__(kSplitThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void walk_split_kernel(
     WalkArgs args) {
-    using SS = SplitShape<E, D, DV, CH>;
+    using SS = SplitShape<E, D, DV, CH, RELU>;
     using W = typename SS::W;
     using Sh = typename SS::Sh;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -1402,6 +1402,7 @@ __global__ __launch_bounds__(kSplitThreads) __attribute__((amdgpu_waves_per_eu(2
 
     // the 4-wave walker's members, renumbered within each kind of wave
     W wk;
+    if constexpr (RELU) wk.fshift = args.fshift;
     wk.init(smem, N, reinterpret_cast<const E*>(args.q) + size_t(bh) * N * D,
             reinterpret_cast<const E*>(args.k) + size_t(bh) * N * D,
             reinterpret_cast<const E*>(args.v) + size_t(bh) * N * DV, nullptr);

@@ -35,10 +35,10 @@ hipError_t run_fwd_walks(const FwdLaunch& p) {
     a.stream_kv = totals_stream_kv(p.BH, p.N, D, DV * VS, int(sizeof(E))) ? 1 : 0;
     auto* k_tot = walk_kernel<E, D, DV, CH, GATED, false, IDENT, RELU, VS, false, FAVOR>;
     // the output walk: the split 8-wave walk where its shape has one, else the 4-wave one
-    constexpr bool kSplit = walk_split(int(sizeof(E)), D, DV, CH, GATED) && VS == 1 && !IDENT && !RELU && !FAVOR;
+    constexpr bool kSplit = walk_split(int(sizeof(E)), D, DV, CH, GATED) && VS == 1 && !IDENT && !FAVOR;
     auto* k_out = [] {
         if constexpr (kSplit)
-            return walk_split_kernel<E, D, DV, CH>;
+            return walk_split_kernel<E, D, DV, CH, RELU>;
         else
             return walk_kernel<E, D, DV, CH, GATED, true, IDENT, RELU, VS, false, FAVOR>;
     }();

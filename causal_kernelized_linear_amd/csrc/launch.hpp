@@ -73,8 +73,8 @@ constexpr size_t walk_lds_bytes(int esize, int D, int Dv, int chunk, bool gated,
 }
 
 // Whether the output walk of a shape runs as the split 8-wave walk (walk_split_kernel),
-// one workgroup per CU: bf16, ungated, features elu + 1, Dv uncut, and D = Dv = 128 with
-// 64-token chunks or D = Dv = 64 with 128-token chunks.
+// one workgroup per CU: bf16, ungated, features elu + 1 or relu + shift, Dv uncut, and
+// D = Dv = 128 with 64-token chunks or D = Dv = 64 with 128-token chunks.
 constexpr bool walk_split(int esize, int D, int Dv, int chunk, bool gated) {
     return esize == 2 && !gated && ((D == 128 && Dv == 128 && chunk == 64) || (D == 64 && Dv == 64 && chunk == 128));
 }
