@@ -1507,9 +1507,20 @@ __global__ __launch_bounds__(kSplitThreads) __attribute__((amdgpu_waves_per_eu(2
             wk.sZb = zb_buf[n & 1];
             wk.sK = k_buf[n & 1];
             wk.sVt = vt_buf[n & 1];
-            // the strip with a runtime key-block loop: the per-wave straight-line form
-            // holds more operands than two waves per SIMD leave registers for
-            wk.outputs_seq(fq, ts, ob, args.eps, args.normalize);
+            // at D = Dv = 64 the per-wave straight-line form (both strips' operands read
+            // once); at 128 x 128 the strip with a runtime key-block loop, since the
+            // straight-line form holds more operands than two waves per SIMD leave
+            // registers for
+            if constexpr (D * DV < 128 * 128) {
+                switch (w) {
+                    case 0: wk.template outputs_w<0>(fq, ts, ob, args.eps, args.normalize); break;
+                    case 1: wk.template outputs_w<1>(fq, ts, ob, args.eps, args.normalize); break;
+                    case 2: wk.template outputs_w<2>(fq, ts, ob, args.eps, args.normalize); break;
+                    default: wk.template outputs_w<3>(fq, ts, ob, args.eps, args.normalize); break;
+                }
+            } else {
+                wk.outputs_seq(fq, ts, ob, args.eps, args.normalize);
+            }
             __syncthreads();
         };
         for (int n = 0; n < nch; n += 2) {
