@@ -110,11 +110,16 @@ struct WalkArgs {
 // Column part and item (head * segments + segment) of a walk workgroup.  With VS parts,
 // groups of 8 consecutive blocks take 8 consecutive items, one group per part in turn,
 // so the parts of an item are 8 blocks apart (the same XCD) and dispatched together.
+// GROUP (one part, a grid of whole groups of 8): blocks are dealt to the 8 XCDs in turn,
+// so block b takes item (b mod 8) (grid / 8) + b / 8 and each XCD runs a run of
+// consecutive items, whole heads: every later segment of a head reads the totals in front
+// of it through one L2 (the direct prefix).
 // item >= items: a padding block of the last group, which does nothing.
-template <int VS>
+template <int VS, bool GROUP = false>
 __device__ __forceinline__ void walk_block(int items, int& item, int& part) {
     if constexpr (VS == 1) {
-        item = blockIdx.x;
+        const unsigned g = gridDim.x;
+        item = GROUP && g % 8 == 0 ? int((blockIdx.x % 8) * (g / 8) + blockIdx.x / 8) : int(blockIdx.x);
         part = 0;
     } else {
         const int lo = blockIdx.x % 8, hi = blockIdx.x / 8;
@@ -124,9 +129,10 @@ __device__ __forceinline__ void walk_block(int items, int& item, int& part) {
     (void)items;
 }
 
-// Blocks of a walk launch over `items` (head, segment) pairs and VS column parts.
-__host__ __device__ constexpr unsigned walk_grid(unsigned items, int VS) {
-    return VS == 1 ? items : (items + 7) / 8 * 8 * unsigned(VS);
+// Blocks of a walk launch over `items` (head, segment) pairs and VS column parts (GROUP:
+// whole groups of 8, as walk_block's GROUP mapping needs).
+__host__ __device__ constexpr unsigned walk_grid(unsigned items, int VS, bool group = false) {
+    return VS == 1 && !group ? items : (items + 7) / 8 * 8 * unsigned(VS);
 }
 
 template <typename E, int D, int DV, int CH, bool GATED, bool OUT>
@@ -1273,7 +1279,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(
     // the totals skip the last segment and cut the others into tparts parts
     const int nsw = OUTPUT ? args.nseg : (args.nseg - 1) * args.tparts;
     int item, part;
-    walk_block<VS>(args.BH * nsw, item, part);
+    walk_block<VS, OUTPUT>(args.BH * nsw, item, part);
     if (item >= args.BH * nsw) return;                      // padding block (uniform over the workgroup)
     const int sub = item % nsw;                             // segment (output) or totals slot
     const int bh = item / nsw;

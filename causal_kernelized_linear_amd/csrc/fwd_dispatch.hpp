@@ -68,7 +68,7 @@ hipError_t run_fwd_walks(const FwdLaunch& p) {
         hipLaunchKernelGGL((scan_kernel<D, DV, GATED, VS>), dim3(vheads * NBLK), dim3(kThreads), 0, p.stream, a.st,
                            a.zt, a.lg, p.s0, p.z0, nslots, nslots - 1);
     mark(2);
-    hipLaunchKernelGGL(k_out, dim3(walk_grid(unsigned(p.BH) * unsigned(p.nseg), VS)), dim3(kOutThreads), kOutBytes,
+    hipLaunchKernelGGL(k_out, dim3(walk_grid(unsigned(p.BH) * unsigned(p.nseg), VS, !kSplit)), dim3(kOutThreads), kOutBytes,
                        p.stream, a);
     if (a.want_final)
         hipLaunchKernelGGL((final_kernel<D, DV, VS>), dim3(vheads * NBLK), dim3(kThreads), 0, p.stream, a.st, a.zt,
