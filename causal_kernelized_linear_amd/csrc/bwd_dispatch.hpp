@@ -83,12 +83,12 @@ hipError_t run_bwd(const BwdLaunch& p) {
             w.N = p.N; w.BH = p.BH; w.nseg = NR; w.L = a.LC; w.tparts = a.FP; w.nslots = a.FS; w.direct = 0; w.want_final = 0; w.eps = p.eps; w.normalize = 1;
             hipLaunchKernelGGL(k_tot, dim3(BH * unsigned((NR - 1) * a.FP)), dim3(kThreads), kTotBytes, p.stream, w);
             hipLaunchKernelGGL((scan_kernel<D, DV, GATED>), dim3(BH * NBLK), dim3(kThreads), 0, p.stream, a.fst, a.fzt,
-                               w.lg, p.s0, p.z0, a.FS, a.FS - 1);
+                               w.lg, p.s0, p.z0, a.FS, a.FS - 1, a.FP);
         }
         hipLaunchKernelGGL(k_dq, dim3(BH * unsigned(NR)), dim3(kThreads), Sh::kBytes, p.stream, a);
         // adjoint states: the scan over the runs' adjoint totals, last run first
         hipLaunchKernelGGL((scan_kernel<D, DV, GATED>), dim3(BH * NBLK), dim3(kThreads), 0, p.stream, a.rst, a.rzt,
-                           a.rlg, static_cast<const float*>(nullptr), static_cast<const float*>(nullptr), NR + 1, NR);
+                           a.rlg, static_cast<const float*>(nullptr), static_cast<const float*>(nullptr), NR + 1, NR, 1);
         hipLaunchKernelGGL(k_dkv, dim3(BH * unsigned(NR)), dim3(kThreads), Sh::kBytes, p.stream, a);
         if (GATED && p.dg) {
             const int nwork = p.BH * NC, per = kThreads / kWave;

@@ -1537,14 +1537,16 @@ __global__ __launch_bounds__(kSplitThreads) __attribute__((amdgpu_waves_per_eu(2
 }
 
 // In place over the first nscan of each head's nslots slots: slot s becomes
-// P_{s+1} = 2^lg_s P_s + T_s with P_0 = S0 (fp32), one thread per state element.
+// P_{s+1} = 2^lg_s P_s + T_s with P_0 = S0 (fp32), one thread per state element.  Only
+// the slots that a reader takes are written back: every keep-th (s + 1 a multiple of
+// keep; keep = the parts per segment, whose prefixes are read only at segment starts).
 // Element e < D*Dv is in accumulator layout: tile u = e / 256 (a = u / (Dv/16),
 // b = u % (Dv/16)), lane = (e / 4) % 64, r = e % 4, which is S[16a + 4(lane/16) + r][16b + lane%16].
 // With VS column parts the slots are per (head, part), vbh = bh * VS + part, each a
 // [D][DV] slice whose initial value is columns part * DV .. of the caller's S0 rows.
 template <int D, int DV, bool GATED, int VS = 1>
 __global__ __launch_bounds__(kThreads) void scan_kernel(float* st, float* zt, const float* lg, const float* s0,
-                                                       const float* z0, int nslots, int nscan) {
+                                                       const float* z0, int nslots, int nscan, int keep) {
     constexpr int NS = D * DV;
     constexpr int NBLK = (NS + D + kThreads - 1) / kThreads;   // workgroups per head and part
     const int e = (blockIdx.x % NBLK) * kThreads + threadIdx.x;
@@ -1586,7 +1588,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(float* st, float* zt, co
         for (int i = 0; i < U; ++i) {
             if (s0i + i < n) {
                 acc = f[i] * acc + t[i];
-                base[size_t(s0i + i) * stride] = acc;
+                if ((s0i + i + 1) % keep == 0) base[size_t(s0i + i) * stride] = acc;
             }
         }
     }

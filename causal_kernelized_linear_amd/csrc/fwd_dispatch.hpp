@@ -66,7 +66,7 @@ hipError_t run_fwd_walks(const FwdLaunch& p) {
     mark(1);
     if (p.nseg > 1 && !a.direct)
         hipLaunchKernelGGL((scan_kernel<D, DV, GATED, VS>), dim3(vheads * NBLK), dim3(kThreads), 0, p.stream, a.st,
-                           a.zt, a.lg, p.s0, p.z0, nslots, nslots - 1);
+                           a.zt, a.lg, p.s0, p.z0, nslots, nslots - 1, tparts);
     mark(2);
     hipLaunchKernelGGL(k_out, dim3(walk_grid(unsigned(p.BH) * unsigned(p.nseg), VS, !kSplit)), dim3(kOutThreads), kOutBytes,
                        p.stream, a);
