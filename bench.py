@@ -129,7 +129,36 @@ def device_input_sets(w, rotate_bytes=600e6):
     return sets
 
 
-def time_forward(w, chunk, steps, warmup, ev, rotate_bytes=600e6, normalize=True, sets=None):
+def warm_up(call, warmup, ev, stream, settle_ms=0.0):
+    """Untimed warmup: `warmup` calls, then (settle_ms > 0) more, until the device has run
+    at least settle_ms of them back to back.  Its clocks reach their steady state only
+    after tens of milliseconds of sustained work, and the host-side set-up before each
+    leg lets them fall; settle_ms is used for the legs beside the headline, whose own
+    warmup is exactly --warmup steps."""
+    import torch
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    if settle_ms <= 0.0:
+        return
+    done_ms, n = 0.0, warmup
+    a, b = ev.create(2)
+    batch = 8
+    while done_ms < settle_ms and n < warmup + 100000:
+        ev.record(a, stream)
+        for j in range(batch):
+            call(n + j)
+        ev.record(b, stream)
+        torch.cuda.synchronize()
+        took = ev.ms(a, b)
+        done_ms += took
+        n += batch
+        per = max(took / batch, 1e-3)
+        batch = max(1, min(4096, int((settle_ms - done_ms) / per) + 1))
+
+
+def time_forward(w, chunk, steps, warmup, ev, rotate_bytes=600e6, normalize=True, sets=None, settle_ms=0.0):
     """Time `steps` forwards of workload w; returns a dict of timings (ms).
 
     Two timed passes of `steps` forwards each.  The first is bracketed by two hipEvents
@@ -160,9 +189,7 @@ def time_forward(w, chunk, steps, warmup, ev, rotate_bytes=600e6, normalize=True
         else:
             binding.fwd_chunked(s["q"], s["k"], s["v"], chunk=chunk, out=outs[i % nsets], workspace=ws)
 
-    for i in range(warmup):
-        call(i)
-    torch.cuda.synchronize()
+    warm_up(call, warmup, ev, stream, settle_ms)
     # pass 1: the whole forward, no per-launch events
     t0, t1 = ev.create(2)
     wall0 = time.perf_counter()
@@ -205,7 +232,7 @@ def time_forward(w, chunk, steps, warmup, ev, rotate_bytes=600e6, normalize=True
     return res
 
 
-def time_decode(w, steps, warmup, ev, normalize=True):
+def time_decode(w, steps, warmup, ev, normalize=True, settle_ms=0.0):
     """Per-step time of the decode step (gated when the workload carries g); in the
     normaliser-free mode z is not passed, so the step moves no z bytes."""
     import torch
@@ -224,9 +251,7 @@ def time_decode(w, steps, warmup, ev, normalize=True):
         binding.decode_step(s["q"], s["k"], s["v"], s["S"], s["z"] if normalize else None, out=outs[i % nsets],
                             g=s.get("g"), normalize=normalize, a=s.get("a"))
 
-    for i in range(warmup):
-        call(i)
-    torch.cuda.synchronize()
+    warm_up(call, warmup, ev, stream, settle_ms)
     evs = [ev.create(2) for _ in range(steps)]
     for i in range(steps):
         ev.record(evs[i][0], stream)
@@ -259,7 +284,7 @@ def bwd_flops_per_unit(w):
     return 12 * w.D * w.Dv + 4 * (BWD_CHUNK + 1) * (w.D + w.Dv)
 
 
-def time_backward(w, steps, warmup, ev):
+def time_backward(w, steps, warmup, ev, settle_ms=0.0):
     """Per-step time of linattn_bwd on workload w (inputs and outputs preallocated)."""
     import torch
     from causal_kernelized_linear_amd import binding, workloads
@@ -278,9 +303,7 @@ def time_backward(w, steps, warmup, ev):
         s = sets[i % 2]
         binding.bwd(s["q"], s["k"], s["v"], s["dout"], g=s.get("g"), workspace=ws, grads=grads[i % 2])
 
-    for i in range(warmup):
-        call(i)
-    torch.cuda.synchronize()
+    warm_up(call, warmup, ev, stream, settle_ms)
     t0, t1 = ev.create(2)
     ev.record(t0, stream)
     for i in range(steps):
@@ -299,7 +322,7 @@ def vd_bytes_per_unit(w):
     return (2 * w.D + w.Dv) * es + 4 * w.D + w.Dv * es
 
 
-def time_vdecay(w, steps, warmup, ev):
+def time_vdecay(w, steps, warmup, ev, settle_ms=0.0):
     """Per-step time of linattn_fwd_vdecay on workload w (two input sets rotated)."""
     import torch
     from causal_kernelized_linear_amd import binding, workloads
@@ -317,9 +340,7 @@ def time_vdecay(w, steps, warmup, ev):
         s = sets[i % 2]
         binding.fwd_vdecay(s["q"], s["k"], s["v"], s["a"], out=outs[i % 2], workspace=ws)
 
-    for i in range(warmup):
-        call(i)
-    torch.cuda.synchronize()
+    warm_up(call, warmup, ev, stream, settle_ms)
     t0, t1 = ev.create(2)
     ev.record(t0, stream)
     for i in range(steps):
@@ -332,7 +353,7 @@ def time_vdecay(w, steps, warmup, ev):
     return {"ms_per_step": ms}
 
 
-def time_features(w, feature, steps, warmup, ev, M=64):
+def time_features(w, feature, steps, warmup, ev, M=64, settle_ms=0.0):
     """Per-step time of linattn_fwd_features on workload w (two input sets rotated)."""
     import torch
     from causal_kernelized_linear_amd import binding, workloads
@@ -354,9 +375,7 @@ def time_features(w, feature, steps, warmup, ev, M=64):
         binding.fwd_features(s["q"], s["k"], s["v"], feature, shift=0.05, W=W, chunk=w.chunks[0], out=outs[i % 2],
                              workspace=ws)
 
-    for i in range(warmup):
-        call(i)
-    torch.cuda.synchronize()
+    warm_up(call, warmup, ev, stream, settle_ms)
     t0, t1 = ev.create(2)
     ev.record(t0, stream)
     for i in range(steps):
@@ -566,9 +585,10 @@ def main():
 
     extra_steps = max(5, min(args.steps, 20))
     # each extra leg follows host-side set-up (its inputs drawn on the CPU, seconds during
-    # which the device idles and its clocks fall): a fixed warmup brings it back to steady
-    # clocks whatever --warmup the headline is given
+    # which the device idles and its clocks fall): its warmup runs at least 100 steps and
+    # 50 ms of them back to back, whatever --warmup the headline is given
     extra_warm = 100
+    extra_settle_ms = 50.0
     chunk = args.chunk
     # the headline's inputs go to the device first, so that its warmup follows the other
     # legs' GPU work directly, with no host-side set-up in between
@@ -579,27 +599,27 @@ def main():
 
     if "train" in legs:
         wt = workloads.WORKLOADS["train_bf16"]
-        rt = time_forward(wt, 128, args.steps, extra_warm, ev)
+        rt = time_forward(wt, 128, args.steps, extra_warm, ev, settle_ms=extra_settle_ms)
         line["train"] = {"workload": "train_bf16: B=8 H=16 N=4096 D=Dv=64 bf16, fp32 state, chunk 128",
                          **fwd_leg(wt, 128, rt),
                          "walk_output_traffic": stored_traffic(output_walk_name(wt, 128), wt.name, 128)}
 
     if "fp32" in legs:
         wf = workloads.WORKLOADS["fp32_small"]
-        rf = time_forward(wf, 64, extra_steps, extra_warm, ev)
+        rf = time_forward(wf, 64, extra_steps, extra_warm, ev, settle_ms=extra_settle_ms)
         line["fp32_small"] = {"workload": "fp32_small: B=1 H=2 N=512 D=Dv=64 fp32, chunk 64 (launch-bound)",
                               "tokens_per_s": wf.B * wf.N / (rf["ms_per_step"] * 1e-3),
                               "ms_per_step": rf["ms_per_step"], "kernel_ms": rf["kernel_ms"]}
 
     wg = workloads.WORKLOADS["gated_bf16"]
     if "gated" in legs:
-        rg = time_forward(wg, 128, extra_steps, extra_warm, ev)
+        rg = time_forward(wg, 128, extra_steps, extra_warm, ev, settle_ms=extra_settle_ms)
         line["gated"] = {"workload": "gated_bf16: B=4 H=16 N=8192 D=Dv=64 bf16, scalar gate, chunk 128",
                          **fwd_leg(wg, 128, rg)}
 
     if "decode" in legs:
         wd = workloads.WORKLOADS["decode_bf16"]
-        rd = time_decode(wd, extra_steps, extra_warm, ev)
+        rd = time_decode(wd, extra_steps, extra_warm, ev, settle_ms=extra_settle_ms)
         sd = rd["ms_per_step"] * 1e-3
         line["decode"] = {
             "workload": "decode_bf16: B=256 H=32 D=Dv=128, fp32 state, one token",
@@ -609,7 +629,7 @@ def main():
         }
 
     if "gated_numerator" in legs:
-        rn = time_forward(wg, 128, extra_steps, extra_warm, ev, normalize=False)
+        rn = time_forward(wg, 128, extra_steps, extra_warm, ev, normalize=False, settle_ms=extra_settle_ms)
         sn = rn["ms_per_step"] * 1e-3
         ug = fwd_units(wg)
         line["gated_numerator"] = {
@@ -622,7 +642,7 @@ def main():
     if "decode_gated" in legs:
         wdg = workloads.WORKLOADS["decode_gated_bf16"]
         for key, norm in (("decode_gated", True), ("decode_gated_numerator", False)):
-            rdg = time_decode(wdg, extra_steps, extra_warm, ev, normalize=norm)
+            rdg = time_decode(wdg, extra_steps, extra_warm, ev, normalize=norm, settle_ms=extra_settle_ms)
             sdg = rdg["ms_per_step"] * 1e-3
             nbytes = decode_bytes(wdg, with_z=norm)
             line[key] = {
@@ -636,7 +656,7 @@ def main():
     if "backward" in legs:
         for key, wname in (("backward", "train_bf16"), ("backward_gated", "gated_bf16")):
             wb = workloads.WORKLOADS[wname]
-            rb = time_backward(wb, extra_steps, extra_warm, ev)
+            rb = time_backward(wb, extra_steps, extra_warm, ev, settle_ms=extra_settle_ms)
             sb = rb["ms_per_step"] * 1e-3
             ub = fwd_units(wb)
             line[key] = {
@@ -651,7 +671,7 @@ def main():
 
     if "vdecay" in legs:
         wvd = workloads.WORKLOADS["vdecay_bf16"]
-        rvd = time_vdecay(wvd, extra_steps, extra_warm, ev)
+        rvd = time_vdecay(wvd, extra_steps, extra_warm, ev, settle_ms=extra_settle_ms)
         svd = rvd["ms_per_step"] * 1e-3
         uvd = fwd_units(wvd)
         line["vdecay"] = {
@@ -663,7 +683,7 @@ def main():
 
     if "decode_vdecay" in legs:
         wdv = workloads.WORKLOADS["decode_vdecay_bf16"]
-        rdv = time_decode(wdv, extra_steps, extra_warm, ev)
+        rdv = time_decode(wdv, extra_steps, extra_warm, ev, settle_ms=extra_settle_ms)
         sdv = rdv["ms_per_step"] * 1e-3
         line["decode_vdecay"] = {
             "workload": "decode_vdecay_bf16: B=256 H=32 D=Dv=128, fp32 state, one token, decay per dimension",
@@ -674,7 +694,7 @@ def main():
     if "features" in legs:
         for key, wname, feat in (("features_relu", "train_bf16", "relu"), ("features_favor", "favor_bf16", "favor")):
             wf = workloads.WORKLOADS[wname]
-            rf = time_features(wf, feat, extra_steps, extra_warm, ev)
+            rf = time_features(wf, feat, extra_steps, extra_warm, ev, settle_ms=extra_settle_ms)
             sf = rf["ms_per_step"] * 1e-3
             uf = fwd_units(wf)
             line[key] = {
@@ -691,7 +711,8 @@ def main():
     if "sweep" in legs:
         sweep = {}
         for c in sorted(wl.chunks, reverse=True):
-            rl = time_forward(wl, c, max(3, extra_steps // 2), extra_warm, ev, rotate_bytes=2.5e9, sets=head_sets)
+            rl = time_forward(wl, c, max(3, extra_steps // 2), extra_warm, ev, rotate_bytes=2.5e9, sets=head_sets,
+                              settle_ms=extra_settle_ms)
             sweep[str(c)] = fwd_leg(wl, c, rl)
         line["longctx_chunk_sweep"] = {"workload": "longctx_bf16: B=1 H=32 N=65536 D=Dv=128 bf16",
                                        **{str(c): sweep[str(c)] for c in wl.chunks}}
